@@ -1,0 +1,148 @@
+"""CPU oracle for the Complex KDA (CKDA) recurrence -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg import
+this package.  The product library never imports, links or calls it, and it
+imports nothing from the product package.
+
+The heavy lifting is the token-by-token fp64 recurrence in ``ckda_oracle.c``
+(see that file's header for the update rule and where it is stated).  This
+module loads it through ctypes and adds two small helpers built on it:
+
+* :func:`transition` -- the one-token transition matrix of the oracle itself,
+  obtained by running it with S0 = I and v = 0 (then S_1 = A S0 = A).
+* :mod:`oracle.chunked` -- a dense chunked (WY/UT) fp64 formulation in NumPy,
+  used only to check on tiny inputs that the chunked algebra equals the
+  sequential recurrence.
+
+Inputs are taken as NumPy arrays of any float dtype and widened to fp64
+exactly (bf16 and fp32 values are exactly representable in fp64).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ckda_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libckda_oracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle with gcc into ``oracle/libckda_oracle.so``."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-shared", "-fPIC", "-pthread",
+                               _SRC, "-o", tmp])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB_PATH)
+        dp = ctypes.POINTER(ctypes.c_double)
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        ci = ctypes.c_int
+        lib.ckda_oracle_forward.argtypes = [dp, dp, dp, dp, dp, dp, i64p, ci, ci, ci, ci,
+                                            ci, ci, dp, dp, ci]
+        lib.ckda_oracle_forward.restype = ci
+        lib.ckda_oracle_decode.argtypes = [dp, dp, dp, dp, dp, dp, dp, ci, ci, ci, ci, ci]
+        lib.ckda_oracle_decode.restype = ci
+        _lib = lib
+    return _lib
+
+
+def _f64(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def default_threads() -> int:
+    return max(1, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity")
+               else (os.cpu_count() or 1))
+
+
+def forward(q, k, v, g, beta, S0=None, cu_seqlens=None, nthreads: int | None = None):
+    """Token-by-token CKDA forward in fp64.
+
+    Shapes: q, k, g ``[B, T, H, dk]``; v ``[B, T, H, dv]``; beta ``[B, T, H]``;
+    S0 ``[N, H, dk, dv]`` or None (zero state); cu_seqlens ``[N+1]`` or None.
+    With cu_seqlens, B must be 1 and the sequences are the packed token ranges
+    ``[cu[n], cu[n+1])``.  Returns ``(o [B, T, H, dv], S_T [N, H, dk, dv])``.
+    """
+    q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or g.shape != q.shape or v.shape[:3] != (B, T, H) \
+            or beta.shape != (B, T, H):
+        raise ValueError("shape mismatch")
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+        N = cu.shape[0] - 1
+        if B != 1:
+            raise ValueError("packed sequences need B == 1")
+    else:
+        cu = None
+        N = B
+    S0a = None if S0 is None else _f64(S0)
+    if S0a is not None and S0a.shape != (N, H, dk, dv):
+        raise ValueError("S0 shape mismatch")
+    o = np.zeros((B, T, H, dv), dtype=np.float64)
+    S_T = np.zeros((N, H, dk, dv), dtype=np.float64)
+    cu_p = None if cu is None else cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    rc = _load().ckda_oracle_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                     _ptr(S0a), cu_p, B, T, H, dk, dv, N, _ptr(o),
+                                     _ptr(S_T), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle rejected the sizes")
+    return o, S_T
+
+
+def decode_step(q, k, v, g, beta, S, nthreads: int | None = None):
+    """One decode step.  ``S`` ([N, H, dk, dv], fp64, C-contiguous) is updated
+    in place; returns o ``[N, H, dv]``."""
+    q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
+    if S.dtype != np.float64 or not S.flags.c_contiguous:
+        raise ValueError("S must be a C-contiguous float64 array (updated in place)")
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    o = np.zeros((N, H, dv), dtype=np.float64)
+    rc = _load().ckda_oracle_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                    _ptr(S), _ptr(o), N, H, dk, dv,
+                                    nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle rejected the sizes")
+    return o
+
+
+def transition(k, g, beta):
+    """The oracle's own one-token transition matrix A (dk x dk).
+
+    Runs the oracle on one token with S0 = I (so dv = dk) and v = 0; then
+    S_1 = A S0 + beta k 0^T = A.
+    """
+    k = _f64(k).reshape(-1)
+    g = _f64(g).reshape(-1)
+    dk = k.shape[0]
+    one = lambda a: a.reshape(1, 1, 1, -1)
+    q = np.zeros(dk)
+    v = np.zeros(dk)
+    b = np.array(float(beta)).reshape(1, 1, 1)
+    S0 = np.eye(dk).reshape(1, 1, dk, dk)
+    _, S_T = forward(one(q), one(k), one(v), one(g), b, S0=S0, nthreads=1)
+    return S_T[0, 0]
+
+
+__all__ = ["build", "forward", "decode_step", "transition", "default_threads"]

@@ -1,0 +1,75 @@
+"""The oracle's pins are sharp: plant plausible mistakes in copies of the C
+oracle (on the CPU, in a temporary directory) and check that the pin suite
+fails for every one of them."""
+import os
+import re
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "ckda_oracle.c")
+
+# (name, regex on the source, replacement)
+MUTANTS = [
+    ("decay dropped", r"S\[c \* dv \+ j\] \*= a\[c\];", ";"),
+    ("gate on value columns", r"S\[c \* dv \+ j\] \*= a\[c\];", "S[c * dv + j] *= a[j % dk];"),
+    ("delta term sign", r"\+= b \* k\[c\] \* \(v\[j\] - u\[j\]\)", "-= b * k[c] * (v[j] - u[j])"),
+    ("erase sign", r"\(v\[j\] - u\[j\]\)", "(v[j] + u[j])"),
+    ("readout of S, not S^T", r"o\[j\] \+= q\[c\] \* S\[c \* dv \+ j\];",
+     "o[j] += q[c] * S[(j % dk) * dv + (c % dv)];"),
+    ("beta squared", r"S\[c \* dv \+ j\] \+= b \* k", "S[c * dv + j] += b * b * k"),
+]
+
+PIN_TESTS = [
+    lambda: [pins.test_householder_dial(r) for r in pins._golden.load("householder_dial.txt")],
+    pins.test_beta_zero_keeps_state_and_reads_it,
+    pins.test_beta_zero_is_pure_gate_decay,
+    pins.test_projection_erases_key_direction,
+    pins.test_first_token_from_zero_state,
+    pins.test_quarter_turn_golden,
+    lambda: [pins.test_closed_form_2x2(r) for r in pins._golden.load("closed_form_rotation.txt")],
+    lambda: [pins.test_sign_condition(r) for r in pins._golden.load("sign_condition.txt")],
+    pins.test_orthogonal_and_non_expansive,
+]
+
+
+def _build_mutant(src, tmp):
+    path = os.path.join(tmp, "mut.c")
+    with open(path, "w") as f:
+        f.write(src)
+    so = os.path.join(tmp, "libmut.so")
+    subprocess.check_call(["gcc", "-O1", "-std=c99", "-shared", "-fPIC", "-pthread", path,
+                           "-o", so])
+    return so
+
+
+def _pins_fail():
+    for t in PIN_TESTS:
+        try:
+            with np.errstate(all="ignore"):
+                t()
+        except (AssertionError, ValueError, np.linalg.LinAlgError):
+            return True
+    return False
+
+
+@pytest.mark.parametrize("name,pat,rep", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(name, pat, rep, monkeypatch):
+    src = open(SRC).read()
+    mutated, n = re.subn(pat, rep, src)
+    assert n >= 1, "mutation pattern no longer matches the oracle source"
+    with tempfile.TemporaryDirectory() as tmp:
+        so = _build_mutant(mutated, tmp)
+        monkeypatch.setattr(oracle, "_LIB_PATH", so)
+        monkeypatch.setattr(oracle, "_lib", None)
+        assert _pins_fail(), f"no pin caught the planted mistake: {name}"
+    monkeypatch.setattr(oracle, "_lib", None)
+
+
+def test_unmutated_oracle_passes_pins():
+    assert not _pins_fail()
