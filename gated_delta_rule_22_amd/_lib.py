@@ -1,0 +1,146 @@
+"""ctypes binding of ``libckda.so`` (declared in ``include/ckda.h``).
+
+Argument marshalling only: shapes and dtypes are read from torch tensors,
+outputs and the workspace are allocated with torch (device memory), and the
+current HIP stream is passed through.  Every step of the computation runs in
+the library's kernels.  There is no fallback: if the library is missing or a
+call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libckda.so")
+
+CKDA_BF16 = 0
+CKDA_F32 = 1
+
+_lib = None
+
+
+class CkdaError(RuntimeError):
+    pass
+
+
+def library() -> ctypes.CDLL:
+    """Load ``libckda.so`` once and declare its signatures."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise CkdaError(f"{LIB_PATH} is not built; run `python -m gated_delta_rule_22_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, ci, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        lib.ckda_abi_version.argtypes = []
+        lib.ckda_abi_version.restype = ci
+        lib.ckda_status_string.argtypes = [ci]
+        lib.ckda_status_string.restype = ctypes.c_char_p
+        lib.ckda_forward_workspace_bytes.argtypes = [ci] * 7
+        lib.ckda_forward_workspace_bytes.restype = sz
+        lib.ckda_forward.argtypes = [vp] * 7 + [ci] * 7 + [vp, vp, vp, sz, vp]
+        lib.ckda_forward.restype = ci
+        lib.ckda_decode_step.argtypes = [vp] * 7 + [ci] * 5 + [vp]
+        lib.ckda_decode_step.restype = ci
+        _lib = lib
+    return _lib
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return CKDA_BF16
+    if t.dtype == torch.float32:
+        return CKDA_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        msg = library().ckda_status_string(status).decode()
+        raise CkdaError(f"{what} failed with status {status}: {msg}")
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def forward_workspace_bytes(B, T, H, dk, dv, N, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else (CKDA_BF16 if dtype == torch.bfloat16 else CKDA_F32)
+    return int(library().ckda_forward_workspace_bytes(B, T, H, dk, dv, N, code))
+
+
+def _need(t, name, dtype=None, shape=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def forward(q, k, v, g, beta, S0=None, cu_seqlens=None, *, out=None, final_state=None,
+            workspace=None, output_final_state=True):
+    """CKDA chunkwise forward.  Returns ``(o, S_T)`` (``S_T`` is None when
+    ``output_final_state`` is False).  See ``ckda_forward`` in include/ckda.h
+    for shapes; ``final_state`` may be ``S0`` itself to advance it in place."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    code = _dtype_code(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype)
+    _need(k, "k", shape=(B, T, H, dk))
+    _need(v, "v", shape=(B, T, H, dv))
+    _need(g, "g", torch.float32, (B, T, H, dk))
+    _need(beta, "beta", torch.float32, (B, T, H))
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32)
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    if S0 is not None:
+        _need(S0, "S0", torch.float32, (N, H, dk, dv))
+    dev = q.device
+    o = out if out is not None else torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    _need(o, "out", torch.float32, (B, T, H, dv))
+    S_T = None
+    if output_final_state:
+        S_T = final_state if final_state is not None else torch.empty(
+            (N, H, dk, dv), dtype=torch.float32, device=dev)
+        _need(S_T, "final_state", torch.float32, (N, H, dk, dv))
+    ws_bytes = forward_workspace_bytes(B, T, H, dk, dv, N, code)
+    if workspace is None or workspace.numel() * workspace.element_size() < ws_bytes:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    st = library().ckda_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0),
+                                _ptr(cu_seqlens), B, T, H, dk, dv, N, code, _ptr(o), _ptr(S_T),
+                                _ptr(workspace), ws_bytes, _stream(dev))
+    _check(st, "ckda_forward")
+    return o, S_T
+
+
+def decode_step(q, k, v, g, beta, S, *, out=None):
+    """One decode step; ``S`` ([N, H, dk, dv] fp32) is updated in place.
+    Returns o ``[N, H, dv]`` fp32."""
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    code = _dtype_code(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype)
+    _need(k, "k", shape=(N, H, dk))
+    _need(v, "v", shape=(N, H, dv))
+    _need(g, "g", torch.float32, (N, H, dk))
+    _need(beta, "beta", torch.float32, (N, H))
+    _need(S, "S", torch.float32, (N, H, dk, dv))
+    o = out if out is not None else torch.empty((N, H, dv), dtype=torch.float32, device=q.device)
+    _need(o, "out", torch.float32, (N, H, dv))
+    st = library().ckda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S),
+                                    _ptr(o), N, H, dk, dv, code, _stream(q.device))
+    _check(st, "ckda_decode_step")
+    return o

@@ -1,0 +1,154 @@
+// C-ABI entry points: argument validation, workspace layout, dispatch.
+// Every check runs on the host before anything is enqueued, and touches no
+// HIP API, so an invalid call has no side effect.
+#include <string.h>
+
+#include "ckda_internal.h"
+
+namespace ckda {
+
+size_t f64_record_bytes(int dk, int dv);   // fwd_f64.hip
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+FwdLayout fwd_layout(int B, int T, int H, int dk, int dv, int N, int in_dtype) {
+  FwdLayout L{};
+  L.table_bytes = align256(sizeof(int32_t) * (3 * (size_t)N + 1 + (size_t)N));
+  // chunks over all sequences: uniform rows give B * ceil(T / C); packed
+  // sequences add at most one partial chunk each.
+  const size_t per_row = ((size_t)T + kChunk - 1) / kChunk;
+  L.n_chunks_ub = (N == B && B > 1) ? (size_t)B * per_row : per_row + (size_t)N;
+  (void)in_dtype;
+  L.rec_bytes = f64_record_bytes(dk, dv);
+  L.total = L.table_bytes + L.n_chunks_ub * (size_t)H * L.rec_bytes;
+  return L;
+}
+
+SeqTable seq_table(void *workspace, int N) {
+  int32_t *base = static_cast<int32_t *>(workspace);
+  SeqTable t;
+  t.seq_start = base;
+  t.seq_len = base + N;
+  t.chunk_off = base + 2 * (size_t)N;
+  t.order = base + 3 * (size_t)N + 1;
+  return t;
+}
+
+}  // namespace ckda
+
+using namespace ckda;
+
+namespace {
+
+bool dims_ok(int d) { return d == 64 || d == 128; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+int forward_shape_status(int B, int T, int H, int dk, int dv, int N, int in_dtype,
+                         bool packed) {
+  if (in_dtype != CKDA_BF16 && in_dtype != CKDA_F32) return CKDA_ERR_DTYPE;
+  if (B < 1 || T < 0 || H < 1 || N < 1 || !dims_ok(dk) || !dims_ok(dv)) return CKDA_ERR_SHAPE;
+  if ((long long)B * T * H >= (1LL << 31)) return CKDA_ERR_SHAPE;
+  if ((long long)N * H >= (1LL << 31)) return CKDA_ERR_SHAPE;
+  if (packed ? B != 1 : N != B) return CKDA_ERR_SHAPE;
+  return CKDA_OK;
+}
+
+}  // namespace
+
+extern "C" int ckda_abi_version(void) { return 1; }
+
+extern "C" const char *ckda_status_string(int status) {
+  switch (status) {
+    case CKDA_OK: return "ok";
+    case CKDA_ERR_NULL: return "a required pointer is NULL";
+    case CKDA_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case CKDA_ERR_DTYPE: return "unknown input dtype";
+    case CKDA_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
+    case CKDA_ERR_WORKSPACE: return "workspace missing or too small";
+    case CKDA_ERR_LAUNCH: return "kernel launch failed";
+    case CKDA_ERR_ALIAS: return "an output overlaps an input it may not alias";
+    default: return "unknown status";
+  }
+}
+
+extern "C" size_t ckda_forward_workspace_bytes(int B, int T, int H, int dk, int dv, int N,
+                                               int in_dtype) {
+  // The layout does not depend on packing; accept either form of N.
+  if (forward_shape_status(B, T, H, dk, dv, N, in_dtype, B == 1 && N != B) != CKDA_OK)
+    return 0;
+  return fwd_layout(B, T, H, dk, dv, N, in_dtype).total;
+}
+
+extern "C" int ckda_forward(const void *q, const void *k, const void *v, const float *g,
+                            const float *beta, const float *S0, const int32_t *cu_seqlens,
+                            int B, int T, int H, int dk, int dv, int N, int in_dtype, float *o,
+                            float *S_T, void *workspace, size_t workspace_bytes, void *stream) {
+  const bool packed = cu_seqlens != nullptr;
+  if (int s = forward_shape_status(B, T, H, dk, dv, N, in_dtype, packed)) return s;
+  const size_t rows = (size_t)B * T * H;
+  if (rows > 0 && (!q || !k || !v || !g || !beta || !o)) return CKDA_ERR_NULL;
+  const void *ptrs[] = {q, k, v, g, beta, S0, cu_seqlens, o, S_T, workspace};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return CKDA_ERR_ALIGN;
+
+  const size_t in_sz = in_dtype == CKDA_BF16 ? 2 : 4;
+  const size_t st_bytes = (size_t)N * H * dk * dv * 4;
+  const size_t o_bytes = rows * dv * 4;
+  struct Span { const void *p; size_t n; };
+  const Span ins[] = {{q, rows * dk * in_sz}, {k, rows * dk * in_sz}, {v, rows * dv * in_sz},
+                      {g, rows * dk * 4},      {beta, rows * 4},       {cu_seqlens, ((size_t)N + 1) * 4}};
+  for (const Span &s : ins) {
+    if (overlaps(o, o_bytes, s.p, s.n)) return CKDA_ERR_ALIAS;
+    if (overlaps(S_T, st_bytes, s.p, s.n)) return CKDA_ERR_ALIAS;
+  }
+  if (overlaps(o, o_bytes, S0, st_bytes) || overlaps(o, o_bytes, S_T, st_bytes))
+    return CKDA_ERR_ALIAS;
+  if (S_T != S0 && overlaps(S_T, st_bytes, S0, st_bytes)) return CKDA_ERR_ALIAS;
+
+  const FwdLayout L = fwd_layout(B, T, H, dk, dv, N, in_dtype);
+  if (!workspace || workspace_bytes < L.total) return CKDA_ERR_WORKSPACE;
+  if (overlaps(workspace, L.total, o, o_bytes) || overlaps(workspace, L.total, S_T, st_bytes) ||
+      overlaps(workspace, L.total, S0, st_bytes))
+    return CKDA_ERR_ALIAS;
+  for (const Span &s : ins)
+    if (overlaps(workspace, L.total, s.p, s.n)) return CKDA_ERR_ALIAS;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const SeqTable tab = seq_table(workspace, N);
+  if (launch_seq_table(cu_seqlens, B, T, N, tab, st) != hipSuccess) return CKDA_ERR_LAUNCH;
+  void *records = static_cast<char *>(workspace) + L.table_bytes;
+  hipError_t e = launch_fwd_f64(q, k, v, g, beta, S0, B * T, H, dk, dv, N, in_dtype, tab,
+                                L.n_chunks_ub, records, L.rec_bytes, o, S_T, st);
+  return e == hipSuccess ? CKDA_OK : CKDA_ERR_LAUNCH;
+}
+
+extern "C" int ckda_decode_step(const void *q, const void *k, const void *v, const float *g,
+                                const float *beta, float *S, float *o, int N, int H, int dk,
+                                int dv, int in_dtype, void *stream) {
+  if (in_dtype != CKDA_BF16 && in_dtype != CKDA_F32) return CKDA_ERR_DTYPE;
+  if (N < 1 || H < 1 || !dims_ok(dk) || !dims_ok(dv)) return CKDA_ERR_SHAPE;
+  if ((long long)N * H >= (1LL << 31)) return CKDA_ERR_SHAPE;
+  if (!q || !k || !v || !g || !beta || !S || !o) return CKDA_ERR_NULL;
+  const void *ptrs[] = {q, k, v, g, beta, S, o};
+  for (const void *p : ptrs)
+    if (!aligned16(p)) return CKDA_ERR_ALIGN;
+  const size_t nh = (size_t)N * H;
+  const size_t in_sz = in_dtype == CKDA_BF16 ? 2 : 4;
+  const size_t s_bytes = nh * dk * dv * 4, o_bytes = nh * dv * 4;
+  struct Span { const void *p; size_t n; };
+  const Span ins[] = {{q, nh * dk * in_sz}, {k, nh * dk * in_sz}, {v, nh * dv * in_sz},
+                      {g, nh * dk * 4},     {beta, nh * 4}};
+  if (overlaps(o, o_bytes, S, s_bytes)) return CKDA_ERR_ALIAS;
+  for (const Span &s : ins)
+    if (overlaps(S, s_bytes, s.p, s.n) || overlaps(o, o_bytes, s.p, s.n)) return CKDA_ERR_ALIAS;
+  hipError_t e = launch_decode(q, k, v, g, beta, S, o, N, H, dk, dv, in_dtype,
+                               static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? CKDA_OK : CKDA_ERR_LAUNCH;
+}

@@ -1,0 +1,56 @@
+// Internal declarations shared by the host entry points and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_bf16.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ckda.h"
+
+namespace ckda {
+
+constexpr int kChunk = 64;          // tokens per chunk of the chunkwise forward
+
+// ---------------------------------------------------------------- input loads
+// q, k, v arrive as bf16 or fp32; both widen exactly to fp32 (and fp64).
+__device__ __forceinline__ float to_f32(__hip_bfloat16 x) { return __bfloat162float(x); }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+
+// ---------------------------------------------------------------- schedule
+// Per-call sequence table, computed on the device from cu_seqlens (or the
+// uniform B x T layout) into the workspace:
+//   seq_start[n], seq_len[n]  token offset and length of sequence n
+//   chunk_off[n]              first flat chunk index of sequence n (N+1 entries)
+//   order[r]                  sequence index of rank r, longest first
+struct SeqTable {
+    int32_t *seq_start;
+    int32_t *seq_len;
+    int32_t *chunk_off;
+    int32_t *order;
+};
+
+// Workspace layout for a forward call (host-side arithmetic only).
+struct FwdLayout {
+    size_t table_bytes;      // the SeqTable arrays, 256-byte aligned
+    size_t rec_bytes;        // fp64 path: bytes of one (chunk, head) record
+    size_t n_chunks_ub;      // upper bound of chunks over all sequences
+    size_t total;            // total workspace bytes
+};
+FwdLayout fwd_layout(int B, int T, int H, int dk, int dv, int N, int in_dtype);
+SeqTable seq_table(void *workspace, int N);
+
+hipError_t launch_seq_table(const int32_t *cu_seqlens, int B, int T, int N, SeqTable tab,
+                            hipStream_t stream);
+
+hipError_t launch_decode(const void *q, const void *k, const void *v, const float *g,
+                         const float *beta, float *S, float *o, int N, int H, int dk, int dv,
+                         int in_dtype, hipStream_t stream);
+
+// fp64 chunkwise forward (fp32 inputs).
+hipError_t launch_fwd_f64(const void *q, const void *k, const void *v, const float *g,
+                          const float *beta, const float *S0, int T_rows, int H, int dk, int dv,
+                          int N, int in_dtype, SeqTable tab, size_t n_chunks_ub, void *records,
+                          size_t rec_bytes, float *o, float *S_T, hipStream_t stream);
+
+}  // namespace ckda

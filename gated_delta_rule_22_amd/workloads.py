@@ -67,14 +67,16 @@ def round_bf16(x) -> np.ndarray:
     """Round to fp32, then to bf16 (round to nearest, ties to even); return
     the bf16 values as an fp32 array.  Inputs here are finite."""
     f = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
-    bits = f.view(np.uint32).astype(np.uint64)
-    bias = np.uint64(0x7FFF) + ((bits >> np.uint64(16)) & np.uint64(1))
-    out = ((bits + bias) & np.uint64(0xFFFF0000)).astype(np.uint32)
+    bits = f.view(np.uint32)
+    # finite inputs: bits + 0x8000 stays below 2^32, so uint32 cannot wrap
+    out = bits + (np.uint32(0x7FFF) + ((bits >> np.uint32(16)) & np.uint32(1)))
+    out &= np.uint32(0xFFFF0000)
     return out.view(np.float32).reshape(f.shape)
 
 
 def _normalise(x):
-    return x / np.linalg.norm(x, axis=-1, keepdims=True)
+    x /= np.sqrt(np.einsum("...i,...i->...", x, x))[..., None]
+    return x
 
 
 def _cast_qkv(x, dtype):
@@ -187,3 +189,12 @@ def scaled(w: Workload | str, **changes) -> Workload:
     from dataclasses import replace
     w = WORKLOADS[w] if isinstance(w, str) else w
     return replace(w, **changes)
+
+
+def decode_steps(w: Workload | str, steps, seed: int = 0, workers: int = 8):
+    """Inputs of several decode steps, drawn in parallel threads (each step
+    has its own stream, so the result does not depend on ``workers``)."""
+    from concurrent.futures import ThreadPoolExecutor
+    steps = list(steps)
+    with ThreadPoolExecutor(max_workers=max(1, workers)) as ex:
+        return list(ex.map(lambda s: decode_step_inputs(w, s, seed), steps))

@@ -1,0 +1,143 @@
+/*
+ * ckda.h -- C ABI of the Complex KDA (CKDA) recurrence library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The recurrence (update rule: blog post "One update, one quarter turn",
+ * section "ELI5: the whiteboard, the mirror, and the clock", paragraph "The
+ * mirror"; gate ranges: "Complex KDA" AI summary, section "What This Paper Is
+ * About", and the authors' abstract):
+ *
+ *   S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *   o_t = S_t^T q_t                       (read after token t's write)
+ *
+ * S is a dk x dv matrix per (sequence, head); alpha_t is a per-key-channel
+ * signed gate (nominally in [-1, 1]) and beta_t a per-token scalar (nominally
+ * in [0, 2]).  Values outside those ranges are accepted and computed by the
+ * same formulas; beta > 2 is a legitimate setting (the summary's Theorem 5).
+ *
+ * Conventions shared by every entry point
+ *  - All pointers except `workspace` bookkeeping are DEVICE pointers in one
+ *    HIP device's memory, owned by the caller.  The library allocates no
+ *    memory, keeps no state between calls, and never synchronises: work is
+ *    enqueued on `stream` (a hipStream_t; NULL = the default stream) and the
+ *    call returns.  Device faults therefore surface at the caller's next
+ *    synchronisation.
+ *  - Tensors are dense, row-major (C order), with the shapes given below.
+ *    Every device pointer must be 16-byte aligned.
+ *  - Arguments are validated on the host before anything is enqueued; an
+ *    invalid call returns an error status and has no side effect.  The
+ *    contents of device buffers (e.g. cu_seqlens) are not inspected on the
+ *    host; out-of-range offsets are clamped by the kernels so that no access
+ *    leaves the buffers, but the results of such a call are unspecified.
+ *  - Calls that share no output buffer may run concurrently on different
+ *    streams.
+ */
+#ifndef CKDA_H
+#define CKDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+    CKDA_OK = 0,
+    CKDA_ERR_NULL = 1,       /* a required pointer is NULL */
+    CKDA_ERR_SHAPE = 2,      /* a size is out of range or inconsistent */
+    CKDA_ERR_DTYPE = 3,      /* unknown input dtype */
+    CKDA_ERR_ALIGN = 4,      /* a device pointer is not 16-byte aligned */
+    CKDA_ERR_WORKSPACE = 5,  /* workspace missing or smaller than required */
+    CKDA_ERR_LAUNCH = 6,     /* the HIP runtime refused a kernel launch */
+    CKDA_ERR_ALIAS = 7       /* an output overlaps an input it may not alias */
+};
+
+/* Input dtypes for q, k, v.  Gates, beta, states and outputs are fp32. */
+enum {
+    CKDA_BF16 = 0,           /* q, k, v are bfloat16 */
+    CKDA_F32 = 1             /* q, k, v are float32 */
+};
+
+/* Version of this ABI (bumped on any incompatible change). */
+int ckda_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char *ckda_status_string(int status);
+
+/*
+ * Workspace needed by ckda_forward for the same sizes and dtype, in bytes.
+ * Depends only on the sizes: a caller may size it once for the largest call.
+ * Returns 0 if the sizes are invalid (ckda_forward would return
+ * CKDA_ERR_SHAPE for them).
+ */
+size_t ckda_forward_workspace_bytes(int B, int T, int H, int dk, int dv, int N,
+                                    int in_dtype);
+
+/*
+ * Chunkwise-parallel CKDA forward over a batch of sequences.
+ *
+ * The token recurrence above, computed in chunks of 64 tokens with the
+ * WY/UT form of the delta rule and the signed-gate split the CKDA summary's
+ * methodology describes (sign kept apart from the log-space gate magnitude).
+ *
+ *  q, k        [B, T, H, dk]  in_dtype
+ *  v           [B, T, H, dv]  in_dtype
+ *  g           [B, T, H, dk]  fp32   the signed linear gate alpha (not a log)
+ *  beta        [B, T, H]      fp32
+ *  S0          [N, H, dk, dv] fp32   initial states, or NULL for zero states
+ *  cu_seqlens  NULL: N must equal B; sequence n is row n, T tokens long.
+ *              else: int32 [N+1] device array of token offsets into the
+ *              T axis (B must be 1): sequence n is tokens
+ *              [cu_seqlens[n], cu_seqlens[n+1]); 0 = cu[0] <= ... <= cu[N] = T.
+ *              Each sequence starts from its own S0[n] and chunks restart at
+ *              every sequence start.
+ *  B, T, H     B >= 1, T >= 0, H >= 1 (B*T*H < 2^31)
+ *  dk, dv      each 64 or 128
+ *  N           number of sequences (>= 1)
+ *  in_dtype    CKDA_BF16 or CKDA_F32
+ *  o           [B, T, H, dv]  fp32   output, every token written
+ *  S_T         [N, H, dk, dv] fp32   final states, or NULL to skip; may be
+ *              the same buffer as S0 (in-place state advance), must not
+ *              otherwise overlap an input
+ *  workspace   device scratch of at least ckda_forward_workspace_bytes(...)
+ *              bytes (may be NULL when that is 0); contents on entry are
+ *              ignored and on return are unspecified
+ *  stream      hipStream_t to enqueue on
+ *
+ * Numerics: bf16 inputs run every contraction on bf16 matrix cores with
+ * fp32 accumulation, splitting fp32 operands into two bf16 terms (hi + lo)
+ * so that products keep ~16 mantissa bits; states and intermediates stay
+ * fp32.  fp32 inputs are computed in fp64 and rounded to fp32 on output.
+ * Gate magnitudes below 2^-126 are treated as 2^-126 (fp32 inputs: 2^-1000).
+ */
+int ckda_forward(const void *q, const void *k, const void *v, const float *g,
+                 const float *beta, const float *S0, const int32_t *cu_seqlens,
+                 int B, int T, int H, int dk, int dv, int N, int in_dtype,
+                 float *o, float *S_T, void *workspace, size_t workspace_bytes,
+                 void *stream);
+
+/*
+ * One recurrent decode step for N*H independent states, in place.
+ *
+ *   S <- (I - beta k k^T) Diag(alpha) S + beta k v^T ;  o = S^T q
+ *
+ *  q, k        [N, H, dk]     in_dtype
+ *  v           [N, H, dv]     in_dtype
+ *  g           [N, H, dk]     fp32 signed gate alpha
+ *  beta        [N, H]         fp32
+ *  S           [N, H, dk, dv] fp32, read and overwritten with the new state
+ *  o           [N, H, dv]     fp32 output (must not overlap S)
+ *  N, H >= 1; dk, dv each 64 or 128; in_dtype CKDA_BF16 or CKDA_F32.
+ *
+ * Numerics: fp32 throughout (one step adds one rounding per state entry).
+ */
+int ckda_decode_step(const void *q, const void *k, const void *v, const float *g,
+                     const float *beta, float *S, float *o, int N, int H, int dk,
+                     int dv, int in_dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CKDA_H */

@@ -1,0 +1,84 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/ckda.h declares, and rejects invalid calls on the host
+with the documented status and no kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_22_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "ckda.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ckda_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert {"ckda_forward", "ckda_decode_step", "ckda_forward_workspace_bytes",
+            "ckda_abi_version", "ckda_status_string"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.ckda_abi_version() == 1
+    for s in range(8):
+        assert lib.ckda_status_string(s)
+    assert lib.ckda_status_string(0) == b"ok"
+
+
+def _fwd(lib, B=2, T=64, H=2, dk=128, dv=128, N=None, dtype=0, ptr=16, cu=None, ws=1 << 40,
+         S0=None, S_T=None, o=None):
+    N = B if N is None else N
+    p = ctypes.c_void_p(ptr) if ptr else None
+    o = ctypes.c_void_p(1 << 32) if (o is None and ptr) else o
+    return lib.ckda_forward(p, p, p, p, p, S0, cu, B, T, H, dk, dv, N, dtype, o, S_T,
+                            ctypes.c_void_p(1 << 20), ws, None)
+
+
+def test_forward_rejects_bad_arguments(lib):
+    # Pointers below are never dereferenced: every call fails validation first.
+    assert _fwd(lib, ptr=0) == 1                       # NULL inputs
+    assert _fwd(lib, dk=96) == 2                       # dk not 64/128
+    assert _fwd(lib, dv=32) == 2
+    assert _fwd(lib, H=0) == 2
+    assert _fwd(lib, B=0) == 2
+    assert _fwd(lib, N=3) == 2                         # N != B without cu_seqlens
+    assert _fwd(lib, B=2, cu=ctypes.c_void_p(4096), N=2) == 2   # packed needs B == 1
+    assert _fwd(lib, dtype=7) == 3
+    assert _fwd(lib, ptr=18) == 4                      # misaligned
+    assert _fwd(lib, ws=0) == 5                        # workspace too small
+    # o aliasing the inputs
+    assert _fwd(lib, ptr=1 << 24, o=ctypes.c_void_p(1 << 24)) == 7
+
+
+def test_workspace_bytes(lib):
+    ws = lib.ckda_forward_workspace_bytes
+    ws.restype = ctypes.c_size_t
+    assert ws(8, 4096, 16, 128, 128, 8, 0) > 0
+    assert ws(8, 4096, 16, 96, 128, 8, 0) == 0
+    assert ws(1, 65536, 16, 128, 128, 12, 0) > 0
+
+
+def test_decode_rejects_bad_arguments(lib):
+    p = ctypes.c_void_p(16)
+    f = lib.ckda_decode_step
+    assert f(None, p, p, p, p, p, p, 1, 1, 128, 128, 0, None) == 1
+    assert f(p, p, p, p, p, p, p, 1, 1, 100, 128, 0, None) == 2
+    assert f(p, p, p, p, p, p, p, 0, 1, 128, 128, 0, None) == 2
+    assert f(p, p, p, p, p, p, p, 1, 1, 128, 128, 2, None) == 3
+    q = ctypes.c_void_p(24)
+    assert f(q, p, p, p, p, ctypes.c_void_p(1 << 30), ctypes.c_void_p(1 << 31), 1, 1, 128, 128,
+             0, None) == 4

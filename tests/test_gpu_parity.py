@@ -1,0 +1,181 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle on
+the same seeded inputs.  Bound: max|x - ref| / rms(ref) <= 2e-3 for bf16
+inputs and <= 1e-5 for fp32 inputs, on the outputs o and the final states.
+
+Small cases compare every element and span several chunks with ragged tails;
+the full-size workloads run exactly as the benchmark launches them and are
+compared on sampled (sequence, head) pairs the oracle computes one by one."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import gated_delta_rule_22_amd as ck
+from gated_delta_rule_22_amd import workloads as wl
+from tests._gpu import TOL, gpu_forward, rel_err, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _rand_forward(seed, B, T, H, dk, dv, dtype, cu=None, s0=True, gate="signed"):
+    rng = np.random.default_rng(seed)
+    N = len(cu) - 1 if cu is not None else B
+    q = rng.normal(size=(B, T, H, dk))
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k = rng.normal(size=(B, T, H, dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.normal(size=(B, T, H, dv))
+    if gate == "signed":
+        g = rng.uniform(0.05, 1, size=(B, T, H, dk)) * np.where(rng.random((B, T, H, dk)) < 0.4, -1, 1)
+    else:
+        g = np.where(rng.random((B, T, H, dk)) < 0.5, -1.0, 1.0)
+    beta = rng.uniform(0, 2, size=(B, T, H))
+    S0 = rng.normal(size=(N, H, dk, dv)) / np.sqrt(dk * dv) if s0 else None
+    cast = wl.round_bf16 if dtype == "bf16" else (lambda a: a.astype(np.float32))
+    return dict(q=cast(q), k=cast(k), v=cast(v), g=g.astype(np.float32),
+                beta=beta.astype(np.float32), S0=None if S0 is None else S0.astype(np.float32),
+                cu_seqlens=None if cu is None else np.asarray(cu, np.int32), dtype=dtype)
+
+
+def _check_full(x, tag):
+    o, S = gpu_forward(x, tag)
+    o_ref, S_ref = oracle.forward(x["q"], x["k"], x["v"], x["g"], x["beta"], S0=x["S0"],
+                                  cu_seqlens=x["cu_seqlens"])
+    eo, es = rel_err(o, o_ref), rel_err(S, S_ref)
+    say(f"  err(o)={eo:.3e} err(S_T)={es:.3e} tol={TOL[x['dtype']]}")
+    assert eo <= TOL[x["dtype"]]
+    assert es <= TOL[x["dtype"]]
+    return eo, es
+
+
+# ---------------------------------------------------------------- decode
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64), (128, 128)])
+def test_decode_small(dtype, dk, dv):
+    rng = np.random.default_rng(7)
+    N, H, steps = 3, 5, 6
+    S = (rng.normal(size=(N, H, dk, dv)) / np.sqrt(dk * dv)).astype(np.float32)
+    S_ref = S.astype(np.float64)
+    S_dev = to_dev(S)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    cast = wl.round_bf16 if dtype == "bf16" else (lambda a: a.astype(np.float32))
+    worst = 0.0
+    for step in range(steps):
+        q = cast(rng.normal(size=(N, H, dk)) / np.sqrt(dk))
+        k = cast(rng.normal(size=(N, H, dk)) / np.sqrt(dk))
+        v = cast(rng.normal(size=(N, H, dv)))
+        g = rng.uniform(-1, 1, size=(N, H, dk)).astype(np.float32)
+        b = rng.uniform(0, 2.5, size=(N, H)).astype(np.float32)
+        say(f"[gpu] ckda_decode_step {dtype} dk={dk} dv={dv} step={step}")
+        o = ck.decode_step(to_dev(q, dt), to_dev(k, dt), to_dev(v, dt), to_dev(g), to_dev(b), S_dev)
+        o_ref = oracle.decode_step(q, k, v, g, b, S_ref)
+        worst = max(worst, rel_err(o.cpu().numpy(), o_ref))
+    es = rel_err(S_dev.cpu().numpy(), S_ref)
+    say(f"  err(o)={worst:.3e} err(S)={es:.3e}")
+    # fp32 arithmetic in the kernel for both input dtypes
+    assert worst <= 1e-5 and es <= 1e-5
+
+
+def test_decode_full_size_sampled():
+    """The 256 x 16-head decode workload, all 1024 steps on the GPU exactly as
+    the benchmark runs them; the oracle follows 48 sampled heads through every
+    step (o at every step, S at the end)."""
+    w = wl.WORKLOADS["decode_256x16"]
+    NH = w.B * w.H
+    heads = np.sort(np.random.default_rng(11).choice(NH, 48, replace=False))
+    S0 = wl.decode_state(w)
+    S_dev = to_dev(S0)
+    S_ref = S0.reshape(NH, 1, w.dk, w.dv)[heads].astype(np.float64).copy()
+    o_gpu, o_ref = [], []
+    block = 64
+    for s0 in range(0, w.steps, block):
+        xs = wl.decode_steps(w, range(s0, min(s0 + block, w.steps)))
+        say(f"[gpu] ckda_decode_step decode_256x16 steps {s0}..{s0 + len(xs) - 1}")
+        for x in xs:
+            o = ck.decode_step(to_dev(x["q"], torch.bfloat16), to_dev(x["k"], torch.bfloat16),
+                               to_dev(x["v"], torch.bfloat16), to_dev(x["g"]), to_dev(x["beta"]),
+                               S_dev)
+            o_gpu.append(o.reshape(NH, w.dv)[torch.from_numpy(heads).cuda()].cpu().numpy())
+            sub = {kk: a.reshape(NH, 1, *a.shape[2:])[heads] for kk, a in x.items()}
+            o_ref.append(oracle.decode_step(sub["q"], sub["k"], sub["v"], sub["g"],
+                                            sub["beta"], S_ref)[:, 0])
+    eo = rel_err(np.stack(o_gpu), np.stack(o_ref))
+    es = rel_err(S_dev.cpu().numpy().reshape(NH, w.dk, w.dv)[heads], S_ref[:, 0])
+    say(f"  err(o)={eo:.3e} err(S)={es:.3e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------- forward, full compare
+
+def test_forward_tiny_f32():
+    _check_full(wl.forward_inputs("tiny_f32"), "tiny_f32")
+
+
+def test_forward_rotation_f32():
+    _check_full(wl.forward_inputs("rotation_f32"), "rotation_f32")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64), (128, 128)])
+def test_forward_uniform_ragged(dtype, dk, dv):
+    """Several chunks and a ragged tail (T = 150 = 2 * 64 + 22)."""
+    _check_full(_rand_forward(3, B=3, T=150, H=2, dk=dk, dv=dv, dtype=dtype),
+                f"uniform {dk}x{dv}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_forward_packed_edge_lengths(dtype):
+    """Packed sequences of lengths 1, 63, 64, 65, 0 (empty), 130 and 200."""
+    lens = [1, 63, 64, 65, 0, 130, 200]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    x = _rand_forward(5, B=1, T=int(cu[-1]), H=3, dk=128, dv=128, dtype=dtype, cu=cu)
+    _check_full(x, "packed edges")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_forward_rotation_gates_long(dtype):
+    """Orthogonal transitions (alpha = +-1, beta = 2) over 1000 tokens:
+    errors are not damped by decay."""
+    x = _rand_forward(9, B=2, T=1000, H=2, dk=128, dv=128, dtype=dtype, gate="rotation")
+    x["beta"][:] = 2.0
+    _check_full(x, "rotation gates")
+
+
+# ---------------------------------------------------------------- forward, full size, sampled
+
+def _check_sampled(x, pairs, tag):
+    """Run the whole workload on the GPU; check the (row/sequence, head) pairs
+    in ``pairs`` against the oracle run on just those heads."""
+    o, S = gpu_forward(x, tag)
+    cu = x["cu_seqlens"]
+    heads = sorted({h for _, h in pairs})
+    sub = {key: x[key][:, :, heads] for key in ("q", "k", "v", "g", "beta")}
+    S0 = None if x["S0"] is None else x["S0"][:, heads]
+    if cu is None:
+        rows = sorted({r for r, _ in pairs})
+        sub = {key: a[rows] for key, a in sub.items()}
+        S0 = None if S0 is None else S0[rows]
+        say(f"  oracle on rows {rows} heads {heads}")
+        o_ref, S_ref = oracle.forward(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], S0=S0)
+        o_g = o[rows][:, :, heads]
+        S_g = S[rows][:, heads]
+    else:
+        say(f"  oracle on all sequences, heads {heads}")
+        o_ref, S_ref = oracle.forward(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], S0=S0,
+                                      cu_seqlens=cu)
+        o_g = o[:, :, heads]
+        S_g = S[:, heads]
+    eo, es = rel_err(o_g, o_ref), rel_err(S_g, S_ref)
+    say(f"  err(o)={eo:.3e} err(S_T)={es:.3e} tol={TOL[x['dtype']]}")
+    assert eo <= TOL[x["dtype"]] and es <= TOL[x["dtype"]]
+
+
+def test_forward_layer_1p3b_sampled():
+    x = wl.forward_inputs("layer_1p3b_bf16")
+    _check_sampled(x, [(0, 0), (3, 7), (7, 15), (5, 2)], "layer_1p3b_bf16")
+
+
+def test_forward_varlen_64k_sampled():
+    x = wl.forward_inputs("varlen_64k_bf16")
+    _check_sampled(x, [(0, 5)], "varlen_64k_bf16")
