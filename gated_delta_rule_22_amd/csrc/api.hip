@@ -43,6 +43,7 @@ namespace {
 bool dims_ok(int d) { return d == 64 || d == 128; }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
   if (!a || !b || na == 0 || nb == 0) return false;
@@ -70,7 +71,7 @@ extern "C" const char *ckda_status_string(int status) {
     case CKDA_ERR_NULL: return "a required pointer is NULL";
     case CKDA_ERR_SHAPE: return "a size is out of range or inconsistent";
     case CKDA_ERR_DTYPE: return "unknown input dtype";
-    case CKDA_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
+    case CKDA_ERR_ALIGN: return "a device pointer is misaligned";
     case CKDA_ERR_WORKSPACE: return "workspace missing or too small";
     case CKDA_ERR_LAUNCH: return "kernel launch failed";
     case CKDA_ERR_ALIAS: return "an output overlaps an input it may not alias";
@@ -94,9 +95,10 @@ extern "C" int ckda_forward(const void *q, const void *k, const void *v, const f
   if (int s = forward_shape_status(B, T, H, dk, dv, N, in_dtype, packed)) return s;
   const size_t rows = (size_t)B * T * H;
   if (rows > 0 && (!q || !k || !v || !g || !beta || !o)) return CKDA_ERR_NULL;
-  const void *ptrs[] = {q, k, v, g, beta, S0, cu_seqlens, o, S_T, workspace};
+  const void *ptrs[] = {q, k, v, g, S0, o, S_T, workspace};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return CKDA_ERR_ALIGN;
+  if ((beta && !aligned4(beta)) || (cu_seqlens && !aligned4(cu_seqlens))) return CKDA_ERR_ALIGN;
 
   const size_t in_sz = in_dtype == CKDA_BF16 ? 2 : 4;
   const size_t st_bytes = (size_t)N * H * dk * dv * 4;
@@ -136,9 +138,10 @@ extern "C" int ckda_decode_step(const void *q, const void *k, const void *v, con
   if (N < 1 || H < 1 || !dims_ok(dk) || !dims_ok(dv)) return CKDA_ERR_SHAPE;
   if ((long long)N * H >= (1LL << 31)) return CKDA_ERR_SHAPE;
   if (!q || !k || !v || !g || !beta || !S || !o) return CKDA_ERR_NULL;
-  const void *ptrs[] = {q, k, v, g, beta, S, o};
+  const void *ptrs[] = {q, k, v, g, S, o};
   for (const void *p : ptrs)
     if (!aligned16(p)) return CKDA_ERR_ALIGN;
+  if (!aligned4(beta)) return CKDA_ERR_ALIGN;
   const size_t nh = (size_t)N * H;
   const size_t in_sz = in_dtype == CKDA_BF16 ? 2 : 4;
   const size_t s_bytes = nh * dk * dv * 4, o_bytes = nh * dv * 4;

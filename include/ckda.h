@@ -16,14 +16,15 @@
  * same formulas; beta > 2 is a legitimate setting (the summary's Theorem 5).
  *
  * Conventions shared by every entry point
- *  - All pointers except `workspace` bookkeeping are DEVICE pointers in one
- *    HIP device's memory, owned by the caller.  The library allocates no
+ *  - All pointers are DEVICE pointers in one HIP device's memory, owned by
+ *    the caller.  The library allocates no
  *    memory, keeps no state between calls, and never synchronises: work is
  *    enqueued on `stream` (a hipStream_t; NULL = the default stream) and the
  *    call returns.  Device faults therefore surface at the caller's next
  *    synchronisation.
  *  - Tensors are dense, row-major (C order), with the shapes given below.
- *    Every device pointer must be 16-byte aligned.
+ *    q, k, v, g, states, outputs and the workspace must be 16-byte aligned;
+ *    beta and cu_seqlens 4-byte aligned.
  *  - Arguments are validated on the host before anything is enqueued; an
  *    invalid call returns an error status and has no side effect.  The
  *    contents of device buffers (e.g. cu_seqlens) are not inspected on the
@@ -48,7 +49,7 @@ enum {
     CKDA_ERR_NULL = 1,       /* a required pointer is NULL */
     CKDA_ERR_SHAPE = 2,      /* a size is out of range or inconsistent */
     CKDA_ERR_DTYPE = 3,      /* unknown input dtype */
-    CKDA_ERR_ALIGN = 4,      /* a device pointer is not 16-byte aligned */
+    CKDA_ERR_ALIGN = 4,      /* a device pointer is misaligned (see conventions) */
     CKDA_ERR_WORKSPACE = 5,  /* workspace missing or smaller than required */
     CKDA_ERR_LAUNCH = 6,     /* the HIP runtime refused a kernel launch */
     CKDA_ERR_ALIAS = 7       /* an output overlaps an input it may not alias */

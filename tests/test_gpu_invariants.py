@@ -86,18 +86,20 @@ def test_deterministic(dtype):
 def test_quarter_turn_at_real_shape():
     """Blog "One update, one quarter turn": gate (-1, 1), beta = 2,
     k = (e1 + e2)/sqrt(2) turns rows 1-2 of the state by 90 degrees and fixes
-    the rest; v = 0, so after 4m tokens the state is back (fp32 inputs)."""
+    the rest; v = 0, so after 4m tokens the state is back (fp32 inputs).
+    beta k k^T is the same matrix for k = e1 + e2 and beta = 1, which fp32
+    holds exactly (sqrt(1/2) it does not), so the turn is exact here."""
     dk = dv = 128
     T = 4 * 33
     k = np.zeros((1, T, 1, dk), np.float32)
-    k[..., :2] = np.float32(np.sqrt(0.5))
+    k[..., :2] = 1.0
     g = np.ones((1, T, 1, dk), np.float32)
     g[..., 0] = -1.0
     rng = np.random.default_rng(3)
     S0 = rng.normal(size=(1, 1, dk, dv)).astype(np.float32)
     q = rng.normal(size=(1, T, 1, dk)).astype(np.float32)
     x = dict(q=q, k=k, v=np.zeros((1, T, 1, dv), np.float32), g=g,
-             beta=np.full((1, T, 1), 2.0, np.float32), S0=S0, cu_seqlens=None, dtype="f32")
+             beta=np.full((1, T, 1), 1.0, np.float32), S0=S0, cu_seqlens=None, dtype="f32")
     say("[gpu] quarter turn dk=128 T=132")
     o, S = _fwd(upload(x))
     S = S.cpu().numpy()[0, 0]
