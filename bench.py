@@ -1,0 +1,184 @@
+"""Benchmark of the CKDA hot path on one MI355X.
+
+One step = one chunkwise forward over the 1.3B-LM-shaped layer workload
+(B=8, T=4096, H=16, dk=dv=128, bf16 q/k/v, fp32 gates and state, chunk 64):
+32768 tokens.  The headline value is forward tokens/s.  The same run also
+times the recurrent decode workload (256 sequences x 16 heads, 1024
+consecutive in-place steps) and reports steps/s and HBM GB/s.
+
+Inputs are seeded synthetic draws (gated_delta_rule_22_amd.workloads), already
+resident in device memory when the timed region starts.  Timing uses HIP
+events on the stream the library launches on.  The CPU baseline is the fp64
+oracle (test infrastructure) on the same forward workload, on all host cores.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "CKDA fwd tokens/s (H=16,d=128,bf16) + %MFMA peak; decode steps/s + HBM GB/s"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix
+
+
+def fwd_algorithmic(w):
+    """Compulsory HBM bytes and dense chunked flops of one forward."""
+    th = w.B * w.T * w.H
+    in_sz = 2 if w.dtype == "bf16" else 4
+    per_th = in_sz * (2 * w.dk + w.dv) + 4 * w.dk + 4 + 4 * w.dv   # q,k,v + alpha + beta + o
+    state = w.B * w.H * w.dk * w.dv * 4                              # S_T written (S0 = 0)
+    if w.s0 != "zero":
+        state *= 2
+    C = w.chunk
+    flops = th * (2 * C * (3 * w.dk + 2 * w.dv) + 6 * w.dk * w.dv)
+    return th * per_th + state, flops, per_th
+
+
+def decode_algorithmic(w):
+    nh = w.B * w.H
+    per_head = 2 * w.dk * w.dv * 4 + 2 * (2 * w.dk + w.dv) + 4 * w.dk + 4 + 4 * w.dv
+    return nh * per_head, per_head
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=None,
+                    help="decode steps to time (default: the workload's 1024)")
+    ap.add_argument("--skip-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--skip-forward", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              "(heads and sequences shard across GPUs without exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_delta_rule_22_amd as ck
+    from gated_delta_rule_22_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ck.library()
+    out = {"metric": METRIC, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
+
+    # ------------------------------------------------------------- forward
+    w = wl.WORKLOADS["layer_1p3b_bf16"]
+    fwd_bytes, fwd_flops, per_th = fwd_algorithmic(w)
+    out["config"] = {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "dk": w.dk, "dv": w.dv,
+                     "chunk": w.chunk, "tokens_per_step": w.B * w.T, "qkv": "bf16",
+                     "gates_state_out": "fp32"}
+    x = wl.forward_inputs(w)
+    if not args.skip_forward:
+        print(f"[bench] forward {w.name}: uploading", file=sys.stderr, flush=True)
+        bf = lambda a: torch.from_numpy(a).to(dev).to(torch.bfloat16)
+        f32 = lambda a: torch.from_numpy(a).to(dev)
+        q, k, v, g, beta = bf(x["q"]), bf(x["k"]), bf(x["v"]), f32(x["g"]), f32(x["beta"])
+        o = torch.empty((w.B, w.T, w.H, w.dv), dtype=torch.float32, device=dev)
+        S_T = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(1, ck.forward_workspace_bytes(w.B, w.T, w.H, w.dk, w.dv, w.B,
+                                                           torch.bfloat16)),
+                         dtype=torch.uint8, device=dev)
+        run = lambda: ck.forward(q, k, v, g, beta, out=o, final_state=S_T, workspace=ws)
+        for _ in range(args.warmup):
+            run()
+        torch.cuda.synchronize()
+        print(f"[bench] forward: timing {args.steps} steps", file=sys.stderr, flush=True)
+        stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(args.steps):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = e0.elapsed_time(e1) / args.steps
+        out["ms_per_step"] = ms
+        out["value"] = w.B * w.T / (ms * 1e-3)
+        gbs = fwd_bytes / (ms * 1e-3) / 1e9
+        tflops = fwd_flops / (ms * 1e-3) / 1e12
+        out["roofline"] = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                           "kernel": "ckda forward (one launch per step for uniform batches)",
+                           "bytes_per_launch": fwd_bytes, "bytes_per_token_head": per_th}
+        out["mfma"] = {"algorithmic_tflops": tflops, "peak_tflops": BF16_PEAK_TFLOPS,
+                       "frac": tflops / BF16_PEAK_TFLOPS, "flops_per_step": fwd_flops}
+        out["wall_s_timed"] = wall
+        del q, k, v, g, beta, o, S_T, ws
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------- decode
+    if not args.skip_decode:
+        wd = wl.WORKLOADS["decode_256x16"]
+        steps = args.decode_steps or wd.steps
+        print(f"[bench] decode {wd.name}: drawing {steps} steps", file=sys.stderr, flush=True)
+        xs = wl.decode_steps(wd, range(steps), workers=min(16, os.cpu_count() or 1))
+        bf = lambda a: torch.from_numpy(a).to(dev).to(torch.bfloat16)
+        f32 = lambda a: torch.from_numpy(a).to(dev)
+        dq = torch.stack([bf(s["q"]) for s in xs])
+        dk_ = torch.stack([bf(s["k"]) for s in xs])
+        dv_ = torch.stack([bf(s["v"]) for s in xs])
+        dg = torch.stack([f32(s["g"]) for s in xs])
+        db = torch.stack([f32(s["beta"]) for s in xs])
+        del xs
+        S = torch.from_numpy(wl.decode_state(wd)).to(dev)
+        do = torch.empty((steps, wd.B, wd.H, wd.dv), dtype=torch.float32, device=dev)
+        step = lambda i: ck.decode_step(dq[i], dk_[i], dv_[i], dg[i], db[i], S, out=do[i])
+        for i in range(min(3, steps)):          # warm-up (advances the state)
+            step(i)
+        torch.cuda.synchronize()
+        print(f"[bench] decode: timing {steps} steps", file=sys.stderr, flush=True)
+        stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            step(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_d = e0.elapsed_time(e1) / steps
+        dbytes, per_head = decode_algorithmic(wd)
+        dgbs = dbytes / (ms_d * 1e-3) / 1e9
+        out["decode"] = {"workload": wd.name, "steps": steps, "us_per_step": ms_d * 1e3,
+                         "steps_per_s": 1e3 / ms_d, "hbm_gbs": dgbs, "hbm_frac": dgbs / HBM_PEAK_GBS,
+                         "bytes_per_step": dbytes, "bytes_per_state": per_head}
+        if args.skip_forward:
+            out["roofline"] = {"bound": "hbm", "achieved": dgbs, "peak": HBM_PEAK_GBS,
+                               "unit": "GB/s", "frac": dgbs / HBM_PEAK_GBS, "traffic": None,
+                               "kernel": "decode step"}
+        del dq, dk_, dv_, dg, db, S, do
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------- CPU oracle baseline
+    if not args.skip_cpu:
+        import oracle
+        nth = oracle.default_threads()
+        print(f"[bench] cpu oracle on {nth} threads", file=sys.stderr, flush=True)
+        t0 = time.perf_counter()
+        oracle.forward(x["q"], x["k"], x["v"], x["g"], x["beta"], nthreads=nth)
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": w.B * w.T / dt, "unit": "tokens/s", "cores": nth,
+                               "kind": "oracle",
+                               "sample": f"the whole {w.name} forward (B={w.B}, T={w.T}, H={w.H}), "
+                                         f"fp64 token-by-token, {dt:.1f} s"}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -18,8 +18,8 @@ FwdLayout fwd_layout(int B, int T, int H, int dk, int dv, int N, int in_dtype) {
   // sequences add at most one partial chunk each.
   const size_t per_row = ((size_t)T + kChunk - 1) / kChunk;
   L.n_chunks_ub = (N == B && B > 1) ? (size_t)B * per_row : per_row + (size_t)N;
-  (void)in_dtype;
-  L.rec_bytes = f64_record_bytes(dk, dv);
+  // bf16 inputs run the fused kernel, which needs only the sequence table.
+  L.rec_bytes = in_dtype == CKDA_F32 ? f64_record_bytes(dk, dv) : 0;
   L.total = L.table_bytes + L.n_chunks_ub * (size_t)H * L.rec_bytes;
   return L;
 }
@@ -124,10 +124,18 @@ extern "C" int ckda_forward(const void *q, const void *k, const void *v, const f
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   const SeqTable tab = seq_table(workspace, N);
-  if (launch_seq_table(cu_seqlens, B, T, N, tab, st) != hipSuccess) return CKDA_ERR_LAUNCH;
-  void *records = static_cast<char *>(workspace) + L.table_bytes;
-  hipError_t e = launch_fwd_f64(q, k, v, g, beta, S0, B * T, H, dk, dv, N, in_dtype, tab,
-                                L.n_chunks_ub, records, L.rec_bytes, o, S_T, st);
+  hipError_t e;
+  if (in_dtype == CKDA_BF16) {
+    // Uniform rows need no table: the kernel derives each sequence from its row.
+    if (packed && launch_seq_table(cu_seqlens, B, T, N, tab, st) != hipSuccess)
+      return CKDA_ERR_LAUNCH;
+    e = launch_fwd_bf16(q, k, v, g, beta, S0, o, S_T, T, H, dk, dv, N, tab, packed ? 1 : 0, st);
+  } else {
+    if (launch_seq_table(cu_seqlens, B, T, N, tab, st) != hipSuccess) return CKDA_ERR_LAUNCH;
+    void *records = static_cast<char *>(workspace) + L.table_bytes;
+    e = launch_fwd_f64(q, k, v, g, beta, S0, B * T, H, dk, dv, N, in_dtype, tab, L.n_chunks_ub,
+                       records, L.rec_bytes, o, S_T, st);
+  }
   return e == hipSuccess ? CKDA_OK : CKDA_ERR_LAUNCH;
 }
 

@@ -53,4 +53,9 @@ hipError_t launch_fwd_f64(const void *q, const void *k, const void *v, const flo
                           int N, int in_dtype, SeqTable tab, size_t n_chunks_ub, void *records,
                           size_t rec_bytes, float *o, float *S_T, hipStream_t stream);
 
+// Fused bf16 chunkwise forward on matrix cores (bf16 inputs).
+hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, const float *g,
+                           const float *beta, const float *S0, float *o, float *S_T, int T, int H,
+                           int dk, int dv, int N, SeqTable tab, int packed, hipStream_t stream);
+
 }  // namespace ckda
