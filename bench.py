@@ -60,6 +60,9 @@ def main():
     ap.add_argument("--skip-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--skip-forward", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run one device-to-device copy of this many MiB (a reference "
+                         "kernel of known traffic for hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
@@ -164,6 +167,16 @@ def main():
                                "kernel": "decode step"}
         del dq, dk_, dv_, dg, db, S, do
         torch.cuda.empty_cache()
+
+    if args.copy_mib:
+        n = args.copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_reference_bytes"] = {"read": n * 4, "write": n * 4}
+        del src, dst
 
     # ------------------------------------------------------------- CPU oracle baseline
     if not args.skip_cpu:

@@ -1,167 +1,178 @@
 // Fused chunkwise CKDA forward for bf16 q/k/v on CDNA4 matrix cores.
 //
 // One workgroup owns one (sequence, head, 64-column block of dv) and walks the
-// sequence's chunks of C = 64 tokens in order, keeping its slice of the fp32
-// state (dk x 64) in MFMA accumulators for the whole sequence.  Each chunk is
-// read from HBM once (the dv blocks of one head share q/k/alpha through the
-// XCD's L2) and o is written once: the only HBM traffic is the compulsory one.
+// sequence's chunks of C = 64 tokens in order.  Its slice of the fp32 state
+// (dk x 64) lives in MFMA accumulators for the whole sequence; each chunk is
+// read from HBM once (the dv blocks of a head share q/k/alpha through the L2
+// of their XCD) and o is written once, so the HBM traffic is the compulsory one.
 //
 // Chunk algebra (update rule: blog post "One update, one quarter turn", ELI5
-// "The mirror", unrolled over a chunk with incoming state S; r_ij is the gate
-// product over tokens j < s <= i, gamma_i = r_i0):
-//   A_ij = beta_i sum_c k_ic r_ij,c k_jc (i > j)    T = (I + A)^-1
-//   X    = V - (gamma K) S                           U = T Diag(beta) X
-//   O    = (gamma Q) S + P U,   P_ij = sum_c q_ic r_ij,c k_jc (j <= i)
+// "The mirror", unrolled over a chunk with incoming state S; gamma_i is the
+// product of the gates of tokens 1..i of the chunk, per key channel):
+//   A_ij = beta_i sum_c (gamma_ic k_ic) (k_jc / gamma_jc)      (i > j)
+//   P_ij =        sum_c (gamma_ic q_ic) (k_jc / gamma_jc)      (j <= i)
+//   X    = V - (gamma K) S,   (I + A) U = Diag(beta) X
+//   O    = (gamma Q) S + P U
 //   S'   = Diag(gamma_n) S + (K gamma_n / gamma)^T U
 //
-// Signed gates (CKDA summary, "Methodology in Plain English": magnitudes live
-// in log space, the sign apart): per channel the chunk keeps the inclusive
-// cumulative sum G of log2|alpha| (fp32, each term clamped at -126) and the
-// cumulative parity pi of negative gates; every ratio is
-// (-1)^(pi_i ^ pi_j) 2^(G_i - G_j).
+// Signed gates (CKDA summary, "Methodology in Plain English": gate magnitudes
+// live in log space, so the sign is kept apart): per channel the chunk keeps
+// the inclusive cumulative sum G of log2|alpha| (fp32, each term clamped at
+// -126) and the cumulative parity pi of negative gates.  Only ratios of gammas
+// matter, so each channel is referenced to R = G_n / 2, the middle of its
+// range: gamma' = (-1)^pi 2^(G - R) and 1/gamma' = (-1)^pi 2^(R - G) both stay
+// within 2^+-100 while the chunk's log-gate range is below 200 (gates averaging
+// above 0.11 in magnitude), and A, P are one product each of gamma'-scaled
+// operands.  The state absorbs 2^R: with S_pre = 2^R S,
+//   X = V - (gamma' K) S_pre,  O = (gamma' Q) S_pre + P U,
+//   S' = (-1)^pi_n 2^(G_n - R) (S_pre + (K / gamma')^T U).
+// A chunk whose range is wider takes an exact element-wise path that only
+// forms 2^(G_i - G_j) <= 1.
 //
-// A and P on matrix cores without overflow: tokens form four 16-token blocks.
-// For a tile of row block I and column block J the row operand is scaled
-// relative to the end of block I-1 (factor <= 1), the column operand relative
-// to the end of block J (factor <= 1), and the per-channel bridge
-// 2^(G_end(I-1) - G_end(J)) is <= 1 for J < I.  On the diagonal the bridge is
-// >= 1; when any channel drops more than 2^100 inside a block, that block's
-// tiles are computed element by element from the raw gates instead.
+// Work split inside the workgroup (512 threads):
+//   waves 0-3  state pass, 16 dv columns each: X, O, U and the state update,
+//              all on matrix cores; wave 0 also inverts the diagonal blocks;
+//   waves 4-7  chunk preparation for the next chunk while the state pass runs:
+//              gate scan, gamma'-scaled operands and their hi/lo bf16 split;
+//              at the hand-off, A and P on matrix cores.
+// (I + A) U = Diag(beta) X is solved by block forward substitution over the
+// four 16-token blocks, so T = (I + A)^-1 is never formed.
 //
 // Precision: every contraction whose operands are not raw bf16 inputs splits
 // each fp32 operand x into hi = bf16(x) and lo = bf16(x - hi) and accumulates
-// hi*hi + hi*lo + lo*hi in fp32 (three MFMAs), which keeps ~16 mantissa bits;
-// T = (I + A)^-1 is formed in fp32 on the vector units (16 x 16 diagonal
-// blocks by forward substitution, then three levels of block products).
+// hi*hi + hi*lo + lo*hi in fp32 (three MFMAs), keeping ~16 mantissa bits.
 //
-// MFMA: v_mfma_f32_16x16x32_bf16 (A 16x32, B 32x16, C 16x16).  Lane l holds
-// A row l%16 / B column l%16 at k = 8(l/16) .. +7, and C rows 4(l/16) .. +3 of
-// column l%16.  An accumulator used as the next product's B operand supplies
-// rows {4g..4g+3, 16+4g..16+4g+3} of a 32-row k block (g = l/16); the matching
-// A operand is read from LDS with the same k order.
+// MFMA shapes (lane l, g = l / 16):
+//   16x16x32: A row l%16 / B column l%16 hold k = 8g .. 8g+7; C rows 4g..4g+3.
+//     An accumulator pair used as a B operand supplies k rows
+//     {4g..4g+3, 16+4g..16+4g+3}; the matching A operand is read in that order.
+//   16x16x16: A row / B column l%16 hold k = 4g .. 4g+3, the accumulator layout,
+//     so a 16-token accumulator is directly the next product's B operand.
 #include "ckda_internal.h"
 
 namespace ckda {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int C = kChunk;        // 64 tokens per chunk
-constexpr int NT = 256;          // threads per workgroup (4 waves)
-constexpr int BV = 64;           // dv columns per workgroup (16 per wave)
-constexpr int RTS = C + 1;       // row stride of the fp32 A/T buffer
+constexpr int NT = 512;          // 8 waves per workgroup
+constexpr int BV = 64;           // dv columns per workgroup (16 per state-pass wave)
+constexpr int PADB = 4;          // bf16 plane row padding (elements)
+constexpr int ADS = 17;          // row stride of the fp32 diagonal A tiles
 constexpr float kLog2Floor = -126.f;
-constexpr float kDiagGuard = 100.f;
+constexpr float kGuard = 100.f;  // |G - R| bound for the factored A and P
 
-__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-// acc += a*b with a = ah + al, b = bh + bl, dropping al*bl.
-__device__ __forceinline__ f32x4 mfma3(f32x4 c, bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl) {
-  c = mfma(al, bh, c);
-  c = mfma(ah, bl, c);
-  return mfma(ah, bh, c);
+__device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ void split8(const float (&x)[8], bf16x8 &h, bf16x8 &l) {
+// acc += a*b with a = ah + al, b = bh + bl (al*bl dropped).
+__device__ __forceinline__ f32x4 mfma32x3(f32x4 c, bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl) {
+  c = mfma32(al, bh, c);
+  c = mfma32(ah, bl, c);
+  return mfma32(ah, bh, c);
+}
+__device__ __forceinline__ f32x4 mfma16x3(f32x4 c, bf16x4 ah, bf16x4 al, bf16x4 bh, bf16x4 bl) {
+  c = mfma16(al, bh, c);
+  c = mfma16(ah, bl, c);
+  return mfma16(ah, bh, c);
+}
+__device__ __forceinline__ void split1(float x, __bf16 &h, __bf16 &l) {
+  h = (__bf16)x;
+  l = (__bf16)(x - (float)h);
+}
+__device__ __forceinline__ void split4(const f32x4 &x, bf16x4 &h, bf16x4 &l) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
+  for (int e = 0; e < 4; ++e) {
     const __bf16 b = (__bf16)x[e];
     h[e] = b;
     l[e] = (__bf16)(x[e] - (float)b);
   }
 }
-__device__ __forceinline__ float sgn(uint32_t odd) { return odd ? -1.f : 1.f; }
+// k-block fragment of two accumulator tiles (rows 0-15 and 16-31 of a 32-row block)
+__device__ __forceinline__ void split8_acc(const f32x4 &t0, const f32x4 &t1, bf16x8 &h,
+                                           bf16x8 &l) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const __bf16 b0 = (__bf16)t0[e], b1 = (__bf16)t1[e];
+    h[e] = b0;
+    h[e + 4] = b1;
+    l[e] = (__bf16)(t0[e] - (float)b0);
+    l[e + 4] = (__bf16)(t1[e] - (float)b1);
+  }
+}
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float flog2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float with_sign(float x, uint32_t odd) {
+  return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, x) ^ (odd << 31));
+}
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __builtin_bit_cast(float, bits16 << 16);
+}
 
 // ---------------------------------------------------------------- LDS layout
-// Rows are padded so that the fragment reads below are bank-conflict free
-// while every address stays (per-lane base) + (compile-time offset): fp32
-// [C][DK] regions by 16 bytes per row (16-byte reads of 8 consecutive rows hit
-// distinct banks), bf16 planes by 8 bytes per row (8-byte reads of 16
-// consecutive rows hit distinct banks).
-constexpr int PADF = 4;          // fp32 row padding, elements
-constexpr int PADB = 4;          // bf16 row padding, elements
-
+// bf16 hi/lo planes; rows padded by 8 bytes so the 8-byte fragment reads of 16
+// consecutive rows hit distinct banks while every address stays (per-lane base)
+// + (compile-time offset).
 template <int DK>
 struct Lds {
-  static constexpr int FR = C * (DK + PADF) * 4;          // fp32 [C][DK] region
-  static constexpr int BQ = 2 * C * (DK + PADB) * 2;      // hi+lo planes [C][DK]
-  static constexpr int BK = 2 * DK * (C + PADB) * 2;      // hi+lo planes [DK][C]
-  static constexpr int BC = 2 * C * (C + PADB) * 2;       // hi+lo planes [C][C]
+  static constexpr int PQ = 2 * C * (DK + PADB) * 2;      // hi+lo [C][DK]
+  static constexpr int PT = 2 * DK * (C + PADB) * 2;      // hi+lo [DK][C]
+  static constexpr int PC = 2 * C * (C + PADB) * 2;       // hi+lo [C][C]
   static constexpr int mx(int a, int b) { return a > b ? a : b; }
-  static constexpr int RA = 0;                            // Xk fp32 -> (-gamma K) planes
-  static constexpr int RB = RA + mx(FR, BQ);              // Xq fp32 -> gamma Q planes
-  static constexpr int RC = RB + mx(FR, BQ);              // Y fp32  -> K_hat^T planes
-  static constexpr int RT = RC + mx(FR, BK);              // A, then T (fp32, stride C+1)
-  static constexpr int RP = RT + C * RTS * 4;             // P fp32 [C][C] -> P planes
-  static constexpr int RTB = RP + mx(C * C * 4, BC);      // T Diag(beta) planes; gate totals
-  static constexpr int RZ = RTB + BC;                     // 3 x 16 x 16 fp32 scratch
-  static constexpr int GE = RZ + 3 * 256 * 4;             // G at block ends [4][DK] fp32
-  static constexpr int PE = GE + 4 * DK * 4;              // parity at block ends [4][DK] u8
-  static constexpr int GN = PE + 4 * DK;                  // gamma_n [DK] fp32
-  static constexpr int BT = GN + DK * 4;                  // beta [C] fp32
-  static constexpr int FL = BT + C * 4;                   // diagonal-guard flags, 2 ints
+  static constexpr int GK = 0;                            // -(gamma K)       [C][DK]
+  static constexpr int GQ = GK + PQ;                      // gamma Q          [C][DK]
+  static constexpr int KT = GQ + PQ;                      // (K/gamma)^T      [DK][C]
+  static constexpr int KG = KT + PT;                      // K/gamma [C][DK]; then P and AT
+  static constexpr int P = KG;                            // P                [C][C]
+  static constexpr int AT = P + PC;                       // -A below, T_II on the diagonal
+  static constexpr int FG = C * DK * 4;                   // exact path: G fp32 [C][DK]
+  static constexpr int KG_BYTES = mx(mx(PQ, 2 * PC), FG + DK * 8);
+  static constexpr int AD = KG + KG_BYTES;                // diagonal A tiles fp32 [4][16][17]
+  static constexpr int BT = AD + 4 * 16 * ADS * 4;        // beta [C]
+  static constexpr int SPRE = BT + C * 4;                 // S_pre = pre * S          [DK]
+  static constexpr int SMID = SPRE + DK * 4;              // S' = post * (mid * S_pre  [DK]
+  static constexpr int SPOST = SMID + DK * 4;             //      + (KT plane)^T U)    [DK]
+  static constexpr int FL = SPOST + DK * 4;               // guard flags (2 ints)
   static constexpr int SIZE = FL + 16;
   static_assert(SIZE <= 160 * 1024, "LDS budget");
 };
 
-// element offsets
-__device__ __forceinline__ int f32at(int row, int c, int DK) { return row * (DK + PADF) + c; }
-__device__ __forceinline__ int bfat(int row, int c, int W) { return row * (W + PADB) + c; }
+__device__ __forceinline__ int at(int row, int c, int W) { return row * (W + PADB) + c; }
 
-// A-operand fragment from a bf16 plane, k block kb, in the accumulator k order:
-// channels 32kb + 4g .. +3 then 32kb + 16 + 4g .. +3.
-__device__ __forceinline__ bf16x8 frag_acc_order(const __bf16 *plane, int W, int row, int kb,
-                                                 int g) {
-  const uint2 a = *reinterpret_cast<const uint2 *>(plane + bfat(row, 32 * kb + 4 * g, W));
-  const uint2 b = *reinterpret_cast<const uint2 *>(plane + bfat(row, 32 * kb + 16 + 4 * g, W));
-  uint4 u = {a.x, a.y, b.x, b.y};
+// 16x16x32 A-operand fragment in the accumulator k order (see header).
+__device__ __forceinline__ bf16x8 frag32(const __bf16 *plane, int W, int row, int kb, int g) {
+  const uint2 a = *reinterpret_cast<const uint2 *>(plane + at(row, 32 * kb + 4 * g, W));
+  const uint2 b = *reinterpret_cast<const uint2 *>(plane + at(row, 32 * kb + 16 + 4 * g, W));
+  const uint4 u = {a.x, a.y, b.x, b.y};
   return __builtin_bit_cast(bf16x8, u);
 }
-// B/C-fragment from two accumulator tiles (rows 0-15 and 16-31 of a k block).
-__device__ __forceinline__ void frag_from_acc(const f32x4 &t0, const f32x4 &t1, bf16x8 &h,
-                                              bf16x8 &l) {
-  const float x[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
-  split8(x, h, l);
+// 16x16x16 A-operand fragment: columns col0 + 4g .. +3 of `row`.
+__device__ __forceinline__ bf16x4 frag16(const __bf16 *plane, int W, int row, int col0, int g) {
+  return __builtin_bit_cast(bf16x4,
+                            *reinterpret_cast<const uint2 *>(plane + at(row, col0 + 4 * g, W)));
 }
 
 template <int DK>
-struct Geo {
-  static constexpr int CQ = DK / 4;     // channel quads
-  static constexpr int TG = NT / CQ;    // token groups
-  static constexpr int TPT = C / TG;    // tokens per thread in the gate phase
-  static_assert(TPT * TG == C && TPT % 4 == 0 && 16 % TPT == 0, "gate-phase geometry");
+struct Prep {                     // chunk-preparation lane geometry (one wave: DK/4 channels)
+  static constexpr int CQW = DK / 16;     // channel quads per wave
+  static constexpr int TGW = 64 / CQW;    // token groups per wave
+  static constexpr int TPL = C / TGW;     // tokens per lane
+  static_assert(TPL * TGW == C && TPL % 4 == 0, "preparation geometry");
 };
 
-// Elementwise A and P for one diagonal block (the rare fallback).
-template <int DK>
-__device__ void diag_block_elementwise(int I, const __hip_bfloat16 *q, const __hip_bfloat16 *k,
-                                       const float *g, const float *s_beta, size_t row0,
-                                       size_t rstride, int nt, float *s_A, float *s_P) {
-  for (int p = threadIdx.x; p < 256; p += NT) {
-    const int a = p >> 4, b = p & 15;
-    const int i = 16 * I + a, j = 16 * I + b;
-    float accA = 0.f, accP = 0.f;
-    if (b <= a && i < nt) {
-      const size_t ri = row0 + (size_t)i * rstride, rj = row0 + (size_t)j * rstride;
-      for (int c = 0; c < DK; ++c) {
-        float r = 1.f;
-        for (int s = j + 1; s <= i; ++s) {
-          const float al = g[(row0 + (size_t)s * rstride) * DK + c];
-          r *= copysignf(fmaxf(fabsf(al), 1.17549435e-38f), al);
-        }
-        const float kj = to_f32(k[rj * DK + c]) * r;
-        accA += to_f32(k[ri * DK + c]) * kj;
-        accP += to_f32(q[ri * DK + c]) * kj;
-      }
-    }
-    s_A[i * RTS + j] = (b < a) ? s_beta[i] * accA : 0.f;
-    s_P[i * C + j] = (b <= a) ? accP : 0.f;
-  }
+__device__ __forceinline__ void tile_of_pair(int pr, int &I, int &J) {
+  // ten (I, J) tile pairs with J <= I: (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) ...
+  I = pr >= 6 ? 3 : pr >= 3 ? 2 : pr >= 1 ? 1 : 0;
+  J = pr - I * (I + 1) / 2;
 }
 
+// ---------------------------------------------------------------- kernel
 template <int DK>
 __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
     const __hip_bfloat16 *__restrict__ q, const __hip_bfloat16 *__restrict__ k,
@@ -169,42 +180,31 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
     const float *__restrict__ beta, const float *__restrict__ S0, float *__restrict__ o,
     float *__restrict__ S_T, int T, int H, int DV, int NH, int NV, SeqTable tab, int packed) {
   using L = Lds<DK>;
-  using GEO = Geo<DK>;
-  constexpr int CQ = GEO::CQ, TPT = GEO::TPT, TG = GEO::TG;
-  constexpr int KB = DK / 32;          // 32-channel k blocks
-  constexpr int ST = DK / 16;          // 16-row state tiles per wave
+  using PG = Prep<DK>;
+  constexpr int CQW = PG::CQW, TGW = PG::TGW, TPL = PG::TPL;
+  constexpr int KB = DK / 32;     // 32-channel k blocks
+  constexpr int ST = DK / 16;     // 16-row state tiles per state-pass wave
   __shared__ __align__(16) char smem[L::SIZE];
-  float *s_Xk = reinterpret_cast<float *>(smem + L::RA);
-  float *s_Xq = reinterpret_cast<float *>(smem + L::RB);
-  float *s_Y = reinterpret_cast<float *>(smem + L::RC);
-  __bf16 *p_gk_h = reinterpret_cast<__bf16 *>(smem + L::RA);
-  __bf16 *p_gk_l = p_gk_h + C * (DK + PADB);
-  __bf16 *p_gq_h = reinterpret_cast<__bf16 *>(smem + L::RB);
-  __bf16 *p_gq_l = p_gq_h + C * (DK + PADB);
-  __bf16 *p_kh_h = reinterpret_cast<__bf16 *>(smem + L::RC);   // [DK][C]
-  __bf16 *p_kh_l = p_kh_h + DK * (C + PADB);
-  float *s_A = reinterpret_cast<float *>(smem + L::RT);
-  float *s_P = reinterpret_cast<float *>(smem + L::RP);
-  __bf16 *p_p_h = reinterpret_cast<__bf16 *>(smem + L::RP);
-  __bf16 *p_p_l = p_p_h + C * (C + PADB);
-  __bf16 *p_tb_h = reinterpret_cast<__bf16 *>(smem + L::RTB);
-  __bf16 *p_tb_l = p_tb_h + C * (C + PADB);
-  float *s_Gtot = reinterpret_cast<float *>(smem + L::RTB);              // [TG][DK]
-  uint8_t *s_Ptot = reinterpret_cast<uint8_t *>(smem + L::RTB + TG * DK * 4);
-  float *s_Z = reinterpret_cast<float *>(smem + L::RZ);
-  float *s_GE = reinterpret_cast<float *>(smem + L::GE);
-  uint8_t *s_PE = reinterpret_cast<uint8_t *>(smem + L::PE);
-  float *s_GN = reinterpret_cast<float *>(smem + L::GN);
+  __bf16 *gk_h = reinterpret_cast<__bf16 *>(smem + L::GK), *gk_l = gk_h + C * (DK + PADB);
+  __bf16 *gq_h = reinterpret_cast<__bf16 *>(smem + L::GQ), *gq_l = gq_h + C * (DK + PADB);
+  __bf16 *kt_h = reinterpret_cast<__bf16 *>(smem + L::KT), *kt_l = kt_h + DK * (C + PADB);
+  __bf16 *kg_h = reinterpret_cast<__bf16 *>(smem + L::KG), *kg_l = kg_h + C * (DK + PADB);
+  __bf16 *p_h = reinterpret_cast<__bf16 *>(smem + L::P), *p_l = p_h + C * (C + PADB);
+  __bf16 *at_h = reinterpret_cast<__bf16 *>(smem + L::AT), *at_l = at_h + C * (C + PADB);
+  float *s_ad = reinterpret_cast<float *>(smem + L::AD);
   float *s_beta = reinterpret_cast<float *>(smem + L::BT);
+  float *s_pre = reinterpret_cast<float *>(smem + L::SPRE);
+  float *s_mid = reinterpret_cast<float *>(smem + L::SMID);
+  float *s_post = reinterpret_cast<float *>(smem + L::SPOST);
   int *s_flag = reinterpret_cast<int *>(smem + L::FL);
 
   // ---- which (sequence, head, dv block): XCD-aware.  Workgroup b runs on XCD
-  // b % 8; the NV dv blocks of one (sequence, head) get the same XCD so they
-  // share q/k/alpha in its L2, and low ranks (longest sequences) start first.
+  // b % 8; the NV dv blocks of one (sequence, head) share an XCD (and its L2),
+  // and low ranks (the longest sequences when packed) start first.
   const int b = blockIdx.x, xcd = b & 7, slot = b >> 3;
-  const int p = (slot / NV) * 8 + xcd, vb = slot % NV;
-  if (p >= NH) return;
-  const int rank = p / H, h = p % H;
+  const int pidx = (slot / NV) * 8 + xcd, vb = slot % NV;
+  if (pidx >= NH) return;
+  const int rank = pidx / H, h = pidx % H;
   int n, start, len;
   if (packed) {
     n = tab.order[rank];
@@ -215,43 +215,25 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
     start = n * T;
     len = T;
   }
-  const int t = threadIdx.x, w = t >> 6, lane = t & 63, l16 = lane & 15, gq = lane >> 4;
-  const int col = vb * BV + 16 * w + l16;         // this lane's dv column
-  const int cq = t % CQ, tg = t / CQ;              // gate phase: channel quad, token group
-  const int c0 = 4 * cq, i0 = tg * TPT, blk = i0 >> 4;
+  const int nch = (len + C - 1) / C;
+  const int w = threadIdx.x >> 6;
+  const bool prep = w >= 4;           // chunk-preparation wave
 
-  // ---- state slice in accumulators: tile tt holds rows 16tt + 4gq + e, column col.
+  // ---- state-pass lane state
   f32x4 accS[ST];
-#pragma unroll
-  for (int tt = 0; tt < ST; ++tt)
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      accS[tt][e] = S0 ? S0[(((size_t)n * H + h) * DK + 16 * tt + 4 * gq + e) * DV + col] : 0.f;
-
-  if (t == 0) { s_flag[0] = 0; s_flag[1] = 0; }
-
-  // ---- input loads for one chunk (issued a chunk ahead).
-  float4 in_a[TPT];
-  uint2 in_k[TPT], in_q[TPT];
-  float in_b = 0.f;
   unsigned short in_v[4][4];
-  auto load_chunk = [&](int lc) {
+  // ---- preparation lane state
+  float4 in_a[TPL];
+  uint2 in_k[TPL], in_q[TPL];
+  float in_b = 0.f;
+  uint2 o_kg_h[TPL], o_kg_l[TPL];
+  float pre4[4], post4[4];
+  uint32_t guard_bad = 0;
+
+  auto sp_load_v = [&](int lc, int tpin) {
+    const int lane = tpin & 63, l16 = lane & 15, gq = lane >> 4;
+    const int col = vb * BV + 16 * (tpin >> 6) + l16;
     const int t0 = start + lc * C, nt = min(C, len - lc * C);
-#pragma unroll
-    for (int r = 0; r < TPT; ++r) {
-      const int i = i0 + r;
-      if (i < nt) {
-        const size_t row = (size_t)(t0 + i) * H + h;
-        in_a[r] = *reinterpret_cast<const float4 *>(g + row * DK + c0);
-        in_k[r] = *reinterpret_cast<const uint2 *>(k + row * DK + c0);
-        in_q[r] = *reinterpret_cast<const uint2 *>(q + row * DK + c0);
-      } else {
-        in_a[r] = make_float4(1.f, 1.f, 1.f, 1.f);
-        in_k[r] = make_uint2(0u, 0u);
-        in_q[r] = make_uint2(0u, 0u);
-      }
-    }
-    in_b = (t < C && t < nt) ? beta[(size_t)(t0 + t) * H + h] : 0.f;
     const unsigned short *vv = reinterpret_cast<const unsigned short *>(v);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
@@ -261,30 +243,41 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
         in_v[mt][e] = i < nt ? vv[((size_t)(t0 + i) * H + h) * DV + col] : (unsigned short)0;
       }
   };
-
-  const int nch = (len + C - 1) / C;
-  if (nch > 0) load_chunk(0);
-  __syncthreads();
-
-  for (int lc = 0; lc < nch; ++lc) {
+  auto pr_load = [&](int lc, int tpin) {
+    const int lane = tpin & 63, pw = (tpin >> 6) - 4;
+    const int c0 = 4 * (pw * CQW + lane % CQW), i0 = (lane / CQW) * TPL;
     const int t0 = start + lc * C, nt = min(C, len - lc * C);
-    const size_t row0 = (size_t)t0 * H + h;
-    // Re-derive the lane indices from an opaque copy of the thread id so that
-    // the compiler recomputes per-chunk address arithmetic inside the loop
-    // instead of keeping hundreds of hoisted addresses live across it.
+#pragma unroll
+    for (int r = 0; r < TPL; ++r) {
+      const int i = i0 + r;
+      if (i < nt) {
+        const size_t row = (size_t)(t0 + i) * H + h;
+        in_a[r] = *reinterpret_cast<const float4 *>(g + row * DK + c0);
+        in_k[r] = *reinterpret_cast<const uint2 *>(k + row * DK + c0);
+        in_q[r] = *reinterpret_cast<const uint2 *>(q + row * DK + c0);
+      } else {   // padding tokens: identity gate, zero key/query
+        in_a[r] = make_float4(1.f, 1.f, 1.f, 1.f);
+        in_k[r] = make_uint2(0u, 0u);
+        in_q[r] = make_uint2(0u, 0u);
+      }
+    }
+    in_b = (pw == 0 && lane < nt) ? beta[(size_t)(t0 + lane) * H + h] : 0.f;
+  };
+
+  // Register stage of chunk preparation: gate scan across the wave's lanes,
+  // gamma'-scaled operands and their hi/lo split.  -(gamma' K) and gamma' Q go
+  // straight to LDS (the state pass is done with those planes once H4 has
+  // passed); K/gamma' is held for the hand-off.
+  auto pr_compute = [&]() {
     int t_opaque = threadIdx.x;
     asm volatile("" : "+v"(t_opaque));
-    const int t = t_opaque, lane = t & 63, l16 = lane & 15, gq = lane >> 4;
-    const int cq = t % CQ, tg = t / CQ, c0 = 4 * cq, i0 = tg * TPT, blk = i0 >> 4;
-    const int col = vb * BV + 16 * w + l16;
-
-    // ===================== P1: signed-gate scan (per channel, over tokens)
-    // Gl: in-thread inclusive sums of log2|alpha|; pbits bit 4r+cc: in-thread
-    // inclusive parity of negative gates for token r, channel cc.
-    float Gl[TPT][4];
-    uint32_t pbits = 0;
+    const int lane = t_opaque & 63, tg = lane / CQW, cql = lane % CQW;
+    const int pw = (t_opaque >> 6) - 4;
+    const int c0 = 4 * (pw * CQW + cql), i0 = tg * TPL;
+    float Gl[TPL][4];
+    uint32_t pbits = 0;     // bit 4r+cc: in-lane inclusive parity of token r, channel cc
 #pragma unroll
-    for (int r = 0; r < TPT; ++r) {
+    for (int r = 0; r < TPL; ++r) {
       const float a4[4] = {in_a[r].x, in_a[r].y, in_a[r].z, in_a[r].w};
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
@@ -295,382 +288,421 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
         pbits |= (prev ^ neg) << (4 * r + cc);
       }
     }
-    *reinterpret_cast<float4 *>(s_Gtot + tg * DK + c0) =
-        make_float4(Gl[TPT - 1][0], Gl[TPT - 1][1], Gl[TPT - 1][2], Gl[TPT - 1][3]);
-    *reinterpret_cast<uint32_t *>(s_Ptot + tg * DK + c0) =
-        ((pbits >> (4 * (TPT - 1))) & 1u) | (((pbits >> (4 * (TPT - 1) + 1)) & 1u) << 8) |
-        (((pbits >> (4 * (TPT - 1) + 2)) & 1u) << 16) | (((pbits >> (4 * (TPT - 1) + 3)) & 1u) << 24);
-    if (t < C) s_beta[t] = in_b;
-    __syncthreads();   // B1
-
-    // prefix over token groups; block-end and chunk-end values per channel.
-    // Gs/Ps: end of the block before this thread's block; Ge/Pe: end of it.
-    float Gx[4], Gs[4], Ge[4], Gn[4];
-    uint32_t Px[4], Ps[4], Pe[4], Pn[4];
-    int myflag = 0;
-    {
-      float run[4] = {0.f, 0.f, 0.f, 0.f}, prev_end[4] = {0.f, 0.f, 0.f, 0.f};
-      uint32_t prun = 0u;   // four parity bytes, one per channel of the quad
+    // inclusive scan of the lane totals over token groups (lanes CQW apart)
+    float incl[4] = {Gl[TPL - 1][0], Gl[TPL - 1][1], Gl[TPL - 1][2], Gl[TPL - 1][3]};
+    uint32_t pincl = (pbits >> (4 * (TPL - 1))) & 0xFu;
+#pragma unroll
+    for (int d = 1; d < TGW; d <<= 1) {
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
-        Gx[cc] = 0.f; Px[cc] = 0u; Gs[cc] = 0.f; Ps[cc] = 0u; Ge[cc] = 0.f; Pe[cc] = 0u;
+        const float y = __shfl_up(incl[cc], d * CQW);
+        if (tg >= d) incl[cc] += y;
       }
-#pragma unroll
-      for (int gg = 0; gg < TG; ++gg) {
-        if (gg == tg) {
-#pragma unroll
-          for (int cc = 0; cc < 4; ++cc) { Gx[cc] = run[cc]; Px[cc] = (prun >> (8 * cc)) & 1u; }
-        }
-        const float4 gt = *reinterpret_cast<const float4 *>(s_Gtot + gg * DK + c0);
-        run[0] += gt.x; run[1] += gt.y; run[2] += gt.z; run[3] += gt.w;
-        prun ^= *reinterpret_cast<const uint32_t *>(s_Ptot + gg * DK + c0);
-        if (((gg + 1) * TPT) % 16 == 0) {
-          const int I = ((gg + 1) * TPT) / 16 - 1;     // block whose end this is
-#pragma unroll
-          for (int cc = 0; cc < 4; ++cc) {
-            if (I == blk) { Ge[cc] = run[cc]; Pe[cc] = (prun >> (8 * cc)) & 1u; }
-            if (I + 1 == blk) { Gs[cc] = run[cc]; Ps[cc] = (prun >> (8 * cc)) & 1u; }
-            if (prev_end[cc] - run[cc] > kDiagGuard) myflag |= 1 << I;
-            prev_end[cc] = run[cc];
-          }
-          if (tg == 0) {
-            *reinterpret_cast<float4 *>(s_GE + I * DK + c0) = make_float4(run[0], run[1], run[2], run[3]);
-            *reinterpret_cast<uint32_t *>(s_PE + I * DK + c0) = prun;
-          }
-        }
-      }
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) { Gn[cc] = run[cc]; Pn[cc] = (prun >> (8 * cc)) & 1u; }
-      if (tg == 0)
-        *reinterpret_cast<float4 *>(s_GN + c0) =
-            make_float4(sgn(Pn[0]) * fexp2(Gn[0]), sgn(Pn[1]) * fexp2(Gn[1]),
-                        sgn(Pn[2]) * fexp2(Gn[2]), sgn(Pn[3]) * fexp2(Gn[3]));
-      if (tg != 0) myflag = 0;
+      const uint32_t yp = __shfl_up(pincl, d * CQW);
+      if (tg >= d) pincl ^= yp;
     }
-    if (myflag) atomicOr(&s_flag[lc & 1], myflag);
-
-    // row operands (relative to block start) and column operand (relative to block end)
+    float excl[4], R[4];
 #pragma unroll
-    for (int r = 0; r < TPT; ++r) {
+    for (int cc = 0; cc < 4; ++cc) {
+      const float y = __shfl_up(incl[cc], CQW);
+      excl[cc] = tg ? y : 0.f;
+      const float Gn = __shfl(incl[cc], (TGW - 1) * CQW + cql);
+      R[cc] = 0.5f * Gn;                 // per-channel reference, middle of [G_n, 0]
+      pre4[cc] = fexp2(R[cc]);
+      post4[cc] = fexp2(Gn - R[cc]);     // sign applied below
+    }
+    const uint32_t pprev = __shfl_up(pincl, CQW);
+    const uint32_t pex = tg ? (pprev & 0xFu) : 0u;
+    const uint32_t pn = __shfl(pincl, (TGW - 1) * CQW + cql);
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) post4[cc] = with_sign(post4[cc], (pn >> cc) & 1u);
+    float gmax = 0.f;
+#pragma unroll
+    for (int r = 0; r < TPL; ++r) {
+      __bf16 hk[4], lk[4], hq[4], lq[4], hg[4], lgg[4];
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        const float D = excl[cc] + Gl[r][cc] - R[cc];
+        const uint32_t odd = ((pex >> cc) ^ (pbits >> (4 * r + cc))) & 1u;
+        gmax = fmaxf(gmax, fabsf(D));
+        const float gam = with_sign(fexp2(D), odd);
+        const float igam = with_sign(fexp2(-D), odd);
+        const uint32_t kw = cc < 2 ? in_k[r].x : in_k[r].y, qw = cc < 2 ? in_q[r].x : in_q[r].y;
+        const float kk = bf16_to_f32((cc & 1) ? (kw >> 16) : (kw & 0xFFFFu));
+        const float qq = bf16_to_f32((cc & 1) ? (qw >> 16) : (qw & 0xFFFFu));
+        split1(-kk * gam, hk[cc], lk[cc]);
+        split1(qq * gam, hq[cc], lq[cc]);
+        split1(kk * igam, hg[cc], lgg[cc]);
+      }
       const int i = i0 + r;
-      const __hip_bfloat16 *kb16 = reinterpret_cast<const __hip_bfloat16 *>(&in_k[r]);
-      const __hip_bfloat16 *qb16 = reinterpret_cast<const __hip_bfloat16 *>(&in_q[r]);
-      float xk[4], xq[4], yk[4];
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-        const float G = Gx[cc] + Gl[r][cc];
-        const uint32_t P = Px[cc] ^ ((pbits >> (4 * r + cc)) & 1u);
-        const float ra = sgn(P ^ Ps[cc]) * fexp2(G - Gs[cc]);
-        const float cb = sgn(Pe[cc] ^ P) * fexp2(Ge[cc] - G);
-        const float kk = __bfloat162float(kb16[cc]);
-        xk[cc] = kk * ra;
-        xq[cc] = __bfloat162float(qb16[cc]) * ra;
-        yk[cc] = kk * cb;
-      }
-      *reinterpret_cast<float4 *>(s_Xk + f32at(i, c0, DK)) = make_float4(xk[0], xk[1], xk[2], xk[3]);
-      *reinterpret_cast<float4 *>(s_Xq + f32at(i, c0, DK)) = make_float4(xq[0], xq[1], xq[2], xq[3]);
-      *reinterpret_cast<float4 *>(s_Y + f32at(i, c0, DK)) = make_float4(yk[0], yk[1], yk[2], yk[3]);
+      *reinterpret_cast<uint2 *>(gk_h + at(i, c0, DK)) = __builtin_bit_cast(uint2, hk);
+      *reinterpret_cast<uint2 *>(gk_l + at(i, c0, DK)) = __builtin_bit_cast(uint2, lk);
+      *reinterpret_cast<uint2 *>(gq_h + at(i, c0, DK)) = __builtin_bit_cast(uint2, hq);
+      *reinterpret_cast<uint2 *>(gq_l + at(i, c0, DK)) = __builtin_bit_cast(uint2, lq);
+      o_kg_h[r] = __builtin_bit_cast(uint2, hg);
+      o_kg_l[r] = __builtin_bit_cast(uint2, lgg);
+      __builtin_amdgcn_sched_barrier(0);   // one token at a time: bounded live range
     }
-    if (t == 0) s_flag[(lc + 1) & 1] = 0;
-    __syncthreads();   // B2
-    const int flags = s_flag[lc & 1];
+    guard_bad = __any(gmax > kGuard) ? 1u : 0u;
+  };
 
-    // ===================== P3: A and P tiles on matrix cores
-    {
-      // ten (I, J) tile pairs, J <= I: (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) ...
-      for (int pr = w; pr < 10; pr += 4) {
-        const int I = pr >= 6 ? 3 : pr >= 3 ? 2 : pr >= 1 ? 1 : 0;
-        const int J = pr - I * (I + 1) / 2;
-        const bool diag = I == J;
-        if (diag && ((flags >> I) & 1)) continue;
-        f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KB; ++ks) {
-          const int c = 32 * ks + 8 * gq;
-          const int ri = 16 * I + l16, rj = 16 * J + l16;
-          float xk[8], xq[8], y[8];
-          *reinterpret_cast<float4 *>(xk) = *reinterpret_cast<const float4 *>(s_Xk + f32at(ri, c, DK));
-          *reinterpret_cast<float4 *>(xk + 4) = *reinterpret_cast<const float4 *>(s_Xk + f32at(ri, c + 4, DK));
-          *reinterpret_cast<float4 *>(xq) = *reinterpret_cast<const float4 *>(s_Xq + f32at(ri, c, DK));
-          *reinterpret_cast<float4 *>(xq + 4) = *reinterpret_cast<const float4 *>(s_Xq + f32at(ri, c + 4, DK));
-          *reinterpret_cast<float4 *>(y) = *reinterpret_cast<const float4 *>(s_Y + f32at(rj, c, DK));
-          *reinterpret_cast<float4 *>(y + 4) = *reinterpret_cast<const float4 *>(s_Y + f32at(rj, c + 4, DK));
-          float gs[8], ge[8];
-          uint2 ps = {0u, 0u};
-          if (I) {
-            *reinterpret_cast<float4 *>(gs) = *reinterpret_cast<const float4 *>(s_GE + (I - 1) * DK + c);
-            *reinterpret_cast<float4 *>(gs + 4) = *reinterpret_cast<const float4 *>(s_GE + (I - 1) * DK + c + 4);
-            ps = *reinterpret_cast<const uint2 *>(s_PE + (I - 1) * DK + c);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) gs[e] = 0.f;
-          }
-          *reinterpret_cast<float4 *>(ge) = *reinterpret_cast<const float4 *>(s_GE + J * DK + c);
-          *reinterpret_cast<float4 *>(ge + 4) = *reinterpret_cast<const float4 *>(s_GE + J * DK + c + 4);
-          const uint2 pe = *reinterpret_cast<const uint2 *>(s_PE + J * DK + c);
-          const uint32_t par_lo = ps.x ^ pe.x, par_hi = ps.y ^ pe.y;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const uint32_t odd = ((e < 4 ? par_lo : par_hi) >> (8 * (e & 3))) & 1u;
-            const float D = sgn(odd) * fexp2(gs[e] - ge[e]);
-            xk[e] *= D;
-            xq[e] *= D;
-          }
-          bf16x8 akh, akl, aqh, aql, yh, yl;
-          split8(xk, akh, akl);
-          split8(xq, aqh, aql);
-          split8(y, yh, yl);
-          accA = mfma3(accA, akh, akl, yh, yl);
-          accP = mfma3(accP, aqh, aql, yh, yl);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 16 * I + 4 * gq + e, j = 16 * J + l16;
-          s_A[i * RTS + j] = (!diag || j < i) ? s_beta[i] * accA[e] : 0.f;
-          s_P[i * C + j] = (!diag || j <= i) ? accP[e] : 0.f;
-        }
-      }
-      // zero P above the diagonal blocks
-      for (int x = t; x < 6 * 256; x += NT) {
-        // blocks (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
-        const int bi = x >> 8, e = x & 255;
-        const int ui = bi < 3 ? 0 : bi < 5 ? 1 : 2;
-        const int uj = bi < 3 ? bi + 1 : bi < 5 ? bi - 1 : 3;
-        s_P[(16 * ui + (e >> 4)) * C + 16 * uj + (e & 15)] = 0.f;
-      }
-    }
-    __syncthreads();   // B3
-    if (flags) {
-#pragma unroll 1
-      for (int I = 0; I < 4; ++I)
-        if ((flags >> I) & 1)
-          diag_block_elementwise<DK>(I, q, k, g, s_beta, row0, (size_t)H, nt, s_A, s_P);
-      __syncthreads();
-    }
+  if (threadIdx.x == 0) { s_flag[0] = 0; s_flag[1] = 0; }
 
-    // ===================== P4: matrix-core operands for the state pass,
-    // T diagonal blocks (wave 0), P to registers
-    // Own Xk, Xq, Y back from LDS; they are rewritten as bf16 planes after B4.
-    float4 rXk[TPT], rXq[TPT], rY[TPT];
-#pragma unroll
-    for (int r = 0; r < TPT; ++r) {
-      rXk[r] = *reinterpret_cast<const float4 *>(s_Xk + f32at(i0 + r, c0, DK));
-      rXq[r] = *reinterpret_cast<const float4 *>(s_Xq + f32at(i0 + r, c0, DK));
-      rY[r] = *reinterpret_cast<const float4 *>(s_Y + f32at(i0 + r, c0, DK));
+  // The two roles run separate loops with the same barrier sequence per chunk
+  // (H1, H2, H3, two more on the exact path, H4), so each role's registers are
+  // live only inside its own loop.
+  if (prep) {
+    // ======================= chunk preparation (waves 4-7)
+    float xA[(C * C) / 256], xP[(C * C) / 256];   // exact path: -A and P held over a barrier
+    if (nch > 0) {
+      pr_load(0, threadIdx.x);
+      pr_compute();
     }
-    if (w == 0) {
-      // (I + A_II)^-1 for the four diagonal blocks; lane = 16 I + column
-      const int I = lane >> 4, j = lane & 15;
-      float x[16];
+    for (int lc = 0; lc < nch; ++lc) {
+      const int t0 = start + lc * C, nt = min(C, len - lc * C);
+      int t_opaque = threadIdx.x;
+      asm volatile("" : "+v"(t_opaque));
+      const int lane = t_opaque & 63, l16 = lane & 15, gq = lane >> 4;
+      const int tid = t_opaque - 256, pw = tid >> 6;      // preparation thread / wave
+      const int tg = lane / CQW, cql = lane % CQW;
+      const int c0 = 4 * (pw * CQW + cql), i0 = tg * TPL;
+
+      __syncthreads();   // H1: the previous chunk's operands are no longer read
+      // ---- hand-off: the register stage's operands into LDS
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float s = (i == j) ? 1.f : 0.f;
-#pragma unroll
-        for (int m = 0; m < i; ++m) s -= s_A[(16 * I + i) * RTS + 16 * I + m] * x[m];
-        x[i] = (i < j) ? 0.f : s;
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s_A[(16 * I + i) * RTS + 16 * I + j] = x[i];
-    }
-    float pv[16];
-    {
-      const int pi = t >> 2, pj = (t & 3) * 16;
-#pragma unroll
-      for (int u = 0; u < 16; u += 4)
-        *reinterpret_cast<float4 *>(pv + u) = *reinterpret_cast<const float4 *>(s_P + pi * C + pj + u);
-    }
-    __syncthreads();   // B4
-    {
-      float gam_s[4], del_e[4];
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-        gam_s[cc] = sgn(Ps[cc]) * fexp2(Gs[cc]);                          // chunk start -> block start
-        del_e[cc] = sgn(Pe[cc] ^ Pn[cc]) * fexp2(Gn[cc] - Ge[cc]);        // block end -> chunk end
-      }
-#pragma unroll
-      for (int r = 0; r < TPT; ++r) {
+      for (int r = 0; r < TPL; ++r) {
         const int i = i0 + r;
-        const float xk[4] = {rXk[r].x, rXk[r].y, rXk[r].z, rXk[r].w};
-        const float xq[4] = {rXq[r].x, rXq[r].y, rXq[r].z, rXq[r].w};
-        __bf16 hk[4], lk[4], hq[4], lq[4];
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-          const float a = -xk[cc] * gam_s[cc];     // -(gamma K)
-          const float bq = xq[cc] * gam_s[cc];     // gamma Q
-          hk[cc] = (__bf16)a; lk[cc] = (__bf16)(a - (float)hk[cc]);
-          hq[cc] = (__bf16)bq; lq[cc] = (__bf16)(bq - (float)hq[cc]);
-        }
-        *reinterpret_cast<uint2 *>(p_gk_h + bfat(i, c0, DK)) = __builtin_bit_cast(uint2, hk);
-        *reinterpret_cast<uint2 *>(p_gk_l + bfat(i, c0, DK)) = __builtin_bit_cast(uint2, lk);
-        *reinterpret_cast<uint2 *>(p_gq_h + bfat(i, c0, DK)) = __builtin_bit_cast(uint2, hq);
-        *reinterpret_cast<uint2 *>(p_gq_l + bfat(i, c0, DK)) = __builtin_bit_cast(uint2, lq);
+        *reinterpret_cast<uint2 *>(kg_h + at(i, c0, DK)) = o_kg_h[r];
+        *reinterpret_cast<uint2 *>(kg_l + at(i, c0, DK)) = o_kg_l[r];
       }
-      // K_hat^T = (K gamma_n / gamma)^T, [channel][token]
+      // (K/gamma)^T: channel rows, 4 tokens per 8-byte store
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
+      for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
-        for (int r4 = 0; r4 < TPT; r4 += 4) {
-          __bf16 hh[4], ll[4];
+        for (int r4 = 0; r4 < TPL; r4 += 4) {
+          uint32_t hw[2], lw[2];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const float y4[4] = {rY[r4 + u].x, rY[r4 + u].y, rY[r4 + u].z, rY[r4 + u].w};
-            const float x = y4[cc] * del_e[cc];
-            hh[u] = (__bf16)x; ll[u] = (__bf16)(x - (float)hh[u]);
+          for (int u = 0; u < 2; ++u) {
+            const int r = r4 + 2 * u;
+            const int sh = 16 * (cc & 1);
+            const uint32_t h0 = (cc < 2 ? o_kg_h[r].x : o_kg_h[r].y) >> sh;
+            const uint32_t h1 = (cc < 2 ? o_kg_h[r + 1].x : o_kg_h[r + 1].y) >> sh;
+            const uint32_t l0 = (cc < 2 ? o_kg_l[r].x : o_kg_l[r].y) >> sh;
+            const uint32_t l1 = (cc < 2 ? o_kg_l[r + 1].x : o_kg_l[r + 1].y) >> sh;
+            hw[u] = (h0 & 0xFFFFu) | (h1 << 16);
+            lw[u] = (l0 & 0xFFFFu) | (l1 << 16);
           }
-          *reinterpret_cast<uint2 *>(p_kh_h + bfat(c0 + cc, i0 + r4, C)) = __builtin_bit_cast(uint2, hh);
-          *reinterpret_cast<uint2 *>(p_kh_l + bfat(c0 + cc, i0 + r4, C)) = __builtin_bit_cast(uint2, ll);
+          *reinterpret_cast<uint2 *>(kt_h + at(c0 + cc, i0 + r4, C)) = make_uint2(hw[0], hw[1]);
+          *reinterpret_cast<uint2 *>(kt_l + at(c0 + cc, i0 + r4, C)) = make_uint2(lw[0], lw[1]);
+        }
+      if (tg == 0) {
+        *reinterpret_cast<float4 *>(s_pre + c0) = make_float4(pre4[0], pre4[1], pre4[2], pre4[3]);
+        *reinterpret_cast<float4 *>(s_mid + c0) = make_float4(1.f, 1.f, 1.f, 1.f);
+        *reinterpret_cast<float4 *>(s_post + c0) =
+            make_float4(post4[0], post4[1], post4[2], post4[3]);
+      }
+      if (pw == 0) s_beta[lane] = in_b;
+      if (guard_bad && lane == 0) atomicOr(&s_flag[lc & 1], 1);
+      if (lc + 1 < nch) pr_load(lc + 1, t_opaque);   // next chunk's inputs, in flight meanwhile
+
+      __syncthreads();   // H2
+      const int fallback = s_flag[lc & 1];
+      f32x4 pA[3], pP[3];                      // A and P tiles, held over H3
+      if (!fallback) {
+        // ---- A and P tiles (I, J), J <= I: row operands -(gamma K) / gamma Q of
+        // block I, column operand K/gamma of block J.  Tile pairs pw, pw+4, pw+8.
+#pragma unroll
+        for (int s = 0; s < 3; ++s) {
+          const int pr = pw + 4 * s;
+          pA[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+          pP[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (pr < 10) {
+            int I, J;
+            tile_of_pair(pr, I, J);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+              const bf16x8 bh = frag32(kg_h, DK, 16 * J + l16, kb, gq);
+              const bf16x8 bl = frag32(kg_l, DK, 16 * J + l16, kb, gq);
+              pA[s] = mfma32x3(pA[s], frag32(gk_h, DK, 16 * I + l16, kb, gq),
+                               frag32(gk_l, DK, 16 * I + l16, kb, gq), bh, bl);
+              pP[s] = mfma32x3(pP[s], frag32(gq_h, DK, 16 * I + l16, kb, gq),
+                               frag32(gq_l, DK, 16 * I + l16, kb, gq), bh, bl);
+            }
+            // pA holds -A_ij / beta_i; scale rows by beta_i -> -A_ij
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pA[s][e] *= s_beta[16 * I + 4 * gq + e];
+            if (I == J) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int a = 4 * gq + e;     // row within the block; the column is l16
+                s_ad[(I * 16 + a) * ADS + l16] = (l16 < a) ? -pA[s][e] : 0.f;
+              }
+            }
+          }
+        }
+      } else {
+        // ---- exact path, part 1: G (fp32) per (token, channel) and the parity
+        // mask of each channel into the K/gamma region, one channel per thread.
+        float *s_G = reinterpret_cast<float *>(smem + L::KG);
+        uint2 *s_pm = reinterpret_cast<uint2 *>(smem + L::KG + L::FG);   // [DK] 64-bit masks
+        const int c = tid;
+        if (c < DK) {
+          float G = 0.f;
+          uint32_t par = 0, m0 = 0, m1 = 0;
+          for (int i = 0; i < C; ++i) {
+            const float a = i < nt ? g[((size_t)(t0 + i) * H + h) * DK + c] : 1.f;
+            G += fmaxf(flog2(fabsf(a)), kLog2Floor);
+            par ^= a < 0.f ? 1u : 0u;
+            s_G[i * DK + c] = G;
+            if (i < 32) m0 |= par << i; else m1 |= par << (i - 32);
+          }
+          s_pm[c] = make_uint2(m0, m1);
         }
       }
-    }
-    {
-      const int pi = t >> 2, pj = (t & 3) * 16;
+
+      __syncthreads();   // H3
+      if (!fallback) {
+        // -A below the diagonal blocks, P on and below them
 #pragma unroll
-      for (int u = 0; u < 16; u += 4) {
-        __bf16 hh[4], ll[4];
+        for (int s = 0; s < 3; ++s) {
+          const int pr = pw + 4 * s;
+          if (pr < 10) {
+            int I, J;
+            tile_of_pair(pr, I, J);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int a = 4 * gq + e, i = 16 * I + a, j = 16 * J + l16;
+              __bf16 hh, ll;
+              if (J < I) {
+                split1(pA[s][e], hh, ll);
+                at_h[at(i, j, C)] = hh;
+                at_l[at(i, j, C)] = ll;
+              }
+              split1((J < I || l16 <= a) ? pP[s][e] : 0.f, hh, ll);
+              p_h[at(i, j, C)] = hh;
+              p_l[at(i, j, C)] = ll;
+            }
+          }
+        }
+      } else {
+        // ---- exact path, part 2: A and P element by element (|2^(G_i - G_j)|
+        // <= 1 for |alpha| <= 1) into registers, the diagonal A tiles,
+        // K_hat^T = (K gamma_n / gamma)^T and the operands relative to the chunk
+        // start; the state pass then uses S_pre = S and
+        // S' = Diag(gamma_n) S + K_hat^T U.
+        const float *s_G = reinterpret_cast<const float *>(smem + L::KG);
+        const uint2 *s_pm = reinterpret_cast<const uint2 *>(smem + L::KG + L::FG);
+        auto par_of = [&](int i, int c) {
+          const uint2 m = s_pm[c];
+          return ((i < 32 ? m.x : m.y) >> (i & 31)) & 1u;
+        };
+#pragma unroll
+        for (int u = 0; u < (C * C) / 256; ++u) {
+          const int pp = tid + 256 * u, i = pp / C, j = pp % C;
+          float accA = 0.f, accP = 0.f;
+          if (j <= i && i < nt) {
+            const size_t ri = (size_t)(t0 + i) * H + h, rj = (size_t)(t0 + j) * H + h;
+            for (int c = 0; c < DK; ++c) {
+              const float r = with_sign(fexp2(s_G[i * DK + c] - s_G[j * DK + c]),
+                                        par_of(i, c) ^ par_of(j, c));
+              const float kj = __bfloat162float(k[rj * DK + c]) * r;
+              accA += __bfloat162float(k[ri * DK + c]) * kj;
+              accP += __bfloat162float(q[ri * DK + c]) * kj;
+            }
+          }
+          const float Aij = (j < i) ? s_beta[i] * accA : 0.f;
+          if ((i >> 4) == (j >> 4)) s_ad[((i >> 4) * 16 + (i & 15)) * ADS + (j & 15)] = Aij;
+          xA[u] = -Aij;
+          xP[u] = (j <= i) ? accP : 0.f;
+        }
+        for (int pp = tid; pp < DK * C; pp += 256) {
+          const int c = pp / C, j = pp % C;
+          float x = 0.f;
+          if (j < nt) {
+            const float r = with_sign(fexp2(s_G[(C - 1) * DK + c] - s_G[j * DK + c]),
+                                      par_of(C - 1, c) ^ par_of(j, c));
+            x = __bfloat162float(k[((size_t)(t0 + j) * H + h) * DK + c]) * r;
+          }
+          __bf16 hh, ll;
+          split1(x, hh, ll);
+          kt_h[at(c, j, C)] = hh;
+          kt_l[at(c, j, C)] = ll;
+        }
+        // -(gamma K) and gamma Q relative to the chunk start (|gamma| <= 1)
+        for (int pp = tid; pp < C * DK; pp += 256) {
+          const int i = pp / DK, c = pp % DK;
+          float xk = 0.f, xq = 0.f;
+          if (i < nt) {
+            const float gam = with_sign(fexp2(s_G[i * DK + c]), par_of(i, c));
+            const size_t ri = (size_t)(t0 + i) * H + h;
+            xk = -__bfloat162float(k[ri * DK + c]) * gam;
+            xq = __bfloat162float(q[ri * DK + c]) * gam;
+          }
+          __bf16 hh, ll;
+          split1(xk, hh, ll);
+          gk_h[at(i, c, DK)] = hh;
+          gk_l[at(i, c, DK)] = ll;
+          split1(xq, hh, ll);
+          gq_h[at(i, c, DK)] = hh;
+          gq_l[at(i, c, DK)] = ll;
+        }
+        for (int c = tid; c < DK; c += 256) {
+          s_pre[c] = 1.f;
+          s_mid[c] = with_sign(fexp2(s_G[(C - 1) * DK + c]), par_of(C - 1, c));
+          s_post[c] = 1.f;
+        }
+        __syncthreads();   // every thread is done reading G: its region takes A and P
+        {
+#pragma unroll
+          for (int u = 0; u < (C * C) / 256; ++u) {
+            const int pp = tid + 256 * u, i = pp / C, j = pp % C;
+            __bf16 hh, ll;
+            if ((i >> 4) > (j >> 4)) {
+              split1(xA[u], hh, ll);
+              at_h[at(i, j, C)] = hh;
+              at_l[at(i, j, C)] = ll;
+            }
+            split1(xP[u], hh, ll);
+            p_h[at(i, j, C)] = hh;
+            p_l[at(i, j, C)] = ll;
+          }
+        }
+        __syncthreads();   // diagonal A tiles complete for the inverses
+      }
+      __syncthreads();   // H4
+      if (lc + 1 < nch) pr_compute();     // next chunk's operands, overlapping the state pass
+    }
+  } else {
+    // ======================= state pass (waves 0-3)
+    {
+      const int lane = threadIdx.x & 63, l16 = lane & 15, gq = lane >> 4;
+      const int col = vb * BV + 16 * w + l16;
+#pragma unroll
+      for (int tt = 0; tt < ST; ++tt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          accS[tt][e] =
+              S0 ? S0[(((size_t)n * H + h) * DK + 16 * tt + 4 * gq + e) * DV + col] : 0.f;
+      if (nch > 0) sp_load_v(0, threadIdx.x);
+    }
+    for (int lc = 0; lc < nch; ++lc) {
+      const int t0 = start + lc * C, nt = min(C, len - lc * C);
+      int t_opaque = threadIdx.x;
+      asm volatile("" : "+v"(t_opaque));
+      const int lane = t_opaque & 63, l16 = lane & 15, gq = lane >> 4;
+      const int col = vb * BV + 16 * (t_opaque >> 6) + l16;
+
+      __syncthreads();   // H1
+      if (threadIdx.x == 0) s_flag[(lc + 1) & 1] = 0;
+      __syncthreads();   // H2
+      const int fallback = s_flag[lc & 1];
+
+      // ---- S_pre = pre * S;  X = V - (gamma' K) S_pre;  O = (gamma' Q) S_pre
+      f32x4 accX[4], accO[4];
+      auto x_and_o = [&]() {
+#pragma unroll
+        for (int tt = 0; tt < ST; ++tt) {
+          const float4 pre = *reinterpret_cast<const float4 *>(s_pre + 16 * tt + 4 * gq);
+          accS[tt][0] *= pre.x; accS[tt][1] *= pre.y; accS[tt][2] *= pre.z; accS[tt][3] *= pre.w;
+        }
+        bf16x8 sh[KB], sl[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) split8_acc(accS[2 * kb], accS[2 * kb + 1], sh[kb], sl[kb]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) accX[mt][e] = bf16_to_f32(in_v[mt][e]);
+          accO[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            accX[mt] = mfma32x3(accX[mt], frag32(gk_h, DK, 16 * mt + l16, kb, gq),
+                                frag32(gk_l, DK, 16 * mt + l16, kb, gq), sh[kb], sl[kb]);
+            accO[mt] = mfma32x3(accO[mt], frag32(gq_h, DK, 16 * mt + l16, kb, gq),
+                                frag32(gq_l, DK, 16 * mt + l16, kb, gq), sh[kb], sl[kb]);
+          }
+        }
+        if (lc + 1 < nch) sp_load_v(lc + 1, t_opaque);
+      };
+      if (!fallback) x_and_o();
+
+      __syncthreads();   // H3
+      if (fallback) {    // the exact path rewrites the operands first
+        __syncthreads();
+        __syncthreads();
+        x_and_o();
+      }
+      if ((t_opaque >> 6) == 0) {
+        // (I + A_II)^-1 for the four diagonal blocks by right-looking forward
+        // substitution; lane = 16 I + column j.
+        const int I = lane >> 4, j = lane & 15;
+        float acc[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] = (i == j) ? 1.f : 0.f;
+#pragma unroll
+        for (int m = 0; m < 16; ++m)
+#pragma unroll
+          for (int i = m + 1; i < 16; ++i) acc[i] -= s_ad[(I * 16 + i) * ADS + m] * acc[m];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          __bf16 hh, ll;
+          split1(acc[i], hh, ll);
+          at_h[at(16 * I + i, 16 * I + j, C)] = hh;
+          at_l[at(16 * I + i, 16 * I + j, C)] = ll;
+        }
+      }
+      __syncthreads();   // H4
+
+      // ---- (I + A) U = Diag(beta) X by block forward substitution
+      bf16x4 uh[4], ul[4];
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        f32x4 y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = s_beta[16 * I + 4 * gq + e] * accX[I][e];
+#pragma unroll
+        for (int J = 0; J < I; ++J)
+          y = mfma16x3(y, frag16(at_h, C, 16 * I + l16, 16 * J, gq),
+                       frag16(at_l, C, 16 * I + l16, 16 * J, gq), uh[J], ul[J]);
+        bf16x4 yh, yl;
+        split4(y, yh, yl);
+        f32x4 u = {0.f, 0.f, 0.f, 0.f};
+        u = mfma16x3(u, frag16(at_h, C, 16 * I + l16, 16 * I, gq),
+                     frag16(at_l, C, 16 * I + l16, 16 * I, gq), yh, yl);
+        split4(u, uh[I], ul[I]);
+      }
+      // ---- O += P U ; store
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+        for (int J = 0; J <= mt; ++J)
+          accO[mt] = mfma16x3(accO[mt], frag16(p_h, C, 16 * mt + l16, 16 * J, gq),
+                              frag16(p_l, C, 16 * mt + l16, 16 * J, gq), uh[J], ul[J]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          hh[e] = (__bf16)pv[u + e];
-          ll[e] = (__bf16)(pv[u + e] - (float)hh[e]);
+          const int i = 16 * mt + 4 * gq + e;
+          if (i < nt) o[((size_t)(t0 + i) * H + h) * DV + col] = accO[mt][e];
         }
-        *reinterpret_cast<uint2 *>(p_p_h + bfat(pi, pj + u, C)) = __builtin_bit_cast(uint2, hh);
-        *reinterpret_cast<uint2 *>(p_p_l + bfat(pi, pj + u, C)) = __builtin_bit_cast(uint2, ll);
+      }
+      // ---- S <- post * (mid * S_pre + (KT plane)^T U)
+#pragma unroll
+      for (int tt = 0; tt < ST; ++tt) {
+        const float4 mid = *reinterpret_cast<const float4 *>(s_mid + 16 * tt + 4 * gq);
+        const float4 post = *reinterpret_cast<const float4 *>(s_post + 16 * tt + 4 * gq);
+        f32x4 a = accS[tt];
+        a[0] *= mid.x; a[1] *= mid.y; a[2] *= mid.z; a[3] *= mid.w;
+#pragma unroll
+        for (int J = 0; J < 4; ++J)
+          a = mfma16x3(a, frag16(kt_h, C, 16 * tt + l16, 16 * J, gq),
+                       frag16(kt_l, C, 16 * tt + l16, 16 * J, gq), uh[J], ul[J]);
+        a[0] *= post.x; a[1] *= post.y; a[2] *= post.z; a[3] *= post.w;
+        accS[tt] = a;
       }
     }
-
-    // ===================== P5: off-diagonal blocks of T, three levels.
-    // T_IJ (I > J) is stored in the free upper block (J, I) of the A/T buffer.
-    auto Tdiag = [&](int I, int a, int bb) { return s_A[(16 * I + a) * RTS + 16 * I + bb]; };
-    auto Toff = [&](int I, int J, int a, int bb) { return s_A[(16 * J + a) * RTS + 16 * I + bb]; };
-    auto Aof = [&](int I, int J, int a, int bb) { return s_A[(16 * I + a) * RTS + 16 * J + bb]; };
-#pragma unroll 1
-    for (int lev = 1; lev <= 3; ++lev) {
-      const int ntile = 4 - lev;
-      for (int x = t; x < ntile * 256; x += NT) {
-        const int J = x >> 8, a = (x >> 4) & 15, bb = x & 15, I = J + lev;
-        float z = 0.f;
-        for (int M = J; M < I; ++M)
-#pragma unroll
-          for (int m = 0; m < 16; ++m)
-            z += Aof(I, M, a, m) * (M == J ? Tdiag(J, m, bb) : Toff(M, J, m, bb));
-        s_Z[x] = z;
-      }
-      __syncthreads();
-      for (int x = t; x < ntile * 256; x += NT) {
-        const int J = x >> 8, a = (x >> 4) & 15, bb = x & 15, I = J + lev;
-        float s = 0.f;
-#pragma unroll
-        for (int m = 0; m < 16; ++m) s += Tdiag(I, a, m) * s_Z[(J << 8) + (m << 4) + bb];
-        s_A[(16 * J + a) * RTS + 16 * I + bb] = -s;
-      }
-      __syncthreads();
-    }
-    // T Diag(beta) -> hi/lo planes (zero above the diagonal)
-    {
-      const int i = t >> 2, j0 = (t & 3) * 16, I = i >> 4, a = i & 15;
-#pragma unroll
-      for (int u = 0; u < 16; u += 4) {
-        __bf16 hh[4], ll[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = j0 + u + e, J = j >> 4, bb = j & 15;
-          float tv = 0.f;
-          if (J == I) tv = bb <= a ? Tdiag(I, a, bb) : 0.f;
-          else if (J < I) tv = Toff(I, J, a, bb);
-          tv *= s_beta[j];
-          hh[e] = (__bf16)tv;
-          ll[e] = (__bf16)(tv - (float)hh[e]);
-        }
-        *reinterpret_cast<uint2 *>(p_tb_h + bfat(i, j0 + u, C)) = __builtin_bit_cast(uint2, hh);
-        *reinterpret_cast<uint2 *>(p_tb_l + bfat(i, j0 + u, C)) = __builtin_bit_cast(uint2, ll);
-      }
-    }
-    __syncthreads();   // B5
-
-    // ===================== state pass (each wave: 16 columns, all tokens)
-    unsigned short cur_v[4][4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) cur_v[mt][e] = in_v[mt][e];
-    if (lc + 1 < nch) load_chunk(lc + 1);     // prefetch the next chunk
-
-    bf16x8 sh[KB], sl[KB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) frag_from_acc(accS[2 * kb], accS[2 * kb + 1], sh[kb], sl[kb]);
-
-    // X = V - (gamma K) S
-    f32x4 accX[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        accX[mt][e] = __bfloat162float(__builtin_bit_cast(__hip_bfloat16, cur_v[mt][e]));
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const bf16x8 ah = frag_acc_order(p_gk_h, DK, 16 * mt + l16, kb, gq);
-        const bf16x8 al = frag_acc_order(p_gk_l, DK, 16 * mt + l16, kb, gq);
-        accX[mt] = mfma3(accX[mt], ah, al, sh[kb], sl[kb]);
-      }
-    }
-    bf16x8 xh[2], xl[2];
-    frag_from_acc(accX[0], accX[1], xh[0], xl[0]);
-    frag_from_acc(accX[2], accX[3], xh[1], xl[1]);
-
-    // U = T Diag(beta) X   (lower triangular: row tile mt needs k blocks <= mt/2)
-    f32x4 accU[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      accU[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb <= (mt >> 1); ++kb) {
-        const bf16x8 ah = frag_acc_order(p_tb_h, C, 16 * mt + l16, kb, gq);
-        const bf16x8 al = frag_acc_order(p_tb_l, C, 16 * mt + l16, kb, gq);
-        accU[mt] = mfma3(accU[mt], ah, al, xh[kb], xl[kb]);
-      }
-    }
-    bf16x8 uh[2], ul[2];
-    frag_from_acc(accU[0], accU[1], uh[0], ul[0]);
-    frag_from_acc(accU[2], accU[3], uh[1], ul[1]);
-
-    // O = (gamma Q) S + P U
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const bf16x8 ah = frag_acc_order(p_gq_h, DK, 16 * mt + l16, kb, gq);
-        const bf16x8 al = frag_acc_order(p_gq_l, DK, 16 * mt + l16, kb, gq);
-        acc = mfma3(acc, ah, al, sh[kb], sl[kb]);
-      }
-#pragma unroll
-      for (int kb = 0; kb <= (mt >> 1); ++kb) {
-        const bf16x8 ah = frag_acc_order(p_p_h, C, 16 * mt + l16, kb, gq);
-        const bf16x8 al = frag_acc_order(p_p_l, C, 16 * mt + l16, kb, gq);
-        acc = mfma3(acc, ah, al, uh[kb], ul[kb]);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 16 * mt + 4 * gq + e;
-        if (i < nt) o[((size_t)(t0 + i) * H + h) * DV + col] = acc[e];
-      }
-    }
-
-    // S <- Diag(gamma_n) S + K_hat^T U
-#pragma unroll
-    for (int tt = 0; tt < ST; ++tt) {
-      const float4 gn = *reinterpret_cast<const float4 *>(s_GN + 16 * tt + 4 * gq);
-      accS[tt][0] *= gn.x; accS[tt][1] *= gn.y; accS[tt][2] *= gn.z; accS[tt][3] *= gn.w;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 ah = frag_acc_order(p_kh_h, C, 16 * tt + l16, kb, gq);
-        const bf16x8 al = frag_acc_order(p_kh_l, C, 16 * tt + l16, kb, gq);
-        accS[tt] = mfma3(accS[tt], ah, al, uh[kb], ul[kb]);
-      }
-    }
-    __syncthreads();   // B6: LDS operands are rewritten by the next chunk
   }
 
-  if (S_T) {
+  if (!prep && S_T) {
+    const int lane = threadIdx.x & 63, l16 = lane & 15, gq = lane >> 4;
+    const int col = vb * BV + 16 * w + l16;
 #pragma unroll
     for (int tt = 0; tt < ST; ++tt)
 #pragma unroll
@@ -694,8 +726,6 @@ hipError_t launch_dk(const void *q, const void *k, const void *v, const float *g
 }
 
 }  // namespace
-
-size_t fwd_bf16_lds_bytes(int dk) { return dk == 64 ? Lds<64>::SIZE : Lds<128>::SIZE; }
 
 hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, const float *g,
                            const float *beta, const float *S0, float *o, float *S_T, int T, int H,
