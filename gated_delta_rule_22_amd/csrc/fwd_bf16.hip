@@ -484,6 +484,13 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
             }
           }
         }
+        // P's blocks (0,1) and (2,3) are read by the 32-token P U products: zero them
+        {
+          const int blk2 = tid >> 7, e = (tid & 127) * 2;     // 2 blocks x 128 threads x 2
+          const int i = 32 * blk2 + (e >> 4), j = 32 * blk2 + 16 + (e & 15);
+          *reinterpret_cast<uint32_t *>(p_h + at(i, j, C)) = 0u;
+          *reinterpret_cast<uint32_t *>(p_l + at(i, j, C)) = 0u;
+        }
       } else {
         // ---- exact path, part 2: A and P element by element (|2^(G_i - G_j)|
         // <= 1 for |alpha| <= 1) into registers, the diagonal A tiles,
@@ -652,17 +659,24 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
       }
       __syncthreads();   // H4
 
-      // ---- (I + A) U = Diag(beta) X by block forward substitution
+      // ---- (I + A) U = Diag(beta) X by block forward substitution.  U's hi/lo
+      // parts are kept per 16-token block (the B operand of a 16x16x16 product);
+      // two consecutive blocks side by side form the 32-token B operand in the
+      // accumulator k order of the 16x16x32 products.
       bf16x4 uh[4], ul[4];
+      auto u32h = [&](int kb) { return __builtin_shufflevector(uh[2 * kb], uh[2 * kb + 1], 0, 1, 2, 3, 4, 5, 6, 7); };
+      auto u32l = [&](int kb) { return __builtin_shufflevector(ul[2 * kb], ul[2 * kb + 1], 0, 1, 2, 3, 4, 5, 6, 7); };
 #pragma unroll
       for (int I = 0; I < 4; ++I) {
         f32x4 y;
 #pragma unroll
         for (int e = 0; e < 4; ++e) y[e] = s_beta[16 * I + 4 * gq + e] * accX[I][e];
-#pragma unroll
-        for (int J = 0; J < I; ++J)
-          y = mfma16x3(y, frag16(at_h, C, 16 * I + l16, 16 * J, gq),
-                       frag16(at_l, C, 16 * I + l16, 16 * J, gq), uh[J], ul[J]);
+        if (I >= 2)
+          y = mfma32x3(y, frag32(at_h, C, 16 * I + l16, 0, gq), frag32(at_l, C, 16 * I + l16, 0, gq),
+                       u32h(0), u32l(0));
+        if (I & 1)
+          y = mfma16x3(y, frag16(at_h, C, 16 * I + l16, 16 * (I - 1), gq),
+                       frag16(at_l, C, 16 * I + l16, 16 * (I - 1), gq), uh[I - 1], ul[I - 1]);
         bf16x4 yh, yl;
         split4(y, yh, yl);
         f32x4 u = {0.f, 0.f, 0.f, 0.f};
@@ -670,13 +684,13 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
                      frag16(at_l, C, 16 * I + l16, 16 * I, gq), yh, yl);
         split4(u, uh[I], ul[I]);
       }
-      // ---- O += P U ; store
+      // ---- O += P U ; store   (P is zero above its diagonal blocks)
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
-        for (int J = 0; J <= mt; ++J)
-          accO[mt] = mfma16x3(accO[mt], frag16(p_h, C, 16 * mt + l16, 16 * J, gq),
-                              frag16(p_l, C, 16 * mt + l16, 16 * J, gq), uh[J], ul[J]);
+        for (int kb = 0; kb <= (mt >> 1); ++kb)
+          accO[mt] = mfma32x3(accO[mt], frag32(p_h, C, 16 * mt + l16, kb, gq),
+                              frag32(p_l, C, 16 * mt + l16, kb, gq), u32h(kb), u32l(kb));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 16 * mt + 4 * gq + e;
@@ -691,9 +705,9 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
         f32x4 a = accS[tt];
         a[0] *= mid.x; a[1] *= mid.y; a[2] *= mid.z; a[3] *= mid.w;
 #pragma unroll
-        for (int J = 0; J < 4; ++J)
-          a = mfma16x3(a, frag16(kt_h, C, 16 * tt + l16, 16 * J, gq),
-                       frag16(kt_l, C, 16 * tt + l16, 16 * J, gq), uh[J], ul[J]);
+        for (int kb = 0; kb < 2; ++kb)
+          a = mfma32x3(a, frag32(kt_h, C, 16 * tt + l16, kb, gq),
+                       frag32(kt_l, C, 16 * tt + l16, kb, gq), u32h(kb), u32l(kb));
         a[0] *= post.x; a[1] *= post.y; a[2] *= post.z; a[3] *= post.w;
         accS[tt] = a;
       }
