@@ -56,6 +56,8 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int C = kChunk;        // 64 tokens per chunk
 constexpr int NT = 512;          // 8 waves per workgroup
@@ -106,6 +108,22 @@ __device__ __forceinline__ void split8_acc(const f32x4 &t0, const f32x4 &t1, bf1
     l[e + 4] = (__bf16)(t1[e] - (float)b1);
   }
 }
+// hi/lo split of four fp32 values into packed bf16 pairs (round to nearest
+// even on both parts): x = hi + lo + O(2^-17 |x|).
+__device__ __forceinline__ void split_quad(const float (&x)[4], uint2 &h, uint2 &l) {
+  uint32_t hw[2], lw[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const bf16x2 hp = __builtin_convertvector((f32x2){x[2 * p], x[2 * p + 1]}, bf16x2);
+    const uint32_t hb = __builtin_bit_cast(uint32_t, hp);
+    const float r0 = x[2 * p] - __builtin_bit_cast(float, hb << 16);
+    const float r1 = x[2 * p + 1] - __builtin_bit_cast(float, hb & 0xFFFF0000u);
+    hw[p] = hb;
+    lw[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){r0, r1}, bf16x2));
+  }
+  h = make_uint2(hw[0], hw[1]);
+  l = make_uint2(lw[0], lw[1]);
+}
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float flog2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float with_sign(float x, uint32_t odd) {
@@ -128,11 +146,11 @@ struct Lds {
   static constexpr int GK = 0;                            // -(gamma K)       [C][DK]
   static constexpr int GQ = GK + PQ;                      // gamma Q          [C][DK]
   static constexpr int KT = GQ + PQ;                      // (K/gamma)^T      [DK][C]
-  static constexpr int KG = KT + PT;                      // K/gamma [C][DK]; then P and AT
-  static constexpr int P = KG;                            // P                [C][C]
-  static constexpr int AT = P + PC;                       // -A below, T_II on the diagonal
+  static constexpr int P = KT + PT;                       // P                [C][C]
+  static constexpr int KG = P + PC;                       // K/gamma [C][DK]; then AT
+  static constexpr int AT = KG;                           // -A below, T_II on the diagonal
   static constexpr int FG = C * DK * 4;                   // exact path: G fp32 [C][DK]
-  static constexpr int KG_BYTES = mx(mx(PQ, 2 * PC), FG + DK * 8);
+  static constexpr int KG_BYTES = mx(mx(PQ, PC), FG + DK * 8);
   static constexpr int AD = KG + KG_BYTES;                // diagonal A tiles fp32 [4][16][17]
   static constexpr int BT = AD + 4 * 16 * ADS * 4;        // beta [C]
   static constexpr int SPRE = BT + C * 4;                 // S_pre = pre * S          [DK]
@@ -230,117 +248,132 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
   float pre4[4], post4[4];
   uint32_t guard_bad = 0;
 
+  // Next-chunk prefetch: every lane loads unconditionally from a row clamped to
+  // the sequence's last token (no branches, so the loads stay in flight); the
+  // padding rows past the sequence end are masked where the values are used.
   auto sp_load_v = [&](int lc, int tpin) {
-    const int lane = tpin & 63, l16 = lane & 15, gq = lane >> 4;
-    const int col = vb * BV + 16 * (tpin >> 6) + l16;
-    const int t0 = start + lc * C, nt = min(C, len - lc * C);
+    const int lane = tpin & 63, gq = lane >> 4;
+    const int col = vb * BV + 16 * (tpin >> 6) + (lane & 15);
+    const int t0 = start + lc * C, last = start + len - 1;
     const unsigned short *vv = reinterpret_cast<const unsigned short *>(v);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int i = 16 * mt + 4 * gq + e;
-        in_v[mt][e] = i < nt ? vv[((size_t)(t0 + i) * H + h) * DV + col] : (unsigned short)0;
+        const int t = min(t0 + 16 * mt + 4 * gq + e, last);
+        in_v[mt][e] = vv[((size_t)t * H + h) * DV + col];
       }
   };
   auto pr_load = [&](int lc, int tpin) {
     const int lane = tpin & 63, pw = (tpin >> 6) - 4;
     const int c0 = 4 * (pw * CQW + lane % CQW), i0 = (lane / CQW) * TPL;
-    const int t0 = start + lc * C, nt = min(C, len - lc * C);
+    const int t0 = start + lc * C, last = start + len - 1;
 #pragma unroll
     for (int r = 0; r < TPL; ++r) {
-      const int i = i0 + r;
-      if (i < nt) {
-        const size_t row = (size_t)(t0 + i) * H + h;
-        in_a[r] = *reinterpret_cast<const float4 *>(g + row * DK + c0);
-        in_k[r] = *reinterpret_cast<const uint2 *>(k + row * DK + c0);
-        in_q[r] = *reinterpret_cast<const uint2 *>(q + row * DK + c0);
-      } else {   // padding tokens: identity gate, zero key/query
-        in_a[r] = make_float4(1.f, 1.f, 1.f, 1.f);
-        in_k[r] = make_uint2(0u, 0u);
-        in_q[r] = make_uint2(0u, 0u);
-      }
+      const size_t row = (size_t)min(t0 + i0 + r, last) * H + h;
+      in_a[r] = *reinterpret_cast<const float4 *>(g + row * DK + c0);
+      in_k[r] = *reinterpret_cast<const uint2 *>(k + row * DK + c0);
+      in_q[r] = *reinterpret_cast<const uint2 *>(q + row * DK + c0);
     }
-    in_b = (pw == 0 && lane < nt) ? beta[(size_t)(t0 + lane) * H + h] : 0.f;
+    in_b = beta[(size_t)min(t0 + lane, last) * H + h];
   };
 
   // Register stage of chunk preparation: gate scan across the wave's lanes,
   // gamma'-scaled operands and their hi/lo split.  -(gamma' K) and gamma' Q go
   // straight to LDS (the state pass is done with those planes once H4 has
   // passed); K/gamma' is held for the hand-off.
-  auto pr_compute = [&]() {
+  //
+  // The running log-gate is kept as m = -G >= 0 with the gate-sign parity in
+  // the sign bit of the same fp32 word, so one word per (token, channel) holds
+  // both and |m| reads the magnitude for free.
+  auto pr_compute = [&](int nt_c) {
     int t_opaque = threadIdx.x;
     asm volatile("" : "+v"(t_opaque));
     const int lane = t_opaque & 63, tg = lane / CQW, cql = lane % CQW;
     const int pw = (t_opaque >> 6) - 4;
     const int c0 = 4 * (pw * CQW + cql), i0 = tg * TPL;
-    float Gl[TPL][4];
-    uint32_t pbits = 0;     // bit 4r+cc: in-lane inclusive parity of token r, channel cc
+    constexpr uint32_t kSign = 0x80000000u;
+    uint32_t nG[TPL][4];
+    {
+      float mag[4] = {0.f, 0.f, 0.f, 0.f};
+      uint32_t par[4] = {0u, 0u, 0u, 0u};
+      if (nt_c < C) {     // padding tokens: identity gate, zero key and query
 #pragma unroll
-    for (int r = 0; r < TPL; ++r) {
-      const float a4[4] = {in_a[r].x, in_a[r].y, in_a[r].z, in_a[r].w};
+        for (int r = 0; r < TPL; ++r)
+          if (i0 + r >= nt_c) {
+            in_a[r] = make_float4(1.f, 1.f, 1.f, 1.f);
+            in_k[r] = make_uint2(0u, 0u);
+            in_q[r] = make_uint2(0u, 0u);
+          }
+      }
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-        const float lg = fmaxf(flog2(fabsf(a4[cc])), kLog2Floor);
-        const uint32_t neg = a4[cc] < 0.f ? 1u : 0u;
-        const uint32_t prev = r ? (pbits >> (4 * (r - 1) + cc)) & 1u : 0u;
-        Gl[r][cc] = (r ? Gl[r - 1][cc] : 0.f) + lg;
-        pbits |= (prev ^ neg) << (4 * r + cc);
+      for (int r = 0; r < TPL; ++r) {
+        const float a4[4] = {in_a[r].x, in_a[r].y, in_a[r].z, in_a[r].w};
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+          mag[cc] -= fmaxf(flog2(fabsf(a4[cc])), kLog2Floor);
+          par[cc] ^= __builtin_bit_cast(uint32_t, a4[cc]);
+          // mag may be -0 (a lane of padding tokens): take its magnitude bits only
+          nG[r][cc] = (par[cc] & kSign) | (__builtin_bit_cast(uint32_t, mag[cc]) & ~kSign);
+        }
       }
     }
-    // inclusive scan of the lane totals over token groups (lanes CQW apart)
-    float incl[4] = {Gl[TPL - 1][0], Gl[TPL - 1][1], Gl[TPL - 1][2], Gl[TPL - 1][3]};
-    uint32_t pincl = (pbits >> (4 * (TPL - 1))) & 0xFu;
+    // inclusive scan of the lane totals over the token groups (lanes CQW apart):
+    // magnitudes add, parities xor
+    uint32_t incl[4] = {nG[TPL - 1][0], nG[TPL - 1][1], nG[TPL - 1][2], nG[TPL - 1][3]};
 #pragma unroll
     for (int d = 1; d < TGW; d <<= 1) {
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
-        const float y = __shfl_up(incl[cc], d * CQW);
-        if (tg >= d) incl[cc] += y;
+        const uint32_t y = __shfl_up(incl[cc], d * CQW);
+        if (tg >= d) {
+          const float m = fabsf(__builtin_bit_cast(float, incl[cc])) + fabsf(__builtin_bit_cast(float, y));
+          incl[cc] = ((incl[cc] ^ y) & kSign) | __builtin_bit_cast(uint32_t, m);
+        }
       }
-      const uint32_t yp = __shfl_up(pincl, d * CQW);
-      if (tg >= d) pincl ^= yp;
     }
-    float excl[4], R[4];
+    float base[4];
+    uint32_t exb[4];
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
-      const float y = __shfl_up(incl[cc], CQW);
-      excl[cc] = tg ? y : 0.f;
-      const float Gn = __shfl(incl[cc], (TGW - 1) * CQW + cql);
-      R[cc] = 0.5f * Gn;                 // per-channel reference, middle of [G_n, 0]
-      pre4[cc] = fexp2(R[cc]);
-      post4[cc] = fexp2(Gn - R[cc]);     // sign applied below
+      const uint32_t y = __shfl_up(incl[cc], CQW);
+      const uint32_t ex = tg ? y : 0u;
+      const uint32_t tot = __shfl(incl[cc], (TGW - 1) * CQW + cql);
+      const float half = 0.5f * fabsf(__builtin_bit_cast(float, tot));   // -R = -G_n / 2
+      // D = G - R = half - (|ex| + |m|);  pre = 2^R, post = (-1)^pi_n 2^(G_n - R): same magnitude
+      base[cc] = half - fabsf(__builtin_bit_cast(float, ex));
+      exb[cc] = ex;
+      const float e = fexp2(-half);
+      pre4[cc] = e;
+      post4[cc] = __builtin_bit_cast(float, (tot & kSign) | __builtin_bit_cast(uint32_t, e));
     }
-    const uint32_t pprev = __shfl_up(pincl, CQW);
-    const uint32_t pex = tg ? (pprev & 0xFu) : 0u;
-    const uint32_t pn = __shfl(pincl, (TGW - 1) * CQW + cql);
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) post4[cc] = with_sign(post4[cc], (pn >> cc) & 1u);
     float gmax = 0.f;
 #pragma unroll
     for (int r = 0; r < TPL; ++r) {
-      __bf16 hk[4], lk[4], hq[4], lq[4], hg[4], lgg[4];
+      float gk[4], gq[4], kg[4];
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
-        const float D = excl[cc] + Gl[r][cc] - R[cc];
-        const uint32_t odd = ((pex >> cc) ^ (pbits >> (4 * r + cc))) & 1u;
+        const float D = base[cc] - fabsf(__builtin_bit_cast(float, nG[r][cc]));
         gmax = fmaxf(gmax, fabsf(D));
-        const float gam = with_sign(fexp2(D), odd);
-        const float igam = with_sign(fexp2(-D), odd);
+        const uint32_t sgn = (nG[r][cc] ^ exb[cc]) & kSign;
+        const float gam = __builtin_bit_cast(float, sgn | __builtin_bit_cast(uint32_t, fexp2(D)));
+        const float igam = __builtin_bit_cast(float, sgn | __builtin_bit_cast(uint32_t, fexp2(-D)));
         const uint32_t kw = cc < 2 ? in_k[r].x : in_k[r].y, qw = cc < 2 ? in_q[r].x : in_q[r].y;
-        const float kk = bf16_to_f32((cc & 1) ? (kw >> 16) : (kw & 0xFFFFu));
-        const float qq = bf16_to_f32((cc & 1) ? (qw >> 16) : (qw & 0xFFFFu));
-        split1(-kk * gam, hk[cc], lk[cc]);
-        split1(qq * gam, hq[cc], lq[cc]);
-        split1(kk * igam, hg[cc], lgg[cc]);
+        const float kk = __builtin_bit_cast(float, (cc & 1) ? (kw & 0xFFFF0000u) : (kw << 16));
+        const float qq = __builtin_bit_cast(float, (cc & 1) ? (qw & 0xFFFF0000u) : (qw << 16));
+        gk[cc] = -kk * gam;
+        gq[cc] = qq * gam;
+        kg[cc] = kk * igam;
       }
       const int i = i0 + r;
-      *reinterpret_cast<uint2 *>(gk_h + at(i, c0, DK)) = __builtin_bit_cast(uint2, hk);
-      *reinterpret_cast<uint2 *>(gk_l + at(i, c0, DK)) = __builtin_bit_cast(uint2, lk);
-      *reinterpret_cast<uint2 *>(gq_h + at(i, c0, DK)) = __builtin_bit_cast(uint2, hq);
-      *reinterpret_cast<uint2 *>(gq_l + at(i, c0, DK)) = __builtin_bit_cast(uint2, lq);
-      o_kg_h[r] = __builtin_bit_cast(uint2, hg);
-      o_kg_l[r] = __builtin_bit_cast(uint2, lgg);
+      uint2 h, l;
+      split_quad(gk, h, l);
+      *reinterpret_cast<uint2 *>(gk_h + at(i, c0, DK)) = h;
+      *reinterpret_cast<uint2 *>(gk_l + at(i, c0, DK)) = l;
+      split_quad(gq, h, l);
+      *reinterpret_cast<uint2 *>(gq_h + at(i, c0, DK)) = h;
+      *reinterpret_cast<uint2 *>(gq_l + at(i, c0, DK)) = l;
+      split_quad(kg, o_kg_h[r], o_kg_l[r]);
       __builtin_amdgcn_sched_barrier(0);   // one token at a time: bounded live range
     }
     guard_bad = __any(gmax > kGuard) ? 1u : 0u;
@@ -353,17 +386,18 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
   // live only inside its own loop.
   if (prep) {
     // ======================= chunk preparation (waves 4-7)
-    float xA[(C * C) / 256], xP[(C * C) / 256];   // exact path: -A and P held over a barrier
+    float xA[6];        // exact path: the off-diagonal -A blocks, held over one barrier
     if (nch > 0) {
       pr_load(0, threadIdx.x);
-      pr_compute();
+      pr_compute(min(C, len));
     }
     for (int lc = 0; lc < nch; ++lc) {
       const int t0 = start + lc * C, nt = min(C, len - lc * C);
       int t_opaque = threadIdx.x;
       asm volatile("" : "+v"(t_opaque));
       const int lane = t_opaque & 63, l16 = lane & 15, gq = lane >> 4;
-      const int tid = t_opaque - 256, pw = tid >> 6;      // preparation thread / wave
+      const int tid = t_opaque - 256;                       // preparation thread
+      const int pw = __builtin_amdgcn_readfirstlane(tid >> 6);   // preparation wave (uniform)
       const int tg = lane / CQW, cql = lane % CQW;
       const int c0 = 4 * (pw * CQW + cql), i0 = tg * TPL;
 
@@ -401,7 +435,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
         *reinterpret_cast<float4 *>(s_post + c0) =
             make_float4(post4[0], post4[1], post4[2], post4[3]);
       }
-      if (pw == 0) s_beta[lane] = in_b;
+      if (pw == 0) s_beta[lane] = lane < nt ? in_b : 0.f;
       if (guard_bad && lane == 0) atomicOr(&s_flag[lc & 1], 1);
       if (lc + 1 < nch) pr_load(lc + 1, t_opaque);   // next chunk's inputs, in flight meanwhile
 
@@ -409,33 +443,57 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
       const int fallback = s_flag[lc & 1];
       f32x4 pA[3], pP[3];                      // A and P tiles, held over H3
       if (!fallback) {
-        // ---- A and P tiles (I, J), J <= I: row operands -(gamma K) / gamma Q of
-        // block I, column operand K/gamma of block J.  Tile pairs pw, pw+4, pw+8.
+        // ---- A and P tiles (I, J), J <= I, computed transposed: the MFMA's row
+        // operand is K/gamma' of block J, its column operand -(gamma' K) or
+        // gamma' Q of block I, so lane (g, l) ends up with row 16 I + l and the
+        // four consecutive columns 16 J + 4 g .. +3.  Tile pairs pw, pw+4, pw+8.
+        // (tile, kb) steps; the fragments of step st + 1 are read while step st's
+        // products run.  Waves 2 and 3 have two tiles, waves 0 and 1 three.
+        const int ntile = pw < 2 ? 3 : 2;
+        bf16x8 fa_h[2], fa_l[2], fk_h[2], fk_l[2], fq_h[2], fq_l[2];
+        auto ld = [&](int st) {
+          int I, J;
+          tile_of_pair(pw + 4 * (st / KB), I, J);
+          const int kb = st % KB, sl2 = st & 1;
+          fa_h[sl2] = frag32(kg_h, DK, 16 * J + l16, kb, gq);
+          fa_l[sl2] = frag32(kg_l, DK, 16 * J + l16, kb, gq);
+          fk_h[sl2] = frag32(gk_h, DK, 16 * I + l16, kb, gq);
+          fk_l[sl2] = frag32(gk_l, DK, 16 * I + l16, kb, gq);
+          fq_h[sl2] = frag32(gq_h, DK, 16 * I + l16, kb, gq);
+          fq_l[sl2] = frag32(gq_l, DK, 16 * I + l16, kb, gq);
+        };
 #pragma unroll
-        for (int s = 0; s < 3; ++s) {
-          const int pr = pw + 4 * s;
-          pA[s] = f32x4{0.f, 0.f, 0.f, 0.f};
-          pP[s] = f32x4{0.f, 0.f, 0.f, 0.f};
-          if (pr < 10) {
+        for (int t = 0; t < 3; ++t) {
+          pA[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+          pP[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        ld(0);
+#pragma unroll
+        for (int st = 0; st < 3 * KB; ++st) {
+          const int t = st / KB;
+          if (t < ntile) {
+            if (st + 1 < ntile * KB) ld(st + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            const int sl2 = st & 1;
+            pA[t] = mfma32x3(pA[t], fa_h[sl2], fa_l[sl2], fk_h[sl2], fk_l[sl2]);
+            pP[t] = mfma32x3(pP[t], fa_h[sl2], fa_l[sl2], fq_h[sl2], fq_l[sl2]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+          if (t < ntile) {
             int I, J;
-            tile_of_pair(pr, I, J);
+            tile_of_pair(pw + 4 * t, I, J);
+            // pA holds -A_ij / beta_i; scale by beta_i (row 16 I + l16) -> -A_ij
+            const float bi = s_beta[16 * I + l16];
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-              const bf16x8 bh = frag32(kg_h, DK, 16 * J + l16, kb, gq);
-              const bf16x8 bl = frag32(kg_l, DK, 16 * J + l16, kb, gq);
-              pA[s] = mfma32x3(pA[s], frag32(gk_h, DK, 16 * I + l16, kb, gq),
-                               frag32(gk_l, DK, 16 * I + l16, kb, gq), bh, bl);
-              pP[s] = mfma32x3(pP[s], frag32(gq_h, DK, 16 * I + l16, kb, gq),
-                               frag32(gq_l, DK, 16 * I + l16, kb, gq), bh, bl);
-            }
-            // pA holds -A_ij / beta_i; scale rows by beta_i -> -A_ij
-#pragma unroll
-            for (int e = 0; e < 4; ++e) pA[s][e] *= s_beta[16 * I + 4 * gq + e];
+            for (int e = 0; e < 4; ++e) pA[t][e] *= bi;
             if (I == J) {
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
-                const int a = 4 * gq + e;     // row within the block; the column is l16
-                s_ad[(I * 16 + a) * ADS + l16] = (l16 < a) ? -pA[s][e] : 0.f;
+                const int cl = 4 * gq + e;    // column within the block; the row is l16
+                s_ad[(I * 16 + l16) * ADS + cl] = (cl < l16) ? -pA[t][e] : 0.f;
               }
             }
           }
@@ -462,25 +520,26 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
 
       __syncthreads();   // H3
       if (!fallback) {
-        // -A below the diagonal blocks, P on and below them
+        // -A below the diagonal blocks, P on and below them: 8-byte stores
 #pragma unroll
         for (int s = 0; s < 3; ++s) {
           const int pr = pw + 4 * s;
           if (pr < 10) {
             int I, J;
             tile_of_pair(pr, I, J);
+            const int i = 16 * I + l16, j = 16 * J + 4 * gq;
+            float pv[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int a = 4 * gq + e, i = 16 * I + a, j = 16 * J + l16;
-              __bf16 hh, ll;
-              if (J < I) {
-                split1(pA[s][e], hh, ll);
-                at_h[at(i, j, C)] = hh;
-                at_l[at(i, j, C)] = ll;
-              }
-              split1((J < I || l16 <= a) ? pP[s][e] : 0.f, hh, ll);
-              p_h[at(i, j, C)] = hh;
-              p_l[at(i, j, C)] = ll;
+            for (int e = 0; e < 4; ++e) pv[e] = (J < I || 4 * gq + e <= l16) ? pP[s][e] : 0.f;
+            uint2 hh, ll;
+            split_quad(pv, hh, ll);
+            *reinterpret_cast<uint2 *>(p_h + at(i, j, C)) = hh;
+            *reinterpret_cast<uint2 *>(p_l + at(i, j, C)) = ll;
+            if (J < I) {
+              const float av[4] = {pA[s][0], pA[s][1], pA[s][2], pA[s][3]};
+              split_quad(av, hh, ll);
+              *reinterpret_cast<uint2 *>(at_h + at(i, j, C)) = hh;
+              *reinterpret_cast<uint2 *>(at_l + at(i, j, C)) = ll;
             }
           }
         }
@@ -503,10 +562,11 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
           const uint2 m = s_pm[c];
           return ((i < 32 ? m.x : m.y) >> (i & 31)) & 1u;
         };
-#pragma unroll
-        for (int u = 0; u < (C * C) / 256; ++u) {
-          const int pp = tid + 256 * u, i = pp / C, j = pp % C;
-          float accA = 0.f, accP = 0.f;
+        // one (i, j) element per thread and step; returns sum_c k_i,c r_ij,c x_j,c
+        // for x = k (A) and the query's row for P
+        auto exact_pair = [&](int i, int j, float &accA, float &accP) {
+          accA = 0.f;
+          accP = 0.f;
           if (j <= i && i < nt) {
             const size_t ri = (size_t)(t0 + i) * H + h, rj = (size_t)(t0 + j) * H + h;
             for (int c = 0; c < DK; ++c) {
@@ -517,10 +577,29 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
               accP += __bfloat162float(q[ri * DK + c]) * kj;
             }
           }
-          const float Aij = (j < i) ? s_beta[i] * accA : 0.f;
-          if ((i >> 4) == (j >> 4)) s_ad[((i >> 4) * 16 + (i & 15)) * ADS + (j & 15)] = Aij;
-          xA[u] = -Aij;
-          xP[u] = (j <= i) ? accP : 0.f;
+        };
+        // P (all of it, zero above the diagonal) and the diagonal A tiles go
+        // straight to LDS; the six off-diagonal -A blocks wait in registers
+        // until the G table is dead.
+        for (int u = 0; u < (C * C) / 256; ++u) {
+          const int pp = tid + 256 * u, i = pp / C, j = pp % C;
+          float accA, accP;
+          exact_pair(i, j, accA, accP);
+          __bf16 hh, ll;
+          split1(accP, hh, ll);
+          p_h[at(i, j, C)] = hh;
+          p_l[at(i, j, C)] = ll;
+          if ((i >> 4) == (j >> 4))
+            s_ad[((i >> 4) * 16 + (i & 15)) * ADS + (j & 15)] = (j < i) ? s_beta[i] * accA : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 6; ++u) {
+          int I, J;
+          tile_of_pair(u < 1 ? 1 : u < 3 ? u + 2 : u + 3, I, J);   // (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+          const int i = 16 * I + (tid >> 4), j = 16 * J + (tid & 15);
+          float accA, accP;
+          exact_pair(i, j, accA, accP);
+          xA[u] = -s_beta[i] * accA;
         }
         for (int pp = tid; pp < DK * C; pp += 256) {
           const int c = pp / C, j = pp % C;
@@ -558,26 +637,21 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
           s_mid[c] = with_sign(fexp2(s_G[(C - 1) * DK + c]), par_of(C - 1, c));
           s_post[c] = 1.f;
         }
-        __syncthreads();   // every thread is done reading G: its region takes A and P
-        {
+        __syncthreads();   // every thread is done reading G: its region takes -A
 #pragma unroll
-          for (int u = 0; u < (C * C) / 256; ++u) {
-            const int pp = tid + 256 * u, i = pp / C, j = pp % C;
-            __bf16 hh, ll;
-            if ((i >> 4) > (j >> 4)) {
-              split1(xA[u], hh, ll);
-              at_h[at(i, j, C)] = hh;
-              at_l[at(i, j, C)] = ll;
-            }
-            split1(xP[u], hh, ll);
-            p_h[at(i, j, C)] = hh;
-            p_l[at(i, j, C)] = ll;
-          }
+        for (int u = 0; u < 6; ++u) {
+          int I, J;
+          tile_of_pair(u < 1 ? 1 : u < 3 ? u + 2 : u + 3, I, J);
+          const int i = 16 * I + (tid >> 4), j = 16 * J + (tid & 15);
+          __bf16 hh, ll;
+          split1(xA[u], hh, ll);
+          at_h[at(i, j, C)] = hh;
+          at_l[at(i, j, C)] = ll;
         }
         __syncthreads();   // diagonal A tiles complete for the inverses
       }
       __syncthreads();   // H4
-      if (lc + 1 < nch) pr_compute();     // next chunk's operands, overlapping the state pass
+      if (lc + 1 < nch) pr_compute(min(C, len - (lc + 1) * C));   // overlaps the state pass
     }
   } else {
     // ======================= state pass (waves 0-3)
@@ -618,15 +692,31 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) accX[mt][e] = bf16_to_f32(in_v[mt][e]);
+          for (int e = 0; e < 4; ++e)
+            accX[mt][e] = 16 * mt + 4 * gq + e < nt ? bf16_to_f32(in_v[mt][e]) : 0.f;
           accO[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        // 4 KB steps (mt, kb); the row fragments of step st + 2 are read while
+        // step st's products run (a ring of three register slots)
+        constexpr int NS = 4 * KB;
+        bf16x8 rk_h[3], rk_l[3], rq_h[3], rq_l[3];
+        auto ld = [&](int st) {
+          const int mt = st / KB, kb = st % KB, sl3 = st % 3;
+          rk_h[sl3] = frag32(gk_h, DK, 16 * mt + l16, kb, gq);
+          rk_l[sl3] = frag32(gk_l, DK, 16 * mt + l16, kb, gq);
+          rq_h[sl3] = frag32(gq_h, DK, 16 * mt + l16, kb, gq);
+          rq_l[sl3] = frag32(gq_l, DK, 16 * mt + l16, kb, gq);
+        };
+        ld(0);
+        ld(1);
 #pragma unroll
-          for (int kb = 0; kb < KB; ++kb) {
-            accX[mt] = mfma32x3(accX[mt], frag32(gk_h, DK, 16 * mt + l16, kb, gq),
-                                frag32(gk_l, DK, 16 * mt + l16, kb, gq), sh[kb], sl[kb]);
-            accO[mt] = mfma32x3(accO[mt], frag32(gq_h, DK, 16 * mt + l16, kb, gq),
-                                frag32(gq_l, DK, 16 * mt + l16, kb, gq), sh[kb], sl[kb]);
-          }
+        for (int st = 0; st < NS; ++st) {
+          if (st + 2 < NS) ld(st + 2);
+          __builtin_amdgcn_sched_barrier(0);
+          const int mt = st / KB, kb = st % KB, sl3 = st % 3;
+          accX[mt] = mfma32x3(accX[mt], rk_h[sl3], rk_l[sl3], sh[kb], sl[kb]);
+          accO[mt] = mfma32x3(accO[mt], rq_h[sl3], rq_l[sl3], sh[kb], sl[kb]);
+          __builtin_amdgcn_sched_barrier(0);
         }
         if (lc + 1 < nch) sp_load_v(lc + 1, t_opaque);
       };
@@ -662,54 +752,105 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
       // ---- (I + A) U = Diag(beta) X by block forward substitution.  U's hi/lo
       // parts are kept per 16-token block (the B operand of a 16x16x16 product);
       // two consecutive blocks side by side form the 32-token B operand in the
-      // accumulator k order of the 16x16x32 products.
+      // accumulator k order of the 16x16x32 products.  All of the solve's row
+      // fragments are read up front.
+      bf16x4 dh[4], dl[4], b1h, b1l, b3h, b3l;
+      bf16x8 c2h, c2l, c3h, c3l;
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        dh[I] = frag16(at_h, C, 16 * I + l16, 16 * I, gq);
+        dl[I] = frag16(at_l, C, 16 * I + l16, 16 * I, gq);
+      }
+      b1h = frag16(at_h, C, 16 + l16, 0, gq);
+      b1l = frag16(at_l, C, 16 + l16, 0, gq);
+      c2h = frag32(at_h, C, 32 + l16, 0, gq);
+      c2l = frag32(at_l, C, 32 + l16, 0, gq);
+      c3h = frag32(at_h, C, 48 + l16, 0, gq);
+      c3l = frag32(at_l, C, 48 + l16, 0, gq);
+      b3h = frag16(at_h, C, 48 + l16, 32, gq);
+      b3l = frag16(at_l, C, 48 + l16, 32, gq);
       bf16x4 uh[4], ul[4];
       auto u32h = [&](int kb) { return __builtin_shufflevector(uh[2 * kb], uh[2 * kb + 1], 0, 1, 2, 3, 4, 5, 6, 7); };
       auto u32l = [&](int kb) { return __builtin_shufflevector(ul[2 * kb], ul[2 * kb + 1], 0, 1, 2, 3, 4, 5, 6, 7); };
+      // P fragments for the first two O += P U steps, read during the solve
+      constexpr int kPuMt[6] = {0, 1, 2, 2, 3, 3}, kPuKb[6] = {0, 0, 0, 1, 0, 1};
+      bf16x8 rp_h[3], rp_l[3];
+      auto ldp = [&](int st) {
+        rp_h[st % 3] = frag32(p_h, C, 16 * kPuMt[st] + l16, kPuKb[st], gq);
+        rp_l[st % 3] = frag32(p_l, C, 16 * kPuMt[st] + l16, kPuKb[st], gq);
+      };
+      ldp(0);
+      ldp(1);
 #pragma unroll
       for (int I = 0; I < 4; ++I) {
         f32x4 y;
 #pragma unroll
         for (int e = 0; e < 4; ++e) y[e] = s_beta[16 * I + 4 * gq + e] * accX[I][e];
-        if (I >= 2)
-          y = mfma32x3(y, frag32(at_h, C, 16 * I + l16, 0, gq), frag32(at_l, C, 16 * I + l16, 0, gq),
-                       u32h(0), u32l(0));
-        if (I & 1)
-          y = mfma16x3(y, frag16(at_h, C, 16 * I + l16, 16 * (I - 1), gq),
-                       frag16(at_l, C, 16 * I + l16, 16 * (I - 1), gq), uh[I - 1], ul[I - 1]);
+        if (I == 1) y = mfma16x3(y, b1h, b1l, uh[0], ul[0]);
+        if (I == 2) y = mfma32x3(y, c2h, c2l, u32h(0), u32l(0));
+        if (I == 3) {
+          y = mfma32x3(y, c3h, c3l, u32h(0), u32l(0));
+          y = mfma16x3(y, b3h, b3l, uh[2], ul[2]);
+        }
         bf16x4 yh, yl;
         split4(y, yh, yl);
         f32x4 u = {0.f, 0.f, 0.f, 0.f};
-        u = mfma16x3(u, frag16(at_h, C, 16 * I + l16, 16 * I, gq),
-                     frag16(at_l, C, 16 * I + l16, 16 * I, gq), yh, yl);
+        u = mfma16x3(u, dh[I], dl[I], yh, yl);
         split4(u, uh[I], ul[I]);
       }
-      // ---- O += P U ; store   (P is zero above its diagonal blocks)
+      // ---- O += P U (P is zero above its diagonal blocks); store
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
+      for (int st = 0; st < 6; ++st) {
+        if (st + 2 < 6) ldp(st + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        const int mt = kPuMt[st], kb = kPuKb[st];
+        accO[mt] = mfma32x3(accO[mt], rp_h[st % 3], rp_l[st % 3], u32h(kb), u32l(kb));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      {
+        float *orow = o + ((size_t)t0 * H + h) * DV + col;
+        const size_t rs = (size_t)H * DV;
+        if (nt == C) {
 #pragma unroll
-        for (int kb = 0; kb <= (mt >> 1); ++kb)
-          accO[mt] = mfma32x3(accO[mt], frag32(p_h, C, 16 * mt + l16, kb, gq),
-                              frag32(p_l, C, 16 * mt + l16, kb, gq), u32h(kb), u32l(kb));
+          for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 16 * mt + 4 * gq + e;
-          if (i < nt) o[((size_t)(t0 + i) * H + h) * DV + col] = accO[mt][e];
+            for (int e = 0; e < 4; ++e) orow[(16 * mt + 4 * gq + e) * rs] = accO[mt][e];
+        } else {
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (16 * mt + 4 * gq + e < nt) orow[(16 * mt + 4 * gq + e) * rs] = accO[mt][e];
         }
       }
-      // ---- S <- post * (mid * S_pre + (KT plane)^T U)
+      // ---- S <- post * (mid * S_pre + (KT plane)^T U): 2 ST steps (tile, kb),
+      // fragments read two steps ahead
+      {
+        constexpr int NS = 2 * ST;
+        bf16x8 rt_h[3], rt_l[3];
+        auto ld = [&](int st) {
+          const int tt = st >> 1, kb = st & 1, sl3 = st % 3;
+          rt_h[sl3] = frag32(kt_h, C, 16 * tt + l16, kb, gq);
+          rt_l[sl3] = frag32(kt_l, C, 16 * tt + l16, kb, gq);
+        };
+        ld(0);
+        ld(1);
 #pragma unroll
-      for (int tt = 0; tt < ST; ++tt) {
-        const float4 mid = *reinterpret_cast<const float4 *>(s_mid + 16 * tt + 4 * gq);
-        const float4 post = *reinterpret_cast<const float4 *>(s_post + 16 * tt + 4 * gq);
-        f32x4 a = accS[tt];
-        a[0] *= mid.x; a[1] *= mid.y; a[2] *= mid.z; a[3] *= mid.w;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          a = mfma32x3(a, frag32(kt_h, C, 16 * tt + l16, kb, gq),
-                       frag32(kt_l, C, 16 * tt + l16, kb, gq), u32h(kb), u32l(kb));
-        a[0] *= post.x; a[1] *= post.y; a[2] *= post.z; a[3] *= post.w;
-        accS[tt] = a;
+        for (int st = 0; st < NS; ++st) {
+          if (st + 2 < NS) ld(st + 2);
+          __builtin_amdgcn_sched_barrier(0);
+          const int tt = st >> 1, kb = st & 1, sl3 = st % 3;
+          if (kb == 0) {
+            const float4 mid = *reinterpret_cast<const float4 *>(s_mid + 16 * tt + 4 * gq);
+            accS[tt][0] *= mid.x; accS[tt][1] *= mid.y; accS[tt][2] *= mid.z; accS[tt][3] *= mid.w;
+          }
+          accS[tt] = mfma32x3(accS[tt], rt_h[sl3], rt_l[sl3], u32h(kb), u32l(kb));
+          if (kb == 1) {
+            const float4 post = *reinterpret_cast<const float4 *>(s_post + 16 * tt + 4 * gq);
+            accS[tt][0] *= post.x; accS[tt][1] *= post.y; accS[tt][2] *= post.z; accS[tt][3] *= post.w;
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
   }
