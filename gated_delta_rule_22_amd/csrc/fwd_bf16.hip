@@ -63,9 +63,11 @@ constexpr int C = kChunk;        // 64 tokens per chunk
 constexpr int NT = 512;          // 8 waves per workgroup
 constexpr int BV = 64;           // dv columns per workgroup (16 per state-pass wave)
 constexpr int PADB = 4;          // bf16 plane row padding (elements)
-constexpr int ADS = 17;          // row stride of the fp32 diagonal A tiles
+constexpr int ADS = 20;          // row stride of the fp32 diagonal A tiles (16-byte rows)
+constexpr int ADB = 16 * ADS + 4; // block stride: the four blocks start on different banks
 constexpr float kLog2Floor = -126.f;
 constexpr float kGuard = 100.f;  // |G - R| bound for the factored A and P
+constexpr int kBufferFlags = 0x00020000;   // buffer resource word 3: raw 32-bit data
 
 __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -151,8 +153,8 @@ struct Lds {
   static constexpr int AT = KG;                           // -A below, T_II on the diagonal
   static constexpr int FG = C * DK * 4;                   // exact path: G fp32 [C][DK]
   static constexpr int KG_BYTES = mx(mx(PQ, PC), FG + DK * 8);
-  static constexpr int AD = KG + KG_BYTES;                // diagonal A tiles fp32 [4][16][17]
-  static constexpr int BT = AD + 4 * 16 * ADS * 4;        // beta [C]
+  static constexpr int AD = KG + KG_BYTES;                // diagonal A tiles fp32 [4][16][20]
+  static constexpr int BT = AD + 4 * ADB * 4;             // beta [C]
   static constexpr int SPRE = BT + C * 4;                 // S_pre = pre * S          [DK]
   static constexpr int SMID = SPRE + DK * 4;              // S' = post * (mid * S_pre  [DK]
   static constexpr int SPOST = SMID + DK * 4;             //      + (KT plane)^T U)    [DK]
@@ -248,34 +250,42 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
   float pre4[4], post4[4];
   uint32_t guard_bad = 0;
 
-  // Next-chunk prefetch: every lane loads unconditionally from a row clamped to
-  // the sequence's last token (no branches, so the loads stay in flight); the
-  // padding rows past the sequence end are masked where the values are used.
+  // Global traffic goes through buffer resources based at a chunk's first
+  // token row, with num_records ending at the sequence's last row of this head:
+  // rows past the sequence end read as zero and writes to them are dropped, so
+  // no lane branches or clamps, and per-token offsets stay 32-bit.
+  auto rsrc = [&](const void *p, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, bytes, kBufferFlags);
+  };
   auto sp_load_v = [&](int lc, int tpin) {
     const int lane = tpin & 63, gq = lane >> 4;
     const int col = vb * BV + 16 * (tpin >> 6) + (lane & 15);
-    const int t0 = start + lc * C, last = start + len - 1;
-    const unsigned short *vv = reinterpret_cast<const unsigned short *>(v);
+    const int t0 = start + lc * C, nt = min(C, len - lc * C);
+    const int rs = H * DV * 2;
+    const auto rv = rsrc(v + ((size_t)t0 * H + h) * DV, (nt - 1) * rs + DV * 2);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = min(t0 + 16 * mt + 4 * gq + e, last);
-        in_v[mt][e] = vv[((size_t)t * H + h) * DV + col];
-      }
+      for (int e = 0; e < 4; ++e)
+        in_v[mt][e] = __builtin_amdgcn_raw_buffer_load_b16(rv, (16 * mt + 4 * gq + e) * rs + 2 * col, 0, 0);
   };
   auto pr_load = [&](int lc, int tpin) {
     const int lane = tpin & 63, pw = (tpin >> 6) - 4;
     const int c0 = 4 * (pw * CQW + lane % CQW), i0 = (lane / CQW) * TPL;
-    const int t0 = start + lc * C, last = start + len - 1;
+    const int t0 = start + lc * C, nt = min(C, len - lc * C);
+    const size_t row0 = (size_t)t0 * H + h;
+    const int rsg = H * DK * 4, rsk = H * DK * 2;
+    const auto rg = rsrc(g + row0 * DK, (nt - 1) * rsg + DK * 4);
+    const auto rk = rsrc(k + row0 * DK, (nt - 1) * rsk + DK * 2);
+    const auto rq = rsrc(q + row0 * DK, (nt - 1) * rsk + DK * 2);
 #pragma unroll
     for (int r = 0; r < TPL; ++r) {
-      const size_t row = (size_t)min(t0 + i0 + r, last) * H + h;
-      in_a[r] = *reinterpret_cast<const float4 *>(g + row * DK + c0);
-      in_k[r] = *reinterpret_cast<const uint2 *>(k + row * DK + c0);
-      in_q[r] = *reinterpret_cast<const uint2 *>(q + row * DK + c0);
+      in_a[r] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rg, (i0 + r) * rsg + 4 * c0, 0, 0));
+      in_k[r] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rk, (i0 + r) * rsk + 2 * c0, 0, 0));
+      in_q[r] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rq, (i0 + r) * rsk + 2 * c0, 0, 0));
     }
-    in_b = beta[(size_t)min(t0 + lane, last) * H + h];
+    const auto rb = rsrc(beta + row0, (nt - 1) * H * 4 + 4);
+    in_b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, lane * H * 4, 0, 0));
   };
 
   // Register stage of chunk preparation: gate scan across the wave's lanes,
@@ -489,12 +499,10 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
             const float bi = s_beta[16 * I + l16];
 #pragma unroll
             for (int e = 0; e < 4; ++e) pA[t][e] *= bi;
-            if (I == J) {
+            if (I == J) {     // A_II transposed, zero on and above the diagonal
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const int cl = 4 * gq + e;    // column within the block; the row is l16
-                s_ad[(I * 16 + l16) * ADS + cl] = (cl < l16) ? -pA[t][e] : 0.f;
-              }
+              for (int e = 0; e < 4; ++e)
+                s_ad[I * ADB + (4 * gq + e) * ADS + l16] = 4 * gq + e < l16 ? -pA[t][e] : 0.f;
             }
           }
         }
@@ -590,7 +598,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
           p_h[at(i, j, C)] = hh;
           p_l[at(i, j, C)] = ll;
           if ((i >> 4) == (j >> 4))
-            s_ad[((i >> 4) * 16 + (i & 15)) * ADS + (j & 15)] = (j < i) ? s_beta[i] * accA : 0.f;
+            s_ad[(i >> 4) * ADB + (j & 15) * ADS + (i & 15)] = (j < i) ? s_beta[i] * accA : 0.f;
         }
 #pragma unroll
         for (int u = 0; u < 6; ++u) {
@@ -729,20 +737,33 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
         x_and_o();
       }
       if ((t_opaque >> 6) == 0) {
-        // (I + A_II)^-1 for the four diagonal blocks by right-looking forward
-        // substitution; lane = 16 I + column j.
+        // (I + A_II)^-1 for the four diagonal blocks, column j of block I per lane,
+        // by right-looking forward substitution: once x_m is final it is
+        // subtracted from every later row.  A_II is stored transposed, so the
+        // entries below x_m are one row of the store, read four at a time; no
+        // read depends on x, so all of them can be in flight early.
         const int I = lane >> 4, j = lane & 15;
-        float acc[16];
+        const float *adb = s_ad + I * ADB;
+        float x[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[i] = (i == j) ? 1.f : 0.f;
+        for (int i = 0; i < 16; ++i) x[i] = (i == j) ? 1.f : 0.f;
 #pragma unroll
-        for (int m = 0; m < 16; ++m)
+        for (int m = 0; m < 15; ++m) {
+          float4 r[4];
 #pragma unroll
-          for (int i = m + 1; i < 16; ++i) acc[i] -= s_ad[(I * 16 + i) * ADS + m] * acc[m];
+          for (int q4 = (m + 1) / 4; q4 < 4; ++q4)
+            r[q4] = *reinterpret_cast<const float4 *>(adb + m * ADS + 4 * q4);
+#pragma unroll
+          for (int i = m + 1; i < 16; ++i) {
+            const float4 &rq = r[i / 4];
+            const float a = (i & 3) == 0 ? rq.x : (i & 3) == 1 ? rq.y : (i & 3) == 2 ? rq.z : rq.w;
+            x[i] -= a * x[m];
+          }
+        }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           __bf16 hh, ll;
-          split1(acc[i], hh, ll);
+          split1(x[i], hh, ll);
           at_h[at(16 * I + i, 16 * I + j, C)] = hh;
           at_l[at(16 * I + i, 16 * I + j, C)] = ll;
         }
@@ -808,20 +829,16 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
       {
-        float *orow = o + ((size_t)t0 * H + h) * DV + col;
-        const size_t rs = (size_t)H * DV;
-        if (nt == C) {
+        const int rs = H * DV * 4;
+        const auto ro = rsrc(o + ((size_t)t0 * H + h) * DV, (nt - 1) * rs + DV * 4);
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) orow[(16 * mt + 4 * gq + e) * rs] = accO[mt][e];
-        } else {
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (16 * mt + 4 * gq + e < nt) orow[(16 * mt + 4 * gq + e) * rs] = accO[mt][e];
-        }
+          for (int e = 0; e < 4; ++e) {
+            const float val = accO[mt][e];   // (a bit_cast of the vector element itself took element 0)
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), ro,
+                                                  (16 * mt + 4 * gq + e) * rs + 4 * col, 0, 0);
+          }
       }
       // ---- S <- post * (mid * S_pre + (KT plane)^T U): 2 ST steps (tile, kb),
       // fragments read two steps ahead
