@@ -124,6 +124,24 @@ def test_forward_uniform_ragged(dtype, dk, dv):
                 f"uniform {dk}x{dv}")
 
 
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128)])
+def test_forward_bf16_strong_decay_chunks(dk, dv):
+    """Chunks whose gates decay a channel by far more than fp32 spans inside
+    one chunk (gates of 1e-20, exact zeros, and a whole chunk at |alpha| =
+    1e-3) mixed with ordinary chunks, a ragged tail and packed sequences:
+    the bf16 path must switch those chunks to its element-wise ratios and
+    still match the oracle."""
+    lens = [300, 75, 140]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    x = _rand_forward(31, B=1, T=int(cu[-1]), H=2, dk=dk, dv=dv, dtype="bf16", cu=cu)
+    g = x["g"]
+    g[0, 70:76, 0, :4] = 1e-20                      # one channel group, 6 tokens: 2^-400
+    g[0, 200:203, 1, 5] = 0.0                        # exact zeros (clamped on the GPU)
+    g[0, 192:256, 0, :] = np.where(g[0, 192:256, 0, :] < 0, -1e-3, 1e-3)   # whole chunk
+    g[0, 300 + 10:300 + 13, :, 7] = -1e-25           # second sequence, negative and tiny
+    _check_full(x, f"strong decay {dk}x{dv}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_forward_packed_edge_lengths(dtype):
     """Packed sequences of lengths 1, 63, 64, 65, 0 (empty), 130 and 200."""
