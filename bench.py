@@ -74,8 +74,10 @@ def decode_algorithmic(w):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # The GPU's clocks need about 50 forward launches (~30 ms) to reach their steady
+    # state; the defaults warm up past that and time 100 steps (~55 ms).
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=60)
     ap.add_argument("--decode-steps", type=int, default=None,
                     help="decode steps to time (default: the workload's 1024)")
     ap.add_argument("--skip-cpu", action="store_true", help="skip the CPU oracle baseline")

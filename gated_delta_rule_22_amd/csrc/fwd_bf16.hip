@@ -447,7 +447,6 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
       }
       if (pw == 0) s_beta[lane] = lane < nt ? in_b : 0.f;
       if (guard_bad && lane == 0) atomicOr(&s_flag[lc & 1], 1);
-      if (lc + 1 < nch) pr_load(lc + 1, t_opaque);   // next chunk's inputs, in flight meanwhile
 
       __syncthreads();   // H2
       const int fallback = s_flag[lc & 1];
@@ -456,21 +455,25 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
         // ---- A and P tiles (I, J), J <= I, computed transposed: the MFMA's row
         // operand is K/gamma' of block J, its column operand -(gamma' K) or
         // gamma' Q of block I, so lane (g, l) ends up with row 16 I + l and the
-        // four consecutive columns 16 J + 4 g .. +3.  Tile pairs pw, pw+4, pw+8.
-        // (tile, kb) steps; the fragments of step st + 1 are read while step st's
-        // products run.  Waves 2 and 3 have two tiles, waves 0 and 1 three.
-        const int ntile = pw < 2 ? 3 : 2;
-        bf16x8 fa_h[2], fa_l[2], fk_h[2], fk_l[2], fq_h[2], fq_l[2];
-        auto ld = [&](int st) {
-          int I, J;
-          tile_of_pair(pw + 4 * (st / KB), I, J);
-          const int kb = st % KB, sl2 = st & 1;
-          fa_h[sl2] = frag32(kg_h, DK, 16 * J + l16, kb, gq);
-          fa_l[sl2] = frag32(kg_l, DK, 16 * J + l16, kb, gq);
-          fk_h[sl2] = frag32(gk_h, DK, 16 * I + l16, kb, gq);
-          fk_l[sl2] = frag32(gk_l, DK, 16 * I + l16, kb, gq);
-          fq_h[sl2] = frag32(gq_h, DK, 16 * I + l16, kb, gq);
-          fq_l[sl2] = frag32(gq_l, DK, 16 * I + l16, kb, gq);
+        // four consecutive columns 16 J + 4 g .. +3.  Each wave takes tiles that
+        // share their column operand block I:
+        //   wave 0: (3,0) (3,1) (3,2)   wave 1: (2,0) (2,1) (2,2)
+        //   wave 2: (1,0) (1,1)         wave 3: (0,0) (3,3)
+        // Tile 0's fragments of k block kb + 1 are read while kb's products run;
+        // the other tiles' fragments of block kb are read at the start of its step,
+        // ahead of that prefetch, so waiting for them never waits for it.
+        const int I0 = 3 - pw;
+        const bool has1 = pw <= 2, has2 = pw != 2, row2 = pw == 3;
+        const int J2 = pw == 3 ? 3 : 2;
+        bf16x8 ka_h[2], ka_l[2], rk_h[2], rk_l[2], rq_h[2], rq_l[2];
+        auto ld = [&](int kb) {
+          const int sl2 = kb & 1;
+          ka_h[sl2] = frag32(kg_h, DK, l16, kb, gq);
+          ka_l[sl2] = frag32(kg_l, DK, l16, kb, gq);
+          rk_h[sl2] = frag32(gk_h, DK, 16 * I0 + l16, kb, gq);
+          rk_l[sl2] = frag32(gk_l, DK, 16 * I0 + l16, kb, gq);
+          rq_h[sl2] = frag32(gq_h, DK, 16 * I0 + l16, kb, gq);
+          rq_l[sl2] = frag32(gq_l, DK, 16 * I0 + l16, kb, gq);
         };
 #pragma unroll
         for (int t = 0; t < 3; ++t) {
@@ -479,27 +482,53 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
         }
         ld(0);
 #pragma unroll
-        for (int st = 0; st < 3 * KB; ++st) {
-          const int t = st / KB;
-          if (t < ntile) {
-            if (st + 1 < ntile * KB) ld(st + 1);
-            __builtin_amdgcn_sched_barrier(0);
-            const int sl2 = st & 1;
-            pA[t] = mfma32x3(pA[t], fa_h[sl2], fa_l[sl2], fk_h[sl2], fk_l[sl2]);
-            pP[t] = mfma32x3(pP[t], fa_h[sl2], fa_l[sl2], fq_h[sl2], fq_l[sl2]);
-            __builtin_amdgcn_sched_barrier(0);
+        for (int kb = 0; kb < KB; ++kb) {
+          const int sl2 = kb & 1;
+          bf16x8 kb_h, kb_l, kc_h, kc_l, sk_h, sk_l, sq_h, sq_l;
+          if (has1) {
+            kb_h = frag32(kg_h, DK, 16 + l16, kb, gq);
+            kb_l = frag32(kg_l, DK, 16 + l16, kb, gq);
           }
+          if (has2) {
+            kc_h = frag32(kg_h, DK, 16 * J2 + l16, kb, gq);
+            kc_l = frag32(kg_l, DK, 16 * J2 + l16, kb, gq);
+          }
+          if (row2) {
+            sk_h = frag32(gk_h, DK, 48 + l16, kb, gq);
+            sk_l = frag32(gk_l, DK, 48 + l16, kb, gq);
+            sq_h = frag32(gq_h, DK, 48 + l16, kb, gq);
+            sq_l = frag32(gq_l, DK, 48 + l16, kb, gq);
+          } else {
+            sk_h = rk_h[sl2];
+            sk_l = rk_l[sl2];
+            sq_h = rq_h[sl2];
+            sq_l = rq_l[sl2];
+          }
+          if (kb + 1 < KB) ld(kb + 1);
+          __builtin_amdgcn_sched_barrier(0);
+          pA[0] = mfma32x3(pA[0], ka_h[sl2], ka_l[sl2], rk_h[sl2], rk_l[sl2]);
+          pP[0] = mfma32x3(pP[0], ka_h[sl2], ka_l[sl2], rq_h[sl2], rq_l[sl2]);
+          if (has1) {
+            pA[1] = mfma32x3(pA[1], kb_h, kb_l, rk_h[sl2], rk_l[sl2]);
+            pP[1] = mfma32x3(pP[1], kb_h, kb_l, rq_h[sl2], rq_l[sl2]);
+          }
+          if (has2) {
+            pA[2] = mfma32x3(pA[2], kc_h, kc_l, sk_h, sk_l);
+            pP[2] = mfma32x3(pP[2], kc_h, kc_l, sq_h, sq_l);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
+        // pA holds -A_ij / beta_i; scale by beta_i (row 16 I + l16) -> -A_ij.
+        // Diagonal tiles also go to the fp32 store, transposed, zero on and above
+        // the diagonal.
 #pragma unroll
         for (int t = 0; t < 3; ++t) {
-          if (t < ntile) {
-            int I, J;
-            tile_of_pair(pw + 4 * t, I, J);
-            // pA holds -A_ij / beta_i; scale by beta_i (row 16 I + l16) -> -A_ij
+          if (t == 0 || (t == 1 && has1) || (t == 2 && has2)) {
+            const int I = (t == 2 && row2) ? 3 : I0, J = t == 2 ? J2 : t;
             const float bi = s_beta[16 * I + l16];
 #pragma unroll
             for (int e = 0; e < 4; ++e) pA[t][e] *= bi;
-            if (I == J) {     // A_II transposed, zero on and above the diagonal
+            if (I == J) {
 #pragma unroll
               for (int e = 0; e < 4; ++e)
                 s_ad[I * ADB + (4 * gq + e) * ADS + l16] = 4 * gq + e < l16 ? -pA[t][e] : 0.f;
@@ -527,24 +556,26 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
       }
 
       __syncthreads();   // H3
+      if (lc + 1 < nch) pr_load(lc + 1, t_opaque);   // next chunk's inputs, in flight meanwhile
       if (!fallback) {
         // -A below the diagonal blocks, P on and below them: 8-byte stores
+        const int I0 = 3 - pw;
+        const bool has1 = pw <= 2, has2 = pw != 2, row2 = pw == 3;
+        const int J2 = pw == 3 ? 3 : 2;
 #pragma unroll
-        for (int s = 0; s < 3; ++s) {
-          const int pr = pw + 4 * s;
-          if (pr < 10) {
-            int I, J;
-            tile_of_pair(pr, I, J);
+        for (int t = 0; t < 3; ++t) {
+          if (t == 0 || (t == 1 && has1) || (t == 2 && has2)) {
+            const int I = (t == 2 && row2) ? 3 : I0, J = t == 2 ? J2 : t;
             const int i = 16 * I + l16, j = 16 * J + 4 * gq;
             float pv[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) pv[e] = (J < I || 4 * gq + e <= l16) ? pP[s][e] : 0.f;
+            for (int e = 0; e < 4; ++e) pv[e] = (J < I || 4 * gq + e <= l16) ? pP[t][e] : 0.f;
             uint2 hh, ll;
             split_quad(pv, hh, ll);
             *reinterpret_cast<uint2 *>(p_h + at(i, j, C)) = hh;
             *reinterpret_cast<uint2 *>(p_l + at(i, j, C)) = ll;
             if (J < I) {
-              const float av[4] = {pA[s][0], pA[s][1], pA[s][2], pA[s][3]};
+              const float av[4] = {pA[t][0], pA[t][1], pA[t][2], pA[t][3]};
               split_quad(av, hh, ll);
               *reinterpret_cast<uint2 *>(at_h + at(i, j, C)) = hh;
               *reinterpret_cast<uint2 *>(at_l + at(i, j, C)) = ll;
