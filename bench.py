@@ -148,7 +148,23 @@ def main():
         out["mfma"] = {"algorithmic_tflops": tflops, "peak_tflops": BF16_PEAK_TFLOPS,
                        "frac": tflops / BF16_PEAK_TFLOPS, "flops_per_step": fwd_flops}
         out["wall_s_timed"] = wall
-        del q, k, v, g, beta, o, S_T, ws
+        # KDA mode on the same shape and gate magnitudes: the comparison the pages
+        # quote for CKDA's kernel throughput (CKDA over KDA).
+        ga = g.abs()
+        run_kda = lambda: ck.kda_forward(q, k, v, ga, beta, out=o, final_state=S_T, workspace=ws)
+        for _ in range(max(3, args.warmup // 4)):
+            run_kda()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            run_kda()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_kda = e0.elapsed_time(e1) / args.steps
+        out["kda"] = {"ms_per_step": ms_kda, "tokens_per_s": w.B * w.T / (ms_kda * 1e-3),
+                      "ckda_over_kda_throughput": ms_kda / ms,
+                      "gates": "|alpha| of the same workload"}
+        del q, k, v, g, ga, beta, o, S_T, ws
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------- decode

@@ -42,6 +42,8 @@ def library() -> ctypes.CDLL:
         lib.ckda_forward_workspace_bytes.restype = sz
         lib.ckda_forward.argtypes = [vp] * 7 + [ci] * 7 + [vp, vp, vp, sz, vp]
         lib.ckda_forward.restype = ci
+        lib.kda_forward.argtypes = [vp] * 7 + [ci] * 7 + [vp, vp, vp, sz, vp]
+        lib.kda_forward.restype = ci
         lib.ckda_decode_step.argtypes = [vp] * 7 + [ci] * 5 + [vp]
         lib.ckda_decode_step.restype = ci
         _lib = lib
@@ -91,6 +93,20 @@ def forward(q, k, v, g, beta, S0=None, cu_seqlens=None, *, out=None, final_state
     """CKDA chunkwise forward.  Returns ``(o, S_T)`` (``S_T`` is None when
     ``output_final_state`` is False).  See ``ckda_forward`` in include/ckda.h
     for shapes; ``final_state`` may be ``S0`` itself to advance it in place."""
+    return _forward("ckda_forward", q, k, v, g, beta, S0, cu_seqlens, out, final_state,
+                    workspace, output_final_state)
+
+
+def kda_forward(q, k, v, g, beta, S0=None, cu_seqlens=None, *, out=None, final_state=None,
+                workspace=None, output_final_state=True):
+    """KDA mode of the forward (gate signs ignored, |g| used); same arguments and
+    results as :func:`forward`.  See ``kda_forward`` in include/ckda.h."""
+    return _forward("kda_forward", q, k, v, g, beta, S0, cu_seqlens, out, final_state,
+                    workspace, output_final_state)
+
+
+def _forward(entry, q, k, v, g, beta, S0, cu_seqlens, out, final_state, workspace,
+             output_final_state):
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     code = _dtype_code(q)
@@ -118,10 +134,10 @@ def forward(q, k, v, g, beta, S0=None, cu_seqlens=None, *, out=None, final_state
     ws_bytes = forward_workspace_bytes(B, T, H, dk, dv, N, code)
     if workspace is None or workspace.numel() * workspace.element_size() < ws_bytes:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    st = library().ckda_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0),
-                                _ptr(cu_seqlens), B, T, H, dk, dv, N, code, _ptr(o), _ptr(S_T),
-                                _ptr(workspace), ws_bytes, _stream(dev))
-    _check(st, "ckda_forward")
+    st = getattr(library(), entry)(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0),
+                                   _ptr(cu_seqlens), B, T, H, dk, dv, N, code, _ptr(o),
+                                   _ptr(S_T), _ptr(workspace), ws_bytes, _stream(dev))
+    _check(st, entry)
     return o, S_T
 
 

@@ -87,10 +87,12 @@ extern "C" size_t ckda_forward_workspace_bytes(int B, int T, int H, int dk, int 
   return fwd_layout(B, T, H, dk, dv, N, in_dtype).total;
 }
 
-extern "C" int ckda_forward(const void *q, const void *k, const void *v, const float *g,
-                            const float *beta, const float *S0, const int32_t *cu_seqlens,
-                            int B, int T, int H, int dk, int dv, int N, int in_dtype, float *o,
-                            float *S_T, void *workspace, size_t workspace_bytes, void *stream) {
+namespace {
+
+int forward_impl(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                 const float *S0, const int32_t *cu_seqlens, int B, int T, int H, int dk, int dv,
+                 int N, int in_dtype, float *o, float *S_T, void *workspace,
+                 size_t workspace_bytes, void *stream, int signed_gates) {
   const bool packed = cu_seqlens != nullptr;
   if (int s = forward_shape_status(B, T, H, dk, dv, N, in_dtype, packed)) return s;
   const size_t rows = (size_t)B * T * H;
@@ -129,14 +131,33 @@ extern "C" int ckda_forward(const void *q, const void *k, const void *v, const f
     // Uniform rows need no table: the kernel derives each sequence from its row.
     if (packed && launch_seq_table(cu_seqlens, B, T, N, tab, st) != hipSuccess)
       return CKDA_ERR_LAUNCH;
-    e = launch_fwd_bf16(q, k, v, g, beta, S0, o, S_T, T, H, dk, dv, N, tab, packed ? 1 : 0, st);
+    e = launch_fwd_bf16(q, k, v, g, beta, S0, o, S_T, T, H, dk, dv, N, tab, packed ? 1 : 0,
+                        signed_gates, st);
   } else {
     if (launch_seq_table(cu_seqlens, B, T, N, tab, st) != hipSuccess) return CKDA_ERR_LAUNCH;
     void *records = static_cast<char *>(workspace) + L.table_bytes;
     e = launch_fwd_f64(q, k, v, g, beta, S0, B * T, H, dk, dv, N, in_dtype, tab, L.n_chunks_ub,
-                       records, L.rec_bytes, o, S_T, st);
+                       records, L.rec_bytes, o, S_T, signed_gates, st);
   }
   return e == hipSuccess ? CKDA_OK : CKDA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" int ckda_forward(const void *q, const void *k, const void *v, const float *g,
+                            const float *beta, const float *S0, const int32_t *cu_seqlens,
+                            int B, int T, int H, int dk, int dv, int N, int in_dtype, float *o,
+                            float *S_T, void *workspace, size_t workspace_bytes, void *stream) {
+  return forward_impl(q, k, v, g, beta, S0, cu_seqlens, B, T, H, dk, dv, N, in_dtype, o, S_T,
+                      workspace, workspace_bytes, stream, 1);
+}
+
+extern "C" int kda_forward(const void *q, const void *k, const void *v, const float *g,
+                           const float *beta, const float *S0, const int32_t *cu_seqlens,
+                           int B, int T, int H, int dk, int dv, int N, int in_dtype, float *o,
+                           float *S_T, void *workspace, size_t workspace_bytes, void *stream) {
+  return forward_impl(q, k, v, g, beta, S0, cu_seqlens, B, T, H, dk, dv, N, in_dtype, o, S_T,
+                      workspace, workspace_bytes, stream, 0);
 }
 
 extern "C" int ckda_decode_step(const void *q, const void *k, const void *v, const float *g,

@@ -193,7 +193,7 @@ __device__ __forceinline__ void tile_of_pair(int pr, int &I, int &J) {
 }
 
 // ---------------------------------------------------------------- kernel
-template <int DK>
+template <int DK, bool SIGNED>
 __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
     const __hip_bfloat16 *__restrict__ q, const __hip_bfloat16 *__restrict__ k,
     const __hip_bfloat16 *__restrict__ v, const float *__restrict__ g,
@@ -304,6 +304,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
     const int c0 = 4 * (pw * CQW + cql), i0 = tg * TPL;
     constexpr uint32_t kSign = 0x80000000u;
     uint32_t nG[TPL][4];
+    float lmax = -1.f;    // largest per-token log2|alpha|: > 0 means a gate above 1
     {
       float mag[4] = {0.f, 0.f, 0.f, 0.f};
       uint32_t par[4] = {0u, 0u, 0u, 0u};
@@ -321,8 +322,10 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
         const float a4[4] = {in_a[r].x, in_a[r].y, in_a[r].z, in_a[r].w};
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
-          mag[cc] -= fmaxf(flog2(fabsf(a4[cc])), kLog2Floor);
-          par[cc] ^= __builtin_bit_cast(uint32_t, a4[cc]);
+          const float lg = fmaxf(flog2(fabsf(a4[cc])), kLog2Floor);
+          lmax = fmaxf(lmax, lg);
+          mag[cc] -= lg;
+          if (SIGNED) par[cc] ^= __builtin_bit_cast(uint32_t, a4[cc]);
           // mag may be -0 (a lane of padding tokens): take its magnitude bits only
           nG[r][cc] = (par[cc] & kSign) | (__builtin_bit_cast(uint32_t, mag[cc]) & ~kSign);
         }
@@ -338,7 +341,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
         const uint32_t y = __shfl_up(incl[cc], d * CQW);
         if (tg >= d) {
           const float m = fabsf(__builtin_bit_cast(float, incl[cc])) + fabsf(__builtin_bit_cast(float, y));
-          incl[cc] = ((incl[cc] ^ y) & kSign) | __builtin_bit_cast(uint32_t, m);
+          incl[cc] = (SIGNED ? ((incl[cc] ^ y) & kSign) : 0u) | __builtin_bit_cast(uint32_t, m);
         }
       }
     }
@@ -355,7 +358,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
       exb[cc] = ex;
       const float e = fexp2(-half);
       pre4[cc] = e;
-      post4[cc] = __builtin_bit_cast(float, (tot & kSign) | __builtin_bit_cast(uint32_t, e));
+      post4[cc] = SIGNED ? __builtin_bit_cast(float, (tot & kSign) | __builtin_bit_cast(uint32_t, e)) : e;
     }
     float gmax = 0.f;
 #pragma unroll
@@ -365,7 +368,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
       for (int cc = 0; cc < 4; ++cc) {
         const float D = base[cc] - fabsf(__builtin_bit_cast(float, nG[r][cc]));
         gmax = fmaxf(gmax, fabsf(D));
-        const uint32_t sgn = (nG[r][cc] ^ exb[cc]) & kSign;
+        const uint32_t sgn = SIGNED ? (nG[r][cc] ^ exb[cc]) & kSign : 0u;
         const float gam = __builtin_bit_cast(float, sgn | __builtin_bit_cast(uint32_t, fexp2(D)));
         const float igam = __builtin_bit_cast(float, sgn | __builtin_bit_cast(uint32_t, fexp2(-D)));
         const uint32_t kw = cc < 2 ? in_k[r].x : in_k[r].y, qw = cc < 2 ? in_q[r].x : in_q[r].y;
@@ -386,7 +389,10 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
       split_quad(kg, o_kg_h[r], o_kg_l[r]);
       __builtin_amdgcn_sched_barrier(0);   // one token at a time: bounded live range
     }
-    guard_bad = __any(gmax > kGuard) ? 1u : 0u;
+    // The factored ratios need |G - R| <= kGuard and a log-gate that never rises
+    // (|alpha| <= 1, so -G >= 0 can share its word with the parity bit); any
+    // other chunk takes the element-wise path.
+    guard_bad = __any(gmax > kGuard || lmax > 0.f) ? 1u : 0u;
   };
 
   if (threadIdx.x == 0) { s_flag[0] = 0; s_flag[1] = 0; }
@@ -547,7 +553,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
           for (int i = 0; i < C; ++i) {
             const float a = i < nt ? g[((size_t)(t0 + i) * H + h) * DK + c] : 1.f;
             G += fmaxf(flog2(fabsf(a)), kLog2Floor);
-            par ^= a < 0.f ? 1u : 0u;
+            if (SIGNED) par ^= a < 0.f ? 1u : 0u;
             s_G[i * DK + c] = G;
             if (i < 32) m0 |= par << i; else m1 |= par << (i - 32);
           }
@@ -590,8 +596,8 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
           *reinterpret_cast<uint32_t *>(p_l + at(i, j, C)) = 0u;
         }
       } else {
-        // ---- exact path, part 2: A and P element by element (|2^(G_i - G_j)|
-        // <= 1 for |alpha| <= 1) into registers, the diagonal A tiles,
+        // ---- exact path, part 2: A and P element by element (fp32 ratios
+        // 2^(G_i - G_j), whatever their size) into registers, the diagonal A tiles,
         // K_hat^T = (K gamma_n / gamma)^T and the operands relative to the chunk
         // start; the state pass then uses S_pre = S and
         // S' = Diag(gamma_n) S + K_hat^T U.
@@ -653,7 +659,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
           kt_h[at(c, j, C)] = hh;
           kt_l[at(c, j, C)] = ll;
         }
-        // -(gamma K) and gamma Q relative to the chunk start (|gamma| <= 1)
+        // -(gamma K) and gamma Q relative to the chunk start
         for (int pp = tid; pp < C * DK; pp += 256) {
           const int i = pp / DK, c = pp % DK;
           float xk = 0.f, xq = 0.f;
@@ -866,7 +872,12 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float val = accO[mt][e];   // (a bit_cast of the vector element itself took element 0)
+            // A store reads its data register after issue, so the accumulator it
+            // came from could not be reused until the write completed; store a
+            // copy instead (this also reads the vector element through a scalar,
+            // as a bit_cast of the element itself took element 0).
+            float val = accO[mt][e];
+            asm volatile("v_mov_b32 %0, %1" : "=v"(val) : "v"(val));
             __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), ro,
                                                   (16 * mt + 4 * gq + e) * rs + 4 * col, 0, 0);
           }
@@ -914,14 +925,14 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
   }
 }
 
-template <int DK>
+template <int DK, bool SIGNED>
 hipError_t launch_dk(const void *q, const void *k, const void *v, const float *g,
                      const float *beta, const float *S0, float *o, float *S_T, int T, int H,
                      int DV, int N, SeqTable tab, int packed, hipStream_t stream) {
   const int NH = N * H, NV = DV / BV;
   const int groups = (NH + 7) / 8;
   const dim3 grid((unsigned)groups * 8u * (unsigned)NV), block(NT);
-  hipLaunchKernelGGL((fwd_bf16_kernel<DK>), grid, block, 0, stream,
+  hipLaunchKernelGGL((fwd_bf16_kernel<DK, SIGNED>), grid, block, 0, stream,
                      static_cast<const __hip_bfloat16 *>(q), static_cast<const __hip_bfloat16 *>(k),
                      static_cast<const __hip_bfloat16 *>(v), g, beta, S0, o, S_T, T, H, DV, NH, NV,
                      tab, packed);
@@ -932,11 +943,16 @@ hipError_t launch_dk(const void *q, const void *k, const void *v, const float *g
 
 hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, const float *g,
                            const float *beta, const float *S0, float *o, float *S_T, int T, int H,
-                           int dk, int dv, int N, SeqTable tab, int packed, hipStream_t stream) {
+                           int dk, int dv, int N, SeqTable tab, int packed, int signed_gates,
+                           hipStream_t stream) {
   if (dk == 64)
-    return launch_dk<64>(q, k, v, g, beta, S0, o, S_T, T, H, dv, N, tab, packed, stream);
+    return signed_gates
+               ? launch_dk<64, true>(q, k, v, g, beta, S0, o, S_T, T, H, dv, N, tab, packed, stream)
+               : launch_dk<64, false>(q, k, v, g, beta, S0, o, S_T, T, H, dv, N, tab, packed, stream);
   if (dk == 128)
-    return launch_dk<128>(q, k, v, g, beta, S0, o, S_T, T, H, dv, N, tab, packed, stream);
+    return signed_gates
+               ? launch_dk<128, true>(q, k, v, g, beta, S0, o, S_T, T, H, dv, N, tab, packed, stream)
+               : launch_dk<128, false>(q, k, v, g, beta, S0, o, S_T, T, H, dv, N, tab, packed, stream);
   return hipErrorInvalidValue;
 }
 

@@ -63,7 +63,7 @@ template <typename TIn, int DK, int DV>
 __global__ __launch_bounds__(kThreads) void f64_intra(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, int H, int N, SeqTable tab,
-    double *__restrict__ records, size_t rec_doubles) {
+    double *__restrict__ records, size_t rec_doubles, int signed_gates) {
   using R = Rec<DK, DV>;
   __shared__ double s_G[C * DK];        // log2-magnitude cumsum; later reused for T
   __shared__ float s_k[C * DK];
@@ -92,7 +92,7 @@ __global__ __launch_bounds__(kThreads) void f64_intra(
         kk = to_f32(k[row(i) * DK + t]);
       }
       G += fmax(log2(fabs((double)a)), kLog2Floor);
-      par ^= (uint8_t)(a < 0.f);
+      par ^= (uint8_t)(signed_gates && a < 0.f);   // KDA mode: signs ignored
       s_G[i * DK + t] = G;
       s_par[i * DK + t] = par;
       s_k[i * DK + t] = kk;
@@ -231,13 +231,13 @@ template <typename TIn, int DK, int DV>
 hipError_t launch_shape(const void *q, const void *k, const void *v, const float *g,
                         const float *beta, const float *S0, int H, int N, SeqTable tab,
                         size_t n_chunks_ub, void *records, size_t rec_bytes, float *o,
-                        float *S_T, hipStream_t stream) {
+                        float *S_T, int signed_gates, hipStream_t stream) {
   const size_t rec_doubles = rec_bytes / sizeof(double);
   if (n_chunks_ub > 0) {
     hipLaunchKernelGGL((f64_intra<TIn, DK, DV>), dim3((unsigned)n_chunks_ub, H), dim3(kThreads),
                        0, stream, static_cast<const TIn *>(q), static_cast<const TIn *>(k),
                        static_cast<const TIn *>(v), g, beta, H, N, tab,
-                       static_cast<double *>(records), rec_doubles);
+                       static_cast<double *>(records), rec_doubles, signed_gates);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -255,12 +255,13 @@ size_t f64_record_bytes(int dk, int dv) {
 hipError_t launch_fwd_f64(const void *q, const void *k, const void *v, const float *g,
                           const float *beta, const float *S0, int T_rows, int H, int dk, int dv,
                           int N, int in_dtype, SeqTable tab, size_t n_chunks_ub, void *records,
-                          size_t rec_bytes, float *o, float *S_T, hipStream_t stream) {
+                          size_t rec_bytes, float *o, float *S_T, int signed_gates,
+                          hipStream_t stream) {
   (void)T_rows;
 #define CKDA_F64_CASE(TIN, DK_, DV_)                                                           \
   if (dk == DK_ && dv == DV_)                                                                  \
     return launch_shape<TIN, DK_, DV_>(q, k, v, g, beta, S0, H, N, tab, n_chunks_ub, records, \
-                                       rec_bytes, o, S_T, stream);
+                                       rec_bytes, o, S_T, signed_gates, stream);
   if (in_dtype == CKDA_BF16) {
     CKDA_F64_CASE(__hip_bfloat16, 64, 64)
     CKDA_F64_CASE(__hip_bfloat16, 64, 128)

@@ -120,6 +120,21 @@ int ckda_forward(const void *q, const void *k, const void *v, const float *g,
                  void *stream);
 
 /*
+ * KDA mode of the same forward: the recurrence with non-negative gates, the
+ * baseline the CKDA summary measures its kernel throughput against (section
+ * "Main Findings", throughput bullet; KDA keeps alpha in [0, 1]).  The sign
+ * of every gate is ignored: |g| is used, so the sign bookkeeping of
+ * ckda_forward is skipped.  For gates that are all >= 0 the two entry points
+ * compute the same recurrence.  Arguments, layouts, workspace, ownership,
+ * aliasing rules and errors are exactly those of ckda_forward.
+ */
+int kda_forward(const void *q, const void *k, const void *v, const float *g,
+                const float *beta, const float *S0, const int32_t *cu_seqlens,
+                int B, int T, int H, int dk, int dv, int N, int in_dtype,
+                float *o, float *S_T, void *workspace, size_t workspace_bytes,
+                void *stream);
+
+/*
  * One recurrent decode step for N*H independent states, in place.
  *
  *   S <- (I - beta k k^T) Diag(alpha) S + beta k v^T ;  o = S^T q

@@ -16,7 +16,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 def _declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(ckda_\w+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b((?:ckda|kda)_\w+)\s*\(", src)))
 
 
 @pytest.fixture(scope="module")
@@ -26,7 +26,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert {"ckda_forward", "ckda_decode_step", "ckda_forward_workspace_bytes",
+    assert {"ckda_forward", "kda_forward", "ckda_decode_step", "ckda_forward_workspace_bytes",
             "ckda_abi_version", "ckda_status_string"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -40,12 +40,18 @@ def test_version_and_status_strings(lib):
 
 
 def _fwd(lib, B=2, T=64, H=2, dk=128, dv=128, N=None, dtype=0, ptr=16, cu=None, ws=1 << 40,
-         S0=None, S_T=None, o=None):
+         S0=None, S_T=None, o=None, entry="ckda_forward"):
     N = B if N is None else N
     p = ctypes.c_void_p(ptr) if ptr else None
     o = ctypes.c_void_p(1 << 32) if (o is None and ptr) else o
-    return lib.ckda_forward(p, p, p, p, p, S0, cu, B, T, H, dk, dv, N, dtype, o, S_T,
-                            ctypes.c_void_p(1 << 20), ws, None)
+    return getattr(lib, entry)(p, p, p, p, p, S0, cu, B, T, H, dk, dv, N, dtype, o, S_T,
+                               ctypes.c_void_p(1 << 20), ws, None)
+
+
+def test_kda_forward_validates_like_ckda_forward(lib):
+    for kw in (dict(ptr=0), dict(dk=96), dict(H=0), dict(N=3), dict(dtype=7), dict(ptr=18),
+               dict(ws=16)):
+        assert _fwd(lib, entry="kda_forward", **kw) == _fwd(lib, **kw) != 0, kw
 
 
 def test_forward_rejects_bad_arguments(lib):

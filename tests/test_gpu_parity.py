@@ -143,6 +143,24 @@ def test_forward_bf16_strong_decay_chunks(dk, dv):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("bmax,amax", [(2.5, 1.1), (3.0, 1.05)])
+def test_forward_expansive_regime(dtype, bmax, amax):
+    """beta beyond 2 and |alpha| beyond 1 (the summary's Theorem 5 uses
+    beta > 2): computed per the definition, not rejected or clamped.  The
+    transitions are no longer non-expansive and the log-gate is no longer
+    monotone inside a chunk; random key directions keep the values modest over
+    these lengths, so the relative bound stays meaningful."""
+    lens = [300, 97, 150]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    x = _rand_forward(41, B=1, T=int(cu[-1]), H=2, dk=128, dv=128, dtype=dtype, cu=cu)
+    rng = np.random.default_rng(7)
+    x["beta"] = rng.uniform(0, bmax, size=x["beta"].shape).astype(np.float32)
+    sign = np.where(rng.random(x["g"].shape) < 0.4, -1.0, 1.0)
+    x["g"] = (sign * rng.uniform(0.3, amax, size=x["g"].shape)).astype(np.float32)
+    _check_full(x, f"expansive beta<={bmax} |alpha|<={amax}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_forward_packed_edge_lengths(dtype):
     """Packed sequences of lengths 1, 63, 64, 65, 0 (empty), 130 and 200."""
     lens = [1, 63, 64, 65, 0, 130, 200]
@@ -197,3 +215,41 @@ def test_forward_layer_1p3b_sampled():
 def test_forward_varlen_64k_sampled():
     x = wl.forward_inputs("varlen_64k_bf16")
     _check_sampled(x, [(0, 5)], "varlen_64k_bf16")
+
+
+# ---------------------------------------------------------------- KDA mode
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128)])
+def test_kda_forward_uses_gate_magnitudes(dtype, dk, dv):
+    """kda_forward is the recurrence with non-negative gates: on signed gates it
+    computes what the oracle computes on |g| (ragged tail, packed sequences)."""
+    from tests._gpu import upload
+    lens = [150, 64, 1, 90]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    x = _rand_forward(51, B=1, T=int(cu[-1]), H=2, dk=dk, dv=dv, dtype=dtype, cu=cu)
+    d = upload(x)
+    say(f"[gpu] kda_forward {dtype} {dk}x{dv}")
+    o, S = ck.kda_forward(d["q"], d["k"], d["v"], d["g"], d["beta"], S0=d["S0"],
+                          cu_seqlens=d["cu_seqlens"])
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.forward(x["q"], x["k"], x["v"], np.abs(x["g"]), x["beta"],
+                                  S0=x["S0"], cu_seqlens=x["cu_seqlens"])
+    eo, es = rel_err(o.cpu().numpy(), o_ref), rel_err(S.cpu().numpy(), S_ref)
+    say(f"  err(o)={eo:.3e} err(S_T)={es:.3e}")
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_kda_equals_ckda_on_nonnegative_gates(dtype):
+    """With every gate >= 0 the two entry points compute the same recurrence."""
+    from tests._gpu import upload
+    x = _rand_forward(52, B=2, T=200, H=3, dk=128, dv=128, dtype=dtype)
+    x["g"] = np.abs(x["g"])
+    d = upload(x)
+    say(f"[gpu] kda vs ckda {dtype}")
+    o1, S1 = ck.forward(d["q"], d["k"], d["v"], d["g"], d["beta"], S0=d["S0"])
+    o2, S2 = ck.kda_forward(d["q"], d["k"], d["v"], d["g"], d["beta"], S0=d["S0"])
+    torch.cuda.synchronize()
+    assert rel_err(o2.cpu().numpy(), o1.cpu().numpy()) <= TOL[dtype] / 10
+    assert rel_err(S2.cpu().numpy(), S1.cpu().numpy()) <= TOL[dtype] / 10
