@@ -269,23 +269,32 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
       for (int e = 0; e < 4; ++e)
         in_v[mt][e] = __builtin_amdgcn_raw_buffer_load_b16(rv, (16 * mt + 4 * gq + e) * rs + 2 * col, 0, 0);
   };
-  auto pr_load = [&](int lc, int tpin) {
+  // part 0: the gates; part 1: keys, queries and beta; 2: both.  The next
+  // chunk's two halves are issued in different phases, so the issue cost of
+  // 16 KB of loads per wave is not paid in one stretch.
+  auto pr_load = [&](int lc, int tpin, int part) {
     const int lane = tpin & 63, pw = (tpin >> 6) - 4;
     const int c0 = 4 * (pw * CQW + lane % CQW), i0 = (lane / CQW) * TPL;
     const int t0 = start + lc * C, nt = min(C, len - lc * C);
     const size_t row0 = (size_t)t0 * H + h;
     const int rsg = H * DK * 4, rsk = H * DK * 2;
-    const auto rg = rsrc(g + row0 * DK, (nt - 1) * rsg + DK * 4);
-    const auto rk = rsrc(k + row0 * DK, (nt - 1) * rsk + DK * 2);
-    const auto rq = rsrc(q + row0 * DK, (nt - 1) * rsk + DK * 2);
+    if (part != 1) {
+      const auto rg = rsrc(g + row0 * DK, (nt - 1) * rsg + DK * 4);
 #pragma unroll
-    for (int r = 0; r < TPL; ++r) {
-      in_a[r] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rg, (i0 + r) * rsg + 4 * c0, 0, 0));
-      in_k[r] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rk, (i0 + r) * rsk + 2 * c0, 0, 0));
-      in_q[r] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rq, (i0 + r) * rsk + 2 * c0, 0, 0));
+      for (int r = 0; r < TPL; ++r)
+        in_a[r] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rg, (i0 + r) * rsg + 4 * c0, 0, 0));
     }
-    const auto rb = rsrc(beta + row0, (nt - 1) * H * 4 + 4);
-    in_b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, lane * H * 4, 0, 0));
+    if (part != 0) {
+      const auto rk = rsrc(k + row0 * DK, (nt - 1) * rsk + DK * 2);
+      const auto rq = rsrc(q + row0 * DK, (nt - 1) * rsk + DK * 2);
+#pragma unroll
+      for (int r = 0; r < TPL; ++r) {
+        in_k[r] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rk, (i0 + r) * rsk + 2 * c0, 0, 0));
+        in_q[r] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rq, (i0 + r) * rsk + 2 * c0, 0, 0));
+      }
+      const auto rb = rsrc(beta + row0, (nt - 1) * H * 4 + 4);
+      in_b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, lane * H * 4, 0, 0));
+    }
   };
 
   // Register stage of chunk preparation: gate scan across the wave's lanes,
@@ -404,7 +413,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
     // ======================= chunk preparation (waves 4-7)
     float xA[6];        // exact path: the off-diagonal -A blocks, held over one barrier
     if (nch > 0) {
-      pr_load(0, threadIdx.x);
+      pr_load(0, threadIdx.x, 2);
       pr_compute(min(C, len));
     }
     for (int lc = 0; lc < nch; ++lc) {
@@ -456,6 +465,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
 
       __syncthreads();   // H2
       const int fallback = s_flag[lc & 1];
+      if (lc + 1 < nch) pr_load(lc + 1, t_opaque, 0);   // next chunk's gates, in flight meanwhile
       f32x4 pA[3], pP[3];                      // A and P tiles, held over H3
       if (!fallback) {
         // ---- A and P tiles (I, J), J <= I, computed transposed: the MFMA's row
@@ -562,7 +572,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
       }
 
       __syncthreads();   // H3
-      if (lc + 1 < nch) pr_load(lc + 1, t_opaque);   // next chunk's inputs, in flight meanwhile
+      if (lc + 1 < nch) pr_load(lc + 1, t_opaque, 1);   // and its keys, queries, beta
       if (!fallback) {
         // -A below the diagonal blocks, P on and below them: 8-byte stores
         const int I0 = 3 - pw;
