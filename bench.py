@@ -83,6 +83,8 @@ def main():
     ap.add_argument("--skip-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--skip-forward", action="store_true")
+    ap.add_argument("--skip-others", action="store_true",
+                    help="skip timing the fp32 and packed-varlen forward configs")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (a reference "
                          "kernel of known traffic for hardware byte counters)")
@@ -208,6 +210,35 @@ def main():
                                "unit": "GB/s", "frac": dgbs / HBM_PEAK_GBS, "traffic": dtraffic,
                                "kernel": "decode step"}
         del dq, dk_, dv_, dg, db, S, do
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------- other configs (time only)
+    if not args.skip_forward and not args.skip_others:
+        others = {}
+        for name in ("tiny_f32", "rotation_f32", "varlen_64k_bf16"):
+            wo = wl.WORKLOADS[name]
+            xo = wl.forward_inputs(wo)
+            dt = torch.bfloat16 if wo.dtype == "bf16" else torch.float32
+            t = lambda a, d=torch.float32: None if a is None else torch.from_numpy(a).to(dev).to(d)
+            qo, ko, vo = t(xo["q"], dt), t(xo["k"], dt), t(xo["v"], dt)
+            go, bo, so = t(xo["g"]), t(xo["beta"]), t(xo.get("S0"))
+            cu = xo.get("cu_seqlens")
+            cu = None if cu is None else torch.from_numpy(np.asarray(cu, np.int32)).to(dev)
+            run_o = lambda: ck.forward(qo, ko, vo, go, bo, S0=so, cu_seqlens=cu)
+            for _ in range(5):
+                run_o()
+            torch.cuda.synchronize()
+            n_o = 20
+            e0.record(stream)
+            for _ in range(n_o):
+                run_o()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms_o = e0.elapsed_time(e1) / n_o
+            toks = int(xo["q"].shape[0] * xo["q"].shape[1])
+            others[name] = {"ms_per_forward": ms_o, "tokens_per_s": toks / (ms_o * 1e-3)}
+            del qo, ko, vo, go, bo, so, cu
+        out["other_configs"] = others
         torch.cuda.empty_cache()
 
     if args.copy_mib:

@@ -44,6 +44,8 @@ def library() -> ctypes.CDLL:
         lib.ckda_forward.restype = ci
         lib.kda_forward.argtypes = [vp] * 7 + [ci] * 7 + [vp, vp, vp, sz, vp]
         lib.kda_forward.restype = ci
+        lib.ckda_forward_ex.argtypes = [vp] * 7 + [ci] * 8 + [vp, vp, vp, sz, vp]
+        lib.ckda_forward_ex.restype = ci
         lib.ckda_decode_step.argtypes = [vp] * 7 + [ci] * 5 + [vp]
         lib.ckda_decode_step.restype = ci
         _lib = lib
@@ -88,13 +90,26 @@ def _need(t, name, dtype=None, shape=None):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
+OPT_KDA, OPT_QK_L2NORM, OPT_O_BF16 = 1, 2, 4     # CKDA_OPT_* in include/ckda.h
+
+
 def forward(q, k, v, g, beta, S0=None, cu_seqlens=None, *, out=None, final_state=None,
-            workspace=None, output_final_state=True):
+            workspace=None, output_final_state=True, normalize_qk=False,
+            out_dtype=torch.float32, kda=False):
     """CKDA chunkwise forward.  Returns ``(o, S_T)`` (``S_T`` is None when
     ``output_final_state`` is False).  See ``ckda_forward`` in include/ckda.h
-    for shapes; ``final_state`` may be ``S0`` itself to advance it in place."""
-    return _forward("ckda_forward", q, k, v, g, beta, S0, cu_seqlens, out, final_state,
-                    workspace, output_final_state)
+    for shapes; ``final_state`` may be ``S0`` itself to advance it in place.
+
+    ``normalize_qk`` (L2-normalise q and k rows in the kernel), ``out_dtype``
+    (``torch.bfloat16`` for a bf16 ``o``) and ``kda`` (gate signs ignored) map
+    to the options of ``ckda_forward_ex``; with none of them set the call goes
+    to ``ckda_forward``."""
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out_dtype must be torch.float32 or torch.bfloat16")
+    opts = ((OPT_KDA if kda else 0) | (OPT_QK_L2NORM if normalize_qk else 0)
+            | (OPT_O_BF16 if out_dtype == torch.bfloat16 else 0))
+    return _forward("ckda_forward_ex" if opts else "ckda_forward", q, k, v, g, beta, S0,
+                    cu_seqlens, out, final_state, workspace, output_final_state, opts)
 
 
 def kda_forward(q, k, v, g, beta, S0=None, cu_seqlens=None, *, out=None, final_state=None,
@@ -106,7 +121,7 @@ def kda_forward(q, k, v, g, beta, S0=None, cu_seqlens=None, *, out=None, final_s
 
 
 def _forward(entry, q, k, v, g, beta, S0, cu_seqlens, out, final_state, workspace,
-             output_final_state):
+             output_final_state, opts=0):
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     code = _dtype_code(q)
@@ -124,8 +139,9 @@ def _forward(entry, q, k, v, g, beta, S0, cu_seqlens, out, final_state, workspac
     if S0 is not None:
         _need(S0, "S0", torch.float32, (N, H, dk, dv))
     dev = q.device
-    o = out if out is not None else torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
-    _need(o, "out", torch.float32, (B, T, H, dv))
+    o_dt = torch.bfloat16 if opts & OPT_O_BF16 else torch.float32
+    o = out if out is not None else torch.empty((B, T, H, dv), dtype=o_dt, device=dev)
+    _need(o, "out", o_dt, (B, T, H, dv))
     S_T = None
     if output_final_state:
         S_T = final_state if final_state is not None else torch.empty(
@@ -134,9 +150,11 @@ def _forward(entry, q, k, v, g, beta, S0, cu_seqlens, out, final_state, workspac
     ws_bytes = forward_workspace_bytes(B, T, H, dk, dv, N, code)
     if workspace is None or workspace.numel() * workspace.element_size() < ws_bytes:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    st = getattr(library(), entry)(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0),
-                                   _ptr(cu_seqlens), B, T, H, dk, dv, N, code, _ptr(o),
-                                   _ptr(S_T), _ptr(workspace), ws_bytes, _stream(dev))
+    head = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(cu_seqlens),
+            B, T, H, dk, dv, N, code)
+    tail = (_ptr(o), _ptr(S_T), _ptr(workspace), ws_bytes, _stream(dev))
+    fn = getattr(library(), entry)
+    st = fn(*head, opts, *tail) if entry == "ckda_forward_ex" else fn(*head, *tail)
     _check(st, entry)
     return o, S_T
 

@@ -91,10 +91,14 @@ namespace {
 
 int forward_impl(const void *q, const void *k, const void *v, const float *g, const float *beta,
                  const float *S0, const int32_t *cu_seqlens, int B, int T, int H, int dk, int dv,
-                 int N, int in_dtype, float *o, float *S_T, void *workspace,
-                 size_t workspace_bytes, void *stream, int signed_gates) {
+                 int N, int in_dtype, int options, void *o, float *S_T, void *workspace,
+                 size_t workspace_bytes, void *stream) {
   const bool packed = cu_seqlens != nullptr;
   if (int s = forward_shape_status(B, T, H, dk, dv, N, in_dtype, packed)) return s;
+  if (options & ~(CKDA_OPT_KDA | CKDA_OPT_QK_L2NORM | CKDA_OPT_O_BF16)) return CKDA_ERR_SHAPE;
+  const int signed_gates = (options & CKDA_OPT_KDA) ? 0 : 1;
+  const int l2norm = (options & CKDA_OPT_QK_L2NORM) ? 1 : 0;
+  const int o_bf16 = (options & CKDA_OPT_O_BF16) ? 1 : 0;
   const size_t rows = (size_t)B * T * H;
   if (rows > 0 && (!q || !k || !v || !g || !beta || !o)) return CKDA_ERR_NULL;
   const void *ptrs[] = {q, k, v, g, S0, o, S_T, workspace};
@@ -104,7 +108,7 @@ int forward_impl(const void *q, const void *k, const void *v, const float *g, co
 
   const size_t in_sz = in_dtype == CKDA_BF16 ? 2 : 4;
   const size_t st_bytes = (size_t)N * H * dk * dv * 4;
-  const size_t o_bytes = rows * dv * 4;
+  const size_t o_bytes = rows * dv * (o_bf16 ? 2 : 4);
   struct Span { const void *p; size_t n; };
   const Span ins[] = {{q, rows * dk * in_sz}, {k, rows * dk * in_sz}, {v, rows * dv * in_sz},
                       {g, rows * dk * 4},      {beta, rows * 4},       {cu_seqlens, ((size_t)N + 1) * 4}};
@@ -132,12 +136,12 @@ int forward_impl(const void *q, const void *k, const void *v, const float *g, co
     if (packed && launch_seq_table(cu_seqlens, B, T, N, tab, st) != hipSuccess)
       return CKDA_ERR_LAUNCH;
     e = launch_fwd_bf16(q, k, v, g, beta, S0, o, S_T, T, H, dk, dv, N, tab, packed ? 1 : 0,
-                        signed_gates, st);
+                        signed_gates, l2norm, o_bf16, st);
   } else {
     if (launch_seq_table(cu_seqlens, B, T, N, tab, st) != hipSuccess) return CKDA_ERR_LAUNCH;
     void *records = static_cast<char *>(workspace) + L.table_bytes;
     e = launch_fwd_f64(q, k, v, g, beta, S0, B * T, H, dk, dv, N, in_dtype, tab, L.n_chunks_ub,
-                       records, L.rec_bytes, o, S_T, signed_gates, st);
+                       records, L.rec_bytes, o, S_T, signed_gates, l2norm, o_bf16, st);
   }
   return e == hipSuccess ? CKDA_OK : CKDA_ERR_LAUNCH;
 }
@@ -148,16 +152,25 @@ extern "C" int ckda_forward(const void *q, const void *k, const void *v, const f
                             const float *beta, const float *S0, const int32_t *cu_seqlens,
                             int B, int T, int H, int dk, int dv, int N, int in_dtype, float *o,
                             float *S_T, void *workspace, size_t workspace_bytes, void *stream) {
-  return forward_impl(q, k, v, g, beta, S0, cu_seqlens, B, T, H, dk, dv, N, in_dtype, o, S_T,
-                      workspace, workspace_bytes, stream, 1);
+  return forward_impl(q, k, v, g, beta, S0, cu_seqlens, B, T, H, dk, dv, N, in_dtype, 0, o, S_T,
+                      workspace, workspace_bytes, stream);
 }
 
 extern "C" int kda_forward(const void *q, const void *k, const void *v, const float *g,
                            const float *beta, const float *S0, const int32_t *cu_seqlens,
                            int B, int T, int H, int dk, int dv, int N, int in_dtype, float *o,
                            float *S_T, void *workspace, size_t workspace_bytes, void *stream) {
-  return forward_impl(q, k, v, g, beta, S0, cu_seqlens, B, T, H, dk, dv, N, in_dtype, o, S_T,
-                      workspace, workspace_bytes, stream, 0);
+  return forward_impl(q, k, v, g, beta, S0, cu_seqlens, B, T, H, dk, dv, N, in_dtype,
+                      CKDA_OPT_KDA, o, S_T, workspace, workspace_bytes, stream);
+}
+
+extern "C" int ckda_forward_ex(const void *q, const void *k, const void *v, const float *g,
+                               const float *beta, const float *S0, const int32_t *cu_seqlens,
+                               int B, int T, int H, int dk, int dv, int N, int in_dtype,
+                               int options, void *o, float *S_T, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+  return forward_impl(q, k, v, g, beta, S0, cu_seqlens, B, T, H, dk, dv, N, in_dtype, options, o,
+                      S_T, workspace, workspace_bytes, stream);
 }
 
 extern "C" int ckda_decode_step(const void *q, const void *k, const void *v, const float *g,

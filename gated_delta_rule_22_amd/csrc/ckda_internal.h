@@ -51,14 +51,16 @@ hipError_t launch_decode(const void *q, const void *k, const void *v, const floa
 hipError_t launch_fwd_f64(const void *q, const void *k, const void *v, const float *g,
                           const float *beta, const float *S0, int T_rows, int H, int dk, int dv,
                           int N, int in_dtype, SeqTable tab, size_t n_chunks_ub, void *records,
-                          size_t rec_bytes, float *o, float *S_T, int signed_gates,
-                          hipStream_t stream);
+                          size_t rec_bytes, void *o, float *S_T, int signed_gates, int l2norm,
+                          int o_bf16, hipStream_t stream);
 
 // Fused bf16 chunkwise forward on matrix cores (bf16 inputs).
 // signed_gates = 0 is KDA mode: the gates' signs are ignored (|g| is used).
+// l2norm: q and k are L2-normalised per (token, head) inside the kernel.
+// o_bf16: o is bfloat16 (else fp32).
 hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, const float *g,
-                           const float *beta, const float *S0, float *o, float *S_T, int T, int H,
+                           const float *beta, const float *S0, void *o, float *S_T, int T, int H,
                            int dk, int dv, int N, SeqTable tab, int packed, int signed_gates,
-                           hipStream_t stream);
+                           int l2norm, int o_bf16, hipStream_t stream);
 
 }  // namespace ckda

@@ -159,7 +159,9 @@ struct Lds {
   static constexpr int SMID = SPRE + DK * 4;              // S' = post * (mid * S_pre  [DK]
   static constexpr int SPOST = SMID + DK * 4;             //      + (KT plane)^T U)    [DK]
   static constexpr int FL = SPOST + DK * 4;               // guard flags (2 ints)
-  static constexpr int SIZE = FL + 16;
+  static constexpr int NRM = FL + 16;                     // q/k norm partials [4][C][2]
+  static constexpr int FAC = NRM + 4 * C * 8;             // q/k norm factors  [C][2]
+  static constexpr int SIZE = FAC + C * 8;
   static_assert(SIZE <= 160 * 1024, "LDS budget");
 };
 
@@ -193,11 +195,13 @@ __device__ __forceinline__ void tile_of_pair(int pr, int &I, int &J) {
 }
 
 // ---------------------------------------------------------------- kernel
-template <int DK, bool SIGNED>
+// SIGNED: CKDA (false: KDA mode, gate signs ignored).  NORM: q and k are
+// L2-normalised per (token, head) on the fly.  OBF16: o is written as bf16.
+template <int DK, bool SIGNED, bool NORM, bool OBF16>
 __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
     const __hip_bfloat16 *__restrict__ q, const __hip_bfloat16 *__restrict__ k,
     const __hip_bfloat16 *__restrict__ v, const float *__restrict__ g,
-    const float *__restrict__ beta, const float *__restrict__ S0, float *__restrict__ o,
+    const float *__restrict__ beta, const float *__restrict__ S0, void *__restrict__ o,
     float *__restrict__ S_T, int T, int H, int DV, int NH, int NV, SeqTable tab, int packed) {
   using L = Lds<DK>;
   using PG = Prep<DK>;
@@ -217,6 +221,8 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
   float *s_mid = reinterpret_cast<float *>(smem + L::SMID);
   float *s_post = reinterpret_cast<float *>(smem + L::SPOST);
   int *s_flag = reinterpret_cast<int *>(smem + L::FL);
+  float *s_nrm = reinterpret_cast<float *>(smem + L::NRM);
+  float *s_fac = reinterpret_cast<float *>(smem + L::FAC);
 
   // ---- which (sequence, head, dv block): XCD-aware.  Workgroup b runs on XCD
   // b % 8; the NV dv blocks of one (sequence, head) share an XCD (and its L2),
@@ -297,6 +303,33 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
     }
   };
 
+  // Squared norms of the prefetched keys and queries over this wave's channels,
+  // summed over the lanes of each token group; the four waves' partials meet in
+  // LDS at the next barrier.
+  auto pr_partials = [&](int tpin) {
+    const int lane = tpin & 63, pw = (tpin >> 6) - 4;
+    const int cql = lane % CQW, i0 = (lane / CQW) * TPL;
+#pragma unroll
+    for (int r = 0; r < TPL; ++r) {
+      float pk = 0.f, pq = 0.f;
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        const uint32_t kw = cc < 2 ? in_k[r].x : in_k[r].y, qw = cc < 2 ? in_q[r].x : in_q[r].y;
+        const float kk = __builtin_bit_cast(float, (cc & 1) ? (kw & 0xFFFF0000u) : (kw << 16));
+        const float qq = __builtin_bit_cast(float, (cc & 1) ? (qw & 0xFFFF0000u) : (qw << 16));
+        pk += kk * kk;
+        pq += qq * qq;
+      }
+#pragma unroll
+      for (int m = 1; m < CQW; m <<= 1) {
+        pk += __shfl_xor(pk, m);
+        pq += __shfl_xor(pq, m);
+      }
+      if (cql == 0)
+        *reinterpret_cast<float2 *>(s_nrm + (pw * C + i0 + r) * 2) = make_float2(pk, pq);
+    }
+  };
+
   // Register stage of chunk preparation: gate scan across the wave's lanes,
   // gamma'-scaled operands and their hi/lo split.  -(gamma' K) and gamma' Q go
   // straight to LDS (the state pass is done with those planes once H4 has
@@ -369,6 +402,26 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
       pre4[cc] = e;
       post4[cc] = SIGNED ? __builtin_bit_cast(float, (tot & kSign) | __builtin_bit_cast(uint32_t, e)) : e;
     }
+    // q/k normalisation factors (sum of squares + 1e-6)^(-1/2) per token
+    float fk[TPL], fq[TPL];
+#pragma unroll
+    for (int r = 0; r < TPL; ++r) {
+      fk[r] = 1.f;
+      fq[r] = 1.f;
+      if (NORM) {
+        float sk = 1e-6f, sq = 1e-6f;
+#pragma unroll
+        for (int pw2 = 0; pw2 < 4; ++pw2) {
+          const float2 pp = *reinterpret_cast<const float2 *>(s_nrm + (pw2 * C + i0 + r) * 2);
+          sk += pp.x;
+          sq += pp.y;
+        }
+        fk[r] = __builtin_amdgcn_rsqf(sk);
+        fq[r] = __builtin_amdgcn_rsqf(sq);
+        if (pw == 0 && cql == 0)
+          *reinterpret_cast<float2 *>(s_fac + (i0 + r) * 2) = make_float2(fk[r], fq[r]);
+      }
+    }
     float gmax = 0.f;
 #pragma unroll
     for (int r = 0; r < TPL; ++r) {
@@ -381,8 +434,12 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
         const float gam = __builtin_bit_cast(float, sgn | __builtin_bit_cast(uint32_t, fexp2(D)));
         const float igam = __builtin_bit_cast(float, sgn | __builtin_bit_cast(uint32_t, fexp2(-D)));
         const uint32_t kw = cc < 2 ? in_k[r].x : in_k[r].y, qw = cc < 2 ? in_q[r].x : in_q[r].y;
-        const float kk = __builtin_bit_cast(float, (cc & 1) ? (kw & 0xFFFF0000u) : (kw << 16));
-        const float qq = __builtin_bit_cast(float, (cc & 1) ? (qw & 0xFFFF0000u) : (qw << 16));
+        float kk = __builtin_bit_cast(float, (cc & 1) ? (kw & 0xFFFF0000u) : (kw << 16));
+        float qq = __builtin_bit_cast(float, (cc & 1) ? (qw & 0xFFFF0000u) : (qw << 16));
+        if (NORM) {
+          kk *= fk[r];
+          qq *= fq[r];
+        }
         gk[cc] = -kk * gam;
         gq[cc] = qq * gam;
         kg[cc] = kk * igam;
@@ -414,8 +471,10 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
     float xA[6];        // exact path: the off-diagonal -A blocks, held over one barrier
     if (nch > 0) {
       pr_load(0, threadIdx.x, 2);
-      pr_compute(min(C, len));
+      if (NORM) pr_partials(threadIdx.x);
     }
+    __syncthreads();   // B0: the first chunk's norm partials
+    if (nch > 0) pr_compute(min(C, len));
     for (int lc = 0; lc < nch; ++lc) {
       const int t0 = start + lc * C, nt = min(C, len - lc * C);
       int t_opaque = threadIdx.x;
@@ -631,6 +690,10 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
               accA += __bfloat162float(k[ri * DK + c]) * kj;
               accP += __bfloat162float(q[ri * DK + c]) * kj;
             }
+            if (NORM) {
+              accA *= s_fac[2 * i] * s_fac[2 * j];
+              accP *= s_fac[2 * i + 1] * s_fac[2 * j];
+            }
           }
         };
         // P (all of it, zero above the diagonal) and the diagonal A tiles go
@@ -663,6 +726,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
             const float r = with_sign(fexp2(s_G[(C - 1) * DK + c] - s_G[j * DK + c]),
                                       par_of(C - 1, c) ^ par_of(j, c));
             x = __bfloat162float(k[((size_t)(t0 + j) * H + h) * DK + c]) * r;
+            if (NORM) x *= s_fac[2 * j];
           }
           __bf16 hh, ll;
           split1(x, hh, ll);
@@ -678,6 +742,10 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
             const size_t ri = (size_t)(t0 + i) * H + h;
             xk = -__bfloat162float(k[ri * DK + c]) * gam;
             xq = __bfloat162float(q[ri * DK + c]) * gam;
+            if (NORM) {
+              xk *= s_fac[2 * i];
+              xq *= s_fac[2 * i + 1];
+            }
           }
           __bf16 hh, ll;
           split1(xk, hh, ll);
@@ -705,6 +773,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
         }
         __syncthreads();   // diagonal A tiles complete for the inverses
       }
+      if (NORM && lc + 1 < nch) pr_partials(t_opaque);   // next chunk's keys and queries
       __syncthreads();   // H4
       if (lc + 1 < nch) pr_compute(min(C, len - (lc + 1) * C));   // overlaps the state pass
     }
@@ -721,6 +790,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
               S0 ? S0[(((size_t)n * H + h) * DK + 16 * tt + 4 * gq + e) * DV + col] : 0.f;
       if (nch > 0) sp_load_v(0, threadIdx.x);
     }
+    __syncthreads();   // B0
     for (int lc = 0; lc < nch; ++lc) {
       const int t0 = start + lc * C, nt = min(C, len - lc * C);
       int t_opaque = threadIdx.x;
@@ -875,9 +945,23 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
         accO[mt] = mfma32x3(accO[mt], rp_h[st % 3], rp_l[st % 3], u32h(kb), u32l(kb));
         __builtin_amdgcn_sched_barrier(0);
       }
-      {
+      if (OBF16) {
+        const int rs = H * DV * 2;
+        const auto ro = rsrc(static_cast<__hip_bfloat16 *>(o) + ((size_t)t0 * H + h) * DV,
+                             (nt - 1) * rs + DV * 2);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float val = accO[mt][e];
+            asm volatile("v_mov_b32 %0, %1" : "=v"(val) : "v"(val));
+            const __bf16 b = (__bf16)val;
+            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, b), ro,
+                                                  (16 * mt + 4 * gq + e) * rs + 2 * col, 0, 0);
+          }
+      } else {
         const int rs = H * DV * 4;
-        const auto ro = rsrc(o + ((size_t)t0 * H + h) * DV, (nt - 1) * rs + DV * 4);
+        const auto ro = rsrc(static_cast<float *>(o) + ((size_t)t0 * H + h) * DV, (nt - 1) * rs + DV * 4);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -935,34 +1019,54 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
   }
 }
 
-template <int DK, bool SIGNED>
+template <int DK, bool SIGNED, bool NORM, bool OBF16>
 hipError_t launch_dk(const void *q, const void *k, const void *v, const float *g,
-                     const float *beta, const float *S0, float *o, float *S_T, int T, int H,
+                     const float *beta, const float *S0, void *o, float *S_T, int T, int H,
                      int DV, int N, SeqTable tab, int packed, hipStream_t stream) {
   const int NH = N * H, NV = DV / BV;
   const int groups = (NH + 7) / 8;
   const dim3 grid((unsigned)groups * 8u * (unsigned)NV), block(NT);
-  hipLaunchKernelGGL((fwd_bf16_kernel<DK, SIGNED>), grid, block, 0, stream,
+  hipLaunchKernelGGL((fwd_bf16_kernel<DK, SIGNED, NORM, OBF16>), grid, block, 0, stream,
                      static_cast<const __hip_bfloat16 *>(q), static_cast<const __hip_bfloat16 *>(k),
                      static_cast<const __hip_bfloat16 *>(v), g, beta, S0, o, S_T, T, H, DV, NH, NV,
                      tab, packed);
   return hipGetLastError();
 }
 
+// One kernel per option combination, so no option costs a branch in the loop.
+template <int DK>
+hipError_t launch_opts(const void *q, const void *k, const void *v, const float *g,
+                       const float *beta, const float *S0, void *o, float *S_T, int T, int H,
+                       int DV, int N, SeqTable tab, int packed, int signed_gates, int l2norm,
+                       int o_bf16, hipStream_t stream) {
+#define CKDA_BF16_CASE(S_, N_, O_)                                                             \
+  if (!!signed_gates == S_ && !!l2norm == N_ && !!o_bf16 == O_)                                \
+    return launch_dk<DK, S_, N_, O_>(q, k, v, g, beta, S0, o, S_T, T, H, DV, N, tab, packed,  \
+                                     stream);
+  CKDA_BF16_CASE(true, false, false)
+  CKDA_BF16_CASE(false, false, false)
+  CKDA_BF16_CASE(true, true, false)
+  CKDA_BF16_CASE(false, true, false)
+  CKDA_BF16_CASE(true, false, true)
+  CKDA_BF16_CASE(false, false, true)
+  CKDA_BF16_CASE(true, true, true)
+  CKDA_BF16_CASE(false, true, true)
+#undef CKDA_BF16_CASE
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, const float *g,
-                           const float *beta, const float *S0, float *o, float *S_T, int T, int H,
+                           const float *beta, const float *S0, void *o, float *S_T, int T, int H,
                            int dk, int dv, int N, SeqTable tab, int packed, int signed_gates,
-                           hipStream_t stream) {
+                           int l2norm, int o_bf16, hipStream_t stream) {
   if (dk == 64)
-    return signed_gates
-               ? launch_dk<64, true>(q, k, v, g, beta, S0, o, S_T, T, H, dv, N, tab, packed, stream)
-               : launch_dk<64, false>(q, k, v, g, beta, S0, o, S_T, T, H, dv, N, tab, packed, stream);
+    return launch_opts<64>(q, k, v, g, beta, S0, o, S_T, T, H, dv, N, tab, packed, signed_gates,
+                           l2norm, o_bf16, stream);
   if (dk == 128)
-    return signed_gates
-               ? launch_dk<128, true>(q, k, v, g, beta, S0, o, S_T, T, H, dv, N, tab, packed, stream)
-               : launch_dk<128, false>(q, k, v, g, beta, S0, o, S_T, T, H, dv, N, tab, packed, stream);
+    return launch_opts<128>(q, k, v, g, beta, S0, o, S_T, T, H, dv, N, tab, packed, signed_gates,
+                            l2norm, o_bf16, stream);
   return hipErrorInvalidValue;
 }
 

@@ -63,13 +63,14 @@ template <typename TIn, int DK, int DV>
 __global__ __launch_bounds__(kThreads) void f64_intra(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, int H, int N, SeqTable tab,
-    double *__restrict__ records, size_t rec_doubles, int signed_gates) {
+    double *__restrict__ records, size_t rec_doubles, int signed_gates, int l2norm) {
   using R = Rec<DK, DV>;
   __shared__ double s_G[C * DK];        // log2-magnitude cumsum; later reused for T
   __shared__ float s_k[C * DK];
   __shared__ uint8_t s_par[C * DK];
   __shared__ double s_A[C * (C + 1)];
   __shared__ double s_beta[C];
+  __shared__ double s_fq[C];            // query normalisation factor per token (1 if off)
 
   const int cflat = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
   if (cflat >= tab.chunk_off[N]) return;
@@ -100,6 +101,24 @@ __global__ __launch_bounds__(kThreads) void f64_intra(
   }
   if (t < C) s_beta[t] = t < nt ? (double)beta[row(t)] : 0.0;
   __syncthreads();
+  // ---- optional L2 normalisation of q and k per token: (sum x^2 + 1e-6)^(-1/2)
+  if (t < C) {
+    double fk = 1.0, fq = 1.0;
+    if (l2norm && t < nt) {
+      double sk = 1e-6, sq = 1e-6;
+      for (int c = 0; c < DK; ++c) {
+        const double kk = s_k[t * DK + c], qq = to_f32(q[row(t) * DK + c]);
+        sk += kk * kk;
+        sq += qq * qq;
+      }
+      fk = 1.0 / sqrt(sk);
+      fq = 1.0 / sqrt(sq);
+    }
+    s_fq[t] = fq;
+    if (l2norm)
+      for (int c = 0; c < DK; ++c) s_k[t * DK + c] = (float)(s_k[t * DK + c] * fk);
+  }
+  __syncthreads();
 
   // ---- A (strictly lower) and P (lower incl. diagonal), element by element.
   for (int p = t; p < C * C; p += kThreads) {
@@ -114,6 +133,7 @@ __global__ __launch_bounds__(kThreads) void f64_intra(
         accA += (double)s_k[i * DK + c] * rk;
         accP += (double)to_f32(qi[c]) * rk;
       }
+      accP *= s_fq[i];
     }
     s_A[i * (C + 1) + j] = (j < i) ? s_beta[i] * accA : 0.0;
     rec[R::P + p] = accP;
@@ -127,7 +147,7 @@ __global__ __launch_bounds__(kThreads) void f64_intra(
     const double sn = (s_par[i * DK + c] ^ s_par[(C - 1) * DK + c]) ? -1.0 : 1.0;
     const double gam = si * exp2(Gi);
     const double kk = s_k[p];
-    const double qq = i < nt ? (double)to_f32(q[row(i) * DK + c]) : 0.0;
+    const double qq = i < nt ? (double)to_f32(q[row(i) * DK + c]) * s_fq[i] : 0.0;
     rec[R::QT + p] = qq * gam;
     rec[R::GK + p] = kk * gam;
     rec[R::KH + p] = kk * sn * exp2(Gn - Gi);
@@ -172,7 +192,7 @@ __global__ __launch_bounds__(kThreads) void f64_intra(
 template <int DK, int DV>
 __global__ __launch_bounds__(kThreads) void f64_inter(
     const float *__restrict__ S0, int H, int N, SeqTable tab, const double *__restrict__ records,
-    size_t rec_doubles, float *__restrict__ o, float *__restrict__ S_T) {
+    size_t rec_doubles, void *__restrict__ o, float *__restrict__ S_T, int o_bf16) {
   using R = Rec<DK, DV>;
   __shared__ double s_S[DK * kBV];
   __shared__ double s_U[C * kBV];
@@ -208,7 +228,11 @@ __global__ __launch_bounds__(kThreads) void f64_inter(
       double acc = 0.0;
       for (int c = 0; c < DK; ++c) acc += rec[R::QT + i * DK + c] * s_S[c * kBV + j];
       for (int m = 0; m <= i; ++m) acc += rec[R::P + i * C + m] * s_U[m * kBV + j];
-      o[((size_t)(start + lc * C + i) * H + h) * DV + jb * kBV + j] = (float)acc;
+      const size_t oi = ((size_t)(start + lc * C + i) * H + h) * DV + jb * kBV + j;
+      if (o_bf16)
+        static_cast<__hip_bfloat16 *>(o)[oi] = __float2bfloat16((float)acc);
+      else
+        static_cast<float *>(o)[oi] = (float)acc;
     }
     __syncthreads();
     // S' = Diag(gamma_n) S + K_hat^T U
@@ -230,19 +254,20 @@ __global__ __launch_bounds__(kThreads) void f64_inter(
 template <typename TIn, int DK, int DV>
 hipError_t launch_shape(const void *q, const void *k, const void *v, const float *g,
                         const float *beta, const float *S0, int H, int N, SeqTable tab,
-                        size_t n_chunks_ub, void *records, size_t rec_bytes, float *o,
-                        float *S_T, int signed_gates, hipStream_t stream) {
+                        size_t n_chunks_ub, void *records, size_t rec_bytes, void *o,
+                        float *S_T, int signed_gates, int l2norm, int o_bf16,
+                        hipStream_t stream) {
   const size_t rec_doubles = rec_bytes / sizeof(double);
   if (n_chunks_ub > 0) {
     hipLaunchKernelGGL((f64_intra<TIn, DK, DV>), dim3((unsigned)n_chunks_ub, H), dim3(kThreads),
                        0, stream, static_cast<const TIn *>(q), static_cast<const TIn *>(k),
                        static_cast<const TIn *>(v), g, beta, H, N, tab,
-                       static_cast<double *>(records), rec_doubles, signed_gates);
+                       static_cast<double *>(records), rec_doubles, signed_gates, l2norm);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((f64_inter<DK, DV>), dim3((DV / kBV) * N * H), dim3(kThreads), 0, stream, S0,
-                     H, N, tab, static_cast<const double *>(records), rec_doubles, o, S_T);
+                     H, N, tab, static_cast<const double *>(records), rec_doubles, o, S_T, o_bf16);
   return hipGetLastError();
 }
 
@@ -255,13 +280,13 @@ size_t f64_record_bytes(int dk, int dv) {
 hipError_t launch_fwd_f64(const void *q, const void *k, const void *v, const float *g,
                           const float *beta, const float *S0, int T_rows, int H, int dk, int dv,
                           int N, int in_dtype, SeqTable tab, size_t n_chunks_ub, void *records,
-                          size_t rec_bytes, float *o, float *S_T, int signed_gates,
-                          hipStream_t stream) {
+                          size_t rec_bytes, void *o, float *S_T, int signed_gates, int l2norm,
+                          int o_bf16, hipStream_t stream) {
   (void)T_rows;
 #define CKDA_F64_CASE(TIN, DK_, DV_)                                                           \
   if (dk == DK_ && dv == DV_)                                                                  \
     return launch_shape<TIN, DK_, DV_>(q, k, v, g, beta, S0, H, N, tab, n_chunks_ub, records, \
-                                       rec_bytes, o, S_T, signed_gates, stream);
+                                       rec_bytes, o, S_T, signed_gates, l2norm, o_bf16, stream);
   if (in_dtype == CKDA_BF16) {
     CKDA_F64_CASE(__hip_bfloat16, 64, 64)
     CKDA_F64_CASE(__hip_bfloat16, 64, 128)

@@ -61,6 +61,13 @@ enum {
     CKDA_F32 = 1             /* q, k, v are float32 */
 };
 
+/* Options of ckda_forward_ex (bitwise or). */
+enum {
+    CKDA_OPT_KDA = 1,        /* KDA mode: gate signs ignored (|g| is used) */
+    CKDA_OPT_QK_L2NORM = 2,  /* q and k L2-normalised per (token, head) in the kernel */
+    CKDA_OPT_O_BF16 = 4      /* o written as bfloat16 (round to nearest even) */
+};
+
 /* Version of this ABI (bumped on any incompatible change). */
 int ckda_abi_version(void);
 
@@ -133,6 +140,32 @@ int kda_forward(const void *q, const void *k, const void *v, const float *g,
                 int B, int T, int H, int dk, int dv, int N, int in_dtype,
                 float *o, float *S_T, void *workspace, size_t workspace_bytes,
                 void *stream);
+
+/*
+ * ckda_forward with the pre- and post-processing a layer otherwise does in
+ * separate passes over HBM, fused into the same kernels (the CKDA summary's
+ * methodology names a variant that fuses the gate signs into the key/query
+ * normalisation):
+ *
+ *  options  0, or any bitwise or of
+ *    CKDA_OPT_KDA        as kda_forward
+ *    CKDA_OPT_QK_L2NORM  each (token, head) row of q and of k is replaced by
+ *                        x * (sum_c x_c^2 + 1e-6)^(-1/2) before use, computed
+ *                        in fp32 (bf16 inputs) or fp64 (fp32 inputs); the
+ *                        caller's arrays are not modified
+ *    CKDA_OPT_O_BF16     o is [B, T, H, dv] bfloat16: the fp32 result rounded
+ *                        to nearest even (halves o's HBM traffic)
+ *  o        fp32 or bf16 per CKDA_OPT_O_BF16; 16-byte aligned
+ *
+ * Every other argument, the workspace size and all error rules are those of
+ * ckda_forward; unknown option bits return CKDA_ERR_SHAPE.  ckda_forward is
+ * ckda_forward_ex with options 0, kda_forward with CKDA_OPT_KDA.
+ */
+int ckda_forward_ex(const void *q, const void *k, const void *v, const float *g,
+                    const float *beta, const float *S0, const int32_t *cu_seqlens,
+                    int B, int T, int H, int dk, int dv, int N, int in_dtype, int options,
+                    void *o, float *S_T, void *workspace, size_t workspace_bytes,
+                    void *stream);
 
 /*
  * One recurrent decode step for N*H independent states, in place.

@@ -88,3 +88,15 @@ def test_decode_rejects_bad_arguments(lib):
     q = ctypes.c_void_p(24)
     assert f(q, p, p, p, p, ctypes.c_void_p(1 << 30), ctypes.c_void_p(1 << 31), 1, 1, 128, 128,
              0, None) == 4
+
+
+def test_forward_ex_rejects_unknown_options(lib):
+    p = ctypes.c_void_p(16)
+    o = ctypes.c_void_p(1 << 32)
+    call = lambda opts: lib.ckda_forward_ex(p, p, p, p, p, None, None, 2, 64, 2, 128, 128, 2, 0,
+                                           opts, o, None, ctypes.c_void_p(1 << 20), 1 << 40, None)
+    assert call(8) == 2 and call(16) == 2
+    q_bad = lambda opts: lib.ckda_forward_ex(ctypes.c_void_p(18), p, p, p, p, None, None, 2, 64, 2,
+                                             128, 128, 2, 0, opts, o, None,
+                                             ctypes.c_void_p(1 << 20), 1 << 40, None)
+    assert q_bad(7) == 4                                        # still checks alignment

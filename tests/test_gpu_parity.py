@@ -253,3 +253,89 @@ def test_kda_equals_ckda_on_nonnegative_gates(dtype):
     torch.cuda.synchronize()
     assert rel_err(o2.cpu().numpy(), o1.cpu().numpy()) <= TOL[dtype] / 10
     assert rel_err(S2.cpu().numpy(), S1.cpu().numpy()) <= TOL[dtype] / 10
+
+
+# ---------------------------------------------------------------- fused pre/post-processing
+
+def _l2norm(a):
+    a = a.astype(np.float64)
+    return a / np.sqrt(np.sum(a * a, axis=-1, keepdims=True) + 1e-6)
+
+
+def _raw_qk(x, seed):
+    """Un-normalised keys and queries with a spread of row norms, rounded like
+    the other inputs of the case."""
+    rng = np.random.default_rng(seed)
+    cast = wl.round_bf16 if x["dtype"] == "bf16" else (lambda a: a.astype(np.float32))
+    scale = lambda a: a * rng.uniform(0.2, 5.0, size=a.shape[:-1] + (1,))
+    x["q"] = cast(scale(rng.normal(size=x["q"].shape)))
+    x["k"] = cast(scale(rng.normal(size=x["k"].shape)))
+    return x
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128)])
+def test_forward_fused_qk_l2norm(dtype, dk, dv):
+    """normalize_qk: the kernel L2-normalises each (token, head) row of q and k
+    (sum of squares + 1e-6) before use; the oracle runs on rows normalised in
+    fp64.  Ragged packed sequences; one chunk forced onto the exact path."""
+    from tests._gpu import upload
+    lens = [200, 37, 130]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    x = _raw_qk(_rand_forward(61, B=1, T=int(cu[-1]), H=2, dk=dk, dv=dv, dtype=dtype, cu=cu), 62)
+    x["g"][0, 70:74, 1, :3] = 1e-30            # an exact-path chunk on the bf16 path
+    d = upload(x)
+    say(f"[gpu] ckda_forward_ex normalize_qk {dtype} {dk}x{dv}")
+    o, S = ck.forward(d["q"], d["k"], d["v"], d["g"], d["beta"], S0=d["S0"],
+                      cu_seqlens=d["cu_seqlens"], normalize_qk=True)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.forward(_l2norm(x["q"]), _l2norm(x["k"]), x["v"], x["g"], x["beta"],
+                                  S0=x["S0"], cu_seqlens=x["cu_seqlens"])
+    eo, es = rel_err(o.cpu().numpy(), o_ref), rel_err(S.cpu().numpy(), S_ref)
+    say(f"  err(o)={eo:.3e} err(S_T)={es:.3e}")
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
+
+
+def _bf16_bound(o_gpu, o_ref, tol):
+    """Error beyond one bf16 rounding of the reference, relative to its RMS."""
+    o_gpu = np.asarray(o_gpu, np.float64)
+    excess = np.abs(o_gpu - o_ref) - np.abs(o_ref) * 2.0 ** -8
+    return float(np.max(excess) / np.sqrt(np.mean(o_ref ** 2))) <= tol
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_forward_bf16_output(dtype):
+    """out_dtype=bfloat16: o is the fp32 result rounded to bf16, so it matches
+    the oracle to within the bound plus one bf16 rounding; S_T is unchanged."""
+    from tests._gpu import upload
+    x = _rand_forward(63, B=2, T=150, H=2, dk=128, dv=128, dtype=dtype)
+    d = upload(x)
+    say(f"[gpu] ckda_forward_ex bf16 o {dtype}")
+    o, S = ck.forward(d["q"], d["k"], d["v"], d["g"], d["beta"], S0=d["S0"],
+                      out_dtype=torch.bfloat16)
+    o32, S32 = ck.forward(d["q"], d["k"], d["v"], d["g"], d["beta"], S0=d["S0"])
+    torch.cuda.synchronize()
+    assert o.dtype == torch.bfloat16
+    o_ref, S_ref = oracle.forward(x["q"], x["k"], x["v"], x["g"], x["beta"], S0=x["S0"])
+    assert _bf16_bound(o.float().cpu().numpy(), o_ref, TOL[dtype])
+    assert torch.equal(o, o32.to(torch.bfloat16))          # the same numbers, rounded
+    assert rel_err(S.cpu().numpy(), S_ref) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_forward_all_options(dtype):
+    """KDA mode, normalised q/k and a bf16 o together."""
+    from tests._gpu import upload
+    lens = [129, 64, 5]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    x = _raw_qk(_rand_forward(64, B=1, T=int(cu[-1]), H=3, dk=128, dv=64, dtype=dtype, cu=cu), 65)
+    d = upload(x)
+    say(f"[gpu] ckda_forward_ex all options {dtype}")
+    o, S = ck.forward(d["q"], d["k"], d["v"], d["g"], d["beta"], S0=d["S0"],
+                      cu_seqlens=d["cu_seqlens"], normalize_qk=True, out_dtype=torch.bfloat16,
+                      kda=True)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.forward(_l2norm(x["q"]), _l2norm(x["k"]), x["v"], np.abs(x["g"]),
+                                  x["beta"], S0=x["S0"], cu_seqlens=x["cu_seqlens"])
+    assert _bf16_bound(o.float().cpu().numpy(), o_ref, TOL[dtype])
+    assert rel_err(S.cpu().numpy(), S_ref) <= TOL[dtype]
