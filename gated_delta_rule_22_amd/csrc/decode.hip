@@ -18,6 +18,7 @@ namespace ckda {
 namespace {
 
 constexpr int kThreads = 256;
+typedef float nf4 __attribute__((ext_vector_type(4)));   // for the non-temporal builtins
 
 template <typename TIn, int DK, int DV>
 __global__ __launch_bounds__(kThreads) void decode_kernel(
@@ -40,11 +41,17 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
   const int rg = t / kColThreads;                    // row group
   float *Sh = S + (size_t)head * DK * DV;
 
-  // Issue the state loads first: they are the traffic that matters.
+  // Issue the state loads first: they are the traffic that matters.  They are
+  // non-temporal: each state is read once per step and the states of one step
+  // exceed the last-level cache, so keeping them cached only evicts other data
+  // (measured: about 3% faster per step; non-temporal stores were slower).
   float4 st[kRows];
 #pragma unroll
-  for (int r = 0; r < kRows; ++r)
-    st[r] = *reinterpret_cast<const float4 *>(Sh + (size_t)(rg * kRows + r) * DV + cg * 4);
+  for (int r = 0; r < kRows; ++r) {
+    const nf4 x = __builtin_nontemporal_load(
+        reinterpret_cast<const nf4 *>(Sh + (size_t)(rg * kRows + r) * DV + cg * 4));
+    st[r] = make_float4(x.x, x.y, x.z, x.w);
+  }
 
   float kq = 0.f;
   if (t < DK) {
