@@ -8,6 +8,8 @@ The heavy lifting is the token-by-token fp64 recurrence in ``ckda_oracle.c``
 (see that file's header for the update rule and where it is stated).  This
 module loads it through ctypes and adds two small helpers built on it:
 
+* :func:`backward` -- the reverse-mode gradient of the same recurrence (the
+  adjoint steps are written out in ``ckda_oracle.c``).
 * :func:`transition` -- the one-token transition matrix of the oracle itself,
   obtained by running it with S0 = I and v = 0 (then S_1 = A S0 = A).
 * :mod:`oracle.chunked` -- a dense chunked (WY/UT) fp64 formulation in NumPy,
@@ -55,6 +57,9 @@ def _load():
         lib.ckda_oracle_forward.restype = ci
         lib.ckda_oracle_decode.argtypes = [dp, dp, dp, dp, dp, dp, dp, ci, ci, ci, ci, ci]
         lib.ckda_oracle_decode.restype = ci
+        lib.ckda_oracle_backward.argtypes = [dp, dp, dp, dp, dp, dp, i64p, ci, ci, ci, ci, ci,
+                                             ci, dp, dp, dp, dp, dp, dp, dp, dp, ci]
+        lib.ckda_oracle_backward.restype = ci
         _lib = lib
     return _lib
 
@@ -110,6 +115,50 @@ def forward(q, k, v, g, beta, S0=None, cu_seqlens=None, nthreads: int | None = N
     return o, S_T
 
 
+def backward(q, k, v, g, beta, do, S0=None, dS_T=None, cu_seqlens=None,
+             nthreads: int | None = None):
+    """Reverse-mode gradient of the token-by-token forward, in fp64.
+
+    For upstream gradients ``do`` (``[B, T, H, dv]``, of o) and ``dS_T``
+    (``[N, H, dk, dv]`` or None for zero, of the final states), returns the
+    gradient of ``sum(do * o) + sum(dS_T * S_T)`` with respect to the inputs:
+    ``(dq, dk, dv, dg, dbeta, dS0)``, shaped like q, k, v, g, beta and
+    ``[N, H, dk, dv]``.  ``dg`` is the derivative with respect to the signed
+    gate alpha itself.  Rows outside every packed sequence get zero gradients.
+    """
+    q, k, v, g, beta, do = map(_f64, (q, k, v, g, beta, do))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or g.shape != q.shape or v.shape[:3] != (B, T, H) \
+            or beta.shape != (B, T, H) or do.shape != v.shape:
+        raise ValueError("shape mismatch")
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+        N = cu.shape[0] - 1
+        if B != 1:
+            raise ValueError("packed sequences need B == 1")
+    else:
+        cu = None
+        N = B
+    S0a = None if S0 is None else _f64(S0)
+    dSTa = None if dS_T is None else _f64(dS_T)
+    for a in (S0a, dSTa):
+        if a is not None and a.shape != (N, H, dk, dv):
+            raise ValueError("state shape mismatch")
+    out = [np.zeros(x.shape, dtype=np.float64) for x in (q, k, v, g, beta)]
+    dS0 = np.zeros((N, H, dk, dv), dtype=np.float64)
+    cu_p = None if cu is None else cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    rc = _load().ckda_oracle_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                      _ptr(S0a), cu_p, B, T, H, dk, dv, N, _ptr(do),
+                                      _ptr(dSTa), *[_ptr(x) for x in out], _ptr(dS0),
+                                      nthreads or default_threads())
+    if rc == -2:
+        raise MemoryError("oracle backward ran out of host memory")
+    if rc != 0:
+        raise ValueError("oracle rejected the sizes")
+    return (*out, dS0)
+
+
 def decode_step(q, k, v, g, beta, S, nthreads: int | None = None):
     """One decode step.  ``S`` ([N, H, dk, dv], fp64, C-contiguous) is updated
     in place; returns o ``[N, H, dv]``."""
@@ -145,4 +194,4 @@ def transition(k, g, beta):
     return S_T[0, 0]
 
 
-__all__ = ["build", "forward", "decode_step", "transition", "default_threads"]
+__all__ = ["build", "forward", "backward", "decode_step", "transition", "default_threads"]

@@ -1,6 +1,7 @@
 """The oracle's pins are sharp: plant plausible mistakes in copies of the C
 oracle (on the CPU, in a temporary directory) and check that the pin suite
-fails for every one of them."""
+fails for every one of them -- the forward's pins for mistakes in the forward,
+the backward's pins for mistakes in the adjoint steps of the backward."""
 import os
 import re
 import subprocess
@@ -10,19 +11,44 @@ import numpy as np
 import pytest
 
 import oracle
+from tests import test_oracle_backward as bpins
 from tests import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "ckda_oracle.c")
 
 # (name, regex on the source, replacement)
 MUTANTS = [
-    ("decay dropped", r"S\[c \* dv \+ j\] \*= a\[c\];", ";"),
-    ("gate on value columns", r"S\[c \* dv \+ j\] \*= a\[c\];", "S[c * dv + j] *= a[j % dk];"),
+    ("decay dropped", r"(?<!d)S\[c \* dv \+ j\] \*= a\[c\];", ";"),
+    ("gate on value columns", r"(?<!d)S\[c \* dv \+ j\] \*= a\[c\];",
+     "S[c * dv + j] *= a[j % dk];"),
     ("delta term sign", r"\+= b \* k\[c\] \* \(v\[j\] - u\[j\]\)", "-= b * k[c] * (v[j] - u[j])"),
     ("erase sign", r"\(v\[j\] - u\[j\]\)", "(v[j] + u[j])"),
     ("readout of S, not S^T", r"o\[j\] \+= q\[c\] \* S\[c \* dv \+ j\];",
      "o[j] += q[c] * S[(j % dk) * dv + (c % dv)];"),
     ("beta squared", r"S\[c \* dv \+ j\] \+= b \* k", "S[c * dv + j] += b * b * k"),
+]
+
+# Mistakes in the backward's adjoint steps (each pattern occurs only there).
+BWD_MUTANTS = [
+    ("bwd readout term dropped", r"dS\[c \* dv \+ j\] \+= q\[c\] \* dO\[j\];", ";"),
+    ("bwd erase term dropped", r"dS\[c \* dv \+ j\] \+= k\[c\] \* \(-b \* dd\[j\]\);", ";"),
+    ("bwd gate gradient against S_t", r"acc \+= dS\[c \* dv \+ j\] \* P\[c \* dv \+ j\];",
+     "acc += dS[c * dv + j] * S[c * dv + j];"),
+    ("bwd state gradient not decayed", r"dS\[c \* dv \+ j\] \*= a\[c\];", ";"),
+    ("bwd beta gradient without u", r"db \+= \(v\[j\] - u\[j\]\) \* dd\[j\];",
+     "db += v[j] * dd[j];"),
+    ("bwd key gradient against the old state",
+     r"acc \+= Sp\[c \* dv \+ j\] \* \(-b \* dd\[j\]\);",
+     "acc += P[c * dv + j] * (-b * dd[j]);"),
+    ("bwd query gradient against S'", r"acc \+= S\[c \* dv \+ j\] \* dO\[j\];",
+     "acc += Sp[c * dv + j] * dO[j];"),
+]
+
+BWD_PIN_TESTS = [
+    bpins.test_backward_matches_finite_differences_uniform,
+    bpins.test_backward_matches_finite_differences_packed,
+    bpins.test_backward_beta_zero_unit_gate_closed_form,
+    bpins.test_backward_first_token_from_zero_state_closed_form,
 ]
 
 PIN_TESTS = [
@@ -48,8 +74,8 @@ def _build_mutant(src, tmp):
     return so
 
 
-def _pins_fail():
-    for t in PIN_TESTS:
+def _pins_fail(tests=None):
+    for t in (PIN_TESTS if tests is None else tests):
         try:
             with np.errstate(all="ignore"):
                 t()
@@ -71,5 +97,19 @@ def test_pins_catch_mutant(name, pat, rep, monkeypatch):
     monkeypatch.setattr(oracle, "_lib", None)
 
 
+@pytest.mark.parametrize("name,pat,rep", BWD_MUTANTS, ids=[m[0] for m in BWD_MUTANTS])
+def test_backward_pins_catch_mutant(name, pat, rep, monkeypatch):
+    src = open(SRC).read()
+    mutated, n = re.subn(pat, rep, src)
+    assert n == 1, "mutation pattern must match exactly one place in the backward"
+    with tempfile.TemporaryDirectory() as tmp:
+        so = _build_mutant(mutated, tmp)
+        monkeypatch.setattr(oracle, "_LIB_PATH", so)
+        monkeypatch.setattr(oracle, "_lib", None)
+        assert _pins_fail(BWD_PIN_TESTS), f"no backward pin caught the planted mistake: {name}"
+    monkeypatch.setattr(oracle, "_lib", None)
+
+
 def test_unmutated_oracle_passes_pins():
     assert not _pins_fail()
+    assert not _pins_fail(BWD_PIN_TESTS)
