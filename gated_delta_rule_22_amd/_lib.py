@@ -46,6 +46,10 @@ def library() -> ctypes.CDLL:
         lib.kda_forward.restype = ci
         lib.ckda_forward_ex.argtypes = [vp] * 7 + [ci] * 8 + [vp, vp, vp, sz, vp]
         lib.ckda_forward_ex.restype = ci
+        lib.ckda_backward_workspace_bytes.argtypes = [ci] * 7
+        lib.ckda_backward_workspace_bytes.restype = sz
+        lib.ckda_backward.argtypes = [vp] * 7 + [ci] * 7 + [vp] * 8 + [vp, sz, vp]
+        lib.ckda_backward.restype = ci
         lib.ckda_decode_step.argtypes = [vp] * 7 + [ci] * 5 + [vp]
         lib.ckda_decode_step.restype = ci
         _lib = lib
@@ -157,6 +161,53 @@ def _forward(entry, q, k, v, g, beta, S0, cu_seqlens, out, final_state, workspac
     st = fn(*head, opts, *tail) if entry == "ckda_forward_ex" else fn(*head, *tail)
     _check(st, entry)
     return o, S_T
+
+
+def backward_workspace_bytes(B, T, H, dk, dv, N, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else (CKDA_BF16 if dtype == torch.bfloat16 else CKDA_F32)
+    return int(library().ckda_backward_workspace_bytes(B, T, H, dk, dv, N, code))
+
+
+def backward(q, k, v, g, beta, do, S0=None, dS_T=None, cu_seqlens=None, *, workspace=None,
+             need_dS0=True):
+    """Gradients of ``sum(do * o) + sum(dS_T * S_T)`` for the forward's inputs:
+    returns ``(dq, dk, dv, dg, dbeta, dS0)`` as fp32 tensors (``dS0`` is None
+    when ``need_dS0`` is False).  See ``ckda_backward`` in include/ckda.h."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    code = _dtype_code(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype)
+    _need(k, "k", shape=(B, T, H, dk))
+    _need(v, "v", shape=(B, T, H, dv))
+    _need(g, "g", torch.float32, (B, T, H, dk))
+    _need(beta, "beta", torch.float32, (B, T, H))
+    _need(do, "do", torch.float32, (B, T, H, dv))
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32)
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    for t, n in ((S0, "S0"), (dS_T, "dS_T")):
+        if t is not None:
+            _need(t, n, torch.float32, (N, H, dk, dv))
+    dev = q.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    dq = torch.empty((B, T, H, dk), **f32)
+    dk_ = torch.empty((B, T, H, dk), **f32)
+    dv_ = torch.empty((B, T, H, dv), **f32)
+    dg = torch.empty((B, T, H, dk), **f32)
+    db = torch.empty((B, T, H), **f32)
+    dS0 = torch.empty((N, H, dk, dv), **f32) if need_dS0 else None
+    ws_bytes = backward_workspace_bytes(B, T, H, dk, dv, N, code)
+    if workspace is None or workspace.numel() * workspace.element_size() < ws_bytes:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    st = library().ckda_backward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(cu_seqlens),
+        B, T, H, dk, dv, N, code, _ptr(do), _ptr(dS_T), _ptr(dq), _ptr(dk_), _ptr(dv_),
+        _ptr(dg), _ptr(db), _ptr(dS0), _ptr(workspace), ws_bytes, _stream(dev))
+    _check(st, "ckda_backward")
+    return dq, dk_, dv_, dg, db, dS0
 
 
 def decode_step(q, k, v, g, beta, S, *, out=None):

@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libckda.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.hip", "schedule.hip", "decode.hip", "fwd_f64.hip", "fwd_bf16.hip"]
+SOURCES = ["api.hip", "schedule.hip", "decode.hip", "fwd_f64.hip", "fwd_bf16.hip", "bwd_f64.hip"]
 
 # Packed fp32 VALU ops stay off: the compiler is not allowed to form them.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

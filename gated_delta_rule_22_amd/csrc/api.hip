@@ -24,6 +24,31 @@ FwdLayout fwd_layout(int B, int T, int H, int dk, int dv, int N, int in_dtype) {
   return L;
 }
 
+// Backward workspace: the sequence table, then per (chunk, head) the fp64
+// record, the state entering the chunk, U, dU, the state gradient at the
+// chunk's end and the per-chunk scratch, each region 256-byte aligned.
+struct BwdLayout {
+  size_t table, rec_bytes, n_chunks_ub;
+  size_t records, S, U, dU, dSe, scratch, total;   // byte offsets, then the total
+};
+
+static BwdLayout bwd_layout(int B, int T, int H, int dk, int dv, int N) {
+  BwdLayout L{};
+  const FwdLayout F = fwd_layout(B, T, H, dk, dv, N, CKDA_F32);
+  const size_t ch = F.n_chunks_ub * (size_t)H;
+  L.n_chunks_ub = F.n_chunks_ub;
+  L.rec_bytes = F.rec_bytes;
+  L.table = F.table_bytes;
+  L.records = L.table;
+  L.S = L.records + align256(ch * L.rec_bytes);
+  L.U = L.S + align256(ch * dk * dv * sizeof(double));
+  L.dU = L.U + align256(ch * kChunk * dv * sizeof(double));
+  L.dSe = L.dU + align256(ch * kChunk * dv * sizeof(double));
+  L.scratch = L.dSe + align256(ch * dk * dv * sizeof(double));
+  L.total = L.scratch + align256(ch * f64_bwd_scratch_bytes(dk, dv));
+  return L;
+}
+
 SeqTable seq_table(void *workspace, int N) {
   int32_t *base = static_cast<int32_t *>(workspace);
   SeqTable t;
@@ -171,6 +196,63 @@ extern "C" int ckda_forward_ex(const void *q, const void *k, const void *v, cons
                                size_t workspace_bytes, void *stream) {
   return forward_impl(q, k, v, g, beta, S0, cu_seqlens, B, T, H, dk, dv, N, in_dtype, options, o,
                       S_T, workspace, workspace_bytes, stream);
+}
+
+extern "C" size_t ckda_backward_workspace_bytes(int B, int T, int H, int dk, int dv, int N,
+                                                int in_dtype) {
+  if (forward_shape_status(B, T, H, dk, dv, N, in_dtype, B == 1 && N != B) != CKDA_OK) return 0;
+  return bwd_layout(B, T, H, dk, dv, N).total;
+}
+
+extern "C" int ckda_backward(const void *q, const void *k, const void *v, const float *g,
+                             const float *beta, const float *S0, const int32_t *cu_seqlens,
+                             int B, int T, int H, int dk, int dv, int N, int in_dtype,
+                             const float *d_o, const float *dS_T, float *dq, float *dk_out,
+                             float *dv_out, float *dg, float *dbeta, float *dS0, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+  const bool packed = cu_seqlens != nullptr;
+  if (int s = forward_shape_status(B, T, H, dk, dv, N, in_dtype, packed)) return s;
+  const size_t rows = (size_t)B * T * H;
+  if (rows > 0 && (!q || !k || !v || !g || !beta || !d_o || !dq || !dk_out || !dv_out || !dg ||
+                   !dbeta))
+    return CKDA_ERR_NULL;
+  const void *ptrs[] = {q, k, v, g, S0, d_o, dS_T, dq, dk_out, dv_out, dg, dS0, workspace};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return CKDA_ERR_ALIGN;
+  if ((beta && !aligned4(beta)) || (dbeta && !aligned4(dbeta)) ||
+      (cu_seqlens && !aligned4(cu_seqlens)))
+    return CKDA_ERR_ALIGN;
+
+  const size_t in_sz = in_dtype == CKDA_BF16 ? 2 : 4;
+  const size_t st_bytes = (size_t)N * H * dk * dv * 4;
+  const BwdLayout L = bwd_layout(B, T, H, dk, dv, N);
+  struct Span { const void *p; size_t n; };
+  const Span ins[] = {{q, rows * dk * in_sz}, {k, rows * dk * in_sz}, {v, rows * dv * in_sz},
+                      {g, rows * dk * 4},      {beta, rows * 4},       {S0, st_bytes},
+                      {cu_seqlens, ((size_t)N + 1) * 4}, {d_o, rows * dv * 4}, {dS_T, st_bytes}};
+  const Span outs[] = {{dq, rows * dk * 4}, {dk_out, rows * dk * 4}, {dv_out, rows * dv * 4},
+                       {dg, rows * dk * 4}, {dbeta, rows * 4},       {dS0, st_bytes},
+                       {workspace, L.total}};
+  const int n_outs = sizeof(outs) / sizeof(outs[0]);
+  for (int a = 0; a < n_outs; ++a) {
+    for (const Span &s : ins)
+      if (overlaps(outs[a].p, outs[a].n, s.p, s.n)) return CKDA_ERR_ALIAS;
+    for (int b = a + 1; b < n_outs; ++b)
+      if (overlaps(outs[a].p, outs[a].n, outs[b].p, outs[b].n)) return CKDA_ERR_ALIAS;
+  }
+  if (!workspace || workspace_bytes < L.total) return CKDA_ERR_WORKSPACE;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const SeqTable tab = seq_table(workspace, N);
+  if (launch_seq_table(cu_seqlens, B, T, N, tab, st) != hipSuccess) return CKDA_ERR_LAUNCH;
+  char *w = static_cast<char *>(workspace);
+  hipError_t e = launch_bwd_f64(
+      q, k, v, g, beta, S0, d_o, dS_T, H, dk, dv, N, in_dtype, tab, L.n_chunks_ub,
+      w + L.records, L.rec_bytes, reinterpret_cast<double *>(w + L.S),
+      reinterpret_cast<double *>(w + L.U), reinterpret_cast<double *>(w + L.dU),
+      reinterpret_cast<double *>(w + L.dSe), reinterpret_cast<double *>(w + L.scratch), dq,
+      dk_out, dv_out, dg, dbeta, dS0, st);
+  return e == hipSuccess ? CKDA_OK : CKDA_ERR_LAUNCH;
 }
 
 extern "C" int ckda_decode_step(const void *q, const void *k, const void *v, const float *g,

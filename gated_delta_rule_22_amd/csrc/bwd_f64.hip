@@ -1,0 +1,501 @@
+// Chunkwise CKDA backward, computed in fp64.
+//
+// Gradient of L = sum(dO * o) + sum(dS_T * S_T) for the recurrence of the
+// blog post "One update, one quarter turn" (ELI5, "The mirror") with the
+// readout o_t = S_t^T q_t, through the chunk algebra of the forward (names as
+// in the record of f64_common.h; inside a chunk with incoming state S):
+//
+//   U  = T X,  X = Diag(beta) (V - (gamma*K) S),  T = (I + A)^-1
+//   O  = (gamma*Q) S + P U
+//   S' = Diag(gamma_n) S + KH^T U
+//
+// Reverse mode, given dO and dS' (the gradient reaching the chunk's end):
+//
+//   dU = KH dS' + P^T dO
+//   dS = Diag(gamma_n) dS' + (gamma*Q)^T dO - W^T dU         (to the previous chunk)
+//   dX = T^T dU,  dV = Diag(beta) dX,  dP = tril(dO U^T),  dA = -strict_tril(dX U^T)
+//   dbeta_i = dX_i . V_i - (gamma*K)_i . (dX S^T)_i + sum_j (A/beta)_ij dA_ij
+//
+// and the key, query and gate gradients collect, per (token i, channel c), the
+// direct terms from gamma*Q, gamma*K and KH and the pair terms from A and P,
+// each of which carries the ratio r_ij = gamma_i / gamma_j.  Because every
+// term depends on the gates only through the in-chunk log-magnitudes
+// Gamma_i = sum_{s<=i} ln|alpha_s|, the gradient with respect to Gamma_i is
+// the sum of those terms weighted +1 where Gamma_i appears in a numerator and
+// -1 in a denominator; then dln|alpha_s| = sum_{i>=s} dGamma_i (a reverse
+// cumulative sum inside the chunk) and dalpha_s = dln|alpha_s| / alpha_s.  The
+// gate signs are piecewise constant and carry no gradient.
+//
+// Kernels (all arithmetic fp64; gradients are written as fp32):
+//   records and the forward's serial pass  (fwd_f64.hip), keeping the state
+//              entering every chunk and every chunk's U;
+//   f64_bwd_state  grid (dv blocks x sequences x heads): the reverse serial
+//              pass over chunks for dS, writing dU and dS' of every chunk and
+//              dS0;
+//   f64_bwd_chunk  grid (chunks, heads): everything else, one chunk per
+//              workgroup, with the dense products as LDS-tiled fp64 loops and
+//              the ratio-weighted pair sums channel group by channel group.
+#include "f64_common.h"
+
+namespace ckda {
+namespace {
+
+using namespace f64;
+
+// --------------------------------------------------------------------------
+// f64_bwd_state: reverse serial pass of dS over the chunks of one
+// (sequence, head, 32-column block).
+template <int DK, int DV>
+__global__ __launch_bounds__(kThreads) void f64_bwd_state(
+    const float *__restrict__ dO, const float *__restrict__ dS_T, int H, int N, SeqTable tab,
+    const double *__restrict__ records, size_t rec_doubles, double *__restrict__ dU_chunks,
+    double *__restrict__ dSe_chunks, float *__restrict__ dS0) {
+  using R = Rec<DK, DV>;
+  __shared__ double s_dS[DK * kBV];
+  __shared__ double s_dO[C * kBV];
+  __shared__ double s_dU[C * kBV];
+
+  constexpr int NV = DV / kBV;
+  const int jb = blockIdx.x % NV, rh = blockIdx.x / NV, t = threadIdx.x;
+  const int n = tab.order[rh / H], h = rh % H;
+  const int len = tab.seq_len[n], start = tab.seq_start[n];
+  const int nch = (len + C - 1) / C;
+  const size_t sbase = ((size_t)n * H + h) * DK * DV + (size_t)jb * kBV;
+
+  for (int p = t; p < DK * kBV; p += kThreads) {
+    const int c = p / kBV, j = p % kBV;
+    s_dS[p] = dS_T ? (double)dS_T[sbase + (size_t)c * DV + j] : 0.0;
+  }
+  for (int lc = nch - 1; lc >= 0; --lc) {
+    const size_t ch = (size_t)(tab.chunk_off[n] + lc) * H + h;
+    const double *rec = records + ch * rec_doubles;
+    const int nt = min(C, len - lc * C);
+    __syncthreads();
+    for (int p = t; p < C * kBV; p += kThreads) {
+      const int i = p / kBV, j = p % kBV;
+      s_dO[p] = i < nt ? (double)dO[((size_t)(start + lc * C + i) * H + h) * DV + jb * kBV + j]
+                       : 0.0;
+    }
+    for (int p = t; p < DK * kBV; p += kThreads)
+      dSe_chunks[ch * DK * DV + (size_t)(p / kBV) * DV + jb * kBV + p % kBV] = s_dS[p];
+    __syncthreads();
+    // dU = KH dS' + P^T dO   (P is lower triangular: P_mi = 0 for m < i)
+    for (int p = t; p < C * kBV; p += kThreads) {
+      const int i = p / kBV, j = p % kBV;
+      double acc = 0.0;
+      for (int c = 0; c < DK; ++c) acc += rec[R::KH + i * DK + c] * s_dS[c * kBV + j];
+      for (int m = i; m < C; ++m) acc += rec[R::P + m * C + i] * s_dO[m * kBV + j];
+      s_dU[p] = acc;
+      dU_chunks[ch * C * DV + (size_t)i * DV + jb * kBV + j] = acc;
+    }
+    __syncthreads();
+    // dS = Diag(gamma_n) dS' + (gamma Q)^T dO - W^T dU   (element-wise in place)
+    for (int p = t; p < DK * kBV; p += kThreads) {
+      const int c = p / kBV, j = p % kBV;
+      double acc = rec[R::GN + c] * s_dS[p];
+      for (int i = 0; i < C; ++i)
+        acc += rec[R::QT + i * DK + c] * s_dO[i * kBV + j] - rec[R::W + i * DK + c] * s_dU[i * kBV + j];
+      s_dS[p] = acc;
+    }
+  }
+  __syncthreads();
+  if (dS0)
+    for (int p = t; p < DK * kBV; p += kThreads) {
+      const int c = p / kBV, j = p % kBV;
+      dS0[sbase + (size_t)c * DV + j] = (float)s_dS[p];
+    }
+}
+
+// --------------------------------------------------------------------------
+// Out(m, n) = sum_{kk < K} A(m, kk) B(kk, n) for m < 64 and n < NB, in fp64,
+// staged through LDS in K-slices of 16.  Thread t owns rows 4 (t / 16) + r
+// (r < 4) and columns t % 16 + 16 jj (jj < NB / 16); the sums are returned in
+// acc[r][jj].  A_MFAST / B_KFAST choose which index runs fastest across
+// threads while staging, so that transposed sources are read along their
+// contiguous axis.  Every thread of the block must call it.
+constexpr int kKB = 16;
+constexpr int kStageA = 64 * (kKB + 1);
+
+template <int NB, int K, bool A_MFAST, bool B_KFAST, typename FA, typename FB>
+__device__ __forceinline__ void gemm64(double *sA, double *sB, const FA &fa, const FB &fb,
+                                       double (&acc)[4][NB / 16]) {
+  static_assert(K % kKB == 0, "K must be a multiple of 16");
+  constexpr int SA = kKB + 1, SB = NB + 1;
+  const int t = threadIdx.x, rgp = t >> 4, cl = t & 15;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int jj = 0; jj < NB / 16; ++jj) acc[r][jj] = 0.0;
+  for (int k0 = 0; k0 < K; k0 += kKB) {
+    __syncthreads();
+    for (int p = t; p < 64 * kKB; p += kThreads) {
+      const int m = A_MFAST ? p % 64 : p / kKB, kk = A_MFAST ? p / 64 : p % kKB;
+      sA[m * SA + kk] = fa(m, k0 + kk);
+    }
+    for (int p = t; p < kKB * NB; p += kThreads) {
+      const int kk = B_KFAST ? p % kKB : p / NB, n = B_KFAST ? p / kKB : p % NB;
+      sB[kk * SB + n] = fb(k0 + kk, n);
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int kk = 0; kk < kKB; ++kk) {
+      double a[4], b[NB / 16];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) a[r] = sA[(rgp * 4 + r) * SA + kk];
+#pragma unroll
+      for (int jj = 0; jj < NB / 16; ++jj) b[jj] = sB[kk * SB + cl + 16 * jj];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int jj = 0; jj < NB / 16; ++jj) acc[r][jj] = fma(a[r], b[jj], acc[r][jj]);
+    }
+  }
+  __syncthreads();
+}
+
+// Sum over the 16 lanes that share a row group (lanes 16 g .. 16 g + 15).
+__device__ __forceinline__ double sum16(double x) {
+  x += __shfl_xor(x, 1);
+  x += __shfl_xor(x, 2);
+  x += __shfl_xor(x, 4);
+  x += __shfl_xor(x, 8);
+  return x;
+}
+
+// Per-chunk scratch (doubles): dX [C][DV], G [C][DK], sign [C][DK].
+template <int DK, int DV>
+struct Scr {
+  static constexpr size_t DX = 0;
+  static constexpr size_t G = DX + C * DV;
+  static constexpr size_t SG = G + C * DK;
+  static constexpr size_t SIZE = SG + C * DK;
+};
+
+constexpr int kCG = 16;                  // channels per group in the pair sums
+
+// --------------------------------------------------------------------------
+// f64_bwd_chunk: all per-chunk gradients of one (chunk, head).
+template <typename TIn, int DK, int DV>
+__global__ __launch_bounds__(kThreads) void f64_bwd_chunk(
+    const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
+    const float *__restrict__ g, const float *__restrict__ beta, const float *__restrict__ dO,
+    int H, int N, SeqTable tab, const double *__restrict__ records, size_t rec_doubles,
+    const double *__restrict__ S_chunks, const double *__restrict__ U_chunks,
+    const double *__restrict__ dU_chunks, const double *__restrict__ dSe_chunks,
+    double *__restrict__ scratch, float *__restrict__ dq, float *__restrict__ dk,
+    float *__restrict__ dv, float *__restrict__ dg, float *__restrict__ dbeta) {
+  using R = Rec<DK, DV>;
+  using X = Scr<DK, DV>;
+  constexpr int NBM = DV > 64 ? DV : 64;
+  constexpr int kStage = kStageA + kKB * (NBM + 1);
+  constexpr int kGroup = 4 * C * kCG;
+  __shared__ double s_P[C * (C + 1)];     // dP (lower incl.)
+  __shared__ double s_DA[C * (C + 1)];    // beta_i dA_ij (strictly lower)
+  __shared__ double s_u[kStage > kGroup ? kStage : kGroup];  // GEMM staging | group operands
+  __shared__ double s_aq[C * kCG], s_ak[C * kCG], s_ag[C * kCG];
+  __shared__ double s_beta[C], s_db[C];
+  __shared__ double s_R[DK];
+  __shared__ int s_fb[DK];
+  __shared__ double s_red[4 * kCG], s_red2[16 * kCG], s_dGn[kCG];
+
+  const int cflat = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+  if (cflat >= tab.chunk_off[N]) return;
+  const int n = find_seq(tab.chunk_off, N, cflat);
+  const int lc = cflat - tab.chunk_off[n];
+  const int t0 = tab.seq_start[n] + lc * C;
+  const int nt = min(C, tab.seq_len[n] - lc * C);
+  const size_t ch = (size_t)cflat * H + h;
+  const double *rec = records + ch * rec_doubles;
+  const double *Sc = S_chunks + ch * DK * DV;
+  const double *dSe = dSe_chunks + ch * DK * DV;
+  const double *Uc = U_chunks + ch * C * DV;
+  const double *dUc = dU_chunks + ch * C * DV;
+  double *scr = scratch + ch * X::SIZE;
+  const int rgp = t >> 4, cl = t & 15, wave = t >> 6;
+  double *sA = s_u, *sB = s_u + kStageA;
+
+  auto row = [&](int i) { return (size_t)(t0 + i) * H + h; };   // token-head row
+  auto dO_at = [&](int m, int c) {
+    return m < nt ? (double)dO[row(m) * DV + c] : 0.0;
+  };
+
+  // ---- phase 0: in-chunk gate log-magnitudes and signs, per channel.
+  if (t < DK) {
+    double G = 0.0, gmax = 0.0, gmin = 0.0;
+    bool par = false;
+    for (int i = 0; i < C; ++i) {
+      const float a = i < nt ? g[row(i) * DK + t] : 1.f;
+      G += fmax(log2(fabs((double)a)), kLog2Floor);
+      par ^= (a < 0.f);
+      gmax = fmax(gmax, G);
+      gmin = fmin(gmin, G);
+      scr[X::G + i * DK + t] = G;
+      scr[X::SG + i * DK + t] = par ? -1.0 : 1.0;
+    }
+    // The pair sums form r_ij = e_i f_j with e = sign 2^(G - Rm), f = sign 2^(Rm - G)
+    // about the midpoint Rm of the channel's range; beyond +-1000 binary orders
+    // that product could leave fp64's range, and the channel takes exp2 per pair.
+    s_R[t] = 0.5 * (gmax + gmin);
+    s_fb[t] = (gmax - gmin) > 2000.0;
+  }
+  if (t < C) {
+    s_beta[t] = t < nt ? (double)beta[row(t)] : 0.0;
+    s_db[t] = 0.0;
+  }
+  __threadfence();
+  __syncthreads();
+
+  // ---- phase 1: dX = T^T dU; dV = Diag(beta) dX; dbeta += dX_i . V_i
+  {
+    double acc[4][DV / 16];
+    gemm64<DV, C, true, false>(
+        sA, sB, [&](int m, int kk) { return rec[R::TI + kk * C + m]; },
+        [&](int kk, int nn) { return dUc[kk * DV + nn]; }, acc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = rgp * 4 + r;
+      double part = 0.0;
+#pragma unroll
+      for (int jj = 0; jj < DV / 16; ++jj) {
+        const int nn = cl + 16 * jj;
+        scr[X::DX + m * DV + nn] = acc[r][jj];
+        if (m < nt) {
+          dv[row(m) * DV + nn] = (float)(s_beta[m] * acc[r][jj]);
+          part += acc[r][jj] * (double)to_f32(v[row(m) * DV + nn]);
+        }
+      }
+      part = sum16(part);
+      if (cl == 0) s_db[m] += part;
+    }
+  }
+  __threadfence();
+  __syncthreads();
+
+  // ---- phase 2: dP = tril(dO U^T) and beta_i dA_ij, dA = -strict_tril(dX U^T)
+  {
+    double acc[4][4];
+    gemm64<64, DV, false, true>(
+        sA, sB, dO_at, [&](int kk, int nn) { return Uc[nn * DV + kk]; }, acc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int m = rgp * 4 + r, j = cl + 16 * jj;
+        s_P[m * (C + 1) + j] = j <= m ? acc[r][jj] : 0.0;
+      }
+    gemm64<64, DV, false, true>(
+        sA, sB, [&](int m, int kk) { return scr[X::DX + m * DV + kk]; },
+        [&](int kk, int nn) { return Uc[nn * DV + kk]; }, acc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = rgp * 4 + r;
+      double part = 0.0;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int j = cl + 16 * jj;
+        const double dA = j < m ? -acc[r][jj] : 0.0;
+        s_DA[m * (C + 1) + j] = s_beta[m] * dA;
+        part += rec[R::AH + m * C + j] * dA;
+      }
+      part = sum16(part);
+      if (cl == 0) s_db[m] += part;
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 3: per group of 16 channels
+  for (int c0 = 0; c0 < DK; c0 += kCG) {
+    const int c = c0 + cl;                   // this thread's channel in the GEMMs
+    double acc[4][1];
+    // dQT = dO S^T: dq += gamma dQT; dGamma += q gamma dQT
+    gemm64<kCG, DV, false, true>(
+        sA, sB, dO_at, [&](int kk, int nn) { return Sc[(c0 + nn) * DV + kk]; }, acc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = rgp * 4 + r;
+      const double gam = scr[X::SG + m * DK + c] * exp2(scr[X::G + m * DK + c]);
+      s_aq[m * kCG + cl] = gam * acc[r][0];
+      s_ag[m * kCG + cl] = rec[R::QT + m * DK + c] * acc[r][0];
+    }
+    // M5 = dX S^T; d(gamma K) = -Diag(beta) M5
+    gemm64<kCG, DV, false, true>(
+        sA, sB, [&](int m, int kk) { return scr[X::DX + m * DV + kk]; },
+        [&](int kk, int nn) { return Sc[(c0 + nn) * DV + kk]; }, acc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = rgp * 4 + r;
+      const double gam = scr[X::SG + m * DK + c] * exp2(scr[X::G + m * DK + c]);
+      const double gk = rec[R::GK + m * DK + c];
+      s_ak[m * kCG + cl] = -s_beta[m] * gam * acc[r][0];
+      s_ag[m * kCG + cl] -= s_beta[m] * gk * acc[r][0];
+      const double part = sum16(-gk * acc[r][0]);
+      if (cl == 0) s_db[m] += part;
+    }
+    // dKH = U dS'^T: dk += (gamma_n / gamma) dKH; dGamma_i -= k (gamma_n/gamma) dKH,
+    // and the same amount, summed over i, goes to dGamma_n.
+    gemm64<kCG, DV, false, true>(
+        sA, sB, [&](int m, int kk) { return Uc[m * DV + kk]; },
+        [&](int kk, int nn) { return dSe[(c0 + nn) * DV + kk]; }, acc);
+    {
+      const double Gn = scr[X::G + (C - 1) * DK + c], sn = scr[X::SG + (C - 1) * DK + c];
+      double col = 0.0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = rgp * 4 + r;
+        const double khr = scr[X::SG + m * DK + c] * sn * exp2(Gn - scr[X::G + m * DK + c]);
+        const double term = rec[R::KH + m * DK + c] * acc[r][0];
+        s_ak[m * kCG + cl] += khr * acc[r][0];
+        s_ag[m * kCG + cl] -= term;
+        col += term;
+      }
+      col += __shfl_xor(col, 16);
+      col += __shfl_xor(col, 32);
+      if ((t & 63) < 16) s_red[wave * kCG + cl] = col;
+    }
+    // gamma_n sum_j dS'[c][j] S[c][j] for the group's channels
+    {
+      double part = 0.0;
+      for (int j = rgp; j < DV; j += 16) part += dSe[c * DV + j] * Sc[c * DV + j];
+      s_red2[rgp * kCG + cl] = part;
+    }
+    __syncthreads();
+    // stage the group's ratio factors and keys/queries; finish dGamma_n
+    {
+      double *e = s_u, *f = s_u + C * kCG, *kk_ = s_u + 2 * C * kCG, *qq = s_u + 3 * C * kCG;
+      for (int p = t; p < C * kCG; p += kThreads) {
+        const int i = p / kCG, cc = c0 + p % kCG;
+        const double G = scr[X::G + i * DK + cc], sg = scr[X::SG + i * DK + cc];
+        if (s_fb[cc]) {
+          e[p] = G;
+          f[p] = sg;
+        } else {
+          e[p] = sg * exp2(G - s_R[cc]);
+          f[p] = sg * exp2(s_R[cc] - G);
+        }
+        kk_[p] = i < nt ? (double)to_f32(k[row(i) * DK + cc]) : 0.0;
+        qq[p] = i < nt ? (double)to_f32(q[row(i) * DK + cc]) : 0.0;
+      }
+      if (t < kCG) {
+        double s = 0.0, col = 0.0;
+        for (int w = 0; w < 4; ++w) col += s_red[w * kCG + t];
+        for (int sgm = 0; sgm < 16; ++sgm) s += s_red2[sgm * kCG + t];
+        s_dGn[t] = col + rec[R::GN + c0 + t] * s;
+      }
+    }
+    __syncthreads();
+    // pair sums; thread (channel cl, rows i = rgp + 16 u)
+    {
+      const double *e = s_u, *f = s_u + C * kCG, *kk_ = s_u + 2 * C * kCG, *qq = s_u + 3 * C * kCG;
+      const bool fb = s_fb[c];
+#pragma unroll 1
+      for (int u = 0; u < C / 16; ++u) {
+        const int i = rgp + 16 * u;
+        double R1 = 0.0, R2 = 0.0, C1 = 0.0, C2 = 0.0;
+        const double ei = e[i * kCG + cl], fi = f[i * kCG + cl];
+        // row i: sum over j <= i of dP_ij k_j r_ij and (beta dA)_ij k_j r_ij
+        for (int j = 0; j <= i; ++j) {
+          const double r = fb ? fi * f[j * kCG + cl] * exp2(ei - e[j * kCG + cl])
+                              : ei * f[j * kCG + cl];
+          const double kr = kk_[j * kCG + cl] * r;
+          R1 = fma(s_P[i * (C + 1) + j], kr, R1);
+          R2 = fma(s_DA[i * (C + 1) + j], kr, R2);
+        }
+        // column i: sum over m >= i of (beta dA)_mi k_m r_mi and dP_mi q_m r_mi
+        for (int m = i; m < C; ++m) {
+          const double r = fb ? f[m * kCG + cl] * fi * exp2(e[m * kCG + cl] - ei)
+                              : e[m * kCG + cl] * fi;
+          C1 = fma(s_DA[m * (C + 1) + i], kk_[m * kCG + cl] * r, C1);
+          C2 = fma(s_P[m * (C + 1) + i], qq[m * kCG + cl] * r, C2);
+        }
+        const double ki = kk_[i * kCG + cl], qi = qq[i * kCG + cl];
+        const double gq = s_aq[i * kCG + cl] + R1;
+        const double gk = s_ak[i * kCG + cl] + R2 + C1 + C2;
+        double gG = s_ag[i * kCG + cl] + qi * R1 + ki * (R2 - C1 - C2);
+        if (i == C - 1) gG += s_dGn[cl];
+        s_ag[i * kCG + cl] = gG;
+        if (i < nt) {
+          dq[row(i) * DK + c] = (float)gq;
+          dk[row(i) * DK + c] = (float)gk;
+        }
+      }
+    }
+    __syncthreads();
+    // dln|alpha_s| = sum_{i >= s} dGamma_i; dalpha = dln|alpha| / alpha
+    if (t < kCG) {
+      const int cc = c0 + t;
+      double acc2 = 0.0;
+      for (int i = C - 1; i >= 0; --i) {
+        acc2 += s_ag[i * kCG + t];
+        if (i < nt) {
+          const double a = (double)g[row(i) * DK + cc];
+          const double floor_mag = exp2(kLog2Floor);
+          const double ae = fabs(a) < floor_mag ? (a < 0.0 ? -floor_mag : floor_mag) : a;
+          dg[row(i) * DK + cc] = (float)(acc2 / ae);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (t < nt) dbeta[row(t)] = (float)s_db[t];
+}
+
+template <typename TIn, int DK, int DV>
+hipError_t launch_bwd_shape(const void *q, const void *k, const void *v, const float *g,
+                            const float *beta, const float *dO, const float *dS_T, int H, int N,
+                            SeqTable tab, size_t n_chunks_ub, const double *records,
+                            size_t rec_bytes, const double *S_chunks, const double *U_chunks,
+                            double *dU_chunks, double *dSe_chunks, double *scratch, float *dq,
+                            float *dk, float *dv, float *dg, float *dbeta, float *dS0,
+                            hipStream_t stream) {
+  const size_t rec_doubles = rec_bytes / sizeof(double);
+  hipLaunchKernelGGL((f64_bwd_state<DK, DV>), dim3((DV / kBV) * N * H), dim3(kThreads), 0, stream,
+                     dO, dS_T, H, N, tab, records, rec_doubles, dU_chunks, dSe_chunks, dS0);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || n_chunks_ub == 0) return e;
+  hipLaunchKernelGGL((f64_bwd_chunk<TIn, DK, DV>), dim3((unsigned)n_chunks_ub, H), dim3(kThreads),
+                     0, stream, static_cast<const TIn *>(q), static_cast<const TIn *>(k),
+                     static_cast<const TIn *>(v), g, beta, dO, H, N, tab, records, rec_doubles,
+                     S_chunks, U_chunks, dU_chunks, dSe_chunks, scratch, dq, dk, dv, dg, dbeta);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t f64_bwd_scratch_bytes(int dk, int dv) {
+  return sizeof(double) * ((size_t)C * dv + 2 * (size_t)C * dk);
+}
+
+hipError_t launch_bwd_f64(const void *q, const void *k, const void *v, const float *g,
+                          const float *beta, const float *S0, const float *dO, const float *dS_T,
+                          int H, int dk, int dv, int N, int in_dtype, SeqTable tab,
+                          size_t n_chunks_ub, void *records, size_t rec_bytes, double *S_chunks,
+                          double *U_chunks, double *dU_chunks, double *dSe_chunks,
+                          double *scratch, float *dq, float *dk_out, float *dv_out, float *dg,
+                          float *dbeta, float *dS0, hipStream_t stream) {
+  hipError_t e = launch_f64_pass(q, k, v, g, beta, S0, H, dk, dv, N, in_dtype, tab, n_chunks_ub,
+                                 records, rec_bytes, nullptr, nullptr, 1, 0, 0, S_chunks,
+                                 U_chunks, stream);
+  if (e != hipSuccess) return e;
+  const double *rec = static_cast<const double *>(records);
+#define CKDA_BWD_CASE(TIN, DK_, DV_)                                                           \
+  if (dk == DK_ && dv == DV_)                                                                  \
+    return launch_bwd_shape<TIN, DK_, DV_>(q, k, v, g, beta, dO, dS_T, H, N, tab, n_chunks_ub,  \
+                                           rec, rec_bytes, S_chunks, U_chunks, dU_chunks,      \
+                                           dSe_chunks, scratch, dq, dk_out, dv_out, dg, dbeta, \
+                                           dS0, stream);
+  if (in_dtype == CKDA_BF16) {
+    CKDA_BWD_CASE(__hip_bfloat16, 64, 64)
+    CKDA_BWD_CASE(__hip_bfloat16, 64, 128)
+    CKDA_BWD_CASE(__hip_bfloat16, 128, 64)
+    CKDA_BWD_CASE(__hip_bfloat16, 128, 128)
+  } else {
+    CKDA_BWD_CASE(float, 64, 64)
+    CKDA_BWD_CASE(float, 64, 128)
+    CKDA_BWD_CASE(float, 128, 64)
+    CKDA_BWD_CASE(float, 128, 128)
+  }
+#undef CKDA_BWD_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ckda

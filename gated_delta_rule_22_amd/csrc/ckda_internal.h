@@ -63,4 +63,16 @@ hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, const fl
                            int dk, int dv, int N, SeqTable tab, int packed, int signed_gates,
                            int l2norm, int o_bf16, hipStream_t stream);
 
+// fp64 chunkwise backward (both input dtypes).  Runs the records and the
+// forward's serial pass (keeping per-chunk states and U), the reverse pass of
+// the state gradient, then the per-chunk gradients.
+size_t f64_bwd_scratch_bytes(int dk, int dv);
+hipError_t launch_bwd_f64(const void *q, const void *k, const void *v, const float *g,
+                          const float *beta, const float *S0, const float *dO, const float *dS_T,
+                          int H, int dk, int dv, int N, int in_dtype, SeqTable tab,
+                          size_t n_chunks_ub, void *records, size_t rec_bytes, double *S_chunks,
+                          double *U_chunks, double *dU_chunks, double *dSe_chunks,
+                          double *scratch, float *dq, float *dk_out, float *dv_out, float *dg,
+                          float *dbeta, float *dS0, hipStream_t stream);
+
 }  // namespace ckda

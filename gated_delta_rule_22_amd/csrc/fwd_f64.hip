@@ -22,42 +22,18 @@
 //   f64_intra  grid (chunks, heads): G, pi, A and P (element by element, so
 //              every ratio is <= 1 in magnitude and nothing can overflow),
 //              T by forward substitution, then W, Ubar, gamma*Q, K_hat, gamma_n.
+//              T and A / beta stay in the record for the backward pass.
 //   f64_inter  grid (dv blocks x sequences x heads): the serial chunk loop on
-//              an fp64 state slice held in LDS.
+//              an fp64 state slice held in LDS; for the backward pass it can
+//              also keep the state entering each chunk and the chunk's U.
 // This path favours clarity and fp64 accuracy (fp32 inputs carry a 1e-5
 // relative tolerance) over speed; bf16 inputs use the matrix-core path.
-#include "ckda_internal.h"
+#include "f64_common.h"
 
 namespace ckda {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int C = kChunk;
-constexpr int kBV = 32;          // dv columns per f64_inter workgroup
-constexpr double kLog2Floor = -1000.0;
-
-// Record of one (chunk, head): offsets in doubles.
-template <int DK, int DV>
-struct Rec {
-  static constexpr size_t TB = 0;                 // T Diag(beta)      [C][C]
-  static constexpr size_t P = TB + C * C;         // P (lower incl.)   [C][C]
-  static constexpr size_t W = P + C * C;          // W                 [C][DK]
-  static constexpr size_t UB = W + C * DK;        // Ubar              [C][DV]
-  static constexpr size_t QT = UB + C * DV;       // gamma * Q         [C][DK]
-  static constexpr size_t KH = QT + C * DK;       // K * gamma_n/gamma [C][DK]
-  static constexpr size_t GK = KH + C * DK;       // gamma * K         [C][DK]
-  static constexpr size_t GN = GK + C * DK;       // gamma_n           [DK]
-  static constexpr size_t SIZE = GN + DK;
-};
-
-__device__ __forceinline__ int find_seq(const int32_t *chunk_off, int N, int c) {
-  int lo = 0, hi = N;          // chunk_off[lo] <= c < chunk_off[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (chunk_off[mid] <= c) lo = mid; else hi = mid;
-  }
-  return lo;
-}
+using namespace f64;
 
 template <typename TIn, int DK, int DV>
 __global__ __launch_bounds__(kThreads) void f64_intra(
@@ -136,6 +112,7 @@ __global__ __launch_bounds__(kThreads) void f64_intra(
       accP *= s_fq[i];
     }
     s_A[i * (C + 1) + j] = (j < i) ? s_beta[i] * accA : 0.0;
+    rec[R::AH + p] = (j < i) ? accA : 0.0;
     rec[R::P + p] = accP;
   }
 
@@ -169,10 +146,10 @@ __global__ __launch_bounds__(kThreads) void f64_intra(
   }
   __syncthreads();
 
-  // ---- T Diag(beta), W = T Diag(beta) (gamma*K), Ubar = T Diag(beta) V.
+  // ---- T, W = T Diag(beta) (gamma*K), Ubar = T Diag(beta) V.
   for (int p = t; p < C * C; p += kThreads) {
     const int i = p / C, j = p % C;
-    rec[R::TB + p] = s_T[i * (C + 1) + j] * s_beta[j];
+    rec[R::TI + p] = s_T[i * (C + 1) + j];
   }
   for (int p = t; p < C * DK; p += kThreads) {
     const int i = p / DK, c = p % DK;
@@ -192,7 +169,8 @@ __global__ __launch_bounds__(kThreads) void f64_intra(
 template <int DK, int DV>
 __global__ __launch_bounds__(kThreads) void f64_inter(
     const float *__restrict__ S0, int H, int N, SeqTable tab, const double *__restrict__ records,
-    size_t rec_doubles, void *__restrict__ o, float *__restrict__ S_T, int o_bf16) {
+    size_t rec_doubles, void *__restrict__ o, float *__restrict__ S_T, int o_bf16,
+    double *__restrict__ S_chunks, double *__restrict__ U_chunks) {
   using R = Rec<DK, DV>;
   __shared__ double s_S[DK * kBV];
   __shared__ double s_U[C * kBV];
@@ -211,18 +189,23 @@ __global__ __launch_bounds__(kThreads) void f64_inter(
   __syncthreads();
 
   for (int lc = 0; lc < nch; ++lc) {
-    const double *rec = records + ((size_t)(tab.chunk_off[n] + lc) * H + h) * rec_doubles;
+    const size_t ch = (size_t)(tab.chunk_off[n] + lc) * H + h;
+    const double *rec = records + ch * rec_doubles;
     const int nt = min(C, len - lc * C);
+    if (S_chunks)
+      for (int p = t; p < DK * kBV; p += kThreads)
+        S_chunks[ch * DK * DV + (size_t)(p / kBV) * DV + jb * kBV + p % kBV] = s_S[p];
     // U = Ubar - W S
     for (int p = t; p < C * kBV; p += kThreads) {
       const int i = p / kBV, j = p % kBV;
       double acc = rec[R::UB + i * DV + jb * kBV + j];
       for (int c = 0; c < DK; ++c) acc -= rec[R::W + i * DK + c] * s_S[c * kBV + j];
       s_U[p] = acc;
+      if (U_chunks) U_chunks[ch * C * DV + (size_t)i * DV + jb * kBV + j] = acc;
     }
     __syncthreads();
     // O = (gamma Q) S + P U
-    for (int p = t; p < C * kBV; p += kThreads) {
+    for (int p = t; p < C * kBV && o; p += kThreads) {
       const int i = p / kBV, j = p % kBV;
       if (i >= nt) continue;
       double acc = 0.0;
@@ -256,7 +239,7 @@ hipError_t launch_shape(const void *q, const void *k, const void *v, const float
                         const float *beta, const float *S0, int H, int N, SeqTable tab,
                         size_t n_chunks_ub, void *records, size_t rec_bytes, void *o,
                         float *S_T, int signed_gates, int l2norm, int o_bf16,
-                        hipStream_t stream) {
+                        double *S_chunks, double *U_chunks, hipStream_t stream) {
   const size_t rec_doubles = rec_bytes / sizeof(double);
   if (n_chunks_ub > 0) {
     hipLaunchKernelGGL((f64_intra<TIn, DK, DV>), dim3((unsigned)n_chunks_ub, H), dim3(kThreads),
@@ -267,26 +250,27 @@ hipError_t launch_shape(const void *q, const void *k, const void *v, const float
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((f64_inter<DK, DV>), dim3((DV / kBV) * N * H), dim3(kThreads), 0, stream, S0,
-                     H, N, tab, static_cast<const double *>(records), rec_doubles, o, S_T, o_bf16);
+                     H, N, tab, static_cast<const double *>(records), rec_doubles, o, S_T, o_bf16,
+                     S_chunks, U_chunks);
   return hipGetLastError();
 }
 
 }  // namespace
 
 size_t f64_record_bytes(int dk, int dv) {
-  return sizeof(double) * (2 * (size_t)C * C + 4 * (size_t)C * dk + (size_t)C * dv + dk);
+  return sizeof(double) * (3 * (size_t)C * C + 4 * (size_t)C * dk + (size_t)C * dv + dk);
 }
 
-hipError_t launch_fwd_f64(const void *q, const void *k, const void *v, const float *g,
-                          const float *beta, const float *S0, int T_rows, int H, int dk, int dv,
-                          int N, int in_dtype, SeqTable tab, size_t n_chunks_ub, void *records,
-                          size_t rec_bytes, void *o, float *S_T, int signed_gates, int l2norm,
-                          int o_bf16, hipStream_t stream) {
-  (void)T_rows;
+hipError_t launch_f64_pass(const void *q, const void *k, const void *v, const float *g,
+                           const float *beta, const float *S0, int H, int dk, int dv, int N,
+                           int in_dtype, SeqTable tab, size_t n_chunks_ub, void *records,
+                           size_t rec_bytes, void *o, float *S_T, int signed_gates, int l2norm,
+                           int o_bf16, double *S_chunks, double *U_chunks, hipStream_t stream) {
 #define CKDA_F64_CASE(TIN, DK_, DV_)                                                           \
   if (dk == DK_ && dv == DV_)                                                                  \
     return launch_shape<TIN, DK_, DV_>(q, k, v, g, beta, S0, H, N, tab, n_chunks_ub, records, \
-                                       rec_bytes, o, S_T, signed_gates, l2norm, o_bf16, stream);
+                                       rec_bytes, o, S_T, signed_gates, l2norm, o_bf16,       \
+                                       S_chunks, U_chunks, stream);
   if (in_dtype == CKDA_BF16) {
     CKDA_F64_CASE(__hip_bfloat16, 64, 64)
     CKDA_F64_CASE(__hip_bfloat16, 64, 128)
@@ -300,6 +284,17 @@ hipError_t launch_fwd_f64(const void *q, const void *k, const void *v, const flo
   }
 #undef CKDA_F64_CASE
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd_f64(const void *q, const void *k, const void *v, const float *g,
+                          const float *beta, const float *S0, int T_rows, int H, int dk, int dv,
+                          int N, int in_dtype, SeqTable tab, size_t n_chunks_ub, void *records,
+                          size_t rec_bytes, void *o, float *S_T, int signed_gates, int l2norm,
+                          int o_bf16, hipStream_t stream) {
+  (void)T_rows;
+  return launch_f64_pass(q, k, v, g, beta, S0, H, dk, dv, N, in_dtype, tab, n_chunks_ub, records,
+                         rec_bytes, o, S_T, signed_gates, l2norm, o_bf16, nullptr, nullptr,
+                         stream);
 }
 
 }  // namespace ckda

@@ -168,6 +168,53 @@ int ckda_forward_ex(const void *q, const void *k, const void *v, const float *g,
                     void *stream);
 
 /*
+ * Workspace needed by ckda_backward for the same sizes, in bytes (the same for
+ * both input dtypes).  Returns 0 if the sizes are invalid.  It holds fp64
+ * per-chunk intermediates: about 0.85 MB per (64-token chunk, head) at
+ * dk = dv = 128.
+ */
+size_t ckda_backward_workspace_bytes(int B, int T, int H, int dk, int dv, int N,
+                                     int in_dtype);
+
+/*
+ * Backward of ckda_forward: the gradient of
+ *
+ *   L = sum(d_o * o) + sum(dS_T * S_T)
+ *
+ * with respect to every input, for the upstream gradients d_o (of o) and dS_T
+ * (of the final states).  The pages benchmark CKDA's kernels forward plus
+ * backward (CKDA summary, "Main Findings", throughput bullet); the gradient is
+ * that of the recurrence above, taken by reverse mode through the chunkwise
+ * form.  The gate gradient is with respect to the signed alpha itself; gate
+ * signs carry no gradient (alpha enters through log|alpha| and its sign).
+ *
+ *  q .. N, in_dtype    exactly as for ckda_forward (same layouts; the forward
+ *                      is recomputed internally, nothing from it is needed)
+ *  d_o         [B, T, H, dv]  fp32
+ *  dS_T        [N, H, dk, dv] fp32, or NULL for zero
+ *  dq, d_k    [B, T, H, dk]  fp32 outputs (gradients of q and k)
+ *  d_v         [B, T, H, dv]  fp32 output
+ *  dg          [B, T, H, dk]  fp32 output: dL/dalpha
+ *  dbeta       [B, T, H]      fp32 output
+ *  dS0         [N, H, dk, dv] fp32 output, or NULL to skip
+ *  workspace   at least ckda_backward_workspace_bytes(...) bytes of device
+ *              scratch; contents on entry ignored, on return unspecified
+ *
+ * No output may overlap an input, another output or the workspace
+ * (CKDA_ERR_ALIAS).  Numerics: every step runs in fp64 (inputs widen
+ * exactly) and each gradient is rounded once to fp32.  A gate of exactly 0 is
+ * differentiated at |alpha| = 2^-1000, the floor of its log-magnitude, so
+ * its own gradient is not meaningful.  The KDA and L2-normalisation options
+ * of ckda_forward_ex have no backward here.
+ */
+int ckda_backward(const void *q, const void *k, const void *v, const float *g,
+                  const float *beta, const float *S0, const int32_t *cu_seqlens,
+                  int B, int T, int H, int dk, int dv, int N, int in_dtype,
+                  const float *d_o, const float *dS_T, float *dq, float *d_k, float *d_v,
+                  float *dg, float *dbeta, float *dS0, void *workspace,
+                  size_t workspace_bytes, void *stream);
+
+/*
  * One recurrent decode step for N*H independent states, in place.
  *
  *   S <- (I - beta k k^T) Diag(alpha) S + beta k v^T ;  o = S^T q

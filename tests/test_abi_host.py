@@ -100,3 +100,49 @@ def test_forward_ex_rejects_unknown_options(lib):
                                              128, 128, 2, 0, opts, o, None,
                                              ctypes.c_void_p(1 << 20), 1 << 40, None)
     assert q_bad(7) == 4                                        # still checks alignment
+
+
+def _bwd(lib, B=2, T=64, H=2, dk=128, dv=128, N=None, dtype=0, ws=1 << 40, null=(), misalign=(),
+         alias=None, dS0=True):
+    """ckda_backward with distinct, far-apart fake device addresses (never
+    dereferenced: every call below fails validation before any launch)."""
+    N = B if N is None else N
+    names = ["q", "k", "v", "g", "beta", "S0", "do", "dST", "dq", "dk", "dv", "dg", "dbeta",
+             "dS0", "ws"]
+    addr = {n: (i + 1) << 36 for i, n in enumerate(names)}
+    for n in misalign:
+        addr[n] += 8
+    if alias:
+        addr[alias[0]] = addr[alias[1]]
+    P = {n: (None if n in null else ctypes.c_void_p(a)) for n, a in addr.items()}
+    if not dS0:
+        P["dS0"] = None
+    return lib.ckda_backward(P["q"], P["k"], P["v"], P["g"], P["beta"], P["S0"], None, B, T, H,
+                             dk, dv, N, dtype, P["do"], P["dST"], P["dq"], P["dk"], P["dv"],
+                             P["dg"], P["dbeta"], P["dS0"], P["ws"], ws, None)
+
+
+def test_backward_rejects_bad_arguments(lib):
+    assert _bwd(lib, dk=96) == 2                             # shape
+    assert _bwd(lib, N=3) == 2                               # N != B without cu_seqlens
+    assert _bwd(lib, dtype=5) == 3                           # dtype
+    for n in ("q", "do", "dq", "dk", "dv", "dg", "dbeta"):
+        assert _bwd(lib, null=(n,)) == 1, n                  # required pointer missing
+    assert _bwd(lib, misalign=("dg",)) == 4                  # 16-byte alignment
+    assert _bwd(lib, misalign=("dq",)) == 4
+    assert _bwd(lib, alias=("dq", "q")) == 7                 # output over an input
+    assert _bwd(lib, alias=("dS0", "S0")) == 7
+    assert _bwd(lib, alias=("dk", "dq")) == 7                # two outputs overlap
+    assert _bwd(lib, alias=("ws", "do")) == 7                # workspace over an input
+    assert _bwd(lib, ws=16) == 5                             # workspace too small
+    assert _bwd(lib, null=("ws",)) == 5
+
+
+def test_backward_workspace_bytes(lib):
+    f = lib.ckda_backward_workspace_bytes
+    assert f(2, 64, 2, 96, 128, 2, 0) == 0                  # invalid sizes
+    a = f(2, 128, 2, 128, 128, 2, 0)
+    assert a > 0 and a == f(2, 128, 2, 128, 128, 2, 1)      # same for both dtypes
+    assert f(2, 256, 2, 128, 128, 2, 0) > a                  # grows with T
+    # At least the fp64 state kept per (chunk, head): 4 chunks x 2 heads x 2 rows.
+    assert a >= 2 * 2 * 2 * 128 * 128 * 8
