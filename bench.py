@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "CKDA fwd tokens/s (H=16,d=128,bf16) + %MFMA peak; decode steps/s + HBM GB/s"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+F64_PEAK_TFLOPS = 78.6         # MI355X fp64 (vector and matrix)
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix
 
 
@@ -65,6 +66,28 @@ def profiled_traffic(summary, source):
         return None
 
 
+def bwd_algorithmic(w):
+    """Compulsory HBM bytes of one backward (inputs and upstream gradients read
+    once, gradients written once) and its fp64 flop count, both per launch.
+
+    Flops per (64-token chunk, head), dense counts as the kernels execute them
+    (C = 64, d = dk = dv): the chunk records (A and P pair sums, T, W, Ubar)
+    4 C^2 d + C^3 / 3 + 2 C^2 d; the forward's state pass (U and the state
+    update) 4 C d^2; the reverse state pass (dU, dS) 6 C d^2 + C^2 d; the
+    chunk gradients (dX, dP, dA, three C x d x d products, pair sums)
+    3 C^2 d + 6 C d^2 + 4 C^2 d."""
+    th = w.B * w.T * w.H
+    in_sz = 2 if w.dtype == "bf16" else 4
+    per_th = (in_sz * (2 * w.dk + w.dv) + 4 * w.dk + 4 + 4 * w.dv        # q,k,v,alpha,beta,dO
+              + 4 * (3 * w.dk + w.dv) + 4)                               # dq,dk,dalpha,dv,dbeta
+    states = 2 * w.B * w.H * w.dk * w.dv * 4                             # dS_T read, dS0 written
+    C, d = w.chunk, w.dk
+    per_chunk = (4 * C * C * d + C ** 3 // 3 + 2 * C * C * d + 4 * C * d * d
+                 + 6 * C * d * d + C * C * d + 3 * C * C * d + 6 * C * d * d + 4 * C * C * d)
+    chunks = w.B * ((w.T + C - 1) // C) * w.H
+    return th * per_th + states, chunks * per_chunk, per_th
+
+
 def decode_algorithmic(w):
     nh = w.B * w.H
     per_head = 2 * w.dk * w.dv * 4 + 2 * (2 * w.dk + w.dv) + 4 * w.dk + 4 + 4 * w.dv
@@ -83,6 +106,8 @@ def main():
     ap.add_argument("--skip-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--skip-forward", action="store_true")
+    ap.add_argument("--skip-backward", action="store_true")
+    ap.add_argument("--bwd-steps", type=int, default=10)
     ap.add_argument("--skip-others", action="store_true",
                     help="skip timing the fp32 and packed-varlen forward configs")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -167,6 +192,46 @@ def main():
                       "ckda_over_kda_throughput": ms_kda / ms,
                       "gates": "|alpha| of the same workload"}
         del q, k, v, g, ga, beta, o, S_T, ws
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------- backward
+    if not args.skip_backward:
+        print(f"[bench] backward {w.name}: uploading", file=sys.stderr, flush=True)
+        bf = lambda a: torch.from_numpy(a).to(dev).to(torch.bfloat16)
+        f32 = lambda a: torch.from_numpy(a).to(dev)
+        q, k, v, g, beta = bf(x["q"]), bf(x["k"]), bf(x["v"]), f32(x["g"]), f32(x["beta"])
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(0)
+        do = torch.randn((w.B, w.T, w.H, w.dv), generator=gen, device=dev)
+        dST = torch.randn((w.B, w.H, w.dk, w.dv), generator=gen, device=dev)
+        ws = torch.empty(ck.backward_workspace_bytes(w.B, w.T, w.H, w.dk, w.dv, w.B,
+                                                     torch.bfloat16), dtype=torch.uint8,
+                         device=dev)
+        run_b = lambda: ck.backward(q, k, v, g, beta, do, dS_T=dST, workspace=ws)
+        for _ in range(3):
+            run_b()
+        torch.cuda.synchronize()
+        print(f"[bench] backward: timing {args.bwd_steps} steps", file=sys.stderr, flush=True)
+        stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.bwd_steps):
+            run_b()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_b = e0.elapsed_time(e1) / args.bwd_steps
+        bbytes, bflops, bper_th = bwd_algorithmic(w)
+        out["backward"] = {
+            "ms_per_step": ms_b, "tokens_per_s": w.B * w.T / (ms_b * 1e-3),
+            "fwd_plus_bwd_tokens_per_s": (w.B * w.T / ((ms_b + out["ms_per_step"]) * 1e-3)
+                                          if "ms_per_step" in out else None),
+            "steps": args.bwd_steps, "arithmetic": "f64",
+            "f64_tflops": bflops / (ms_b * 1e-3) / 1e12, "f64_peak_tflops": F64_PEAK_TFLOPS,
+            "f64_frac": bflops / (ms_b * 1e-3) / 1e12 / F64_PEAK_TFLOPS,
+            "hbm_gbs_compulsory": bbytes / (ms_b * 1e-3) / 1e9,
+            "flops_per_step": bflops, "compulsory_bytes_per_step": bbytes,
+            "upstream": "do ~ N(0,1), dS_T ~ N(0,1)"}
+        del q, k, v, g, beta, do, dST, ws
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------- decode
