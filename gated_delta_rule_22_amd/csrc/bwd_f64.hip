@@ -33,8 +33,9 @@
 //              pass over chunks for dS, writing dU and dS' of every chunk and
 //              dS0;
 //   f64_bwd_chunk  grid (chunks, heads): everything else, one chunk per
-//              workgroup, with the dense products as LDS-tiled fp64 loops and
-//              the ratio-weighted pair sums channel group by channel group.
+//              workgroup, with the dense products as LDS-staged block products
+//              (f64_common.h) and the ratio-weighted pair sums channel group by
+//              channel group.
 #include "f64_common.h"
 
 namespace ckda {
@@ -44,16 +45,18 @@ using namespace f64;
 
 // --------------------------------------------------------------------------
 // f64_bwd_state: reverse serial pass of dS over the chunks of one
-// (sequence, head, 32-column block).
+// (sequence, head, kBV-column block).
 template <int DK, int DV>
 __global__ __launch_bounds__(kThreads) void f64_bwd_state(
     const float *__restrict__ dO, const float *__restrict__ dS_T, int H, int N, SeqTable tab,
     const double *__restrict__ records, size_t rec_doubles, double *__restrict__ dU_chunks,
     double *__restrict__ dSe_chunks, float *__restrict__ dS0) {
   using R = Rec<DK, DV>;
+  constexpr int NJ = kBV / 16;
   __shared__ double s_dS[DK * kBV];
   __shared__ double s_dO[C * kBV];
   __shared__ double s_dU[C * kBV];
+  __shared__ double s_st[stage_doubles(kBV)];
 
   constexpr int NV = DV / kBV;
   const int jb = blockIdx.x % NV, rh = blockIdx.x / NV, t = threadIdx.x;
@@ -61,6 +64,8 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_state(
   const int len = tab.seq_len[n], start = tab.seq_start[n];
   const int nch = (len + C - 1) / C;
   const size_t sbase = ((size_t)n * H + h) * DK * DV + (size_t)jb * kBV;
+  const int rgp = t >> 4, cl = t & 15;
+  double *sA = s_st, *sB = s_st + kStageA;
 
   for (int p = t; p < DK * kBV; p += kThreads) {
     const int c = p / kBV, j = p % kBV;
@@ -78,24 +83,47 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_state(
     }
     for (int p = t; p < DK * kBV; p += kThreads)
       dSe_chunks[ch * DK * DV + (size_t)(p / kBV) * DV + jb * kBV + p % kBV] = s_dS[p];
-    __syncthreads();
-    // dU = KH dS' + P^T dO   (P is lower triangular: P_mi = 0 for m < i)
-    for (int p = t; p < C * kBV; p += kThreads) {
-      const int i = p / kBV, j = p % kBV;
-      double acc = 0.0;
-      for (int c = 0; c < DK; ++c) acc += rec[R::KH + i * DK + c] * s_dS[c * kBV + j];
-      for (int m = i; m < C; ++m) acc += rec[R::P + m * C + i] * s_dO[m * kBV + j];
-      s_dU[p] = acc;
-      dU_chunks[ch * C * DV + (size_t)i * DV + jb * kBV + j] = acc;
+    // dU = KH dS' + P^T dO, as one product over [dS'; dO]
+    {
+      double acc[4][NJ];
+      gemm64<kBV, DK + C, false, false>(
+          sA, sB,
+          [&](int m, int kk) {
+            return kk < DK ? rec[R::KH + m * DK + kk] : rec[R::P + (kk - DK) * C + m];
+          },
+          [&](int kk, int nn) {
+            return kk < DK ? s_dS[kk * kBV + nn] : s_dO[(kk - DK) * kBV + nn];
+          },
+          acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) {
+          const int i = rgp * 4 + r, j = cl + 16 * jj;
+          s_dU[i * kBV + j] = acc[r][jj];
+          dU_chunks[ch * C * DV + (size_t)i * DV + jb * kBV + j] = acc[r][jj];
+        }
     }
-    __syncthreads();
-    // dS = Diag(gamma_n) dS' + (gamma Q)^T dO - W^T dU   (element-wise in place)
-    for (int p = t; p < DK * kBV; p += kThreads) {
-      const int c = p / kBV, j = p % kBV;
-      double acc = rec[R::GN + c] * s_dS[p];
-      for (int i = 0; i < C; ++i)
-        acc += rec[R::QT + i * DK + c] * s_dO[i * kBV + j] - rec[R::W + i * DK + c] * s_dU[i * kBV + j];
-      s_dS[p] = acc;
+    // dS = Diag(gamma_n) dS' + (gamma Q)^T dO - W^T dU, 64 state rows at a time
+    // (in place: the product reads dO and dU only)
+#pragma unroll
+    for (int half = 0; half < DK / 64; ++half) {
+      double acc[4][NJ];
+      gemm64<kBV, 2 * C, true, false>(
+          sA, sB,
+          [&](int m, int kk) {
+            return kk < C ? rec[R::QT + kk * DK + half * 64 + m]
+                          : -rec[R::W + (kk - C) * DK + half * 64 + m];
+          },
+          [&](int kk, int nn) { return kk < C ? s_dO[kk * kBV + nn] : s_dU[(kk - C) * kBV + nn]; },
+          acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) {
+          const int c = half * 64 + rgp * 4 + r, j = cl + 16 * jj;
+          s_dS[c * kBV + j] = rec[R::GN + c] * s_dS[c * kBV + j] + acc[r][jj];
+        }
     }
   }
   __syncthreads();
@@ -106,72 +134,22 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_state(
     }
 }
 
-// --------------------------------------------------------------------------
-// Out(m, n) = sum_{kk < K} A(m, kk) B(kk, n) for m < 64 and n < NB, in fp64,
-// staged through LDS in K-slices of 16.  Thread t owns rows 4 (t / 16) + r
-// (r < 4) and columns t % 16 + 16 jj (jj < NB / 16); the sums are returned in
-// acc[r][jj].  A_MFAST / B_KFAST choose which index runs fastest across
-// threads while staging, so that transposed sources are read along their
-// contiguous axis.  Every thread of the block must call it.
-constexpr int kKB = 16;
-constexpr int kStageA = 64 * (kKB + 1);
-
-template <int NB, int K, bool A_MFAST, bool B_KFAST, typename FA, typename FB>
-__device__ __forceinline__ void gemm64(double *sA, double *sB, const FA &fa, const FB &fb,
-                                       double (&acc)[4][NB / 16]) {
-  static_assert(K % kKB == 0, "K must be a multiple of 16");
-  constexpr int SA = kKB + 1, SB = NB + 1;
-  const int t = threadIdx.x, rgp = t >> 4, cl = t & 15;
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int jj = 0; jj < NB / 16; ++jj) acc[r][jj] = 0.0;
-  for (int k0 = 0; k0 < K; k0 += kKB) {
-    __syncthreads();
-    for (int p = t; p < 64 * kKB; p += kThreads) {
-      const int m = A_MFAST ? p % 64 : p / kKB, kk = A_MFAST ? p / 64 : p % kKB;
-      sA[m * SA + kk] = fa(m, k0 + kk);
-    }
-    for (int p = t; p < kKB * NB; p += kThreads) {
-      const int kk = B_KFAST ? p % kKB : p / NB, n = B_KFAST ? p / kKB : p % NB;
-      sB[kk * SB + n] = fb(k0 + kk, n);
-    }
-    __syncthreads();
-#pragma unroll 4
-    for (int kk = 0; kk < kKB; ++kk) {
-      double a[4], b[NB / 16];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) a[r] = sA[(rgp * 4 + r) * SA + kk];
-#pragma unroll
-      for (int jj = 0; jj < NB / 16; ++jj) b[jj] = sB[kk * SB + cl + 16 * jj];
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int jj = 0; jj < NB / 16; ++jj) acc[r][jj] = fma(a[r], b[jj], acc[r][jj]);
-    }
-  }
-  __syncthreads();
-}
-
-// Sum over the 16 lanes that share a row group (lanes 16 g .. 16 g + 15).
-__device__ __forceinline__ double sum16(double x) {
-  x += __shfl_xor(x, 1);
-  x += __shfl_xor(x, 2);
-  x += __shfl_xor(x, 4);
-  x += __shfl_xor(x, 8);
-  return x;
-}
-
-// Per-chunk scratch (doubles): dX [C][DV], G [C][DK], sign [C][DK].
+// Per-chunk scratch (doubles): dX [C][DV]; G, sign and the direct parts of
+// dq, dk and dGamma, each [C][DK].
 template <int DK, int DV>
 struct Scr {
   static constexpr size_t DX = 0;
   static constexpr size_t G = DX + C * DV;
   static constexpr size_t SG = G + C * DK;
-  static constexpr size_t SIZE = SG + C * DK;
+  static constexpr size_t AQ = SG + C * DK;
+  static constexpr size_t AK = AQ + C * DK;
+  static constexpr size_t AG = AK + C * DK;
+  static constexpr size_t SIZE = AG + C * DK;
 };
 
 constexpr int kCG = 16;                  // channels per group in the pair sums
+constexpr int kTri = C * (C + 1) / 2;    // packed lower triangle (incl. diagonal)
+__device__ __forceinline__ int tri(int i, int j) { return i * (i + 1) / 2 + j; }   // j <= i
 
 // --------------------------------------------------------------------------
 // f64_bwd_chunk: all per-chunk gradients of one (chunk, head).
@@ -187,16 +165,16 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_chunk(
   using R = Rec<DK, DV>;
   using X = Scr<DK, DV>;
   constexpr int NBM = DV > 64 ? DV : 64;
-  constexpr int kStage = kStageA + kKB * (NBM + 1);
-  constexpr int kGroup = 4 * C * kCG;
-  __shared__ double s_P[C * (C + 1)];     // dP (lower incl.)
-  __shared__ double s_DA[C * (C + 1)];    // beta_i dA_ij (strictly lower)
-  __shared__ double s_u[kStage > kGroup ? kStage : kGroup];  // GEMM staging | group operands
-  __shared__ double s_aq[C * kCG], s_ak[C * kCG], s_ag[C * kCG];
+  constexpr int kStage = stage_doubles(NBM);
+  constexpr int kGroup = 8 * C * kCG > C * DK / 2 ? 8 * C * kCG : C * DK / 2;
+  __shared__ double s_P[kTri];            // dP (lower incl.), packed
+  __shared__ double s_DA[kTri];           // beta_i dA_ij (strictly lower; diagonal 0), packed
+  __shared__ double s_u[kStage > kGroup ? kStage : kGroup];  // staging | group operands
+  __shared__ double s_ag[C * kCG];
   __shared__ double s_beta[C], s_db[C];
   __shared__ double s_R[DK];
   __shared__ int s_fb[DK];
-  __shared__ double s_red[4 * kCG], s_red2[16 * kCG], s_dGn[kCG];
+  __shared__ double s_red[4 * DK], s_red2[2 * DK], s_dGn[DK];
 
   const int cflat = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
   if (cflat >= tab.chunk_off[N]) return;
@@ -215,16 +193,23 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_chunk(
   double *sA = s_u, *sB = s_u + kStageA;
 
   auto row = [&](int i) { return (size_t)(t0 + i) * H + h; };   // token-head row
-  auto dO_at = [&](int m, int c) {
-    return m < nt ? (double)dO[row(m) * DV + c] : 0.0;
+  auto dO_at = [&](int m, int c) { return m < nt ? (double)dO[row(m) * DV + c] : 0.0; };
+  auto gam_at = [&](int m, int c) {
+    return scr[X::SG + m * DK + c] * exp2(scr[X::G + m * DK + c]);
   };
 
-  // ---- phase 0: in-chunk gate log-magnitudes and signs, per channel.
+  // ---- phase 0: in-chunk gate log-magnitudes and signs, per channel (the
+  // gates are first staged in LDS with coalesced loads).
+  float *s_g = reinterpret_cast<float *>(s_u);
+  for (int p = t; p < C * DK; p += kThreads)
+    s_g[p] = p / DK < nt ? g[row(p / DK) * DK + p % DK] : 1.f;
+  __syncthreads();
   if (t < DK) {
     double G = 0.0, gmax = 0.0, gmin = 0.0;
     bool par = false;
+#pragma unroll 8
     for (int i = 0; i < C; ++i) {
-      const float a = i < nt ? g[row(i) * DK + t] : 1.f;
+      const float a = s_g[i * DK + t];
       G += fmax(log2(fabs((double)a)), kLog2Floor);
       par ^= (a < 0.f);
       gmax = fmax(gmax, G);
@@ -242,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_chunk(
     s_beta[t] = t < nt ? (double)beta[row(t)] : 0.0;
     s_db[t] = 0.0;
   }
-  __threadfence();
+  __threadfence_block();   // scratch is read back by this workgroup only
   __syncthreads();
 
   // ---- phase 1: dX = T^T dU; dV = Diag(beta) dX; dbeta += dX_i . V_i
@@ -268,7 +253,7 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_chunk(
       if (cl == 0) s_db[m] += part;
     }
   }
-  __threadfence();
+  __threadfence_block();   // scratch is read back by this workgroup only
   __syncthreads();
 
   // ---- phase 2: dP = tril(dO U^T) and beta_i dA_ij, dA = -strict_tril(dX U^T)
@@ -281,7 +266,7 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_chunk(
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int m = rgp * 4 + r, j = cl + 16 * jj;
-        s_P[m * (C + 1) + j] = j <= m ? acc[r][jj] : 0.0;
+        if (j <= m) s_P[tri(m, j)] = acc[r][jj];
       }
     gemm64<64, DV, false, true>(
         sA, sB, [&](int m, int kk) { return scr[X::DX + m * DV + kk]; },
@@ -294,125 +279,196 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_chunk(
       for (int jj = 0; jj < 4; ++jj) {
         const int j = cl + 16 * jj;
         const double dA = j < m ? -acc[r][jj] : 0.0;
-        s_DA[m * (C + 1) + j] = s_beta[m] * dA;
+        if (j <= m) s_DA[tri(m, j)] = s_beta[m] * dA;
         part += rec[R::AH + m * C + j] * dA;
       }
       part = sum16(part);
       if (cl == 0) s_db[m] += part;
     }
   }
-  __syncthreads();
 
-  // ---- phase 3: per group of 16 channels
-  for (int c0 = 0; c0 < DK; c0 += kCG) {
-    const int c = c0 + cl;                   // this thread's channel in the GEMMs
-    double acc[4][1];
-    // dQT = dO S^T: dq += gamma dQT; dGamma += q gamma dQT
-    gemm64<kCG, DV, false, true>(
-        sA, sB, dO_at, [&](int kk, int nn) { return Sc[(c0 + nn) * DV + kk]; }, acc);
+  // ---- phase 3: the direct parts, 64 channels at a time, kept in registers
+  // over the three products and stored once.
+#pragma unroll 1
+  for (int hf = 0; hf < DK / 64; ++hf) {
+    const int cb = hf * 64;
+    double aq[4][4], ak[4][4], ag[4][4], gam[4][4], acc[4][4];
+    // dQT = dO S^T: dq = gamma dQT; dGamma = q gamma dQT
+    gemm64<64, DV, false, true>(
+        sA, sB, dO_at, [&](int kk, int nn) { return Sc[(cb + nn) * DV + kk]; }, acc);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = rgp * 4 + r;
-      const double gam = scr[X::SG + m * DK + c] * exp2(scr[X::G + m * DK + c]);
-      s_aq[m * kCG + cl] = gam * acc[r][0];
-      s_ag[m * kCG + cl] = rec[R::QT + m * DK + c] * acc[r][0];
-    }
-    // M5 = dX S^T; d(gamma K) = -Diag(beta) M5
-    gemm64<kCG, DV, false, true>(
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int m = rgp * 4 + r, c = cb + cl + 16 * jj;
+        gam[r][jj] = gam_at(m, c);
+        aq[r][jj] = gam[r][jj] * acc[r][jj];
+        ag[r][jj] = rec[R::QT + m * DK + c] * acc[r][jj];
+      }
+    // M5 = dX S^T: d(gamma K) = -Diag(beta) M5
+    gemm64<64, DV, false, true>(
         sA, sB, [&](int m, int kk) { return scr[X::DX + m * DV + kk]; },
-        [&](int kk, int nn) { return Sc[(c0 + nn) * DV + kk]; }, acc);
+        [&](int kk, int nn) { return Sc[(cb + nn) * DV + kk]; }, acc);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = rgp * 4 + r;
-      const double gam = scr[X::SG + m * DK + c] * exp2(scr[X::G + m * DK + c]);
-      const double gk = rec[R::GK + m * DK + c];
-      s_ak[m * kCG + cl] = -s_beta[m] * gam * acc[r][0];
-      s_ag[m * kCG + cl] -= s_beta[m] * gk * acc[r][0];
-      const double part = sum16(-gk * acc[r][0]);
+      double part = 0.0;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int c = cb + cl + 16 * jj;
+        const double gk = rec[R::GK + m * DK + c];
+        ak[r][jj] = -s_beta[m] * gam[r][jj] * acc[r][jj];
+        ag[r][jj] -= s_beta[m] * gk * acc[r][jj];
+        part -= gk * acc[r][jj];
+      }
+      part = sum16(part);
       if (cl == 0) s_db[m] += part;
     }
     // dKH = U dS'^T: dk += (gamma_n / gamma) dKH; dGamma_i -= k (gamma_n/gamma) dKH,
     // and the same amount, summed over i, goes to dGamma_n.
-    gemm64<kCG, DV, false, true>(
+    gemm64<64, DV, false, true>(
         sA, sB, [&](int m, int kk) { return Uc[m * DV + kk]; },
-        [&](int kk, int nn) { return dSe[(c0 + nn) * DV + kk]; }, acc);
-    {
+        [&](int kk, int nn) { return dSe[(cb + nn) * DV + kk]; }, acc);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int c = cb + cl + 16 * jj;
       const double Gn = scr[X::G + (C - 1) * DK + c], sn = scr[X::SG + (C - 1) * DK + c];
       double col = 0.0;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = rgp * 4 + r;
         const double khr = scr[X::SG + m * DK + c] * sn * exp2(Gn - scr[X::G + m * DK + c]);
-        const double term = rec[R::KH + m * DK + c] * acc[r][0];
-        s_ak[m * kCG + cl] += khr * acc[r][0];
-        s_ag[m * kCG + cl] -= term;
+        const double term = rec[R::KH + m * DK + c] * acc[r][jj];
+        ak[r][jj] += khr * acc[r][jj];
+        ag[r][jj] -= term;
         col += term;
       }
       col += __shfl_xor(col, 16);
       col += __shfl_xor(col, 32);
-      if ((t & 63) < 16) s_red[wave * kCG + cl] = col;
+      if ((t & 63) < 16) s_red[wave * DK + c] = col;
     }
-    // gamma_n sum_j dS'[c][j] S[c][j] for the group's channels
-    {
-      double part = 0.0;
-      for (int j = rgp; j < DV; j += 16) part += dSe[c * DV + j] * Sc[c * DV + j];
-      s_red2[rgp * kCG + cl] = part;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int m = rgp * 4 + r, c = cb + cl + 16 * jj;
+        scr[X::AQ + m * DK + c] = aq[r][jj];
+        scr[X::AK + m * DK + c] = ak[r][jj];
+        scr[X::AG + m * DK + c] = ag[r][jj];
+      }
+  }
+  // gamma_n sum_j dS'[c][j] S[c][j]: two threads per channel
+  for (int p = t; p < 2 * DK; p += kThreads) {
+    const int c = p % DK, half = p / DK;
+    double part = 0.0;
+#pragma unroll 16
+    for (int j = half * (DV / 2); j < (half + 1) * (DV / 2); ++j)
+      part += dSe[c * DV + j] * Sc[c * DV + j];
+    s_red2[half * DK + c] = part;
+  }
+  __threadfence_block();   // scratch is read back by this workgroup only
+  __syncthreads();
+  for (int c = t; c < DK; c += kThreads)
+    s_dGn[c] = s_red[c] + s_red[DK + c] + s_red[2 * DK + c] + s_red[3 * DK + c] +
+               rec[R::GN + c] * (s_red2[c] + s_red2[DK + c]);
+
+  // ---- phase 4: pair sums per group of kCG channels, then the gate gradients
+  const int gcl = t % kCG, grw = t / kCG;          // channel in the group, row slot
+  constexpr int kRowSlots = kThreads / kCG;
+  for (int c0 = 0; c0 < DK; c0 += kCG) {
+    const int c = c0 + gcl;
+    double *e = s_u, *f = s_u + C * kCG, *kk_ = s_u + 2 * C * kCG, *qq = s_u + 3 * C * kCG;
+    double *ra = s_u + 4 * C * kCG;       // 1 / alpha (floored magnitude)
+    double *saq = s_u + 5 * C * kCG, *sak = s_u + 6 * C * kCG, *sag = s_u + 7 * C * kCG;
+    __syncthreads();
+#pragma unroll
+    for (int p = t; p < C * kCG; p += kThreads) {
+      const int i = p / kCG, cc = c0 + p % kCG;
+      const double G = scr[X::G + i * DK + cc], sg = scr[X::SG + i * DK + cc];
+      {
+        const double floor_mag = exp2(kLog2Floor);
+        const double a = i < nt ? (double)g[row(i) * DK + cc] : 1.0;
+        ra[p] = 1.0 / (fabs(a) < floor_mag ? (a < 0.0 ? -floor_mag : floor_mag) : a);
+      }
+      if (s_fb[cc]) {
+        e[p] = G;
+        f[p] = sg;
+      } else {
+        e[p] = sg * exp2(G - s_R[cc]);
+        f[p] = sg * exp2(s_R[cc] - G);
+      }
+      kk_[p] = i < nt ? (double)to_f32(k[row(i) * DK + cc]) : 0.0;
+      qq[p] = i < nt ? (double)to_f32(q[row(i) * DK + cc]) : 0.0;
+      saq[p] = scr[X::AQ + i * DK + cc];
+      sak[p] = scr[X::AK + i * DK + cc];
+      sag[p] = scr[X::AG + i * DK + cc];
     }
     __syncthreads();
-    // stage the group's ratio factors and keys/queries; finish dGamma_n
     {
-      double *e = s_u, *f = s_u + C * kCG, *kk_ = s_u + 2 * C * kCG, *qq = s_u + 3 * C * kCG;
-      for (int p = t; p < C * kCG; p += kThreads) {
-        const int i = p / kCG, cc = c0 + p % kCG;
-        const double G = scr[X::G + i * DK + cc], sg = scr[X::SG + i * DK + cc];
-        if (s_fb[cc]) {
-          e[p] = G;
-          f[p] = sg;
-        } else {
-          e[p] = sg * exp2(G - s_R[cc]);
-          f[p] = sg * exp2(s_R[cc] - G);
-        }
-        kk_[p] = i < nt ? (double)to_f32(k[row(i) * DK + cc]) : 0.0;
-        qq[p] = i < nt ? (double)to_f32(q[row(i) * DK + cc]) : 0.0;
-      }
-      if (t < kCG) {
-        double s = 0.0, col = 0.0;
-        for (int w = 0; w < 4; ++w) col += s_red[w * kCG + t];
-        for (int sgm = 0; sgm < 16; ++sgm) s += s_red2[sgm * kCG + t];
-        s_dGn[t] = col + rec[R::GN + c0 + t] * s;
-      }
-    }
-    __syncthreads();
-    // pair sums; thread (channel cl, rows i = rgp + 16 u)
-    {
-      const double *e = s_u, *f = s_u + C * kCG, *kk_ = s_u + 2 * C * kCG, *qq = s_u + 3 * C * kCG;
       const bool fb = s_fb[c];
 #pragma unroll 1
-      for (int u = 0; u < C / 16; ++u) {
-        const int i = rgp + 16 * u;
+      for (int u = 0; u < C / kRowSlots; ++u) {
+        const int i = grw + kRowSlots * u;
         double R1 = 0.0, R2 = 0.0, C1 = 0.0, C2 = 0.0;
-        const double ei = e[i * kCG + cl], fi = f[i * kCG + cl];
-        // row i: sum over j <= i of dP_ij k_j r_ij and (beta dA)_ij k_j r_ij
-        for (int j = 0; j <= i; ++j) {
-          const double r = fb ? fi * f[j * kCG + cl] * exp2(ei - e[j * kCG + cl])
-                              : ei * f[j * kCG + cl];
-          const double kr = kk_[j * kCG + cl] * r;
-          R1 = fma(s_P[i * (C + 1) + j], kr, R1);
-          R2 = fma(s_DA[i * (C + 1) + j], kr, R2);
+        const double ei = e[i * kCG + gcl], fi = f[i * kCG + gcl];
+        const double *Pi = s_P + tri(i, 0), *DAi = s_DA + tri(i, 0);
+        // row i: sum over j <= i of dP_ij k_j r_ij and (beta dA)_ij k_j r_ij;
+        // column i: sum over m >= i of (beta dA)_mi k_m r_mi and dP_mi q_m r_mi.
+        if (!fb) {
+          // four independent partial sums per quantity keep the FMA chains short
+          double r1[4] = {0.0, 0.0, 0.0, 0.0}, r2[4] = {0.0, 0.0, 0.0, 0.0};
+          int j = 0;
+          for (; j + 3 <= i; j += 4) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              const double kr = kk_[(j + w) * kCG + gcl] * (ei * f[(j + w) * kCG + gcl]);
+              r1[w] = fma(Pi[j + w], kr, r1[w]);
+              r2[w] = fma(DAi[j + w], kr, r2[w]);
+            }
+          }
+          for (; j <= i; ++j) {
+            const double kr = kk_[j * kCG + gcl] * (ei * f[j * kCG + gcl]);
+            r1[0] = fma(Pi[j], kr, r1[0]);
+            r2[0] = fma(DAi[j], kr, r2[0]);
+          }
+          R1 = (r1[0] + r1[1]) + (r1[2] + r1[3]);
+          R2 = (r2[0] + r2[1]) + (r2[2] + r2[3]);
+          double c1[4] = {0.0, 0.0, 0.0, 0.0}, c2[4] = {0.0, 0.0, 0.0, 0.0};
+          int m = i;
+          for (; m + 3 < C; m += 4) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              const double r = e[(m + w) * kCG + gcl] * fi;
+              c1[w] = fma(s_DA[tri(m + w, i)], kk_[(m + w) * kCG + gcl] * r, c1[w]);
+              c2[w] = fma(s_P[tri(m + w, i)], qq[(m + w) * kCG + gcl] * r, c2[w]);
+            }
+          }
+          for (; m < C; ++m) {
+            const double r = e[m * kCG + gcl] * fi;
+            c1[0] = fma(s_DA[tri(m, i)], kk_[m * kCG + gcl] * r, c1[0]);
+            c2[0] = fma(s_P[tri(m, i)], qq[m * kCG + gcl] * r, c2[0]);
+          }
+          C1 = (c1[0] + c1[1]) + (c1[2] + c1[3]);
+          C2 = (c2[0] + c2[1]) + (c2[2] + c2[3]);
+        } else {                          // e holds G and f the sign
+          for (int j = 0; j <= i; ++j) {
+            const double r = fi * f[j * kCG + gcl] * exp2(ei - e[j * kCG + gcl]);
+            const double kr = kk_[j * kCG + gcl] * r;
+            R1 = fma(Pi[j], kr, R1);
+            R2 = fma(DAi[j], kr, R2);
+          }
+          for (int m = i; m < C; ++m) {
+            const double r = f[m * kCG + gcl] * fi * exp2(e[m * kCG + gcl] - ei);
+            C1 = fma(s_DA[tri(m, i)], kk_[m * kCG + gcl] * r, C1);
+            C2 = fma(s_P[tri(m, i)], qq[m * kCG + gcl] * r, C2);
+          }
         }
-        // column i: sum over m >= i of (beta dA)_mi k_m r_mi and dP_mi q_m r_mi
-        for (int m = i; m < C; ++m) {
-          const double r = fb ? f[m * kCG + cl] * fi * exp2(e[m * kCG + cl] - ei)
-                              : e[m * kCG + cl] * fi;
-          C1 = fma(s_DA[m * (C + 1) + i], kk_[m * kCG + cl] * r, C1);
-          C2 = fma(s_P[m * (C + 1) + i], qq[m * kCG + cl] * r, C2);
-        }
-        const double ki = kk_[i * kCG + cl], qi = qq[i * kCG + cl];
-        const double gq = s_aq[i * kCG + cl] + R1;
-        const double gk = s_ak[i * kCG + cl] + R2 + C1 + C2;
-        double gG = s_ag[i * kCG + cl] + qi * R1 + ki * (R2 - C1 - C2);
-        if (i == C - 1) gG += s_dGn[cl];
-        s_ag[i * kCG + cl] = gG;
+        const double ki = kk_[i * kCG + gcl], qi = qq[i * kCG + gcl];
+        const double gq = saq[i * kCG + gcl] + R1;
+        const double gk = sak[i * kCG + gcl] + R2 + C1 + C2;
+        double gG = sag[i * kCG + gcl] + qi * R1 + ki * (R2 - C1 - C2);
+        if (i == C - 1) gG += s_dGn[c];
+        s_ag[i * kCG + gcl] = gG;
         if (i < nt) {
           dq[row(i) * DK + c] = (float)gq;
           dk[row(i) * DK + c] = (float)gk;
@@ -424,18 +480,14 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_chunk(
     if (t < kCG) {
       const int cc = c0 + t;
       double acc2 = 0.0;
+#pragma unroll 8
       for (int i = C - 1; i >= 0; --i) {
         acc2 += s_ag[i * kCG + t];
-        if (i < nt) {
-          const double a = (double)g[row(i) * DK + cc];
-          const double floor_mag = exp2(kLog2Floor);
-          const double ae = fabs(a) < floor_mag ? (a < 0.0 ? -floor_mag : floor_mag) : a;
-          dg[row(i) * DK + cc] = (float)(acc2 / ae);
-        }
+        if (i < nt) dg[row(i) * DK + cc] = (float)(acc2 * ra[i * kCG + t]);
       }
     }
-    __syncthreads();
   }
+  __syncthreads();
   if (t < nt) dbeta[row(t)] = (float)s_db[t];
 }
 
@@ -462,7 +514,7 @@ hipError_t launch_bwd_shape(const void *q, const void *k, const void *v, const f
 }  // namespace
 
 size_t f64_bwd_scratch_bytes(int dk, int dv) {
-  return sizeof(double) * ((size_t)C * dv + 2 * (size_t)C * dk);
+  return sizeof(double) * ((size_t)C * dv + 5 * (size_t)C * dk);
 }
 
 hipError_t launch_bwd_f64(const void *q, const void *k, const void *v, const float *g,

@@ -19,13 +19,16 @@
 //
 // Two kernels, with the S-independent work stored per (chunk, head) in the
 // workspace:
-//   f64_intra  grid (chunks, heads): G, pi, A and P (element by element, so
-//              every ratio is <= 1 in magnitude and nothing can overflow),
+//   f64_intra  grid (chunks, heads): G, pi, then A and P as sums over the
+//              channels of per-pair ratio products (each ratio is one product
+//              of two factors taken about the channel's midpoint, or exp2 of
+//              the difference where the channel spans too many binary orders),
 //              T by forward substitution, then W, Ubar, gamma*Q, K_hat, gamma_n.
 //              T and A / beta stay in the record for the backward pass.
 //   f64_inter  grid (dv blocks x sequences x heads): the serial chunk loop on
-//              an fp64 state slice held in LDS; for the backward pass it can
-//              also keep the state entering each chunk and the chunk's U.
+//              an fp64 state slice held in LDS, each product an LDS-staged
+//              block product; for the backward pass it can also keep the
+//              state entering each chunk and the chunk's U.
 // This path favours clarity and fp64 accuracy (fp32 inputs carry a 1e-5
 // relative tolerance) over speed; bf16 inputs use the matrix-core path.
 #include "f64_common.h"
@@ -35,18 +38,24 @@ namespace {
 
 using namespace f64;
 
+constexpr int kCG = 16;              // channels per group in the pair sums
+
 template <typename TIn, int DK, int DV>
 __global__ __launch_bounds__(kThreads) void f64_intra(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, int H, int N, SeqTable tab,
     double *__restrict__ records, size_t rec_doubles, int signed_gates, int l2norm) {
   using R = Rec<DK, DV>;
-  __shared__ double s_G[C * DK];        // log2-magnitude cumsum; later reused for T
-  __shared__ float s_k[C * DK];
+  constexpr int NBM = DK > DV ? DK : DV;
+  constexpr int kG = 4 * C * kCG > C * DK / 2 ? 4 * C * kCG : C * DK / 2;
+  constexpr int kU = stage_doubles(NBM) > kG ? stage_doubles(NBM) : kG;
+  __shared__ double s_G[C * DK > C * (C + 1) ? C * DK : C * (C + 1)];  // G, later T
   __shared__ uint8_t s_par[C * DK];
   __shared__ double s_A[C * (C + 1)];
-  __shared__ double s_beta[C];
-  __shared__ double s_fq[C];            // query normalisation factor per token (1 if off)
+  __shared__ double s_u[kU];            // group operands | product staging
+  __shared__ double s_beta[C], s_fk[C], s_fq[C];
+  __shared__ double s_R[DK];
+  __shared__ int s_fb[DK];
 
   const int cflat = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
   if (cflat >= tab.chunk_off[N]) return;
@@ -58,79 +67,146 @@ __global__ __launch_bounds__(kThreads) void f64_intra(
 
   auto row = [&](int i) { return (size_t)(t0 + i) * H + h; };   // token-head row
 
-  // ---- gates: inclusive cumsum of log2|alpha| and parity of negatives.
+  // ---- gates: inclusive cumsum of log2|alpha| and parity of negatives (the
+  // gates are first staged in LDS with coalesced loads).
+  float *s_g = reinterpret_cast<float *>(s_u);
+  for (int p = t; p < C * DK; p += kThreads)
+    s_g[p] = p / DK < nt ? g[row(p / DK) * DK + p % DK] : 1.f;
+  __syncthreads();
   if (t < DK) {
-    double G = 0.0;
+    double G = 0.0, gmax = 0.0, gmin = 0.0;
     uint8_t par = 0;
+#pragma unroll 8
     for (int i = 0; i < C; ++i) {
-      float a = 1.f, kk = 0.f;
-      if (i < nt) {
-        a = g[row(i) * DK + t];
-        kk = to_f32(k[row(i) * DK + t]);
-      }
+      const float a = s_g[i * DK + t];
       G += fmax(log2(fabs((double)a)), kLog2Floor);
       par ^= (uint8_t)(signed_gates && a < 0.f);   // KDA mode: signs ignored
+      gmax = fmax(gmax, G);
+      gmin = fmin(gmin, G);
       s_G[i * DK + t] = G;
       s_par[i * DK + t] = par;
-      s_k[i * DK + t] = kk;
     }
+    // Pair ratios are formed as e_i f_j with e = 2^(G - Rm), f = 2^(Rm - G)
+    // about the midpoint Rm of the channel's range; past +-1000 binary orders
+    // that product could leave fp64's range and the channel takes exp2 per pair.
+    s_R[t] = 0.5 * (gmax + gmin);
+    s_fb[t] = (gmax - gmin) > 2000.0;
   }
-  if (t < C) s_beta[t] = t < nt ? (double)beta[row(t)] : 0.0;
-  __syncthreads();
   // ---- optional L2 normalisation of q and k per token: (sum x^2 + 1e-6)^(-1/2)
   if (t < C) {
     double fk = 1.0, fq = 1.0;
     if (l2norm && t < nt) {
       double sk = 1e-6, sq = 1e-6;
       for (int c = 0; c < DK; ++c) {
-        const double kk = s_k[t * DK + c], qq = to_f32(q[row(t) * DK + c]);
+        const double kk = to_f32(k[row(t) * DK + c]), qq = to_f32(q[row(t) * DK + c]);
         sk += kk * kk;
         sq += qq * qq;
       }
       fk = 1.0 / sqrt(sk);
       fq = 1.0 / sqrt(sq);
     }
+    s_fk[t] = fk;
     s_fq[t] = fq;
-    if (l2norm)
-      for (int c = 0; c < DK; ++c) s_k[t * DK + c] = (float)(s_k[t * DK + c] * fk);
+    s_beta[t] = t < nt ? (double)beta[row(t)] : 0.0;
   }
   __syncthreads();
 
-  // ---- A (strictly lower) and P (lower incl. diagonal), element by element.
-  for (int p = t; p < C * C; p += kThreads) {
-    const int i = p / C, j = p % C;
-    double accA = 0.0, accP = 0.0;
-    if (j <= i && i < nt) {
-      const TIn *qi = q + row(i) * DK;
-      for (int c = 0; c < DK; ++c) {
-        const double r = ((s_par[i * DK + c] ^ s_par[j * DK + c]) ? -1.0 : 1.0) *
-                         exp2(s_G[i * DK + c] - s_G[j * DK + c]);
-        const double rk = r * (double)s_k[j * DK + c];
-        accA += (double)s_k[i * DK + c] * rk;
-        accP += (double)to_f32(qi[c]) * rk;
+  // ---- A (strictly lower) and P (lower incl. diagonal), channel group by
+  // channel group.  Thread t owns pairs (i, j) = (t/16 + 16 ii, t%16 + 16 jj).
+  {
+    const int bi = t >> 4, bj = t & 15;
+    double accA[4][4], accP[4][4];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) accA[ii][jj] = accP[ii][jj] = 0.0;
+    double *e = s_u, *f = s_u + C * kCG, *kg = s_u + 2 * C * kCG, *qg = s_u + 3 * C * kCG;
+    for (int c0 = 0; c0 < DK; c0 += kCG) {
+      __syncthreads();
+      // group operands, channel-major: x[cl * C + i]
+#pragma unroll
+      for (int p = t; p < C * kCG; p += kThreads) {
+        const int i = p / kCG, cl = p % kCG, c = c0 + cl;
+        const double G = s_G[i * DK + c], sg = s_par[i * DK + c] ? -1.0 : 1.0;
+        if (s_fb[c]) {
+          e[cl * C + i] = G;
+          f[cl * C + i] = sg;
+        } else {
+          e[cl * C + i] = sg * exp2(G - s_R[c]);
+          f[cl * C + i] = sg * exp2(s_R[c] - G);
+        }
+        kg[cl * C + i] = i < nt ? (double)to_f32(k[row(i) * DK + c]) * s_fk[i] : 0.0;
+        qg[cl * C + i] = i < nt ? (double)to_f32(q[row(i) * DK + c]) * s_fq[i] : 0.0;
       }
-      accP *= s_fq[i];
+      __syncthreads();
+      for (int cl = 0; cl < kCG; ++cl) {
+        const double *ec = e + cl * C, *fc = f + cl * C, *kc = kg + cl * C, *qc = qg + cl * C;
+        double ei[4], ki[4], qi[4], fj[4], kj[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          ei[u] = ec[bi + 16 * u];
+          ki[u] = kc[bi + 16 * u];
+          qi[u] = qc[bi + 16 * u];
+          fj[u] = fc[bj + 16 * u];
+          kj[u] = kc[bj + 16 * u];
+        }
+        if (!s_fb[c0 + cl]) {        // uniform across the block
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              const double kr = ei[ii] * fj[jj] * kj[jj];
+              accA[ii][jj] = fma(ki[ii], kr, accA[ii][jj]);
+              accP[ii][jj] = fma(qi[ii], kr, accP[ii][jj]);
+            }
+        } else {                     // e holds G and f the sign
+          double ej[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) ej[u] = ec[bj + 16 * u];
+          double fi[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) fi[u] = fc[bi + 16 * u];
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              const int i = bi + 16 * ii, j = bj + 16 * jj;
+              const double r = j <= i ? fi[ii] * fj[jj] * exp2(ei[ii] - ej[jj]) : 0.0;
+              const double kr = r * kj[jj];
+              accA[ii][jj] = fma(ki[ii], kr, accA[ii][jj]);
+              accP[ii][jj] = fma(qi[ii], kr, accP[ii][jj]);
+            }
+        }
+      }
     }
-    s_A[i * (C + 1) + j] = (j < i) ? s_beta[i] * accA : 0.0;
-    rec[R::AH + p] = (j < i) ? accA : 0.0;
-    rec[R::P + p] = accP;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int i = bi + 16 * ii, j = bj + 16 * jj;
+        const double a = j < i ? accA[ii][jj] : 0.0;
+        s_A[i * (C + 1) + j] = s_beta[i] * a;
+        rec[R::AH + i * C + j] = a;
+        rec[R::P + i * C + j] = j <= i ? accP[ii][jj] : 0.0;
+      }
   }
 
   // ---- gamma-scaled operands (masked tokens have k = q = 0).
+#pragma unroll 4
   for (int p = t; p < C * DK; p += kThreads) {
     const int i = p / DK, c = p % DK;
     const double Gi = s_G[i * DK + c], Gn = s_G[(C - 1) * DK + c];
     const double si = s_par[i * DK + c] ? -1.0 : 1.0;
     const double sn = (s_par[i * DK + c] ^ s_par[(C - 1) * DK + c]) ? -1.0 : 1.0;
     const double gam = si * exp2(Gi);
-    const double kk = s_k[p];
+    const double kk = i < nt ? (double)to_f32(k[row(i) * DK + c]) * s_fk[i] : 0.0;
     const double qq = i < nt ? (double)to_f32(q[row(i) * DK + c]) * s_fq[i] : 0.0;
     rec[R::QT + p] = qq * gam;
     rec[R::GK + p] = kk * gam;
     rec[R::KH + p] = kk * sn * exp2(Gn - Gi);
     if (i == C - 1) rec[R::GN + c] = gam;
   }
-  __threadfence();
+  __threadfence_block();   // scratch is read back by this workgroup only
   __syncthreads();
 
   // ---- T = (I + A)^-1 by forward substitution; column j per thread.
@@ -147,33 +223,44 @@ __global__ __launch_bounds__(kThreads) void f64_intra(
   __syncthreads();
 
   // ---- T, W = T Diag(beta) (gamma*K), Ubar = T Diag(beta) V.
-  for (int p = t; p < C * C; p += kThreads) {
-    const int i = p / C, j = p % C;
-    rec[R::TI + p] = s_T[i * (C + 1) + j];
+  for (int p = t; p < C * C; p += kThreads) rec[R::TI + p] = s_T[(p / C) * (C + 1) + p % C];
+  double *sA = s_u, *sB = s_u + kStageA;
+  auto tb = [&](int m, int kk) { return s_T[m * (C + 1) + kk] * s_beta[kk]; };
+  {
+    double acc[4][DK / 16];
+    gemm64<DK, C, false, false>(
+        sA, sB, tb, [&](int kk, int nn) { return rec[R::GK + kk * DK + nn]; }, acc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int jj = 0; jj < DK / 16; ++jj)
+        rec[R::W + ((t >> 4) * 4 + r) * DK + (t & 15) + 16 * jj] = acc[r][jj];
   }
-  for (int p = t; p < C * DK; p += kThreads) {
-    const int i = p / DK, c = p % DK;
-    double acc = 0.0;
-    for (int j = 0; j <= i; ++j) acc += s_T[i * (C + 1) + j] * s_beta[j] * rec[R::GK + j * DK + c];
-    rec[R::W + p] = acc;
-  }
-  for (int p = t; p < C * DV; p += kThreads) {
-    const int i = p / DV, c = p % DV;
-    double acc = 0.0;
-    for (int j = 0; j <= i && j < nt; ++j)
-      acc += s_T[i * (C + 1) + j] * s_beta[j] * (double)to_f32(v[row(j) * DV + c]);
-    rec[R::UB + p] = acc;
+  {
+    double acc[4][DV / 16];
+    gemm64<DV, C, false, false>(
+        sA, sB, tb,
+        [&](int kk, int nn) { return kk < nt ? (double)to_f32(v[row(kk) * DV + nn]) : 0.0; },
+        acc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int jj = 0; jj < DV / 16; ++jj)
+        rec[R::UB + ((t >> 4) * 4 + r) * DV + (t & 15) + 16 * jj] = acc[r][jj];
   }
 }
 
+// Serial pass over the chunks of one (sequence, head, kBV-column block).
 template <int DK, int DV>
 __global__ __launch_bounds__(kThreads) void f64_inter(
     const float *__restrict__ S0, int H, int N, SeqTable tab, const double *__restrict__ records,
     size_t rec_doubles, void *__restrict__ o, float *__restrict__ S_T, int o_bf16,
     double *__restrict__ S_chunks, double *__restrict__ U_chunks) {
   using R = Rec<DK, DV>;
+  constexpr int NJ = kBV / 16;
   __shared__ double s_S[DK * kBV];
   __shared__ double s_U[C * kBV];
+  __shared__ double s_st[stage_doubles(kBV)];
 
   constexpr int NV = DV / kBV;
   const int jb = blockIdx.x % NV, rh = blockIdx.x / NV, t = threadIdx.x;
@@ -181,6 +268,8 @@ __global__ __launch_bounds__(kThreads) void f64_inter(
   const int len = tab.seq_len[n], start = tab.seq_start[n];
   const int nch = (len + C - 1) / C;
   const size_t sbase = ((size_t)n * H + h) * DK * DV + (size_t)jb * kBV;
+  const int rgp = t >> 4, cl = t & 15;
+  double *sA = s_st, *sB = s_st + kStageA;
 
   for (int p = t; p < DK * kBV; p += kThreads) {
     const int c = p / kBV, j = p % kBV;
@@ -196,34 +285,61 @@ __global__ __launch_bounds__(kThreads) void f64_inter(
       for (int p = t; p < DK * kBV; p += kThreads)
         S_chunks[ch * DK * DV + (size_t)(p / kBV) * DV + jb * kBV + p % kBV] = s_S[p];
     // U = Ubar - W S
-    for (int p = t; p < C * kBV; p += kThreads) {
-      const int i = p / kBV, j = p % kBV;
-      double acc = rec[R::UB + i * DV + jb * kBV + j];
-      for (int c = 0; c < DK; ++c) acc -= rec[R::W + i * DK + c] * s_S[c * kBV + j];
-      s_U[p] = acc;
-      if (U_chunks) U_chunks[ch * C * DV + (size_t)i * DV + jb * kBV + j] = acc;
+    {
+      double acc[4][NJ];
+      gemm64<kBV, DK, false, false>(
+          sA, sB, [&](int m, int kk) { return rec[R::W + m * DK + kk]; },
+          [&](int kk, int nn) { return s_S[kk * kBV + nn]; }, acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) {
+          const int i = rgp * 4 + r, j = cl + 16 * jj;
+          const double u = rec[R::UB + i * DV + jb * kBV + j] - acc[r][jj];
+          s_U[i * kBV + j] = u;
+          if (U_chunks) U_chunks[ch * C * DV + (size_t)i * DV + jb * kBV + j] = u;
+        }
     }
-    __syncthreads();
-    // O = (gamma Q) S + P U
-    for (int p = t; p < C * kBV && o; p += kThreads) {
-      const int i = p / kBV, j = p % kBV;
-      if (i >= nt) continue;
-      double acc = 0.0;
-      for (int c = 0; c < DK; ++c) acc += rec[R::QT + i * DK + c] * s_S[c * kBV + j];
-      for (int m = 0; m <= i; ++m) acc += rec[R::P + i * C + m] * s_U[m * kBV + j];
-      const size_t oi = ((size_t)(start + lc * C + i) * H + h) * DV + jb * kBV + j;
-      if (o_bf16)
-        static_cast<__hip_bfloat16 *>(o)[oi] = __float2bfloat16((float)acc);
-      else
-        static_cast<float *>(o)[oi] = (float)acc;
+    // O = (gamma Q) S + P U, as one product over [S; U]
+    if (o) {
+      double acc[4][NJ];
+      gemm64<kBV, DK + C, false, false>(
+          sA, sB,
+          [&](int m, int kk) {
+            return kk < DK ? rec[R::QT + m * DK + kk] : rec[R::P + m * C + kk - DK];
+          },
+          [&](int kk, int nn) { return kk < DK ? s_S[kk * kBV + nn] : s_U[(kk - DK) * kBV + nn]; },
+          acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) {
+          const int i = rgp * 4 + r, j = cl + 16 * jj;
+          if (i >= nt) continue;
+          const size_t oi = ((size_t)(start + lc * C + i) * H + h) * DV + jb * kBV + j;
+          if (o_bf16)
+            static_cast<__hip_bfloat16 *>(o)[oi] = __float2bfloat16((float)acc[r][jj]);
+          else
+            static_cast<float *>(o)[oi] = (float)acc[r][jj];
+        }
+    } else {
+      __syncthreads();       // s_U complete before the state update reads it
     }
-    __syncthreads();
-    // S' = Diag(gamma_n) S + K_hat^T U
-    for (int p = t; p < DK * kBV; p += kThreads) {
-      const int c = p / kBV, j = p % kBV;
-      double acc = rec[R::GN + c] * s_S[p];
-      for (int m = 0; m < nt; ++m) acc += rec[R::KH + m * DK + c] * s_U[m * kBV + j];
-      s_S[p] = acc;
+    // S' = Diag(gamma_n) S + K_hat^T U, 64 state rows at a time (in place: each
+    // thread rewrites only its own elements, and the product reads U only)
+#pragma unroll
+    for (int half = 0; half < DK / 64; ++half) {
+      double acc[4][NJ];
+      gemm64<kBV, C, true, false>(
+          sA, sB, [&](int m, int kk) { return rec[R::KH + kk * DK + half * 64 + m]; },
+          [&](int kk, int nn) { return s_U[kk * kBV + nn]; }, acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) {
+          const int c = half * 64 + rgp * 4 + r, j = cl + 16 * jj;
+          s_S[c * kBV + j] = rec[R::GN + c] * s_S[c * kBV + j] + acc[r][jj];
+        }
     }
     __syncthreads();
   }
