@@ -220,18 +220,34 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         ms_b = e0.elapsed_time(e1) / args.bwd_steps
+        # KDA mode of the backward on |alpha|: with the KDA forward, the pages'
+        # forward-plus-backward throughput comparison.
+        ga = g.abs()
+        run_bk = lambda: ck.backward(q, k, v, ga, beta, do, dS_T=dST, workspace=ws, kda=True)
+        run_bk()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.bwd_steps):
+            run_bk()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_bk = e0.elapsed_time(e1) / args.bwd_steps
         bbytes, bflops, bper_th = bwd_algorithmic(w)
         out["backward"] = {
             "ms_per_step": ms_b, "tokens_per_s": w.B * w.T / (ms_b * 1e-3),
             "fwd_plus_bwd_tokens_per_s": (w.B * w.T / ((ms_b + out["ms_per_step"]) * 1e-3)
                                           if "ms_per_step" in out else None),
             "steps": args.bwd_steps, "arithmetic": "f64",
+            "kda_ms_per_step": ms_bk,
+            "fwd_bwd_ckda_over_kda_throughput": (
+                (out["kda"]["ms_per_step"] + ms_bk) / (out["ms_per_step"] + ms_b)
+                if "kda" in out else None),
             "f64_tflops": bflops / (ms_b * 1e-3) / 1e12, "f64_peak_tflops": F64_PEAK_TFLOPS,
             "f64_frac": bflops / (ms_b * 1e-3) / 1e12 / F64_PEAK_TFLOPS,
             "hbm_gbs_compulsory": bbytes / (ms_b * 1e-3) / 1e9,
             "flops_per_step": bflops, "compulsory_bytes_per_step": bbytes,
             "upstream": "do ~ N(0,1), dS_T ~ N(0,1)"}
-        del q, k, v, g, beta, do, dST, ws
+        del q, k, v, g, ga, beta, do, dST, ws
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------- decode

@@ -50,6 +50,8 @@ def library() -> ctypes.CDLL:
         lib.ckda_backward_workspace_bytes.restype = sz
         lib.ckda_backward.argtypes = [vp] * 7 + [ci] * 7 + [vp] * 8 + [vp, sz, vp]
         lib.ckda_backward.restype = ci
+        lib.kda_backward.argtypes = [vp] * 7 + [ci] * 7 + [vp] * 8 + [vp, sz, vp]
+        lib.kda_backward.restype = ci
         lib.ckda_decode_step.argtypes = [vp] * 7 + [ci] * 5 + [vp]
         lib.ckda_decode_step.restype = ci
         _lib = lib
@@ -169,10 +171,11 @@ def backward_workspace_bytes(B, T, H, dk, dv, N, dtype) -> int:
 
 
 def backward(q, k, v, g, beta, do, S0=None, dS_T=None, cu_seqlens=None, *, workspace=None,
-             need_dS0=True):
+             need_dS0=True, kda=False):
     """Gradients of ``sum(do * o) + sum(dS_T * S_T)`` for the forward's inputs:
     returns ``(dq, dk, dv, dg, dbeta, dS0)`` as fp32 tensors (``dS0`` is None
-    when ``need_dS0`` is False).  See ``ckda_backward`` in include/ckda.h."""
+    when ``need_dS0`` is False).  See ``ckda_backward`` in include/ckda.h;
+    ``kda=True`` calls ``kda_backward`` (the backward of :func:`kda_forward`)."""
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     code = _dtype_code(q)
@@ -202,11 +205,12 @@ def backward(q, k, v, g, beta, do, S0=None, dS_T=None, cu_seqlens=None, *, works
     ws_bytes = backward_workspace_bytes(B, T, H, dk, dv, N, code)
     if workspace is None or workspace.numel() * workspace.element_size() < ws_bytes:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    st = library().ckda_backward(
+    entry = "kda_backward" if kda else "ckda_backward"
+    st = getattr(library(), entry)(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(cu_seqlens),
         B, T, H, dk, dv, N, code, _ptr(do), _ptr(dS_T), _ptr(dq), _ptr(dk_), _ptr(dv_),
         _ptr(dg), _ptr(db), _ptr(dS0), _ptr(workspace), ws_bytes, _stream(dev))
-    _check(st, "ckda_backward")
+    _check(st, entry)
     return dq, dk_, dv_, dg, db, dS0
 
 

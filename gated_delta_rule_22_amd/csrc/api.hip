@@ -204,12 +204,13 @@ extern "C" size_t ckda_backward_workspace_bytes(int B, int T, int H, int dk, int
   return bwd_layout(B, T, H, dk, dv, N).total;
 }
 
-extern "C" int ckda_backward(const void *q, const void *k, const void *v, const float *g,
-                             const float *beta, const float *S0, const int32_t *cu_seqlens,
-                             int B, int T, int H, int dk, int dv, int N, int in_dtype,
-                             const float *d_o, const float *dS_T, float *dq, float *dk_out,
-                             float *dv_out, float *dg, float *dbeta, float *dS0, void *workspace,
-                             size_t workspace_bytes, void *stream) {
+namespace {
+
+int backward_impl(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                  const float *S0, const int32_t *cu_seqlens, int B, int T, int H, int dk, int dv,
+                  int N, int in_dtype, const float *d_o, const float *dS_T, float *dq,
+                  float *dk_out, float *dv_out, float *dg, float *dbeta, float *dS0,
+                  void *workspace, size_t workspace_bytes, int signed_gates, void *stream) {
   const bool packed = cu_seqlens != nullptr;
   if (int s = forward_shape_status(B, T, H, dk, dv, N, in_dtype, packed)) return s;
   const size_t rows = (size_t)B * T * H;
@@ -251,8 +252,30 @@ extern "C" int ckda_backward(const void *q, const void *k, const void *v, const 
       w + L.records, L.rec_bytes, reinterpret_cast<double *>(w + L.S),
       reinterpret_cast<double *>(w + L.U), reinterpret_cast<double *>(w + L.dU),
       reinterpret_cast<double *>(w + L.dSe), reinterpret_cast<double *>(w + L.scratch), dq,
-      dk_out, dv_out, dg, dbeta, dS0, st);
+      dk_out, dv_out, dg, dbeta, dS0, signed_gates, st);
   return e == hipSuccess ? CKDA_OK : CKDA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" int ckda_backward(const void *q, const void *k, const void *v, const float *g,
+                             const float *beta, const float *S0, const int32_t *cu_seqlens,
+                             int B, int T, int H, int dk, int dv, int N, int in_dtype,
+                             const float *d_o, const float *dS_T, float *dq, float *dk_out,
+                             float *dv_out, float *dg, float *dbeta, float *dS0, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+  return backward_impl(q, k, v, g, beta, S0, cu_seqlens, B, T, H, dk, dv, N, in_dtype, d_o, dS_T,
+                       dq, dk_out, dv_out, dg, dbeta, dS0, workspace, workspace_bytes, 1, stream);
+}
+
+extern "C" int kda_backward(const void *q, const void *k, const void *v, const float *g,
+                            const float *beta, const float *S0, const int32_t *cu_seqlens,
+                            int B, int T, int H, int dk, int dv, int N, int in_dtype,
+                            const float *d_o, const float *dS_T, float *dq, float *dk_out,
+                            float *dv_out, float *dg, float *dbeta, float *dS0, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+  return backward_impl(q, k, v, g, beta, S0, cu_seqlens, B, T, H, dk, dv, N, in_dtype, d_o, dS_T,
+                       dq, dk_out, dv_out, dg, dbeta, dS0, workspace, workspace_bytes, 0, stream);
 }
 
 extern "C" int ckda_decode_step(const void *q, const void *k, const void *v, const float *g,

@@ -161,7 +161,7 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_chunk(
     const double *__restrict__ S_chunks, const double *__restrict__ U_chunks,
     const double *__restrict__ dU_chunks, const double *__restrict__ dSe_chunks,
     double *__restrict__ scratch, float *__restrict__ dq, float *__restrict__ dk,
-    float *__restrict__ dv, float *__restrict__ dg, float *__restrict__ dbeta) {
+    float *__restrict__ dv, float *__restrict__ dg, float *__restrict__ dbeta, int signed_gates) {
   using R = Rec<DK, DV>;
   using X = Scr<DK, DV>;
   constexpr int NBM = DV > 64 ? DV : 64;
@@ -211,7 +211,7 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_chunk(
     for (int i = 0; i < C; ++i) {
       const float a = s_g[i * DK + t];
       G += fmax(log2(fabs((double)a)), kLog2Floor);
-      par ^= (a < 0.f);
+      par ^= (signed_gates && a < 0.f);   // KDA mode: signs ignored
       gmax = fmax(gmax, G);
       gmin = fmin(gmin, G);
       scr[X::G + i * DK + t] = G;
@@ -498,7 +498,7 @@ hipError_t launch_bwd_shape(const void *q, const void *k, const void *v, const f
                             size_t rec_bytes, const double *S_chunks, const double *U_chunks,
                             double *dU_chunks, double *dSe_chunks, double *scratch, float *dq,
                             float *dk, float *dv, float *dg, float *dbeta, float *dS0,
-                            hipStream_t stream) {
+                            int signed_gates, hipStream_t stream) {
   const size_t rec_doubles = rec_bytes / sizeof(double);
   hipLaunchKernelGGL((f64_bwd_state<DK, DV>), dim3((DV / kBV) * N * H), dim3(kThreads), 0, stream,
                      dO, dS_T, H, N, tab, records, rec_doubles, dU_chunks, dSe_chunks, dS0);
@@ -507,7 +507,8 @@ hipError_t launch_bwd_shape(const void *q, const void *k, const void *v, const f
   hipLaunchKernelGGL((f64_bwd_chunk<TIn, DK, DV>), dim3((unsigned)n_chunks_ub, H), dim3(kThreads),
                      0, stream, static_cast<const TIn *>(q), static_cast<const TIn *>(k),
                      static_cast<const TIn *>(v), g, beta, dO, H, N, tab, records, rec_doubles,
-                     S_chunks, U_chunks, dU_chunks, dSe_chunks, scratch, dq, dk, dv, dg, dbeta);
+                     S_chunks, U_chunks, dU_chunks, dSe_chunks, scratch, dq, dk, dv, dg, dbeta,
+                     signed_gates);
   return hipGetLastError();
 }
 
@@ -523,9 +524,9 @@ hipError_t launch_bwd_f64(const void *q, const void *k, const void *v, const flo
                           size_t n_chunks_ub, void *records, size_t rec_bytes, double *S_chunks,
                           double *U_chunks, double *dU_chunks, double *dSe_chunks,
                           double *scratch, float *dq, float *dk_out, float *dv_out, float *dg,
-                          float *dbeta, float *dS0, hipStream_t stream) {
+                          float *dbeta, float *dS0, int signed_gates, hipStream_t stream) {
   hipError_t e = launch_f64_pass(q, k, v, g, beta, S0, H, dk, dv, N, in_dtype, tab, n_chunks_ub,
-                                 records, rec_bytes, nullptr, nullptr, 1, 0, 0, S_chunks,
+                                 records, rec_bytes, nullptr, nullptr, signed_gates, 0, 0, S_chunks,
                                  U_chunks, stream);
   if (e != hipSuccess) return e;
   const double *rec = static_cast<const double *>(records);
@@ -534,7 +535,7 @@ hipError_t launch_bwd_f64(const void *q, const void *k, const void *v, const flo
     return launch_bwd_shape<TIN, DK_, DV_>(q, k, v, g, beta, dO, dS_T, H, N, tab, n_chunks_ub,  \
                                            rec, rec_bytes, S_chunks, U_chunks, dU_chunks,      \
                                            dSe_chunks, scratch, dq, dk_out, dv_out, dg, dbeta, \
-                                           dS0, stream);
+                                           dS0, signed_gates, stream);
   if (in_dtype == CKDA_BF16) {
     CKDA_BWD_CASE(__hip_bfloat16, 64, 64)
     CKDA_BWD_CASE(__hip_bfloat16, 64, 128)

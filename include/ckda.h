@@ -215,6 +215,20 @@ int ckda_backward(const void *q, const void *k, const void *v, const float *g,
                   size_t workspace_bytes, void *stream);
 
 /*
+ * Backward of kda_forward (KDA mode: gate signs ignored, |g| used), the
+ * baseline of the CKDA summary's forward-plus-backward throughput comparison
+ * ("Main Findings", throughput bullet).  The loss depends on g only through
+ * log|g|, so dg = dlog|g| / g as in ckda_backward.  Arguments, layouts,
+ * workspace, aliasing rules and errors are exactly those of ckda_backward.
+ */
+int kda_backward(const void *q, const void *k, const void *v, const float *g,
+                 const float *beta, const float *S0, const int32_t *cu_seqlens,
+                 int B, int T, int H, int dk, int dv, int N, int in_dtype,
+                 const float *d_o, const float *dS_T, float *dq, float *d_k, float *d_v,
+                 float *dg, float *dbeta, float *dS0, void *workspace,
+                 size_t workspace_bytes, void *stream);
+
+/*
  * One recurrent decode step for N*H independent states, in place.
  *
  *   S <- (I - beta k k^T) Diag(alpha) S + beta k v^T ;  o = S^T q

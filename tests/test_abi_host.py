@@ -146,3 +146,16 @@ def test_backward_workspace_bytes(lib):
     assert f(2, 256, 2, 128, 128, 2, 0) > a                  # grows with T
     # At least the fp64 state kept per (chunk, head): 4 chunks x 2 heads x 2 rows.
     assert a >= 2 * 2 * 2 * 128 * 128 * 8
+
+
+def test_kda_backward_validates_like_ckda_backward(lib):
+    def call(entry, **kw):
+        saved = lib.ckda_backward
+        try:
+            lib.ckda_backward = getattr(lib, entry)
+            return _bwd(lib, **kw)
+        finally:
+            lib.ckda_backward = saved
+    for kw in (dict(dk=96), dict(dtype=5), dict(null=("dq",)), dict(misalign=("dg",)),
+               dict(alias=("dq", "q")), dict(ws=16)):
+        assert call("kda_backward", **kw) == call("ckda_backward", **kw) != 0, kw

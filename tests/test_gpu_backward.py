@@ -167,3 +167,37 @@ def test_backward_full_size_sampled():
         say(f"  sequence {b}")
         for name, a, r in zip(NAMES, got, ref):
             _assert_close(name, a[b:b + 1], r)
+
+
+def test_kda_backward_uses_gate_magnitudes():
+    """kda_backward is the backward of the recurrence on |g|: every gradient
+    matches the oracle's on |g|, with dg = d/d|g| * sign(g)."""
+    x = _inputs(29, B=1, T=140, H=2, dk=64, dv=128, dtype="bf16")
+    dt = torch.bfloat16
+    say("[gpu] kda_backward")
+    got = ck.backward(to_dev(x["q"], dt), to_dev(x["k"], dt), to_dev(x["v"], dt), to_dev(x["g"]),
+                      to_dev(x["beta"]), to_dev(x["do"]), S0=to_dev(x["S0"]),
+                      dS_T=to_dev(x["dST"]), kda=True)
+    torch.cuda.synchronize()
+    got = [t.cpu().numpy().astype(np.float64) for t in got]
+    ga = np.abs(x["g"])
+    ref = list(oracle.backward(x["q"], x["k"], x["v"], ga, x["beta"], x["do"], S0=x["S0"],
+                               dS_T=x["dST"]))
+    ref[3] = ref[3] * np.sign(x["g"])
+    for name, a, b in zip(NAMES, got, ref):
+        _assert_close(name, a, b)
+
+
+def test_kda_backward_equals_ckda_backward_on_nonnegative_gates():
+    x = _inputs(30, B=2, T=100, H=2, dk=128, dv=64, dtype="f32")
+    x["g"] = np.abs(x["g"])
+    dt = torch.float32
+    args = (to_dev(x["q"], dt), to_dev(x["k"], dt), to_dev(x["v"], dt), to_dev(x["g"]),
+            to_dev(x["beta"]), to_dev(x["do"]))
+    kw = dict(S0=to_dev(x["S0"]), dS_T=to_dev(x["dST"]))
+    say("[gpu] kda_backward vs ckda_backward, alpha >= 0")
+    a = ck.backward(*args, **kw)
+    b = ck.backward(*args, **kw, kda=True)
+    torch.cuda.synchronize()
+    for name, u, w in zip(NAMES, a, b):
+        assert torch.equal(u, w), name
