@@ -201,3 +201,53 @@ def test_kda_backward_equals_ckda_backward_on_nonnegative_gates():
     torch.cuda.synchronize()
     for name, u, w in zip(NAMES, a, b):
         assert torch.equal(u, w), name
+
+
+def test_backward_is_deterministic():
+    """No atomics or order-dependent reductions: two calls agree bit for bit."""
+    x = _inputs(31, B=2, T=130, H=2, dk=128, dv=128, dtype="bf16")
+    a = _gpu_backward(x, "call 1")
+    b = _gpu_backward(x, "call 2")
+    for name, u, w in zip(NAMES, a, b):
+        np.testing.assert_array_equal(u, w, err_msg=name)
+
+
+def test_backward_packed_equals_separate_calls():
+    """Sequences packed with cu_seqlens give the same gradients, bit for bit,
+    as each sequence run on its own (chunks restart at every sequence)."""
+    lens = [70, 129, 64]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    x = _inputs(32, B=1, T=int(cu[-1]), H=2, dk=64, dv=64, dtype="f32", cu=cu)
+    packed = _gpu_backward(x, "packed")
+    for n, (s0, s1) in enumerate(zip(cu[:-1], cu[1:])):
+        sub = dict(x)
+        for key in ("q", "k", "v", "g", "beta", "do"):
+            sub[key] = np.ascontiguousarray(x[key][:, s0:s1])
+        sub["S0"] = np.ascontiguousarray(x["S0"][n:n + 1])
+        sub["dST"] = np.ascontiguousarray(x["dST"][n:n + 1])
+        sub["cu"] = None
+        one = _gpu_backward(sub, f"sequence {n}")
+        for name, a, b in zip(NAMES[:5], packed[:5], one[:5]):
+            np.testing.assert_array_equal(a[:, s0:s1], b, err_msg=f"{name} seq {n}")
+        np.testing.assert_array_equal(packed[5][n:n + 1], one[5], err_msg=f"dS0 seq {n}")
+
+
+def test_backward_is_linear_in_the_upstream_gradients():
+    """Every gradient is linear in (d_o, dS_T), up to the fp32 rounding of the
+    three results compared (one half-ulp each) and the fp64 allowance."""
+    x = _inputs(33, B=1, T=100, H=2, dk=64, dv=64, dtype="f32")
+    rng = np.random.default_rng(34)
+    # upstream gradients on a 2^-8 grid, so that their fp32 sums are exact
+    grid = lambda shape: (rng.integers(-512, 513, size=shape) / 256.0).astype(np.float32)
+    d1, d2 = grid(x["do"].shape), grid(x["do"].shape)
+    s1, s2 = grid(x["dST"].shape), grid(x["dST"].shape)
+    x = dict(x, do=d1, dST=s1)
+    y = dict(x, do=d2, dST=s2)
+    xs = dict(x, do=d1 + d2, dST=s1 + s2)
+    a, b, s = _gpu_backward(x, "d1"), _gpu_backward(y, "d2"), _gpu_backward(xs, "d1 + d2")
+    for name, u, w, z in zip(NAMES, a, b, s):
+        rms = np.sqrt(np.mean(z * z))
+        bound = 2.0 ** -24 * (np.abs(u) + np.abs(w) + np.abs(z)) + 1e-7 * rms
+        ex = np.abs(u + w - z) - bound
+        j = np.unravel_index(np.argmax(ex), ex.shape)
+        assert ex[j] <= 0.0, (name, j, u[j], w[j], z[j], float(np.abs(u + w - z)[j]), rms)
