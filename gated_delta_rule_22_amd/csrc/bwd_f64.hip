@@ -166,7 +166,7 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_chunk(
   using X = Scr<DK, DV>;
   constexpr int NBM = DV > 64 ? DV : 64;
   constexpr int kStage = stage_doubles(NBM);
-  constexpr int kGroup = 8 * C * kCG > C * DK / 2 ? 8 * C * kCG : C * DK / 2;
+  constexpr int kGroup = 8 * C * kCG > C * DK * 3 / 2 ? 8 * C * kCG : C * DK * 3 / 2;
   __shared__ double s_P[kTri];            // dP (lower incl.), packed
   __shared__ double s_DA[kTri];           // beta_i dA_ij (strictly lower; diagonal 0), packed
   __shared__ double s_u[kStage > kGroup ? kStage : kGroup];  // staging | group operands
@@ -198,19 +198,25 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_chunk(
     return scr[X::SG + m * DK + c] * exp2(scr[X::G + m * DK + c]);
   };
 
-  // ---- phase 0: in-chunk gate log-magnitudes and signs, per channel (the
-  // gates are first staged in LDS with coalesced loads).
-  float *s_g = reinterpret_cast<float *>(s_u);
-  for (int p = t; p < C * DK; p += kThreads)
-    s_g[p] = p / DK < nt ? g[row(p / DK) * DK + p % DK] : 1.f;
+  // ---- phase 0: in-chunk gate log-magnitudes and signs: log2|alpha| for
+  // every (token, channel) in parallel into LDS (the sign rides in the sign
+  // bit of a float copy of alpha), then the scans per channel.
+  double *s_l = s_u;                                   // [C][DK] log2|alpha|
+  float *s_sg = reinterpret_cast<float *>(s_u + C * DK); // [C][DK] alpha (sign only)
+#pragma unroll 4
+  for (int p = t; p < C * DK; p += kThreads) {
+    const float a = p / DK < nt ? g[row(p / DK) * DK + p % DK] : 1.f;
+    s_l[p] = fmax(log2(fabs((double)a)), kLog2Floor);
+    s_sg[p] = a;
+  }
   __syncthreads();
   if (t < DK) {
     double G = 0.0, gmax = 0.0, gmin = 0.0;
     bool par = false;
 #pragma unroll 8
     for (int i = 0; i < C; ++i) {
-      const float a = s_g[i * DK + t];
-      G += fmax(log2(fabs((double)a)), kLog2Floor);
+      const float a = s_sg[i * DK + t];
+      G += s_l[i * DK + t];
       par ^= (signed_gates && a < 0.f);   // KDA mode: signs ignored
       gmax = fmax(gmax, G);
       gmin = fmin(gmin, G);
@@ -375,6 +381,20 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_chunk(
   // ---- phase 4: pair sums per group of kCG channels, then the gate gradients
   const int gcl = t % kCG, grw = t / kCG;          // channel in the group, row slot
   constexpr int kRowSlots = kThreads / kCG;
+  // this thread's gates, keys and queries of the next channel group, loaded
+  // while the current group is summed
+  constexpr int NG = C * kCG / kThreads;
+  float pg[NG], pk[NG], pq[NG];
+  auto load_group = [&](int c0) {
+#pragma unroll
+    for (int u = 0; u < NG; ++u) {
+      const int p = t + u * kThreads, i = p / kCG, cc = c0 + p % kCG;
+      pg[u] = i < nt ? g[row(i) * DK + cc] : 1.f;
+      pk[u] = i < nt ? to_f32(k[row(i) * DK + cc]) : 0.f;
+      pq[u] = i < nt ? to_f32(q[row(i) * DK + cc]) : 0.f;
+    }
+  };
+  load_group(0);
   for (int c0 = 0; c0 < DK; c0 += kCG) {
     const int c = c0 + gcl;
     double *e = s_u, *f = s_u + C * kCG, *kk_ = s_u + 2 * C * kCG, *qq = s_u + 3 * C * kCG;
@@ -382,12 +402,12 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_chunk(
     double *saq = s_u + 5 * C * kCG, *sak = s_u + 6 * C * kCG, *sag = s_u + 7 * C * kCG;
     __syncthreads();
 #pragma unroll
-    for (int p = t; p < C * kCG; p += kThreads) {
-      const int i = p / kCG, cc = c0 + p % kCG;
+    for (int u = 0; u < NG; ++u) {
+      const int p = t + u * kThreads, i = p / kCG, cc = c0 + p % kCG;
       const double G = scr[X::G + i * DK + cc], sg = scr[X::SG + i * DK + cc];
       {
         const double floor_mag = exp2(kLog2Floor);
-        const double a = i < nt ? (double)g[row(i) * DK + cc] : 1.0;
+        const double a = pg[u];
         ra[p] = 1.0 / (fabs(a) < floor_mag ? (a < 0.0 ? -floor_mag : floor_mag) : a);
       }
       if (s_fb[cc]) {
@@ -397,13 +417,14 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_chunk(
         e[p] = sg * exp2(G - s_R[cc]);
         f[p] = sg * exp2(s_R[cc] - G);
       }
-      kk_[p] = i < nt ? (double)to_f32(k[row(i) * DK + cc]) : 0.0;
-      qq[p] = i < nt ? (double)to_f32(q[row(i) * DK + cc]) : 0.0;
+      kk_[p] = pk[u];
+      qq[p] = pq[u];
       saq[p] = scr[X::AQ + i * DK + cc];
       sak[p] = scr[X::AK + i * DK + cc];
       sag[p] = scr[X::AG + i * DK + cc];
     }
     __syncthreads();
+    if (c0 + kCG < DK) load_group(c0 + kCG);
     {
       const bool fb = s_fb[c];
 #pragma unroll 1

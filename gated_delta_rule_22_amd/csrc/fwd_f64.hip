@@ -23,7 +23,8 @@
 //              channels of per-pair ratio products (each ratio is one product
 //              of two factors taken about the channel's midpoint, or exp2 of
 //              the difference where the channel spans too many binary orders),
-//              T by forward substitution, then W, Ubar, gamma*Q, K_hat, gamma_n.
+//              T blockwise (diagonal 16 x 16 blocks by forward substitution,
+//              then block rows), then W, Ubar, gamma*Q, K_hat, gamma_n.
 //              T and A / beta stay in the record for the backward pass.
 //   f64_inter  grid (dv blocks x sequences x heads): the serial chunk loop on
 //              an fp64 state slice held in LDS, each product an LDS-staged
@@ -67,20 +68,23 @@ __global__ __launch_bounds__(kThreads) void f64_intra(
 
   auto row = [&](int i) { return (size_t)(t0 + i) * H + h; };   // token-head row
 
-  // ---- gates: inclusive cumsum of log2|alpha| and parity of negatives (the
-  // gates are first staged in LDS with coalesced loads).
-  float *s_g = reinterpret_cast<float *>(s_u);
-  for (int p = t; p < C * DK; p += kThreads)
-    s_g[p] = p / DK < nt ? g[row(p / DK) * DK + p % DK] : 1.f;
+  // ---- gates: log2|alpha| and the sign of every (token, channel) in
+  // parallel, then the inclusive scans (cumsum of the log-magnitudes, parity
+  // of the negatives) per channel.
+#pragma unroll 4
+  for (int p = t; p < C * DK; p += kThreads) {
+    const float a = p / DK < nt ? g[row(p / DK) * DK + p % DK] : 1.f;
+    s_G[p] = fmax(log2(fabs((double)a)), kLog2Floor);
+    s_par[p] = (uint8_t)(signed_gates && a < 0.f);   // KDA mode: signs ignored
+  }
   __syncthreads();
   if (t < DK) {
     double G = 0.0, gmax = 0.0, gmin = 0.0;
     uint8_t par = 0;
 #pragma unroll 8
     for (int i = 0; i < C; ++i) {
-      const float a = s_g[i * DK + t];
-      G += fmax(log2(fabs((double)a)), kLog2Floor);
-      par ^= (uint8_t)(signed_gates && a < 0.f);   // KDA mode: signs ignored
+      G += s_G[i * DK + t];
+      par ^= s_par[i * DK + t];
       gmax = fmax(gmax, G);
       gmin = fmin(gmin, G);
       s_G[i * DK + t] = G;
@@ -121,12 +125,25 @@ __global__ __launch_bounds__(kThreads) void f64_intra(
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) accA[ii][jj] = accP[ii][jj] = 0.0;
     double *e = s_u, *f = s_u + C * kCG, *kg = s_u + 2 * C * kCG, *qg = s_u + 3 * C * kCG;
+    // this thread's keys and queries of the next channel group, loaded while
+    // the current group is summed
+    constexpr int NG = C * kCG / kThreads;
+    float rk[NG], rq[NG];
+    auto load_group = [&](int c0) {
+#pragma unroll
+      for (int u = 0; u < NG; ++u) {
+        const int p = t + u * kThreads, i = p / kCG, c = c0 + p % kCG;
+        rk[u] = i < nt ? to_f32(k[row(i) * DK + c]) : 0.f;
+        rq[u] = i < nt ? to_f32(q[row(i) * DK + c]) : 0.f;
+      }
+    };
+    load_group(0);
     for (int c0 = 0; c0 < DK; c0 += kCG) {
       __syncthreads();
       // group operands, channel-major: x[cl * C + i]
 #pragma unroll
-      for (int p = t; p < C * kCG; p += kThreads) {
-        const int i = p / kCG, cl = p % kCG, c = c0 + cl;
+      for (int u = 0; u < NG; ++u) {
+        const int p = t + u * kThreads, i = p / kCG, cl = p % kCG, c = c0 + cl;
         const double G = s_G[i * DK + c], sg = s_par[i * DK + c] ? -1.0 : 1.0;
         if (s_fb[c]) {
           e[cl * C + i] = G;
@@ -135,10 +152,11 @@ __global__ __launch_bounds__(kThreads) void f64_intra(
           e[cl * C + i] = sg * exp2(G - s_R[c]);
           f[cl * C + i] = sg * exp2(s_R[c] - G);
         }
-        kg[cl * C + i] = i < nt ? (double)to_f32(k[row(i) * DK + c]) * s_fk[i] : 0.0;
-        qg[cl * C + i] = i < nt ? (double)to_f32(q[row(i) * DK + c]) * s_fq[i] : 0.0;
+        kg[cl * C + i] = (double)rk[u] * s_fk[i];
+        qg[cl * C + i] = (double)rq[u] * s_fq[i];
       }
       __syncthreads();
+      if (c0 + kCG < DK) load_group(c0 + kCG);
       for (int cl = 0; cl < kCG; ++cl) {
         const double *ec = e + cl * C, *fc = f + cl * C, *kc = kg + cl * C, *qc = qg + cl * C;
         double ei[4], ki[4], qi[4], fj[4], kj[4];
@@ -192,7 +210,7 @@ __global__ __launch_bounds__(kThreads) void f64_intra(
   }
 
   // ---- gamma-scaled operands (masked tokens have k = q = 0).
-#pragma unroll 4
+#pragma unroll 8
   for (int p = t; p < C * DK; p += kThreads) {
     const int i = p / DK, c = p % DK;
     const double Gi = s_G[i * DK + c], Gn = s_G[(C - 1) * DK + c];
@@ -209,18 +227,43 @@ __global__ __launch_bounds__(kThreads) void f64_intra(
   __threadfence_block();   // scratch is read back by this workgroup only
   __syncthreads();
 
-  // ---- T = (I + A)^-1 by forward substitution; column j per thread.
+  // ---- T = (I + A)^-1, blockwise over 16 x 16 blocks: the four diagonal
+  // blocks by forward substitution (a column per thread), then block rows
+  // I = 1..3 in turn: T_IJ = -T_II sum_{J<=K<I} A_IK T_KJ for every J < I.
   double *s_T = s_G;     // G is dead; T is C x (C+1)
+  for (int p = t; p < C * (C + 1); p += kThreads) s_T[p] = (p / (C + 1) == p % (C + 1)) ? 1.0 : 0.0;
+  __syncthreads();
   if (t < C) {
-    const int j = t;
-    for (int i = 0; i < C; ++i) s_T[i * (C + 1) + j] = (i == j) ? 1.0 : 0.0;
-    for (int i = j + 1; i < C; ++i) {
-      double s = 0.0;
-      for (int m = j; m < i; ++m) s += s_A[i * (C + 1) + m] * s_T[m * (C + 1) + j];
-      s_T[i * (C + 1) + j] = -s;
+    const int j = t, ie = (j / 16) * 16 + 16;
+    for (int i = j + 1; i < ie; ++i) {
+      double acc = 0.0;
+      for (int m = j; m < i; ++m) acc += s_A[i * (C + 1) + m] * s_T[m * (C + 1) + j];
+      s_T[i * (C + 1) + j] = -acc;
     }
   }
   __syncthreads();
+  {
+    double *s_M = s_u;   // M_IJ = sum_K A_IK T_KJ, up to three 16 x 16 blocks
+    for (int I = 1; I < C / 16; ++I) {
+      for (int e = t; e < I * 256; e += kThreads) {
+        const int J = e / 256, r = (e % 256) / 16, c = e % 16;
+        double acc = 0.0;
+        for (int K = J; K < I; ++K)
+#pragma unroll 4
+          for (int m = 0; m < 16; ++m)
+            acc += s_A[(16 * I + r) * (C + 1) + 16 * K + m] * s_T[(16 * K + m) * (C + 1) + 16 * J + c];
+        s_M[e] = acc;
+      }
+      __syncthreads();
+      for (int e = t; e < I * 256; e += kThreads) {
+        const int J = e / 256, r = (e % 256) / 16, c = e % 16;
+        double acc = 0.0;
+        for (int m = 0; m <= r; ++m) acc += s_T[(16 * I + r) * (C + 1) + 16 * I + m] * s_M[J * 256 + m * 16 + c];
+        s_T[(16 * I + r) * (C + 1) + 16 * J + c] = -acc;
+      }
+      __syncthreads();
+    }
+  }
 
   // ---- T, W = T Diag(beta) (gamma*K), Ubar = T Diag(beta) V.
   for (int p = t; p < C * C; p += kThreads) rec[R::TI + p] = s_T[(p / C) * (C + 1) + p % C];
