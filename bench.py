@@ -194,6 +194,49 @@ def main():
         del q, k, v, g, ga, beta, o, S_T, ws
         torch.cuda.empty_cache()
 
+    # ------------------------------------------------------------- decode
+    if not args.skip_decode:
+        wd = wl.WORKLOADS["decode_256x16"]
+        steps = args.decode_steps or wd.steps
+        print(f"[bench] decode {wd.name}: drawing {steps} steps", file=sys.stderr, flush=True)
+        xs = wl.decode_steps(wd, range(steps), workers=min(16, os.cpu_count() or 1))
+        bf = lambda a: torch.from_numpy(a).to(dev).to(torch.bfloat16)
+        f32 = lambda a: torch.from_numpy(a).to(dev)
+        dq = torch.stack([bf(s["q"]) for s in xs])
+        dk_ = torch.stack([bf(s["k"]) for s in xs])
+        dv_ = torch.stack([bf(s["v"]) for s in xs])
+        dg = torch.stack([f32(s["g"]) for s in xs])
+        db = torch.stack([f32(s["beta"]) for s in xs])
+        del xs
+        S = torch.from_numpy(wl.decode_state(wd)).to(dev)
+        do = torch.empty((steps, wd.B, wd.H, wd.dv), dtype=torch.float32, device=dev)
+        step = lambda i: ck.decode_step(dq[i], dk_[i], dv_[i], dg[i], db[i], S, out=do[i])
+        for i in range(min(3, steps)):          # warm-up (advances the state)
+            step(i)
+        torch.cuda.synchronize()
+        print(f"[bench] decode: timing {steps} steps", file=sys.stderr, flush=True)
+        stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            step(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_d = e0.elapsed_time(e1) / steps
+        dbytes, per_head = decode_algorithmic(wd)
+        dgbs = dbytes / (ms_d * 1e-3) / 1e9
+        dtraffic = profiled_traffic("decode_256x16.md", "gated_delta_rule_22_amd/csrc/decode.hip")
+        out["decode"] = {"workload": wd.name, "steps": steps, "us_per_step": ms_d * 1e3,
+                         "traffic": dtraffic,
+                         "steps_per_s": 1e3 / ms_d, "hbm_gbs": dgbs, "hbm_frac": dgbs / HBM_PEAK_GBS,
+                         "bytes_per_step": dbytes, "bytes_per_state": per_head}
+        if args.skip_forward:
+            out["roofline"] = {"bound": "hbm", "achieved": dgbs, "peak": HBM_PEAK_GBS,
+                               "unit": "GB/s", "frac": dgbs / HBM_PEAK_GBS, "traffic": dtraffic,
+                               "kernel": "decode step"}
+        del dq, dk_, dv_, dg, db, S, do
+        torch.cuda.empty_cache()
+
     # ------------------------------------------------------------- backward
     if not args.skip_backward:
         print(f"[bench] backward {w.name}: uploading", file=sys.stderr, flush=True)
@@ -250,49 +293,6 @@ def main():
         del q, k, v, g, ga, beta, do, dST, ws
         torch.cuda.empty_cache()
 
-    # ------------------------------------------------------------- decode
-    if not args.skip_decode:
-        wd = wl.WORKLOADS["decode_256x16"]
-        steps = args.decode_steps or wd.steps
-        print(f"[bench] decode {wd.name}: drawing {steps} steps", file=sys.stderr, flush=True)
-        xs = wl.decode_steps(wd, range(steps), workers=min(16, os.cpu_count() or 1))
-        bf = lambda a: torch.from_numpy(a).to(dev).to(torch.bfloat16)
-        f32 = lambda a: torch.from_numpy(a).to(dev)
-        dq = torch.stack([bf(s["q"]) for s in xs])
-        dk_ = torch.stack([bf(s["k"]) for s in xs])
-        dv_ = torch.stack([bf(s["v"]) for s in xs])
-        dg = torch.stack([f32(s["g"]) for s in xs])
-        db = torch.stack([f32(s["beta"]) for s in xs])
-        del xs
-        S = torch.from_numpy(wl.decode_state(wd)).to(dev)
-        do = torch.empty((steps, wd.B, wd.H, wd.dv), dtype=torch.float32, device=dev)
-        step = lambda i: ck.decode_step(dq[i], dk_[i], dv_[i], dg[i], db[i], S, out=do[i])
-        for i in range(min(3, steps)):          # warm-up (advances the state)
-            step(i)
-        torch.cuda.synchronize()
-        print(f"[bench] decode: timing {steps} steps", file=sys.stderr, flush=True)
-        stream = torch.cuda.current_stream()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(steps):
-            step(i)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms_d = e0.elapsed_time(e1) / steps
-        dbytes, per_head = decode_algorithmic(wd)
-        dgbs = dbytes / (ms_d * 1e-3) / 1e9
-        dtraffic = profiled_traffic("decode_256x16.md", "gated_delta_rule_22_amd/csrc/decode.hip")
-        out["decode"] = {"workload": wd.name, "steps": steps, "us_per_step": ms_d * 1e3,
-                         "traffic": dtraffic,
-                         "steps_per_s": 1e3 / ms_d, "hbm_gbs": dgbs, "hbm_frac": dgbs / HBM_PEAK_GBS,
-                         "bytes_per_step": dbytes, "bytes_per_state": per_head}
-        if args.skip_forward:
-            out["roofline"] = {"bound": "hbm", "achieved": dgbs, "peak": HBM_PEAK_GBS,
-                               "unit": "GB/s", "frac": dgbs / HBM_PEAK_GBS, "traffic": dtraffic,
-                               "kernel": "decode step"}
-        del dq, dk_, dv_, dg, db, S, do
-        torch.cuda.empty_cache()
-
     # ------------------------------------------------------------- other configs (time only)
     if not args.skip_forward and not args.skip_others:
         others = {}
@@ -344,6 +344,21 @@ def main():
                                "kind": "oracle",
                                "sample": f"the whole {w.name} forward (B={w.B}, T={w.T}, H={w.H}), "
                                          f"fp64 token-by-token, {dt:.1f} s"}
+        if "backward" in out:
+            # the oracle's backward on one of the batch rows (all heads), with the
+            # same kind of upstream gradients
+            rng = np.random.default_rng(0)
+            sl = slice(0, 1)
+            do1 = rng.normal(size=(1, w.T, w.H, w.dv))
+            dST1 = rng.normal(size=(1, w.H, w.dk, w.dv))
+            t0 = time.perf_counter()
+            oracle.backward(x["q"][sl], x["k"][sl], x["v"][sl], x["g"][sl], x["beta"][sl], do1,
+                            dS_T=dST1, nthreads=nth)
+            dtb = time.perf_counter() - t0
+            out["backward"]["cpu_baseline"] = {
+                "value": w.T / dtb, "unit": "tokens/s", "cores": min(nth, w.H), "kind": "oracle",
+                "sample": f"one of the {w.B} sequences of {w.name} (T={w.T}, H={w.H}), fp64 "
+                          f"reverse mode with recomputed states, {dtb:.1f} s"}
     print(json.dumps(out), flush=True)
 
 
