@@ -147,3 +147,75 @@ def test_exact_zero_gate_and_large_beta():
     o_ref, S_ref = oracle.forward(x["q"], x["k"], x["v"], x["g"], x["beta"], S0=x["S0"])
     assert rel_err(o.cpu().numpy(), o_ref) <= 1e-5
     assert rel_err(S.cpu().numpy(), S_ref) <= 1e-5
+
+
+def test_segment_transition_composes_at_real_shape():
+    """The building block of sharding one long sequence over several GPUs, on
+    one GPU at the rotation workload's real shape (fp32, T = 4096, H = 4,
+    d = 128; gates +-1, beta = 2, unit keys): split at t1 = 2000 (not a chunk
+    boundary).  Running the second segment from S0 = I with v = 0 extracts its
+    transition M = prod A_t (dk x dk); from S0 = 0 with the real v, its offset
+    R.  Then the full run's S_T = M S_mid + R, where S_mid is the first
+    segment's final state, and M is orthogonal (every A_t is, at beta = 2,
+    |alpha| = 1, |k| = 1)."""
+    w = wl.scaled("rotation_f32", B=1)
+    x = wl.forward_inputs(w)
+    d = upload(x)
+    dk = x["q"].shape[-1]
+    t1 = 2000
+    seg = lambda lo, hi: {k_: d[k_][:, lo:hi].contiguous() for k_ in ("q", "k", "v", "g", "beta")}
+    say("[gpu] segment transition composition, rotation shape")
+    _, S_full = _fwd(d)
+    a = seg(0, t1)
+    a["S0"] = d["S0"]
+    _, S_mid = _fwd(a)
+    b = seg(t1, x["q"].shape[1])
+    H = x["q"].shape[2]
+    eye = torch.eye(dk, device="cuda").expand(1, H, dk, dk).contiguous()
+    bm = dict(b, v=torch.zeros_like(b["v"]), S0=eye)
+    _, M = _fwd(bm)
+    br = dict(b, S0=None)
+    _, Rr = _fwd(br)
+    composed = torch.matmul(M.double(), S_mid.double()) + Rr.double()
+    assert rel_err(composed.cpu().numpy(), S_full.cpu().numpy()) <= TOL["f32"]
+    Mt = M.double()
+    gram = torch.matmul(Mt.transpose(-1, -2), Mt)
+    err = (gram - torch.eye(dk, device="cuda", dtype=torch.float64)).abs().max().item()
+    say(f"  |M^T M - I|_max = {err:.2e}")
+    assert err <= 1e-4
+
+
+def test_forward_is_linear_in_values_and_initial_state():
+    """With q, k, alpha, beta fixed, (o, S_T) is linear in (v, S0).  Inputs on
+    a 2^-8 grid so that the fp32 sums are exact; fp64 arithmetic inside."""
+    x = _rand_forward(23, B=2, T=150, H=2, dk=64, dv=64, dtype="f32")
+    rng = np.random.default_rng(23)
+    grid = lambda shape: (rng.integers(-256, 257, size=shape) / 256.0).astype(np.float32)
+    v1, v2 = grid(x["v"].shape), grid(x["v"].shape)
+    s1, s2 = grid(x["S0"].shape), grid(x["S0"].shape)
+    run = lambda v, s: _fwd(upload(dict(x, v=v, S0=s)))
+    say("[gpu] linearity in (v, S0)")
+    o1, S1 = run(v1, s1)
+    o2, S2 = run(v2, s2)
+    o3, S3 = run(v1 + v2, s1 + s2)
+    for a, b, c in ((o1, o2, o3), (S1, S2, S3)):
+        a, b, c = (t.double().cpu().numpy() for t in (a, b, c))
+        bound = 2.0 ** -24 * (np.abs(a) + np.abs(b) + np.abs(c)) + 1e-12 * np.sqrt(np.mean(c * c))
+        assert np.all(np.abs(a + b - c) <= 2 * bound)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_head_permutation_equivariance(dtype):
+    """Heads are independent: permuting them in the inputs permutes the
+    outputs, bit for bit."""
+    x = _rand_forward(24, B=2, T=130, H=4, dk=128, dv=128, dtype=dtype)
+    d = upload(x)
+    perm = torch.tensor([2, 0, 3, 1], device="cuda")
+    dp = {k_: (v_.index_select(2, perm).contiguous() if k_ in ("q", "k", "v", "g", "beta")
+               else v_.index_select(1, perm).contiguous() if k_ == "S0" and v_ is not None
+               else v_) for k_, v_ in d.items()}
+    say(f"[gpu] head permutation {dtype}")
+    o, S = _fwd(d)
+    op, Sp = _fwd(dp)
+    assert torch.equal(op, o.index_select(2, perm))
+    assert torch.equal(Sp, S.index_select(1, perm))
