@@ -115,8 +115,15 @@ def forward(q, k, v, g, beta, S0=None, cu_seqlens=None, nthreads: int | None = N
     return o, S_T
 
 
+def l2_normalise(x):
+    """Each row (last axis) scaled by (sum x^2 + 1e-6)^(-1/2), in fp64: the
+    key/query normalisation the fused forward option applies."""
+    x = _f64(x)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + 1e-6)
+
+
 def backward(q, k, v, g, beta, do, S0=None, dS_T=None, cu_seqlens=None,
-             nthreads: int | None = None):
+             nthreads: int | None = None, normalize_qk: bool = False):
     """Reverse-mode gradient of the token-by-token forward, in fp64.
 
     For upstream gradients ``do`` (``[B, T, H, dv]``, of o) and ``dS_T``
@@ -125,7 +132,22 @@ def backward(q, k, v, g, beta, do, S0=None, dS_T=None, cu_seqlens=None,
     ``(dq, dk, dv, dg, dbeta, dS0)``, shaped like q, k, v, g, beta and
     ``[N, H, dk, dv]``.  ``dg`` is the derivative with respect to the signed
     gate alpha itself.  Rows outside every packed sequence get zero gradients.
+
+    ``normalize_qk``: the forward first replaces every row x of q and of k by
+    x s with s = (sum x^2 + 1e-6)^(-1/2); the chain rule through that step
+    (d x = s (d xh - xh (xh . d xh)) with xh = x s) follows the recurrence's
+    gradient with respect to the normalised rows.
     """
+    if normalize_qk:
+        qh, kh = l2_normalise(q), l2_normalise(k)
+        out = list(backward(qh, kh, v, g, beta, do, S0=S0, dS_T=dS_T, cu_seqlens=cu_seqlens,
+                            nthreads=nthreads))
+        for idx, (x, xh) in ((0, (q, qh)), (1, (k, kh))):
+            x = _f64(x)
+            s = 1.0 / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + 1e-6)
+            dxh = out[idx]
+            out[idx] = s * (dxh - xh * np.sum(xh * dxh, axis=-1, keepdims=True))
+        return tuple(out)
     q, k, v, g, beta, do = map(_f64, (q, k, v, g, beta, do))
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -194,4 +216,5 @@ def transition(k, g, beta):
     return S_T[0, 0]
 
 
-__all__ = ["build", "forward", "backward", "decode_step", "transition", "default_threads"]
+__all__ = ["build", "forward", "backward", "l2_normalise", "decode_step", "transition",
+           "default_threads"]

@@ -150,3 +150,33 @@ def test_backward_rejects_bad_shapes():
     args, do, dST = _inputs(rng, B=1, T=3, H=1, dk=2, dv=2)
     with pytest.raises(ValueError):
         oracle.backward(*args[:5], do[..., :1], S0=args[5])
+
+
+def test_backward_with_qk_normalisation_matches_finite_differences():
+    """The gradient through the fused key/query L2 normalisation: central
+    differences of forward(normalise(q), normalise(k), ...) for every element
+    of q and k, and the other gradients unchanged by the option."""
+    rng = np.random.default_rng(18)
+    args, do, dST = _inputs(rng, B=1, T=6, H=2, dk=3, dv=2)
+    q, k, v, g, beta, S0 = args
+    grads = oracle.backward(q, k, v, g, beta, do, S0=S0, dS_T=dST, nthreads=1,
+                            normalize_qk=True)
+
+    def loss(qq, kk):
+        o, ST = oracle.forward(oracle.l2_normalise(qq), oracle.l2_normalise(kk), v, g, beta,
+                               S0=S0, nthreads=1)
+        return float((o * do).sum() + (ST * dST).sum())
+
+    for which, x in ((0, q), (1, k)):
+        scale = max(1.0, float(np.abs(grads[which]).max()))
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += H_FD
+            xm[idx] -= H_FD
+            pair = lambda a: (a, k) if which == 0 else (q, a)
+            fd = (loss(*pair(xp)) - loss(*pair(xm))) / (2 * H_FD)
+            assert abs(fd - grads[which][idx]) <= 1e-7 * scale, (which, idx)
+    plain = oracle.backward(oracle.l2_normalise(q), oracle.l2_normalise(k), v, g, beta, do,
+                            S0=S0, dS_T=dST, nthreads=1)
+    for a, b in zip(grads[2:], plain[2:]):
+        np.testing.assert_array_equal(a, b)
