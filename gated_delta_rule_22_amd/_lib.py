@@ -52,6 +52,8 @@ def library() -> ctypes.CDLL:
         lib.ckda_backward.restype = ci
         lib.kda_backward.argtypes = [vp] * 7 + [ci] * 7 + [vp] * 8 + [vp, sz, vp]
         lib.kda_backward.restype = ci
+        lib.ckda_backward_ex.argtypes = [vp] * 7 + [ci] * 8 + [vp] * 8 + [vp, sz, vp]
+        lib.ckda_backward_ex.restype = ci
         lib.ckda_decode_step.argtypes = [vp] * 7 + [ci] * 5 + [vp]
         lib.ckda_decode_step.restype = ci
         _lib = lib
@@ -171,11 +173,13 @@ def backward_workspace_bytes(B, T, H, dk, dv, N, dtype) -> int:
 
 
 def backward(q, k, v, g, beta, do, S0=None, dS_T=None, cu_seqlens=None, *, workspace=None,
-             need_dS0=True, kda=False):
+             need_dS0=True, kda=False, normalize_qk=False):
     """Gradients of ``sum(do * o) + sum(dS_T * S_T)`` for the forward's inputs:
     returns ``(dq, dk, dv, dg, dbeta, dS0)`` as fp32 tensors (``dS0`` is None
     when ``need_dS0`` is False).  See ``ckda_backward`` in include/ckda.h;
-    ``kda=True`` calls ``kda_backward`` (the backward of :func:`kda_forward`)."""
+    ``kda=True`` calls ``kda_backward`` (the backward of :func:`kda_forward`);
+    ``normalize_qk=True`` is the backward of ``forward(..., normalize_qk=True)``
+    (``ckda_backward_ex``)."""
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     code = _dtype_code(q)
@@ -205,11 +209,16 @@ def backward(q, k, v, g, beta, do, S0=None, dS_T=None, cu_seqlens=None, *, works
     ws_bytes = backward_workspace_bytes(B, T, H, dk, dv, N, code)
     if workspace is None or workspace.numel() * workspace.element_size() < ws_bytes:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    entry = "kda_backward" if kda else "ckda_backward"
-    st = getattr(library(), entry)(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(cu_seqlens),
-        B, T, H, dk, dv, N, code, _ptr(do), _ptr(dS_T), _ptr(dq), _ptr(dk_), _ptr(dv_),
-        _ptr(dg), _ptr(db), _ptr(dS0), _ptr(workspace), ws_bytes, _stream(dev))
+    head = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(cu_seqlens),
+            B, T, H, dk, dv, N, code)
+    tail = (_ptr(do), _ptr(dS_T), _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(dg), _ptr(db),
+            _ptr(dS0), _ptr(workspace), ws_bytes, _stream(dev))
+    if normalize_qk:
+        entry = "ckda_backward_ex"
+        st = library().ckda_backward_ex(*head, OPT_QK_L2NORM | (OPT_KDA if kda else 0), *tail)
+    else:
+        entry = "kda_backward" if kda else "ckda_backward"
+        st = getattr(library(), entry)(*head, *tail)
     _check(st, entry)
     return dq, dk_, dv_, dg, db, dS0
 

@@ -210,9 +210,12 @@ int backward_impl(const void *q, const void *k, const void *v, const float *g, c
                   const float *S0, const int32_t *cu_seqlens, int B, int T, int H, int dk, int dv,
                   int N, int in_dtype, const float *d_o, const float *dS_T, float *dq,
                   float *dk_out, float *dv_out, float *dg, float *dbeta, float *dS0,
-                  void *workspace, size_t workspace_bytes, int signed_gates, void *stream) {
+                  void *workspace, size_t workspace_bytes, int options, void *stream) {
   const bool packed = cu_seqlens != nullptr;
   if (int s = forward_shape_status(B, T, H, dk, dv, N, in_dtype, packed)) return s;
+  if (options & ~(CKDA_OPT_KDA | CKDA_OPT_QK_L2NORM)) return CKDA_ERR_SHAPE;
+  const int signed_gates = (options & CKDA_OPT_KDA) ? 0 : 1;
+  const int l2norm = (options & CKDA_OPT_QK_L2NORM) ? 1 : 0;
   const size_t rows = (size_t)B * T * H;
   if (rows > 0 && (!q || !k || !v || !g || !beta || !d_o || !dq || !dk_out || !dv_out || !dg ||
                    !dbeta))
@@ -252,7 +255,7 @@ int backward_impl(const void *q, const void *k, const void *v, const float *g, c
       w + L.records, L.rec_bytes, reinterpret_cast<double *>(w + L.S),
       reinterpret_cast<double *>(w + L.U), reinterpret_cast<double *>(w + L.dU),
       reinterpret_cast<double *>(w + L.dSe), reinterpret_cast<double *>(w + L.scratch), dq,
-      dk_out, dv_out, dg, dbeta, dS0, signed_gates, st);
+      dk_out, dv_out, dg, dbeta, dS0, signed_gates, l2norm, st);
   return e == hipSuccess ? CKDA_OK : CKDA_ERR_LAUNCH;
 }
 
@@ -265,7 +268,19 @@ extern "C" int ckda_backward(const void *q, const void *k, const void *v, const 
                              float *dv_out, float *dg, float *dbeta, float *dS0, void *workspace,
                              size_t workspace_bytes, void *stream) {
   return backward_impl(q, k, v, g, beta, S0, cu_seqlens, B, T, H, dk, dv, N, in_dtype, d_o, dS_T,
-                       dq, dk_out, dv_out, dg, dbeta, dS0, workspace, workspace_bytes, 1, stream);
+                       dq, dk_out, dv_out, dg, dbeta, dS0, workspace, workspace_bytes, 0, stream);
+}
+
+extern "C" int ckda_backward_ex(const void *q, const void *k, const void *v, const float *g,
+                                const float *beta, const float *S0, const int32_t *cu_seqlens,
+                                int B, int T, int H, int dk, int dv, int N, int in_dtype,
+                                int options, const float *d_o, const float *dS_T, float *dq,
+                                float *dk_out, float *dv_out, float *dg, float *dbeta,
+                                float *dS0, void *workspace, size_t workspace_bytes,
+                                void *stream) {
+  return backward_impl(q, k, v, g, beta, S0, cu_seqlens, B, T, H, dk, dv, N, in_dtype, d_o, dS_T,
+                       dq, dk_out, dv_out, dg, dbeta, dS0, workspace, workspace_bytes, options,
+                       stream);
 }
 
 extern "C" int kda_backward(const void *q, const void *k, const void *v, const float *g,
@@ -275,7 +290,8 @@ extern "C" int kda_backward(const void *q, const void *k, const void *v, const f
                             float *dv_out, float *dg, float *dbeta, float *dS0, void *workspace,
                             size_t workspace_bytes, void *stream) {
   return backward_impl(q, k, v, g, beta, S0, cu_seqlens, B, T, H, dk, dv, N, in_dtype, d_o, dS_T,
-                       dq, dk_out, dv_out, dg, dbeta, dS0, workspace, workspace_bytes, 0, stream);
+                       dq, dk_out, dv_out, dg, dbeta, dS0, workspace, workspace_bytes, CKDA_OPT_KDA,
+                       stream);
 }
 
 extern "C" int ckda_decode_step(const void *q, const void *k, const void *v, const float *g,

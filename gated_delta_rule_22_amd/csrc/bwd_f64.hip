@@ -161,7 +161,8 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_chunk(
     const double *__restrict__ S_chunks, const double *__restrict__ U_chunks,
     const double *__restrict__ dU_chunks, const double *__restrict__ dSe_chunks,
     double *__restrict__ scratch, float *__restrict__ dq, float *__restrict__ dk,
-    float *__restrict__ dv, float *__restrict__ dg, float *__restrict__ dbeta, int signed_gates) {
+    float *__restrict__ dv, float *__restrict__ dg, float *__restrict__ dbeta, int signed_gates,
+    int l2norm) {
   using R = Rec<DK, DV>;
   using X = Scr<DK, DV>;
   constexpr int NBM = DV > 64 ? DV : 64;
@@ -175,6 +176,8 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_chunk(
   __shared__ double s_R[DK];
   __shared__ int s_fb[DK];
   __shared__ double s_red[4 * DK], s_red2[2 * DK], s_dGn[DK];
+  __shared__ double s_fk[C], s_fq[C];     // key/query normalisation factors per token (1 if off)
+  __shared__ double s_kd[C], s_qd[C];     // khat . dkhat and qhat . dqhat per token
 
   const int cflat = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
   if (cflat >= tab.chunk_off[N]) return;
@@ -232,6 +235,30 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_chunk(
   if (t < C) {
     s_beta[t] = t < nt ? (double)beta[row(t)] : 0.0;
     s_db[t] = 0.0;
+    s_kd[t] = 0.0;
+    s_qd[t] = 0.0;
+  }
+  // optional q/k normalisation factors (sum x^2 + 1e-6)^(-1/2): four threads per
+  // token, 32 channels each
+  {
+    const int i = t >> 2, part = t & 3;
+    double sk = 0.0, sq = 0.0;
+    if (l2norm && i < nt) {
+#pragma unroll 8
+      for (int c = part * (DK / 4); c < (part + 1) * (DK / 4); ++c) {
+        const double kk = to_f32(k[row(i) * DK + c]), qq = to_f32(q[row(i) * DK + c]);
+        sk += kk * kk;
+        sq += qq * qq;
+      }
+    }
+    sk += __shfl_xor(sk, 1);
+    sk += __shfl_xor(sk, 2);
+    sq += __shfl_xor(sq, 1);
+    sq += __shfl_xor(sq, 2);
+    if (part == 0 && i < C) {
+      s_fk[i] = (l2norm && i < nt) ? 1.0 / sqrt(sk + 1e-6) : 1.0;
+      s_fq[i] = (l2norm && i < nt) ? 1.0 / sqrt(sq + 1e-6) : 1.0;
+    }
   }
   __threadfence_block();   // scratch is read back by this workgroup only
   __syncthreads();
@@ -417,8 +444,8 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_chunk(
         e[p] = sg * exp2(G - s_R[cc]);
         f[p] = sg * exp2(s_R[cc] - G);
       }
-      kk_[p] = pk[u];
-      qq[p] = pq[u];
+      kk_[p] = pk[u] * s_fk[i];
+      qq[p] = pq[u] * s_fq[i];
       saq[p] = scr[X::AQ + i * DK + cc];
       sak[p] = scr[X::AK + i * DK + cc];
       sag[p] = scr[X::AG + i * DK + cc];
@@ -490,7 +517,17 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_chunk(
         double gG = sag[i * kCG + gcl] + qi * R1 + ki * (R2 - C1 - C2);
         if (i == C - 1) gG += s_dGn[c];
         s_ag[i * kCG + gcl] = gG;
-        if (i < nt) {
+        if (l2norm) {
+          // gradients with respect to the normalised rows; the normalisation's
+          // Jacobian is applied once every channel is done
+          scr[X::AQ + i * DK + c] = gq;
+          scr[X::AK + i * DK + c] = gk;
+          const double dqd = sum16(qi * gq), dkd = sum16(ki * gk);
+          if (gcl == 0) {
+            s_qd[i] += dqd;
+            s_kd[i] += dkd;
+          }
+        } else if (i < nt) {
           dq[row(i) * DK + c] = (float)gq;
           dk[row(i) * DK + c] = (float)gk;
         }
@@ -508,7 +545,19 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_chunk(
       }
     }
   }
+  __threadfence_block();   // scratch is read back by this workgroup only
   __syncthreads();
+  if (l2norm) {
+    // x = xhat / f_x with xhat = x f_x:  dx = f_x (dxhat - xhat (xhat . dxhat))
+#pragma unroll 4
+    for (int p = t; p < nt * DK; p += kThreads) {
+      const int i = p / DK, c = p % DK;
+      const double qh = to_f32(q[row(i) * DK + c]) * s_fq[i];
+      const double kh = to_f32(k[row(i) * DK + c]) * s_fk[i];
+      dq[row(i) * DK + c] = (float)(s_fq[i] * (scr[X::AQ + p] - qh * s_qd[i]));
+      dk[row(i) * DK + c] = (float)(s_fk[i] * (scr[X::AK + p] - kh * s_kd[i]));
+    }
+  }
   if (t < nt) dbeta[row(t)] = (float)s_db[t];
 }
 
@@ -519,7 +568,7 @@ hipError_t launch_bwd_shape(const void *q, const void *k, const void *v, const f
                             size_t rec_bytes, const double *S_chunks, const double *U_chunks,
                             double *dU_chunks, double *dSe_chunks, double *scratch, float *dq,
                             float *dk, float *dv, float *dg, float *dbeta, float *dS0,
-                            int signed_gates, hipStream_t stream) {
+                            int signed_gates, int l2norm, hipStream_t stream) {
   const size_t rec_doubles = rec_bytes / sizeof(double);
   hipLaunchKernelGGL((f64_bwd_state<DK, DV>), dim3((DV / kBV) * N * H), dim3(kThreads), 0, stream,
                      dO, dS_T, H, N, tab, records, rec_doubles, dU_chunks, dSe_chunks, dS0);
@@ -529,7 +578,7 @@ hipError_t launch_bwd_shape(const void *q, const void *k, const void *v, const f
                      0, stream, static_cast<const TIn *>(q), static_cast<const TIn *>(k),
                      static_cast<const TIn *>(v), g, beta, dO, H, N, tab, records, rec_doubles,
                      S_chunks, U_chunks, dU_chunks, dSe_chunks, scratch, dq, dk, dv, dg, dbeta,
-                     signed_gates);
+                     signed_gates, l2norm);
   return hipGetLastError();
 }
 
@@ -545,9 +594,9 @@ hipError_t launch_bwd_f64(const void *q, const void *k, const void *v, const flo
                           size_t n_chunks_ub, void *records, size_t rec_bytes, double *S_chunks,
                           double *U_chunks, double *dU_chunks, double *dSe_chunks,
                           double *scratch, float *dq, float *dk_out, float *dv_out, float *dg,
-                          float *dbeta, float *dS0, int signed_gates, hipStream_t stream) {
+                          float *dbeta, float *dS0, int signed_gates, int l2norm, hipStream_t stream) {
   hipError_t e = launch_f64_pass(q, k, v, g, beta, S0, H, dk, dv, N, in_dtype, tab, n_chunks_ub,
-                                 records, rec_bytes, nullptr, nullptr, signed_gates, 0, 0, S_chunks,
+                                 records, rec_bytes, nullptr, nullptr, signed_gates, l2norm, 0, S_chunks,
                                  U_chunks, stream);
   if (e != hipSuccess) return e;
   const double *rec = static_cast<const double *>(records);
@@ -556,7 +605,7 @@ hipError_t launch_bwd_f64(const void *q, const void *k, const void *v, const flo
     return launch_bwd_shape<TIN, DK_, DV_>(q, k, v, g, beta, dO, dS_T, H, N, tab, n_chunks_ub,  \
                                            rec, rec_bytes, S_chunks, U_chunks, dU_chunks,      \
                                            dSe_chunks, scratch, dq, dk_out, dv_out, dg, dbeta, \
-                                           dS0, signed_gates, stream);
+                                           dS0, signed_gates, l2norm, stream);
   if (in_dtype == CKDA_BF16) {
     CKDA_BWD_CASE(__hip_bfloat16, 64, 64)
     CKDA_BWD_CASE(__hip_bfloat16, 64, 128)

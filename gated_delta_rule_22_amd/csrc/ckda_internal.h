@@ -67,7 +67,8 @@ hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, const fl
 // forward's serial pass (keeping per-chunk states and U), the reverse pass of
 // the state gradient, then the per-chunk gradients.  signed_gates = 0 is KDA
 // mode (|g| is used; the gradient with respect to g is then dlog|g| / g, the
-// same formula).
+// same formula).  l2norm: q and k are L2-normalised per (token, head) before
+// use, and their gradients pass back through that normalisation.
 size_t f64_bwd_scratch_bytes(int dk, int dv);
 hipError_t launch_bwd_f64(const void *q, const void *k, const void *v, const float *g,
                           const float *beta, const float *S0, const float *dO, const float *dS_T,
@@ -75,6 +76,7 @@ hipError_t launch_bwd_f64(const void *q, const void *k, const void *v, const flo
                           size_t n_chunks_ub, void *records, size_t rec_bytes, double *S_chunks,
                           double *U_chunks, double *dU_chunks, double *dSe_chunks,
                           double *scratch, float *dq, float *dk_out, float *dv_out, float *dg,
-                          float *dbeta, float *dS0, int signed_gates, hipStream_t stream);
+                          float *dbeta, float *dS0, int signed_gates, int l2norm,
+                          hipStream_t stream);
 
 }  // namespace ckda

@@ -204,8 +204,8 @@ size_t ckda_backward_workspace_bytes(int B, int T, int H, int dk, int dv, int N,
  * (CKDA_ERR_ALIAS).  Numerics: every step runs in fp64 (inputs widen
  * exactly) and each gradient is rounded once to fp32.  A gate of exactly 0 is
  * differentiated at |alpha| = 2^-1000, the floor of its log-magnitude, so
- * its own gradient is not meaningful.  The KDA and L2-normalisation options
- * of ckda_forward_ex have no backward here.
+ * its own gradient is not meaningful.  ckda_backward_ex below covers the
+ * KDA and L2-normalisation options of ckda_forward_ex.
  */
 int ckda_backward(const void *q, const void *k, const void *v, const float *g,
                   const float *beta, const float *S0, const int32_t *cu_seqlens,
@@ -227,6 +227,26 @@ int kda_backward(const void *q, const void *k, const void *v, const float *g,
                  const float *d_o, const float *dS_T, float *dq, float *d_k, float *d_v,
                  float *dg, float *dbeta, float *dS0, void *workspace,
                  size_t workspace_bytes, void *stream);
+
+/*
+ * ckda_backward with options (bitwise or), the backward of ckda_forward_ex
+ * for the same options (the CKDA summary's methodology names Triton kernels
+ * that fuse the signs into the key/query normalisation and its backward pass):
+ *    0                   as ckda_backward
+ *    CKDA_OPT_KDA        as kda_backward
+ *    CKDA_OPT_QK_L2NORM  q and k were L2-normalised per (token, head) in the
+ *                        forward: x -> x (sum_c x_c^2 + 1e-6)^(-1/2).  dq and
+ *                        dk are the gradients with respect to the caller's
+ *                        raw q and k, through that normalisation (in fp64)
+ * CKDA_OPT_O_BF16 and unknown bits return CKDA_ERR_SHAPE.  Every other
+ * argument, the workspace and all error rules are those of ckda_backward.
+ */
+int ckda_backward_ex(const void *q, const void *k, const void *v, const float *g,
+                     const float *beta, const float *S0, const int32_t *cu_seqlens,
+                     int B, int T, int H, int dk, int dv, int N, int in_dtype, int options,
+                     const float *d_o, const float *dS_T, float *dq, float *d_k, float *d_v,
+                     float *dg, float *dbeta, float *dS0, void *workspace,
+                     size_t workspace_bytes, void *stream);
 
 /*
  * One recurrent decode step for N*H independent states, in place.

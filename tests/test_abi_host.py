@@ -159,3 +159,21 @@ def test_kda_backward_validates_like_ckda_backward(lib):
     for kw in (dict(dk=96), dict(dtype=5), dict(null=("dq",)), dict(misalign=("dg",)),
                dict(alias=("dq", "q")), dict(ws=16)):
         assert call("kda_backward", **kw) == call("ckda_backward", **kw) != 0, kw
+
+
+def test_backward_ex_rejects_output_dtype_and_unknown_options(lib):
+    # Every call below fails host validation (a 16-byte workspace at most), so
+    # nothing is ever launched on the fake pointers.
+    def call(options, ws):
+        saved = lib.ckda_backward
+
+        def ex(*a):
+            return lib.ckda_backward_ex(*a[:14], options, *a[14:])
+        try:
+            lib.ckda_backward = ex
+            return _bwd(lib, ws=ws)
+        finally:
+            lib.ckda_backward = saved
+    assert call(4, 16) == 2          # CKDA_OPT_O_BF16 has no backward
+    assert call(8, 16) == 2          # unknown bit
+    assert call(1, 16) == call(3, 16) == call(0, 16) == 5   # valid options reach the workspace check

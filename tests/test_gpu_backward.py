@@ -281,3 +281,31 @@ def test_backward_packed_64k_sampled():
         for name, a, r in zip(NAMES[:5], got[:5], ref[:5]):
             _assert_close(name, a[:, s0:s1], r)
         _assert_close("dS0", got[5][n:n + 1], ref[5])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("kda", [False, True])
+def test_backward_through_qk_normalisation(dtype, kda):
+    """ckda_backward_ex with CKDA_OPT_QK_L2NORM (and KDA mode): the gradient
+    with respect to the raw keys and queries, through the fused normalisation,
+    against the oracle's chain rule.  Unnormalised inputs, so the Jacobian of
+    the normalisation matters."""
+    x = _inputs(36, B=2, T=140, H=2, dk=128, dv=64, dtype=dtype)
+    rng = np.random.default_rng(36)
+    cast = wl.round_bf16 if dtype == "bf16" else (lambda a: a.astype(np.float32))
+    x["q"] = cast(rng.normal(size=x["q"].shape) * 0.7)
+    x["k"] = cast(rng.normal(size=x["k"].shape) * 0.3)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    say(f"[gpu] ckda_backward_ex L2NORM kda={kda} {dtype}")
+    got = ck.backward(to_dev(x["q"], dt), to_dev(x["k"], dt), to_dev(x["v"], dt), to_dev(x["g"]),
+                      to_dev(x["beta"]), to_dev(x["do"]), S0=to_dev(x["S0"]),
+                      dS_T=to_dev(x["dST"]), kda=kda, normalize_qk=True)
+    torch.cuda.synchronize()
+    got = [t.cpu().numpy().astype(np.float64) for t in got]
+    g = np.abs(x["g"]) if kda else x["g"]
+    ref = list(oracle.backward(x["q"], x["k"], x["v"], g, x["beta"], x["do"], S0=x["S0"],
+                               dS_T=x["dST"], normalize_qk=True))
+    if kda:
+        ref[3] = ref[3] * np.sign(x["g"])
+    for name, a, b in zip(NAMES, got, ref):
+        _assert_close(name, a, b)
