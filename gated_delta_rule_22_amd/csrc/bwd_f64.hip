@@ -153,8 +153,13 @@ __device__ __forceinline__ int tri(int i, int j) { return i * (i + 1) / 2 + j; }
 
 // --------------------------------------------------------------------------
 // f64_bwd_chunk: all per-chunk gradients of one (chunk, head).
+// The chunk-gradient kernel runs 512 threads (two waves per SIMD) over the
+// same LDS, so that each wave holds half the rows of every block product.
+constexpr int kBT = 512;
+constexpr int kRPT = 1024 / kBT;          // rows per thread in the block products
+
 template <typename TIn, int DK, int DV>
-__global__ __launch_bounds__(kThreads) void f64_bwd_chunk(
+__global__ __launch_bounds__(kBT) void f64_bwd_chunk(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, const float *__restrict__ dO,
     int H, int N, SeqTable tab, const double *__restrict__ records, size_t rec_doubles,
@@ -175,7 +180,7 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_chunk(
   __shared__ double s_beta[C], s_db[C];
   __shared__ double s_R[DK];
   __shared__ int s_fb[DK];
-  __shared__ double s_red[4 * DK], s_red2[2 * DK], s_dGn[DK];
+  __shared__ double s_red[(kBT / 64) * DK], s_red2[2 * DK], s_dGn[DK];
   __shared__ double s_fk[C], s_fq[C];     // key/query normalisation factors per token (1 if off)
   __shared__ double s_kd[C], s_qd[C];     // khat . dkhat and qhat . dqhat per token
 
@@ -207,7 +212,7 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_chunk(
   double *s_l = s_u;                                   // [C][DK] log2|alpha|
   float *s_sg = reinterpret_cast<float *>(s_u + C * DK); // [C][DK] alpha (sign only)
 #pragma unroll 4
-  for (int p = t; p < C * DK; p += kThreads) {
+  for (int p = t; p < C * DK; p += kBT) {
     const float a = p / DK < nt ? g[row(p / DK) * DK + p % DK] : 1.f;
     s_l[p] = fmax(log2(fabs((double)a)), kLog2Floor);
     s_sg[p] = a;
@@ -265,13 +270,13 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_chunk(
 
   // ---- phase 1: dX = T^T dU; dV = Diag(beta) dX; dbeta += dX_i . V_i
   {
-    double acc[4][DV / 16];
-    gemm64<DV, C, true, false>(
+    double acc[kRPT][DV / 16];
+    gemm64<DV, C, true, false, kBT>(
         sA, sB, [&](int m, int kk) { return rec[R::TI + kk * C + m]; },
         [&](int kk, int nn) { return dUc[kk * DV + nn]; }, acc);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = rgp * 4 + r;
+    for (int r = 0; r < kRPT; ++r) {
+      const int m = rgp * kRPT + r;
       double part = 0.0;
 #pragma unroll
       for (int jj = 0; jj < DV / 16; ++jj) {
@@ -291,22 +296,22 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_chunk(
 
   // ---- phase 2: dP = tril(dO U^T) and beta_i dA_ij, dA = -strict_tril(dX U^T)
   {
-    double acc[4][4];
-    gemm64<64, DV, false, true>(
+    double acc[kRPT][4];
+    gemm64<64, DV, false, true, kBT>(
         sA, sB, dO_at, [&](int kk, int nn) { return Uc[nn * DV + kk]; }, acc);
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < kRPT; ++r)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const int m = rgp * 4 + r, j = cl + 16 * jj;
+        const int m = rgp * kRPT + r, j = cl + 16 * jj;
         if (j <= m) s_P[tri(m, j)] = acc[r][jj];
       }
-    gemm64<64, DV, false, true>(
+    gemm64<64, DV, false, true, kBT>(
         sA, sB, [&](int m, int kk) { return scr[X::DX + m * DV + kk]; },
         [&](int kk, int nn) { return Uc[nn * DV + kk]; }, acc);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = rgp * 4 + r;
+    for (int r = 0; r < kRPT; ++r) {
+      const int m = rgp * kRPT + r;
       double part = 0.0;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
@@ -325,26 +330,26 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_chunk(
 #pragma unroll 1
   for (int hf = 0; hf < DK / 64; ++hf) {
     const int cb = hf * 64;
-    double aq[4][4], ak[4][4], ag[4][4], gam[4][4], acc[4][4];
+    double aq[kRPT][4], ak[kRPT][4], ag[kRPT][4], gam[kRPT][4], acc[kRPT][4];
     // dQT = dO S^T: dq = gamma dQT; dGamma = q gamma dQT
-    gemm64<64, DV, false, true>(
+    gemm64<64, DV, false, true, kBT>(
         sA, sB, dO_at, [&](int kk, int nn) { return Sc[(cb + nn) * DV + kk]; }, acc);
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < kRPT; ++r)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const int m = rgp * 4 + r, c = cb + cl + 16 * jj;
+        const int m = rgp * kRPT + r, c = cb + cl + 16 * jj;
         gam[r][jj] = gam_at(m, c);
         aq[r][jj] = gam[r][jj] * acc[r][jj];
         ag[r][jj] = rec[R::QT + m * DK + c] * acc[r][jj];
       }
     // M5 = dX S^T: d(gamma K) = -Diag(beta) M5
-    gemm64<64, DV, false, true>(
+    gemm64<64, DV, false, true, kBT>(
         sA, sB, [&](int m, int kk) { return scr[X::DX + m * DV + kk]; },
         [&](int kk, int nn) { return Sc[(cb + nn) * DV + kk]; }, acc);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = rgp * 4 + r;
+    for (int r = 0; r < kRPT; ++r) {
+      const int m = rgp * kRPT + r;
       double part = 0.0;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
@@ -359,7 +364,7 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_chunk(
     }
     // dKH = U dS'^T: dk += (gamma_n / gamma) dKH; dGamma_i -= k (gamma_n/gamma) dKH,
     // and the same amount, summed over i, goes to dGamma_n.
-    gemm64<64, DV, false, true>(
+    gemm64<64, DV, false, true, kBT>(
         sA, sB, [&](int m, int kk) { return Uc[m * DV + kk]; },
         [&](int kk, int nn) { return dSe[(cb + nn) * DV + kk]; }, acc);
 #pragma unroll
@@ -368,8 +373,8 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_chunk(
       const double Gn = scr[X::G + (C - 1) * DK + c], sn = scr[X::SG + (C - 1) * DK + c];
       double col = 0.0;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = rgp * 4 + r;
+      for (int r = 0; r < kRPT; ++r) {
+        const int m = rgp * kRPT + r;
         const double khr = scr[X::SG + m * DK + c] * sn * exp2(Gn - scr[X::G + m * DK + c]);
         const double term = rec[R::KH + m * DK + c] * acc[r][jj];
         ak[r][jj] += khr * acc[r][jj];
@@ -381,17 +386,17 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_chunk(
       if ((t & 63) < 16) s_red[wave * DK + c] = col;
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < kRPT; ++r)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const int m = rgp * 4 + r, c = cb + cl + 16 * jj;
+        const int m = rgp * kRPT + r, c = cb + cl + 16 * jj;
         scr[X::AQ + m * DK + c] = aq[r][jj];
         scr[X::AK + m * DK + c] = ak[r][jj];
         scr[X::AG + m * DK + c] = ag[r][jj];
       }
   }
   // gamma_n sum_j dS'[c][j] S[c][j]: two threads per channel
-  for (int p = t; p < 2 * DK; p += kThreads) {
+  for (int p = t; p < 2 * DK; p += kBT) {
     const int c = p % DK, half = p / DK;
     double part = 0.0;
 #pragma unroll 16
@@ -401,21 +406,25 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_chunk(
   }
   __threadfence_block();   // scratch is read back by this workgroup only
   __syncthreads();
-  for (int c = t; c < DK; c += kThreads)
-    s_dGn[c] = s_red[c] + s_red[DK + c] + s_red[2 * DK + c] + s_red[3 * DK + c] +
-               rec[R::GN + c] * (s_red2[c] + s_red2[DK + c]);
+  for (int c = t; c < DK; c += kBT)
+  {
+    double col = 0.0;
+#pragma unroll
+    for (int w = 0; w < kBT / 64; ++w) col += s_red[w * DK + c];
+    s_dGn[c] = col + rec[R::GN + c] * (s_red2[c] + s_red2[DK + c]);
+  }
 
   // ---- phase 4: pair sums per group of kCG channels, then the gate gradients
   const int gcl = t % kCG, grw = t / kCG;          // channel in the group, row slot
-  constexpr int kRowSlots = kThreads / kCG;
+  constexpr int kRowSlots = kBT / kCG;
   // this thread's gates, keys and queries of the next channel group, loaded
   // while the current group is summed
-  constexpr int NG = C * kCG / kThreads;
+  constexpr int NG = C * kCG / kBT;
   float pg[NG], pk[NG], pq[NG];
   auto load_group = [&](int c0) {
 #pragma unroll
     for (int u = 0; u < NG; ++u) {
-      const int p = t + u * kThreads, i = p / kCG, cc = c0 + p % kCG;
+      const int p = t + u * kBT, i = p / kCG, cc = c0 + p % kCG;
       pg[u] = i < nt ? g[row(i) * DK + cc] : 1.f;
       pk[u] = i < nt ? to_f32(k[row(i) * DK + cc]) : 0.f;
       pq[u] = i < nt ? to_f32(q[row(i) * DK + cc]) : 0.f;
@@ -430,7 +439,7 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_chunk(
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < NG; ++u) {
-      const int p = t + u * kThreads, i = p / kCG, cc = c0 + p % kCG;
+      const int p = t + u * kBT, i = p / kCG, cc = c0 + p % kCG;
       const double G = scr[X::G + i * DK + cc], sg = scr[X::SG + i * DK + cc];
       {
         const double floor_mag = exp2(kLog2Floor);
@@ -550,7 +559,7 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_chunk(
   if (l2norm) {
     // x = xhat / f_x with xhat = x f_x:  dx = f_x (dxhat - xhat (xhat . dxhat))
 #pragma unroll 4
-    for (int p = t; p < nt * DK; p += kThreads) {
+    for (int p = t; p < nt * DK; p += kBT) {
       const int i = p / DK, c = p % DK;
       const double qh = to_f32(q[row(i) * DK + c]) * s_fq[i];
       const double kh = to_f32(k[row(i) * DK + c]) * s_fk[i];
@@ -574,7 +583,7 @@ hipError_t launch_bwd_shape(const void *q, const void *k, const void *v, const f
                      dO, dS_T, H, N, tab, records, rec_doubles, dU_chunks, dSe_chunks, dS0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_chunks_ub == 0) return e;
-  hipLaunchKernelGGL((f64_bwd_chunk<TIn, DK, DV>), dim3((unsigned)n_chunks_ub, H), dim3(kThreads),
+  hipLaunchKernelGGL((f64_bwd_chunk<TIn, DK, DV>), dim3((unsigned)n_chunks_ub, H), dim3(kBT),
                      0, stream, static_cast<const TIn *>(q), static_cast<const TIn *>(k),
                      static_cast<const TIn *>(v), g, beta, dO, H, N, tab, records, rec_doubles,
                      S_chunks, U_chunks, dU_chunks, dSe_chunks, scratch, dq, dk, dv, dg, dbeta,

@@ -30,9 +30,10 @@ struct Rec {
 
 // --------------------------------------------------------------------------
 // Block product in fp64: Out(m, n) = sum_{kk < K} A(m, kk) B(kk, n) for
-// m < 64 and n < NB, staged through LDS in K-slices of 16.  Thread t owns rows
-// 4 (t / 16) + r (r < 4) and columns t % 16 + 16 jj (jj < NB / 16) and gets
-// its sums in acc[r][jj].  fa / fb return the operands (from global memory or
+// m < 64 and n < NB, staged through LDS in K-slices of 16, by a block of NT
+// (256 or 512) threads.  Thread t owns rows RPT (t / 16) + r (r < RPT =
+// 1024 / NT) and columns t % 16 + 16 jj (jj < NB / 16) and gets its sums in
+// acc[r][jj].  fa / fb return the operands (from global memory or
 // LDS); the next slice is loaded into registers while the current one is
 // multiplied, so its latency hides behind the arithmetic.  A_MFAST / B_KFAST
 // choose which index runs fastest across threads when loading, so that a
@@ -43,30 +44,34 @@ constexpr int kKB = 16;
 constexpr int kStageA = 64 * (kKB + 1);
 __host__ __device__ constexpr int stage_doubles(int nb) { return kStageA + kKB * (nb + 1); }
 
-template <int NB, int K, bool A_MFAST, bool B_KFAST, typename FA, typename FB>
+template <int NB, int K, bool A_MFAST, bool B_KFAST, int NT = kThreads, typename FA,
+          typename FB>
 __device__ __forceinline__ void gemm64(double *sA, double *sB, const FA &fa, const FB &fb,
-                                       double (&acc)[4][NB / 16]) {
+                                       double (&acc)[1024 / NT][NB / 16]) {
   static_assert(K % kKB == 0 && NB % 16 == 0, "K and NB must be multiples of 16");
+  static_assert(NT == 256 || NT == 512, "256 or 512 threads");
+  constexpr int RPT = 1024 / NT;                     // rows per thread: 4 or 2
   constexpr int SA = kKB + 1, SB = NB + 1;
-  constexpr int NA = 64 * kKB / kThreads, NBL = kKB * NB / kThreads;
+  constexpr int NA = 64 * kKB / NT, NBL = kKB * NB / NT;
+  static_assert(NBL >= 1, "NB too small for this thread count");
   const int t = threadIdx.x, rgp = t >> 4, cl = t & 15;
   double ra[NA], rb[NBL];
   auto load = [&](int k0) {
 #pragma unroll
     for (int u = 0; u < NA; ++u) {
-      const int p = t + u * kThreads;
+      const int p = t + u * NT;
       const int m = A_MFAST ? p % 64 : p / kKB, kk = A_MFAST ? p / 64 : p % kKB;
       ra[u] = fa(m, k0 + kk);
     }
 #pragma unroll
     for (int u = 0; u < NBL; ++u) {
-      const int p = t + u * kThreads;
+      const int p = t + u * NT;
       const int kk = B_KFAST ? p % kKB : p / NB, n = B_KFAST ? p / kKB : p % NB;
       rb[u] = fb(k0 + kk, n);
     }
   };
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+  for (int r = 0; r < RPT; ++r)
 #pragma unroll
     for (int jj = 0; jj < NB / 16; ++jj) acc[r][jj] = 0.0;
   load(0);
@@ -75,13 +80,13 @@ __device__ __forceinline__ void gemm64(double *sA, double *sB, const FA &fa, con
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < NA; ++u) {
-      const int p = t + u * kThreads;
+      const int p = t + u * NT;
       const int m = A_MFAST ? p % 64 : p / kKB, kk = A_MFAST ? p / 64 : p % kKB;
       sA[m * SA + kk] = ra[u];
     }
 #pragma unroll
     for (int u = 0; u < NBL; ++u) {
-      const int p = t + u * kThreads;
+      const int p = t + u * NT;
       const int kk = B_KFAST ? p % kKB : p / NB, n = B_KFAST ? p / kKB : p % NB;
       sB[kk * SB + n] = rb[u];
     }
@@ -89,13 +94,13 @@ __device__ __forceinline__ void gemm64(double *sA, double *sB, const FA &fa, con
     if (k0 + kKB < K) load(k0 + kKB);
 #pragma unroll 4
     for (int kk = 0; kk < kKB; ++kk) {
-      double a[4], b[NB / 16];
+      double a[RPT], b[NB / 16];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) a[r] = sA[(rgp * 4 + r) * SA + kk];
+      for (int r = 0; r < RPT; ++r) a[r] = sA[(rgp * RPT + r) * SA + kk];
 #pragma unroll
       for (int jj = 0; jj < NB / 16; ++jj) b[jj] = sB[kk * SB + cl + 16 * jj];
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+      for (int r = 0; r < RPT; ++r)
 #pragma unroll
         for (int jj = 0; jj < NB / 16; ++jj) acc[r][jj] = fma(a[r], b[jj], acc[r][jj]);
     }
