@@ -41,8 +41,13 @@ using namespace f64;
 
 constexpr int kCG = 16;              // channels per group in the pair sums
 
+// The record kernel runs 512 threads (two waves per SIMD over one block's
+// LDS); each thread holds kIR rows of every 64-row tile.
+constexpr int kIT = 512;
+constexpr int kIR = 1024 / kIT;
+
 template <typename TIn, int DK, int DV>
-__global__ __launch_bounds__(kThreads) void f64_intra(
+__global__ __launch_bounds__(kIT) void f64_intra(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, int H, int N, SeqTable tab,
     double *__restrict__ records, size_t rec_doubles, int signed_gates, int l2norm) {
@@ -72,7 +77,7 @@ __global__ __launch_bounds__(kThreads) void f64_intra(
   // parallel, then the inclusive scans (cumsum of the log-magnitudes, parity
   // of the negatives) per channel.
 #pragma unroll 4
-  for (int p = t; p < C * DK; p += kThreads) {
+  for (int p = t; p < C * DK; p += kIT) {
     const float a = p / DK < nt ? g[row(p / DK) * DK + p % DK] : 1.f;
     s_G[p] = fmax(log2(fabs((double)a)), kLog2Floor);
     s_par[p] = (uint8_t)(signed_gates && a < 0.f);   // KDA mode: signs ignored
@@ -116,23 +121,23 @@ __global__ __launch_bounds__(kThreads) void f64_intra(
   __syncthreads();
 
   // ---- A (strictly lower) and P (lower incl. diagonal), channel group by
-  // channel group.  Thread t owns pairs (i, j) = (t/16 + 16 ii, t%16 + 16 jj).
+  // channel group.  Thread t owns pairs (i, j) = (t/16 + 32 ii, t%16 + 16 jj).
   {
     const int bi = t >> 4, bj = t & 15;
-    double accA[4][4], accP[4][4];
+    double accA[kIR][4], accP[kIR][4];
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii)
+    for (int ii = 0; ii < kIR; ++ii)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) accA[ii][jj] = accP[ii][jj] = 0.0;
     double *e = s_u, *f = s_u + C * kCG, *kg = s_u + 2 * C * kCG, *qg = s_u + 3 * C * kCG;
     // this thread's keys and queries of the next channel group, loaded while
     // the current group is summed
-    constexpr int NG = C * kCG / kThreads;
+    constexpr int NG = C * kCG / kIT;
     float rk[NG], rq[NG];
     auto load_group = [&](int c0) {
 #pragma unroll
       for (int u = 0; u < NG; ++u) {
-        const int p = t + u * kThreads, i = p / kCG, c = c0 + p % kCG;
+        const int p = t + u * kIT, i = p / kCG, c = c0 + p % kCG;
         rk[u] = i < nt ? to_f32(k[row(i) * DK + c]) : 0.f;
         rq[u] = i < nt ? to_f32(q[row(i) * DK + c]) : 0.f;
       }
@@ -143,7 +148,7 @@ __global__ __launch_bounds__(kThreads) void f64_intra(
       // group operands, channel-major: x[cl * C + i]
 #pragma unroll
       for (int u = 0; u < NG; ++u) {
-        const int p = t + u * kThreads, i = p / kCG, cl = p % kCG, c = c0 + cl;
+        const int p = t + u * kIT, i = p / kCG, cl = p % kCG, c = c0 + cl;
         const double G = s_G[i * DK + c], sg = s_par[i * DK + c] ? -1.0 : 1.0;
         if (s_fb[c]) {
           e[cl * C + i] = G;
@@ -157,20 +162,24 @@ __global__ __launch_bounds__(kThreads) void f64_intra(
       }
       __syncthreads();
       if (c0 + kCG < DK) load_group(c0 + kCG);
+#pragma unroll 2
       for (int cl = 0; cl < kCG; ++cl) {
         const double *ec = e + cl * C, *fc = f + cl * C, *kc = kg + cl * C, *qc = qg + cl * C;
-        double ei[4], ki[4], qi[4], fj[4], kj[4];
+        double ei[kIR], ki[kIR], qi[kIR], fj[4], kj[4];
+#pragma unroll
+        for (int u = 0; u < kIR; ++u) {
+          ei[u] = ec[bi + 32 * u];
+          ki[u] = kc[bi + 32 * u];
+          qi[u] = qc[bi + 32 * u];
+        }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          ei[u] = ec[bi + 16 * u];
-          ki[u] = kc[bi + 16 * u];
-          qi[u] = qc[bi + 16 * u];
           fj[u] = fc[bj + 16 * u];
           kj[u] = kc[bj + 16 * u];
         }
         if (!s_fb[c0 + cl]) {        // uniform across the block
 #pragma unroll
-          for (int ii = 0; ii < 4; ++ii)
+          for (int ii = 0; ii < kIR; ++ii)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
               const double kr = ei[ii] * fj[jj] * kj[jj];
@@ -181,14 +190,14 @@ __global__ __launch_bounds__(kThreads) void f64_intra(
           double ej[4];
 #pragma unroll
           for (int u = 0; u < 4; ++u) ej[u] = ec[bj + 16 * u];
-          double fi[4];
+          double fi[kIR];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) fi[u] = fc[bi + 16 * u];
+          for (int u = 0; u < kIR; ++u) fi[u] = fc[bi + 32 * u];
 #pragma unroll
-          for (int ii = 0; ii < 4; ++ii)
+          for (int ii = 0; ii < kIR; ++ii)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-              const int i = bi + 16 * ii, j = bj + 16 * jj;
+              const int i = bi + 32 * ii, j = bj + 16 * jj;
               const double r = j <= i ? fi[ii] * fj[jj] * exp2(ei[ii] - ej[jj]) : 0.0;
               const double kr = r * kj[jj];
               accA[ii][jj] = fma(ki[ii], kr, accA[ii][jj]);
@@ -198,10 +207,10 @@ __global__ __launch_bounds__(kThreads) void f64_intra(
       }
     }
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii)
+    for (int ii = 0; ii < kIR; ++ii)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const int i = bi + 16 * ii, j = bj + 16 * jj;
+        const int i = bi + 32 * ii, j = bj + 16 * jj;
         const double a = j < i ? accA[ii][jj] : 0.0;
         s_A[i * (C + 1) + j] = s_beta[i] * a;
         rec[R::AH + i * C + j] = a;
@@ -211,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void f64_intra(
 
   // ---- gamma-scaled operands (masked tokens have k = q = 0).
 #pragma unroll 8
-  for (int p = t; p < C * DK; p += kThreads) {
+  for (int p = t; p < C * DK; p += kIT) {
     const int i = p / DK, c = p % DK;
     const double Gi = s_G[i * DK + c], Gn = s_G[(C - 1) * DK + c];
     const double si = s_par[i * DK + c] ? -1.0 : 1.0;
@@ -231,7 +240,7 @@ __global__ __launch_bounds__(kThreads) void f64_intra(
   // blocks by forward substitution (a column per thread), then block rows
   // I = 1..3 in turn: T_IJ = -T_II sum_{J<=K<I} A_IK T_KJ for every J < I.
   double *s_T = s_G;     // G is dead; T is C x (C+1)
-  for (int p = t; p < C * (C + 1); p += kThreads) s_T[p] = (p / (C + 1) == p % (C + 1)) ? 1.0 : 0.0;
+  for (int p = t; p < C * (C + 1); p += kIT) s_T[p] = (p / (C + 1) == p % (C + 1)) ? 1.0 : 0.0;
   __syncthreads();
   if (t < C) {
     const int j = t, ie = (j / 16) * 16 + 16;
@@ -245,7 +254,7 @@ __global__ __launch_bounds__(kThreads) void f64_intra(
   {
     double *s_M = s_u;   // M_IJ = sum_K A_IK T_KJ, up to three 16 x 16 blocks
     for (int I = 1; I < C / 16; ++I) {
-      for (int e = t; e < I * 256; e += kThreads) {
+      for (int e = t; e < I * 256; e += kIT) {
         const int J = e / 256, r = (e % 256) / 16, c = e % 16;
         double acc = 0.0;
         for (int K = J; K < I; ++K)
@@ -255,7 +264,7 @@ __global__ __launch_bounds__(kThreads) void f64_intra(
         s_M[e] = acc;
       }
       __syncthreads();
-      for (int e = t; e < I * 256; e += kThreads) {
+      for (int e = t; e < I * 256; e += kIT) {
         const int J = e / 256, r = (e % 256) / 16, c = e % 16;
         double acc = 0.0;
         for (int m = 0; m <= r; ++m) acc += s_T[(16 * I + r) * (C + 1) + 16 * I + m] * s_M[J * 256 + m * 16 + c];
@@ -266,30 +275,30 @@ __global__ __launch_bounds__(kThreads) void f64_intra(
   }
 
   // ---- T, W = T Diag(beta) (gamma*K), Ubar = T Diag(beta) V.
-  for (int p = t; p < C * C; p += kThreads) rec[R::TI + p] = s_T[(p / C) * (C + 1) + p % C];
+  for (int p = t; p < C * C; p += kIT) rec[R::TI + p] = s_T[(p / C) * (C + 1) + p % C];
   double *sA = s_u, *sB = s_u + kStageA;
   auto tb = [&](int m, int kk) { return s_T[m * (C + 1) + kk] * s_beta[kk]; };
   {
-    double acc[4][DK / 16];
-    gemm64<DK, C, false, false>(
+    double acc[kIR][DK / 16];
+    gemm64<DK, C, false, false, kIT>(
         sA, sB, tb, [&](int kk, int nn) { return rec[R::GK + kk * DK + nn]; }, acc);
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < kIR; ++r)
 #pragma unroll
       for (int jj = 0; jj < DK / 16; ++jj)
-        rec[R::W + ((t >> 4) * 4 + r) * DK + (t & 15) + 16 * jj] = acc[r][jj];
+        rec[R::W + ((t >> 4) * kIR + r) * DK + (t & 15) + 16 * jj] = acc[r][jj];
   }
   {
-    double acc[4][DV / 16];
-    gemm64<DV, C, false, false>(
+    double acc[kIR][DV / 16];
+    gemm64<DV, C, false, false, kIT>(
         sA, sB, tb,
         [&](int kk, int nn) { return kk < nt ? (double)to_f32(v[row(kk) * DV + nn]) : 0.0; },
         acc);
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < kIR; ++r)
 #pragma unroll
       for (int jj = 0; jj < DV / 16; ++jj)
-        rec[R::UB + ((t >> 4) * 4 + r) * DV + (t & 15) + 16 * jj] = acc[r][jj];
+        rec[R::UB + ((t >> 4) * kIR + r) * DV + (t & 15) + 16 * jj] = acc[r][jj];
   }
 }
 
@@ -401,7 +410,7 @@ hipError_t launch_shape(const void *q, const void *k, const void *v, const float
                         double *S_chunks, double *U_chunks, hipStream_t stream) {
   const size_t rec_doubles = rec_bytes / sizeof(double);
   if (n_chunks_ub > 0) {
-    hipLaunchKernelGGL((f64_intra<TIn, DK, DV>), dim3((unsigned)n_chunks_ub, H), dim3(kThreads),
+    hipLaunchKernelGGL((f64_intra<TIn, DK, DV>), dim3((unsigned)n_chunks_ub, H), dim3(kIT),
                        0, stream, static_cast<const TIn *>(q), static_cast<const TIn *>(k),
                        static_cast<const TIn *>(v), g, beta, H, N, tab,
                        static_cast<double *>(records), rec_doubles, signed_gates, l2norm);
