@@ -45,18 +45,19 @@ using namespace f64;
 
 // --------------------------------------------------------------------------
 // f64_bwd_state: reverse serial pass of dS over the chunks of one
-// (sequence, head, kBV-column block).
+// (sequence, head, kBV-column block), the products on the fp64 matrix cores
+// with their right operands (dS', dO, dU) in LDS.
 template <int DK, int DV>
 __global__ __launch_bounds__(kThreads) void f64_bwd_state(
     const float *__restrict__ dO, const float *__restrict__ dS_T, int H, int N, SeqTable tab,
     const double *__restrict__ records, size_t rec_doubles, double *__restrict__ dU_chunks,
     double *__restrict__ dSe_chunks, float *__restrict__ dS0) {
   using R = Rec<DK, DV>;
-  constexpr int NJ = kBV / 16;
+  using Own = MOwn<kBV>;
+  constexpr int TPW = Own::TPW;
   __shared__ double s_dS[DK * kBV];
   __shared__ double s_dO[C * kBV];
   __shared__ double s_dU[C * kBV];
-  __shared__ double s_st[stage_doubles(kBV)];
 
   constexpr int NV = DV / kBV;
   const int jb = blockIdx.x % NV, rh = blockIdx.x / NV, t = threadIdx.x;
@@ -64,8 +65,6 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_state(
   const int len = tab.seq_len[n], start = tab.seq_start[n];
   const int nch = (len + C - 1) / C;
   const size_t sbase = ((size_t)n * H + h) * DK * DV + (size_t)jb * kBV;
-  const int rgp = t >> 4, cl = t & 15;
-  double *sA = s_st, *sB = s_st + kStageA;
 
   for (int p = t; p < DK * kBV; p += kThreads) {
     const int c = p / kBV, j = p % kBV;
@@ -75,19 +74,18 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_state(
     const size_t ch = (size_t)(tab.chunk_off[n] + lc) * H + h;
     const double *rec = records + ch * rec_doubles;
     const int nt = min(C, len - lc * C);
-    __syncthreads();
     for (int p = t; p < C * kBV; p += kThreads) {
       const int i = p / kBV, j = p % kBV;
       s_dO[p] = i < nt ? (double)dO[((size_t)(start + lc * C + i) * H + h) * DV + jb * kBV + j]
                        : 0.0;
     }
+    __syncthreads();         // dS' and dO complete
     for (int p = t; p < DK * kBV; p += kThreads)
       dSe_chunks[ch * DK * DV + (size_t)(p / kBV) * DV + jb * kBV + p % kBV] = s_dS[p];
     // dU = KH dS' + P^T dO, as one product over [dS'; dO]
     {
-      double acc[4][NJ];
-      gemm64<kBV, DK + C, false, false>(
-          sA, sB,
+      d4 acc[TPW];
+      mgemm<kBV, DK + C>(
           [&](int m, int kk) {
             return kk < DK ? rec[R::KH + m * DK + kk] : rec[R::P + (kk - DK) * C + m];
           },
@@ -96,21 +94,21 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_state(
           },
           acc);
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+      for (int jj = 0; jj < TPW; ++jj)
 #pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) {
-          const int i = rgp * 4 + r, j = cl + 16 * jj;
-          s_dU[i * kBV + j] = acc[r][jj];
-          dU_chunks[ch * C * DV + (size_t)i * DV + jb * kBV + j] = acc[r][jj];
+        for (int r = 0; r < 4; ++r) {
+          const int i = Own::row(r), j = Own::col(jj);
+          s_dU[i * kBV + j] = acc[jj][r];
+          dU_chunks[ch * C * DV + (size_t)i * DV + jb * kBV + j] = acc[jj][r];
         }
     }
+    __syncthreads();         // dU complete; every read of dS' done
     // dS = Diag(gamma_n) dS' + (gamma Q)^T dO - W^T dU, 64 state rows at a time
     // (in place: the product reads dO and dU only)
 #pragma unroll
     for (int half = 0; half < DK / 64; ++half) {
-      double acc[4][NJ];
-      gemm64<kBV, 2 * C, true, false>(
-          sA, sB,
+      d4 acc[TPW];
+      mgemm<kBV, 2 * C>(
           [&](int m, int kk) {
             return kk < C ? rec[R::QT + kk * DK + half * 64 + m]
                           : -rec[R::W + (kk - C) * DK + half * 64 + m];
@@ -118,15 +116,15 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_state(
           [&](int kk, int nn) { return kk < C ? s_dO[kk * kBV + nn] : s_dU[(kk - C) * kBV + nn]; },
           acc);
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+      for (int jj = 0; jj < TPW; ++jj)
 #pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) {
-          const int c = half * 64 + rgp * 4 + r, j = cl + 16 * jj;
-          s_dS[c * kBV + j] = rec[R::GN + c] * s_dS[c * kBV + j] + acc[r][jj];
+        for (int r = 0; r < 4; ++r) {
+          const int c = half * 64 + Own::row(r), j = Own::col(jj);
+          s_dS[c * kBV + j] = rec[R::GN + c] * s_dS[c * kBV + j] + acc[jj][r];
         }
     }
+    __syncthreads();         // dS complete; dO and dU free
   }
-  __syncthreads();
   if (dS0)
     for (int p = t; p < DK * kBV; p += kThreads) {
       const int c = p / kBV, j = p % kBV;

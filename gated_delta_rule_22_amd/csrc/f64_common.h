@@ -108,6 +108,76 @@ __device__ __forceinline__ void gemm64(double *sA, double *sB, const FA &fa, con
   __syncthreads();
 }
 
+// --------------------------------------------------------------------------
+// Block product on the fp64 matrix cores, v_mfma_f64_16x16x4_f64:
+// Out(m, n) = sum_{kk < K} A(m, kk) B(kk, n) for m < 64, n < NB, by NT (256
+// or 512) threads, with no LDS staging and no barrier inside: fa and fb are
+// called in the instruction's operand layout, fa (typically global memory)
+// PF 16-deep K-slices ahead of the multiply, fb (typically LDS) as it is used.  The output is cut into 16 x 16
+// tiles; wave w takes row block w % 4 and column blocks (w / 4) TPW + jj
+// (jj < TPW).  The caller reads its results through MOwn: accumulator
+// element acc[jj][r] is Out(MOwn::row(r), MOwn::col(jj)).  Operand layout of
+// the instruction (one lane l, one K step of 4): A(l % 16, l / 16) and
+// B(l / 16, l % 16); result tile element (4 r + l / 16, l % 16) in
+// accumulator r.  Within a slice lane l takes K indices 4 (l / 16) + q for
+// q < 4 (any fixed permutation of K is the same sum), so that each lane reads
+// four consecutive K of one row of A.
+typedef double d4 __attribute__((ext_vector_type(4)));
+
+template <int NB, int NT = kThreads>
+struct MOwn {
+  static_assert(NT == 256 || NT == 512, "256 or 512 threads");
+  static constexpr int TPW = NB / 16 / (NT / 256);     // column tiles per wave
+  static_assert(TPW >= 1 && NB % 16 == 0, "NB must be a multiple of 16 * NT / 256");
+  __device__ static int row(int r) {
+    return 16 * ((threadIdx.x >> 6) & 3) + 4 * r + ((threadIdx.x & 63) >> 4);
+  }
+  __device__ static int col(int jj) {
+    return 16 * ((threadIdx.x >> 8) * TPW + jj) + (threadIdx.x & 15);
+  }
+};
+
+template <int NB, int K, int NT = kThreads, int PF = 3, typename FA, typename FB>
+__device__ __forceinline__ void mgemm(const FA &fa, const FB &fb,
+                                      d4 (&acc)[MOwn<NB, NT>::TPW]) {
+  constexpr int TPW = MOwn<NB, NT>::TPW;
+  constexpr int NS = K / 16;              // K-slices
+  constexpr int RING = PF + 1;            // A-operand slices held in registers
+  static_assert(K % 16 == 0 && NS % RING == 0, "K must be a multiple of 16 (PF + 1)");
+  const int l = threadIdx.x & 63;
+  const int m = 16 * ((threadIdx.x >> 6) & 3) + (l & 15);
+  const int n0 = 16 * ((threadIdx.x >> 8) * TPW) + (l & 15);
+  const int kq = 4 * (l >> 4);
+  double ra[RING][4];
+  auto load = [&](int s, double (&a)[4]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) a[q] = fa(m, 16 * s + kq + q);
+  };
+#pragma unroll
+  for (int jj = 0; jj < TPW; ++jj) acc[jj] = d4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int b = 0; b < PF; ++b) load(b, ra[b]);
+  // A's slice s is loaded PF slices before it is multiplied; B is read from
+  // LDS as it is used
+#pragma unroll 1
+  for (int s0 = 0; s0 < NS; s0 += RING) {
+#pragma unroll
+    for (int b = 0; b < RING; ++b) {
+      if (s0 + b + PF < NS) load(s0 + b + PF, ra[(b + PF) % RING]);
+      double rb[4][TPW];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int jj = 0; jj < TPW; ++jj) rb[q][jj] = fb(16 * (s0 + b) + kq + q, n0 + 16 * jj);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int jj = 0; jj < TPW; ++jj)
+          acc[jj] = __builtin_amdgcn_mfma_f64_16x16x4f64(ra[b][q], rb[q][jj], acc[jj], 0, 0, 0);
+    }
+  }
+}
+
 // Sum over the 16 lanes that share a row group of gemm64 (lanes 16 g .. 16 g + 15).
 __device__ __forceinline__ double sum16(double x) {
   x += __shfl_xor(x, 1);

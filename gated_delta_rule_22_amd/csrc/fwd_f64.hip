@@ -302,17 +302,19 @@ __global__ __launch_bounds__(kIT) void f64_intra(
   }
 }
 
-// Serial pass over the chunks of one (sequence, head, kBV-column block).
+// Serial pass over the chunks of one (sequence, head, kBV-column block).  The
+// products run on the fp64 matrix cores with their right operands (S, U) in
+// LDS; three barriers per chunk order the phases.
 template <int DK, int DV>
 __global__ __launch_bounds__(kThreads) void f64_inter(
     const float *__restrict__ S0, int H, int N, SeqTable tab, const double *__restrict__ records,
     size_t rec_doubles, void *__restrict__ o, float *__restrict__ S_T, int o_bf16,
     double *__restrict__ S_chunks, double *__restrict__ U_chunks) {
   using R = Rec<DK, DV>;
-  constexpr int NJ = kBV / 16;
+  using Own = MOwn<kBV>;
+  constexpr int TPW = Own::TPW;
   __shared__ double s_S[DK * kBV];
   __shared__ double s_U[C * kBV];
-  __shared__ double s_st[stage_doubles(kBV)];
 
   constexpr int NV = DV / kBV;
   const int jb = blockIdx.x % NV, rh = blockIdx.x / NV, t = threadIdx.x;
@@ -320,8 +322,6 @@ __global__ __launch_bounds__(kThreads) void f64_inter(
   const int len = tab.seq_len[n], start = tab.seq_start[n];
   const int nch = (len + C - 1) / C;
   const size_t sbase = ((size_t)n * H + h) * DK * DV + (size_t)jb * kBV;
-  const int rgp = t >> 4, cl = t & 15;
-  double *sA = s_st, *sB = s_st + kStageA;
 
   for (int p = t; p < DK * kBV; p += kThreads) {
     const int c = p / kBV, j = p % kBV;
@@ -338,62 +338,59 @@ __global__ __launch_bounds__(kThreads) void f64_inter(
         S_chunks[ch * DK * DV + (size_t)(p / kBV) * DV + jb * kBV + p % kBV] = s_S[p];
     // U = Ubar - W S
     {
-      double acc[4][NJ];
-      gemm64<kBV, DK, false, false>(
-          sA, sB, [&](int m, int kk) { return rec[R::W + m * DK + kk]; },
-          [&](int kk, int nn) { return s_S[kk * kBV + nn]; }, acc);
+      d4 acc[TPW];
+      mgemm<kBV, DK>([&](int m, int kk) { return rec[R::W + m * DK + kk]; },
+                     [&](int kk, int nn) { return s_S[kk * kBV + nn]; }, acc);
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+      for (int jj = 0; jj < TPW; ++jj)
 #pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) {
-          const int i = rgp * 4 + r, j = cl + 16 * jj;
-          const double u = rec[R::UB + i * DV + jb * kBV + j] - acc[r][jj];
+        for (int r = 0; r < 4; ++r) {
+          const int i = Own::row(r), j = Own::col(jj);
+          const double u = rec[R::UB + i * DV + jb * kBV + j] - acc[jj][r];
           s_U[i * kBV + j] = u;
           if (U_chunks) U_chunks[ch * C * DV + (size_t)i * DV + jb * kBV + j] = u;
         }
     }
+    __syncthreads();         // U complete
     // O = (gamma Q) S + P U, as one product over [S; U]
     if (o) {
-      double acc[4][NJ];
-      gemm64<kBV, DK + C, false, false>(
-          sA, sB,
+      d4 acc[TPW];
+      mgemm<kBV, DK + C>(
           [&](int m, int kk) {
             return kk < DK ? rec[R::QT + m * DK + kk] : rec[R::P + m * C + kk - DK];
           },
           [&](int kk, int nn) { return kk < DK ? s_S[kk * kBV + nn] : s_U[(kk - DK) * kBV + nn]; },
           acc);
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+      for (int jj = 0; jj < TPW; ++jj)
 #pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) {
-          const int i = rgp * 4 + r, j = cl + 16 * jj;
+        for (int r = 0; r < 4; ++r) {
+          const int i = Own::row(r), j = Own::col(jj);
           if (i >= nt) continue;
           const size_t oi = ((size_t)(start + lc * C + i) * H + h) * DV + jb * kBV + j;
           if (o_bf16)
-            static_cast<__hip_bfloat16 *>(o)[oi] = __float2bfloat16((float)acc[r][jj]);
+            static_cast<__hip_bfloat16 *>(o)[oi] = __float2bfloat16((float)acc[jj][r]);
           else
-            static_cast<float *>(o)[oi] = (float)acc[r][jj];
+            static_cast<float *>(o)[oi] = (float)acc[jj][r];
         }
-    } else {
-      __syncthreads();       // s_U complete before the state update reads it
+      __syncthreads();       // every read of S done before it is rewritten
     }
     // S' = Diag(gamma_n) S + K_hat^T U, 64 state rows at a time (in place: each
     // thread rewrites only its own elements, and the product reads U only)
 #pragma unroll
     for (int half = 0; half < DK / 64; ++half) {
-      double acc[4][NJ];
-      gemm64<kBV, C, true, false>(
-          sA, sB, [&](int m, int kk) { return rec[R::KH + kk * DK + half * 64 + m]; },
-          [&](int kk, int nn) { return s_U[kk * kBV + nn]; }, acc);
+      d4 acc[TPW];
+      mgemm<kBV, C>([&](int m, int kk) { return rec[R::KH + kk * DK + half * 64 + m]; },
+                    [&](int kk, int nn) { return s_U[kk * kBV + nn]; }, acc);
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+      for (int jj = 0; jj < TPW; ++jj)
 #pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) {
-          const int c = half * 64 + rgp * 4 + r, j = cl + 16 * jj;
-          s_S[c * kBV + j] = rec[R::GN + c] * s_S[c * kBV + j] + acc[r][jj];
+        for (int r = 0; r < 4; ++r) {
+          const int c = half * 64 + Own::row(r), j = Own::col(jj);
+          s_S[c * kBV + j] = rec[R::GN + c] * s_S[c * kBV + j] + acc[jj][r];
         }
     }
-    __syncthreads();
+    __syncthreads();         // S' complete, U free
   }
   if (S_T)
     for (int p = t; p < DK * kBV; p += kThreads) {
