@@ -132,29 +132,40 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_state(
     }
 }
 
-// Per-chunk scratch (doubles): dX [C][DV]; G, sign and the direct parts of
-// dq, dk and dGamma, each [C][DK].
+// Per-chunk scratch (doubles): dX [C][DV], then [C][DK] arrays of the
+// in-chunk gate factors, per (token i, channel c):
+//   G    log2|gamma_i|                GAM  gamma_i (signed)
+//   KHR  gamma_n / gamma_i            E, F the ratio split sign 2^(+-(G - Rm))
+// and AQ, AK: the pair terms R1, R2 of exact-path channels, later the
+// gradients with respect to the normalised q and k (q/k normalisation on).
+// Exact-path channels keep their pair terms C1, C2 in E and F.
 template <int DK, int DV>
 struct Scr {
   static constexpr size_t DX = 0;
   static constexpr size_t G = DX + C * DV;
-  static constexpr size_t SG = G + C * DK;
-  static constexpr size_t AQ = SG + C * DK;
+  static constexpr size_t GAM = G + C * DK;
+  static constexpr size_t KHR = GAM + C * DK;
+  static constexpr size_t E = KHR + C * DK;
+  static constexpr size_t F = E + C * DK;
+  static constexpr size_t AQ = F + C * DK;
   static constexpr size_t AK = AQ + C * DK;
-  static constexpr size_t AG = AK + C * DK;
-  static constexpr size_t SIZE = AG + C * DK;
+  static constexpr size_t SIZE = AK + C * DK;
 };
 
-constexpr int kCG = 16;                  // channels per group in the pair sums
-constexpr int kTri = C * (C + 1) / 2;    // packed lower triangle (incl. diagonal)
-__device__ __forceinline__ int tri(int i, int j) { return i * (i + 1) / 2 + j; }   // j <= i
+constexpr int kSM = C + 1;               // padded row of the C x C LDS matrices
 
 // --------------------------------------------------------------------------
-// f64_bwd_chunk: all per-chunk gradients of one (chunk, head).
-// The chunk-gradient kernel runs 512 threads (two waves per SIMD) over the
-// same LDS, so that each wave holds half the rows of every block product.
+// f64_bwd_chunk: all per-chunk gradients of one (chunk, head), 512 threads.
+// Every contraction runs on the fp64 matrix cores (mgemm) with its right
+// operand staged in LDS; each thread's share of a 64-row result follows MOwn.
+// The pair terms use the ratio split r_ij = e_i f_j about each channel's
+// midpoint, which turns them into four dense products:
+//   R1 = E o (dP (F o K)),      R2 = E o ((beta dA) (F o K)),
+//   C1 = F o ((beta dA)^T (E o K)),  C2 = F o (dP^T (E o Q))
+// (o: elementwise; K, Q the normalised keys and queries).  A channel whose
+// log-gate range is too wide for the split takes the ratios one pair at a time.
 constexpr int kBT = 512;
-constexpr int kRPT = 1024 / kBT;          // rows per thread in the block products
+constexpr int kCH = 32;                  // channels per pass of the direct and pair terms
 
 template <typename TIn, int DK, int DV>
 __global__ __launch_bounds__(kBT) void f64_bwd_chunk(
@@ -168,19 +179,27 @@ __global__ __launch_bounds__(kBT) void f64_bwd_chunk(
     int l2norm) {
   using R = Rec<DK, DV>;
   using X = Scr<DK, DV>;
-  constexpr int NBM = DV > 64 ? DV : 64;
-  constexpr int kStage = stage_doubles(NBM);
-  constexpr int kGroup = 8 * C * kCG > C * DK * 3 / 2 ? 8 * C * kCG : C * DK * 3 / 2;
-  __shared__ double s_P[kTri];            // dP (lower incl.), packed
-  __shared__ double s_DA[kTri];           // beta_i dA_ij (strictly lower; diagonal 0), packed
-  __shared__ double s_u[kStage > kGroup ? kStage : kGroup];  // staging | group operands
-  __shared__ double s_ag[C * kCG];
-  __shared__ double s_beta[C], s_db[C];
-  __shared__ double s_R[DK];
+  using OwnV = MOwn<DV, kBT>;              // C x DV results
+  using OwnC = MOwn<C, kBT>;               // C x C results
+  using Own = MOwn<kCH, kBT>;              // C x kCH results (a channel block)
+  constexpr int TV = OwnV::TPW, TC = OwnC::TPW, T64 = Own::TPW;
+  constexpr int SV = DV + 1, SC = kCH + 1;  // padded LDS rows
+  constexpr int kB0 = C * DK + C * DK / 2;
+  constexpr int kBA = C * SV > 3 * C * SC ? C * SV : 3 * C * SC;
+  constexpr int kPool = (kB0 > kBA + 2 * C * kSM ? kB0 : kBA + 2 * C * kSM);
+  // one LDS pool: the phase-0 gates, later the staged right operands (s_b)
+  // beside dP and beta dA as full C x C matrices, zero above the diagonal
+  __shared__ double s_pool[kPool];
+  double *s_b = s_pool;
+  double *s_P = s_pool + kBA;             // dP (lower incl.)
+  double *s_DA = s_P + C * kSM;           // beta_i dA_ij (strictly lower)
+  __shared__ double s_beta[C], s_dbp[2][C];
+  __shared__ double s_R[DK], s_red2[DK], s_dGn[kCH];
+  __shared__ double s_red[4][kCH];
   __shared__ int s_fb[DK];
-  __shared__ double s_red[(kBT / 64) * DK], s_red2[2 * DK], s_dGn[DK];
+  __shared__ int s_anyfb;
   __shared__ double s_fk[C], s_fq[C];     // key/query normalisation factors per token (1 if off)
-  __shared__ double s_kd[C], s_qd[C];     // khat . dkhat and qhat . dqhat per token
+  __shared__ double s_kd[2][C], s_qd[2][C];  // khat . dkhat and qhat . dqhat, per half-block
 
   const int cflat = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
   if (cflat >= tab.chunk_off[N]) return;
@@ -195,20 +214,24 @@ __global__ __launch_bounds__(kBT) void f64_bwd_chunk(
   const double *Uc = U_chunks + ch * C * DV;
   const double *dUc = dU_chunks + ch * C * DV;
   double *scr = scratch + ch * X::SIZE;
-  const int rgp = t >> 4, cl = t & 15, wave = t >> 6;
-  double *sA = s_u, *sB = s_u + kStageA;
+  const int wh = t >> 8;                  // which half of the column tiles this wave holds
+  const bool lead = (t & 15) == 0;        // lane that owns a row's sum over 16 lanes
 
   auto row = [&](int i) { return (size_t)(t0 + i) * H + h; };   // token-head row
   auto dO_at = [&](int m, int c) { return m < nt ? (double)dO[row(m) * DV + c] : 0.0; };
-  auto gam_at = [&](int m, int c) {
-    return scr[X::SG + m * DK + c] * exp2(scr[X::G + m * DK + c]);
+  auto khat = [&](int i, int c) {
+    return i < nt ? (double)to_f32(k[row(i) * DK + c]) * s_fk[i] : 0.0;
+  };
+  auto qhat = [&](int i, int c) {
+    return i < nt ? (double)to_f32(q[row(i) * DK + c]) * s_fq[i] : 0.0;
   };
 
   // ---- phase 0: in-chunk gate log-magnitudes and signs: log2|alpha| for
-  // every (token, channel) in parallel into LDS (the sign rides in the sign
-  // bit of a float copy of alpha), then the scans per channel.
-  double *s_l = s_u;                                   // [C][DK] log2|alpha|
-  float *s_sg = reinterpret_cast<float *>(s_u + C * DK); // [C][DK] alpha (sign only)
+  // every (token, channel) in parallel into LDS (the sign rides in a float
+  // copy of alpha), then the scans per channel.
+  double *s_l = s_b;                                    // [C][DK] log2|alpha|
+  float *s_sg = reinterpret_cast<float *>(s_b + C * DK);  // [C][DK] alpha (sign only)
+  if (t == 0) s_anyfb = 0;
 #pragma unroll 4
   for (int p = t; p < C * DK; p += kBT) {
     const float a = p / DK < nt ? g[row(p / DK) * DK + p % DK] : 1.f;
@@ -217,6 +240,7 @@ __global__ __launch_bounds__(kBT) void f64_bwd_chunk(
   }
   __syncthreads();
   if (t < DK) {
+    // in place: s_l becomes the running G, s_sg the sign of gamma
     double G = 0.0, gmax = 0.0, gmin = 0.0;
     bool par = false;
 #pragma unroll 8
@@ -226,331 +250,382 @@ __global__ __launch_bounds__(kBT) void f64_bwd_chunk(
       par ^= (signed_gates && a < 0.f);   // KDA mode: signs ignored
       gmax = fmax(gmax, G);
       gmin = fmin(gmin, G);
-      scr[X::G + i * DK + t] = G;
-      scr[X::SG + i * DK + t] = par ? -1.0 : 1.0;
+      s_l[i * DK + t] = G;
+      s_sg[i * DK + t] = par ? -1.f : 1.f;
     }
-    // The pair sums form r_ij = e_i f_j with e = sign 2^(G - Rm), f = sign 2^(Rm - G)
-    // about the midpoint Rm of the channel's range; beyond +-1000 binary orders
-    // that product could leave fp64's range, and the channel takes exp2 per pair.
+    // r_ij = e_i f_j with e = sign 2^(G - Rm), f = sign 2^(Rm - G) about the
+    // midpoint Rm of the channel's range; beyond +-1000 binary orders that
+    // product could leave fp64's range, and the channel takes exp2 per pair.
     s_R[t] = 0.5 * (gmax + gmin);
     s_fb[t] = (gmax - gmin) > 2000.0;
+    if (gmax - gmin > 2000.0) s_anyfb = 1;
   }
   if (t < C) {
     s_beta[t] = t < nt ? (double)beta[row(t)] : 0.0;
-    s_db[t] = 0.0;
-    s_kd[t] = 0.0;
-    s_qd[t] = 0.0;
+    s_dbp[0][t] = s_dbp[1][t] = 0.0;
+    s_kd[0][t] = s_kd[1][t] = 0.0;
+    s_qd[0][t] = s_qd[1][t] = 0.0;
   }
-  // optional q/k normalisation factors (sum x^2 + 1e-6)^(-1/2): four threads per
-  // token, 32 channels each
+  // optional q/k normalisation factors (sum x^2 + 1e-6)^(-1/2): eight threads
+  // per token
   {
-    const int i = t >> 2, part = t & 3;
+    const int i = t >> 3, part = t & 7;
     double sk = 0.0, sq = 0.0;
     if (l2norm && i < nt) {
-#pragma unroll 8
-      for (int c = part * (DK / 4); c < (part + 1) * (DK / 4); ++c) {
+#pragma unroll 4
+      for (int c = part * (DK / 8); c < (part + 1) * (DK / 8); ++c) {
         const double kk = to_f32(k[row(i) * DK + c]), qq = to_f32(q[row(i) * DK + c]);
         sk += kk * kk;
         sq += qq * qq;
       }
     }
-    sk += __shfl_xor(sk, 1);
-    sk += __shfl_xor(sk, 2);
-    sq += __shfl_xor(sq, 1);
-    sq += __shfl_xor(sq, 2);
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) {
+      sk += __shfl_xor(sk, o);
+      sq += __shfl_xor(sq, o);
+    }
     if (part == 0 && i < C) {
       s_fk[i] = (l2norm && i < nt) ? 1.0 / sqrt(sk + 1e-6) : 1.0;
       s_fq[i] = (l2norm && i < nt) ? 1.0 / sqrt(sq + 1e-6) : 1.0;
     }
   }
+  __syncthreads();
+  // the gate factors of every (token, channel), once
+#pragma unroll 2
+  for (int p = t; p < C * DK; p += kBT) {
+    const int c = p % DK;
+    const double G = s_l[p], sg = s_sg[p];
+    const double Gn = s_l[(C - 1) * DK + c], sn = s_sg[(C - 1) * DK + c];
+    scr[X::G + p] = G;
+    scr[X::GAM + p] = sg * exp2(G);
+    scr[X::KHR + p] = sg * sn * exp2(Gn - G);
+    scr[X::E + p] = s_fb[c] ? 0.0 : sg * exp2(G - s_R[c]);
+    scr[X::F + p] = s_fb[c] ? 0.0 : sg * exp2(s_R[c] - G);
+  }
+  // sum_j dS'[c][j] S[c][j] per channel: four threads per channel
+  {
+    const int c = t >> 2, part = t & 3;
+    double s = 0.0;
+    if (c < DK) {
+#pragma unroll 8
+      for (int j = part * (DV / 4); j < (part + 1) * (DV / 4); ++j)
+        s += dSe[c * DV + j] * Sc[c * DV + j];
+    }
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    if (part == 0 && c < DK) s_red2[c] = s;
+  }
   __threadfence_block();   // scratch is read back by this workgroup only
   __syncthreads();
 
+  // row sums over a wave's 16 lanes, kept per half-block so that every
+  // (half, row) slot has a single writer: deterministic order
+  auto add_row = [&](double (&dst)[2][C], int i, double part) {
+    part = sum16(part);
+    if (lead) dst[wh][i] += part;
+  };
+
   // ---- phase 1: dX = T^T dU; dV = Diag(beta) dX; dbeta += dX_i . V_i
+  for (int p = t; p < C * DV; p += kBT) s_b[(p / DV) * SV + p % DV] = dUc[p];
+  __syncthreads();
   {
-    double acc[kRPT][DV / 16];
-    gemm64<DV, C, true, false, kBT>(
-        sA, sB, [&](int m, int kk) { return rec[R::TI + kk * C + m]; },
-        [&](int kk, int nn) { return dUc[kk * DV + nn]; }, acc);
+    d4 acc[TV];
+    mgemm<DV, C, kBT>([&](int m, int kk) { return rec[R::TI + kk * C + m]; },
+                      [&](int kk, int nn) { return s_b[kk * SV + nn]; }, acc);
 #pragma unroll
-    for (int r = 0; r < kRPT; ++r) {
-      const int m = rgp * kRPT + r;
+    for (int r = 0; r < 4; ++r) {
+      const int i = OwnV::row(r);
       double part = 0.0;
 #pragma unroll
-      for (int jj = 0; jj < DV / 16; ++jj) {
-        const int nn = cl + 16 * jj;
-        scr[X::DX + m * DV + nn] = acc[r][jj];
-        if (m < nt) {
-          dv[row(m) * DV + nn] = (float)(s_beta[m] * acc[r][jj]);
-          part += acc[r][jj] * (double)to_f32(v[row(m) * DV + nn]);
+      for (int jj = 0; jj < TV; ++jj) {
+        const int j = OwnV::col(jj);
+        const double x = acc[jj][r];
+        scr[X::DX + i * DV + j] = x;
+        if (i < nt) {
+          dv[row(i) * DV + j] = (float)(s_beta[i] * x);
+          part += x * (double)to_f32(v[row(i) * DV + j]);
         }
       }
-      part = sum16(part);
-      if (cl == 0) s_db[m] += part;
+      add_row(s_dbp, i, part);
     }
   }
-  __threadfence_block();   // scratch is read back by this workgroup only
+  __threadfence_block();
   __syncthreads();
 
   // ---- phase 2: dP = tril(dO U^T) and beta_i dA_ij, dA = -strict_tril(dX U^T)
+  for (int p = t; p < C * DV; p += kBT) s_b[(p / DV) * SV + p % DV] = Uc[p];
+  __syncthreads();
   {
-    double acc[kRPT][4];
-    gemm64<64, DV, false, true, kBT>(
-        sA, sB, dO_at, [&](int kk, int nn) { return Uc[nn * DV + kk]; }, acc);
+    auto ut = [&](int kk, int nn) { return s_b[nn * SV + kk]; };   // U^T
+    d4 acc[TC];
+    mgemm<64, DV, kBT>(dO_at, ut, acc);
 #pragma unroll
-    for (int r = 0; r < kRPT; ++r)
+    for (int jj = 0; jj < TC; ++jj)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int m = rgp * kRPT + r, j = cl + 16 * jj;
-        if (j <= m) s_P[tri(m, j)] = acc[r][jj];
+      for (int r = 0; r < 4; ++r) {
+        const int i = OwnC::row(r), j = OwnC::col(jj);
+        s_P[i * kSM + j] = j <= i ? acc[jj][r] : 0.0;
       }
-    gemm64<64, DV, false, true, kBT>(
-        sA, sB, [&](int m, int kk) { return scr[X::DX + m * DV + kk]; },
-        [&](int kk, int nn) { return Uc[nn * DV + kk]; }, acc);
+    mgemm<64, DV, kBT>([&](int m, int kk) { return scr[X::DX + m * DV + kk]; }, ut, acc);
 #pragma unroll
-    for (int r = 0; r < kRPT; ++r) {
-      const int m = rgp * kRPT + r;
+    for (int r = 0; r < 4; ++r) {
+      const int i = OwnC::row(r);
       double part = 0.0;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int j = cl + 16 * jj;
-        const double dA = j < m ? -acc[r][jj] : 0.0;
-        if (j <= m) s_DA[tri(m, j)] = s_beta[m] * dA;
-        part += rec[R::AH + m * C + j] * dA;
+      for (int jj = 0; jj < TC; ++jj) {
+        const int j = OwnC::col(jj);
+        const double dA = j < i ? -acc[jj][r] : 0.0;
+        s_DA[i * kSM + j] = s_beta[i] * dA;
+        part += rec[R::AH + i * C + j] * dA;
       }
-      part = sum16(part);
-      if (cl == 0) s_db[m] += part;
+      add_row(s_dbp, i, part);
     }
   }
+  __syncthreads();
 
-  // ---- phase 3: the direct parts, 64 channels at a time, kept in registers
-  // over the three products and stored once.
+  // ---- phases 3 and 4, kCH channels at a time.  The direct parts of dq, dk and
+  // dGamma stay in registers (same ownership) until the pair terms are added.
 #pragma unroll 1
-  for (int hf = 0; hf < DK / 64; ++hf) {
-    const int cb = hf * 64;
-    double aq[kRPT][4], ak[kRPT][4], ag[kRPT][4], gam[kRPT][4], acc[kRPT][4];
-    // dQT = dO S^T: dq = gamma dQT; dGamma = q gamma dQT
-    gemm64<64, DV, false, true, kBT>(
-        sA, sB, dO_at, [&](int kk, int nn) { return Sc[(cb + nn) * DV + kk]; }, acc);
+  for (int hf = 0; hf < DK / kCH; ++hf) {
+    const int cb = hf * kCH;
+    // this thread's first row and column of the block, made opaque to the
+    // optimiser in every pass (an empty asm statement) so that no per-element
+    // address is hoisted out of the loop and held in registers across it
+    int r0 = Own::row(0), c0 = Own::col(0);
+    asm volatile("" : "+v"(r0), "+v"(c0));
+    auto orow = [&](int r) { return r0 + 4 * r; };
+    auto ocol = [&](int jj) { return c0 + 16 * jj; };
+    double aq[T64][4], ak[T64][4], ag[T64][4];
+    d4 acc[T64];
+    // dQT = dO S^T: dq = gamma dQT; dGamma = q gamma dQT.  M5 = dX S^T:
+    // d(gamma K) = -Diag(beta) M5.
+    for (int p = t; p < kCH * DV; p += kBT) s_b[(p / DV) * SV + p % DV] = Sc[cb * DV + p];
+    __syncthreads();
+    {
+      auto st = [&](int kk, int nn) { return s_b[nn * SV + kk]; };   // S^T (this half)
+      double gam[T64][4];
+      mgemm<kCH, DV, kBT>(dO_at, st, acc);
 #pragma unroll
-    for (int r = 0; r < kRPT; ++r)
+      for (int jj = 0; jj < T64; ++jj)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int m = rgp * kRPT + r, c = cb + cl + 16 * jj;
-        gam[r][jj] = gam_at(m, c);
-        aq[r][jj] = gam[r][jj] * acc[r][jj];
-        ag[r][jj] = rec[R::QT + m * DK + c] * acc[r][jj];
+        for (int r = 0; r < 4; ++r) {
+          const int i = orow(r), c = cb + ocol(jj);
+          gam[jj][r] = scr[X::GAM + i * DK + c];
+          aq[jj][r] = gam[jj][r] * acc[jj][r];
+          ag[jj][r] = rec[R::QT + i * DK + c] * acc[jj][r];
+        }
+      mgemm<kCH, DV, kBT>([&](int m, int kk) { return scr[X::DX + m * DV + kk]; }, st, acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = orow(r);
+        double part = 0.0;
+#pragma unroll
+        for (int jj = 0; jj < T64; ++jj) {
+          const int c = cb + ocol(jj);
+          const double gk = rec[R::GK + i * DK + c];
+          ak[jj][r] = -s_beta[i] * gam[jj][r] * acc[jj][r];
+          ag[jj][r] -= s_beta[i] * gk * acc[jj][r];
+          part -= gk * acc[jj][r];
+        }
+        add_row(s_dbp, i, part);
       }
-    // M5 = dX S^T: d(gamma K) = -Diag(beta) M5
-    gemm64<64, DV, false, true, kBT>(
-        sA, sB, [&](int m, int kk) { return scr[X::DX + m * DV + kk]; },
-        [&](int kk, int nn) { return Sc[(cb + nn) * DV + kk]; }, acc);
-#pragma unroll
-    for (int r = 0; r < kRPT; ++r) {
-      const int m = rgp * kRPT + r;
-      double part = 0.0;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int c = cb + cl + 16 * jj;
-        const double gk = rec[R::GK + m * DK + c];
-        ak[r][jj] = -s_beta[m] * gam[r][jj] * acc[r][jj];
-        ag[r][jj] -= s_beta[m] * gk * acc[r][jj];
-        part -= gk * acc[r][jj];
-      }
-      part = sum16(part);
-      if (cl == 0) s_db[m] += part;
     }
+    __syncthreads();
     // dKH = U dS'^T: dk += (gamma_n / gamma) dKH; dGamma_i -= k (gamma_n/gamma) dKH,
     // and the same amount, summed over i, goes to dGamma_n.
-    gemm64<64, DV, false, true, kBT>(
-        sA, sB, [&](int m, int kk) { return Uc[m * DV + kk]; },
-        [&](int kk, int nn) { return dSe[(cb + nn) * DV + kk]; }, acc);
+    for (int p = t; p < kCH * DV; p += kBT) s_b[(p / DV) * SV + p % DV] = dSe[cb * DV + p];
+    __syncthreads();
+    mgemm<kCH, DV, kBT>([&](int m, int kk) { return Uc[m * DV + kk]; },
+                       [&](int kk, int nn) { return s_b[nn * SV + kk]; }, acc);
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int c = cb + cl + 16 * jj;
-      const double Gn = scr[X::G + (C - 1) * DK + c], sn = scr[X::SG + (C - 1) * DK + c];
+    for (int jj = 0; jj < T64; ++jj) {
+      const int cl = ocol(jj), c = cb + cl;
       double col = 0.0;
 #pragma unroll
-      for (int r = 0; r < kRPT; ++r) {
-        const int m = rgp * kRPT + r;
-        const double khr = scr[X::SG + m * DK + c] * sn * exp2(Gn - scr[X::G + m * DK + c]);
-        const double term = rec[R::KH + m * DK + c] * acc[r][jj];
-        ak[r][jj] += khr * acc[r][jj];
-        ag[r][jj] -= term;
+      for (int r = 0; r < 4; ++r) {
+        const int i = orow(r);
+        const double khr = scr[X::KHR + i * DK + c];
+        const double term = rec[R::KH + i * DK + c] * acc[jj][r];
+        ak[jj][r] += khr * acc[jj][r];
+        ag[jj][r] -= term;
         col += term;
       }
       col += __shfl_xor(col, 16);
       col += __shfl_xor(col, 32);
-      if ((t & 63) < 16) s_red[wave * DK + c] = col;
+      if ((t & 63) < 16) s_red[(t >> 6) & 3][cl] = col;
     }
-#pragma unroll
-    for (int r = 0; r < kRPT; ++r)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int m = rgp * kRPT + r, c = cb + cl + 16 * jj;
-        scr[X::AQ + m * DK + c] = aq[r][jj];
-        scr[X::AK + m * DK + c] = ak[r][jj];
-        scr[X::AG + m * DK + c] = ag[r][jj];
-      }
-  }
-  // gamma_n sum_j dS'[c][j] S[c][j]: two threads per channel
-  for (int p = t; p < 2 * DK; p += kBT) {
-    const int c = p % DK, half = p / DK;
-    double part = 0.0;
-#pragma unroll 16
-    for (int j = half * (DV / 2); j < (half + 1) * (DV / 2); ++j)
-      part += dSe[c * DV + j] * Sc[c * DV + j];
-    s_red2[half * DK + c] = part;
-  }
-  __threadfence_block();   // scratch is read back by this workgroup only
-  __syncthreads();
-  for (int c = t; c < DK; c += kBT)
-  {
-    double col = 0.0;
-#pragma unroll
-    for (int w = 0; w < kBT / 64; ++w) col += s_red[w * DK + c];
-    s_dGn[c] = col + rec[R::GN + c] * (s_red2[c] + s_red2[DK + c]);
-  }
+    __syncthreads();
+    if (t < kCH)
+      s_dGn[t] = ((s_red[0][t] + s_red[1][t]) + (s_red[2][t] + s_red[3][t])) +
+                 rec[R::GN + cb + t] * s_red2[cb + t];
 
-  // ---- phase 4: pair sums per group of kCG channels, then the gate gradients
-  const int gcl = t % kCG, grw = t / kCG;          // channel in the group, row slot
-  constexpr int kRowSlots = kBT / kCG;
-  // this thread's gates, keys and queries of the next channel group, loaded
-  // while the current group is summed
-  constexpr int NG = C * kCG / kBT;
-  float pg[NG], pk[NG], pq[NG];
-  auto load_group = [&](int c0) {
-#pragma unroll
-    for (int u = 0; u < NG; ++u) {
-      const int p = t + u * kBT, i = p / kCG, cc = c0 + p % kCG;
-      pg[u] = i < nt ? g[row(i) * DK + cc] : 1.f;
-      pk[u] = i < nt ? to_f32(k[row(i) * DK + cc]) : 0.f;
-      pq[u] = i < nt ? to_f32(q[row(i) * DK + cc]) : 0.f;
+    // ---- phase 4: the right operands F o K, E o K, E o Q of this half
+    double *sFK = s_b, *sEK = s_b + C * SC, *sEQ = s_b + 2 * C * SC;
+    for (int p = t; p < C * kCH; p += kBT) {
+      const int i = p / kCH, cl = p % kCH, c = cb + cl;
+      const double e = scr[X::E + i * DK + c], f = scr[X::F + i * DK + c];
+      const double kh = khat(i, c), qh = qhat(i, c);
+      sFK[i * SC + cl] = f * kh;
+      sEK[i * SC + cl] = e * kh;
+      sEQ[i * SC + cl] = e * qh;
     }
-  };
-  load_group(0);
-  for (int c0 = 0; c0 < DK; c0 += kCG) {
-    const int c = c0 + gcl;
-    double *e = s_u, *f = s_u + C * kCG, *kk_ = s_u + 2 * C * kCG, *qq = s_u + 3 * C * kCG;
-    double *ra = s_u + 4 * C * kCG;       // 1 / alpha (floored magnitude)
-    double *saq = s_u + 5 * C * kCG, *sak = s_u + 6 * C * kCG, *sag = s_u + 7 * C * kCG;
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < NG; ++u) {
-      const int p = t + u * kBT, i = p / kCG, cc = c0 + p % kCG;
-      const double G = scr[X::G + i * DK + cc], sg = scr[X::SG + i * DK + cc];
-      {
-        const double floor_mag = exp2(kLog2Floor);
-        const double a = pg[u];
-        ra[p] = 1.0 / (fabs(a) < floor_mag ? (a < 0.0 ? -floor_mag : floor_mag) : a);
-      }
-      if (s_fb[cc]) {
-        e[p] = G;
-        f[p] = sg;
-      } else {
-        e[p] = sg * exp2(G - s_R[cc]);
-        f[p] = sg * exp2(s_R[cc] - G);
-      }
-      kk_[p] = pk[u] * s_fk[i];
-      qq[p] = pq[u] * s_fq[i];
-      saq[p] = scr[X::AQ + i * DK + cc];
-      sak[p] = scr[X::AK + i * DK + cc];
-      sag[p] = scr[X::AG + i * DK + cc];
-    }
-    __syncthreads();
-    if (c0 + kCG < DK) load_group(c0 + kCG);
-    {
-      const bool fb = s_fb[c];
-#pragma unroll 1
-      for (int u = 0; u < C / kRowSlots; ++u) {
-        const int i = grw + kRowSlots * u;
+    if (s_anyfb) {
+      // channels too wide for the split: the four pair terms with exp2 per pair
+      // (the sign of gamma is that of GAM, which keeps it when it underflows)
+      __syncthreads();                // E and F of this half read by the staging
+      auto sgn = [&](int i, int c) { return copysign(1.0, scr[X::GAM + i * DK + c]); };
+      for (int cg = 0; cg < kCH; cg += kBT / C) {
+        const int c = cb + cg + t / C, i = t % C;
+        if (!s_fb[c]) continue;
+        const double Gi = scr[X::G + i * DK + c], si = sgn(i, c);
         double R1 = 0.0, R2 = 0.0, C1 = 0.0, C2 = 0.0;
-        const double ei = e[i * kCG + gcl], fi = f[i * kCG + gcl];
-        const double *Pi = s_P + tri(i, 0), *DAi = s_DA + tri(i, 0);
-        // row i: sum over j <= i of dP_ij k_j r_ij and (beta dA)_ij k_j r_ij;
-        // column i: sum over m >= i of (beta dA)_mi k_m r_mi and dP_mi q_m r_mi.
-        if (!fb) {
-          // four independent partial sums per quantity keep the FMA chains short
-          double r1[4] = {0.0, 0.0, 0.0, 0.0}, r2[4] = {0.0, 0.0, 0.0, 0.0};
-          int j = 0;
-          for (; j + 3 <= i; j += 4) {
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-              const double kr = kk_[(j + w) * kCG + gcl] * (ei * f[(j + w) * kCG + gcl]);
-              r1[w] = fma(Pi[j + w], kr, r1[w]);
-              r2[w] = fma(DAi[j + w], kr, r2[w]);
-            }
-          }
-          for (; j <= i; ++j) {
-            const double kr = kk_[j * kCG + gcl] * (ei * f[j * kCG + gcl]);
-            r1[0] = fma(Pi[j], kr, r1[0]);
-            r2[0] = fma(DAi[j], kr, r2[0]);
-          }
-          R1 = (r1[0] + r1[1]) + (r1[2] + r1[3]);
-          R2 = (r2[0] + r2[1]) + (r2[2] + r2[3]);
-          double c1[4] = {0.0, 0.0, 0.0, 0.0}, c2[4] = {0.0, 0.0, 0.0, 0.0};
-          int m = i;
-          for (; m + 3 < C; m += 4) {
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-              const double r = e[(m + w) * kCG + gcl] * fi;
-              c1[w] = fma(s_DA[tri(m + w, i)], kk_[(m + w) * kCG + gcl] * r, c1[w]);
-              c2[w] = fma(s_P[tri(m + w, i)], qq[(m + w) * kCG + gcl] * r, c2[w]);
-            }
-          }
-          for (; m < C; ++m) {
-            const double r = e[m * kCG + gcl] * fi;
-            c1[0] = fma(s_DA[tri(m, i)], kk_[m * kCG + gcl] * r, c1[0]);
-            c2[0] = fma(s_P[tri(m, i)], qq[m * kCG + gcl] * r, c2[0]);
-          }
-          C1 = (c1[0] + c1[1]) + (c1[2] + c1[3]);
-          C2 = (c2[0] + c2[1]) + (c2[2] + c2[3]);
-        } else {                          // e holds G and f the sign
-          for (int j = 0; j <= i; ++j) {
-            const double r = fi * f[j * kCG + gcl] * exp2(ei - e[j * kCG + gcl]);
-            const double kr = kk_[j * kCG + gcl] * r;
-            R1 = fma(Pi[j], kr, R1);
-            R2 = fma(DAi[j], kr, R2);
-          }
-          for (int m = i; m < C; ++m) {
-            const double r = f[m * kCG + gcl] * fi * exp2(e[m * kCG + gcl] - ei);
-            C1 = fma(s_DA[tri(m, i)], kk_[m * kCG + gcl] * r, C1);
-            C2 = fma(s_P[tri(m, i)], qq[m * kCG + gcl] * r, C2);
-          }
+        for (int j = 0; j <= i; ++j) {
+          const double r = si * sgn(j, c) * exp2(Gi - scr[X::G + j * DK + c]);
+          const double kr = khat(j, c) * r;
+          R1 = fma(s_P[i * kSM + j], kr, R1);
+          R2 = fma(s_DA[i * kSM + j], kr, R2);
         }
-        const double ki = kk_[i * kCG + gcl], qi = qq[i * kCG + gcl];
-        const double gq = saq[i * kCG + gcl] + R1;
-        const double gk = sak[i * kCG + gcl] + R2 + C1 + C2;
-        double gG = sag[i * kCG + gcl] + qi * R1 + ki * (R2 - C1 - C2);
-        if (i == C - 1) gG += s_dGn[c];
-        s_ag[i * kCG + gcl] = gG;
-        if (l2norm) {
-          // gradients with respect to the normalised rows; the normalisation's
-          // Jacobian is applied once every channel is done
-          scr[X::AQ + i * DK + c] = gq;
-          scr[X::AK + i * DK + c] = gk;
-          const double dqd = sum16(qi * gq), dkd = sum16(ki * gk);
-          if (gcl == 0) {
-            s_qd[i] += dqd;
-            s_kd[i] += dkd;
-          }
-        } else if (i < nt) {
-          dq[row(i) * DK + c] = (float)gq;
-          dk[row(i) * DK + c] = (float)gk;
+        for (int m = i; m < C; ++m) {
+          const double r = si * sgn(m, c) * exp2(scr[X::G + m * DK + c] - Gi);
+          C1 = fma(s_DA[m * kSM + i], khat(m, c) * r, C1);
+          C2 = fma(s_P[m * kSM + i], qhat(m, c) * r, C2);
         }
+        scr[X::AQ + i * DK + c] = R1;
+        scr[X::AK + i * DK + c] = R2;
+        scr[X::E + i * DK + c] = C1;
+        scr[X::F + i * DK + c] = C2;
       }
+      __threadfence_block();
     }
     __syncthreads();
-    // dln|alpha_s| = sum_{i >= s} dGamma_i; dalpha = dln|alpha| / alpha
-    if (t < kCG) {
-      const int cc = c0 + t;
-      double acc2 = 0.0;
-#pragma unroll 8
-      for (int i = C - 1; i >= 0; --i) {
-        acc2 += s_ag[i * kCG + t];
-        if (i < nt) dg[row(i) * DK + cc] = (float)(acc2 * ra[i * kCG + t]);
+    {
+      // the split factor of each owned (token, channel): e for the R terms,
+      // then f = sign 2^(Rm - G) for the C terms (0 on exact-path channels).
+      // The left operands sit in LDS: one slice of prefetch is enough.
+      double ef[T64][4];
+      auto split = [&](size_t arr) {
+#pragma unroll
+        for (int jj = 0; jj < T64; ++jj)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = orow(r), c = cb + ocol(jj);
+            ef[jj][r] = s_fb[c] ? 0.0 : scr[arr + i * DK + c];
+          }
+      };
+      split(X::E);
+      // R1 = E o (dP (F o K)): into dq and dGamma (+ q R1); dq is then complete
+      mgemm<kCH, C, kBT, 1>([&](int m, int kk) { return s_P[m * kSM + kk]; },
+                           [&](int kk, int nn) { return sFK[kk * SC + nn]; }, acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = orow(r);
+        double dqd = 0.0;
+#pragma unroll
+        for (int jj = 0; jj < T64; ++jj) {
+          const int c = cb + ocol(jj);
+          double R1 = ef[jj][r] * acc[jj][r];
+          if (s_fb[c]) R1 = scr[X::AQ + i * DK + c];      // exact-path channel
+          const double gq = aq[jj][r] + R1, qh = qhat(i, c);
+          ag[jj][r] += qh * R1;
+          if (l2norm) {
+            // the gradient with respect to the normalised row; the
+            // normalisation's Jacobian is applied once every channel is done
+            scr[X::AQ + i * DK + c] = gq;
+            dqd += qh * gq;
+          } else if (i < nt) {
+            dq[row(i) * DK + c] = (float)gq;
+          }
+        }
+        if (l2norm) add_row(s_qd, i, dqd);
+      }
+      // R2 = E o ((beta dA) (F o K)): into dk and dGamma (+ k R2)
+      mgemm<kCH, C, kBT, 1>([&](int m, int kk) { return s_DA[m * kSM + kk]; },
+                           [&](int kk, int nn) { return sFK[kk * SC + nn]; }, acc);
+#pragma unroll
+      for (int jj = 0; jj < T64; ++jj)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = orow(r), c = cb + ocol(jj);
+          const double R2 = ef[jj][r] * acc[jj][r];
+          ak[jj][r] += R2;
+          ag[jj][r] += khat(i, c) * R2;
+        }
+      split(X::F);
+      // C1 = F o ((beta dA)^T (E o K)): into dk and dGamma (- k C1)
+      mgemm<kCH, C, kBT, 1>([&](int m, int kk) { return s_DA[kk * kSM + m]; },
+                           [&](int kk, int nn) { return sEK[kk * SC + nn]; }, acc);
+#pragma unroll
+      for (int jj = 0; jj < T64; ++jj)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = orow(r), c = cb + ocol(jj);
+          const double C1 = ef[jj][r] * acc[jj][r];
+          ak[jj][r] += C1;
+          ag[jj][r] -= khat(i, c) * C1;
+        }
+      // C2 = F o (dP^T (E o Q)): into dk and dGamma (- k C2)
+      mgemm<kCH, C, kBT, 1>([&](int m, int kk) { return s_P[kk * kSM + m]; },
+                           [&](int kk, int nn) { return sEQ[kk * SC + nn]; }, acc);
+      // exact-path channels, the last token's dGamma_n, and dk
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = orow(r);
+        double dkd = 0.0;
+#pragma unroll
+        for (int jj = 0; jj < T64; ++jj) {
+          const int cl = ocol(jj), c = cb + cl;
+          const double kh = khat(i, c);
+          const double C2 = ef[jj][r] * acc[jj][r];
+          ak[jj][r] += C2;
+          ag[jj][r] -= kh * C2;
+          if (s_fb[c]) {
+            const double R2 = scr[X::AK + i * DK + c];
+            const double C1 = scr[X::E + i * DK + c], C2x = scr[X::F + i * DK + c];
+            ak[jj][r] += R2 + C1 + C2x;
+            ag[jj][r] += kh * (R2 - C1 - C2x);
+          }
+          if (i == C - 1) ag[jj][r] += s_dGn[cl];
+          if (l2norm) {
+            scr[X::AK + i * DK + c] = ak[jj][r];
+            dkd += kh * ak[jj][r];
+          } else if (i < nt) {
+            dk[row(i) * DK + c] = (float)ak[jj][r];
+          }
+        }
+        if (l2norm) add_row(s_kd, i, dkd);
       }
     }
+    __syncthreads();                    // every read of the staged operands done
+    // dln|alpha_s| = sum_{i >= s} dGamma_i; dalpha = dln|alpha| / alpha.
+    // NSEG segments of C / NSEG tokens per channel, then the segment offsets.
+    constexpr int NSEG = kBT / kCH, LSEG = C / NSEG;
+    double *s_ag = s_b, *s_seg = s_b + C * SC;
+#pragma unroll
+    for (int jj = 0; jj < T64; ++jj)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s_ag[orow(r) * SC + ocol(jj)] = ag[jj][r];
+    __syncthreads();
+    {
+      const int cl = t % kCH, sgm = t / kCH;
+      double sum = 0.0;
+#pragma unroll
+      for (int i = LSEG * sgm; i < LSEG * sgm + LSEG; ++i) sum += s_ag[i * SC + cl];
+      s_seg[sgm * kCH + cl] = sum;
+      __syncthreads();
+      double acc2 = 0.0;
+      for (int s2 = NSEG - 1; s2 > sgm; --s2) acc2 += s_seg[s2 * kCH + cl];
+      const double floor_mag = exp2(kLog2Floor);
+#pragma unroll
+      for (int i = LSEG * sgm + LSEG - 1; i >= LSEG * sgm; --i) {
+        acc2 += s_ag[i * SC + cl];
+        if (i < nt) {
+          const double a = g[row(i) * DK + cb + cl];
+          const double am = fabs(a) < floor_mag ? (a < 0.0 ? -floor_mag : floor_mag) : a;
+          dg[row(i) * DK + cb + cl] = (float)(acc2 / am);
+        }
+      }
+    }
+    __syncthreads();                    // s_b free for the next block
   }
   __threadfence_block();   // scratch is read back by this workgroup only
   __syncthreads();
@@ -561,11 +636,12 @@ __global__ __launch_bounds__(kBT) void f64_bwd_chunk(
       const int i = p / DK, c = p % DK;
       const double qh = to_f32(q[row(i) * DK + c]) * s_fq[i];
       const double kh = to_f32(k[row(i) * DK + c]) * s_fk[i];
-      dq[row(i) * DK + c] = (float)(s_fq[i] * (scr[X::AQ + p] - qh * s_qd[i]));
-      dk[row(i) * DK + c] = (float)(s_fk[i] * (scr[X::AK + p] - kh * s_kd[i]));
+      const double qd = s_qd[0][i] + s_qd[1][i], kd = s_kd[0][i] + s_kd[1][i];
+      dq[row(i) * DK + c] = (float)(s_fq[i] * (scr[X::AQ + p] - qh * qd));
+      dk[row(i) * DK + c] = (float)(s_fk[i] * (scr[X::AK + p] - kh * kd));
     }
   }
-  if (t < nt) dbeta[row(t)] = (float)s_db[t];
+  if (t < nt) dbeta[row(t)] = (float)(s_dbp[0][t] + s_dbp[1][t]);
 }
 
 template <typename TIn, int DK, int DV>
@@ -592,7 +668,7 @@ hipError_t launch_bwd_shape(const void *q, const void *k, const void *v, const f
 }  // namespace
 
 size_t f64_bwd_scratch_bytes(int dk, int dv) {
-  return sizeof(double) * ((size_t)C * dv + 5 * (size_t)C * dk);
+  return sizeof(double) * ((size_t)C * dv + 7 * (size_t)C * dk);
 }
 
 hipError_t launch_bwd_f64(const void *q, const void *k, const void *v, const float *g,
