@@ -137,7 +137,8 @@ struct MOwn {
   }
 };
 
-template <int NB, int K, int NT = kThreads, int PF = 3, typename FA, typename FB>
+template <int NB, int K, int NT = kThreads, int PF = 3, bool ZERO = true, typename FA,
+          typename FB>
 __device__ __forceinline__ void mgemm(const FA &fa, const FB &fb,
                                       d4 (&acc)[MOwn<NB, NT>::TPW]) {
   constexpr int TPW = MOwn<NB, NT>::TPW;
@@ -153,8 +154,10 @@ __device__ __forceinline__ void mgemm(const FA &fa, const FB &fb,
 #pragma unroll
     for (int q = 0; q < 4; ++q) a[q] = fa(m, 16 * s + kq + q);
   };
+  if (ZERO) {                              // else accumulate onto acc
 #pragma unroll
-  for (int jj = 0; jj < TPW; ++jj) acc[jj] = d4{0.0, 0.0, 0.0, 0.0};
+    for (int jj = 0; jj < TPW; ++jj) acc[jj] = d4{0.0, 0.0, 0.0, 0.0};
+  }
 #pragma unroll
   for (int b = 0; b < PF; ++b) load(b, ra[b]);
   // A's slice s is loaded PF slices before it is multiplied; B is read from

@@ -39,7 +39,7 @@ namespace {
 
 using namespace f64;
 
-constexpr int kCG = 16;              // channels per group in the pair sums
+constexpr int kCB = 32;              // channels per block of the A and P products
 
 // The record kernel runs 512 threads (two waves per SIMD over one block's
 // LDS); each thread holds kIR rows of every 64-row tile.
@@ -53,7 +53,7 @@ __global__ __launch_bounds__(kIT) void f64_intra(
     double *__restrict__ records, size_t rec_doubles, int signed_gates, int l2norm) {
   using R = Rec<DK, DV>;
   constexpr int NBM = DK > DV ? DK : DV;
-  constexpr int kG = 4 * C * kCG > C * DK / 2 ? 4 * C * kCG : C * DK / 2;
+  constexpr int kG = 3 * C * (kCB + 1) > C * DK / 2 ? 3 * C * (kCB + 1) : C * DK / 2;
   constexpr int kU = stage_doubles(NBM) > kG ? stage_doubles(NBM) : kG;
   __shared__ double s_G[C * DK > C * (C + 1) ? C * DK : C * (C + 1)];  // G, later T
   __shared__ uint8_t s_par[C * DK];
@@ -62,9 +62,11 @@ __global__ __launch_bounds__(kIT) void f64_intra(
   __shared__ double s_beta[C], s_fk[C], s_fq[C];
   __shared__ double s_R[DK];
   __shared__ int s_fb[DK];
+  __shared__ int s_anyfb;
 
   const int cflat = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
   if (cflat >= tab.chunk_off[N]) return;
+  if (t == 0) s_anyfb = 0;
   const int n = find_seq(tab.chunk_off, N, cflat);
   const int lc = cflat - tab.chunk_off[n];
   const int t0 = tab.seq_start[n] + lc * C;
@@ -100,6 +102,7 @@ __global__ __launch_bounds__(kIT) void f64_intra(
     // that product could leave fp64's range and the channel takes exp2 per pair.
     s_R[t] = 0.5 * (gmax + gmin);
     s_fb[t] = (gmax - gmin) > 2000.0;
+    if (gmax - gmin > 2000.0) s_anyfb = 1;
   }
   // ---- optional L2 normalisation of q and k per token: (sum x^2 + 1e-6)^(-1/2)
   if (t < C) {
@@ -120,101 +123,80 @@ __global__ __launch_bounds__(kIT) void f64_intra(
   }
   __syncthreads();
 
-  // ---- A (strictly lower) and P (lower incl. diagonal), channel group by
-  // channel group.  Thread t owns pairs (i, j) = (t/16 + 32 ii, t%16 + 16 jj).
+  // ---- A (strictly lower) and P (lower incl. diagonal) on the fp64 matrix
+  // cores.  With the ratio split r_ij = e_i f_j about each channel's midpoint,
+  // A/beta = (K o E)(K o F)^T and P = (Q o E)(K o F)^T (K, Q the normalised
+  // keys and queries), summed over blocks of kCB channels staged in LDS.
+  // Channels too wide for the split are left out of the products (e = f = 0)
+  // and added pair by pair afterwards.
   {
-    const int bi = t >> 4, bj = t & 15;
-    double accA[kIR][4], accP[kIR][4];
-#pragma unroll
-    for (int ii = 0; ii < kIR; ++ii)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) accA[ii][jj] = accP[ii][jj] = 0.0;
-    double *e = s_u, *f = s_u + C * kCG, *kg = s_u + 2 * C * kCG, *qg = s_u + 3 * C * kCG;
-    // this thread's keys and queries of the next channel group, loaded while
-    // the current group is summed
-    constexpr int NG = C * kCG / kIT;
+    using Own = MOwn<C, kIT>;
+    constexpr int TP = Own::TPW, SB = kCB + 1;
+    double *sKE = s_u, *sQE = s_u + C * SB, *sKF = s_u + 2 * C * SB;
+    constexpr int NG = C * kCB / kIT;
     float rk[NG], rq[NG];
-    auto load_group = [&](int c0) {
+    auto load_block = [&](int c0) {
 #pragma unroll
       for (int u = 0; u < NG; ++u) {
-        const int p = t + u * kIT, i = p / kCG, c = c0 + p % kCG;
+        const int p = t + u * kIT, i = p / kCB, c = c0 + p % kCB;
         rk[u] = i < nt ? to_f32(k[row(i) * DK + c]) : 0.f;
         rq[u] = i < nt ? to_f32(q[row(i) * DK + c]) : 0.f;
       }
     };
-    load_group(0);
-    for (int c0 = 0; c0 < DK; c0 += kCG) {
-      __syncthreads();
-      // group operands, channel-major: x[cl * C + i]
+    d4 accA[TP], accP[TP];
+#pragma unroll
+    for (int jj = 0; jj < TP; ++jj) accA[jj] = accP[jj] = d4{0.0, 0.0, 0.0, 0.0};
+    load_block(0);
+#pragma unroll 1
+    for (int c0 = 0; c0 < DK; c0 += kCB) {
+      __syncthreads();                  // the previous block's products are done
 #pragma unroll
       for (int u = 0; u < NG; ++u) {
-        const int p = t + u * kIT, i = p / kCG, cl = p % kCG, c = c0 + cl;
-        const double G = s_G[i * DK + c], sg = s_par[i * DK + c] ? -1.0 : 1.0;
-        if (s_fb[c]) {
-          e[cl * C + i] = G;
-          f[cl * C + i] = sg;
-        } else {
-          e[cl * C + i] = sg * exp2(G - s_R[c]);
-          f[cl * C + i] = sg * exp2(s_R[c] - G);
+        const int p = t + u * kIT, i = p / kCB, cl = p % kCB, c = c0 + cl;
+        double e = 0.0, f = 0.0;
+        if (!s_fb[c]) {
+          const double G = s_G[i * DK + c], sg = s_par[i * DK + c] ? -1.0 : 1.0;
+          e = sg * exp2(G - s_R[c]);
+          f = sg * exp2(s_R[c] - G);
         }
-        kg[cl * C + i] = (double)rk[u] * s_fk[i];
-        qg[cl * C + i] = (double)rq[u] * s_fq[i];
+        const double kh = (double)rk[u] * s_fk[i], qh = (double)rq[u] * s_fq[i];
+        sKE[i * SB + cl] = kh * e;
+        sQE[i * SB + cl] = qh * e;
+        sKF[i * SB + cl] = kh * f;
       }
       __syncthreads();
-      if (c0 + kCG < DK) load_group(c0 + kCG);
-#pragma unroll 2
-      for (int cl = 0; cl < kCG; ++cl) {
-        const double *ec = e + cl * C, *fc = f + cl * C, *kc = kg + cl * C, *qc = qg + cl * C;
-        double ei[kIR], ki[kIR], qi[kIR], fj[4], kj[4];
+      if (c0 + kCB < DK) load_block(c0 + kCB);
+      auto kf = [&](int kk, int nn) { return sKF[nn * SB + kk]; };   // (K o F)^T
+      mgemm<C, kCB, kIT, 1, false>([&](int m, int kk) { return sKE[m * SB + kk]; }, kf, accA);
+      mgemm<C, kCB, kIT, 1, false>([&](int m, int kk) { return sQE[m * SB + kk]; }, kf, accP);
+    }
+    if (s_anyfb) {
+      // r_ij = sign_i sign_j 2^(G_i - G_j) one pair at a time (j <= i)
+      for (int c = 0; c < DK; ++c) {
+        if (!s_fb[c]) continue;         // uniform across the block
 #pragma unroll
-        for (int u = 0; u < kIR; ++u) {
-          ei[u] = ec[bi + 32 * u];
-          ki[u] = kc[bi + 32 * u];
-          qi[u] = qc[bi + 32 * u];
-        }
+        for (int jj = 0; jj < TP; ++jj)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          fj[u] = fc[bj + 16 * u];
-          kj[u] = kc[bj + 16 * u];
-        }
-        if (!s_fb[c0 + cl]) {        // uniform across the block
-#pragma unroll
-          for (int ii = 0; ii < kIR; ++ii)
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-              const double kr = ei[ii] * fj[jj] * kj[jj];
-              accA[ii][jj] = fma(ki[ii], kr, accA[ii][jj]);
-              accP[ii][jj] = fma(qi[ii], kr, accP[ii][jj]);
-            }
-        } else {                     // e holds G and f the sign
-          double ej[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) ej[u] = ec[bj + 16 * u];
-          double fi[kIR];
-#pragma unroll
-          for (int u = 0; u < kIR; ++u) fi[u] = fc[bi + 32 * u];
-#pragma unroll
-          for (int ii = 0; ii < kIR; ++ii)
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-              const int i = bi + 32 * ii, j = bj + 16 * jj;
-              const double r = j <= i ? fi[ii] * fj[jj] * exp2(ei[ii] - ej[jj]) : 0.0;
-              const double kr = r * kj[jj];
-              accA[ii][jj] = fma(ki[ii], kr, accA[ii][jj]);
-              accP[ii][jj] = fma(qi[ii], kr, accP[ii][jj]);
-            }
-        }
+          for (int r = 0; r < 4; ++r) {
+            const int i = Own::row(r), j = Own::col(jj);
+            if (j > i || i >= nt) continue;
+            const double sgn = (s_par[i * DK + c] ^ s_par[j * DK + c]) ? -1.0 : 1.0;
+            const double rr = sgn * exp2(s_G[i * DK + c] - s_G[j * DK + c]);
+            const double kj = (double)to_f32(k[row(j) * DK + c]) * s_fk[j] * rr;
+            accA[jj][r] += (double)to_f32(k[row(i) * DK + c]) * s_fk[i] * kj;
+            accP[jj][r] += (double)to_f32(q[row(i) * DK + c]) * s_fq[i] * kj;
+          }
       }
     }
 #pragma unroll
-    for (int ii = 0; ii < kIR; ++ii)
+    for (int jj = 0; jj < TP; ++jj)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int i = bi + 32 * ii, j = bj + 16 * jj;
-        const double a = j < i ? accA[ii][jj] : 0.0;
+      for (int r = 0; r < 4; ++r) {
+        const int i = Own::row(r), j = Own::col(jj);
+        const double a = j < i ? accA[jj][r] : 0.0;
         s_A[i * (C + 1) + j] = s_beta[i] * a;
         rec[R::AH + i * C + j] = a;
-        rec[R::P + i * C + j] = j <= i ? accP[ii][jj] : 0.0;
+        rec[R::P + i * C + j] = j <= i ? accP[jj][r] : 0.0;
       }
   }
 
