@@ -256,31 +256,38 @@ __global__ __launch_bounds__(kIT) void f64_intra(
     }
   }
 
-  // ---- T, W = T Diag(beta) (gamma*K), Ubar = T Diag(beta) V.
+  // ---- T, W = T Diag(beta) (gamma*K), Ubar = T Diag(beta) V, formed
+  // transposed on the fp64 matrix cores 64 columns at a time:
+  // W^T = (gamma*K)^T (T Diag(beta))^T and Ubar^T = V^T (T Diag(beta))^T, the
+  // left operand streamed from global memory, the right one read from T in LDS.
   for (int p = t; p < C * C; p += kIT) rec[R::TI + p] = s_T[(p / C) * (C + 1) + p % C];
-  double *sA = s_u, *sB = s_u + kStageA;
-  auto tb = [&](int m, int kk) { return s_T[m * (C + 1) + kk] * s_beta[kk]; };
   {
-    double acc[kIR][DK / 16];
-    gemm64<DK, C, false, false, kIT>(
-        sA, sB, tb, [&](int kk, int nn) { return rec[R::GK + kk * DK + nn]; }, acc);
+    using Own = MOwn<C, kIT>;
+    constexpr int TP = Own::TPW;
+    auto tbt = [&](int kk, int nn) { return s_T[nn * (C + 1) + kk] * s_beta[kk]; };
+    d4 acc[TP];
+#pragma unroll 1
+    for (int cb = 0; cb < DK; cb += 64) {
+      mgemm<C, C, kIT>([&](int m, int kk) { return rec[R::GK + kk * DK + cb + m]; }, tbt, acc);
 #pragma unroll
-    for (int r = 0; r < kIR; ++r)
+      for (int jj = 0; jj < TP; ++jj)
 #pragma unroll
-      for (int jj = 0; jj < DK / 16; ++jj)
-        rec[R::W + ((t >> 4) * kIR + r) * DK + (t & 15) + 16 * jj] = acc[r][jj];
-  }
-  {
-    double acc[kIR][DV / 16];
-    gemm64<DV, C, false, false, kIT>(
-        sA, sB, tb,
-        [&](int kk, int nn) { return kk < nt ? (double)to_f32(v[row(kk) * DV + nn]) : 0.0; },
-        acc);
+        for (int r = 0; r < 4; ++r)
+          rec[R::W + Own::col(jj) * DK + cb + Own::row(r)] = acc[jj][r];
+    }
+#pragma unroll 1
+    for (int cb = 0; cb < DV; cb += 64) {
+      mgemm<C, C, kIT>(
+          [&](int m, int kk) {
+            return kk < nt ? (double)to_f32(v[row(kk) * DV + cb + m]) : 0.0;
+          },
+          tbt, acc);
 #pragma unroll
-    for (int r = 0; r < kIR; ++r)
+      for (int jj = 0; jj < TP; ++jj)
 #pragma unroll
-      for (int jj = 0; jj < DV / 16; ++jj)
-        rec[R::UB + ((t >> 4) * kIR + r) * DV + (t & 15) + 16 * jj] = acc[r][jj];
+        for (int r = 0; r < 4; ++r)
+          rec[R::UB + Own::col(jj) * DV + cb + Own::row(r)] = acc[jj][r];
+    }
   }
 }
 
