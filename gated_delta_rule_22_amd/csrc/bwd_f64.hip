@@ -194,7 +194,7 @@ __global__ __launch_bounds__(kBT) void f64_bwd_chunk(
   double *s_P = s_pool + kBA;             // dP (lower incl.)
   double *s_DA = s_P + C * kSM;           // beta_i dA_ij (strictly lower)
   __shared__ double s_beta[C], s_dbp[2][C];
-  __shared__ double s_R[DK], s_red2[DK], s_dGn[kCH];
+  __shared__ double s_R[DK], s_sig[DK], s_red2[kCH], s_dGn[kCH];
   __shared__ double s_red[4][kCH];
   __shared__ int s_fb[DK];
   __shared__ int s_anyfb;
@@ -256,7 +256,10 @@ __global__ __launch_bounds__(kBT) void f64_bwd_chunk(
     // r_ij = e_i f_j with e = sign 2^(G - Rm), f = sign 2^(Rm - G) about the
     // midpoint Rm of the channel's range; beyond +-1000 binary orders that
     // product could leave fp64's range, and the channel takes exp2 per pair.
-    s_R[t] = 0.5 * (gmax + gmin);
+    // (an integer midpoint: gamma = e 2^Rm is then an exact scaling of e)
+    const double Rm = rint(0.5 * (gmax + gmin));
+    s_R[t] = Rm;
+    s_sig[t] = (par ? -1.0 : 1.0) * exp2(G - Rm);   // sign(gamma_n) 2^(G_n - Rm)
     s_fb[t] = (gmax - gmin) > 2000.0;
     if (gmax - gmin > 2000.0) s_anyfb = 1;
   }
@@ -290,30 +293,27 @@ __global__ __launch_bounds__(kBT) void f64_bwd_chunk(
     }
   }
   __syncthreads();
-  // the gate factors of every (token, channel), once
+  // the gate factors of every (token, channel), once: e = 2^(G - Rm) and
+  // f = 2^(Rm - G) (signed), gamma = sign e 2^Rm and gamma_n / gamma =
+  // (sign_n 2^(G_n - Rm)) f; channels on the exact path take exp2 directly
 #pragma unroll 2
   for (int p = t; p < C * DK; p += kBT) {
     const int c = p % DK;
     const double G = s_l[p], sg = s_sg[p];
-    const double Gn = s_l[(C - 1) * DK + c], sn = s_sg[(C - 1) * DK + c];
     scr[X::G + p] = G;
-    scr[X::GAM + p] = sg * exp2(G);
-    scr[X::KHR + p] = sg * sn * exp2(Gn - G);
-    scr[X::E + p] = s_fb[c] ? 0.0 : sg * exp2(G - s_R[c]);
-    scr[X::F + p] = s_fb[c] ? 0.0 : sg * exp2(s_R[c] - G);
-  }
-  // sum_j dS'[c][j] S[c][j] per channel: four threads per channel
-  {
-    const int c = t >> 2, part = t & 3;
-    double s = 0.0;
-    if (c < DK) {
-#pragma unroll 8
-      for (int j = part * (DV / 4); j < (part + 1) * (DV / 4); ++j)
-        s += dSe[c * DV + j] * Sc[c * DV + j];
+    if (s_fb[c]) {
+      const double Gn = s_l[(C - 1) * DK + c], sn = s_sg[(C - 1) * DK + c];
+      scr[X::GAM + p] = sg * exp2(G);
+      scr[X::KHR + p] = sg * sn * exp2(Gn - G);
+      scr[X::E + p] = 0.0;
+      scr[X::F + p] = 0.0;
+    } else {
+      const double Rm = s_R[c], e = exp2(G - Rm), f = sg * exp2(Rm - G);
+      scr[X::GAM + p] = sg * ldexp(e, (int)Rm);
+      scr[X::KHR + p] = s_sig[c] * f;
+      scr[X::E + p] = sg * e;
+      scr[X::F + p] = f;
     }
-    s += __shfl_xor(s, 1);
-    s += __shfl_xor(s, 2);
-    if (part == 0 && c < DK) s_red2[c] = s;
   }
   __threadfence_block();   // scratch is read back by this workgroup only
   __syncthreads();
@@ -388,6 +388,7 @@ __global__ __launch_bounds__(kBT) void f64_bwd_chunk(
 #pragma unroll 1
   for (int hf = 0; hf < DK / kCH; ++hf) {
     const int cb = hf * kCH;
+
     // this thread's first row and column of the block, made opaque to the
     // optimiser in every pass (an empty asm statement) so that no per-element
     // address is hoisted out of the loop and held in registers across it
@@ -435,6 +436,16 @@ __global__ __launch_bounds__(kBT) void f64_bwd_chunk(
     // and the same amount, summed over i, goes to dGamma_n.
     for (int p = t; p < kCH * DV; p += kBT) s_b[(p / DV) * SV + p % DV] = dSe[cb * DV + p];
     __syncthreads();
+    // sum_j dS'[c][j] S[c][j] per channel of the block: 16 lanes per channel
+    {
+      static_assert(kCH * 16 == kBT, "16 threads per channel");
+      const int cl = t >> 4, jp = t & 15;
+      double sdot = 0.0;
+#pragma unroll 8
+      for (int j = jp; j < DV; j += 16) sdot += s_b[cl * SV + j] * Sc[(cb + cl) * DV + j];
+      sdot = sum16(sdot);
+      if (jp == 0) s_red2[cl] = sdot;
+    }
     mgemm<kCH, DV, kBT>([&](int m, int kk) { return Uc[m * DV + kk]; },
                        [&](int kk, int nn) { return s_b[nn * SV + kk]; }, acc);
 #pragma unroll
@@ -457,7 +468,7 @@ __global__ __launch_bounds__(kBT) void f64_bwd_chunk(
     __syncthreads();
     if (t < kCH)
       s_dGn[t] = ((s_red[0][t] + s_red[1][t]) + (s_red[2][t] + s_red[3][t])) +
-                 rec[R::GN + cb + t] * s_red2[cb + t];
+                 rec[R::GN + cb + t] * s_red2[t];
 
     // ---- phase 4: the right operands F o K, E o K, E o Q of this half
     double *sFK = s_b, *sEK = s_b + C * SC, *sEQ = s_b + 2 * C * SC;
