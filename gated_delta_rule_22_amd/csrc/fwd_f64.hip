@@ -60,7 +60,7 @@ __global__ __launch_bounds__(kIT) void f64_intra(
   __shared__ double s_A[C * (C + 1)];
   __shared__ double s_u[kU];            // group operands | product staging
   __shared__ double s_beta[C], s_fk[C], s_fq[C];
-  __shared__ double s_R[DK];
+  __shared__ double s_R[DK], s_sig[DK];
   __shared__ int s_fb[DK];
   __shared__ int s_anyfb;
 
@@ -100,7 +100,10 @@ __global__ __launch_bounds__(kIT) void f64_intra(
     // Pair ratios are formed as e_i f_j with e = 2^(G - Rm), f = 2^(Rm - G)
     // about the midpoint Rm of the channel's range; past +-1000 binary orders
     // that product could leave fp64's range and the channel takes exp2 per pair.
-    s_R[t] = 0.5 * (gmax + gmin);
+    // (an integer midpoint: gamma = e 2^Rm is then an exact scaling of e)
+    const double Rm = rint(0.5 * (gmax + gmin));
+    s_R[t] = Rm;
+    s_sig[t] = (par ? -1.0 : 1.0) * exp2(G - Rm);   // sign(gamma_n) 2^(G_n - Rm)
     s_fb[t] = (gmax - gmin) > 2000.0;
     if (gmax - gmin > 2000.0) s_anyfb = 1;
   }
@@ -152,14 +155,29 @@ __global__ __launch_bounds__(kIT) void f64_intra(
       __syncthreads();                  // the previous block's products are done
 #pragma unroll
       for (int u = 0; u < NG; ++u) {
+        // the split factors, and the gamma-scaled records of this (token,
+        // channel): gamma Q, gamma K, K gamma_n / gamma and gamma_n (masked
+        // tokens have k = q = 0)
         const int p = t + u * kIT, i = p / kCB, cl = p % kCB, c = c0 + cl;
-        double e = 0.0, f = 0.0;
-        if (!s_fb[c]) {
-          const double G = s_G[i * DK + c], sg = s_par[i * DK + c] ? -1.0 : 1.0;
-          e = sg * exp2(G - s_R[c]);
-          f = sg * exp2(s_R[c] - G);
-        }
+        const double G = s_G[i * DK + c], sg = s_par[i * DK + c] ? -1.0 : 1.0;
         const double kh = (double)rk[u] * s_fk[i], qh = (double)rq[u] * s_fq[i];
+        double e = 0.0, f = 0.0, gam, khr;
+        if (!s_fb[c]) {
+          const double Rm = s_R[c], eu = exp2(G - Rm);
+          e = sg * eu;
+          f = sg * exp2(Rm - G);
+          gam = sg * ldexp(eu, (int)Rm);
+          khr = s_sig[c] * f;
+        } else {
+          const double Gn = s_G[(C - 1) * DK + c];
+          const double sn = s_par[(C - 1) * DK + c] ? -1.0 : 1.0;
+          gam = sg * exp2(G);
+          khr = sg * sn * exp2(Gn - G);
+        }
+        rec[R::QT + i * DK + c] = qh * gam;
+        rec[R::GK + i * DK + c] = kh * gam;
+        rec[R::KH + i * DK + c] = kh * khr;
+        if (i == C - 1) rec[R::GN + c] = gam;
         sKE[i * SB + cl] = kh * e;
         sQE[i * SB + cl] = qh * e;
         sKF[i * SB + cl] = kh * f;
@@ -200,21 +218,6 @@ __global__ __launch_bounds__(kIT) void f64_intra(
       }
   }
 
-  // ---- gamma-scaled operands (masked tokens have k = q = 0).
-#pragma unroll 8
-  for (int p = t; p < C * DK; p += kIT) {
-    const int i = p / DK, c = p % DK;
-    const double Gi = s_G[i * DK + c], Gn = s_G[(C - 1) * DK + c];
-    const double si = s_par[i * DK + c] ? -1.0 : 1.0;
-    const double sn = (s_par[i * DK + c] ^ s_par[(C - 1) * DK + c]) ? -1.0 : 1.0;
-    const double gam = si * exp2(Gi);
-    const double kk = i < nt ? (double)to_f32(k[row(i) * DK + c]) * s_fk[i] : 0.0;
-    const double qq = i < nt ? (double)to_f32(q[row(i) * DK + c]) * s_fq[i] : 0.0;
-    rec[R::QT + p] = qq * gam;
-    rec[R::GK + p] = kk * gam;
-    rec[R::KH + p] = kk * sn * exp2(Gn - Gi);
-    if (i == C - 1) rec[R::GN + c] = gam;
-  }
   __threadfence_block();   // scratch is read back by this workgroup only
   __syncthreads();
 
