@@ -70,8 +70,9 @@ def bwd_algorithmic(w):
     """Compulsory HBM bytes of one backward (inputs and upstream gradients read
     once, gradients written once) and its fp64 flop count, both per launch.
 
-    Flops per (64-token chunk, head), dense counts as the kernels execute them
-    (C = 64, d = dk = dv): the chunk records (A and P pair sums, T, W, Ubar)
+    Flops per (64-token chunk, head), counting each product's nonzero work (a
+    product with a triangular factor at half; the matrix-core kernels execute
+    the full tiles) (C = 64, d = dk = dv): the chunk records (A, P, T, W, Ubar)
     4 C^2 d + C^3 / 3 + 2 C^2 d; the forward's state pass (U and the state
     update) 4 C d^2; the reverse state pass (dU, dS) 6 C d^2 + C^2 d; the
     chunk gradients (dX, dP, dA, three C x d x d products, pair sums)

@@ -29,86 +29,6 @@ struct Rec {
 };
 
 // --------------------------------------------------------------------------
-// Block product in fp64: Out(m, n) = sum_{kk < K} A(m, kk) B(kk, n) for
-// m < 64 and n < NB, staged through LDS in K-slices of 16, by a block of NT
-// (256 or 512) threads.  Thread t owns rows RPT (t / 16) + r (r < RPT =
-// 1024 / NT) and columns t % 16 + 16 jj (jj < NB / 16) and gets its sums in
-// acc[r][jj].  fa / fb return the operands (from global memory or
-// LDS); the next slice is loaded into registers while the current one is
-// multiplied, so its latency hides behind the arithmetic.  A_MFAST / B_KFAST
-// choose which index runs fastest across threads when loading, so that a
-// transposed source is read along its contiguous axis.  sA / sB need
-// kStageA and kKB * (NB + 1) doubles.  Every thread of the block must call it;
-// it begins and ends with a barrier.
-constexpr int kKB = 16;
-constexpr int kStageA = 64 * (kKB + 1);
-__host__ __device__ constexpr int stage_doubles(int nb) { return kStageA + kKB * (nb + 1); }
-
-template <int NB, int K, bool A_MFAST, bool B_KFAST, int NT = kThreads, typename FA,
-          typename FB>
-__device__ __forceinline__ void gemm64(double *sA, double *sB, const FA &fa, const FB &fb,
-                                       double (&acc)[1024 / NT][NB / 16]) {
-  static_assert(K % kKB == 0 && NB % 16 == 0, "K and NB must be multiples of 16");
-  static_assert(NT == 256 || NT == 512, "256 or 512 threads");
-  constexpr int RPT = 1024 / NT;                     // rows per thread: 4 or 2
-  constexpr int SA = kKB + 1, SB = NB + 1;
-  constexpr int NA = 64 * kKB / NT, NBL = kKB * NB / NT;
-  static_assert(NBL >= 1, "NB too small for this thread count");
-  const int t = threadIdx.x, rgp = t >> 4, cl = t & 15;
-  double ra[NA], rb[NBL];
-  auto load = [&](int k0) {
-#pragma unroll
-    for (int u = 0; u < NA; ++u) {
-      const int p = t + u * NT;
-      const int m = A_MFAST ? p % 64 : p / kKB, kk = A_MFAST ? p / 64 : p % kKB;
-      ra[u] = fa(m, k0 + kk);
-    }
-#pragma unroll
-    for (int u = 0; u < NBL; ++u) {
-      const int p = t + u * NT;
-      const int kk = B_KFAST ? p % kKB : p / NB, n = B_KFAST ? p / kKB : p % NB;
-      rb[u] = fb(k0 + kk, n);
-    }
-  };
-#pragma unroll
-  for (int r = 0; r < RPT; ++r)
-#pragma unroll
-    for (int jj = 0; jj < NB / 16; ++jj) acc[r][jj] = 0.0;
-  load(0);
-#pragma unroll 1
-  for (int k0 = 0; k0 < K; k0 += kKB) {
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < NA; ++u) {
-      const int p = t + u * NT;
-      const int m = A_MFAST ? p % 64 : p / kKB, kk = A_MFAST ? p / 64 : p % kKB;
-      sA[m * SA + kk] = ra[u];
-    }
-#pragma unroll
-    for (int u = 0; u < NBL; ++u) {
-      const int p = t + u * NT;
-      const int kk = B_KFAST ? p % kKB : p / NB, n = B_KFAST ? p / kKB : p % NB;
-      sB[kk * SB + n] = rb[u];
-    }
-    __syncthreads();
-    if (k0 + kKB < K) load(k0 + kKB);
-#pragma unroll 4
-    for (int kk = 0; kk < kKB; ++kk) {
-      double a[RPT], b[NB / 16];
-#pragma unroll
-      for (int r = 0; r < RPT; ++r) a[r] = sA[(rgp * RPT + r) * SA + kk];
-#pragma unroll
-      for (int jj = 0; jj < NB / 16; ++jj) b[jj] = sB[kk * SB + cl + 16 * jj];
-#pragma unroll
-      for (int r = 0; r < RPT; ++r)
-#pragma unroll
-        for (int jj = 0; jj < NB / 16; ++jj) acc[r][jj] = fma(a[r], b[jj], acc[r][jj]);
-    }
-  }
-  __syncthreads();
-}
-
-// --------------------------------------------------------------------------
 // Block product on the fp64 matrix cores, v_mfma_f64_16x16x4_f64:
 // Out(m, n) = sum_{kk < K} A(m, kk) B(kk, n) for m < 64, n < NB, by NT (256
 // or 512) threads, with no LDS staging and no barrier inside: fa and fb are
@@ -181,7 +101,8 @@ __device__ __forceinline__ void mgemm(const FA &fa, const FB &fb,
   }
 }
 
-// Sum over the 16 lanes that share a row group of gemm64 (lanes 16 g .. 16 g + 15).
+// Sum over 16 consecutive lanes (16 g .. 16 g + 15): the lanes that hold one
+// row of an mgemm result tile.
 __device__ __forceinline__ double sum16(double x) {
   x += __shfl_xor(x, 1);
   x += __shfl_xor(x, 2);

@@ -41,10 +41,8 @@ using namespace f64;
 
 constexpr int kCB = 32;              // channels per block of the A and P products
 
-// The record kernel runs 512 threads (two waves per SIMD over one block's
-// LDS); each thread holds kIR rows of every 64-row tile.
+// The record kernel runs 512 threads (two waves per SIMD over one block's LDS).
 constexpr int kIT = 512;
-constexpr int kIR = 1024 / kIT;
 
 template <typename TIn, int DK, int DV>
 __global__ __launch_bounds__(kIT) void f64_intra(
@@ -52,13 +50,12 @@ __global__ __launch_bounds__(kIT) void f64_intra(
     const float *__restrict__ g, const float *__restrict__ beta, int H, int N, SeqTable tab,
     double *__restrict__ records, size_t rec_doubles, int signed_gates, int l2norm) {
   using R = Rec<DK, DV>;
-  constexpr int NBM = DK > DV ? DK : DV;
-  constexpr int kG = 3 * C * (kCB + 1) > C * DK / 2 ? 3 * C * (kCB + 1) : C * DK / 2;
-  constexpr int kU = stage_doubles(NBM) > kG ? stage_doubles(NBM) : kG;
+  constexpr int kU = 3 * C * (kCB + 1);  // the A/P product operands of one channel block
+  static_assert(kU >= 3 * 256, "room for the blocked inverse's partial products");
   __shared__ double s_G[C * DK > C * (C + 1) ? C * DK : C * (C + 1)];  // G, later T
   __shared__ uint8_t s_par[C * DK];
   __shared__ double s_A[C * (C + 1)];
-  __shared__ double s_u[kU];            // group operands | product staging
+  __shared__ double s_u[kU];            // A/P operands | blocked-inverse partial products
   __shared__ double s_beta[C], s_fk[C], s_fq[C];
   __shared__ double s_R[DK], s_sig[DK];
   __shared__ int s_fb[DK];
