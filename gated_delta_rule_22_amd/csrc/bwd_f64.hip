@@ -132,15 +132,38 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_state(
     }
 }
 
-// Per-chunk scratch (doubles): dX [C][DV], then [C][DK] arrays of the
-// in-chunk gate factors, per (token i, channel c):
-//   G    log2|gamma_i|                GAM  gamma_i (signed)
-//   KHR  gamma_n / gamma_i            E, F the ratio split sign 2^(+-(G - Rm))
-// and AQ, AK: the pair terms R1, R2 of exact-path channels, later the
-// gradients with respect to the normalised q and k (q/k normalisation on).
-// Exact-path channels keep their pair terms C1, C2 in E and F.
+// The per-chunk gradients run in three kernels (all 512 or 256 threads):
+//   f64_bwd_prep   (chunk, head): the gate factors, dX = T^T dU (dV, the dX.V
+//                  part of dbeta), dP and beta dA (the A/beta . dA part);
+//   f64_bwd_pairs  (32-channel block, chunk, head): the direct terms and the
+//                  pair terms of dq, dk and dGamma for its channels, and dalpha;
+//   f64_bwd_final  (chunk, head): dbeta, and the Jacobian of the fused q/k
+//                  normalisation.
+// Every contraction runs on the fp64 matrix cores (mgemm).  The pair terms
+// use the ratio split r_ij = e_i f_j about each channel's midpoint, which turns
+// them into four dense products:
+//   R1 = E o (dP (F o K)),      R2 = E o ((beta dA) (F o K)),
+//   C1 = F o ((beta dA)^T (E o K)),  C2 = F o (dP^T (E o Q))
+// (o: elementwise; K, Q the normalised keys and queries).  A channel whose
+// log-gate range is too wide for the split takes the ratios one pair at a time.
+constexpr int kBT = 512;                 // threads of the prep and pair kernels
+constexpr int kCH = 32;                  // channels per pair-kernel workgroup
+
+// Per-chunk scratch (doubles), written by f64_bwd_prep and f64_bwd_pairs:
+//   DX [C][DV]        dX = T^T dU
+//   G, GAM, KHR [C][DK]  log2|gamma_i|, gamma_i (signed), gamma_n / gamma_i
+//   E, F [C][DK]      the ratio split sign 2^(+-(G - Rm)); on exact-path
+//                     channels 0, later their pair terms C1 and C2
+//   AQ, AK [C][DK]    the pair terms R1, R2 of exact-path channels, later the
+//                     gradients with respect to the normalised q and k
+//   DP, DA [C][C]     dP and beta dA, zero above the diagonal
+//   FB [DK]           1 on channels that take the exact path
+//   FQ, FK [C]        the q/k normalisation factors (1 if off)
+//   DB [1 + NB][C]    dbeta: the prep kernel's part, then one row per block
+//   QD, KD [NB][C]    qhat . dqhat and khat . dkhat per channel block
 template <int DK, int DV>
 struct Scr {
+  static constexpr int NB = DK / kCH;
   static constexpr size_t DX = 0;
   static constexpr size_t G = DX + C * DV;
   static constexpr size_t GAM = G + C * DK;
@@ -149,57 +172,45 @@ struct Scr {
   static constexpr size_t F = E + C * DK;
   static constexpr size_t AQ = F + C * DK;
   static constexpr size_t AK = AQ + C * DK;
-  static constexpr size_t SIZE = AK + C * DK;
+  static constexpr size_t DP = AK + C * DK;
+  static constexpr size_t DA = DP + C * C;
+  static constexpr size_t FB = DA + C * C;
+  static constexpr size_t FQ = FB + DK;
+  static constexpr size_t FK = FQ + C;
+  static constexpr size_t DB = FK + C;
+  static constexpr size_t QD = DB + (1 + NB) * C;
+  static constexpr size_t KD = QD + NB * C;
+  static constexpr size_t SIZE = KD + NB * C;
 };
 
-constexpr int kSM = C + 1;               // padded row of the C x C LDS matrices
+// Row sums over a wave's 16 lanes, kept per half of the column tiles (wave
+// t / 256) so that every (half, row) slot has a single writer.
+__device__ __forceinline__ void add_row(double (&dst)[2][C], int i, double part) {
+  part = sum16(part);
+  if ((threadIdx.x & 15) == 0) dst[threadIdx.x >> 8][i] += part;
+}
 
 // --------------------------------------------------------------------------
-// f64_bwd_chunk: all per-chunk gradients of one (chunk, head), 512 threads.
-// Every contraction runs on the fp64 matrix cores (mgemm) with its right
-// operand staged in LDS; each thread's share of a 64-row result follows MOwn.
-// The pair terms use the ratio split r_ij = e_i f_j about each channel's
-// midpoint, which turns them into four dense products:
-//   R1 = E o (dP (F o K)),      R2 = E o ((beta dA) (F o K)),
-//   C1 = F o ((beta dA)^T (E o K)),  C2 = F o (dP^T (E o Q))
-// (o: elementwise; K, Q the normalised keys and queries).  A channel whose
-// log-gate range is too wide for the split takes the ratios one pair at a time.
-constexpr int kBT = 512;
-constexpr int kCH = 32;                  // channels per pass of the direct and pair terms
-
 template <typename TIn, int DK, int DV>
-__global__ __launch_bounds__(kBT) void f64_bwd_chunk(
+__global__ __launch_bounds__(kBT) void f64_bwd_prep(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, const float *__restrict__ dO,
     int H, int N, SeqTable tab, const double *__restrict__ records, size_t rec_doubles,
-    const double *__restrict__ S_chunks, const double *__restrict__ U_chunks,
-    const double *__restrict__ dU_chunks, const double *__restrict__ dSe_chunks,
-    double *__restrict__ scratch, float *__restrict__ dq, float *__restrict__ dk,
-    float *__restrict__ dv, float *__restrict__ dg, float *__restrict__ dbeta, int signed_gates,
-    int l2norm) {
+    const double *__restrict__ U_chunks, const double *__restrict__ dU_chunks,
+    double *__restrict__ scratch, float *__restrict__ dv, int signed_gates, int l2norm) {
   using R = Rec<DK, DV>;
   using X = Scr<DK, DV>;
   using OwnV = MOwn<DV, kBT>;              // C x DV results
   using OwnC = MOwn<C, kBT>;               // C x C results
-  using Own = MOwn<kCH, kBT>;              // C x kCH results (a channel block)
-  constexpr int TV = OwnV::TPW, TC = OwnC::TPW, T64 = Own::TPW;
-  constexpr int SV = DV + 1, SC = kCH + 1;  // padded LDS rows
+  constexpr int TV = OwnV::TPW, TC = OwnC::TPW;
+  constexpr int SV = DV + 1;               // padded LDS row
   constexpr int kB0 = C * DK + C * DK / 2;
-  constexpr int kBA = C * SV > 3 * C * SC ? C * SV : 3 * C * SC;
-  constexpr int kPool = (kB0 > kBA + 2 * C * kSM ? kB0 : kBA + 2 * C * kSM);
-  // one LDS pool: the phase-0 gates, later the staged right operands (s_b)
-  // beside dP and beta dA as full C x C matrices, zero above the diagonal
-  __shared__ double s_pool[kPool];
-  double *s_b = s_pool;
-  double *s_P = s_pool + kBA;             // dP (lower incl.)
-  double *s_DA = s_P + C * kSM;           // beta_i dA_ij (strictly lower)
+  constexpr int kPool = kB0 > C * SV ? kB0 : C * SV;
+  // one LDS pool: the phase-0 gates, later the staged right operands
+  __shared__ double s_b[kPool];
   __shared__ double s_beta[C], s_dbp[2][C];
-  __shared__ double s_R[DK], s_sig[DK], s_red2[kCH], s_dGn[kCH];
-  __shared__ double s_red[4][kCH];
+  __shared__ double s_R[DK], s_sig[DK];
   __shared__ int s_fb[DK];
-  __shared__ int s_anyfb;
-  __shared__ double s_fk[C], s_fq[C];     // key/query normalisation factors per token (1 if off)
-  __shared__ double s_kd[2][C], s_qd[2][C];  // khat . dkhat and qhat . dqhat, per half-block
 
   const int cflat = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
   if (cflat >= tab.chunk_off[N]) return;
@@ -209,29 +220,18 @@ __global__ __launch_bounds__(kBT) void f64_bwd_chunk(
   const int nt = min(C, tab.seq_len[n] - lc * C);
   const size_t ch = (size_t)cflat * H + h;
   const double *rec = records + ch * rec_doubles;
-  const double *Sc = S_chunks + ch * DK * DV;
-  const double *dSe = dSe_chunks + ch * DK * DV;
   const double *Uc = U_chunks + ch * C * DV;
   const double *dUc = dU_chunks + ch * C * DV;
   double *scr = scratch + ch * X::SIZE;
-  const int wh = t >> 8;                  // which half of the column tiles this wave holds
-  const bool lead = (t & 15) == 0;        // lane that owns a row's sum over 16 lanes
 
   auto row = [&](int i) { return (size_t)(t0 + i) * H + h; };   // token-head row
   auto dO_at = [&](int m, int c) { return m < nt ? (double)dO[row(m) * DV + c] : 0.0; };
-  auto khat = [&](int i, int c) {
-    return i < nt ? (double)to_f32(k[row(i) * DK + c]) * s_fk[i] : 0.0;
-  };
-  auto qhat = [&](int i, int c) {
-    return i < nt ? (double)to_f32(q[row(i) * DK + c]) * s_fq[i] : 0.0;
-  };
 
   // ---- phase 0: in-chunk gate log-magnitudes and signs: log2|alpha| for
   // every (token, channel) in parallel into LDS (the sign rides in a float
   // copy of alpha), then the scans per channel.
   double *s_l = s_b;                                    // [C][DK] log2|alpha|
   float *s_sg = reinterpret_cast<float *>(s_b + C * DK);  // [C][DK] alpha (sign only)
-  if (t == 0) s_anyfb = 0;
 #pragma unroll 4
   for (int p = t; p < C * DK; p += kBT) {
     const float a = p / DK < nt ? g[row(p / DK) * DK + p % DK] : 1.f;
@@ -258,16 +258,15 @@ __global__ __launch_bounds__(kBT) void f64_bwd_chunk(
     // product could leave fp64's range, and the channel takes exp2 per pair.
     // (an integer midpoint: gamma = e 2^Rm is then an exact scaling of e)
     const double Rm = rint(0.5 * (gmax + gmin));
+    const int fb = (gmax - gmin) > 2000.0;
     s_R[t] = Rm;
     s_sig[t] = (par ? -1.0 : 1.0) * exp2(G - Rm);   // sign(gamma_n) 2^(G_n - Rm)
-    s_fb[t] = (gmax - gmin) > 2000.0;
-    if (gmax - gmin > 2000.0) s_anyfb = 1;
+    s_fb[t] = fb;
+    scr[X::FB + t] = fb;
   }
   if (t < C) {
     s_beta[t] = t < nt ? (double)beta[row(t)] : 0.0;
     s_dbp[0][t] = s_dbp[1][t] = 0.0;
-    s_kd[0][t] = s_kd[1][t] = 0.0;
-    s_qd[0][t] = s_qd[1][t] = 0.0;
   }
   // optional q/k normalisation factors (sum x^2 + 1e-6)^(-1/2): eight threads
   // per token
@@ -288,8 +287,8 @@ __global__ __launch_bounds__(kBT) void f64_bwd_chunk(
       sq += __shfl_xor(sq, o);
     }
     if (part == 0 && i < C) {
-      s_fk[i] = (l2norm && i < nt) ? 1.0 / sqrt(sk + 1e-6) : 1.0;
-      s_fq[i] = (l2norm && i < nt) ? 1.0 / sqrt(sq + 1e-6) : 1.0;
+      scr[X::FK + i] = (l2norm && i < nt) ? 1.0 / sqrt(sk + 1e-6) : 1.0;
+      scr[X::FQ + i] = (l2norm && i < nt) ? 1.0 / sqrt(sq + 1e-6) : 1.0;
     }
   }
   __syncthreads();
@@ -315,15 +314,7 @@ __global__ __launch_bounds__(kBT) void f64_bwd_chunk(
       scr[X::F + p] = f;
     }
   }
-  __threadfence_block();   // scratch is read back by this workgroup only
   __syncthreads();
-
-  // row sums over a wave's 16 lanes, kept per half-block so that every
-  // (half, row) slot has a single writer: deterministic order
-  auto add_row = [&](double (&dst)[2][C], int i, double part) {
-    part = sum16(part);
-    if (lead) dst[wh][i] += part;
-  };
 
   // ---- phase 1: dX = T^T dU; dV = Diag(beta) dX; dbeta += dX_i . V_i
   for (int p = t; p < C * DV; p += kBT) s_b[(p / DV) * SV + p % DV] = dUc[p];
@@ -349,24 +340,25 @@ __global__ __launch_bounds__(kBT) void f64_bwd_chunk(
       add_row(s_dbp, i, part);
     }
   }
-  __threadfence_block();
+  __threadfence_block();   // scratch is read back by this workgroup
   __syncthreads();
 
-  // ---- phase 2: dP = tril(dO U^T) and beta_i dA_ij, dA = -strict_tril(dX U^T)
+  // ---- phase 2: dP = tril(dO U^T) and beta_i dA_ij, dA = -strict_tril(dX U^T),
+  // stored as full C x C matrices (zero above the diagonal)
   for (int p = t; p < C * DV; p += kBT) s_b[(p / DV) * SV + p % DV] = Uc[p];
   __syncthreads();
   {
     auto ut = [&](int kk, int nn) { return s_b[nn * SV + kk]; };   // U^T
     d4 acc[TC];
-    mgemm<64, DV, kBT>(dO_at, ut, acc);
+    mgemm<C, DV, kBT>(dO_at, ut, acc);
 #pragma unroll
     for (int jj = 0; jj < TC; ++jj)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = OwnC::row(r), j = OwnC::col(jj);
-        s_P[i * kSM + j] = j <= i ? acc[jj][r] : 0.0;
+        scr[X::DP + i * C + j] = j <= i ? acc[jj][r] : 0.0;
       }
-    mgemm<64, DV, kBT>([&](int m, int kk) { return scr[X::DX + m * DV + kk]; }, ut, acc);
+    mgemm<C, DV, kBT>([&](int m, int kk) { return scr[X::DX + m * DV + kk]; }, ut, acc);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = OwnC::row(r);
@@ -375,284 +367,372 @@ __global__ __launch_bounds__(kBT) void f64_bwd_chunk(
       for (int jj = 0; jj < TC; ++jj) {
         const int j = OwnC::col(jj);
         const double dA = j < i ? -acc[jj][r] : 0.0;
-        s_DA[i * kSM + j] = s_beta[i] * dA;
+        scr[X::DA + i * C + j] = s_beta[i] * dA;
         part += rec[R::AH + i * C + j] * dA;
       }
       add_row(s_dbp, i, part);
     }
   }
   __syncthreads();
+  if (t < C) scr[X::DB + t] = s_dbp[0][t] + s_dbp[1][t];
+}
 
-  // ---- phases 3 and 4, kCH channels at a time.  The direct parts of dq, dk and
-  // dGamma stay in registers (same ownership) until the pair terms are added.
-#pragma unroll 1
-  for (int hf = 0; hf < DK / kCH; ++hf) {
-    const int cb = hf * kCH;
+// --------------------------------------------------------------------------
+// One workgroup per (kCH-channel block, chunk, head).  The workgroups of one
+// (chunk, head) are placed on the same XCD (workgroups are dealt to the eight
+// XCDs in turn), so that the operands they share are read once into its L2.
+template <typename TIn, int DK, int DV>
+__global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
+    const TIn *__restrict__ q, const TIn *__restrict__ k, const float *__restrict__ g,
+    const float *__restrict__ beta, const float *__restrict__ dO, int H, int N, SeqTable tab,
+    const double *__restrict__ records, size_t rec_doubles, const double *__restrict__ S_chunks,
+    const double *__restrict__ U_chunks, const double *__restrict__ dSe_chunks,
+    double *__restrict__ scratch, size_t n_ch, float *__restrict__ dq, float *__restrict__ dk,
+    float *__restrict__ dg, int l2norm) {
+  using R = Rec<DK, DV>;
+  using X = Scr<DK, DV>;
+  using Own = MOwn<kCH, kBT>;              // C x kCH results
+  constexpr int T64 = Own::TPW;
+  constexpr int NB = X::NB;
+  constexpr int SV = DV + 1, SC = kCH + 1;  // padded LDS rows
+  constexpr int NSEG = kBT / kCH, LSEG = C / NSEG;
+  constexpr int kB = kCH * SV > 3 * C * SC ? kCH * SV : 3 * C * SC;
+  static_assert(kB >= C * SC + NSEG * kCH, "room for the cumulative sum");
+  __shared__ double s_b[kB];              // staged right operands | dGamma
+  __shared__ double s_beta[C], s_dbp[2][C], s_kd[2][C], s_qd[2][C];
+  __shared__ double s_fk[C], s_fq[C];
+  __shared__ double s_red[4][kCH], s_red2[kCH], s_dGn[kCH];
+  __shared__ int s_fb[kCH];
 
-    // this thread's first row and column of the block, made opaque to the
-    // optimiser in every pass (an empty asm statement) so that no per-element
-    // address is hoisted out of the loop and held in registers across it
-    int r0 = Own::row(0), c0 = Own::col(0);
-    asm volatile("" : "+v"(r0), "+v"(c0));
-    auto orow = [&](int r) { return r0 + 4 * r; };
-    auto ocol = [&](int jj) { return c0 + 16 * jj; };
-    double aq[T64][4], ak[T64][4], ag[T64][4];
-    d4 acc[T64];
-    // dQT = dO S^T: dq = gamma dQT; dGamma = q gamma dQT.  M5 = dX S^T:
-    // d(gamma K) = -Diag(beta) M5.
-    for (int p = t; p < kCH * DV; p += kBT) s_b[(p / DV) * SV + p % DV] = Sc[cb * DV + p];
-    __syncthreads();
-    {
-      auto st = [&](int kk, int nn) { return s_b[nn * SV + kk]; };   // S^T (this half)
-      double gam[T64][4];
-      mgemm<kCH, DV, kBT>(dO_at, st, acc);
-#pragma unroll
-      for (int jj = 0; jj < T64; ++jj)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = orow(r), c = cb + ocol(jj);
-          gam[jj][r] = scr[X::GAM + i * DK + c];
-          aq[jj][r] = gam[jj][r] * acc[jj][r];
-          ag[jj][r] = rec[R::QT + i * DK + c] * acc[jj][r];
-        }
-      mgemm<kCH, DV, kBT>([&](int m, int kk) { return scr[X::DX + m * DV + kk]; }, st, acc);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = orow(r);
-        double part = 0.0;
-#pragma unroll
-        for (int jj = 0; jj < T64; ++jj) {
-          const int c = cb + ocol(jj);
-          const double gk = rec[R::GK + i * DK + c];
-          ak[jj][r] = -s_beta[i] * gam[jj][r] * acc[jj][r];
-          ag[jj][r] -= s_beta[i] * gk * acc[jj][r];
-          part -= gk * acc[jj][r];
-        }
-        add_row(s_dbp, i, part);
-      }
-    }
-    __syncthreads();
-    // dKH = U dS'^T: dk += (gamma_n / gamma) dKH; dGamma_i -= k (gamma_n/gamma) dKH,
-    // and the same amount, summed over i, goes to dGamma_n.
-    for (int p = t; p < kCH * DV; p += kBT) s_b[(p / DV) * SV + p % DV] = dSe[cb * DV + p];
-    __syncthreads();
-    // sum_j dS'[c][j] S[c][j] per channel of the block: 16 lanes per channel
-    {
-      static_assert(kCH * 16 == kBT, "16 threads per channel");
-      const int cl = t >> 4, jp = t & 15;
-      double sdot = 0.0;
-#pragma unroll 8
-      for (int j = jp; j < DV; j += 16) sdot += s_b[cl * SV + j] * Sc[(cb + cl) * DV + j];
-      sdot = sum16(sdot);
-      if (jp == 0) s_red2[cl] = sdot;
-    }
-    mgemm<kCH, DV, kBT>([&](int m, int kk) { return Uc[m * DV + kk]; },
-                       [&](int kk, int nn) { return s_b[nn * SV + kk]; }, acc);
-#pragma unroll
-    for (int jj = 0; jj < T64; ++jj) {
-      const int cl = ocol(jj), c = cb + cl;
-      double col = 0.0;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = orow(r);
-        const double khr = scr[X::KHR + i * DK + c];
-        const double term = rec[R::KH + i * DK + c] * acc[jj][r];
-        ak[jj][r] += khr * acc[jj][r];
-        ag[jj][r] -= term;
-        col += term;
-      }
-      col += __shfl_xor(col, 16);
-      col += __shfl_xor(col, 32);
-      if ((t & 63) < 16) s_red[(t >> 6) & 3][cl] = col;
-    }
-    __syncthreads();
-    if (t < kCH)
-      s_dGn[t] = ((s_red[0][t] + s_red[1][t]) + (s_red[2][t] + s_red[3][t])) +
-                 rec[R::GN + cb + t] * s_red2[t];
+  const unsigned wg = blockIdx.x, t = threadIdx.x;
+  const int blk = (int)((wg >> 3) % NB);
+  const size_t chx = (size_t)((wg >> 3) / NB) * 8 + (wg & 7);
+  if (chx >= n_ch) return;
+  const int cflat = (int)(chx / H), h = (int)(chx % H);
+  if (cflat >= tab.chunk_off[N]) return;
+  const int n = find_seq(tab.chunk_off, N, cflat);
+  const int lc = cflat - tab.chunk_off[n];
+  const int t0 = tab.seq_start[n] + lc * C;
+  const int nt = min(C, tab.seq_len[n] - lc * C);
+  const size_t ch = (size_t)cflat * H + h;
+  const double *rec = records + ch * rec_doubles;
+  const double *Sc = S_chunks + ch * DK * DV;
+  const double *dSe = dSe_chunks + ch * DK * DV;
+  const double *Uc = U_chunks + ch * C * DV;
+  double *scr = scratch + ch * X::SIZE;
+  const int cb = blk * kCH;
 
-    // ---- phase 4: the right operands F o K, E o K, E o Q of this half
-    double *sFK = s_b, *sEK = s_b + C * SC, *sEQ = s_b + 2 * C * SC;
-    for (int p = t; p < C * kCH; p += kBT) {
-      const int i = p / kCH, cl = p % kCH, c = cb + cl;
-      const double e = scr[X::E + i * DK + c], f = scr[X::F + i * DK + c];
-      const double kh = khat(i, c), qh = qhat(i, c);
-      sFK[i * SC + cl] = f * kh;
-      sEK[i * SC + cl] = e * kh;
-      sEQ[i * SC + cl] = e * qh;
-    }
-    if (s_anyfb) {
-      // channels too wide for the split: the four pair terms with exp2 per pair
-      // (the sign of gamma is that of GAM, which keeps it when it underflows)
-      __syncthreads();                // E and F of this half read by the staging
-      auto sgn = [&](int i, int c) { return copysign(1.0, scr[X::GAM + i * DK + c]); };
-      for (int cg = 0; cg < kCH; cg += kBT / C) {
-        const int c = cb + cg + t / C, i = t % C;
-        if (!s_fb[c]) continue;
-        const double Gi = scr[X::G + i * DK + c], si = sgn(i, c);
-        double R1 = 0.0, R2 = 0.0, C1 = 0.0, C2 = 0.0;
-        for (int j = 0; j <= i; ++j) {
-          const double r = si * sgn(j, c) * exp2(Gi - scr[X::G + j * DK + c]);
-          const double kr = khat(j, c) * r;
-          R1 = fma(s_P[i * kSM + j], kr, R1);
-          R2 = fma(s_DA[i * kSM + j], kr, R2);
-        }
-        for (int m = i; m < C; ++m) {
-          const double r = si * sgn(m, c) * exp2(scr[X::G + m * DK + c] - Gi);
-          C1 = fma(s_DA[m * kSM + i], khat(m, c) * r, C1);
-          C2 = fma(s_P[m * kSM + i], qhat(m, c) * r, C2);
-        }
-        scr[X::AQ + i * DK + c] = R1;
-        scr[X::AK + i * DK + c] = R2;
-        scr[X::E + i * DK + c] = C1;
-        scr[X::F + i * DK + c] = C2;
-      }
-      __threadfence_block();
-    }
-    __syncthreads();
-    {
-      // the split factor of each owned (token, channel): e for the R terms,
-      // then f = sign 2^(Rm - G) for the C terms (0 on exact-path channels).
-      // The left operands sit in LDS: one slice of prefetch is enough.
-      double ef[T64][4];
-      auto split = [&](size_t arr) {
-#pragma unroll
-        for (int jj = 0; jj < T64; ++jj)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int i = orow(r), c = cb + ocol(jj);
-            ef[jj][r] = s_fb[c] ? 0.0 : scr[arr + i * DK + c];
-          }
-      };
-      split(X::E);
-      // R1 = E o (dP (F o K)): into dq and dGamma (+ q R1); dq is then complete
-      mgemm<kCH, C, kBT, 1>([&](int m, int kk) { return s_P[m * kSM + kk]; },
-                           [&](int kk, int nn) { return sFK[kk * SC + nn]; }, acc);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = orow(r);
-        double dqd = 0.0;
-#pragma unroll
-        for (int jj = 0; jj < T64; ++jj) {
-          const int c = cb + ocol(jj);
-          double R1 = ef[jj][r] * acc[jj][r];
-          if (s_fb[c]) R1 = scr[X::AQ + i * DK + c];      // exact-path channel
-          const double gq = aq[jj][r] + R1, qh = qhat(i, c);
-          ag[jj][r] += qh * R1;
-          if (l2norm) {
-            // the gradient with respect to the normalised row; the
-            // normalisation's Jacobian is applied once every channel is done
-            scr[X::AQ + i * DK + c] = gq;
-            dqd += qh * gq;
-          } else if (i < nt) {
-            dq[row(i) * DK + c] = (float)gq;
-          }
-        }
-        if (l2norm) add_row(s_qd, i, dqd);
-      }
-      // R2 = E o ((beta dA) (F o K)): into dk and dGamma (+ k R2)
-      mgemm<kCH, C, kBT, 1>([&](int m, int kk) { return s_DA[m * kSM + kk]; },
-                           [&](int kk, int nn) { return sFK[kk * SC + nn]; }, acc);
-#pragma unroll
-      for (int jj = 0; jj < T64; ++jj)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = orow(r), c = cb + ocol(jj);
-          const double R2 = ef[jj][r] * acc[jj][r];
-          ak[jj][r] += R2;
-          ag[jj][r] += khat(i, c) * R2;
-        }
-      split(X::F);
-      // C1 = F o ((beta dA)^T (E o K)): into dk and dGamma (- k C1)
-      mgemm<kCH, C, kBT, 1>([&](int m, int kk) { return s_DA[kk * kSM + m]; },
-                           [&](int kk, int nn) { return sEK[kk * SC + nn]; }, acc);
-#pragma unroll
-      for (int jj = 0; jj < T64; ++jj)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = orow(r), c = cb + ocol(jj);
-          const double C1 = ef[jj][r] * acc[jj][r];
-          ak[jj][r] += C1;
-          ag[jj][r] -= khat(i, c) * C1;
-        }
-      // C2 = F o (dP^T (E o Q)): into dk and dGamma (- k C2)
-      mgemm<kCH, C, kBT, 1>([&](int m, int kk) { return s_P[kk * kSM + m]; },
-                           [&](int kk, int nn) { return sEQ[kk * SC + nn]; }, acc);
-      // exact-path channels, the last token's dGamma_n, and dk
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = orow(r);
-        double dkd = 0.0;
-#pragma unroll
-        for (int jj = 0; jj < T64; ++jj) {
-          const int cl = ocol(jj), c = cb + cl;
-          const double kh = khat(i, c);
-          const double C2 = ef[jj][r] * acc[jj][r];
-          ak[jj][r] += C2;
-          ag[jj][r] -= kh * C2;
-          if (s_fb[c]) {
-            const double R2 = scr[X::AK + i * DK + c];
-            const double C1 = scr[X::E + i * DK + c], C2x = scr[X::F + i * DK + c];
-            ak[jj][r] += R2 + C1 + C2x;
-            ag[jj][r] += kh * (R2 - C1 - C2x);
-          }
-          if (i == C - 1) ag[jj][r] += s_dGn[cl];
-          if (l2norm) {
-            scr[X::AK + i * DK + c] = ak[jj][r];
-            dkd += kh * ak[jj][r];
-          } else if (i < nt) {
-            dk[row(i) * DK + c] = (float)ak[jj][r];
-          }
-        }
-        if (l2norm) add_row(s_kd, i, dkd);
-      }
-    }
-    __syncthreads();                    // every read of the staged operands done
-    // dln|alpha_s| = sum_{i >= s} dGamma_i; dalpha = dln|alpha| / alpha.
-    // NSEG segments of C / NSEG tokens per channel, then the segment offsets.
-    constexpr int NSEG = kBT / kCH, LSEG = C / NSEG;
-    double *s_ag = s_b, *s_seg = s_b + C * SC;
+  auto row = [&](int i) { return (size_t)(t0 + i) * H + h; };   // token-head row
+  auto dO_at = [&](int m, int c) { return m < nt ? (double)dO[row(m) * DV + c] : 0.0; };
+  auto khat = [&](int i, int c) {
+    return i < nt ? (double)to_f32(k[row(i) * DK + c]) * s_fk[i] : 0.0;
+  };
+  auto qhat = [&](int i, int c) {
+    return i < nt ? (double)to_f32(q[row(i) * DK + c]) * s_fq[i] : 0.0;
+  };
+
+  if (t < C) {
+    s_beta[t] = t < nt ? (double)beta[row(t)] : 0.0;
+    s_fk[t] = scr[X::FK + t];
+    s_fq[t] = scr[X::FQ + t];
+    s_dbp[0][t] = s_dbp[1][t] = s_kd[0][t] = s_kd[1][t] = s_qd[0][t] = s_qd[1][t] = 0.0;
+  }
+  const bool fbc = t < kCH && scr[X::FB + cb + t] != 0.0;
+  if (t < kCH) s_fb[t] = fbc;
+  // the direct terms: S^T of this block staged (also a barrier for the above)
+  for (int p = t; p < kCH * DV; p += kBT) s_b[(p / DV) * SV + p % DV] = Sc[cb * DV + p];
+  const int anyfb = __syncthreads_or(fbc);
+
+  double aq[T64][4], ak[T64][4], ag[T64][4];
+  d4 acc[T64];
+  // dQT = dO S^T: dq = gamma dQT; dGamma = q gamma dQT.  M5 = dX S^T:
+  // d(gamma K) = -Diag(beta) M5.
+  {
+    auto st = [&](int kk, int nn) { return s_b[nn * SV + kk]; };   // S^T (this block)
+    double gam[T64][4];
+    mgemm<kCH, DV, kBT>(dO_at, st, acc);
 #pragma unroll
     for (int jj = 0; jj < T64; ++jj)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) s_ag[orow(r) * SC + ocol(jj)] = ag[jj][r];
-    __syncthreads();
-    {
-      const int cl = t % kCH, sgm = t / kCH;
-      double sum = 0.0;
+      for (int r = 0; r < 4; ++r) {
+        const int i = Own::row(r), c = cb + Own::col(jj);
+        gam[jj][r] = scr[X::GAM + i * DK + c];
+        aq[jj][r] = gam[jj][r] * acc[jj][r];
+        ag[jj][r] = rec[R::QT + i * DK + c] * acc[jj][r];
+      }
+    mgemm<kCH, DV, kBT>([&](int m, int kk) { return scr[X::DX + m * DV + kk]; }, st, acc);
 #pragma unroll
-      for (int i = LSEG * sgm; i < LSEG * sgm + LSEG; ++i) sum += s_ag[i * SC + cl];
-      s_seg[sgm * kCH + cl] = sum;
-      __syncthreads();
-      double acc2 = 0.0;
-      for (int s2 = NSEG - 1; s2 > sgm; --s2) acc2 += s_seg[s2 * kCH + cl];
-      const double floor_mag = exp2(kLog2Floor);
+    for (int r = 0; r < 4; ++r) {
+      const int i = Own::row(r);
+      double part = 0.0;
 #pragma unroll
-      for (int i = LSEG * sgm + LSEG - 1; i >= LSEG * sgm; --i) {
-        acc2 += s_ag[i * SC + cl];
-        if (i < nt) {
-          const double a = g[row(i) * DK + cb + cl];
-          const double am = fabs(a) < floor_mag ? (a < 0.0 ? -floor_mag : floor_mag) : a;
-          dg[row(i) * DK + cb + cl] = (float)(acc2 / am);
+      for (int jj = 0; jj < T64; ++jj) {
+        const int c = cb + Own::col(jj);
+        const double gk = rec[R::GK + i * DK + c];
+        ak[jj][r] = -s_beta[i] * gam[jj][r] * acc[jj][r];
+        ag[jj][r] -= s_beta[i] * gk * acc[jj][r];
+        part -= gk * acc[jj][r];
+      }
+      add_row(s_dbp, i, part);
+    }
+  }
+  __syncthreads();
+  // dKH = U dS'^T: dk += (gamma_n / gamma) dKH; dGamma_i -= k (gamma_n/gamma) dKH,
+  // and the same amount, summed over i, goes to dGamma_n.
+  for (int p = t; p < kCH * DV; p += kBT) s_b[(p / DV) * SV + p % DV] = dSe[cb * DV + p];
+  __syncthreads();
+  // sum_j dS'[c][j] S[c][j] per channel of the block: 16 lanes per channel
+  {
+    static_assert(kCH * 16 == kBT, "16 threads per channel");
+    const int cl = t >> 4, jp = t & 15;
+    double sdot = 0.0;
+#pragma unroll 8
+    for (int j = jp; j < DV; j += 16) sdot += s_b[cl * SV + j] * Sc[(cb + cl) * DV + j];
+    sdot = sum16(sdot);
+    if (jp == 0) s_red2[cl] = sdot;
+  }
+  mgemm<kCH, DV, kBT>([&](int m, int kk) { return Uc[m * DV + kk]; },
+                      [&](int kk, int nn) { return s_b[nn * SV + kk]; }, acc);
+#pragma unroll
+  for (int jj = 0; jj < T64; ++jj) {
+    const int cl = Own::col(jj), c = cb + cl;
+    double col = 0.0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = Own::row(r);
+      const double khr = scr[X::KHR + i * DK + c];
+      const double term = rec[R::KH + i * DK + c] * acc[jj][r];
+      ak[jj][r] += khr * acc[jj][r];
+      ag[jj][r] -= term;
+      col += term;
+    }
+    col += __shfl_xor(col, 16);
+    col += __shfl_xor(col, 32);
+    if ((t & 63) < 16) s_red[(t >> 6) & 3][cl] = col;
+  }
+  __syncthreads();
+  if (t < kCH)
+    s_dGn[t] = ((s_red[0][t] + s_red[1][t]) + (s_red[2][t] + s_red[3][t])) +
+               rec[R::GN + cb + t] * s_red2[t];
+
+  // ---- the pair terms: right operands F o K, E o K, E o Q of this block
+  double *sFK = s_b, *sEK = s_b + C * SC, *sEQ = s_b + 2 * C * SC;
+  for (int p = t; p < C * kCH; p += kBT) {
+    const int i = p / kCH, cl = p % kCH, c = cb + cl;
+    const double e = scr[X::E + i * DK + c], f = scr[X::F + i * DK + c];
+    const double kh = khat(i, c), qh = qhat(i, c);
+    sFK[i * SC + cl] = f * kh;
+    sEK[i * SC + cl] = e * kh;
+    sEQ[i * SC + cl] = e * qh;
+  }
+  if (anyfb) {
+    // channels too wide for the split: the four pair terms with exp2 per pair
+    // (the sign of gamma is that of GAM, which keeps it when it underflows)
+    __syncthreads();                    // E and F of this block read by the staging
+    auto sgn = [&](int i, int c) { return copysign(1.0, scr[X::GAM + i * DK + c]); };
+    for (int cg = 0; cg < kCH; cg += kBT / C) {
+      const int c = cb + cg + t / C, i = t % C;
+      if (!s_fb[c - cb]) continue;
+      const double Gi = scr[X::G + i * DK + c], si = sgn(i, c);
+      double R1 = 0.0, R2 = 0.0, C1 = 0.0, C2 = 0.0;
+      for (int j = 0; j <= i; ++j) {
+        const double r = si * sgn(j, c) * exp2(Gi - scr[X::G + j * DK + c]);
+        const double kr = khat(j, c) * r;
+        R1 = fma(scr[X::DP + i * C + j], kr, R1);
+        R2 = fma(scr[X::DA + i * C + j], kr, R2);
+      }
+      for (int m = i; m < C; ++m) {
+        const double r = si * sgn(m, c) * exp2(scr[X::G + m * DK + c] - Gi);
+        C1 = fma(scr[X::DA + m * C + i], khat(m, c) * r, C1);
+        C2 = fma(scr[X::DP + m * C + i], qhat(m, c) * r, C2);
+      }
+      scr[X::AQ + i * DK + c] = R1;
+      scr[X::AK + i * DK + c] = R2;
+      scr[X::E + i * DK + c] = C1;
+      scr[X::F + i * DK + c] = C2;
+    }
+    __threadfence_block();
+  }
+  __syncthreads();
+  {
+    // the split factor of each owned (token, channel): e for the R terms,
+    // then f for the C terms (0 on exact-path channels)
+    double ef[T64][4];
+    auto split = [&](size_t arr) {
+#pragma unroll
+      for (int jj = 0; jj < T64; ++jj)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = Own::row(r), cl = Own::col(jj);
+          ef[jj][r] = s_fb[cl] ? 0.0 : scr[arr + i * DK + cb + cl];
+        }
+    };
+    split(X::E);
+    // R1 = E o (dP (F o K)): into dq and dGamma (+ q R1); dq is then complete
+    mgemm<kCH, C, kBT>([&](int m, int kk) { return scr[X::DP + m * C + kk]; },
+                       [&](int kk, int nn) { return sFK[kk * SC + nn]; }, acc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = Own::row(r);
+      double dqd = 0.0;
+#pragma unroll
+      for (int jj = 0; jj < T64; ++jj) {
+        const int cl = Own::col(jj), c = cb + cl;
+        double R1 = ef[jj][r] * acc[jj][r];
+        if (s_fb[cl]) R1 = scr[X::AQ + i * DK + c];      // exact-path channel
+        const double gq = aq[jj][r] + R1, qh = qhat(i, c);
+        ag[jj][r] += qh * R1;
+        if (l2norm) {
+          // the gradient with respect to the normalised row; the
+          // normalisation's Jacobian is applied once every channel is done
+          scr[X::AQ + i * DK + c] = gq;
+          dqd += qh * gq;
+        } else if (i < nt) {
+          dq[row(i) * DK + c] = (float)gq;
         }
       }
+      if (l2norm) add_row(s_qd, i, dqd);
     }
-    __syncthreads();                    // s_b free for the next block
+    // R2 = E o ((beta dA) (F o K)): into dk and dGamma (+ k R2)
+    mgemm<kCH, C, kBT>([&](int m, int kk) { return scr[X::DA + m * C + kk]; },
+                       [&](int kk, int nn) { return sFK[kk * SC + nn]; }, acc);
+#pragma unroll
+    for (int jj = 0; jj < T64; ++jj)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = Own::row(r), c = cb + Own::col(jj);
+        const double R2 = ef[jj][r] * acc[jj][r];
+        ak[jj][r] += R2;
+        ag[jj][r] += khat(i, c) * R2;
+      }
+    split(X::F);
+    // C1 = F o ((beta dA)^T (E o K)): into dk and dGamma (- k C1)
+    mgemm<kCH, C, kBT>([&](int m, int kk) { return scr[X::DA + kk * C + m]; },
+                       [&](int kk, int nn) { return sEK[kk * SC + nn]; }, acc);
+#pragma unroll
+    for (int jj = 0; jj < T64; ++jj)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = Own::row(r), c = cb + Own::col(jj);
+        const double C1 = ef[jj][r] * acc[jj][r];
+        ak[jj][r] += C1;
+        ag[jj][r] -= khat(i, c) * C1;
+      }
+    // C2 = F o (dP^T (E o Q)): into dk and dGamma (- k C2)
+    mgemm<kCH, C, kBT>([&](int m, int kk) { return scr[X::DP + kk * C + m]; },
+                       [&](int kk, int nn) { return sEQ[kk * SC + nn]; }, acc);
+    // exact-path channels, the last token's dGamma_n, and dk
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = Own::row(r);
+      double dkd = 0.0;
+#pragma unroll
+      for (int jj = 0; jj < T64; ++jj) {
+        const int cl = Own::col(jj), c = cb + cl;
+        const double kh = khat(i, c);
+        const double C2 = ef[jj][r] * acc[jj][r];
+        ak[jj][r] += C2;
+        ag[jj][r] -= kh * C2;
+        if (s_fb[cl]) {
+          const double R2 = scr[X::AK + i * DK + c];
+          const double C1 = scr[X::E + i * DK + c], C2x = scr[X::F + i * DK + c];
+          ak[jj][r] += R2 + C1 + C2x;
+          ag[jj][r] += kh * (R2 - C1 - C2x);
+        }
+        if (i == C - 1) ag[jj][r] += s_dGn[cl];
+        if (l2norm) {
+          scr[X::AK + i * DK + c] = ak[jj][r];
+          dkd += kh * ak[jj][r];
+        } else if (i < nt) {
+          dk[row(i) * DK + c] = (float)ak[jj][r];
+        }
+      }
+      if (l2norm) add_row(s_kd, i, dkd);
+    }
   }
-  __threadfence_block();   // scratch is read back by this workgroup only
+  __syncthreads();                      // every read of the staged operands done
+  // dln|alpha_s| = sum_{i >= s} dGamma_i; dalpha = dln|alpha| / alpha.
+  // NSEG segments of C / NSEG tokens per channel, then the segment offsets.
+  double *s_ag = s_b, *s_seg = s_b + C * SC;
+#pragma unroll
+  for (int jj = 0; jj < T64; ++jj)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s_ag[Own::row(r) * SC + Own::col(jj)] = ag[jj][r];
   __syncthreads();
-  if (l2norm) {
-    // x = xhat / f_x with xhat = x f_x:  dx = f_x (dxhat - xhat (xhat . dxhat))
-#pragma unroll 4
-    for (int p = t; p < nt * DK; p += kBT) {
-      const int i = p / DK, c = p % DK;
-      const double qh = to_f32(q[row(i) * DK + c]) * s_fq[i];
-      const double kh = to_f32(k[row(i) * DK + c]) * s_fk[i];
-      const double qd = s_qd[0][i] + s_qd[1][i], kd = s_kd[0][i] + s_kd[1][i];
-      dq[row(i) * DK + c] = (float)(s_fq[i] * (scr[X::AQ + p] - qh * qd));
-      dk[row(i) * DK + c] = (float)(s_fk[i] * (scr[X::AK + p] - kh * kd));
+  {
+    const int cl = t % kCH, sgm = t / kCH;
+    double sum = 0.0;
+#pragma unroll
+    for (int i = LSEG * sgm; i < LSEG * sgm + LSEG; ++i) sum += s_ag[i * SC + cl];
+    s_seg[sgm * kCH + cl] = sum;
+    __syncthreads();
+    double acc2 = 0.0;
+    for (int s2 = NSEG - 1; s2 > sgm; --s2) acc2 += s_seg[s2 * kCH + cl];
+    const double floor_mag = exp2(kLog2Floor);
+#pragma unroll
+    for (int i = LSEG * sgm + LSEG - 1; i >= LSEG * sgm; --i) {
+      acc2 += s_ag[i * SC + cl];
+      if (i < nt) {
+        const double a = g[row(i) * DK + cb + cl];
+        const double am = fabs(a) < floor_mag ? (a < 0.0 ? -floor_mag : floor_mag) : a;
+        dg[row(i) * DK + cb + cl] = (float)(acc2 / am);
+      }
     }
   }
-  if (t < nt) dbeta[row(t)] = (float)(s_dbp[0][t] + s_dbp[1][t]);
+  // this block's parts of dbeta and of the normalisation dots
+  if (t < C) {
+    scr[X::DB + (1 + blk) * C + t] = s_dbp[0][t] + s_dbp[1][t];
+    scr[X::QD + blk * C + t] = s_qd[0][t] + s_qd[1][t];
+    scr[X::KD + blk * C + t] = s_kd[0][t] + s_kd[1][t];
+  }
+}
+
+// --------------------------------------------------------------------------
+// dbeta (the prep kernel's part plus every channel block's, in a fixed
+// order) and, with q/k normalisation, dx = f_x (dxhat - xhat (xhat . dxhat)).
+constexpr int kFT = 256;
+
+template <typename TIn, int DK, int DV>
+__global__ __launch_bounds__(kFT) void f64_bwd_final(
+    const TIn *__restrict__ q, const TIn *__restrict__ k, int H, int N, SeqTable tab,
+    const double *__restrict__ scratch, float *__restrict__ dq, float *__restrict__ dk,
+    float *__restrict__ dbeta, int l2norm) {
+  using X = Scr<DK, DV>;
+  constexpr int NB = X::NB;
+  __shared__ double s_qd[C], s_kd[C], s_fq[C], s_fk[C];
+  const int cflat = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+  if (cflat >= tab.chunk_off[N]) return;
+  const int n = find_seq(tab.chunk_off, N, cflat);
+  const int lc = cflat - tab.chunk_off[n];
+  const int t0 = tab.seq_start[n] + lc * C;
+  const int nt = min(C, tab.seq_len[n] - lc * C);
+  const double *scr = scratch + ((size_t)cflat * H + h) * X::SIZE;
+  auto row = [&](int i) { return (size_t)(t0 + i) * H + h; };
+  if (t < nt) {
+    double db = 0.0, qd = 0.0, kd = 0.0;
+#pragma unroll
+    for (int b = 0; b <= NB; ++b) db += scr[X::DB + b * C + t];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      qd += scr[X::QD + b * C + t];
+      kd += scr[X::KD + b * C + t];
+    }
+    dbeta[row(t)] = (float)db;
+    s_qd[t] = qd;
+    s_kd[t] = kd;
+    s_fq[t] = scr[X::FQ + t];
+    s_fk[t] = scr[X::FK + t];
+  }
+  if (!l2norm) return;                  // uniform across the block
+  __syncthreads();
+#pragma unroll 4
+  for (int p = t; p < nt * DK; p += kFT) {
+    const int i = p / DK, c = p % DK;
+    const double qh = to_f32(q[row(i) * DK + c]) * s_fq[i];
+    const double kh = to_f32(k[row(i) * DK + c]) * s_fk[i];
+    dq[row(i) * DK + c] = (float)(s_fq[i] * (scr[X::AQ + p] - qh * s_qd[i]));
+    dk[row(i) * DK + c] = (float)(s_fk[i] * (scr[X::AK + p] - kh * s_kd[i]));
+  }
 }
 
 template <typename TIn, int DK, int DV>
@@ -664,22 +744,35 @@ hipError_t launch_bwd_shape(const void *q, const void *k, const void *v, const f
                             float *dk, float *dv, float *dg, float *dbeta, float *dS0,
                             int signed_gates, int l2norm, hipStream_t stream) {
   const size_t rec_doubles = rec_bytes / sizeof(double);
+  const TIn *tq = static_cast<const TIn *>(q), *tk = static_cast<const TIn *>(k);
   hipLaunchKernelGGL((f64_bwd_state<DK, DV>), dim3((DV / kBV) * N * H), dim3(kThreads), 0, stream,
                      dO, dS_T, H, N, tab, records, rec_doubles, dU_chunks, dSe_chunks, dS0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_chunks_ub == 0) return e;
-  hipLaunchKernelGGL((f64_bwd_chunk<TIn, DK, DV>), dim3((unsigned)n_chunks_ub, H), dim3(kBT),
-                     0, stream, static_cast<const TIn *>(q), static_cast<const TIn *>(k),
-                     static_cast<const TIn *>(v), g, beta, dO, H, N, tab, records, rec_doubles,
-                     S_chunks, U_chunks, dU_chunks, dSe_chunks, scratch, dq, dk, dv, dg, dbeta,
-                     signed_gates, l2norm);
+  hipLaunchKernelGGL((f64_bwd_prep<TIn, DK, DV>), dim3((unsigned)n_chunks_ub, H), dim3(kBT), 0,
+                     stream, tq, tk, static_cast<const TIn *>(v), g, beta, dO, H, N, tab,
+                     records, rec_doubles, U_chunks, dU_chunks, scratch, dv, signed_gates, l2norm);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // (channel block, chunk, head) workgroups, eight chunk-heads per XCD round
+  const size_t n_ch = n_chunks_ub * (size_t)H;
+  const size_t n_wg = (n_ch + 7) / 8 * 8 * (DK / kCH);
+  hipLaunchKernelGGL((f64_bwd_pairs<TIn, DK, DV>), dim3((unsigned)n_wg), dim3(kBT), 0, stream,
+                     tq, tk, g, beta, dO, H, N, tab, records, rec_doubles, S_chunks, U_chunks,
+                     dSe_chunks, scratch, n_ch, dq, dk, dg, l2norm);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((f64_bwd_final<TIn, DK, DV>), dim3((unsigned)n_chunks_ub, H), dim3(kFT), 0,
+                     stream, tq, tk, H, N, tab, scratch, dq, dk, dbeta, l2norm);
   return hipGetLastError();
 }
 
 }  // namespace
 
 size_t f64_bwd_scratch_bytes(int dk, int dv) {
-  return sizeof(double) * ((size_t)C * dv + 7 * (size_t)C * dk);
+  const size_t nb = (size_t)dk / kCH;
+  return sizeof(double) * ((size_t)C * dv + 7 * (size_t)C * dk + 2 * (size_t)C * C + dk +
+                           2 * (size_t)C + (1 + 3 * nb) * (size_t)C);
 }
 
 hipError_t launch_bwd_f64(const void *q, const void *k, const void *v, const float *g,
