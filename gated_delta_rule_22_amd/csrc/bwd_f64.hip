@@ -204,10 +204,10 @@ __global__ __launch_bounds__(kBT) void f64_bwd_prep(
   using OwnC = MOwn<C, kBT>;               // C x C results
   constexpr int TV = OwnV::TPW, TC = OwnC::TPW;
   constexpr int SV = DV + 1;               // padded LDS row
-  constexpr int kB0 = C * DK + C * DK / 2;
-  constexpr int kPool = kB0 > C * SV ? kB0 : C * SV;
-  // one LDS pool: the phase-0 gates, later the staged right operands
+  constexpr int kPool = C * DK > C * SV ? C * DK : C * SV;
+  // one LDS pool: the phase-0 log-gates, later the staged right operands
   __shared__ double s_b[kPool];
+  __shared__ int8_t s_sg[C * DK];         // the gates' signs, then the sign of gamma
   __shared__ double s_beta[C], s_dbp[2][C];
   __shared__ double s_R[DK], s_sig[DK];
   __shared__ int s_fb[DK];
@@ -231,12 +231,11 @@ __global__ __launch_bounds__(kBT) void f64_bwd_prep(
   // every (token, channel) in parallel into LDS (the sign rides in a float
   // copy of alpha), then the scans per channel.
   double *s_l = s_b;                                    // [C][DK] log2|alpha|
-  float *s_sg = reinterpret_cast<float *>(s_b + C * DK);  // [C][DK] alpha (sign only)
 #pragma unroll 4
   for (int p = t; p < C * DK; p += kBT) {
     const float a = p / DK < nt ? g[row(p / DK) * DK + p % DK] : 1.f;
     s_l[p] = fmax(log2(fabs((double)a)), kLog2Floor);
-    s_sg[p] = a;
+    s_sg[p] = (signed_gates && a < 0.f) ? -1 : 1;   // KDA mode: signs ignored
   }
   __syncthreads();
   if (t < DK) {
@@ -245,13 +244,12 @@ __global__ __launch_bounds__(kBT) void f64_bwd_prep(
     bool par = false;
 #pragma unroll 8
     for (int i = 0; i < C; ++i) {
-      const float a = s_sg[i * DK + t];
+      par ^= s_sg[i * DK + t] < 0;
       G += s_l[i * DK + t];
-      par ^= (signed_gates && a < 0.f);   // KDA mode: signs ignored
       gmax = fmax(gmax, G);
       gmin = fmin(gmin, G);
       s_l[i * DK + t] = G;
-      s_sg[i * DK + t] = par ? -1.f : 1.f;
+      s_sg[i * DK + t] = par ? -1 : 1;
     }
     // r_ij = e_i f_j with e = sign 2^(G - Rm), f = sign 2^(Rm - G) about the
     // midpoint Rm of the channel's range; beyond +-1000 binary orders that
