@@ -70,15 +70,24 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_state(
     const int c = p / kBV, j = p % kBV;
     s_dS[p] = dS_T ? (double)dS_T[sbase + (size_t)c * DV + j] : 0.0;
   }
+  // dO of a chunk is loaded into registers one chunk ahead of its use
+  constexpr int NO = C * kBV / kThreads;
+  float pre[NO];
+  auto load_do = [&](int lc) {
+    const int nt = min(C, len - lc * C);
+#pragma unroll
+    for (int u = 0; u < NO; ++u) {
+      const int p = t + u * kThreads, i = p / kBV, j = p % kBV;
+      pre[u] = i < nt ? dO[((size_t)(start + lc * C + i) * H + h) * DV + jb * kBV + j] : 0.f;
+    }
+  };
+  if (nch > 0) load_do(nch - 1);
   for (int lc = nch - 1; lc >= 0; --lc) {
     const size_t ch = (size_t)(tab.chunk_off[n] + lc) * H + h;
     const double *rec = records + ch * rec_doubles;
-    const int nt = min(C, len - lc * C);
-    for (int p = t; p < C * kBV; p += kThreads) {
-      const int i = p / kBV, j = p % kBV;
-      s_dO[p] = i < nt ? (double)dO[((size_t)(start + lc * C + i) * H + h) * DV + jb * kBV + j]
-                       : 0.0;
-    }
+#pragma unroll
+    for (int u = 0; u < NO; ++u) s_dO[t + u * kThreads] = (double)pre[u];
+    if (lc > 0) load_do(lc - 1);
     __syncthreads();         // dS' and dO complete
     for (int p = t; p < DK * kBV; p += kThreads)
       dSe_chunks[ch * DK * DV + (size_t)(p / kBV) * DV + jb * kBV + p % kBV] = s_dS[p];
