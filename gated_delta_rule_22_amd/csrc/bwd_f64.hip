@@ -85,6 +85,19 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_state(
   for (int lc = nch - 1; lc >= 0; --lc) {
     const size_t ch = (size_t)(tab.chunk_off[n] + lc) * H + h;
     const double *rec = records + ch * rec_doubles;
+    // the left operands are records, independent of the state gradient: the
+    // first slices of each product are issued ahead of the barrier before it
+    auto fa_u = [&](int m, int kk) {
+      return kk < DK ? rec[R::KH + m * DK + kk] : rec[R::P + (kk - DK) * C + m];
+    };
+    auto fa_s = [&](int half) {
+      return [&, half](int m, int kk) {
+        return kk < C ? rec[R::QT + kk * DK + half * 64 + m]
+                      : -rec[R::W + (kk - C) * DK + half * 64 + m];
+      };
+    };
+    ARing<> ring_u, ring_s[DK / 64];
+    mgemm_start(fa_u, ring_u);
 #pragma unroll
     for (int u = 0; u < NO; ++u) s_dO[t + u * kThreads] = (double)pre[u];
     if (lc > 0) load_do(lc - 1);
@@ -94,14 +107,13 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_state(
     // dU = KH dS' + P^T dO, as one product over [dS'; dO]
     {
       d4 acc[TPW];
-      mgemm<kBV, DK + C>(
-          [&](int m, int kk) {
-            return kk < DK ? rec[R::KH + m * DK + kk] : rec[R::P + (kk - DK) * C + m];
-          },
+      mgemm_run<kBV, DK + C>(
+          fa_u,
           [&](int kk, int nn) {
             return kk < DK ? s_dS[kk * kBV + nn] : s_dO[(kk - DK) * kBV + nn];
           },
-          acc);
+          ring_u, acc);
+      mgemm_start(fa_s(0), ring_s[0]);
 #pragma unroll
       for (int jj = 0; jj < TPW; ++jj)
 #pragma unroll
@@ -117,13 +129,11 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_state(
 #pragma unroll
     for (int half = 0; half < DK / 64; ++half) {
       d4 acc[TPW];
-      mgemm<kBV, 2 * C>(
-          [&](int m, int kk) {
-            return kk < C ? rec[R::QT + kk * DK + half * 64 + m]
-                          : -rec[R::W + (kk - C) * DK + half * 64 + m];
-          },
+      mgemm_run<kBV, 2 * C>(
+          fa_s(half),
           [&](int kk, int nn) { return kk < C ? s_dO[kk * kBV + nn] : s_dU[(kk - C) * kBV + nn]; },
-          acc);
+          ring_s[half], acc);
+      if (half + 1 < DK / 64) mgemm_start(fa_s(half + 1), ring_s[half + 1]);
 #pragma unroll
       for (int jj = 0; jj < TPW; ++jj)
 #pragma unroll

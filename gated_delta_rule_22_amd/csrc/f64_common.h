@@ -57,10 +57,30 @@ struct MOwn {
   }
 };
 
+// The left operand's slices in flight: mgemm_start issues the first PF of
+// them, mgemm_run multiplies.  A kernel may call mgemm_start early (before a
+// barrier, or before the previous product's epilogue) when the left operand
+// does not depend on what happens in between.
+template <int PF = 3>
+struct ARing {
+  double r[PF + 1][4];
+};
+
+template <int PF = 3, typename FA>
+__device__ __forceinline__ void mgemm_start(const FA &fa, ARing<PF> &ring) {
+  const int l = threadIdx.x & 63;
+  const int m = 16 * ((threadIdx.x >> 6) & 3) + (l & 15);
+  const int kq = 4 * (l >> 4);
+#pragma unroll
+  for (int b = 0; b < PF; ++b)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ring.r[b][q] = fa(m, 16 * b + kq + q);
+}
+
 template <int NB, int K, int NT = kThreads, int PF = 3, bool ZERO = true, typename FA,
           typename FB>
-__device__ __forceinline__ void mgemm(const FA &fa, const FB &fb,
-                                      d4 (&acc)[MOwn<NB, NT>::TPW]) {
+__device__ __forceinline__ void mgemm_run(const FA &fa, const FB &fb, ARing<PF> &ring,
+                                          d4 (&acc)[MOwn<NB, NT>::TPW]) {
   constexpr int TPW = MOwn<NB, NT>::TPW;
   constexpr int NS = K / 16;              // K-slices
   constexpr int RING = PF + 1;            // A-operand slices held in registers
@@ -69,7 +89,6 @@ __device__ __forceinline__ void mgemm(const FA &fa, const FB &fb,
   const int m = 16 * ((threadIdx.x >> 6) & 3) + (l & 15);
   const int n0 = 16 * ((threadIdx.x >> 8) * TPW) + (l & 15);
   const int kq = 4 * (l >> 4);
-  double ra[RING][4];
   auto load = [&](int s, double (&a)[4]) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) a[q] = fa(m, 16 * s + kq + q);
@@ -78,15 +97,13 @@ __device__ __forceinline__ void mgemm(const FA &fa, const FB &fb,
 #pragma unroll
     for (int jj = 0; jj < TPW; ++jj) acc[jj] = d4{0.0, 0.0, 0.0, 0.0};
   }
-#pragma unroll
-  for (int b = 0; b < PF; ++b) load(b, ra[b]);
   // A's slice s is loaded PF slices before it is multiplied; B is read from
   // LDS as it is used
 #pragma unroll 1
   for (int s0 = 0; s0 < NS; s0 += RING) {
 #pragma unroll
     for (int b = 0; b < RING; ++b) {
-      if (s0 + b + PF < NS) load(s0 + b + PF, ra[(b + PF) % RING]);
+      if (s0 + b + PF < NS) load(s0 + b + PF, ring.r[(b + PF) % RING]);
       double rb[4][TPW];
 #pragma unroll
       for (int q = 0; q < 4; ++q)
@@ -96,9 +113,19 @@ __device__ __forceinline__ void mgemm(const FA &fa, const FB &fb,
       for (int q = 0; q < 4; ++q)
 #pragma unroll
         for (int jj = 0; jj < TPW; ++jj)
-          acc[jj] = __builtin_amdgcn_mfma_f64_16x16x4f64(ra[b][q], rb[q][jj], acc[jj], 0, 0, 0);
+          acc[jj] =
+              __builtin_amdgcn_mfma_f64_16x16x4f64(ring.r[b][q], rb[q][jj], acc[jj], 0, 0, 0);
     }
   }
+}
+
+template <int NB, int K, int NT = kThreads, int PF = 3, bool ZERO = true, typename FA,
+          typename FB>
+__device__ __forceinline__ void mgemm(const FA &fa, const FB &fb,
+                                      d4 (&acc)[MOwn<NB, NT>::TPW]) {
+  ARing<PF> ring;
+  mgemm_start<PF>(fa, ring);
+  mgemm_run<NB, K, NT, PF, ZERO>(fa, fb, ring, acc);
 }
 
 // Sum over 16 consecutive lanes (16 g .. 16 g + 15): the lanes that hold one

@@ -322,14 +322,28 @@ __global__ __launch_bounds__(kThreads) void f64_inter(
     const size_t ch = (size_t)(tab.chunk_off[n] + lc) * H + h;
     const double *rec = records + ch * rec_doubles;
     const int nt = min(C, len - lc * C);
+    // the left operands are records, independent of the state: the first
+    // slices of each product are issued ahead of the work before it
+    auto fa_w = [&](int m, int kk) { return rec[R::W + m * DK + kk]; };
+    auto fa_o = [&](int m, int kk) {
+      return kk < DK ? rec[R::QT + m * DK + kk] : rec[R::P + m * C + kk - DK];
+    };
+    auto fa_k = [&](int half) {
+      return [&, half](int m, int kk) { return rec[R::KH + kk * DK + half * 64 + m]; };
+    };
+    ARing<> ring_w, ring_o, ring_k[DK / 64];
+    mgemm_start(fa_w, ring_w);
     if (S_chunks)
       for (int p = t; p < DK * kBV; p += kThreads)
         S_chunks[ch * DK * DV + (size_t)(p / kBV) * DV + jb * kBV + p % kBV] = s_S[p];
     // U = Ubar - W S
     {
       d4 acc[TPW];
-      mgemm<kBV, DK>([&](int m, int kk) { return rec[R::W + m * DK + kk]; },
-                     [&](int kk, int nn) { return s_S[kk * kBV + nn]; }, acc);
+      mgemm_run<kBV, DK>(fa_w, [&](int kk, int nn) { return s_S[kk * kBV + nn]; }, ring_w, acc);
+      if (o)
+        mgemm_start(fa_o, ring_o);
+      else
+        mgemm_start(fa_k(0), ring_k[0]);
 #pragma unroll
       for (int jj = 0; jj < TPW; ++jj)
 #pragma unroll
@@ -344,12 +358,11 @@ __global__ __launch_bounds__(kThreads) void f64_inter(
     // O = (gamma Q) S + P U, as one product over [S; U]
     if (o) {
       d4 acc[TPW];
-      mgemm<kBV, DK + C>(
-          [&](int m, int kk) {
-            return kk < DK ? rec[R::QT + m * DK + kk] : rec[R::P + m * C + kk - DK];
-          },
+      mgemm_run<kBV, DK + C>(
+          fa_o,
           [&](int kk, int nn) { return kk < DK ? s_S[kk * kBV + nn] : s_U[(kk - DK) * kBV + nn]; },
-          acc);
+          ring_o, acc);
+      mgemm_start(fa_k(0), ring_k[0]);
 #pragma unroll
       for (int jj = 0; jj < TPW; ++jj)
 #pragma unroll
@@ -369,8 +382,9 @@ __global__ __launch_bounds__(kThreads) void f64_inter(
 #pragma unroll
     for (int half = 0; half < DK / 64; ++half) {
       d4 acc[TPW];
-      mgemm<kBV, C>([&](int m, int kk) { return rec[R::KH + kk * DK + half * 64 + m]; },
-                    [&](int kk, int nn) { return s_U[kk * kBV + nn]; }, acc);
+      mgemm_run<kBV, C>(fa_k(half), [&](int kk, int nn) { return s_U[kk * kBV + nn]; },
+                        ring_k[half], acc);
+      if (half + 1 < DK / 64) mgemm_start(fa_k(half + 1), ring_k[half + 1]);
 #pragma unroll
       for (int jj = 0; jj < TPW; ++jj)
 #pragma unroll
