@@ -32,10 +32,10 @@
 //   f64_bwd_state  grid (dv blocks x sequences x heads): the reverse serial
 //              pass over chunks for dS, writing dU and dS' of every chunk and
 //              dS0;
-//   f64_bwd_chunk  grid (chunks, heads): everything else, one chunk per
-//              workgroup, with the dense products as LDS-staged block products
-//              (f64_common.h) and the ratio-weighted pair sums channel group by
-//              channel group.
+//   f64_bwd_prep, f64_bwd_pairs, f64_bwd_final  everything else, per chunk
+//              (the pair kernel per 32-channel block of a chunk), with every
+//              contraction on the fp64 matrix cores (f64_common.h) and the
+//              ratio-weighted pair sums as dense products (see below).
 #include "f64_common.h"
 
 namespace ckda {
