@@ -413,9 +413,13 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
   constexpr int NB = X::NB;
   constexpr int SV = DV + 1, SC = kCH + 1;  // padded LDS rows
   constexpr int NSEG = kBT / kCH, LSEG = C / NSEG;
+  // the direct-term products stream their left operands from global memory:
+  // seven K-slices of prefetch where K allows
+  constexpr int PFD = DV % 128 == 0 ? 7 : 3;
   constexpr int kB = kCH * SV > 3 * C * SC ? kCH * SV : 3 * C * SC;
   static_assert(kB >= C * SC + NSEG * kCH, "room for the cumulative sum");
   __shared__ double s_b[kB];              // staged right operands | dGamma
+  __shared__ double s_P[C * (C + 1)], s_DA[C * (C + 1)];   // dP and beta dA, padded rows
   __shared__ double s_beta[C], s_dbp[2][C], s_kd[2][C], s_qd[2][C];
   __shared__ double s_fk[C], s_fq[C];
   __shared__ double s_red[4][kCH], s_red2[kCH], s_dGn[kCH];
@@ -456,8 +460,19 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
   }
   const bool fbc = t < kCH && scr[X::FB + cb + t] != 0.0;
   if (t < kCH) s_fb[t] = fbc;
-  // the direct terms: S^T of this block staged (also a barrier for the above)
+  // the left operands of the direct-term products stream from global memory:
+  // each product's first slices are issued ahead of the work before it
+  auto fa_dx = [&](int m, int kk) { return scr[X::DX + m * DV + kk]; };
+  auto fa_u = [&](int m, int kk) { return Uc[m * DV + kk]; };
+  ARing<PFD> ring;
+  mgemm_start(dO_at, ring);
+  // S^T of this block, and dP and beta dA for the pair terms, into LDS (the
+  // barrier also covers the per-token values above)
   for (int p = t; p < kCH * DV; p += kBT) s_b[(p / DV) * SV + p % DV] = Sc[cb * DV + p];
+  for (int p = t; p < C * C; p += kBT) {
+    s_P[(p / C) * (C + 1) + p % C] = scr[X::DP + p];
+    s_DA[(p / C) * (C + 1) + p % C] = scr[X::DA + p];
+  }
   const int anyfb = __syncthreads_or(fbc);
 
   double aq[T64][4], ak[T64][4], ag[T64][4];
@@ -467,7 +482,8 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
   {
     auto st = [&](int kk, int nn) { return s_b[nn * SV + kk]; };   // S^T (this block)
     double gam[T64][4];
-    mgemm<kCH, DV, kBT>(dO_at, st, acc);
+    mgemm_run<kCH, DV, kBT, PFD>(dO_at, st, ring, acc);
+    mgemm_start(fa_dx, ring);
 #pragma unroll
     for (int jj = 0; jj < T64; ++jj)
 #pragma unroll
@@ -477,7 +493,8 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
         aq[jj][r] = gam[jj][r] * acc[jj][r];
         ag[jj][r] = rec[R::QT + i * DK + c] * acc[jj][r];
       }
-    mgemm<kCH, DV, kBT>([&](int m, int kk) { return scr[X::DX + m * DV + kk]; }, st, acc);
+    mgemm_run<kCH, DV, kBT, PFD>(fa_dx, st, ring, acc);
+    mgemm_start(fa_u, ring);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = Own::row(r);
@@ -508,8 +525,8 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
     sdot = sum16(sdot);
     if (jp == 0) s_red2[cl] = sdot;
   }
-  mgemm<kCH, DV, kBT>([&](int m, int kk) { return Uc[m * DV + kk]; },
-                      [&](int kk, int nn) { return s_b[nn * SV + kk]; }, acc);
+  mgemm_run<kCH, DV, kBT, PFD>(fa_u, [&](int kk, int nn) { return s_b[nn * SV + kk]; }, ring,
+                               acc);
 #pragma unroll
   for (int jj = 0; jj < T64; ++jj) {
     const int cl = Own::col(jj), c = cb + cl;
@@ -555,13 +572,13 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
       for (int j = 0; j <= i; ++j) {
         const double r = si * sgn(j, c) * exp2(Gi - scr[X::G + j * DK + c]);
         const double kr = khat(j, c) * r;
-        R1 = fma(scr[X::DP + i * C + j], kr, R1);
-        R2 = fma(scr[X::DA + i * C + j], kr, R2);
+        R1 = fma(s_P[i * (C + 1) + j], kr, R1);
+        R2 = fma(s_DA[i * (C + 1) + j], kr, R2);
       }
       for (int m = i; m < C; ++m) {
         const double r = si * sgn(m, c) * exp2(scr[X::G + m * DK + c] - Gi);
-        C1 = fma(scr[X::DA + m * C + i], khat(m, c) * r, C1);
-        C2 = fma(scr[X::DP + m * C + i], qhat(m, c) * r, C2);
+        C1 = fma(s_DA[m * (C + 1) + i], khat(m, c) * r, C1);
+        C2 = fma(s_P[m * (C + 1) + i], qhat(m, c) * r, C2);
       }
       scr[X::AQ + i * DK + c] = R1;
       scr[X::AK + i * DK + c] = R2;
@@ -586,7 +603,7 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
     };
     split(X::E);
     // R1 = E o (dP (F o K)): into dq and dGamma (+ q R1); dq is then complete
-    mgemm<kCH, C, kBT>([&](int m, int kk) { return scr[X::DP + m * C + kk]; },
+    mgemm<kCH, C, kBT, 1>([&](int m, int kk) { return s_P[m * (C + 1) + kk]; },
                        [&](int kk, int nn) { return sFK[kk * SC + nn]; }, acc);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -611,7 +628,7 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
       if (l2norm) add_row(s_qd, i, dqd);
     }
     // R2 = E o ((beta dA) (F o K)): into dk and dGamma (+ k R2)
-    mgemm<kCH, C, kBT>([&](int m, int kk) { return scr[X::DA + m * C + kk]; },
+    mgemm<kCH, C, kBT, 1>([&](int m, int kk) { return s_DA[m * (C + 1) + kk]; },
                        [&](int kk, int nn) { return sFK[kk * SC + nn]; }, acc);
 #pragma unroll
     for (int jj = 0; jj < T64; ++jj)
@@ -624,7 +641,7 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
       }
     split(X::F);
     // C1 = F o ((beta dA)^T (E o K)): into dk and dGamma (- k C1)
-    mgemm<kCH, C, kBT>([&](int m, int kk) { return scr[X::DA + kk * C + m]; },
+    mgemm<kCH, C, kBT, 1>([&](int m, int kk) { return s_DA[kk * (C + 1) + m]; },
                        [&](int kk, int nn) { return sEK[kk * SC + nn]; }, acc);
 #pragma unroll
     for (int jj = 0; jj < T64; ++jj)
@@ -636,7 +653,7 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
         ag[jj][r] -= khat(i, c) * C1;
       }
     // C2 = F o (dP^T (E o Q)): into dk and dGamma (- k C2)
-    mgemm<kCH, C, kBT>([&](int m, int kk) { return scr[X::DP + kk * C + m]; },
+    mgemm<kCH, C, kBT, 1>([&](int m, int kk) { return s_P[kk * (C + 1) + m]; },
                        [&](int kk, int nn) { return sEQ[kk * SC + nn]; }, acc);
     // exact-path channels, the last token's dGamma_n, and dk
 #pragma unroll

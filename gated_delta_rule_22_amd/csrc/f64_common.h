@@ -33,7 +33,7 @@ struct Rec {
 // Out(m, n) = sum_{kk < K} A(m, kk) B(kk, n) for m < 64, n < NB, by NT (256
 // or 512) threads, with no LDS staging and no barrier inside: fa and fb are
 // called in the instruction's operand layout, fa (typically global memory)
-// PF 16-deep K-slices ahead of the multiply, fb (typically LDS) as it is used.  The output is cut into 16 x 16
+// PF 16-deep K-slices ahead of the multiply, fb (typically LDS) one slice ahead.  The output is cut into 16 x 16
 // tiles; wave w takes row block w % 4 and column blocks (w / 4) TPW + jj
 // (jj < TPW).  The caller reads its results through MOwn: accumulator
 // element acc[jj][r] is Out(MOwn::row(r), MOwn::col(jj)).  Operand layout of
@@ -85,6 +85,7 @@ __device__ __forceinline__ void mgemm_run(const FA &fa, const FB &fb, ARing<PF> 
   constexpr int NS = K / 16;              // K-slices
   constexpr int RING = PF + 1;            // A-operand slices held in registers
   static_assert(K % 16 == 0 && NS % RING == 0, "K must be a multiple of 16 (PF + 1)");
+  static_assert(RING % 2 == 0, "B's two-slice rotation is indexed by the slice's parity");
   const int l = threadIdx.x & 63;
   const int m = 16 * ((threadIdx.x >> 6) & 3) + (l & 15);
   const int n0 = 16 * ((threadIdx.x >> 8) * TPW) + (l & 15);
@@ -97,24 +98,28 @@ __device__ __forceinline__ void mgemm_run(const FA &fa, const FB &fb, ARing<PF> 
 #pragma unroll
     for (int jj = 0; jj < TPW; ++jj) acc[jj] = d4{0.0, 0.0, 0.0, 0.0};
   }
-  // A's slice s is loaded PF slices before it is multiplied; B is read from
-  // LDS as it is used
+  // A's slice s is loaded PF slices before it is multiplied, B's one slice
+  // before (B is typically in LDS)
+  double rb[2][4][TPW];
+  auto loadb = [&](int s, double (&bb)[4][TPW]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int jj = 0; jj < TPW; ++jj) bb[q][jj] = fb(16 * s + kq + q, n0 + 16 * jj);
+  };
+  loadb(0, rb[0]);
 #pragma unroll 1
   for (int s0 = 0; s0 < NS; s0 += RING) {
 #pragma unroll
     for (int b = 0; b < RING; ++b) {
       if (s0 + b + PF < NS) load(s0 + b + PF, ring.r[(b + PF) % RING]);
-      double rb[4][TPW];
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int jj = 0; jj < TPW; ++jj) rb[q][jj] = fb(16 * (s0 + b) + kq + q, n0 + 16 * jj);
+      if (s0 + b + 1 < NS) loadb(s0 + b + 1, rb[(b + 1) & 1]);
 #pragma unroll
       for (int q = 0; q < 4; ++q)
 #pragma unroll
         for (int jj = 0; jj < TPW; ++jj)
-          acc[jj] =
-              __builtin_amdgcn_mfma_f64_16x16x4f64(ring.r[b][q], rb[q][jj], acc[jj], 0, 0, 0);
+          acc[jj] = __builtin_amdgcn_mfma_f64_16x16x4f64(ring.r[b][q], rb[b & 1][q][jj], acc[jj],
+                                                         0, 0, 0);
     }
   }
 }
