@@ -481,17 +481,25 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
   // d(gamma K) = -Diag(beta) M5.
   {
     auto st = [&](int kk, int nn) { return s_b[nn * SV + kk]; };   // S^T (this block)
-    double gam[T64][4];
-    mgemm_run<kCH, DV, kBT, PFD>(dO_at, st, ring, acc);
-    mgemm_start(fa_dx, ring);
+    // the epilogue's per-element factors are loaded before the product
+    double gam[T64][4], qt[T64][4];
 #pragma unroll
     for (int jj = 0; jj < T64; ++jj)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = Own::row(r), c = cb + Own::col(jj);
         gam[jj][r] = scr[X::GAM + i * DK + c];
+        qt[jj][r] = rec[R::QT + i * DK + c];
+      }
+    mgemm_run<kCH, DV, kBT, PFD>(dO_at, st, ring, acc);
+    mgemm_start(fa_dx, ring);
+#pragma unroll
+    for (int jj = 0; jj < T64; ++jj)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
         aq[jj][r] = gam[jj][r] * acc[jj][r];
-        ag[jj][r] = rec[R::QT + i * DK + c] * acc[jj][r];
+        ag[jj][r] = qt[jj][r] * acc[jj][r];
+        qt[jj][r] = rec[R::GK + Own::row(r) * DK + cb + Own::col(jj)];   // now gamma K
       }
     mgemm_run<kCH, DV, kBT, PFD>(fa_dx, st, ring, acc);
     mgemm_start(fa_u, ring);
@@ -501,8 +509,7 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
       double part = 0.0;
 #pragma unroll
       for (int jj = 0; jj < T64; ++jj) {
-        const int c = cb + Own::col(jj);
-        const double gk = rec[R::GK + i * DK + c];
+        const double gk = qt[jj][r];
         ak[jj][r] = -s_beta[i] * gam[jj][r] * acc[jj][r];
         ag[jj][r] -= s_beta[i] * gk * acc[jj][r];
         part -= gk * acc[jj][r];
@@ -525,18 +532,26 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
     sdot = sum16(sdot);
     if (jp == 0) s_red2[cl] = sdot;
   }
+  double khr[T64][4], khd[T64][4];       // gamma_n / gamma and K_hat, loaded early
+#pragma unroll
+  for (int jj = 0; jj < T64; ++jj)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = Own::row(r), c = cb + Own::col(jj);
+      khr[jj][r] = scr[X::KHR + i * DK + c];
+      khd[jj][r] = rec[R::KH + i * DK + c];
+    }
   mgemm_run<kCH, DV, kBT, PFD>(fa_u, [&](int kk, int nn) { return s_b[nn * SV + kk]; }, ring,
                                acc);
 #pragma unroll
   for (int jj = 0; jj < T64; ++jj) {
-    const int cl = Own::col(jj), c = cb + cl;
+    const int cl = Own::col(jj);
     double col = 0.0;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int i = Own::row(r);
-      const double khr = scr[X::KHR + i * DK + c];
-      const double term = rec[R::KH + i * DK + c] * acc[jj][r];
-      ak[jj][r] += khr * acc[jj][r];
+      const double term = khd[jj][r] * acc[jj][r];
+      const double kr = khr[jj][r];
+      ak[jj][r] += kr * acc[jj][r];
       ag[jj][r] -= term;
       col += term;
     }
@@ -591,7 +606,15 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
   {
     // the split factor of each owned (token, channel): e for the R terms,
     // then f for the C terms (0 on exact-path channels)
-    double ef[T64][4];
+    double ef[T64][4], kh[T64][4], qh[T64][4];
+#pragma unroll
+    for (int jj = 0; jj < T64; ++jj)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = Own::row(r), c = cb + Own::col(jj);
+        kh[jj][r] = khat(i, c);
+        qh[jj][r] = qhat(i, c);
+      }
     auto split = [&](size_t arr) {
 #pragma unroll
       for (int jj = 0; jj < T64; ++jj)
@@ -614,13 +637,13 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
         const int cl = Own::col(jj), c = cb + cl;
         double R1 = ef[jj][r] * acc[jj][r];
         if (s_fb[cl]) R1 = scr[X::AQ + i * DK + c];      // exact-path channel
-        const double gq = aq[jj][r] + R1, qh = qhat(i, c);
-        ag[jj][r] += qh * R1;
+        const double gq = aq[jj][r] + R1;
+        ag[jj][r] += qh[jj][r] * R1;
         if (l2norm) {
           // the gradient with respect to the normalised row; the
           // normalisation's Jacobian is applied once every channel is done
           scr[X::AQ + i * DK + c] = gq;
-          dqd += qh * gq;
+          dqd += qh[jj][r] * gq;
         } else if (i < nt) {
           dq[row(i) * DK + c] = (float)gq;
         }
@@ -637,7 +660,7 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
         const int i = Own::row(r), c = cb + Own::col(jj);
         const double R2 = ef[jj][r] * acc[jj][r];
         ak[jj][r] += R2;
-        ag[jj][r] += khat(i, c) * R2;
+        ag[jj][r] += kh[jj][r] * R2;
       }
     split(X::F);
     // C1 = F o ((beta dA)^T (E o K)): into dk and dGamma (- k C1)
@@ -650,7 +673,7 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
         const int i = Own::row(r), c = cb + Own::col(jj);
         const double C1 = ef[jj][r] * acc[jj][r];
         ak[jj][r] += C1;
-        ag[jj][r] -= khat(i, c) * C1;
+        ag[jj][r] -= kh[jj][r] * C1;
       }
     // C2 = F o (dP^T (E o Q)): into dk and dGamma (- k C2)
     mgemm<kCH, C, kBT, 1>([&](int m, int kk) { return s_P[kk * (C + 1) + m]; },
@@ -663,20 +686,19 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
 #pragma unroll
       for (int jj = 0; jj < T64; ++jj) {
         const int cl = Own::col(jj), c = cb + cl;
-        const double kh = khat(i, c);
         const double C2 = ef[jj][r] * acc[jj][r];
         ak[jj][r] += C2;
-        ag[jj][r] -= kh * C2;
+        ag[jj][r] -= kh[jj][r] * C2;
         if (s_fb[cl]) {
           const double R2 = scr[X::AK + i * DK + c];
           const double C1 = scr[X::E + i * DK + c], C2x = scr[X::F + i * DK + c];
           ak[jj][r] += R2 + C1 + C2x;
-          ag[jj][r] += kh * (R2 - C1 - C2x);
+          ag[jj][r] += kh[jj][r] * (R2 - C1 - C2x);
         }
         if (i == C - 1) ag[jj][r] += s_dGn[cl];
         if (l2norm) {
           scr[X::AK + i * DK + c] = ak[jj][r];
-          dkd += kh * ak[jj][r];
+          dkd += kh[jj][r] * ak[jj][r];
         } else if (i < nt) {
           dk[row(i) * DK + c] = (float)ak[jj][r];
         }
