@@ -135,7 +135,7 @@ def test_forward_bf16_strong_decay_chunks(dk, dv):
     cu = np.concatenate([[0], np.cumsum(lens)])
     x = _rand_forward(31, B=1, T=int(cu[-1]), H=2, dk=dk, dv=dv, dtype="bf16", cu=cu)
     g = x["g"]
-    g[0, 70:76, 0, :4] = 1e-20                      # one channel group, 6 tokens: 2^-400
+    g[0, 70:76, 0, :4] = 1e-20                      # four channels, 6 tokens: 2^-400
     g[0, 200:203, 1, 5] = 0.0                        # exact zeros (clamped on the GPU)
     g[0, 192:256, 0, :] = np.where(g[0, 192:256, 0, :] < 0, -1e-3, 1e-3)   # whole chunk
     g[0, 300 + 10:300 + 13, :, 7] = -1e-25           # second sequence, negative and tiny
