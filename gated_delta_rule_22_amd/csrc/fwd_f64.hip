@@ -291,29 +291,30 @@ __global__ __launch_bounds__(kIT) void f64_intra(
   }
 }
 
-// Serial pass over the chunks of one (sequence, head, kBV-column block).  The
+// Serial pass over the chunks of one (sequence, head, BV-column block).  The
 // products run on the fp64 matrix cores with their right operands (S, U) in
-// LDS; three barriers per chunk order the phases.
-template <int DK, int DV>
+// LDS; three barriers per chunk order the phases.  BV is 32, or 16 when the
+// 32-column grid would leave most of the GPU idle.
+template <int DK, int DV, int BV>
 __global__ __launch_bounds__(kThreads) void f64_inter(
     const float *__restrict__ S0, int H, int N, SeqTable tab, const double *__restrict__ records,
     size_t rec_doubles, void *__restrict__ o, float *__restrict__ S_T, int o_bf16,
     double *__restrict__ S_chunks, double *__restrict__ U_chunks) {
   using R = Rec<DK, DV>;
-  using Own = MOwn<kBV>;
+  using Own = MOwn<BV>;
   constexpr int TPW = Own::TPW;
-  __shared__ double s_S[DK * kBV];
-  __shared__ double s_U[C * kBV];
+  __shared__ double s_S[DK * BV];
+  __shared__ double s_U[C * BV];
 
-  constexpr int NV = DV / kBV;
+  constexpr int NV = DV / BV;
   const int jb = blockIdx.x % NV, rh = blockIdx.x / NV, t = threadIdx.x;
   const int n = tab.order[rh / H], h = rh % H;
   const int len = tab.seq_len[n], start = tab.seq_start[n];
   const int nch = (len + C - 1) / C;
-  const size_t sbase = ((size_t)n * H + h) * DK * DV + (size_t)jb * kBV;
+  const size_t sbase = ((size_t)n * H + h) * DK * DV + (size_t)jb * BV;
 
-  for (int p = t; p < DK * kBV; p += kThreads) {
-    const int c = p / kBV, j = p % kBV;
+  for (int p = t; p < DK * BV; p += kThreads) {
+    const int c = p / BV, j = p % BV;
     s_S[p] = S0 ? (double)S0[sbase + (size_t)c * DV + j] : 0.0;
   }
   __syncthreads();
@@ -334,12 +335,12 @@ __global__ __launch_bounds__(kThreads) void f64_inter(
     ARing<> ring_w, ring_o, ring_k[DK / 64];
     mgemm_start(fa_w, ring_w);
     if (S_chunks)
-      for (int p = t; p < DK * kBV; p += kThreads)
-        S_chunks[ch * DK * DV + (size_t)(p / kBV) * DV + jb * kBV + p % kBV] = s_S[p];
+      for (int p = t; p < DK * BV; p += kThreads)
+        S_chunks[ch * DK * DV + (size_t)(p / BV) * DV + jb * BV + p % BV] = s_S[p];
     // U = Ubar - W S
     {
       d4 acc[TPW];
-      mgemm_run<kBV, DK>(fa_w, [&](int kk, int nn) { return s_S[kk * kBV + nn]; }, ring_w, acc);
+      mgemm_run<BV, DK>(fa_w, [&](int kk, int nn) { return s_S[kk * BV + nn]; }, ring_w, acc);
       if (o)
         mgemm_start(fa_o, ring_o);
       else
@@ -349,18 +350,18 @@ __global__ __launch_bounds__(kThreads) void f64_inter(
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = Own::row(r), j = Own::col(jj);
-          const double u = rec[R::UB + i * DV + jb * kBV + j] - acc[jj][r];
-          s_U[i * kBV + j] = u;
-          if (U_chunks) U_chunks[ch * C * DV + (size_t)i * DV + jb * kBV + j] = u;
+          const double u = rec[R::UB + i * DV + jb * BV + j] - acc[jj][r];
+          s_U[i * BV + j] = u;
+          if (U_chunks) U_chunks[ch * C * DV + (size_t)i * DV + jb * BV + j] = u;
         }
     }
     __syncthreads();         // U complete
     // O = (gamma Q) S + P U, as one product over [S; U]
     if (o) {
       d4 acc[TPW];
-      mgemm_run<kBV, DK + C>(
+      mgemm_run<BV, DK + C>(
           fa_o,
-          [&](int kk, int nn) { return kk < DK ? s_S[kk * kBV + nn] : s_U[(kk - DK) * kBV + nn]; },
+          [&](int kk, int nn) { return kk < DK ? s_S[kk * BV + nn] : s_U[(kk - DK) * BV + nn]; },
           ring_o, acc);
       mgemm_start(fa_k(0), ring_k[0]);
 #pragma unroll
@@ -369,7 +370,7 @@ __global__ __launch_bounds__(kThreads) void f64_inter(
         for (int r = 0; r < 4; ++r) {
           const int i = Own::row(r), j = Own::col(jj);
           if (i >= nt) continue;
-          const size_t oi = ((size_t)(start + lc * C + i) * H + h) * DV + jb * kBV + j;
+          const size_t oi = ((size_t)(start + lc * C + i) * H + h) * DV + jb * BV + j;
           if (o_bf16)
             static_cast<__hip_bfloat16 *>(o)[oi] = __float2bfloat16((float)acc[jj][r]);
           else
@@ -382,7 +383,7 @@ __global__ __launch_bounds__(kThreads) void f64_inter(
 #pragma unroll
     for (int half = 0; half < DK / 64; ++half) {
       d4 acc[TPW];
-      mgemm_run<kBV, C>(fa_k(half), [&](int kk, int nn) { return s_U[kk * kBV + nn]; },
+      mgemm_run<BV, C>(fa_k(half), [&](int kk, int nn) { return s_U[kk * BV + nn]; },
                         ring_k[half], acc);
       if (half + 1 < DK / 64) mgemm_start(fa_k(half + 1), ring_k[half + 1]);
 #pragma unroll
@@ -390,14 +391,14 @@ __global__ __launch_bounds__(kThreads) void f64_inter(
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int c = half * 64 + Own::row(r), j = Own::col(jj);
-          s_S[c * kBV + j] = rec[R::GN + c] * s_S[c * kBV + j] + acc[jj][r];
+          s_S[c * BV + j] = rec[R::GN + c] * s_S[c * BV + j] + acc[jj][r];
         }
     }
     __syncthreads();         // S' complete, U free
   }
   if (S_T)
-    for (int p = t; p < DK * kBV; p += kThreads) {
-      const int c = p / kBV, j = p % kBV;
+    for (int p = t; p < DK * BV; p += kThreads) {
+      const int c = p / BV, j = p % BV;
       S_T[sbase + (size_t)c * DV + j] = (float)s_S[p];
     }
 }
@@ -417,9 +418,17 @@ hipError_t launch_shape(const void *q, const void *k, const void *v, const float
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((f64_inter<DK, DV>), dim3((DV / kBV) * N * H), dim3(kThreads), 0, stream, S0,
-                     H, N, tab, static_cast<const double *>(records), rec_doubles, o, S_T, o_bf16,
-                     S_chunks, U_chunks);
+  // fewer 32-column workgroups than compute units: 16-column blocks instead
+  if ((size_t)(DV / kBV) * N * H < 256) {
+    hipLaunchKernelGGL((f64_inter<DK, DV, kBV / 2>), dim3((DV / (kBV / 2)) * N * H),
+                       dim3(kThreads), 0, stream, S0, H, N, tab,
+                       static_cast<const double *>(records), rec_doubles, o, S_T, o_bf16,
+                       S_chunks, U_chunks);
+  } else {
+    hipLaunchKernelGGL((f64_inter<DK, DV, kBV>), dim3((DV / kBV) * N * H), dim3(kThreads), 0,
+                       stream, S0, H, N, tab, static_cast<const double *>(records), rec_doubles,
+                       o, S_T, o_bf16, S_chunks, U_chunks);
+  }
   return hipGetLastError();
 }
 
