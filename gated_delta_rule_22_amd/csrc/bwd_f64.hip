@@ -60,7 +60,9 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_state(
   __shared__ double s_dU[C * kBV];
 
   constexpr int NV = DV / kBV;
-  const int jb = blockIdx.x % NV, rh = blockIdx.x / NV, t = threadIdx.x;
+  const int t = threadIdx.x;
+  int rh, jb;
+  if (!xcd_block(NV, N * H, rh, jb)) return;
   const int n = tab.order[rh / H], h = rh % H;
   const int len = tab.seq_len[n], start = tab.seq_start[n];
   const int nch = (len + C - 1) / C;
@@ -801,7 +803,8 @@ hipError_t launch_bwd_shape(const void *q, const void *k, const void *v, const f
                             int signed_gates, int l2norm, hipStream_t stream) {
   const size_t rec_doubles = rec_bytes / sizeof(double);
   const TIn *tq = static_cast<const TIn *>(q), *tk = static_cast<const TIn *>(k);
-  hipLaunchKernelGGL((f64_bwd_state<DK, DV>), dim3((DV / kBV) * N * H), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((f64_bwd_state<DK, DV>), dim3(xcd_grid(DV / kBV, N * H)), dim3(kThreads), 0,
+                     stream,
                      dO, dS_T, H, N, tab, records, rec_doubles, dU_chunks, dSe_chunks, dS0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_chunks_ub == 0) return e;

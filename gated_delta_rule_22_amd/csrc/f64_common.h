@@ -143,6 +143,20 @@ __device__ __forceinline__ double sum16(double x) {
   return x;
 }
 
+// Workgroups are dealt to the eight XCDs in turn.  For a grid of
+// round_up(rows, 8) * nv workgroups, xcd_block gives this workgroup's row and
+// column block so that the nv column blocks of one row run on the same XCD and
+// share its L2 (they read the same per-chunk records).  False past the last row.
+__device__ __forceinline__ bool xcd_block(int nv, int rows, int &row, int &jb) {
+  const unsigned wg = blockIdx.x, local = wg >> 3;
+  jb = (int)(local % (unsigned)nv);
+  row = (int)((local / (unsigned)nv) * 8 + (wg & 7));
+  return row < rows;
+}
+__host__ __forceinline__ unsigned xcd_grid(int nv, int rows) {
+  return (unsigned)(((rows + 7) / 8) * 8 * nv);
+}
+
 __device__ __forceinline__ int find_seq(const int32_t *chunk_off, int N, int c) {
   int lo = 0, hi = N;          // chunk_off[lo] <= c < chunk_off[hi]
   while (hi - lo > 1) {

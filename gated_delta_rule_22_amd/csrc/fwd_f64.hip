@@ -307,7 +307,9 @@ __global__ __launch_bounds__(kThreads) void f64_inter(
   __shared__ double s_U[C * BV];
 
   constexpr int NV = DV / BV;
-  const int jb = blockIdx.x % NV, rh = blockIdx.x / NV, t = threadIdx.x;
+  const int t = threadIdx.x;
+  int rh, jb;
+  if (!xcd_block(NV, N * H, rh, jb)) return;
   const int n = tab.order[rh / H], h = rh % H;
   const int len = tab.seq_len[n], start = tab.seq_start[n];
   const int nch = (len + C - 1) / C;
@@ -420,12 +422,12 @@ hipError_t launch_shape(const void *q, const void *k, const void *v, const float
   }
   // fewer 32-column workgroups than compute units: 16-column blocks instead
   if ((size_t)(DV / kBV) * N * H < 256) {
-    hipLaunchKernelGGL((f64_inter<DK, DV, kBV / 2>), dim3((DV / (kBV / 2)) * N * H),
+    hipLaunchKernelGGL((f64_inter<DK, DV, kBV / 2>), dim3(xcd_grid(DV / (kBV / 2), N * H)),
                        dim3(kThreads), 0, stream, S0, H, N, tab,
                        static_cast<const double *>(records), rec_doubles, o, S_T, o_bf16,
                        S_chunks, U_chunks);
   } else {
-    hipLaunchKernelGGL((f64_inter<DK, DV, kBV>), dim3((DV / kBV) * N * H), dim3(kThreads), 0,
+    hipLaunchKernelGGL((f64_inter<DK, DV, kBV>), dim3(xcd_grid(DV / kBV, N * H)), dim3(kThreads), 0,
                        stream, S0, H, N, tab, static_cast<const double *>(records), rec_doubles,
                        o, S_T, o_bf16, S_chunks, U_chunks);
   }
