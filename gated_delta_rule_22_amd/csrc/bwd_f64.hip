@@ -172,36 +172,40 @@ constexpr int kCH = 32;                  // channels per pair-kernel workgroup
 
 // Per-chunk scratch (doubles), written by f64_bwd_prep and f64_bwd_pairs:
 //   DX [C][DV]        dX = T^T dU
-//   G, GAM, KHR [C][DK]  log2|gamma_i|, gamma_i (signed), gamma_n / gamma_i
-//   E, F [C][DK]      the ratio split sign 2^(+-(G - Rm)); on exact-path
-//                     channels 0, later their pair terms C1 and C2
+//   E [C][DK]         the ratio split e = sign(gamma) 2^(G - Rm) (G = log2|gamma|,
+//                     Rm the channel's integer midpoint); on exact-path
+//                     channels G itself.  The other factors follow from e:
+//                     gamma = e 2^Rm, f = 1 / e, gamma_n / gamma = SIG f.
 //   AQ, AK [C][DK]    the pair terms R1, R2 of exact-path channels, later the
 //                     gradients with respect to the normalised q and k
+//   X3, X4 [C][DK]    the pair terms C1, C2 of exact-path channels
 //   DP, DA [C][C]     dP and beta dA, zero above the diagonal
-//   FB [DK]           1 on channels that take the exact path
+//   FB, RM, SIG [DK]  1 on exact-path channels; Rm; sign(gamma_n) 2^(G_n - Rm)
 //   FQ, FK [C]        the q/k normalisation factors (1 if off)
 //   DB [1 + NB][C]    dbeta: the prep kernel's part, then one row per block
 //   QD, KD [NB][C]    qhat . dqhat and khat . dkhat per channel block
+//   SGN [C][DK]       sign of gamma, one byte each (read on exact-path channels)
 template <int DK, int DV>
 struct Scr {
   static constexpr int NB = DK / kCH;
   static constexpr size_t DX = 0;
-  static constexpr size_t G = DX + C * DV;
-  static constexpr size_t GAM = G + C * DK;
-  static constexpr size_t KHR = GAM + C * DK;
-  static constexpr size_t E = KHR + C * DK;
-  static constexpr size_t F = E + C * DK;
-  static constexpr size_t AQ = F + C * DK;
+  static constexpr size_t E = DX + C * DV;
+  static constexpr size_t AQ = E + C * DK;
   static constexpr size_t AK = AQ + C * DK;
-  static constexpr size_t DP = AK + C * DK;
+  static constexpr size_t X3 = AK + C * DK;
+  static constexpr size_t X4 = X3 + C * DK;
+  static constexpr size_t DP = X4 + C * DK;
   static constexpr size_t DA = DP + C * C;
   static constexpr size_t FB = DA + C * C;
-  static constexpr size_t FQ = FB + DK;
+  static constexpr size_t RM = FB + DK;
+  static constexpr size_t SIG = RM + DK;
+  static constexpr size_t FQ = SIG + DK;
   static constexpr size_t FK = FQ + C;
   static constexpr size_t DB = FK + C;
   static constexpr size_t QD = DB + (1 + NB) * C;
   static constexpr size_t KD = QD + NB * C;
-  static constexpr size_t SIZE = KD + NB * C;
+  static constexpr size_t SGN = KD + NB * C;      // C * DK bytes
+  static constexpr size_t SIZE = SGN + C * DK / 8;
 };
 
 // Row sums over a wave's 16 lanes, kept per half of the column tiles (wave
@@ -230,7 +234,7 @@ __global__ __launch_bounds__(kBT) void f64_bwd_prep(
   __shared__ double s_b[kPool];
   __shared__ int8_t s_sg[C * DK];         // the gates' signs, then the sign of gamma
   __shared__ double s_beta[C], s_dbp[2][C];
-  __shared__ double s_R[DK], s_sig[DK];
+  __shared__ double s_R[DK];
   __shared__ int s_fb[DK];
 
   const int cflat = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
@@ -279,9 +283,10 @@ __global__ __launch_bounds__(kBT) void f64_bwd_prep(
     const double Rm = rint(0.5 * (gmax + gmin));
     const int fb = (gmax - gmin) > 2000.0;
     s_R[t] = Rm;
-    s_sig[t] = (par ? -1.0 : 1.0) * exp2(G - Rm);   // sign(gamma_n) 2^(G_n - Rm)
     s_fb[t] = fb;
     scr[X::FB + t] = fb;
+    scr[X::RM + t] = Rm;
+    scr[X::SIG + t] = (par ? -1.0 : 1.0) * exp2(G - Rm);   // sign(gamma_n) 2^(G_n - Rm)
   }
   if (t < C) {
     s_beta[t] = t < nt ? (double)beta[row(t)] : 0.0;
@@ -311,27 +316,15 @@ __global__ __launch_bounds__(kBT) void f64_bwd_prep(
     }
   }
   __syncthreads();
-  // the gate factors of every (token, channel), once: e = 2^(G - Rm) and
-  // f = 2^(Rm - G) (signed), gamma = sign e 2^Rm and gamma_n / gamma =
-  // (sign_n 2^(G_n - Rm)) f; channels on the exact path take exp2 directly
+  // the split factor of every (token, channel), once (G itself on exact-path
+  // channels), and the sign of gamma
+  int8_t *sgn8 = reinterpret_cast<int8_t *>(scr + X::SGN);
 #pragma unroll 2
   for (int p = t; p < C * DK; p += kBT) {
     const int c = p % DK;
-    const double G = s_l[p], sg = s_sg[p];
-    scr[X::G + p] = G;
-    if (s_fb[c]) {
-      const double Gn = s_l[(C - 1) * DK + c], sn = s_sg[(C - 1) * DK + c];
-      scr[X::GAM + p] = sg * exp2(G);
-      scr[X::KHR + p] = sg * sn * exp2(Gn - G);
-      scr[X::E + p] = 0.0;
-      scr[X::F + p] = 0.0;
-    } else {
-      const double Rm = s_R[c], e = exp2(G - Rm), f = sg * exp2(Rm - G);
-      scr[X::GAM + p] = sg * ldexp(e, (int)Rm);
-      scr[X::KHR + p] = s_sig[c] * f;
-      scr[X::E + p] = sg * e;
-      scr[X::F + p] = f;
-    }
+    const double G = s_l[p];
+    scr[X::E + p] = s_fb[c] ? G : s_sg[p] * exp2(G - s_R[c]);
+    sgn8[p] = s_sg[p];
   }
   __syncthreads();
 
@@ -425,6 +418,7 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
   __shared__ double s_beta[C], s_dbp[2][C], s_kd[2][C], s_qd[2][C];
   __shared__ double s_fk[C], s_fq[C];
   __shared__ double s_red[4][kCH], s_red2[kCH], s_dGn[kCH];
+  __shared__ double s_rm[kCH], s_sig[kCH];
   __shared__ int s_fb[kCH];
 
   const unsigned wg = blockIdx.x, t = threadIdx.x;
@@ -461,7 +455,22 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
     s_dbp[0][t] = s_dbp[1][t] = s_kd[0][t] = s_kd[1][t] = s_qd[0][t] = s_qd[1][t] = 0.0;
   }
   const bool fbc = t < kCH && scr[X::FB + cb + t] != 0.0;
-  if (t < kCH) s_fb[t] = fbc;
+  if (t < kCH) {
+    s_fb[t] = fbc;
+    s_rm[t] = scr[X::RM + cb + t];
+    s_sig[t] = scr[X::SIG + cb + t];
+  }
+  // the gate factors of (token i, channel cb + cl) from e (exact-path
+  // channels: exp2 of G directly)
+  const int8_t *sgn8 = reinterpret_cast<const int8_t *>(scr + X::SGN);
+  auto gam_of = [&](double e, int i, int cl) {
+    return s_fb[cl] ? sgn8[i * DK + cb + cl] * exp2(e) : ldexp(e, (int)s_rm[cl]);
+  };
+  auto khr_of = [&](double e, int i, int cl) {
+    if (!s_fb[cl]) return s_sig[cl] / e;
+    const double en = scr[X::E + (C - 1) * DK + cb + cl];
+    return sgn8[i * DK + cb + cl] * sgn8[(C - 1) * DK + cb + cl] * exp2(en - e);
+  };
   // the left operands of the direct-term products stream from global memory:
   // each product's first slices are issued ahead of the work before it
   auto fa_dx = [&](int m, int kk) { return scr[X::DX + m * DV + kk]; };
@@ -478,6 +487,7 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
   const int anyfb = __syncthreads_or(fbc);
 
   double aq[T64][4], ak[T64][4], ag[T64][4];
+  double er[T64][4];                      // this thread's raw split factors, loaded once
   d4 acc[T64];
   // dQT = dO S^T: dq = gamma dQT; dGamma = q gamma dQT.  M5 = dX S^T:
   // d(gamma K) = -Diag(beta) M5.
@@ -490,7 +500,7 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = Own::row(r), c = cb + Own::col(jj);
-        gam[jj][r] = scr[X::GAM + i * DK + c];
+        er[jj][r] = scr[X::E + i * DK + c];
         qt[jj][r] = rec[R::QT + i * DK + c];
       }
     mgemm_run<kCH, DV, kBT, PFD>(dO_at, st, ring, acc);
@@ -499,6 +509,7 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
     for (int jj = 0; jj < T64; ++jj)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
+        gam[jj][r] = gam_of(er[jj][r], Own::row(r), Own::col(jj));
         aq[jj][r] = gam[jj][r] * acc[jj][r];
         ag[jj][r] = qt[jj][r] * acc[jj][r];
         qt[jj][r] = rec[R::GK + Own::row(r) * DK + cb + Own::col(jj)];   // now gamma K
@@ -534,15 +545,12 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
     sdot = sum16(sdot);
     if (jp == 0) s_red2[cl] = sdot;
   }
-  double khr[T64][4], khd[T64][4];       // gamma_n / gamma and K_hat, loaded early
+  double khd[T64][4];                    // K_hat, loaded early
 #pragma unroll
   for (int jj = 0; jj < T64; ++jj)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = Own::row(r), c = cb + Own::col(jj);
-      khr[jj][r] = scr[X::KHR + i * DK + c];
-      khd[jj][r] = rec[R::KH + i * DK + c];
-    }
+    for (int r = 0; r < 4; ++r)
+      khd[jj][r] = rec[R::KH + Own::row(r) * DK + cb + Own::col(jj)];
   mgemm_run<kCH, DV, kBT, PFD>(fa_u, [&](int kk, int nn) { return s_b[nn * SV + kk]; }, ring,
                                acc);
 #pragma unroll
@@ -552,7 +560,7 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const double term = khd[jj][r] * acc[jj][r];
-      const double kr = khr[jj][r];
+      const double kr = khr_of(er[jj][r], Own::row(r), cl);
       ak[jj][r] += kr * acc[jj][r];
       ag[jj][r] -= term;
       col += term;
@@ -570,7 +578,8 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
   double *sFK = s_b, *sEK = s_b + C * SC, *sEQ = s_b + 2 * C * SC;
   for (int p = t; p < C * kCH; p += kBT) {
     const int i = p / kCH, cl = p % kCH, c = cb + cl;
-    const double e = scr[X::E + i * DK + c], f = scr[X::F + i * DK + c];
+    const double e = s_fb[cl] ? 0.0 : scr[X::E + i * DK + c];
+    const double f = s_fb[cl] ? 0.0 : 1.0 / e;
     const double kh = khat(i, c), qh = qhat(i, c);
     sFK[i * SC + cl] = f * kh;
     sEK[i * SC + cl] = e * kh;
@@ -578,29 +587,28 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
   }
   if (anyfb) {
     // channels too wide for the split: the four pair terms with exp2 per pair
-    // (the sign of gamma is that of GAM, which keeps it when it underflows)
-    __syncthreads();                    // E and F of this block read by the staging
-    auto sgn = [&](int i, int c) { return copysign(1.0, scr[X::GAM + i * DK + c]); };
+    // (E holds G on these channels)
+    auto sgn = [&](int i, int c) { return (double)sgn8[i * DK + c]; };
     for (int cg = 0; cg < kCH; cg += kBT / C) {
       const int c = cb + cg + t / C, i = t % C;
       if (!s_fb[c - cb]) continue;
-      const double Gi = scr[X::G + i * DK + c], si = sgn(i, c);
+      const double Gi = scr[X::E + i * DK + c], si = sgn(i, c);
       double R1 = 0.0, R2 = 0.0, C1 = 0.0, C2 = 0.0;
       for (int j = 0; j <= i; ++j) {
-        const double r = si * sgn(j, c) * exp2(Gi - scr[X::G + j * DK + c]);
+        const double r = si * sgn(j, c) * exp2(Gi - scr[X::E + j * DK + c]);
         const double kr = khat(j, c) * r;
         R1 = fma(s_P[i * (C + 1) + j], kr, R1);
         R2 = fma(s_DA[i * (C + 1) + j], kr, R2);
       }
       for (int m = i; m < C; ++m) {
-        const double r = si * sgn(m, c) * exp2(scr[X::G + m * DK + c] - Gi);
+        const double r = si * sgn(m, c) * exp2(scr[X::E + m * DK + c] - Gi);
         C1 = fma(s_DA[m * (C + 1) + i], khat(m, c) * r, C1);
         C2 = fma(s_P[m * (C + 1) + i], qhat(m, c) * r, C2);
       }
       scr[X::AQ + i * DK + c] = R1;
       scr[X::AK + i * DK + c] = R2;
-      scr[X::E + i * DK + c] = C1;
-      scr[X::F + i * DK + c] = C2;
+      scr[X::X3 + i * DK + c] = C1;
+      scr[X::X4 + i * DK + c] = C2;
     }
     __threadfence_block();
   }
@@ -617,16 +625,16 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
         kh[jj][r] = khat(i, c);
         qh[jj][r] = qhat(i, c);
       }
-    auto split = [&](size_t arr) {
+    auto split = [&](bool want_f) {
 #pragma unroll
       for (int jj = 0; jj < T64; ++jj)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int i = Own::row(r), cl = Own::col(jj);
-          ef[jj][r] = s_fb[cl] ? 0.0 : scr[arr + i * DK + cb + cl];
+          const double e = er[jj][r];
+          ef[jj][r] = s_fb[Own::col(jj)] ? 0.0 : want_f ? 1.0 / e : e;
         }
     };
-    split(X::E);
+    split(false);
     // R1 = E o (dP (F o K)): into dq and dGamma (+ q R1); dq is then complete
     mgemm<kCH, C, kBT, 1>([&](int m, int kk) { return s_P[m * (C + 1) + kk]; },
                        [&](int kk, int nn) { return sFK[kk * SC + nn]; }, acc);
@@ -664,7 +672,7 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
         ak[jj][r] += R2;
         ag[jj][r] += kh[jj][r] * R2;
       }
-    split(X::F);
+    split(true);
     // C1 = F o ((beta dA)^T (E o K)): into dk and dGamma (- k C1)
     mgemm<kCH, C, kBT, 1>([&](int m, int kk) { return s_DA[kk * (C + 1) + m]; },
                        [&](int kk, int nn) { return sEK[kk * SC + nn]; }, acc);
@@ -693,7 +701,7 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
         ag[jj][r] -= kh[jj][r] * C2;
         if (s_fb[cl]) {
           const double R2 = scr[X::AK + i * DK + c];
-          const double C1 = scr[X::E + i * DK + c], C2x = scr[X::F + i * DK + c];
+          const double C1 = scr[X::X3 + i * DK + c], C2x = scr[X::X4 + i * DK + c];
           ak[jj][r] += R2 + C1 + C2x;
           ag[jj][r] += kh[jj][r] * (R2 - C1 - C2x);
         }
@@ -830,8 +838,8 @@ hipError_t launch_bwd_shape(const void *q, const void *k, const void *v, const f
 
 size_t f64_bwd_scratch_bytes(int dk, int dv) {
   const size_t nb = (size_t)dk / kCH;
-  return sizeof(double) * ((size_t)C * dv + 7 * (size_t)C * dk + 2 * (size_t)C * C + dk +
-                           2 * (size_t)C + (1 + 3 * nb) * (size_t)C);
+  return sizeof(double) * ((size_t)C * dv + 5 * (size_t)C * dk + 2 * (size_t)C * C + 3 * dk +
+                           2 * (size_t)C + (1 + 3 * nb) * (size_t)C + (size_t)C * dk / 8);
 }
 
 hipError_t launch_bwd_f64(const void *q, const void *k, const void *v, const float *g,

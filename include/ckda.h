@@ -170,7 +170,7 @@ int ckda_forward_ex(const void *q, const void *k, const void *v, const float *g,
 /*
  * Workspace needed by ckda_backward for the same sizes, in bytes (the same for
  * both input dtypes).  Returns 0 if the sizes are invalid.  It holds fp64
- * per-chunk intermediates: about 1.35 MB per (64-token chunk, head) at
+ * per-chunk intermediates: about 1.3 MB per (64-token chunk, head) at
  * dk = dv = 128.
  */
 size_t ckda_backward_workspace_bytes(int B, int T, int H, int dk, int dv, int N,
