@@ -487,21 +487,24 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
   const int anyfb = __syncthreads_or(fbc);
 
   double aq[T64][4], ak[T64][4], ag[T64][4];
-  double er[T64][4];                      // this thread's raw split factors, loaded once
+  // this thread's raw split factors and normalised keys and queries, loaded
+  // once: gamma Q, gamma K and K gamma_n / gamma follow from them
+  double er[T64][4], kh[T64][4], qh[T64][4];
   d4 acc[T64];
   // dQT = dO S^T: dq = gamma dQT; dGamma = q gamma dQT.  M5 = dX S^T:
   // d(gamma K) = -Diag(beta) M5.
   {
     auto st = [&](int kk, int nn) { return s_b[nn * SV + kk]; };   // S^T (this block)
     // the epilogue's per-element factors are loaded before the product
-    double gam[T64][4], qt[T64][4];
+    double gam[T64][4];
 #pragma unroll
     for (int jj = 0; jj < T64; ++jj)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = Own::row(r), c = cb + Own::col(jj);
         er[jj][r] = scr[X::E + i * DK + c];
-        qt[jj][r] = rec[R::QT + i * DK + c];
+        kh[jj][r] = khat(i, c);
+        qh[jj][r] = qhat(i, c);
       }
     mgemm_run<kCH, DV, kBT, PFD>(dO_at, st, ring, acc);
     mgemm_start(fa_dx, ring);
@@ -511,8 +514,7 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
       for (int r = 0; r < 4; ++r) {
         gam[jj][r] = gam_of(er[jj][r], Own::row(r), Own::col(jj));
         aq[jj][r] = gam[jj][r] * acc[jj][r];
-        ag[jj][r] = qt[jj][r] * acc[jj][r];
-        qt[jj][r] = rec[R::GK + Own::row(r) * DK + cb + Own::col(jj)];   // now gamma K
+        ag[jj][r] = gam[jj][r] * qh[jj][r] * acc[jj][r];
       }
     mgemm_run<kCH, DV, kBT, PFD>(fa_dx, st, ring, acc);
     mgemm_start(fa_u, ring);
@@ -522,7 +524,7 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
       double part = 0.0;
 #pragma unroll
       for (int jj = 0; jj < T64; ++jj) {
-        const double gk = qt[jj][r];
+        const double gk = gam[jj][r] * kh[jj][r];
         ak[jj][r] = -s_beta[i] * gam[jj][r] * acc[jj][r];
         ag[jj][r] -= s_beta[i] * gk * acc[jj][r];
         part -= gk * acc[jj][r];
@@ -545,12 +547,6 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
     sdot = sum16(sdot);
     if (jp == 0) s_red2[cl] = sdot;
   }
-  double khd[T64][4];                    // K_hat, loaded early
-#pragma unroll
-  for (int jj = 0; jj < T64; ++jj)
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      khd[jj][r] = rec[R::KH + Own::row(r) * DK + cb + Own::col(jj)];
   mgemm_run<kCH, DV, kBT, PFD>(fa_u, [&](int kk, int nn) { return s_b[nn * SV + kk]; }, ring,
                                acc);
 #pragma unroll
@@ -559,8 +555,8 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
     double col = 0.0;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const double term = khd[jj][r] * acc[jj][r];
       const double kr = khr_of(er[jj][r], Own::row(r), cl);
+      const double term = kh[jj][r] * kr * acc[jj][r];
       ak[jj][r] += kr * acc[jj][r];
       ag[jj][r] -= term;
       col += term;
@@ -616,15 +612,7 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
   {
     // the split factor of each owned (token, channel): e for the R terms,
     // then f for the C terms (0 on exact-path channels)
-    double ef[T64][4], kh[T64][4], qh[T64][4];
-#pragma unroll
-    for (int jj = 0; jj < T64; ++jj)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = Own::row(r), c = cb + Own::col(jj);
-        kh[jj][r] = khat(i, c);
-        qh[jj][r] = qhat(i, c);
-      }
+    double ef[T64][4];
     auto split = [&](bool want_f) {
 #pragma unroll
       for (int jj = 0; jj < T64; ++jj)
