@@ -139,6 +139,7 @@ def main():
                      "chunk": w.chunk, "tokens_per_step": w.B * w.T, "qkv": "bf16",
                      "gates_state_out": "fp32"}
     x = wl.forward_inputs(w)
+    fwd_result = None
     if not args.skip_forward:
         print(f"[bench] forward {w.name}: uploading", file=sys.stderr, flush=True)
         bf = lambda a: torch.from_numpy(a).to(dev).to(torch.bfloat16)
@@ -176,6 +177,9 @@ def main():
         out["mfma"] = {"algorithmic_tflops": tflops, "peak_tflops": BF16_PEAK_TFLOPS,
                        "frac": tflops / BF16_PEAK_TFLOPS, "flops_per_step": fwd_flops}
         out["wall_s_timed"] = wall
+        if not args.skip_cpu:
+            # the timed forward's outputs, checked against the oracle in the CPU leg
+            fwd_result = (o.cpu().numpy(), S_T.cpu().numpy())
         # KDA mode on the same shape and gate magnitudes: the comparison the pages
         # quote for CKDA's kernel throughput (CKDA over KDA).
         ga = g.abs()
@@ -339,8 +343,16 @@ def main():
         nth = min(16, oracle.default_threads())     # one GPU's share of the host
         print(f"[bench] cpu oracle on {nth} threads", file=sys.stderr, flush=True)
         t0 = time.perf_counter()
-        oracle.forward(x["q"], x["k"], x["v"], x["g"], x["beta"], nthreads=nth)
+        o_ref, S_ref = oracle.forward(x["q"], x["k"], x["v"], x["g"], x["beta"], nthreads=nth)
         dt = time.perf_counter() - t0
+        if fwd_result is not None:
+            # parity of the timed forward at the full size: max |gpu - oracle| / rms(oracle)
+            err = lambda got, ref: float(np.max(np.abs(got.astype(np.float64) - ref)) /
+                                         np.sqrt(np.mean(ref * ref)))
+            out["parity"] = {"workload": w.name, "err_o": err(fwd_result[0], o_ref),
+                             "err_S_T": err(fwd_result[1], S_ref), "tol": 2e-3,
+                             "reference": "the fp64 oracle on the same inputs"}
+        del o_ref, S_ref
         out["cpu_baseline"] = {"value": w.B * w.T / dt, "unit": "tokens/s", "cores": nth,
                                "kind": "oracle",
                                "sample": f"the whole {w.name} forward (B={w.B}, T={w.T}, H={w.H}), "
