@@ -421,7 +421,8 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
   __shared__ double s_rm[kCH], s_sig[kCH];
   __shared__ int s_fb[kCH];
 
-  const unsigned wg = blockIdx.x, t = threadIdx.x;
+  const unsigned wg = blockIdx.x;
+  const int t = threadIdx.x;
   const int blk = (int)((wg >> 3) % NB);
   const size_t chx = (size_t)((wg >> 3) / NB) * 8 + (wg & 7);
   if (chx >= n_ch) return;
@@ -655,7 +656,6 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
     for (int jj = 0; jj < T64; ++jj)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int i = Own::row(r), c = cb + Own::col(jj);
         const double R2 = ef[jj][r] * acc[jj][r];
         ak[jj][r] += R2;
         ag[jj][r] += kh[jj][r] * R2;
@@ -668,7 +668,6 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
     for (int jj = 0; jj < T64; ++jj)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int i = Own::row(r), c = cb + Own::col(jj);
         const double C1 = ef[jj][r] * acc[jj][r];
         ak[jj][r] += C1;
         ag[jj][r] -= kh[jj][r] * C1;
