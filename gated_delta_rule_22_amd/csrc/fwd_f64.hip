@@ -72,6 +72,16 @@ __global__ __launch_bounds__(kIT) void f64_intra(
 
   auto row = [&](int i) { return (size_t)(t0 + i) * H + h; };   // token-head row
 
+  // this chunk's values, loaded now (their latency hides behind everything up
+  // to the Ubar product) and staged in LDS as fp32 just before it
+  constexpr int NVL = C * DV / kIT;
+  float vpre[NVL];
+#pragma unroll
+  for (int u = 0; u < NVL; ++u) {
+    const int p = t + u * kIT, i = p / DV;
+    vpre[u] = i < nt ? to_f32(v[row(i) * DV + p % DV]) : 0.f;
+  }
+
   // ---- gates: log2|alpha| and the sign of every (token, channel) in
   // parallel, then the inclusive scans (cumsum of the log-magnitudes, parity
   // of the negatives) per channel.
@@ -275,13 +285,18 @@ __global__ __launch_bounds__(kIT) void f64_intra(
         for (int r = 0; r < 4; ++r)
           rec[R::W + Own::col(jj) * DK + cb + Own::row(r)] = acc[jj][r];
     }
+    float *s_v = reinterpret_cast<float *>(s_u);   // [C][DV + 1] (the A/P operands are done)
+    static_assert(C * (DV + 1) <= 2 * kU, "room for V in fp32");
+#pragma unroll
+    for (int u = 0; u < NVL; ++u) {
+      const int p = t + u * kIT;
+      s_v[(p / DV) * (DV + 1) + p % DV] = vpre[u];
+    }
+    __syncthreads();
 #pragma unroll 1
     for (int cb = 0; cb < DV; cb += 64) {
-      mgemm<C, C, kIT>(
-          [&](int m, int kk) {
-            return kk < nt ? (double)to_f32(v[row(kk) * DV + cb + m]) : 0.0;
-          },
-          tbt, acc);
+      mgemm<C, C, kIT>([&](int m, int kk) { return (double)s_v[kk * (DV + 1) + cb + m]; }, tbt,
+                       acc);
 #pragma unroll
       for (int jj = 0; jj < TP; ++jj)
 #pragma unroll
