@@ -256,9 +256,17 @@ __global__ __launch_bounds__(kBT) void f64_bwd_prep(
   // every (token, channel) in parallel into LDS (the sign rides in a float
   // copy of alpha), then the scans per channel.
   double *s_l = s_b;                                    // [C][DK] log2|alpha|
-#pragma unroll 4
-  for (int p = t; p < C * DK; p += kBT) {
-    const float a = p / DK < nt ? g[row(p / DK) * DK + p % DK] : 1.f;
+  constexpr int NGL = C * DK / kBT;
+  float gpre[NGL];                                      // all gate loads issued first
+#pragma unroll
+  for (int u = 0; u < NGL; ++u) {
+    const int p = t + u * kBT;
+    gpre[u] = p / DK < nt ? g[row(p / DK) * DK + p % DK] : 1.f;
+  }
+#pragma unroll
+  for (int u = 0; u < NGL; ++u) {
+    const int p = t + u * kBT;
+    const float a = gpre[u];
     s_l[p] = fmax(log2(fabs((double)a)), kLog2Floor);
     s_sg[p] = (signed_gates && a < 0.f) ? -1 : 1;   // KDA mode: signs ignored
   }

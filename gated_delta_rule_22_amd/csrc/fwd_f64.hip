@@ -81,13 +81,22 @@ __global__ __launch_bounds__(kIT) void f64_intra(
     const int p = t + u * kIT, i = p / DV;
     vpre[u] = i < nt ? to_f32(v[row(i) * DV + p % DV]) : 0.f;
   }
+  // and the gates, all issued before the first is used
+  constexpr int NGL = C * DK / kIT;
+  float gpre[NGL];
+#pragma unroll
+  for (int u = 0; u < NGL; ++u) {
+    const int p = t + u * kIT;
+    gpre[u] = p / DK < nt ? g[row(p / DK) * DK + p % DK] : 1.f;
+  }
 
   // ---- gates: log2|alpha| and the sign of every (token, channel) in
   // parallel, then the inclusive scans (cumsum of the log-magnitudes, parity
   // of the negatives) per channel.
-#pragma unroll 4
-  for (int p = t; p < C * DK; p += kIT) {
-    const float a = p / DK < nt ? g[row(p / DK) * DK + p % DK] : 1.f;
+#pragma unroll
+  for (int u = 0; u < NGL; ++u) {
+    const int p = t + u * kIT;
+    const float a = gpre[u];
     s_G[p] = fmax(log2(fabs((double)a)), kLog2Floor);
     s_par[p] = (uint8_t)(signed_gates && a < 0.f);   // KDA mode: signs ignored
   }
