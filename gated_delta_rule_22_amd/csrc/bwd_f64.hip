@@ -499,6 +499,7 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
   // this thread's raw split factors and normalised keys and queries, loaded
   // once: gamma Q, gamma K and K gamma_n / gamma follow from them
   double er[T64][4], kh[T64][4], qh[T64][4];
+  float gseg[LSEG];
   d4 acc[T64];
   // dQT = dO S^T: dq = gamma dQT; dGamma = q gamma dQT.  M5 = dX S^T:
   // d(gamma K) = -Diag(beta) M5.
@@ -632,6 +633,12 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
         }
     };
     split(false);
+    // the gates of this thread's dalpha segment, in flight during the products
+#pragma unroll
+    for (int u = 0; u < LSEG; ++u) {
+      const int i = LSEG * (t / kCH) + u;
+      gseg[u] = i < nt ? g[row(i) * DK + cb + t % kCH] : 1.f;
+    }
     // R1 = E o (dP (F o K)): into dq and dGamma (+ q R1); dq is then complete
     mgemm<kCH, C, kBT, 1>([&](int m, int kk) { return s_P[m * (C + 1) + kk]; },
                        [&](int kk, int nn) { return sFK[kk * SC + nn]; }, acc);
@@ -734,7 +741,7 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
     for (int i = LSEG * sgm + LSEG - 1; i >= LSEG * sgm; --i) {
       acc2 += s_ag[i * SC + cl];
       if (i < nt) {
-        const double a = g[row(i) * DK + cb + cl];
+        const double a = gseg[i - LSEG * sgm];
         const double am = fabs(a) < floor_mag ? (a < 0.0 ? -floor_mag : floor_mag) : a;
         dg[row(i) * DK + cb + cl] = (float)(acc2 / am);
       }
