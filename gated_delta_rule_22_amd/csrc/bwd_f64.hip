@@ -557,6 +557,17 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
     sdot = sum16(sdot);
     if (jp == 0) s_red2[cl] = sdot;
   }
+  // the pair-term staging's inputs, in flight during this product
+  constexpr int NST = C * kCH / kBT;
+  double pe[NST];
+  float pk[NST], pq[NST];
+#pragma unroll
+  for (int u = 0; u < NST; ++u) {
+    const int p = t + u * kBT, i = p / kCH, c = cb + p % kCH;
+    pe[u] = scr[X::E + i * DK + c];
+    pk[u] = i < nt ? to_f32(k[row(i) * DK + c]) : 0.f;
+    pq[u] = i < nt ? to_f32(q[row(i) * DK + c]) : 0.f;
+  }
   mgemm_run<kCH, DV, kBT, PFD>(fa_u, [&](int kk, int nn) { return s_b[nn * SV + kk]; }, ring,
                                acc);
 #pragma unroll
@@ -582,11 +593,12 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
 
   // ---- the pair terms: right operands F o K, E o K, E o Q of this block
   double *sFK = s_b, *sEK = s_b + C * SC, *sEQ = s_b + 2 * C * SC;
-  for (int p = t; p < C * kCH; p += kBT) {
-    const int i = p / kCH, cl = p % kCH, c = cb + cl;
-    const double e = s_fb[cl] ? 0.0 : scr[X::E + i * DK + c];
+#pragma unroll
+  for (int u = 0; u < NST; ++u) {
+    const int p = t + u * kBT, i = p / kCH, cl = p % kCH;
+    const double e = s_fb[cl] ? 0.0 : pe[u];
     const double f = s_fb[cl] ? 0.0 : 1.0 / e;
-    const double kh = khat(i, c), qh = qhat(i, c);
+    const double kh = (double)pk[u] * s_fk[i], qh = (double)pq[u] * s_fq[i];
     sFK[i * SC + cl] = f * kh;
     sEK[i * SC + cl] = e * kh;
     sEQ[i * SC + cl] = e * qh;
