@@ -131,6 +131,9 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_state(
 #pragma unroll
     for (int half = 0; half < DK / 64; ++half) {
       d4 acc[TPW];
+      double gn[4];                        // gamma_n of this thread's state rows
+#pragma unroll
+      for (int r = 0; r < 4; ++r) gn[r] = rec[R::GN + half * 64 + Own::row(r)];
       mgemm_run<kBV, 2 * C>(
           fa_s(half),
           [&](int kk, int nn) { return kk < C ? s_dO[kk * kBV + nn] : s_dU[(kk - C) * kBV + nn]; },
@@ -141,7 +144,7 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_state(
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int c = half * 64 + Own::row(r), j = Own::col(jj);
-          s_dS[c * kBV + j] = rec[R::GN + c] * s_dS[c * kBV + j] + acc[jj][r];
+          s_dS[c * kBV + j] = gn[r] * s_dS[c * kBV + j] + acc[jj][r];
         }
     }
     __syncthreads();         // dS complete; dO and dU free

@@ -366,6 +366,12 @@ __global__ __launch_bounds__(kThreads) void f64_inter(
     // U = Ubar - W S
     {
       d4 acc[TPW];
+      double ub[TPW][4];                   // the epilogue's Ubar, loaded ahead
+#pragma unroll
+      for (int jj = 0; jj < TPW; ++jj)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          ub[jj][r] = rec[R::UB + Own::row(r) * DV + jb * BV + Own::col(jj)];
       mgemm_run<BV, DK>(fa_w, [&](int kk, int nn) { return s_S[kk * BV + nn]; }, ring_w, acc);
       if (o)
         mgemm_start(fa_o, ring_o);
@@ -376,7 +382,7 @@ __global__ __launch_bounds__(kThreads) void f64_inter(
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = Own::row(r), j = Own::col(jj);
-          const double u = rec[R::UB + i * DV + jb * BV + j] - acc[jj][r];
+          const double u = ub[jj][r] - acc[jj][r];
           s_U[i * BV + j] = u;
           if (U_chunks) U_chunks[ch * C * DV + (size_t)i * DV + jb * BV + j] = u;
         }
@@ -409,6 +415,9 @@ __global__ __launch_bounds__(kThreads) void f64_inter(
 #pragma unroll
     for (int half = 0; half < DK / 64; ++half) {
       d4 acc[TPW];
+      double gn[4];                        // gamma_n of this thread's state rows
+#pragma unroll
+      for (int r = 0; r < 4; ++r) gn[r] = rec[R::GN + half * 64 + Own::row(r)];
       mgemm_run<BV, C>(fa_k(half), [&](int kk, int nn) { return s_U[kk * BV + nn]; },
                         ring_k[half], acc);
       if (half + 1 < DK / 64) mgemm_start(fa_k(half + 1), ring_k[half + 1]);
@@ -417,7 +426,7 @@ __global__ __launch_bounds__(kThreads) void f64_inter(
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int c = half * 64 + Own::row(r), j = Own::col(jj);
-          s_S[c * BV + j] = rec[R::GN + c] * s_S[c * BV + j] + acc[jj][r];
+          s_S[c * BV + j] = gn[r] * s_S[c * BV + j] + acc[jj][r];
         }
     }
     __syncthreads();         // S' complete, U free
