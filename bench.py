@@ -231,10 +231,28 @@ def main():
         dbytes, per_head = decode_algorithmic(wd)
         dgbs = dbytes / (ms_d * 1e-3) / 1e9
         dtraffic = profiled_traffic("decode_256x16.md", "gated_delta_rule_22_amd/csrc/decode.hip")
+        # what a plain device copy of the same state bytes reaches on this GPU (one
+        # read and one write per byte, like the decode step): the practical ceiling
+        S2 = torch.empty_like(S)
+        S2.copy_(S)
+        torch.cuda.synchronize()
+        ncopy = 50
+        e0.record(stream)
+        for _ in range(ncopy):
+            S2.copy_(S)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_c = e0.elapsed_time(e1) / ncopy
+        cgbs = 2 * S.numel() * 4 / (ms_c * 1e-3) / 1e9
+        del S2
         out["decode"] = {"workload": wd.name, "steps": steps, "us_per_step": ms_d * 1e3,
                          "traffic": dtraffic,
                          "steps_per_s": 1e3 / ms_d, "hbm_gbs": dgbs, "hbm_frac": dgbs / HBM_PEAK_GBS,
-                         "bytes_per_step": dbytes, "bytes_per_state": per_head}
+                         "bytes_per_step": dbytes, "bytes_per_state": per_head,
+                         "copy_reference": {"gbs": cgbs, "us": ms_c * 1e3,
+                                            "what": "torch copy_ of the fp32 state buffer "
+                                                    f"({S.numel() * 4} B read + written)"},
+                         "frac_of_copy": dgbs / cgbs}
         if args.skip_forward:
             out["roofline"] = {"bound": "hbm", "achieved": dgbs, "peak": HBM_PEAK_GBS,
                                "unit": "GB/s", "frac": dgbs / HBM_PEAK_GBS, "traffic": dtraffic,
