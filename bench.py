@@ -116,8 +116,8 @@ def main():
                          "kernel of known traffic for hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
-              "(heads and sequences shard across GPUs without exchange; see DESIGN.md)",
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(heads and sequences would shard across GPUs with no exchange between them)",
               file=sys.stderr)
         sys.exit(2)
 
