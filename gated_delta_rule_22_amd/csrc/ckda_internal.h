@@ -16,6 +16,15 @@ constexpr int kChunk = 64;          // tokens per chunk of the chunkwise forward
 // q, k, v arrive as bf16 or fp32; both widen exactly to fp32 (and fp64).
 __device__ __forceinline__ float to_f32(__hip_bfloat16 x) { return __bfloat162float(x); }
 __device__ __forceinline__ float to_f32(float x) { return x; }
+// Four consecutive elements (8-byte aligned for bf16, 16-byte for fp32) as fp32.
+__device__ __forceinline__ float4 load4_f32(const float *p) {
+  return *reinterpret_cast<const float4 *>(p);
+}
+__device__ __forceinline__ float4 load4_f32(const __hip_bfloat16 *p) {
+  const uint2 u = *reinterpret_cast<const uint2 *>(p);
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
+}
 
 // ---------------------------------------------------------------- schedule
 // Per-call sequence table, computed on the device from cu_seqlens (or the

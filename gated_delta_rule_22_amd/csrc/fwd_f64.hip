@@ -52,7 +52,7 @@ __global__ __launch_bounds__(kIT) void f64_intra(
   using R = Rec<DK, DV>;
   constexpr int kU = 3 * C * (kCB + 1);  // the A/P product operands of one channel block
   static_assert(kU >= 3 * 256, "room for the blocked inverse's partial products");
-  __shared__ double s_G[C * DK > C * (C + 1) ? C * DK : C * (C + 1)];  // G, later T
+  __shared__ double s_G[C * DK > C * (C + 1) ? C * DK : C * (C + 1)];  // gate factors, later T
   __shared__ uint8_t s_par[C * DK];
   __shared__ double s_A[C * (C + 1)];
   __shared__ double s_u[kU];            // A/P operands | blocked-inverse partial products
@@ -72,56 +72,90 @@ __global__ __launch_bounds__(kIT) void f64_intra(
 
   auto row = [&](int i) { return (size_t)(t0 + i) * H + h; };   // token-head row
 
-  // this chunk's values, loaded now (their latency hides behind everything up
-  // to the Ubar product) and staged in LDS as fp32 just before it
-  constexpr int NVL = C * DV / kIT;
-  float vpre[NVL];
+  // Every input of the chunk is loaded up front, four consecutive channels
+  // per load, so a workgroup waits for global memory once.  The values are
+  // staged in LDS as fp32 just before the Ubar product.
+  const float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f), one4 = make_float4(1.f, 1.f, 1.f, 1.f);
+  constexpr int NVL = C * DV / (4 * kIT);
+  float4 vpre[NVL];
 #pragma unroll
   for (int u = 0; u < NVL; ++u) {
-    const int p = t + u * kIT, i = p / DV;
-    vpre[u] = i < nt ? to_f32(v[row(i) * DV + p % DV]) : 0.f;
+    const int e = 4 * (t + u * kIT), i = e / DV;
+    vpre[u] = i < nt ? load4_f32(v + row(i) * DV + e % DV) : zero4;
   }
-  // and the gates, all issued before the first is used
-  constexpr int NGL = C * DK / kIT;
-  float gpre[NGL];
+  // the gates
+  constexpr int NGL = C * DK / (4 * kIT);
+  float4 gpre[NGL];
 #pragma unroll
   for (int u = 0; u < NGL; ++u) {
-    const int p = t + u * kIT;
-    gpre[u] = p / DK < nt ? g[row(p / DK) * DK + p % DK] : 1.f;
+    const int e = 4 * (t + u * kIT), i = e / DK;
+    gpre[u] = i < nt ? *reinterpret_cast<const float4 *>(g + row(i) * DK + e % DK) : one4;
+  }
+  // the keys and queries of every kCB-channel block of the A/P products: in
+  // block b, thread t takes token t / (kCB / 4) and channels
+  // b kCB + 4 (t % (kCB / 4)) .. + 3
+  constexpr int NKB = DK / kCB;
+  static_assert(C * kCB == 4 * kIT, "one load of four channels per thread and block");
+  float4 rk[NKB], rq[NKB];
+  const int ki = t / (kCB / 4), kc = 4 * (t % (kCB / 4));
+#pragma unroll
+  for (int b = 0; b < NKB; ++b) {
+    rk[b] = ki < nt ? load4_f32(k + row(ki) * DK + b * kCB + kc) : zero4;
+    rq[b] = ki < nt ? load4_f32(q + row(ki) * DK + b * kCB + kc) : zero4;
   }
 
-  // ---- gates: log2|alpha| and the sign of every (token, channel) in
-  // parallel, then the inclusive scans (cumsum of the log-magnitudes, parity
-  // of the negatives) per channel.
+  // ---- gates: |alpha| (floored at 2^kLog2Floor, so that a zero gate keeps
+  // the products finite) and the sign of every (token, channel) in parallel,
+  // then per channel the inclusive scans: the running product of the
+  // magnitudes and the parity of the negatives.
 #pragma unroll
-  for (int u = 0; u < NGL; ++u) {
-    const int p = t + u * kIT;
-    const float a = gpre[u];
-    s_G[p] = fmax(log2(fabs((double)a)), kLog2Floor);
-    s_par[p] = (uint8_t)(signed_gates && a < 0.f);   // KDA mode: signs ignored
-  }
+  for (int u = 0; u < NGL; ++u)
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const int p = 4 * (t + u * kIT) + cc;
+      const float a = cc == 0 ? gpre[u].x : cc == 1 ? gpre[u].y : cc == 2 ? gpre[u].z : gpre[u].w;
+      s_G[p] = fmax(fabs((double)a), ldexp(1.0, (int)kLog2Floor));
+      s_par[p] = (uint8_t)(signed_gates && a < 0.f);   // KDA mode: signs ignored
+    }
   __syncthreads();
   if (t < DK) {
-    double G = 0.0, gmax = 0.0, gmin = 0.0;
+    // gamma_i = prod_{s<=i} |alpha_s| is carried as m 2^x with m in [0.5, 1),
+    // renormalised after every factor, so no product leaves fp64's range and
+    // G = log2 gamma = x + log2 m is never needed for the usual channel.  The
+    // chunk start (gamma = 1) counts in the range; x - 1 <= G < x.
+    double m = 0.5;
+    int x = 1, xmax = 1, xmin = 1;
     uint8_t par = 0;
 #pragma unroll 8
     for (int i = 0; i < C; ++i) {
-      G += s_G[i * DK + t];
+      int dx;
+      m = frexp(m * s_G[i * DK + t], &dx);
+      x += dx;
+      xmax = max(xmax, x);
+      xmin = min(xmin, x);
       par ^= s_par[i * DK + t];
-      gmax = fmax(gmax, G);
-      gmin = fmin(gmin, G);
-      s_G[i * DK + t] = G;
       s_par[i * DK + t] = par;
     }
-    // Pair ratios are formed as e_i f_j with e = 2^(G - Rm), f = 2^(Rm - G)
-    // about the midpoint Rm of the channel's range; past +-1000 binary orders
-    // that product could leave fp64's range and the channel takes exp2 per pair.
-    // (an integer midpoint: gamma = e 2^Rm is then an exact scaling of e)
-    const double Rm = rint(0.5 * (gmax + gmin));
-    s_R[t] = Rm;
-    s_sig[t] = (par ? -1.0 : 1.0) * exp2(G - Rm);   // sign(gamma_n) 2^(G_n - Rm)
-    s_fb[t] = (gmax - gmin) > 2000.0;
-    if (gmax - gmin > 2000.0) s_anyfb = 1;
+    // Pair ratios are formed as e_i f_j with e = 2^(G - Rm), f = 1 / e about
+    // an integer midpoint Rm of the channel's range (gamma = e 2^Rm is then an
+    // exact scaling of e).  Past +-1000 binary orders e f could leave fp64's
+    // range; such a channel keeps G itself and takes exp2 per pair.
+    const int Rm = (xmax + xmin - 2) / 2;
+    const bool fb = xmax - xmin + 1 > 2000;
+    m = 0.5;
+    x = 1;
+#pragma unroll 8
+    for (int i = 0; i < C; ++i) {      // the same products again, now scaled
+      int dx;
+      const double a = s_G[i * DK + t];
+      m = frexp(m * a, &dx);
+      x += dx;
+      s_G[i * DK + t] = fb ? (double)x + log2(m) : ldexp(m, x - Rm);   // G, or |e| = 2^(G - Rm)
+    }
+    s_R[t] = (double)Rm;
+    s_sig[t] = fb ? 0.0 : (par ? -1.0 : 1.0) * ldexp(m, x - Rm);   // sign(gamma_n) 2^(G_n - Rm)
+    s_fb[t] = fb;
+    if (fb) s_anyfb = 1;
   }
   // ---- optional L2 normalisation of q and k per token: (sum x^2 + 1e-6)^(-1/2)
   if (t < C) {
@@ -152,37 +186,30 @@ __global__ __launch_bounds__(kIT) void f64_intra(
     using Own = MOwn<C, kIT>;
     constexpr int TP = Own::TPW, SB = kCB + 1;
     double *sKE = s_u, *sQE = s_u + C * SB, *sKF = s_u + 2 * C * SB;
-    constexpr int NG = C * kCB / kIT;
-    float rk[NG], rq[NG];
-    auto load_block = [&](int c0) {
-#pragma unroll
-      for (int u = 0; u < NG; ++u) {
-        const int p = t + u * kIT, i = p / kCB, c = c0 + p % kCB;
-        rk[u] = i < nt ? to_f32(k[row(i) * DK + c]) : 0.f;
-        rq[u] = i < nt ? to_f32(q[row(i) * DK + c]) : 0.f;
-      }
-    };
     d4 accA[TP], accP[TP];
 #pragma unroll
     for (int jj = 0; jj < TP; ++jj) accA[jj] = accP[jj] = d4{0.0, 0.0, 0.0, 0.0};
-    load_block(0);
 #pragma unroll 1
     for (int c0 = 0; c0 < DK; c0 += kCB) {
       __syncthreads();                  // the previous block's products are done
+      // the split factors, and the gamma-scaled records of this thread's four
+      // (token, channel) pairs: gamma Q, gamma K, K gamma_n / gamma and
+      // gamma_n (masked tokens have k = q = 0)
+      const int i = ki;
+      d4 oq, ok, okh;
 #pragma unroll
-      for (int u = 0; u < NG; ++u) {
-        // the split factors, and the gamma-scaled records of this (token,
-        // channel): gamma Q, gamma K, K gamma_n / gamma and gamma_n (masked
-        // tokens have k = q = 0)
-        const int p = t + u * kIT, i = p / kCB, cl = p % kCB, c = c0 + cl;
+      for (int u = 0; u < 4; ++u) {
+        const int cl = kc + u, c = c0 + cl;
+        const float rku = u == 0 ? rk[0].x : u == 1 ? rk[0].y : u == 2 ? rk[0].z : rk[0].w;
+        const float rqu = u == 0 ? rq[0].x : u == 1 ? rq[0].y : u == 2 ? rq[0].z : rq[0].w;
         const double G = s_G[i * DK + c], sg = s_par[i * DK + c] ? -1.0 : 1.0;
-        const double kh = (double)rk[u] * s_fk[i], qh = (double)rq[u] * s_fq[i];
+        const double kh = (double)rku * s_fk[i], qh = (double)rqu * s_fq[i];
         double e = 0.0, f = 0.0, gam, khr;
         if (!s_fb[c]) {
-          const double Rm = s_R[c], eu = exp2(G - Rm);
+          const double eu = G;           // |e| = 2^(G - Rm) for such a channel
           e = sg * eu;
-          f = sg * exp2(Rm - G);
-          gam = sg * ldexp(eu, (int)Rm);
+          f = sg / eu;
+          gam = sg * ldexp(eu, (int)s_R[c]);
           khr = s_sig[c] * f;
         } else {
           const double Gn = s_G[(C - 1) * DK + c];
@@ -190,16 +217,23 @@ __global__ __launch_bounds__(kIT) void f64_intra(
           gam = sg * exp2(G);
           khr = sg * sn * exp2(Gn - G);
         }
-        rec[R::QT + i * DK + c] = qh * gam;
-        rec[R::GK + i * DK + c] = kh * gam;
-        rec[R::KH + i * DK + c] = kh * khr;
+        oq[u] = qh * gam;
+        ok[u] = kh * gam;
+        okh[u] = kh * khr;
         if (i == C - 1) rec[R::GN + c] = gam;
         sKE[i * SB + cl] = kh * e;
         sQE[i * SB + cl] = qh * e;
         sKF[i * SB + cl] = kh * f;
       }
+      *reinterpret_cast<d4 *>(rec + R::QT + i * DK + c0 + kc) = oq;
+      *reinterpret_cast<d4 *>(rec + R::GK + i * DK + c0 + kc) = ok;
+      *reinterpret_cast<d4 *>(rec + R::KH + i * DK + c0 + kc) = okh;
       __syncthreads();
-      if (c0 + kCB < DK) load_block(c0 + kCB);
+#pragma unroll
+      for (int b = 0; b + 1 < NKB; ++b) {   // the next block's keys and queries move up
+        rk[b] = rk[b + 1];
+        rq[b] = rq[b + 1];
+      }
       auto kf = [&](int kk, int nn) { return sKF[nn * SB + kk]; };   // (K o F)^T
       mgemm<C, kCB, kIT, 1, false>([&](int m, int kk) { return sKE[m * SB + kk]; }, kf, accA);
       mgemm<C, kCB, kIT, 1, false>([&](int m, int kk) { return sQE[m * SB + kk]; }, kf, accP);
@@ -298,8 +332,11 @@ __global__ __launch_bounds__(kIT) void f64_intra(
     static_assert(C * (DV + 1) <= 2 * kU, "room for V in fp32");
 #pragma unroll
     for (int u = 0; u < NVL; ++u) {
-      const int p = t + u * kIT;
-      s_v[(p / DV) * (DV + 1) + p % DV] = vpre[u];
+      const int e = 4 * (t + u * kIT), i = e / DV, c = e % DV;
+      s_v[i * (DV + 1) + c] = vpre[u].x;
+      s_v[i * (DV + 1) + c + 1] = vpre[u].y;
+      s_v[i * (DV + 1) + c + 2] = vpre[u].z;
+      s_v[i * (DV + 1) + c + 3] = vpre[u].w;
     }
     __syncthreads();
 #pragma unroll 1
