@@ -452,7 +452,10 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
   const int cb = blk * kCH;
 
   auto row = [&](int i) { return (size_t)(t0 + i) * H + h; };   // token-head row
-  auto dO_at = [&](int m, int c) { return m < nt ? (double)dO[row(m) * DV + c] : 0.0; };
+  // four consecutive columns of d_o per load
+  auto dO_at = quad([&](int m, int c) {
+    return m < nt ? ld4f(dO + row(m) * DV + c) : d4{0.0, 0.0, 0.0, 0.0};
+  });
   auto khat = [&](int i, int c) {
     return i < nt ? (double)to_f32(k[row(i) * DK + c]) * s_fk[i] : 0.0;
   };
@@ -485,8 +488,8 @@ __global__ __launch_bounds__(kBT, 2) void f64_bwd_pairs(
   };
   // the left operands of the direct-term products stream from global memory:
   // each product's first slices are issued ahead of the work before it
-  auto fa_dx = [&](int m, int kk) { return scr[X::DX + m * DV + kk]; };
-  auto fa_u = [&](int m, int kk) { return Uc[m * DV + kk]; };
+  auto fa_dx = quad([&](int m, int kk) { return ld4d(scr + X::DX + m * DV + kk); });
+  auto fa_u = quad([&](int m, int kk) { return ld4d(Uc + m * DV + kk); });
   ARing<PFD> ring;
   mgemm_start(dO_at, ring);
   // S^T of this block, and dP and beta dA for the pair terms, into LDS (the

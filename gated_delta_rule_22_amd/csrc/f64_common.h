@@ -57,6 +57,36 @@ struct MOwn {
   }
 };
 
+// A left operand whose rows are contiguous in K can be wrapped as a Quad:
+// f(m, k0) returns A(m, k0 .. k0 + 3) from one or two wide loads, where the
+// plain form makes four.
+template <typename F4>
+struct Quad {
+  F4 f;
+};
+template <typename F4>
+__device__ __forceinline__ Quad<F4> quad(F4 f) {
+  return Quad<F4>{f};
+}
+template <typename T>
+struct IsQuad {
+  static constexpr bool value = false;
+};
+template <typename F4>
+struct IsQuad<Quad<F4>> {
+  static constexpr bool value = true;
+};
+// Four consecutive doubles (16-byte aligned) and four consecutive floats
+// (16-byte aligned) as a d4.
+__device__ __forceinline__ d4 ld4d(const double *p) {
+  const double2 a = *reinterpret_cast<const double2 *>(p), b = *reinterpret_cast<const double2 *>(p + 2);
+  return d4{a.x, a.y, b.x, b.y};
+}
+__device__ __forceinline__ d4 ld4f(const float *p) {
+  const float4 a = *reinterpret_cast<const float4 *>(p);
+  return d4{a.x, a.y, a.z, a.w};
+}
+
 // The left operand's slices in flight: mgemm_start issues the first PF of
 // them, mgemm_run multiplies.  A kernel may call mgemm_start early (before a
 // barrier, or before the previous product's epilogue) when the left operand
@@ -72,9 +102,16 @@ __device__ __forceinline__ void mgemm_start(const FA &fa, ARing<PF> &ring) {
   const int m = 16 * ((threadIdx.x >> 6) & 3) + (l & 15);
   const int kq = 4 * (l >> 4);
 #pragma unroll
-  for (int b = 0; b < PF; ++b)
+  for (int b = 0; b < PF; ++b) {
+    if constexpr (IsQuad<FA>::value) {
+      const d4 x = fa.f(m, 16 * b + kq);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) ring.r[b][q] = fa(m, 16 * b + kq + q);
+      for (int q = 0; q < 4; ++q) ring.r[b][q] = x[q];
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ring.r[b][q] = fa(m, 16 * b + kq + q);
+    }
+  }
 }
 
 template <int NB, int K, int NT = kThreads, int PF = 3, bool ZERO = true, typename FA,
@@ -91,8 +128,14 @@ __device__ __forceinline__ void mgemm_run(const FA &fa, const FB &fb, ARing<PF> 
   const int n0 = 16 * ((threadIdx.x >> 8) * TPW) + (l & 15);
   const int kq = 4 * (l >> 4);
   auto load = [&](int s, double (&a)[4]) {
+    if constexpr (IsQuad<FA>::value) {
+      const d4 x = fa.f(m, 16 * s + kq);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) a[q] = fa(m, 16 * s + kq + q);
+      for (int q = 0; q < 4; ++q) a[q] = x[q];
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) a[q] = fa(m, 16 * s + kq + q);
+    }
   };
   if (ZERO) {                              // else accumulate onto acc
 #pragma unroll
