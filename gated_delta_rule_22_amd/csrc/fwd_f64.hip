@@ -272,38 +272,50 @@ __global__ __launch_bounds__(kIT) void f64_intra(
   __syncthreads();
 
   // ---- T = (I + A)^-1, blockwise over 16 x 16 blocks: the four diagonal
-  // blocks by forward substitution (a column per thread), then block rows
-  // I = 1..3 in turn: T_IJ = -T_II sum_{J<=K<I} A_IK T_KJ for every J < I.
+  // blocks by forward substitution (one column per thread, held in
+  // registers), then block rows I = 1..3 in turn on the fp64 matrix cores:
+  // T_IJ = -T_II M_IJ with M_IJ = sum_{J<=K<I} A_IK T_KJ, one wave per J < I.
   double *s_T = s_G;     // G is dead; T is C x (C+1)
   for (int p = t; p < C * (C + 1); p += kIT) s_T[p] = (p / (C + 1) == p % (C + 1)) ? 1.0 : 0.0;
   __syncthreads();
   if (t < C) {
-    const int j = t, ie = (j / 16) * 16 + 16;
-    for (int i = j + 1; i < ie; ++i) {
+    // column jl of diagonal block I: x_r = -sum_{m<r} A_rm x_m below the unit entry
+    const int I = t >> 4, jl = t & 15;
+    const double *a = s_A + 16 * I * (C + 1) + 16 * I;
+    double x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
       double acc = 0.0;
-      for (int m = j; m < i; ++m) acc += s_A[i * (C + 1) + m] * s_T[m * (C + 1) + j];
-      s_T[i * (C + 1) + j] = -acc;
+#pragma unroll
+      for (int m = 0; m < r; ++m) acc = fma(a[r * (C + 1) + m], x[m], acc);
+      x[r] = r < jl ? 0.0 : r == jl ? 1.0 : -acc;
     }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s_T[(16 * I + r) * (C + 1) + 16 * I + jl] = x[r];
   }
   __syncthreads();
   {
-    double *s_M = s_u;   // M_IJ = sum_K A_IK T_KJ, up to three 16 x 16 blocks
+    // operand layout of the fp64 product (lane l, K-slice sl of 4):
+    // A(l % 16, 4 sl + l / 16), B(4 sl + l / 16, l % 16); accumulator entry r
+    // holds (4 r + l / 16, l % 16), so M's K-slice sl is the lane's entry sl
+    const int w = t >> 6, l = t & 63, lr = l & 15, lk = l >> 4;
     for (int I = 1; I < C / 16; ++I) {
-      for (int e = t; e < I * 256; e += kIT) {
-        const int J = e / 256, r = (e % 256) / 16, c = e % 16;
-        double acc = 0.0;
+      if (w < I) {
+        const int J = w;
+        d4 m4 = {0.0, 0.0, 0.0, 0.0};
         for (int K = J; K < I; ++K)
-#pragma unroll 4
-          for (int m = 0; m < 16; ++m)
-            acc += s_A[(16 * I + r) * (C + 1) + 16 * K + m] * s_T[(16 * K + m) * (C + 1) + 16 * J + c];
-        s_M[e] = acc;
-      }
-      __syncthreads();
-      for (int e = t; e < I * 256; e += kIT) {
-        const int J = e / 256, r = (e % 256) / 16, c = e % 16;
-        double acc = 0.0;
-        for (int m = 0; m <= r; ++m) acc += s_T[(16 * I + r) * (C + 1) + 16 * I + m] * s_M[J * 256 + m * 16 + c];
-        s_T[(16 * I + r) * (C + 1) + 16 * J + c] = -acc;
+#pragma unroll
+          for (int sl = 0; sl < 4; ++sl)
+            m4 = __builtin_amdgcn_mfma_f64_16x16x4f64(
+                s_A[(16 * I + lr) * (C + 1) + 16 * K + 4 * sl + lk],
+                s_T[(16 * K + 4 * sl + lk) * (C + 1) + 16 * J + lr], m4, 0, 0, 0);
+        d4 t4 = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl)
+          t4 = __builtin_amdgcn_mfma_f64_16x16x4f64(
+              s_T[(16 * I + lr) * (C + 1) + 16 * I + 4 * sl + lk], m4[sl], t4, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s_T[(16 * I + 4 * r + lk) * (C + 1) + 16 * J + lr] = -t4[r];
       }
       __syncthreads();
     }
