@@ -118,44 +118,82 @@ __global__ __launch_bounds__(kIT) void f64_intra(
       s_par[p] = (uint8_t)(signed_gates && a < 0.f);   // KDA mode: signs ignored
     }
   __syncthreads();
-  if (t < DK) {
+  {
     // gamma_i = prod_{s<=i} |alpha_s| is carried as m 2^x with m in [0.5, 1),
     // renormalised after every factor, so no product leaves fp64's range and
-    // G = log2 gamma = x + log2 m is never needed for the usual channel.  The
-    // chunk start (gamma = 1) counts in the range; x - 1 <= G < x.
+    // G = log2 gamma (x - 1 <= G < x) is never needed for the usual channel.
+    // Each channel's tokens are cut into NSG segments, one thread each: a pass
+    // over the segment from 1, the segments' totals combined in order, then a
+    // second pass from the segment's prefix.  Combining: (m1, x1) (m2, x2) =
+    // (m, x1 + x2 + d) with m 2^d = m1 m2.
+    constexpr int NSG = kIT / DK, LS = C / NSG;
+    static_assert(NSG * DK == kIT && NSG * LS == C, "segments of the gate scan");
+    const int c = t % DK, sg = t / DK, i0 = sg * LS;
+    double *tot_m = s_u, *tot_x = s_u + kIT, *tot_hi = s_u + 2 * kIT, *tot_lo = s_u + 3 * kIT,
+           *tot_p = s_u + 4 * kIT;       // per (segment, channel); s_u is free until A and P
+    static_assert(5 * kIT <= kU, "room for the segment totals");
     double m = 0.5;
-    int x = 1, xmax = 1, xmin = 1;
+    int x = 1, xhi = 1, xlo = 1;
     uint8_t par = 0;
-#pragma unroll 8
-    for (int i = 0; i < C; ++i) {
+#pragma unroll
+    for (int i = i0; i < i0 + LS; ++i) {
       int dx;
-      m = frexp(m * s_G[i * DK + t], &dx);
+      m = frexp(m * s_G[i * DK + c], &dx);
       x += dx;
-      xmax = max(xmax, x);
-      xmin = min(xmin, x);
-      par ^= s_par[i * DK + t];
-      s_par[i * DK + t] = par;
+      xhi = max(xhi, x);
+      xlo = min(xlo, x);
+      par ^= s_par[i * DK + c];
+      s_par[i * DK + c] = par;            // parity within the segment, for now
+    }
+    tot_m[t] = m;
+    tot_x[t] = x;
+    tot_hi[t] = xhi;
+    tot_lo[t] = xlo;
+    tot_p[t] = par;
+    __syncthreads();
+    // this segment's prefix, and bounds on the channel's G: a token of segment
+    // s2 has x in [xp + x_local - 1, xp + x_local], so lo <= G < hi (the chunk
+    // start, G = 0, counts)
+    double mp = 0.5, mseg = 0.5;
+    int xp = 1, xseg = 1, hi = 1, lo = 0;
+    uint8_t pp = 0, pseg = 0;
+    for (int s2 = 0; s2 < NSG; ++s2) {
+      const int u = s2 * DK + c;
+      if (s2 == sg) {
+        mseg = mp;
+        xseg = xp;
+        pseg = pp;
+      }
+      hi = max(hi, xp + (int)tot_hi[u]);
+      lo = min(lo, xp + (int)tot_lo[u] - 2);
+      int dx;
+      mp = frexp(mp * tot_m[u], &dx);
+      xp += (int)tot_x[u] + dx;
+      pp ^= (uint8_t)tot_p[u];
     }
     // Pair ratios are formed as e_i f_j with e = 2^(G - Rm), f = 1 / e about
     // an integer midpoint Rm of the channel's range (gamma = e 2^Rm is then an
     // exact scaling of e).  Past +-1000 binary orders e f could leave fp64's
     // range; such a channel keeps G itself and takes exp2 per pair.
-    const int Rm = (xmax + xmin - 2) / 2;
-    const bool fb = xmax - xmin + 1 > 2000;
-    m = 0.5;
-    x = 1;
-#pragma unroll 8
-    for (int i = 0; i < C; ++i) {      // the same products again, now scaled
+    const int Rm = (hi + lo) / 2;
+    const bool fb = hi - lo > 2000;
+    m = mseg;
+    x = xseg;
+#pragma unroll
+    for (int i = i0; i < i0 + LS; ++i) {     // the same products again, now scaled
       int dx;
-      const double a = s_G[i * DK + t];
-      m = frexp(m * a, &dx);
+      m = frexp(m * s_G[i * DK + c], &dx);
       x += dx;
-      s_G[i * DK + t] = fb ? (double)x + log2(m) : ldexp(m, x - Rm);   // G, or |e| = 2^(G - Rm)
+      s_G[i * DK + c] = fb ? (double)x + log2(m) : ldexp(m, x - Rm);   // G, or |e| = 2^(G - Rm)
+      s_par[i * DK + c] ^= pseg;
     }
-    s_R[t] = (double)Rm;
-    s_sig[t] = fb ? 0.0 : (par ? -1.0 : 1.0) * ldexp(m, x - Rm);   // sign(gamma_n) 2^(G_n - Rm)
-    s_fb[t] = fb;
-    if (fb) s_anyfb = 1;
+    if (sg == NSG - 1)     // sign(gamma_n) 2^(G_n - Rm)
+      s_sig[c] = fb ? 0.0 : ((par ^ pseg) ? -1.0 : 1.0) * ldexp(m, x - Rm);
+    if (sg == 0) {
+      s_R[c] = (double)Rm;
+      s_fb[c] = fb;
+      if (fb) s_anyfb = 1;
+    }
   }
   // ---- optional L2 normalisation of q and k per token: (sum x^2 + 1e-6)^(-1/2)
   if (t < C) {
