@@ -98,7 +98,10 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_state(
                       : -rec[R::W + (kk - C) * DK + half * 64 + m];
       };
     };
-    ARing<> ring_u, ring_s[DK / 64];
+    // (deeper rings where K allows: a ring of PF + 1 slices must divide K / 16)
+    constexpr int PFU = ((DK + C) / 16) % 6 == 0 ? 5 : 3;
+    ARing<PFU> ring_u;
+    ARing<7> ring_s[DK / 64];
     mgemm_start(fa_u, ring_u);
 #pragma unroll
     for (int u = 0; u < NO; ++u) s_dO[t + u * kThreads] = (double)pre[u];
@@ -109,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_state(
     // dU = KH dS' + P^T dO, as one product over [dS'; dO]
     {
       d4 acc[TPW];
-      mgemm_run<kBV, DK + C>(
+      mgemm_run<kBV, DK + C, kThreads, PFU>(
           fa_u,
           [&](int kk, int nn) {
             return kk < DK ? s_dS[kk * kBV + nn] : s_dO[(kk - DK) * kBV + nn];
@@ -134,7 +137,7 @@ __global__ __launch_bounds__(kThreads) void f64_bwd_state(
       double gn[4];                        // gamma_n of this thread's state rows
 #pragma unroll
       for (int r = 0; r < 4; ++r) gn[r] = rec[R::GN + half * 64 + Own::row(r)];
-      mgemm_run<kBV, 2 * C>(
+      mgemm_run<kBV, 2 * C, kThreads, 7>(
           fa_s(half),
           [&](int kk, int nn) { return kk < C ? s_dO[kk * kBV + nn] : s_dU[(kk - C) * kBV + nn]; },
           ring_s[half], acc);
