@@ -347,7 +347,7 @@ __global__ __launch_bounds__(kBT) void f64_bwd_prep(
   __syncthreads();
   {
     d4 acc[TV];
-    mgemm<DV, C, kBT>([&](int m, int kk) { return rec[R::TI + kk * C + m]; },
+    mgemm<DV, C, kBT>(quad([&](int m, int kk) { return ld4d(rec + R::TI + m * C + kk); }),   // T^T
                       [&](int kk, int nn) { return s_b[kk * SV + nn]; }, acc);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -384,6 +384,11 @@ __global__ __launch_bounds__(kBT) void f64_bwd_prep(
         const int i = OwnC::row(r), j = OwnC::col(jj);
         scr[X::DP + i * C + j] = j <= i ? acc[jj][r] : 0.0;
       }
+    double ah[TC][4];                  // the epilogue's A / beta, loaded ahead
+#pragma unroll
+    for (int jj = 0; jj < TC; ++jj)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ah[jj][r] = rec[R::AH + OwnC::row(r) * C + OwnC::col(jj)];
     mgemm<C, DV, kBT>([&](int m, int kk) { return scr[X::DX + m * DV + kk]; }, ut, acc);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -394,7 +399,7 @@ __global__ __launch_bounds__(kBT) void f64_bwd_prep(
         const int j = OwnC::col(jj);
         const double dA = j < i ? -acc[jj][r] : 0.0;
         scr[X::DA + i * C + j] = s_beta[i] * dA;
-        part += rec[R::AH + i * C + j] * dA;
+        part += ah[jj][r] * dA;
       }
       add_row(s_dbp, i, part);
     }

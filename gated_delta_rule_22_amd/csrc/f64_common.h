@@ -16,7 +16,7 @@ constexpr double kLog2Floor = -1000.0;  // log2|alpha| is floored here (alpha = 
 // gamma_i = prod_{s<=i} alpha_s inside the chunk:
 template <int DK, int DV>
 struct Rec {
-  static constexpr size_t TI = 0;                 // T = (I + A)^-1     [C][C]
+  static constexpr size_t TI = 0;                 // T^T, T = (I + A)^-1 [C][C]
   static constexpr size_t P = TI + C * C;         // P (lower incl.)    [C][C]
   static constexpr size_t AH = P + C * C;         // A / beta (strict)  [C][C]
   static constexpr size_t W = AH + C * C;         // W                  [C][DK]

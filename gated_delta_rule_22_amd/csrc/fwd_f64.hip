@@ -363,7 +363,7 @@ __global__ __launch_bounds__(kIT) void f64_intra(
   // transposed on the fp64 matrix cores 64 columns at a time:
   // W^T = (gamma*K)^T (T Diag(beta))^T and Ubar^T = V^T (T Diag(beta))^T, the
   // left operand streamed from global memory, the right one read from T in LDS.
-  for (int p = t; p < C * C; p += kIT) rec[R::TI + p] = s_T[(p / C) * (C + 1) + p % C];
+  for (int p = t; p < C * C; p += kIT) rec[R::TI + p] = s_T[(p % C) * (C + 1) + p / C];   // T^T
   {
     using Own = MOwn<C, kIT>;
     constexpr int TP = Own::TPW;
