@@ -8,12 +8,12 @@ is missing the call raises instead of falling back to any other code.
 from . import workloads  # noqa: F401  (seeded input generators; no GPU needed)
 
 __all__ = ["forward", "kda_forward", "backward", "decode_step", "forward_workspace_bytes",
-           "backward_workspace_bytes", "library", "workloads"]
+           "backward_workspace_bytes", "library", "CkdaError", "workloads"]
 
 
 def __getattr__(name):
     if name in ("forward", "kda_forward", "backward", "decode_step", "forward_workspace_bytes",
-                "backward_workspace_bytes", "library"):
+                "backward_workspace_bytes", "library", "CkdaError"):
         from . import _lib
         return getattr(_lib, name)
     raise AttributeError(name)

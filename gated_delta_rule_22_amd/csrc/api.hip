@@ -1,7 +1,16 @@
 // C-ABI entry points: argument validation, workspace layout, dispatch.
 // Every check runs on the host before anything is enqueued, and touches no
 // HIP API, so an invalid call has no side effect.
+//
+// Debug mode (environment variable CKDA_DEBUG set to anything but "" or "0",
+// read at every call): cu_seqlens is copied to the host and checked
+// (0 = cu[0] <= ... <= cu[N] = T, else CKDA_ERR_SHAPE), which synchronises
+// the stream; and the workspace is filled with NaN before the kernels run, so
+// a read of anything they did not write shows up in the outputs.
+#include <stdlib.h>
 #include <string.h>
+
+#include <vector>
 
 #include "ckda_internal.h"
 
@@ -82,7 +91,39 @@ int forward_shape_status(int B, int T, int H, int dk, int dv, int N, int in_dtyp
   if (B < 1 || T < 0 || H < 1 || N < 1 || !dims_ok(dk) || !dims_ok(dv)) return CKDA_ERR_SHAPE;
   if ((long long)B * T * H >= (1LL << 31)) return CKDA_ERR_SHAPE;
   if ((long long)N * H >= (1LL << 31)) return CKDA_ERR_SHAPE;
+  // The kernels address one chunk of one head's rows with 32-bit byte offsets:
+  // 64 token rows of H heads at up to max(dk, dv) fp32 values each.
+  if ((long long)H * (dk > dv ? dk : dv) * 4 * kChunk >= (1LL << 31)) return CKDA_ERR_SHAPE;
   if (packed ? B != 1 : N != B) return CKDA_ERR_SHAPE;
+  return CKDA_OK;
+}
+
+bool debug_mode() {
+  const char *e = getenv("CKDA_DEBUG");
+  return e && *e && strcmp(e, "0") != 0;
+}
+
+// Debug mode: the host copy of cu_seqlens must be non-decreasing from 0 to T.
+int debug_check_cu(const int32_t *cu_seqlens, int N, int T, hipStream_t st) {
+  std::vector<int32_t> h((size_t)N + 1);
+  if (hipMemcpyAsync(h.data(), cu_seqlens, h.size() * sizeof(int32_t), hipMemcpyDeviceToHost,
+                     st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return CKDA_ERR_LAUNCH;
+  if (h[0] != 0 || h[N] != T) return CKDA_ERR_SHAPE;
+  for (int n = 0; n < N; ++n)
+    if (h[n + 1] < h[n]) return CKDA_ERR_SHAPE;
+  return CKDA_OK;
+}
+
+// Debug-mode steps shared by the forward and the backward, after validation.
+int debug_prologue(const int32_t *cu_seqlens, int N, int T, void *workspace, size_t bytes,
+                   hipStream_t st) {
+  if (!debug_mode()) return CKDA_OK;
+  if (cu_seqlens)
+    if (int s = debug_check_cu(cu_seqlens, N, T, st)) return s;
+  if (workspace && launch_poison(workspace, bytes & ~(size_t)3, st) != hipSuccess)
+    return CKDA_ERR_LAUNCH;
   return CKDA_OK;
 }
 
@@ -154,6 +195,7 @@ int forward_impl(const void *q, const void *k, const void *v, const float *g, co
     if (overlaps(workspace, L.total, s.p, s.n)) return CKDA_ERR_ALIAS;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (int s = debug_prologue(cu_seqlens, N, T, workspace, L.total, st)) return s;
   const SeqTable tab = seq_table(workspace, N);
   hipError_t e;
   if (in_dtype == CKDA_BF16) {
@@ -247,6 +289,7 @@ int backward_impl(const void *q, const void *k, const void *v, const float *g, c
   if (!workspace || workspace_bytes < L.total) return CKDA_ERR_WORKSPACE;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (int s = debug_prologue(cu_seqlens, N, T, workspace, L.total, st)) return s;
   const SeqTable tab = seq_table(workspace, N);
   if (launch_seq_table(cu_seqlens, B, T, N, tab, st) != hipSuccess) return CKDA_ERR_LAUNCH;
   char *w = static_cast<char *>(workspace);

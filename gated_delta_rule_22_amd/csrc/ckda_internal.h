@@ -51,6 +51,8 @@ SeqTable seq_table(void *workspace, int N);
 
 hipError_t launch_seq_table(const int32_t *cu_seqlens, int B, int T, int N, SeqTable tab,
                             hipStream_t stream);
+// Fills `bytes` (a multiple of 4; 4-byte aligned) with a NaN bit pattern.
+hipError_t launch_poison(void *buf, size_t bytes, hipStream_t stream);
 
 hipError_t launch_decode(const void *q, const void *k, const void *v, const float *g,
                          const float *beta, float *S, float *o, int N, int H, int dk, int dv,

@@ -201,8 +201,8 @@ template <int DK, bool SIGNED, bool NORM, bool OBF16>
 __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
     const __hip_bfloat16 *__restrict__ q, const __hip_bfloat16 *__restrict__ k,
     const __hip_bfloat16 *__restrict__ v, const float *__restrict__ g,
-    const float *__restrict__ beta, const float *__restrict__ S0, void *__restrict__ o,
-    float *__restrict__ S_T, int T, int H, int DV, int NH, int NV, SeqTable tab, int packed) {
+    const float *__restrict__ beta, const float *S0, void *__restrict__ o,
+    float *S_T, int T, int H, int DV, int NH, int NV, SeqTable tab, int packed) {
   using L = Lds<DK>;
   using PG = Prep<DK>;
   constexpr int CQW = PG::CQW, TGW = PG::TGW, TPL = PG::TPL;

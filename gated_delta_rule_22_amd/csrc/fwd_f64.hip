@@ -408,8 +408,8 @@ __global__ __launch_bounds__(kIT) void f64_intra(
 // 32-column grid would leave most of the GPU idle.
 template <int DK, int DV, int BV>
 __global__ __launch_bounds__(kThreads) void f64_inter(
-    const float *__restrict__ S0, int H, int N, SeqTable tab, const double *__restrict__ records,
-    size_t rec_doubles, void *__restrict__ o, float *__restrict__ S_T, int o_bf16,
+    const float *S0, int H, int N, SeqTable tab, const double *__restrict__ records,
+    size_t rec_doubles, void *__restrict__ o, float *S_T, int o_bf16,
     double *__restrict__ S_chunks, double *__restrict__ U_chunks) {
   using R = Rec<DK, DV>;
   using Own = MOwn<BV>;

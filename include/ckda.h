@@ -28,8 +28,15 @@
  *  - Arguments are validated on the host before anything is enqueued; an
  *    invalid call returns an error status and has no side effect.  The
  *    contents of device buffers (e.g. cu_seqlens) are not inspected on the
- *    host; out-of-range offsets are clamped by the kernels so that no access
- *    leaves the buffers, but the results of such a call are unspecified.
+ *    host.  Offsets that leave [0, T] or decrease are made monotone on the
+ *    device: sequence n covers tokens [P_n, P_{n+1}) with
+ *    P_i = min(max(0, cu[0], ..., cu[i]), T), so sequences never overlap and
+ *    no access leaves the buffers; rows outside every sequence are not
+ *    written.  With the environment variable CKDA_DEBUG set (to anything but
+ *    "" or "0") the library instead copies cu_seqlens to the host, which
+ *    synchronises the stream, returns CKDA_ERR_SHAPE unless
+ *    0 = cu[0] <= ... <= cu[N] = T, and fills the workspace with NaN before
+ *    the kernels run.
  *  - Calls that share no output buffer may run concurrently on different
  *    streams.
  */
@@ -101,7 +108,7 @@ size_t ckda_forward_workspace_bytes(int B, int T, int H, int dk, int dv, int N,
  *              [cu_seqlens[n], cu_seqlens[n+1]); 0 = cu[0] <= ... <= cu[N] = T.
  *              Each sequence starts from its own S0[n] and chunks restart at
  *              every sequence start.
- *  B, T, H     B >= 1, T >= 0, H >= 1 (B*T*H < 2^31)
+ *  B, T, H     B >= 1, T >= 0, H >= 1 (B*T*H < 2^31, H*max(dk,dv)*256 < 2^31)
  *  dk, dv      each 64 or 128
  *  N           number of sequences (>= 1)
  *  in_dtype    CKDA_BF16 or CKDA_F32
@@ -118,7 +125,10 @@ size_t ckda_forward_workspace_bytes(int B, int T, int H, int dk, int dv, int N,
  * fp32 accumulation, splitting fp32 operands into two bf16 terms (hi + lo)
  * so that products keep ~16 mantissa bits; states and intermediates stay
  * fp32.  fp32 inputs are computed in fp64 and rounded to fp32 on output.
- * Gate magnitudes below 2^-126 are treated as 2^-126 (fp32 inputs: 2^-1000).
+ * Gate magnitudes below 2^-126 are treated as 2^-126 (fp32 inputs: 2^-1000),
+ * and so is a NaN gate (the clamp of log2|alpha| to that floor keeps the
+ * floor).  A NaN anywhere else reaches only the outputs of its own
+ * (sequence, head).
  */
 int ckda_forward(const void *q, const void *k, const void *v, const float *g,
                  const float *beta, const float *S0, const int32_t *cu_seqlens,

@@ -177,3 +177,14 @@ def test_backward_ex_rejects_output_dtype_and_unknown_options(lib):
     assert call(4, 16) == 2          # CKDA_OPT_O_BF16 has no backward
     assert call(8, 16) == 2          # unknown bit
     assert call(1, 16) == call(3, 16) == call(0, 16) == 5   # valid options reach the workspace check
+
+
+def test_forward_rejects_heads_whose_chunk_offsets_overflow(lib):
+    """One chunk of one head spans 64 token rows of H heads; at max(dk, dv)
+    fp32 values per row its byte extent must stay below 2^31 (the kernels
+    address it with 32-bit offsets).  H = 65536 at d = 128 reaches 2^31."""
+    for entry in ("ckda_forward", "kda_forward"):
+        assert _fwd(lib, B=1, T=1, H=65536, entry=entry) == 2
+        assert _fwd(lib, B=1, T=1, H=65536, dk=64, dv=128, entry=entry) == 2
+    assert lib.ckda_forward_workspace_bytes(1, 1, 65536, 128, 128, 1, 0) == 0
+    assert lib.ckda_backward_workspace_bytes(1, 1, 65536, 128, 128, 1, 0) == 0

@@ -16,16 +16,36 @@ from tests import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "ckda_oracle.c")
 
-# (name, regex on the source, replacement)
+# (name, [(regex on the source, replacement), ...]); the edits apply in order.
+_DECAY = r"(?<!d)for \(int c = 0; c < dk; \+\+c\)\n\s*for \(int j = 0; j < dv; \+\+j\) S\[c \* dv \+ j\] \*= a\[c\];"
+_DECAY_TEXT = ("for (int c = 0; c < dk; ++c)\n            "
+               "for (int j = 0; j < dv; ++j) S[c * dv + j] *= a[c];")
+_READOUT = (r"        /\* readout o = S\^T q \*/\n"
+            r"        for \(int j = 0; j < dv; \+\+j\) o\[j\] = 0\.0;\n"
+            r"        for \(int c = 0; c < dk; \+\+c\)\n"
+            r"            for \(int j = 0; j < dv; \+\+j\) o\[j\] \+= q\[c\] \* S\[c \* dv \+ j\];\n")
+_READOUT_TEXT = ("        for (int j = 0; j < dv; ++j) o[j] = 0.0;\n"
+                 "        for (int c = 0; c < dk; ++c)\n"
+                 "            for (int j = 0; j < dv; ++j) o[j] += q[c] * S[c * dv + j];\n")
 MUTANTS = [
-    ("decay dropped", r"(?<!d)S\[c \* dv \+ j\] \*= a\[c\];", ";"),
-    ("gate on value columns", r"(?<!d)S\[c \* dv \+ j\] \*= a\[c\];",
-     "S[c * dv + j] *= a[j % dk];"),
-    ("delta term sign", r"\+= b \* k\[c\] \* \(v\[j\] - u\[j\]\)", "-= b * k[c] * (v[j] - u[j])"),
-    ("erase sign", r"\(v\[j\] - u\[j\]\)", "(v[j] + u[j])"),
-    ("readout of S, not S^T", r"o\[j\] \+= q\[c\] \* S\[c \* dv \+ j\];",
-     "o[j] += q[c] * S[(j % dk) * dv + (c % dv)];"),
-    ("beta squared", r"S\[c \* dv \+ j\] \+= b \* k", "S[c * dv + j] += b * b * k"),
+    ("decay dropped", [(r"(?<!d)S\[c \* dv \+ j\] \*= a\[c\];", ";")]),
+    ("gate on value columns", [(r"(?<!d)S\[c \* dv \+ j\] \*= a\[c\];",
+                                "S[c * dv + j] *= a[j % dk];")]),
+    ("delta term sign", [(r"\+= b \* k\[c\] \* \(v\[j\] - u\[j\]\)",
+                          "-= b * k[c] * (v[j] - u[j])")]),
+    ("erase sign", [(r"\(v\[j\] - u\[j\]\)", "(v[j] + u[j])")]),
+    ("readout of S, not S^T", [(r"o\[j\] \+= q\[c\] \* S\[c \* dv \+ j\];",
+                                "o[j] += q[c] * S[(j % dk) * dv + (c % dv)];")]),
+    ("beta squared", [(r"S\[c \* dv \+ j\] \+= b \* k", "S[c * dv + j] += b * b * k")]),
+    ("beta dropped", [(r"S\[c \* dv \+ j\] \+= b \* k", "S[c * dv + j] += k")]),
+    # decay applied after the erase and write instead of before them
+    ("decay after the write", [(_DECAY, ";"),
+                               (r"        /\* readout o = S\^T q \*/",
+                                "        " + _DECAY_TEXT + "\n        /* readout */")]),
+    # the readout taken from the state before token t's erase and write
+    ("readout before the write", [(_READOUT, ""),
+                                  (r"        /\* erase along k and write k v\^T",
+                                   _READOUT_TEXT + "        /* erase along k and write k v^T")]),
 ]
 
 # Mistakes in the backward's adjoint steps (each pattern occurs only there).
@@ -84,11 +104,12 @@ def _pins_fail(tests=None):
     return False
 
 
-@pytest.mark.parametrize("name,pat,rep", MUTANTS, ids=[m[0] for m in MUTANTS])
-def test_pins_catch_mutant(name, pat, rep, monkeypatch):
-    src = open(SRC).read()
-    mutated, n = re.subn(pat, rep, src)
-    assert n >= 1, "mutation pattern no longer matches the oracle source"
+@pytest.mark.parametrize("name,edits", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(name, edits, monkeypatch):
+    mutated = open(SRC).read()
+    for pat, rep in edits:
+        mutated, n = re.subn(pat, lambda m, r=rep: r, mutated, count=1)
+        assert n == 1, f"mutation pattern no longer matches the oracle source: {pat}"
     with tempfile.TemporaryDirectory() as tmp:
         so = _build_mutant(mutated, tmp)
         monkeypatch.setattr(oracle, "_LIB_PATH", so)

@@ -360,3 +360,42 @@ def test_decode_equals_forward():
         ot = oracle.decode_step(q[:, t], k[:, t], v[:, t], g[:, t], beta[:, t], S)
         np.testing.assert_allclose(ot, o[:, t], atol=1e-13)
     np.testing.assert_allclose(S, S_T, atol=1e-13)
+
+
+# ---------------------------------------------------------------- fused q/k normalisation
+
+def test_l2_normalise_hand_values():
+    """The fused key/query normalisation (CKDA summary, "Methodology in Plain
+    English": the Triton variant fuses the signs into the normalisation) as
+    this build reads it: each row x becomes x (sum x^2 + 1e-6)^(-1/2).  Hand
+    values: (3, 4) -> (3, 4) / sqrt(25 + 1e-6); a zero row stays zero; a row
+    far below the epsilon is scaled by about 1000 instead of to unit norm."""
+    got = oracle.l2_normalise(np.array([[3.0, 4.0], [0.0, 0.0], [1e-6, 0.0]]))
+    den = np.sqrt(25.0 + 1e-6)
+    np.testing.assert_array_equal(got[0], [3.0 / den, 4.0 / den])
+    np.testing.assert_array_equal(got[1], [0.0, 0.0])
+    assert got[2, 0] == pytest.approx(1e-6 / np.sqrt(1e-12 + 1e-6), rel=1e-15)
+    assert got[2, 0] == pytest.approx(1e-3, rel=1e-6)
+
+
+def test_l2_normalise_is_per_row_of_the_last_axis():
+    """Unit norm along the last axis for every (token, head) row with sum x^2
+    >> 1e-6, each row independently (a wrong axis or a shared norm fails),
+    direction unchanged, and scale invariance up to the epsilon."""
+    x = RNG.normal(size=(3, 5, 4, 16)) * RNG.uniform(0.1, 10.0, size=(3, 5, 4, 1))
+    y = oracle.l2_normalise(x)
+    norms = np.linalg.norm(y, axis=-1)
+    eps_rel = 1e-6 / np.sum(x * x, axis=-1)
+    np.testing.assert_allclose(norms, 1.0 / np.sqrt(1.0 + eps_rel), rtol=1e-14)
+    cos = np.sum(x * y, axis=-1) / (np.linalg.norm(x, axis=-1) * norms)
+    np.testing.assert_allclose(cos, 1.0, rtol=1e-14)
+    ss = np.sum(x * x, axis=-1, keepdims=True)
+    np.testing.assert_allclose(oracle.l2_normalise(7.0 * x),
+                               y * 7.0 * np.sqrt(ss + 1e-6) / np.sqrt(49.0 * ss + 1e-6),
+                               rtol=1e-14)
+    # one row changed: only that row's output changes
+    x2 = x.copy()
+    x2[1, 2, 3] *= 3.0
+    y2 = oracle.l2_normalise(x2)
+    diff = np.any(y2 != y, axis=-1)
+    assert diff[1, 2, 3] and diff.sum() == 1
