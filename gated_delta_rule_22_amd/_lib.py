@@ -46,6 +46,10 @@ def library() -> ctypes.CDLL:
         lib.kda_forward.restype = ci
         lib.ckda_forward_ex.argtypes = [vp] * 7 + [ci] * 8 + [vp, vp, vp, sz, vp]
         lib.ckda_forward_ex.restype = ci
+        lib.ckda_forward_noalloc.argtypes = [vp] * 7 + [ci] * 8 + [vp, vp, vp]
+        lib.ckda_forward_noalloc.restype = ci
+        lib.ckda_forward_noalloc_max_bytes.argtypes = []
+        lib.ckda_forward_noalloc_max_bytes.restype = sz
         lib.ckda_backward_workspace_bytes.argtypes = [ci] * 7
         lib.ckda_backward_workspace_bytes.restype = sz
         lib.ckda_backward.argtypes = [vp] * 7 + [ci] * 7 + [vp] * 8 + [vp, sz, vp]
@@ -103,7 +107,7 @@ OPT_KDA, OPT_QK_L2NORM, OPT_O_BF16 = 1, 2, 4     # CKDA_OPT_* in include/ckda.h
 
 def forward(q, k, v, g, beta, S0=None, cu_seqlens=None, *, out=None, final_state=None,
             workspace=None, output_final_state=True, normalize_qk=False,
-            out_dtype=torch.float32, kda=False):
+            out_dtype=torch.float32, kda=False, no_alloc=False):
     """CKDA chunkwise forward.  Returns ``(o, S_T)`` (``S_T`` is None when
     ``output_final_state`` is False).  See ``ckda_forward`` in include/ckda.h
     for shapes; ``final_state`` may be ``S0`` itself to advance it in place.
@@ -111,13 +115,18 @@ def forward(q, k, v, g, beta, S0=None, cu_seqlens=None, *, out=None, final_state
     ``normalize_qk`` (L2-normalise q and k rows in the kernel), ``out_dtype``
     (``torch.bfloat16`` for a bf16 ``o``) and ``kda`` (gate signs ignored) map
     to the options of ``ckda_forward_ex``; with none of them set the call goes
-    to ``ckda_forward``."""
+    to ``ckda_forward``.  ``no_alloc=True`` calls ``ckda_forward_noalloc``,
+    which uses the library's fixed scratch instead of a workspace (pass
+    ``out``, and ``final_state`` or ``output_final_state=False``, so that
+    nothing is allocated here either)."""
     if out_dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("out_dtype must be torch.float32 or torch.bfloat16")
     opts = ((OPT_KDA if kda else 0) | (OPT_QK_L2NORM if normalize_qk else 0)
             | (OPT_O_BF16 if out_dtype == torch.bfloat16 else 0))
-    return _forward("ckda_forward_ex" if opts else "ckda_forward", q, k, v, g, beta, S0,
-                    cu_seqlens, out, final_state, workspace, output_final_state, opts)
+    entry = "ckda_forward_noalloc" if no_alloc else (
+        "ckda_forward_ex" if opts else "ckda_forward")
+    return _forward(entry, q, k, v, g, beta, S0, cu_seqlens, out, final_state, workspace,
+                    output_final_state, opts)
 
 
 def kda_forward(q, k, v, g, beta, S0=None, cu_seqlens=None, *, out=None, final_state=None,
@@ -155,11 +164,15 @@ def _forward(entry, q, k, v, g, beta, S0, cu_seqlens, out, final_state, workspac
         S_T = final_state if final_state is not None else torch.empty(
             (N, H, dk, dv), dtype=torch.float32, device=dev)
         _need(S_T, "final_state", torch.float32, (N, H, dk, dv))
+    head = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(cu_seqlens),
+            B, T, H, dk, dv, N, code)
+    if entry == "ckda_forward_noalloc":
+        st = library().ckda_forward_noalloc(*head, opts, _ptr(o), _ptr(S_T), _stream(dev))
+        _check(st, entry)
+        return o, S_T
     ws_bytes = forward_workspace_bytes(B, T, H, dk, dv, N, code)
     if workspace is None or workspace.numel() * workspace.element_size() < ws_bytes:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    head = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(cu_seqlens),
-            B, T, H, dk, dv, N, code)
     tail = (_ptr(o), _ptr(S_T), _ptr(workspace), ws_bytes, _stream(dev))
     fn = getattr(library(), entry)
     st = fn(*head, opts, *tail) if entry == "ckda_forward_ex" else fn(*head, *tail)

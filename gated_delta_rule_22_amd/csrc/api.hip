@@ -10,7 +10,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-#include <vector>
+#include <mutex>
 
 #include "ckda_internal.h"
 
@@ -104,16 +104,23 @@ bool debug_mode() {
 }
 
 // Debug mode: the host copy of cu_seqlens must be non-decreasing from 0 to T.
+// Copied in pieces through a stack buffer, so the check allocates nothing.
 int debug_check_cu(const int32_t *cu_seqlens, int N, int T, hipStream_t st) {
-  std::vector<int32_t> h((size_t)N + 1);
-  if (hipMemcpyAsync(h.data(), cu_seqlens, h.size() * sizeof(int32_t), hipMemcpyDeviceToHost,
-                     st) != hipSuccess ||
-      hipStreamSynchronize(st) != hipSuccess)
-    return CKDA_ERR_LAUNCH;
-  if (h[0] != 0 || h[N] != T) return CKDA_ERR_SHAPE;
-  for (int n = 0; n < N; ++n)
-    if (h[n + 1] < h[n]) return CKDA_ERR_SHAPE;
-  return CKDA_OK;
+  constexpr int kPiece = 256;
+  int32_t h[kPiece];
+  int32_t prev = 0;
+  for (int i0 = 0; i0 <= N; i0 += kPiece) {
+    const int n = (N + 1 - i0) < kPiece ? (N + 1 - i0) : kPiece;
+    if (hipMemcpyAsync(h, cu_seqlens + i0, (size_t)n * sizeof(int32_t), hipMemcpyDeviceToHost,
+                       st) != hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess)
+      return CKDA_ERR_LAUNCH;
+    for (int i = 0; i < n; ++i) {
+      if ((i0 + i == 0 && h[i] != 0) || h[i] < prev) return CKDA_ERR_SHAPE;
+      prev = h[i];
+    }
+  }
+  return prev == T ? CKDA_OK : CKDA_ERR_SHAPE;
 }
 
 // Debug-mode steps shared by the forward and the backward, after validation.
@@ -141,6 +148,8 @@ extern "C" const char *ckda_status_string(int status) {
     case CKDA_ERR_WORKSPACE: return "workspace missing or too small";
     case CKDA_ERR_LAUNCH: return "kernel launch failed";
     case CKDA_ERR_ALIAS: return "an output overlaps an input it may not alias";
+    case CKDA_ERR_SCRATCH:
+      return "the call needs more scratch than the fixed no-allocation buffer holds";
     default: return "unknown status";
   }
 }
@@ -238,6 +247,53 @@ extern "C" int ckda_forward_ex(const void *q, const void *k, const void *v, cons
                                size_t workspace_bytes, void *stream) {
   return forward_impl(q, k, v, g, beta, S0, cu_seqlens, B, T, H, dk, dv, N, in_dtype, options, o,
                       S_T, workspace, workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------- no allocation
+// For callers that cannot allocate (graph capture, tight serving loops): the
+// workspace is a fixed file-scope device array.  Host code never passes the
+// array's name to a kernel; it uses the device address that
+// hipGetSymbolAddress returns for the current device, kept per device.
+namespace {
+
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// Device address of this device's copy of `scratch`, looked up once per
+// device with that device current; NULL if the lookup fails.
+void *static_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" size_t ckda_forward_noalloc_max_bytes(void) { return kStaticScratchBytes; }
+
+extern "C" int ckda_forward_noalloc(const void *q, const void *k, const void *v, const float *g,
+                                    const float *beta, const float *S0,
+                                    const int32_t *cu_seqlens, int B, int T, int H, int dk,
+                                    int dv, int N, int in_dtype, int options, void *o,
+                                    float *S_T, void *stream) {
+  const bool packed = cu_seqlens != nullptr;
+  if (int s = forward_shape_status(B, T, H, dk, dv, N, in_dtype, packed)) return s;
+  if (fwd_layout(B, T, H, dk, dv, N, in_dtype).total > kStaticScratchBytes)
+    return CKDA_ERR_SCRATCH;
+  void *ws = static_scratch();
+  if (!ws) return CKDA_ERR_LAUNCH;
+  return forward_impl(q, k, v, g, beta, S0, cu_seqlens, B, T, H, dk, dv, N, in_dtype, options,
+                      o, S_T, ws, kStaticScratchBytes, stream);
 }
 
 extern "C" size_t ckda_backward_workspace_bytes(int B, int T, int H, int dk, int dv, int N,

@@ -59,7 +59,9 @@ enum {
     CKDA_ERR_ALIGN = 4,      /* a device pointer is misaligned (see conventions) */
     CKDA_ERR_WORKSPACE = 5,  /* workspace missing or smaller than required */
     CKDA_ERR_LAUNCH = 6,     /* the HIP runtime refused a kernel launch */
-    CKDA_ERR_ALIAS = 7       /* an output overlaps an input it may not alias */
+    CKDA_ERR_ALIAS = 7,      /* an output overlaps an input it may not alias */
+    CKDA_ERR_SCRATCH = 8     /* ckda_forward_noalloc: the call needs more scratch than
+                                its fixed buffer holds */
 };
 
 /* Input dtypes for q, k, v.  Gates, beta, states and outputs are fp32. */
@@ -176,6 +178,34 @@ int ckda_forward_ex(const void *q, const void *k, const void *v, const float *g,
                     int B, int T, int H, int dk, int dv, int N, int in_dtype, int options,
                     void *o, float *S_T, void *workspace, size_t workspace_bytes,
                     void *stream);
+
+/*
+ * ckda_forward_ex for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * It takes no workspace: the library keeps one fixed scratch array of
+ * ckda_forward_noalloc_max_bytes() bytes (64 MiB) per GPU, in device memory
+ * that stays held until the process ends, and the call itself allocates
+ * nothing (host or device).  Every other argument, layout, option and error
+ * is that of ckda_forward_ex; the results are bit-identical to it.
+ *
+ *  Returns CKDA_ERR_SCRATCH when ckda_forward_workspace_bytes(...) for the
+ *  call exceeds the fixed size (bf16 inputs need only a sequence table of
+ *  16 bytes per sequence; fp32 inputs need their per-chunk records, so only
+ *  small fp32 calls fit).
+ *
+ *  Concurrency: all calls on one GPU share that GPU's scratch, which keeps
+ *  the last call's contents (nothing in it needs to start at zero).  Calls
+ *  that overlap in time on one GPU -- on different streams, or from
+ *  different host threads without ordering -- race on it and give undefined
+ *  results; order them on one stream.
+ */
+int ckda_forward_noalloc(const void *q, const void *k, const void *v, const float *g,
+                         const float *beta, const float *S0, const int32_t *cu_seqlens,
+                         int B, int T, int H, int dk, int dv, int N, int in_dtype,
+                         int options, void *o, float *S_T, void *stream);
+
+/* Size in bytes of the fixed scratch array ckda_forward_noalloc uses. */
+size_t ckda_forward_noalloc_max_bytes(void);
 
 /*
  * Workspace needed by ckda_backward for the same sizes, in bytes (the same for

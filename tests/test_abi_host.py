@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.ckda_abi_version() == 1
-    for s in range(8):
+    for s in range(9):
         assert lib.ckda_status_string(s)
     assert lib.ckda_status_string(0) == b"ok"
 
@@ -188,3 +188,21 @@ def test_forward_rejects_heads_whose_chunk_offsets_overflow(lib):
         assert _fwd(lib, B=1, T=1, H=65536, dk=64, dv=128, entry=entry) == 2
     assert lib.ckda_forward_workspace_bytes(1, 1, 65536, 128, 128, 1, 0) == 0
     assert lib.ckda_backward_workspace_bytes(1, 1, 65536, 128, 128, 1, 0) == 0
+
+
+def test_noalloc_rejects_bad_sizes_on_the_host(lib):
+    """ckda_forward_noalloc validates like ckda_forward_ex, and rejects a call
+    whose workspace would exceed its fixed scratch with CKDA_ERR_SCRATCH before
+    touching the device (fp32 inputs at B=2, T=4096, H=4, d=128 need ~220 MB
+    of chunk records)."""
+    assert lib.ckda_forward_noalloc_max_bytes() == 64 << 20
+    assert lib.ckda_status_string(8).startswith(b"the call needs more scratch")
+    p = ctypes.c_void_p(16)
+    call = lambda B, T, H, dk, dv, N, dt: lib.ckda_forward_noalloc(
+        p, p, p, p, p, None, None, B, T, H, dk, dv, N, dt, 0, ctypes.c_void_p(1 << 32), None,
+        None)
+    assert call(2, 4096, 4, 128, 128, 2, 1) == 8
+    assert lib.ckda_forward_workspace_bytes(2, 4096, 4, 128, 128, 2, 1) > 64 << 20
+    assert call(2, 64, 2, 96, 128, 2, 0) == 2          # dk not 64/128
+    assert call(2, 64, 2, 128, 128, 3, 0) == 2         # N != B without cu_seqlens
+    assert call(2, 64, 2, 128, 128, 2, 9) == 3         # unknown dtype
