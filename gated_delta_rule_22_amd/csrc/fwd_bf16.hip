@@ -86,29 +86,45 @@ __device__ __forceinline__ f32x4 mfma16x3(f32x4 c, bf16x4 ah, bf16x4 al, bf16x4 
   c = mfma16(ah, bl, c);
   return mfma16(ah, bh, c);
 }
+// Padding between a 16x16x16 bf16 product and the vector instructions that
+// read its accumulator.  On gfx950 the wait states the compiler inserts there
+// were measured too few: the first registers of the result were read stale.
+// Sixteen idle cycles, fenced so that no instruction moves across them.
+__device__ __forceinline__ void settle16() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7");
+  __builtin_amdgcn_sched_barrier(0);
+}
 __device__ __forceinline__ void split1(float x, __bf16 &h, __bf16 &l) {
   h = (__bf16)x;
   l = (__bf16)(x - (float)h);
 }
+// hi/lo split of two fp32 values into packed bf16 pairs (round to nearest
+// even on both parts), with one packed conversion for each part.
+__device__ __forceinline__ void split2(float a, float b, uint32_t &h, uint32_t &l) {
+  const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+  const float ra = a - __builtin_bit_cast(float, hb << 16);
+  const float rb = b - __builtin_bit_cast(float, hb & 0xFFFF0000u);
+  h = hb;
+  l = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){ra, rb}, bf16x2));
+}
 __device__ __forceinline__ void split4(const f32x4 &x, bf16x4 &h, bf16x4 &l) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const __bf16 b = (__bf16)x[e];
-    h[e] = b;
-    l[e] = (__bf16)(x[e] - (float)b);
-  }
+  uint2 hh, ll;
+  split2(x[0], x[1], hh.x, ll.x);
+  split2(x[2], x[3], hh.y, ll.y);
+  h = __builtin_bit_cast(bf16x4, hh);
+  l = __builtin_bit_cast(bf16x4, ll);
 }
 // k-block fragment of two accumulator tiles (rows 0-15 and 16-31 of a 32-row block)
 __device__ __forceinline__ void split8_acc(const f32x4 &t0, const f32x4 &t1, bf16x8 &h,
                                            bf16x8 &l) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const __bf16 b0 = (__bf16)t0[e], b1 = (__bf16)t1[e];
-    h[e] = b0;
-    h[e + 4] = b1;
-    l[e] = (__bf16)(t0[e] - (float)b0);
-    l[e + 4] = (__bf16)(t1[e] - (float)b1);
-  }
+  uint4 hh, ll;
+  split2(t0[0], t0[1], hh.x, ll.x);
+  split2(t0[2], t0[3], hh.y, ll.y);
+  split2(t1[0], t1[1], hh.z, ll.z);
+  split2(t1[2], t1[3], hh.w, ll.w);
+  h = __builtin_bit_cast(bf16x8, hh);
+  l = __builtin_bit_cast(bf16x8, ll);
 }
 // hi/lo split of four fp32 values into packed bf16 pairs (round to nearest
 // even on both parts): x = hi + lo + O(2^-17 |x|).
@@ -179,6 +195,31 @@ __device__ __forceinline__ bf16x4 frag16(const __bf16 *plane, int W, int row, in
   return __builtin_bit_cast(bf16x4,
                             *reinterpret_cast<const uint2 *>(plane + at(row, col0 + 4 * g, W)));
 }
+
+// A per-lane LDS byte offset the compiler must keep in a register: reads at
+// (offset + compile-time constant) then fold the constant into the
+// instruction's 16-bit offset field instead of recomputing the address.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+template <class T>
+__device__ __forceinline__ T lds_at(const char *smem, int base, int imm) {
+  return *reinterpret_cast<const T *>(smem + base + imm);
+}
+// 16x16x32 fragment (accumulator k order) at byte base + imm: the lane's
+// columns 4g..4g+3 and 16+4g..16+4g+3 of a 32-column block.
+__device__ __forceinline__ bf16x8 frag32o(const char *smem, int base, int imm) {
+  const uint2 a = lds_at<uint2>(smem, base, imm);
+  const uint2 b = lds_at<uint2>(smem, base, imm + 32);
+  const uint4 u = {a.x, a.y, b.x, b.y};
+  return __builtin_bit_cast(bf16x8, u);
+}
+__device__ __forceinline__ bf16x4 frag16o(const char *smem, int base, int imm) {
+  return __builtin_bit_cast(bf16x4, lds_at<uint2>(smem, base, imm));
+}
+// byte offset of (row, col) in a bf16 plane of width W (padded rows)
+constexpr int pb(int row, int col, int W) { return 2 * (row * (W + PADB) + col); }
 
 template <int DK>
 struct Prep {                     // chunk-preparation lane geometry (one wave: DK/4 channels)
@@ -797,6 +838,14 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
       asm volatile("" : "+v"(t_opaque));
       const int lane = t_opaque & 63, l16 = lane & 15, gq = lane >> 4;
       const int col = vb * BV + 16 * (t_opaque >> 6) + l16;
+      // per-lane LDS byte offsets of the regions this loop reads
+      const int lpD = pb(l16, 4 * gq, DK), lpC = pb(l16, 4 * gq, C);
+      const int gk_b = opaque(L::GK + lpD), gq_b = opaque(L::GQ + lpD);
+      const int kt_b = opaque(L::KT + lpC), p_b = opaque(L::P + lpC);
+      const int at_b = opaque(L::AT + lpC), fac_b = opaque(L::SPRE + 16 * gq);
+      const int bt_b = opaque(L::BT + 16 * gq);
+      constexpr int LO_D = 2 * C * (DK + PADB), LO_C = 2 * C * (C + PADB);
+      constexpr int LO_T = 2 * DK * (C + PADB);
 
       __syncthreads();   // H1
       if (threadIdx.x == 0) s_flag[(lc + 1) & 1] = 0;
@@ -808,7 +857,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
       auto x_and_o = [&]() {
 #pragma unroll
         for (int tt = 0; tt < ST; ++tt) {
-          const float4 pre = *reinterpret_cast<const float4 *>(s_pre + 16 * tt + 4 * gq);
+          const float4 pre = lds_at<float4>(smem, fac_b, 64 * tt);
           accS[tt][0] *= pre.x; accS[tt][1] *= pre.y; accS[tt][2] *= pre.z; accS[tt][3] *= pre.w;
         }
         bf16x8 sh[KB], sl[KB];
@@ -827,10 +876,10 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
         bf16x8 rk_h[3], rk_l[3], rq_h[3], rq_l[3];
         auto ld = [&](int st) {
           const int mt = st / KB, kb = st % KB, sl3 = st % 3;
-          rk_h[sl3] = frag32(gk_h, DK, 16 * mt + l16, kb, gq);
-          rk_l[sl3] = frag32(gk_l, DK, 16 * mt + l16, kb, gq);
-          rq_h[sl3] = frag32(gq_h, DK, 16 * mt + l16, kb, gq);
-          rq_l[sl3] = frag32(gq_l, DK, 16 * mt + l16, kb, gq);
+          rk_h[sl3] = frag32o(smem, gk_b, pb(16 * mt, 32 * kb, DK));
+          rk_l[sl3] = frag32o(smem, gk_b, LO_D + pb(16 * mt, 32 * kb, DK));
+          rq_h[sl3] = frag32o(smem, gq_b, pb(16 * mt, 32 * kb, DK));
+          rq_l[sl3] = frag32o(smem, gq_b, LO_D + pb(16 * mt, 32 * kb, DK));
         };
         ld(0);
         ld(1);
@@ -860,7 +909,8 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
         // entries below x_m are one row of the store, read four at a time; no
         // read depends on x, so all of them can be in flight early.
         const int I = lane >> 4, j = lane & 15;
-        const float *adb = s_ad + I * ADB;
+        const int ad_b = opaque(L::AD + 4 * I * ADB);
+        const int ti_b = opaque(L::AT + pb(16 * I, 16 * I + j, C));
         float x[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) x[i] = (i == j) ? 1.f : 0.f;
@@ -869,7 +919,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
           float4 r[4];
 #pragma unroll
           for (int q4 = (m + 1) / 4; q4 < 4; ++q4)
-            r[q4] = *reinterpret_cast<const float4 *>(adb + m * ADS + 4 * q4);
+            r[q4] = lds_at<float4>(smem, ad_b, 4 * (m * ADS + 4 * q4));
 #pragma unroll
           for (int i = m + 1; i < 16; ++i) {
             const float4 &rq = r[i / 4];
@@ -881,8 +931,8 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
         for (int i = 0; i < 16; ++i) {
           __bf16 hh, ll;
           split1(x[i], hh, ll);
-          at_h[at(16 * I + i, 16 * I + j, C)] = hh;
-          at_l[at(16 * I + i, 16 * I + j, C)] = ll;
+          *reinterpret_cast<__bf16 *>(smem + ti_b + pb(i, 0, C)) = hh;
+          *reinterpret_cast<__bf16 *>(smem + ti_b + LO_C + pb(i, 0, C)) = ll;
         }
       }
       __syncthreads();   // H4
@@ -896,17 +946,17 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
       bf16x8 c2h, c2l, c3h, c3l;
 #pragma unroll
       for (int I = 0; I < 4; ++I) {
-        dh[I] = frag16(at_h, C, 16 * I + l16, 16 * I, gq);
-        dl[I] = frag16(at_l, C, 16 * I + l16, 16 * I, gq);
+        dh[I] = frag16o(smem, at_b, pb(16 * I, 16 * I, C));
+        dl[I] = frag16o(smem, at_b, LO_C + pb(16 * I, 16 * I, C));
       }
-      b1h = frag16(at_h, C, 16 + l16, 0, gq);
-      b1l = frag16(at_l, C, 16 + l16, 0, gq);
-      c2h = frag32(at_h, C, 32 + l16, 0, gq);
-      c2l = frag32(at_l, C, 32 + l16, 0, gq);
-      c3h = frag32(at_h, C, 48 + l16, 0, gq);
-      c3l = frag32(at_l, C, 48 + l16, 0, gq);
-      b3h = frag16(at_h, C, 48 + l16, 32, gq);
-      b3l = frag16(at_l, C, 48 + l16, 32, gq);
+      b1h = frag16o(smem, at_b, pb(16, 0, C));
+      b1l = frag16o(smem, at_b, LO_C + pb(16, 0, C));
+      c2h = frag32o(smem, at_b, pb(32, 0, C));
+      c2l = frag32o(smem, at_b, LO_C + pb(32, 0, C));
+      c3h = frag32o(smem, at_b, pb(48, 0, C));
+      c3l = frag32o(smem, at_b, LO_C + pb(48, 0, C));
+      b3h = frag16o(smem, at_b, pb(48, 32, C));
+      b3l = frag16o(smem, at_b, LO_C + pb(48, 32, C));
       bf16x4 uh[4], ul[4];
       auto u32h = [&](int kb) { return __builtin_shufflevector(uh[2 * kb], uh[2 * kb + 1], 0, 1, 2, 3, 4, 5, 6, 7); };
       auto u32l = [&](int kb) { return __builtin_shufflevector(ul[2 * kb], ul[2 * kb + 1], 0, 1, 2, 3, 4, 5, 6, 7); };
@@ -914,26 +964,31 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
       constexpr int kPuMt[6] = {0, 1, 2, 2, 3, 3}, kPuKb[6] = {0, 0, 0, 1, 0, 1};
       bf16x8 rp_h[3], rp_l[3];
       auto ldp = [&](int st) {
-        rp_h[st % 3] = frag32(p_h, C, 16 * kPuMt[st] + l16, kPuKb[st], gq);
-        rp_l[st % 3] = frag32(p_l, C, 16 * kPuMt[st] + l16, kPuKb[st], gq);
+        rp_h[st % 3] = frag32o(smem, p_b, pb(16 * kPuMt[st], 32 * kPuKb[st], C));
+        rp_l[st % 3] = frag32o(smem, p_b, LO_C + pb(16 * kPuMt[st], 32 * kPuKb[st], C));
       };
       ldp(0);
       ldp(1);
 #pragma unroll
       for (int I = 0; I < 4; ++I) {
         f32x4 y;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = s_beta[16 * I + 4 * gq + e] * accX[I][e];
+        const float4 bq = lds_at<float4>(smem, bt_b, 64 * I);
+        y[0] = bq.x * accX[I][0];
+        y[1] = bq.y * accX[I][1];
+        y[2] = bq.z * accX[I][2];
+        y[3] = bq.w * accX[I][3];
         if (I == 1) y = mfma16x3(y, b1h, b1l, uh[0], ul[0]);
         if (I == 2) y = mfma32x3(y, c2h, c2l, u32h(0), u32l(0));
         if (I == 3) {
           y = mfma32x3(y, c3h, c3l, u32h(0), u32l(0));
           y = mfma16x3(y, b3h, b3l, uh[2], ul[2]);
         }
+        if (I == 1 || I == 3) settle16();
         bf16x4 yh, yl;
         split4(y, yh, yl);
         f32x4 u = {0.f, 0.f, 0.f, 0.f};
         u = mfma16x3(u, dh[I], dl[I], yh, yl);
+        settle16();
         split4(u, uh[I], ul[I]);
       }
       // ---- O += P U (P is zero above its diagonal blocks); store
@@ -983,8 +1038,8 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
         bf16x8 rt_h[3], rt_l[3];
         auto ld = [&](int st) {
           const int tt = st >> 1, kb = st & 1, sl3 = st % 3;
-          rt_h[sl3] = frag32(kt_h, C, 16 * tt + l16, kb, gq);
-          rt_l[sl3] = frag32(kt_l, C, 16 * tt + l16, kb, gq);
+          rt_h[sl3] = frag32o(smem, kt_b, pb(16 * tt, 32 * kb, C));
+          rt_l[sl3] = frag32o(smem, kt_b, LO_T + pb(16 * tt, 32 * kb, C));
         };
         ld(0);
         ld(1);
@@ -994,12 +1049,14 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
           __builtin_amdgcn_sched_barrier(0);
           const int tt = st >> 1, kb = st & 1, sl3 = st % 3;
           if (kb == 0) {
-            const float4 mid = *reinterpret_cast<const float4 *>(s_mid + 16 * tt + 4 * gq);
-            accS[tt][0] *= mid.x; accS[tt][1] *= mid.y; accS[tt][2] *= mid.z; accS[tt][3] *= mid.w;
+            if (fallback) {   // the mid factor is 1 except on the element-wise path
+              const float4 mid = lds_at<float4>(smem, fac_b, (L::SMID - L::SPRE) + 64 * tt);
+              accS[tt][0] *= mid.x; accS[tt][1] *= mid.y; accS[tt][2] *= mid.z; accS[tt][3] *= mid.w;
+            }
           }
           accS[tt] = mfma32x3(accS[tt], rt_h[sl3], rt_l[sl3], u32h(kb), u32l(kb));
           if (kb == 1) {
-            const float4 post = *reinterpret_cast<const float4 *>(s_post + 16 * tt + 4 * gq);
+            const float4 post = lds_at<float4>(smem, fac_b, (L::SPOST - L::SPRE) + 64 * tt);
             accS[tt][0] *= post.x; accS[tt][1] *= post.y; accS[tt][2] *= post.z; accS[tt][3] *= post.w;
           }
           __builtin_amdgcn_sched_barrier(0);
