@@ -9,7 +9,9 @@ consecutive in-place steps) and reports steps/s and HBM GB/s.
 Inputs are seeded synthetic draws (gated_delta_rule_22_amd.workloads), already
 resident in device memory when the timed region starts.  Timing uses HIP
 events on the stream the library launches on.  The CPU baseline is the fp64
-oracle (test infrastructure) on the same forward workload, on all host cores.
+oracle (test infrastructure) on the same forward workload, on 16 host threads
+(the host's share per GPU on the measurement boxes), with the CPU model and the
+visible thread count recorded beside it.
 
 Prints one JSON line.
 """
@@ -95,6 +97,18 @@ def decode_algorithmic(w):
     return nh * per_head, per_head
 
 
+def _cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo ("unknown" if absent)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -102,6 +116,8 @@ def main():
     # state; the defaults warm up past that and time 100 steps (~55 ms).
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=60)
+    ap.add_argument("--settle-s", type=float, default=0.3,
+                    help="seconds of untimed forward launches before the warm-up steps")
     ap.add_argument("--decode-steps", type=int, default=None,
                     help="decode steps to time (default: the workload's 1024)")
     ap.add_argument("--skip-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -151,6 +167,14 @@ def main():
                                                            torch.bfloat16)),
                          dtype=torch.uint8, device=dev)
         run = lambda: ck.forward(q, k, v, g, beta, out=o, final_state=S_T, workspace=ws)
+        # The clocks ramp up over the first ~30 ms of load, whatever --warmup is:
+        # settle them with untimed launches first, then run the W warm-up steps.
+        t_settle = time.perf_counter()
+        while time.perf_counter() - t_settle < args.settle_s:
+            for _ in range(10):
+                run()
+            torch.cuda.synchronize()
+        out["settle_s"] = round(time.perf_counter() - t_settle, 3)
         for _ in range(args.warmup):
             run()
         torch.cuda.synchronize()
@@ -372,7 +396,8 @@ def main():
                              "reference": "the fp64 oracle on the same inputs"}
         del o_ref, S_ref
         out["cpu_baseline"] = {"value": w.B * w.T / dt, "unit": "tokens/s", "cores": nth,
-                               "kind": "oracle",
+                               "kind": "oracle", "cpu_model": _cpu_model(),
+                               "host_threads_visible": oracle.default_threads(),
                                "sample": f"the whole {w.name} forward (B={w.B}, T={w.T}, H={w.H}), "
                                          f"fp64 token-by-token, {dt:.1f} s"}
         if "backward" in out:

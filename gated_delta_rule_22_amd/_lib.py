@@ -14,7 +14,8 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libckda.so")
+# CKDA_LIB names another build of the same library (e.g. a host-sanitized one).
+LIB_PATH = os.environ.get("CKDA_LIB") or os.path.join(_PKG, "libckda.so")
 
 CKDA_BF16 = 0
 CKDA_F32 = 1

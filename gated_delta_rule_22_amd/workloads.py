@@ -52,6 +52,11 @@ WORKLOADS = {
     # One layer shaped like a 1.3B-parameter LM (hidden 2048 = 16 heads x 128).
     "layer_1p3b_bf16": Workload("layer_1p3b_bf16", B=8, T=4096, H=16, dk=128, dv=128,
                                 dtype="bf16", gate="tanh", q_scale=False, s0="zero"),
+    # The same layer with every eighth key channel forgetting fast (|alpha| in
+    # [0.01, 0.1]): those channels' gates fall by 2^-213 or more over a chunk.
+    "layer_1p3b_fastdecay_bf16": Workload("layer_1p3b_fastdecay_bf16", B=8, T=4096, H=16,
+                                          dk=128, dv=128, dtype="bf16", gate="tanh_fastdecay",
+                                          q_scale=False, s0="zero"),
     # 65536 packed tokens in 12 sequences of log-uniform length.
     "varlen_64k_bf16": Workload("varlen_64k_bf16", B=1, T=65536, H=16, dk=128, dv=128,
                                 dtype="bf16", gate="rotation", q_scale=False, s0="zero",
@@ -92,10 +97,15 @@ def _gates(rng, shape, kind):
     if kind == "rotation":
         neg = rng.random(shape) < 0.5            # gate sign only, |alpha| = 1
         return np.where(neg, -1.0, 1.0)
-    if kind == "tanh":
+    if kind in ("tanh", "tanh_fastdecay"):
         a = np.tanh(rng.normal(0.0, 1.5, shape))  # std 1.5
         sgn = np.where(a < 0, -1.0, 1.0)          # sign(0) := +
-        return sgn * np.maximum(np.abs(a), 1e-3)
+        mag = np.maximum(np.abs(a), 1e-3)
+        if kind == "tanh_fastdecay":
+            # every eighth channel forgets fast: |alpha| uniform in [0.01, 0.1]
+            fast = rng.uniform(0.01, 0.1, shape)
+            mag = np.where(np.arange(shape[-1]) % 8 == 7, fast, mag)
+        return sgn * mag
     raise ValueError(kind)
 
 

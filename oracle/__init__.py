@@ -29,15 +29,21 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ckda_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "libckda_oracle.so")
+# CKDA_ORACLE_SANITIZE=1 builds and loads an AddressSanitizer + UBSan copy
+# instead (the process must then preload gcc's libasan and libubsan).
+_SANITIZE = os.environ.get("CKDA_ORACLE_SANITIZE") == "1"
+_LIB_PATH = os.path.join(_HERE, "libckda_oracle_san.so" if _SANITIZE else "libckda_oracle.so")
 _lib = None
 
 
 def build(force: bool = True) -> str:
-    """Compile the C oracle with gcc into ``oracle/libckda_oracle.so``."""
+    """Compile the C oracle with gcc into ``oracle/libckda_oracle.so`` (or the
+    sanitizer copy, see above)."""
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp"
-        subprocess.check_call(["gcc", "-O2", "-std=c99", "-shared", "-fPIC", "-pthread",
+        flags = (["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                  "-fno-sanitize-recover=undefined"] if _SANITIZE else ["-O2"])
+        subprocess.check_call(["gcc", *flags, "-std=c99", "-shared", "-fPIC", "-pthread",
                                _SRC, "-o", tmp])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
