@@ -343,7 +343,7 @@ def main():
     # ------------------------------------------------------------- other configs (time only)
     if not args.skip_forward and not args.skip_others:
         others = {}
-        for name in ("tiny_f32", "rotation_f32", "varlen_64k_bf16"):
+        for name in ("tiny_f32", "rotation_f32", "varlen_64k_bf16", "layer_1p3b_fastdecay_bf16"):
             wo = wl.WORKLOADS[name]
             xo = wl.forward_inputs(wo)
             dt = torch.bfloat16 if wo.dtype == "bf16" else torch.float32
@@ -353,10 +353,10 @@ def main():
             cu = xo.get("cu_seqlens")
             cu = None if cu is None else torch.from_numpy(np.asarray(cu, np.int32)).to(dev)
             run_o = lambda: ck.forward(qo, ko, vo, go, bo, S0=so, cu_seqlens=cu)
-            for _ in range(5):
+            for _ in range(20):
                 run_o()
             torch.cuda.synchronize()
-            n_o = 20
+            n_o = 30
             e0.record(stream)
             for _ in range(n_o):
                 run_o()
@@ -365,6 +365,9 @@ def main():
             ms_o = e0.elapsed_time(e1) / n_o
             toks = int(xo["q"].shape[0] * xo["q"].shape[1])
             others[name] = {"ms_per_forward": ms_o, "tokens_per_s": toks / (ms_o * 1e-3)}
+            if name == "layer_1p3b_fastdecay_bf16" and "ms_per_step" in out:
+                # strongly forgetting channels against the headline layer
+                others[name]["time_over_layer"] = ms_o / out["ms_per_step"]
             del qo, ko, vo, go, bo, so, cu
         out["other_configs"] = others
         torch.cuda.empty_cache()

@@ -19,16 +19,17 @@
 // live in log space, the sign is kept apart): per channel the block keeps the
 // cumulative sum G of log2|alpha| (each term clamped at -126) and the
 // cumulative parity pi of negative gates.  Only ratios of gammas matter, so
-// each channel is referenced to R = G_n / 2, the middle of its range in the
-// block: gamma' = (-1)^pi 2^(G - R) and 1/gamma' stay within 2^+-100 while the
-// block's log-gate spread is below 200 (gates averaging above 2^-12.5 in
-// magnitude over 16 tokens, or rising at most that much), so A and P are one
-// matrix-core product each of gamma'-scaled operands.  The state absorbs 2^R:
-//   S_pre = 2^R S,  X = V - (gamma' K) S_pre,  O = (gamma' Q) S_pre + P U,
-//   S' = (-1)^pi_n 2^(G_n - R) (S_pre + (K / gamma')^T U).
+// each channel is referenced to the block's last token: gamma' = gamma /
+// gamma_n = (-1)^(pi - pi_n) 2^(G - G_n) and 1/gamma' stay within 2^+-110
+// while no token's log-gate is more than 110 from the block end's (gates
+// averaging above 2^-6.8 in magnitude over 16 tokens), so A and P are one
+// matrix-core product each of gamma'-scaled operands, and the state absorbs
+// gamma_n once per block:
+//   S_pre = Diag(gamma_n) S,  X = V - (gamma' K) S_pre,  O = (gamma' Q) S_pre + P U,
+//   S' = S_pre + (K / gamma')^T U.
 // A block whose spread is wider takes an exact path: A and P element by
-// element from fp32 ratios 2^(G_i - G_j), the operands referenced to the block
-// start, S' = Diag(gamma_n) S + (K gamma_n / gamma)^T U.
+// element from fp32 ratios 2^(G_i - G_j), the row operands referenced to the
+// block start (X = V - (gamma K) S), S' = Diag(gamma_n) S + (K gamma_n / gamma)^T U.
 //
 // Work split inside the workgroup (512 threads), a pipeline with no barrier
 // inside the sequence loop:
@@ -73,7 +74,7 @@ constexpr int BV = 64;           // dv columns per workgroup (16 per state-pass 
 constexpr int PADB = 4;          // bf16 plane row padding (elements)
 constexpr int ADS = 20;          // row stride of the fp32 A tile (16-byte rows)
 constexpr float kLog2Floor = -126.f;
-constexpr float kGuard = 100.f;  // |G - R| bound for the factored A and P
+constexpr float kGuard = 110.f;  // |G - G_n| bound for the factored A and P
 constexpr int kBufferFlags = 0x00020000;   // buffer resource word 3: raw 32-bit data
 constexpr int kSpinLimit = 1 << 18;        // polls of a hand-over counter before giving up
 __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -193,9 +194,8 @@ struct Slot {
   static constexpr int TT = KT + 2 * KTH;       // (I + A)^-1         [CB][CB]
   static constexpr int PT = TT + 2 * TH;        // P, zero above the diagonal
   static constexpr int AD = PT + 2 * TH;        // A fp32, transposed [CB][ADS] (preparation only)
-  static constexpr int PRE = AD + CB * ADS * 4; // pre [DK]  (exact path: Diag(gamma_n))
-  static constexpr int POST = PRE + DK * 4;     // post [DK]
-  static constexpr int BT = POST + DK * 4;      // beta [CB]
+  static constexpr int PRE = AD + CB * ADS * 4; // gamma_n [DK], signed
+  static constexpr int BT = PRE + DK * 4;       // beta [CB]
   static constexpr int MODE = BT + CB * 4;      // 0: factored, 1: exact
   static constexpr int SIZE = MODE + 16;
   // Exact path scratch: G fp32 [CB][DK] and the parity words in the K/gamma'
@@ -462,11 +462,11 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
         exP = tg ? y : 0u;
         endP = __shfl(ptot, (TG - 1) * CG + cg);
       }
-      // the factored form needs |G - R| <= kGuard for every token and channel
+      // the factored form needs |G - G_n| <= kGuard for every token and channel
       float dev = 0.f;
 #pragma unroll
       for (int cc = 0; cc < 8; ++cc) {
-        const float R = 0.5f * Gend[cc];
+        const float R = Gend[cc];
         dev = fmaxf(dev, fmaxf(fabsf(ex[cc] + gmx[cc] - R), fabsf(ex[cc] + gmn[cc] - R)));
       }
       const bool exact = __any(!(dev <= kGuard));
@@ -508,67 +508,69 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
       }
 
       // ---- operands: rows -(gamma' K), gamma' Q and K / gamma', columns (K / gamma')^T.
-      // Factored: both references R = G_n / 2.  Exact: rows referenced to the
-      // block start, columns to its end (all ratios then gamma_n / gamma_t).
+      // Factored: rows gamma' = gamma / gamma_n, columns 1 / gamma'.  Exact: rows
+      // gamma (from the block start), columns gamma_n / gamma.  The row factor's
+      // reference is rref (G_n or 0), its parity reference rpar (pi_n or 0).
+      {
+        const uint32_t rpar = exact ? 0u : endP;
 #pragma unroll
-      for (int r2 = 0; r2 < TPL; r2 += 2) {
-        uint32_t kwh[2][4], kwl[2][4];
+        for (int r2 = 0; r2 < TPL; r2 += 2) {
+          uint32_t kwh[2][4], kwl[2][4];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int r = r2 + u, t = tg * TPL + r;
-          const uint32_t pr = (exP ^ (pbits >> (8 * r))) & 0xFFu;
-          const uint32_t pc = exact ? pr ^ (endP & 0xFFu) : pr;
-          float fk, fq;
-          norm_factors(r, fk, fq);
-          float gk[8], gq[8], kg[8];
+          for (int u = 0; u < 2; ++u) {
+            const int r = r2 + u, t = tg * TPL + r;
+            const uint32_t pr = (exP ^ (pbits >> (8 * r))) & 0xFFu;   // parity from the block start
+            const uint32_t prow = pr ^ (rpar & 0xFFu), pcol = pr ^ (endP & 0xFFu);
+            float fk, fq;
+            norm_factors(r, fk, fq);
+            float gk[8], gq[8], kg[8];
+#pragma unroll
+            for (int cc = 0; cc < 8; ++cc) {
+              const float G = Gv[r][cc];
+              const float kk = bf16_of(in_k[r], cc) * fk, qq = bf16_of(in_q[r], cc) * fq;
+              const float gam = with_sign(fexp2(G - (exact ? 0.f : Gend[cc])), (prow >> cc) & 1u);
+              const float kf = with_sign(fexp2(Gend[cc] - G), (pcol >> cc) & 1u);
+              gk[cc] = -kk * gam;
+              gq[cc] = qq * gam;
+              kg[cc] = kk * kf;
+            }
+            const int ro = 2 * (t * SL::RW + c0);
+            uint2 h0, l0, h1, l1;
+            split_quad(*reinterpret_cast<const float(*)[4]>(gk), h0, l0);
+            split_quad(*reinterpret_cast<const float(*)[4]>(gk + 4), h1, l1);
+            lds_put(smem, sb + SL::GK + ro, h0);
+            lds_put(smem, sb + SL::GK + ro + 8, h1);
+            lds_put(smem, sb + SL::GK + SL::PL + ro, l0);
+            lds_put(smem, sb + SL::GK + SL::PL + ro + 8, l1);
+            split_quad(*reinterpret_cast<const float(*)[4]>(gq), h0, l0);
+            split_quad(*reinterpret_cast<const float(*)[4]>(gq + 4), h1, l1);
+            lds_put(smem, sb + SL::GQ + ro, h0);
+            lds_put(smem, sb + SL::GQ + ro + 8, h1);
+            lds_put(smem, sb + SL::GQ + SL::PL + ro, l0);
+            lds_put(smem, sb + SL::GQ + SL::PL + ro + 8, l1);
+            split_quad(*reinterpret_cast<const float(*)[4]>(kg), h0, l0);
+            split_quad(*reinterpret_cast<const float(*)[4]>(kg + 4), h1, l1);
+            if (!exact) {
+              lds_put(smem, sb + SL::KG + ro, h0);
+              lds_put(smem, sb + SL::KG + ro + 8, h1);
+              lds_put(smem, sb + SL::KG + SL::PL + ro, l0);
+              lds_put(smem, sb + SL::KG + SL::PL + ro + 8, l1);
+            }
+            kwh[u][0] = h0.x; kwh[u][1] = h0.y; kwh[u][2] = h1.x; kwh[u][3] = h1.y;
+            kwl[u][0] = l0.x; kwl[u][1] = l0.y; kwl[u][2] = l1.x; kwl[u][3] = l1.y;
+          }
+          // (K / gamma')^T: channel rows, two consecutive tokens per 4-byte store
 #pragma unroll
           for (int cc = 0; cc < 8; ++cc) {
-            const float G = Gv[r][cc];
-            const float rr = exact ? 0.f : 0.5f * Gend[cc];
-            const float rc = exact ? Gend[cc] : 0.5f * Gend[cc];
-            const float gam = with_sign(fexp2(G - rr), (pr >> cc) & 1u);
-            const float kf = with_sign(fexp2(rc - G), (pc >> cc) & 1u);
-            const float kk = bf16_of(in_k[r], cc) * fk, qq = bf16_of(in_q[r], cc) * fq;
-            gk[cc] = -kk * gam;
-            gq[cc] = qq * gam;
-            kg[cc] = kk * kf;
+            const int sh = 16 * (cc & 1), wd = cc >> 1;
+            const uint32_t hw = ((kwh[0][wd] >> sh) & 0xFFFFu) | (((kwh[1][wd] >> sh) & 0xFFFFu) << 16);
+            const uint32_t lw = ((kwl[0][wd] >> sh) & 0xFFFFu) | (((kwl[1][wd] >> sh) & 0xFFFFu) << 16);
+            const int off = 2 * ((c0 + cc) * SL::TW + tg * TPL + r2);
+            lds_put(smem, sb + SL::KT + off, hw);
+            lds_put(smem, sb + SL::KT + SL::KTH + off, lw);
           }
-          const int ro = 2 * (t * SL::RW + c0);
-          uint2 h0, l0, h1, l1;
-          split_quad(*reinterpret_cast<const float(*)[4]>(gk), h0, l0);
-          split_quad(*reinterpret_cast<const float(*)[4]>(gk + 4), h1, l1);
-          lds_put(smem, sb + SL::GK + ro, h0);
-          lds_put(smem, sb + SL::GK + ro + 8, h1);
-          lds_put(smem, sb + SL::GK + SL::PL + ro, l0);
-          lds_put(smem, sb + SL::GK + SL::PL + ro + 8, l1);
-          split_quad(*reinterpret_cast<const float(*)[4]>(gq), h0, l0);
-          split_quad(*reinterpret_cast<const float(*)[4]>(gq + 4), h1, l1);
-          lds_put(smem, sb + SL::GQ + ro, h0);
-          lds_put(smem, sb + SL::GQ + ro + 8, h1);
-          lds_put(smem, sb + SL::GQ + SL::PL + ro, l0);
-          lds_put(smem, sb + SL::GQ + SL::PL + ro + 8, l1);
-          split_quad(*reinterpret_cast<const float(*)[4]>(kg), h0, l0);
-          split_quad(*reinterpret_cast<const float(*)[4]>(kg + 4), h1, l1);
-          if (!exact) {
-            lds_put(smem, sb + SL::KG + ro, h0);
-            lds_put(smem, sb + SL::KG + ro + 8, h1);
-            lds_put(smem, sb + SL::KG + SL::PL + ro, l0);
-            lds_put(smem, sb + SL::KG + SL::PL + ro + 8, l1);
-          }
-          kwh[u][0] = h0.x; kwh[u][1] = h0.y; kwh[u][2] = h1.x; kwh[u][3] = h1.y;
-          kwl[u][0] = l0.x; kwl[u][1] = l0.y; kwl[u][2] = l1.x; kwl[u][3] = l1.y;
+          __builtin_amdgcn_sched_barrier(0);   // two tokens at a time: bounded live range
         }
-        // (K / gamma')^T: channel rows, two consecutive tokens per 4-byte store
-#pragma unroll
-        for (int cc = 0; cc < 8; ++cc) {
-          const int sh = 16 * (cc & 1), wd = cc >> 1;
-          const uint32_t hw = ((kwh[0][wd] >> sh) & 0xFFFFu) | (((kwh[1][wd] >> sh) & 0xFFFFu) << 16);
-          const uint32_t lw = ((kwl[0][wd] >> sh) & 0xFFFFu) | (((kwl[1][wd] >> sh) & 0xFFFFu) << 16);
-          const int off = 2 * ((c0 + cc) * SL::TW + tg * TPL + r2);
-          lds_put(smem, sb + SL::KT + off, hw);
-          lds_put(smem, sb + SL::KT + SL::KTH + off, lw);
-        }
-        __builtin_amdgcn_sched_barrier(0);   // two tokens at a time: bounded live range
       }
 
       if (!exact) {
@@ -607,6 +609,16 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
         lds_put(smem, sb + SL::PT + SL::TH + 2 * (l * SL::TW + 4 * gg), ll);
       }
 
+      // ---- state factor gamma_n, beta, mode
+      if (tg == 0) {
+        float gn[8];   // gamma_n, signed
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc) gn[cc] = with_sign(fexp2(Gend[cc]), (endP >> cc) & 1u);
+        lds_put(smem, sb + SL::PRE + 4 * c0, make_float4(gn[0], gn[1], gn[2], gn[3]));
+        lds_put(smem, sb + SL::PRE + 4 * c0 + 16, make_float4(gn[4], gn[5], gn[6], gn[7]));
+      }
+      if (lane < CB) lds_put(smem, sb + SL::BT + 4 * lane, in_b);
+      if (lane == 0) lds_put(smem, sb + SL::MODE, exact ? 1 : 0);
       // ---- (I + A)^-1 by right-looking forward substitution, column j per
       // lane: once x_m is final it is subtracted from every later row; row m of
       // the transposed store holds the entries below x_m.
@@ -642,23 +654,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
         }
       }
 
-      // ---- state factors, beta, mode; then hand the slot over
-      if (tg == 0) {
-        float pre[8], post[8];
-#pragma unroll
-        for (int cc = 0; cc < 8; ++cc) {
-          const uint32_t odd = (endP >> cc) & 1u;
-          const float m = fexp2(exact ? Gend[cc] : 0.5f * Gend[cc]);
-          pre[cc] = exact ? with_sign(m, odd) : m;     // exact: Diag(gamma_n)
-          post[cc] = with_sign(m, odd);
-        }
-        lds_put(smem, sb + SL::PRE + 4 * c0, make_float4(pre[0], pre[1], pre[2], pre[3]));
-        lds_put(smem, sb + SL::PRE + 4 * c0 + 16, make_float4(pre[4], pre[5], pre[6], pre[7]));
-        lds_put(smem, sb + SL::POST + 4 * c0, make_float4(post[0], post[1], post[2], post[3]));
-        lds_put(smem, sb + SL::POST + 4 * c0 + 16, make_float4(post[4], post[5], post[6], post[7]));
-      }
-      if (lane < CB) lds_put(smem, sb + SL::BT + 4 * lane, in_b);
-      if (lane == 0) lds_put(smem, sb + SL::MODE, exact ? 1 : 0);
+      // ---- hand the slot over
       publish(s_ready + I, lc + 1, lane == 0);
 
       if ((lc + 1) * C + CB * I < len) load(lc + 1);   // next round's block, in flight meanwhile
@@ -711,12 +707,12 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
           fq_l[s] = frag32o(smem, gqb, SL::PL + 64 * kb);
         };
         ld(0);
-        // ---- S_pre = pre * S (factored blocks), split for the products
+        // ---- S_pre = Diag(gamma_n) S (factored blocks), split for the products
         if (!exact) {
 #pragma unroll
           for (int tt = 0; tt < ST; ++tt) {
-            const float4 pre = lds_at<float4>(smem, sb + SL::PRE, 4 * (16 * tt + 4 * gq));
-            accS[tt][0] *= pre.x; accS[tt][1] *= pre.y; accS[tt][2] *= pre.z; accS[tt][3] *= pre.w;
+            const float4 gn = lds_at<float4>(smem, sb + SL::PRE, 4 * (16 * tt + 4 * gq));
+            accS[tt][0] *= gn.x; accS[tt][1] *= gn.y; accS[tt][2] *= gn.z; accS[tt][3] *= gn.w;
           }
         }
         bf16x8 sh[KB], sl[KB];
@@ -757,26 +753,19 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
         settle16();
         bf16x4 uh, ul;
         split4(u, uh, ul);
-        // ---- O += P U;  S <- post * (S_pre + (K/gamma')^T U)  (exact: Diag(gamma_n) S + ...)
+        // ---- O += P U;  S <- S_pre + (K/gamma')^T U  (exact: Diag(gamma_n) S + ...)
         accO = mfma16x3(accO, ph, pl, uh, ul);
         if (exact) {
 #pragma unroll
           for (int tt = 0; tt < ST; ++tt) {
-            const float4 mid = lds_at<float4>(smem, sb + SL::PRE, 4 * (16 * tt + 4 * gq));
-            accS[tt][0] *= mid.x; accS[tt][1] *= mid.y; accS[tt][2] *= mid.z; accS[tt][3] *= mid.w;
+            const float4 gn = lds_at<float4>(smem, sb + SL::PRE, 4 * (16 * tt + 4 * gq));
+            accS[tt][0] *= gn.x; accS[tt][1] *= gn.y; accS[tt][2] *= gn.z; accS[tt][3] *= gn.w;
           }
         }
 #pragma unroll
         for (int tt = 0; tt < ST; ++tt) accS[tt] = mfma16x3(accS[tt], kh[tt], kl[tt], uh, ul);
-        settle16();
-        if (!exact) {
-#pragma unroll
-          for (int tt = 0; tt < ST; ++tt) {
-            const float4 post = lds_at<float4>(smem, sb + SL::POST, 4 * (16 * tt + 4 * gq));
-            accS[tt][0] *= post.x; accS[tt][1] *= post.y; accS[tt][2] *= post.z; accS[tt][3] *= post.w;
-          }
-        }
         count_done(s_done + I, lane == 0);
+        settle16();
         // ---- store o (rows past the sequence end are dropped by the resource)
         if (OBF16) {
           const int rs = H * DV * 2;

@@ -187,6 +187,13 @@ def test_forward_layer_1p3b_full():
     _check_full(wl.forward_inputs("layer_1p3b_bf16"), "layer_1p3b_bf16")
 
 
+def test_forward_layer_fastdecay_full():
+    """The layer workload with every eighth key channel forgetting fast
+    (|alpha| in [0.01, 0.1]: a fall of 2^-213 or more over 64 tokens): every
+    element of o and S_T against the oracle."""
+    _check_full(wl.forward_inputs("layer_1p3b_fastdecay_bf16"), "layer_1p3b_fastdecay_bf16")
+
+
 def test_forward_varlen_64k_full():
     """12 packed sequences, 65,536 tokens, H=16: every element of o and of the
     per-sequence final states against the oracle."""
