@@ -71,7 +71,7 @@ constexpr int CB = 16;           // tokens per block
 constexpr int NB = C / CB;       // block slots, one preparation wave each
 constexpr int NT = 512;          // 8 waves per workgroup
 constexpr int BV = 64;           // dv columns per workgroup (16 per state-pass wave)
-constexpr int PADB = 4;          // bf16 plane row padding (elements)
+constexpr int PADB = 4;          // [DK][CB] plane and tile row padding (elements)
 constexpr int ADS = 20;          // row stride of the fp32 A tile (16-byte rows)
 constexpr float kLog2Floor = -126.f;
 constexpr float kGuard = 110.f;  // |G - G_n| bound for the factored A and P
@@ -163,13 +163,9 @@ template <class T>
 __device__ __forceinline__ T lds_at(const char *smem, int base, int imm) {
   return *reinterpret_cast<const T *>(smem + base + imm);
 }
-// 16x16x32 fragment (accumulator k order) at byte base + imm: the lane's
-// columns 4g..4g+3 and 16+4g..16+4g+3 of a 32-column block.
-__device__ __forceinline__ bf16x8 frag32o(const char *smem, int base, int imm) {
-  const uint2 a = lds_at<uint2>(smem, base, imm);
-  const uint2 b = lds_at<uint2>(smem, base, imm + 32);
-  const uint4 u = {a.x, a.y, b.x, b.y};
-  return __builtin_bit_cast(bf16x8, u);
+// 16x16x32 fragment stored contiguously (16 bytes at base + imm, 16-byte aligned)
+__device__ __forceinline__ bf16x8 frag32p(const char *smem, int base, int imm) {
+  return __builtin_bit_cast(bf16x8, lds_at<uint4>(smem, base, imm));
 }
 __device__ __forceinline__ bf16x4 frag16o(const char *smem, int base, int imm) {
   return __builtin_bit_cast(bf16x4, lds_at<uint2>(smem, base, imm));
@@ -177,12 +173,13 @@ __device__ __forceinline__ bf16x4 frag16o(const char *smem, int base, int imm) {
 
 // ---------------------------------------------------------------- LDS layout
 // One slot per block position b (0..3): everything the state pass reads for a
-// block, plus the preparation wave's own scratch.  bf16 planes are hi then lo;
-// rows are padded by 8 bytes so 8-byte fragment reads of 16 consecutive rows
-// spread over the banks.
+// block, plus the preparation wave's own scratch.  bf16 planes are hi then lo.
+// [CB][DK] rows are padded by 16 bytes and their channels permuted within each
+// 32-channel block, so a lane's 16x16x32 fragment is one aligned 16-byte read;
+// [DK][CB] rows and the tiles are padded by 8 bytes.
 template <int DK>
 struct Slot {
-  static constexpr int RW = DK + PADB;          // row of a [CB][DK] plane (elements)
+  static constexpr int RW = DK + 8;             // row of a [CB][DK] plane (elements, 16-byte rows)
   static constexpr int PL = CB * RW * 2;        // bytes of one half of such a plane
   static constexpr int TW = CB + PADB;          // row of a [DK][CB] plane or of a tile
   static constexpr int KTH = DK * TW * 2;       // bytes of one half of the [DK][CB] plane
@@ -534,27 +531,32 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
               gq[cc] = qq * gam;
               kg[cc] = kk * kf;
             }
-            const int ro = 2 * (t * SL::RW + c0);
+            // channels are stored permuted within each 32-channel block so that a
+            // lane's eight fragment values (k = 4g..4g+3, 16+4g..16+4g+3) are
+            // contiguous: channel x of the block sits at 8 ((x % 16) / 4) + 4 (x / 16) + x % 4
+            const int xa = c0 % 32, xb = xa + 4, kb0 = c0 - xa;
+            const int ro = 2 * (t * SL::RW + kb0 + 8 * ((xa % 16) / 4) + 4 * (xa / 16));
+            const int ro2 = 2 * (t * SL::RW + kb0 + 8 * ((xb % 16) / 4) + 4 * (xb / 16));
             uint2 h0, l0, h1, l1;
             split_quad(*reinterpret_cast<const float(*)[4]>(gk), h0, l0);
             split_quad(*reinterpret_cast<const float(*)[4]>(gk + 4), h1, l1);
             lds_put(smem, sb + SL::GK + ro, h0);
-            lds_put(smem, sb + SL::GK + ro + 8, h1);
+            lds_put(smem, sb + SL::GK + ro2, h1);
             lds_put(smem, sb + SL::GK + SL::PL + ro, l0);
-            lds_put(smem, sb + SL::GK + SL::PL + ro + 8, l1);
+            lds_put(smem, sb + SL::GK + SL::PL + ro2, l1);
             split_quad(*reinterpret_cast<const float(*)[4]>(gq), h0, l0);
             split_quad(*reinterpret_cast<const float(*)[4]>(gq + 4), h1, l1);
             lds_put(smem, sb + SL::GQ + ro, h0);
-            lds_put(smem, sb + SL::GQ + ro + 8, h1);
+            lds_put(smem, sb + SL::GQ + ro2, h1);
             lds_put(smem, sb + SL::GQ + SL::PL + ro, l0);
-            lds_put(smem, sb + SL::GQ + SL::PL + ro + 8, l1);
+            lds_put(smem, sb + SL::GQ + SL::PL + ro2, l1);
             split_quad(*reinterpret_cast<const float(*)[4]>(kg), h0, l0);
             split_quad(*reinterpret_cast<const float(*)[4]>(kg + 4), h1, l1);
             if (!exact) {
               lds_put(smem, sb + SL::KG + ro, h0);
-              lds_put(smem, sb + SL::KG + ro + 8, h1);
+              lds_put(smem, sb + SL::KG + ro2, h1);
               lds_put(smem, sb + SL::KG + SL::PL + ro, l0);
-              lds_put(smem, sb + SL::KG + SL::PL + ro + 8, l1);
+              lds_put(smem, sb + SL::KG + SL::PL + ro2, l1);
             }
             kwh[u][0] = h0.x; kwh[u][1] = h0.y; kwh[u][2] = h1.x; kwh[u][3] = h1.y;
             kwl[u][0] = l0.x; kwl[u][1] = l0.y; kwl[u][2] = l1.x; kwl[u][3] = l1.y;
@@ -579,16 +581,16 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
         // (g, l) holds row l and columns 4g .. 4g+3.  The wave reads only
         // what it wrote, and LDS serves one wave's accesses in order.
         const int l = lane & 15, gg = lane >> 4;
-        const int rb = sb + 2 * (l * SL::RW + 4 * gg);
+        const int rb = sb + 2 * (l * SL::RW + 8 * gg);
         f32x4 pA = {0.f, 0.f, 0.f, 0.f}, pP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-          const bf16x8 ka_h = frag32o(smem, rb + SL::KG, 64 * kb);
-          const bf16x8 ka_l = frag32o(smem, rb + SL::KG + SL::PL, 64 * kb);
-          const bf16x8 rk_h = frag32o(smem, rb + SL::GK, 64 * kb);
-          const bf16x8 rk_l = frag32o(smem, rb + SL::GK + SL::PL, 64 * kb);
-          const bf16x8 rq_h = frag32o(smem, rb + SL::GQ, 64 * kb);
-          const bf16x8 rq_l = frag32o(smem, rb + SL::GQ + SL::PL, 64 * kb);
+          const bf16x8 ka_h = frag32p(smem, rb + SL::KG, 64 * kb);
+          const bf16x8 ka_l = frag32p(smem, rb + SL::KG + SL::PL, 64 * kb);
+          const bf16x8 rk_h = frag32p(smem, rb + SL::GK, 64 * kb);
+          const bf16x8 rk_l = frag32p(smem, rb + SL::GK + SL::PL, 64 * kb);
+          const bf16x8 rq_h = frag32p(smem, rb + SL::GQ, 64 * kb);
+          const bf16x8 rq_l = frag32p(smem, rb + SL::GQ + SL::PL, 64 * kb);
           pA = mfma32x3(pA, ka_h, ka_l, rk_h, rk_l);
           pP = mfma32x3(pP, ka_h, ka_l, rq_h, rq_l);
         }
@@ -669,7 +671,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         accS[tt][e] = S0 ? S0[(((size_t)n * H + h) * DK + 16 * tt + 4 * gq + e) * DV + col] : 0.f;
-    const int lpD = 2 * (l16 * SL::RW + 4 * gq), lpT = 2 * (l16 * SL::TW + 4 * gq);
+    const int lpD = 2 * (l16 * SL::RW + 8 * gq), lpT = 2 * (l16 * SL::TW + 4 * gq);
     const int rs_v = H * DV * 2;
     // v of the next block, one block ahead
     unsigned short nv[4] = {0, 0, 0, 0};
@@ -701,10 +703,10 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
         bf16x8 fk_h[2], fk_l[2], fq_h[2], fq_l[2];
         auto ld = [&](int kb) {
           const int s = kb & 1;
-          fk_h[s] = frag32o(smem, gkb, 64 * kb);
-          fk_l[s] = frag32o(smem, gkb, SL::PL + 64 * kb);
-          fq_h[s] = frag32o(smem, gqb, 64 * kb);
-          fq_l[s] = frag32o(smem, gqb, SL::PL + 64 * kb);
+          fk_h[s] = frag32p(smem, gkb, 64 * kb);
+          fk_l[s] = frag32p(smem, gkb, SL::PL + 64 * kb);
+          fq_h[s] = frag32p(smem, gqb, 64 * kb);
+          fq_l[s] = frag32p(smem, gqb, SL::PL + 64 * kb);
         };
         ld(0);
         // ---- S_pre = Diag(gamma_n) S (factored blocks), split for the products
