@@ -15,26 +15,27 @@
 //   O    = (gamma Q) S + P U
 //   S'   = Diag(gamma_n) S + (K gamma_n / gamma)^T U
 //
-// Signed gates (CKDA summary, "Methodology in Plain English": gate magnitudes
-// live in log space, the sign is kept apart): per channel the block keeps the
-// cumulative sum G of log2|alpha| (each term clamped at -126) and the
-// cumulative parity pi of negative gates.  Only ratios of gammas matter, so
-// each channel is referenced to the block's last token: gamma' = gamma /
-// gamma_n = (-1)^(pi - pi_n) 2^(G - G_n) and 1/gamma' stay within 2^+-110
-// while no token's log-gate is more than 110 from the block end's (gates
-// averaging above 2^-6.8 in magnitude over 16 tokens), so A and P are one
-// matrix-core product each of gamma'-scaled operands, and the state absorbs
-// gamma_n once per block:
+// Signed gates.  Only ratios of gammas matter, so each channel is referenced
+// to the block's last token: gamma' = gamma / gamma_n = 1 / (product of the
+// gates after the token), formed as a running product of the signed gates
+// (each gate's magnitude floored at 2^-126), so the sign needs no separate
+// bookkeeping.  While every gamma' and 1/gamma' of the block lies within
+// 2^+-110 (gates averaging above 2^-6.8 in magnitude over 16 tokens), A and P
+// are one matrix-core product each of gamma'-scaled operands, and the state
+// absorbs gamma_n once per block:
 //   S_pre = Diag(gamma_n) S,  X = V - (gamma' K) S_pre,  O = (gamma' Q) S_pre + P U,
 //   S' = S_pre + (K / gamma')^T U.
-// A block whose spread is wider takes an exact path: A and P element by
-// element from fp32 ratios 2^(G_i - G_j), the row operands referenced to the
-// block start (X = V - (gamma K) S), S' = Diag(gamma_n) S + (K gamma_n / gamma)^T U.
+// A block whose spread is wider takes an exact path that works in log space,
+// as the CKDA summary ("Methodology in Plain English") keeps gate magnitudes:
+// per channel the cumulative sum G of log2|alpha| (each term floored at -126)
+// and the cumulative parity of negative gates; A and P element by element
+// from fp32 ratios 2^(G_i - G_j), the row operands referenced to the block
+// start (X = V - (gamma K) S), S' = Diag(gamma_n) S + (K gamma_n / gamma)^T U.
 //
 // Work split inside the workgroup (512 threads), a pipeline with no barrier
 // inside the sequence loop:
 //   waves 4-7  preparation: wave 4 + b prepares block b of every 64-token
-//              round (gate scan, gamma'-scaled operands and their hi/lo bf16
+//              round (gate products, gamma'-scaled operands and their hi/lo bf16
 //              split, A and P on matrix cores, (I + A)^-1 by substitution)
 //              into LDS slot b;
 //   waves 0-3  state pass, 16 dv columns each: X, O, U and the state update
@@ -74,7 +75,8 @@ constexpr int BV = 64;           // dv columns per workgroup (16 per state-pass 
 constexpr int PADB = 4;          // [DK][CB] plane and tile row padding (elements)
 constexpr int ADS = 20;          // row stride of the fp32 A tile (16-byte rows)
 constexpr float kLog2Floor = -126.f;
-constexpr float kGuard = 110.f;  // |G - G_n| bound for the factored A and P
+constexpr float kGuardScale = 0x1p110f;   // bound on gamma_n / gamma_t and its inverse
+constexpr float kGateFloor = 0x1p-126f;    // floor of a gate's magnitude
 constexpr int kBufferFlags = 0x00020000;   // buffer resource word 3: raw 32-bit data
 constexpr int kSpinLimit = 1 << 18;        // polls of a hand-over counter before giving up
 __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -414,168 +416,233 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
         }
       };
 
-      // ---- gate scan: G (cumulative log2|alpha|) and the parity of negative
-      // gates, lane-local over the lane's tokens, then across token groups
-      float Gv[TPL][8], gmn[8], gmx[8], tot[8];
-      uint32_t pbits = 0u, ptot = 0u;    // pbits: bit 8r + cc, lane-local inclusive
+      // ---- gate products.  Each gate's magnitude is floored at 2^-126 (a NaN
+      // gate counts as that floor, with its sign bit); KDA mode takes |alpha|.
+      auto gate = [&](int r, int cc) {
+        const float4 &v = in_a[r][cc >> 2];
+        const float a = (cc & 3) == 0 ? v.x : (cc & 3) == 1 ? v.y : (cc & 3) == 2 ? v.z : v.w;
+        const float m = fmaxf(fabsf(a), kGateFloor);
+        return SIGNED ? __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, m) |
+                                                      (__builtin_bit_cast(uint32_t, a) & 0x80000000u))
+                      : m;
+      };
+      // lane-local: the product of the lane's gates, and the extremes of the
+      // products of the gates after each of its tokens (within the lane)
+      float tp[8], smin[8], smax[8];
 #pragma unroll
-      for (int cc = 0; cc < 8; ++cc) tot[cc] = 0.f;
+      for (int cc = 0; cc < 8; ++cc) { tp[cc] = 1.f; smin[cc] = 1.f; smax[cc] = 1.f; }
 #pragma unroll
-      for (int r = 0; r < TPL; ++r) {
-        const float a8[8] = {in_a[r][0].x, in_a[r][0].y, in_a[r][0].z, in_a[r][0].w,
-                             in_a[r][1].x, in_a[r][1].y, in_a[r][1].z, in_a[r][1].w};
-#pragma unroll
-        for (int cc = 0; cc < 8; ++cc) {
-          tot[cc] += fmaxf(flog2(fabsf(a8[cc])), kLog2Floor);
-          Gv[r][cc] = tot[cc];
-          gmn[cc] = r ? fminf(gmn[cc], tot[cc]) : tot[cc];
-          gmx[cc] = r ? fmaxf(gmx[cc], tot[cc]) : tot[cc];
-          if (SIGNED) ptot ^= (__builtin_bit_cast(uint32_t, a8[cc]) >> 31) << cc;
-        }
-        pbits |= ptot << (8 * r);
-      }
-#pragma unroll
-      for (int d = 1; d < TG; d <<= 1) {
+      for (int r = TPL - 1; r >= 0; --r)
 #pragma unroll
         for (int cc = 0; cc < 8; ++cc) {
-          const float y = __shfl_up(tot[cc], d * CG);
-          if (tg >= d) tot[cc] += y;
+          if (r < TPL - 1) {
+            smin[cc] = fminf(smin[cc], fabsf(tp[cc]));
+            smax[cc] = fmaxf(smax[cc], fabsf(tp[cc]));
+          }
+          tp[cc] *= gate(r, cc);
         }
-        if (SIGNED) {
-          const uint32_t y = __shfl_up(ptot, d * CG);
-          if (tg >= d) ptot ^= y;
+      // across token groups: exS = product of the gates of all later groups,
+      // gn = gamma_n, the product of all sixteen
+      float exS[8], gn[8];
+#pragma unroll
+      for (int d = 1; d < TG; d <<= 1)
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc) {
+          const float y = __shfl_down(tp[cc], d * CG);
+          if (tg + d < TG) tp[cc] *= y;
         }
-      }
-      float ex[8], Gend[8];
 #pragma unroll
       for (int cc = 0; cc < 8; ++cc) {
-        const float y = __shfl_up(tot[cc], CG);
-        ex[cc] = tg ? y : 0.f;
-        Gend[cc] = __shfl(tot[cc], (TG - 1) * CG + cg);
+        const float y = __shfl_down(tp[cc], CG);
+        exS[cc] = tg + 1 < TG ? y : 1.f;
+        gn[cc] = __shfl(tp[cc], cg);
       }
-      uint32_t exP = 0u, endP = 0u;
-      if (SIGNED) {
-        const uint32_t y = __shfl_up(ptot, CG);
-        exP = tg ? y : 0u;
-        endP = __shfl(ptot, (TG - 1) * CG + cg);
-      }
-      // the factored form needs |G - G_n| <= kGuard for every token and channel
-      float dev = 0.f;
+      // the factored form needs every gamma_n / gamma_t within 2^+-110
+      bool bad = false;
 #pragma unroll
       for (int cc = 0; cc < 8; ++cc) {
-        const float R = Gend[cc];
-        dev = fmaxf(dev, fmaxf(fabsf(ex[cc] + gmx[cc] - R), fabsf(ex[cc] + gmn[cc] - R)));
+        const float e = fabsf(exS[cc]);
+        bad |= !(e * smax[cc] <= kGuardScale && e * smin[cc] >= 1.f / kGuardScale);
       }
-      const bool exact = __any(!(dev <= kGuard));
-#pragma unroll
-      for (int r = 0; r < TPL; ++r)
-#pragma unroll
-        for (int cc = 0; cc < 8; ++cc) Gv[r][cc] += ex[cc];   // G from the block start
+      const bool exact = __any(bad);
 
       // ---- the slot is free once the state pass is done with the previous round
       wait_for(s_done + I, 4 * lc);
 
+      // (K / gamma')^T of tokens r2, r2 + 1 (hi and lo words of eight channels
+      // each): channel rows, two consecutive tokens per 4-byte store
+      auto kt_store = [&](int r2, const uint32_t (&kwh)[2][4], const uint32_t (&kwl)[2][4]) {
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc) {
+          const int sh = 16 * (cc & 1), wd = cc >> 1;
+          const uint32_t hw = ((kwh[0][wd] >> sh) & 0xFFFFu) | (((kwh[1][wd] >> sh) & 0xFFFFu) << 16);
+          const uint32_t lw = ((kwl[0][wd] >> sh) & 0xFFFFu) | (((kwl[1][wd] >> sh) & 0xFFFFu) << 16);
+          const int off = 2 * ((c0 + cc) * SL::TW + tg * TPL + r2);
+          lds_put(smem, sb + SL::KT + off, hw);
+          lds_put(smem, sb + SL::KT + SL::KTH + off, lw);
+        }
+      };
+
+      // exact path: G at the block end, parities (block start to the lane's
+      // first token, and of the whole block), lane-local parities
+      float Gend[8];
+      uint32_t exP = 0u, endP = 0u, pbits = 0u;
+      auto g_at = [&](int r, int hf) {    // exact path: G of the lane's token r, channels 4 hf ..
+        return lds_at<float4>(smem, sb + SL::XG + 4 * ((tg * TPL + r) * DK + c0), 16 * hf);
+      };
       if (exact) {
-        // G and the parities into LDS (and, with NORM, the per-token factors
-        // into the T tile, written only later), then A and P element by element
+        // Exact path.  G (cumulative log2|alpha|, each term floored at -126) and
+        // the parities of negative gates go to LDS rather than registers: the
+        // lane-local running sums first, then the earlier token groups' prefix is
+        // added in place.
+        float tot[8];
+        uint32_t ptot = 0u;
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc) tot[cc] = 0.f;
 #pragma unroll
         for (int r = 0; r < TPL; ++r) {
-          const int t = tg * TPL + r;
-          lds_put(smem, sb + SL::XG + 4 * (t * DK + c0),
-                  make_float4(Gv[r][0], Gv[r][1], Gv[r][2], Gv[r][3]));
-          lds_put(smem, sb + SL::XG + 4 * (t * DK + c0) + 16,
-                  make_float4(Gv[r][4], Gv[r][5], Gv[r][6], Gv[r][7]));
-          if (NORM) {
-            float fk, fq;
-            norm_factors(r, fk, fq);
-            if (cg == 0) lds_put(smem, sb + SL::TT + 8 * t, make_float2(fk, fq));
+          const float a8[8] = {in_a[r][0].x, in_a[r][0].y, in_a[r][0].z, in_a[r][0].w,
+                               in_a[r][1].x, in_a[r][1].y, in_a[r][1].z, in_a[r][1].w};
+#pragma unroll
+          for (int cc = 0; cc < 8; ++cc) {
+            tot[cc] += fmaxf(flog2(fabsf(a8[cc])), kLog2Floor);
+            if (SIGNED) ptot ^= (__builtin_bit_cast(uint32_t, a8[cc]) >> 31) << cc;
+          }
+          const int go = SL::XG + 4 * ((tg * TPL + r) * DK + c0);
+          lds_put(smem, sb + go, make_float4(tot[0], tot[1], tot[2], tot[3]));
+          lds_put(smem, sb + go + 16, make_float4(tot[4], tot[5], tot[6], tot[7]));
+          pbits |= ptot << (8 * r);
+        }
+#pragma unroll
+        for (int d = 1; d < TG; d <<= 1) {
+#pragma unroll
+          for (int cc = 0; cc < 8; ++cc) {
+            const float y = __shfl_up(tot[cc], d * CG);
+            if (tg >= d) tot[cc] += y;
+          }
+          if (SIGNED) {
+            const uint32_t y = __shfl_up(ptot, d * CG);
+            if (tg >= d) ptot ^= y;
           }
         }
+        float ex[8];
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc) {
+          const float y = __shfl_up(tot[cc], CG);
+          ex[cc] = tg ? y : 0.f;
+          Gend[cc] = __shfl(tot[cc], (TG - 1) * CG + cg);
+        }
+        if (SIGNED) {
+          const uint32_t y = __shfl_up(ptot, CG);
+          exP = tg ? y : 0u;
+          endP = __shfl(ptot, (TG - 1) * CG + cg);
+        }
+#pragma unroll
+        for (int r = 0; r < TPL; ++r)
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            float4 gg = g_at(r, hf);
+            gg.x += ex[4 * hf]; gg.y += ex[4 * hf + 1]; gg.z += ex[4 * hf + 2]; gg.w += ex[4 * hf + 3];
+            lds_put(smem, sb + SL::XG + 4 * ((tg * TPL + r) * DK + c0) + 16 * hf, gg);
+          }
         {
           uint32_t pw = 0u;
 #pragma unroll
           for (int r = 0; r < TPL; ++r) pw |= ((exP ^ (pbits >> (8 * r))) & 0xFFu) << (8 * r);
           lds_put(smem, sb + SL::XP + 4 * lane, pw);
         }
+        if (NORM) {    // per-token factors into the T tile (written only later)
+#pragma unroll
+          for (int r = 0; r < TPL; ++r) {
+            float fk, fq;
+            norm_factors(r, fk, fq);
+            if (cg == 0) lds_put(smem, sb + SL::TT + 8 * (tg * TPL + r), make_float2(fk, fq));
+          }
+        }
         const size_t row0 = (size_t)(start + tb) * H + h;
         const int rsk = H * DK * 2;
         exact_tiles<DK, SIGNED, NORM>(smem, sb, lane, __shfl(in_b, lane >> 2),
                                       rsrc(k + row0 * DK, (nbt - 1) * rsk + DK * 2),
                                       rsrc(q + row0 * DK, (nbt - 1) * rsk + DK * 2), rsk);
+
       }
 
-      // ---- operands: rows -(gamma' K), gamma' Q and K / gamma', columns (K / gamma')^T.
-      // Factored: rows gamma' = gamma / gamma_n, columns 1 / gamma'.  Exact: rows
-      // gamma (from the block start), columns gamma_n / gamma.  The row factor's
-      // reference is rref (G_n or 0), its parity reference rpar (pi_n or 0).
-      {
-        const uint32_t rpar = exact ? 0u : endP;
+      // ---- operands: rows gamma' K and gamma' Q, columns K / gamma'.  Factored:
+      // gamma' = gamma_t / gamma_n = 1 / (product of the gates after t), a running
+      // product going backwards from the block end.  Exact: rows gamma_t (from the
+      // block start) and columns gamma_n / gamma_t, from G.
+      float run[8];
 #pragma unroll
-        for (int r2 = 0; r2 < TPL; r2 += 2) {
-          uint32_t kwh[2][4], kwl[2][4];
+      for (int cc = 0; cc < 8; ++cc) run[cc] = exS[cc];
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int r = r2 + u, t = tg * TPL + r;
-            const uint32_t pr = (exP ^ (pbits >> (8 * r))) & 0xFFu;   // parity from the block start
-            const uint32_t prow = pr ^ (rpar & 0xFFu), pcol = pr ^ (endP & 0xFFu);
-            float fk, fq;
-            norm_factors(r, fk, fq);
-            float gk[8], gq[8], kg[8];
+      for (int r2 = TPL - 2; r2 >= 0; r2 -= 2) {
+        uint32_t kwh[2][4], kwl[2][4];
+#pragma unroll
+        for (int u = 1; u >= 0; --u) {
+          const int r = r2 + u, t = tg * TPL + r;
+          float fk, fq;
+          norm_factors(r, fk, fq);
+          float gam8[8], kf8[8];
+          if (!exact) {
 #pragma unroll
             for (int cc = 0; cc < 8; ++cc) {
-              const float G = Gv[r][cc];
-              const float kk = bf16_of(in_k[r], cc) * fk, qq = bf16_of(in_q[r], cc) * fq;
-              const float gam = with_sign(fexp2(G - (exact ? 0.f : Gend[cc])), (prow >> cc) & 1u);
-              const float kf = with_sign(fexp2(Gend[cc] - G), (pcol >> cc) & 1u);
-              gk[cc] = -kk * gam;
-              gq[cc] = qq * gam;
-              kg[cc] = kk * kf;
+              const float sa = run[cc];                      // gamma_n / gamma_t
+              gam8[cc] = __builtin_amdgcn_rcpf(sa);         // gamma'
+              kf8[cc] = sa;
+              run[cc] = sa * gate(r, cc);
             }
-            // channels are stored permuted within each 32-channel block so that a
-            // lane's eight fragment values (k = 4g..4g+3, 16+4g..16+4g+3) are
-            // contiguous: channel x of the block sits at 8 ((x % 16) / 4) + 4 (x / 16) + x % 4
-            const int xa = c0 % 32, xb = xa + 4, kb0 = c0 - xa;
-            const int ro = 2 * (t * SL::RW + kb0 + 8 * ((xa % 16) / 4) + 4 * (xa / 16));
-            const int ro2 = 2 * (t * SL::RW + kb0 + 8 * ((xb % 16) / 4) + 4 * (xb / 16));
-            uint2 h0, l0, h1, l1;
-            split_quad(*reinterpret_cast<const float(*)[4]>(gk), h0, l0);
-            split_quad(*reinterpret_cast<const float(*)[4]>(gk + 4), h1, l1);
-            lds_put(smem, sb + SL::GK + ro, h0);
-            lds_put(smem, sb + SL::GK + ro2, h1);
-            lds_put(smem, sb + SL::GK + SL::PL + ro, l0);
-            lds_put(smem, sb + SL::GK + SL::PL + ro2, l1);
-            split_quad(*reinterpret_cast<const float(*)[4]>(gq), h0, l0);
-            split_quad(*reinterpret_cast<const float(*)[4]>(gq + 4), h1, l1);
-            lds_put(smem, sb + SL::GQ + ro, h0);
-            lds_put(smem, sb + SL::GQ + ro2, h1);
-            lds_put(smem, sb + SL::GQ + SL::PL + ro, l0);
-            lds_put(smem, sb + SL::GQ + SL::PL + ro2, l1);
-            split_quad(*reinterpret_cast<const float(*)[4]>(kg), h0, l0);
-            split_quad(*reinterpret_cast<const float(*)[4]>(kg + 4), h1, l1);
-            if (!exact) {
-              lds_put(smem, sb + SL::KG + ro, h0);
-              lds_put(smem, sb + SL::KG + ro2, h1);
-              lds_put(smem, sb + SL::KG + SL::PL + ro, l0);
-              lds_put(smem, sb + SL::KG + SL::PL + ro2, l1);
+          } else {
+            const uint32_t pr = (exP ^ (pbits >> (8 * r))) & 0xFFu;   // parity from the block start
+            const uint32_t pc = pr ^ (endP & 0xFFu);
+            const float4 g0 = g_at(r, 0), g1 = g_at(r, 1);
+            const float G8[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+            for (int cc = 0; cc < 8; ++cc) {
+              gam8[cc] = with_sign(fexp2(G8[cc]), (pr >> cc) & 1u);
+              kf8[cc] = with_sign(fexp2(Gend[cc] - G8[cc]), (pc >> cc) & 1u);
             }
-            kwh[u][0] = h0.x; kwh[u][1] = h0.y; kwh[u][2] = h1.x; kwh[u][3] = h1.y;
-            kwl[u][0] = l0.x; kwl[u][1] = l0.y; kwl[u][2] = l1.x; kwl[u][3] = l1.y;
           }
-          // (K / gamma')^T: channel rows, two consecutive tokens per 4-byte store
+          float gk[8], gq[8], kg[8];
 #pragma unroll
           for (int cc = 0; cc < 8; ++cc) {
-            const int sh = 16 * (cc & 1), wd = cc >> 1;
-            const uint32_t hw = ((kwh[0][wd] >> sh) & 0xFFFFu) | (((kwh[1][wd] >> sh) & 0xFFFFu) << 16);
-            const uint32_t lw = ((kwl[0][wd] >> sh) & 0xFFFFu) | (((kwl[1][wd] >> sh) & 0xFFFFu) << 16);
-            const int off = 2 * ((c0 + cc) * SL::TW + tg * TPL + r2);
-            lds_put(smem, sb + SL::KT + off, hw);
-            lds_put(smem, sb + SL::KT + SL::KTH + off, lw);
+            const float kk = bf16_of(in_k[r], cc) * fk, qq = bf16_of(in_q[r], cc) * fq;
+            gk[cc] = -kk * gam8[cc];
+            gq[cc] = qq * gam8[cc];
+            kg[cc] = kk * kf8[cc];
           }
-          __builtin_amdgcn_sched_barrier(0);   // two tokens at a time: bounded live range
+          const int xa = c0 % 32, xb = xa + 4, kb0 = c0 - xa;
+          const int ro = 2 * (t * SL::RW + kb0 + 8 * ((xa % 16) / 4) + 4 * (xa / 16));
+          const int ro2 = 2 * (t * SL::RW + kb0 + 8 * ((xb % 16) / 4) + 4 * (xb / 16));
+          uint2 h0, l0, h1, l1;
+          split_quad(*reinterpret_cast<const float(*)[4]>(gk), h0, l0);
+          split_quad(*reinterpret_cast<const float(*)[4]>(gk + 4), h1, l1);
+          lds_put(smem, sb + SL::GK + ro, h0);
+          lds_put(smem, sb + SL::GK + ro2, h1);
+          lds_put(smem, sb + SL::GK + SL::PL + ro, l0);
+          lds_put(smem, sb + SL::GK + SL::PL + ro2, l1);
+          split_quad(*reinterpret_cast<const float(*)[4]>(gq), h0, l0);
+          split_quad(*reinterpret_cast<const float(*)[4]>(gq + 4), h1, l1);
+          lds_put(smem, sb + SL::GQ + ro, h0);
+          lds_put(smem, sb + SL::GQ + ro2, h1);
+          lds_put(smem, sb + SL::GQ + SL::PL + ro, l0);
+          lds_put(smem, sb + SL::GQ + SL::PL + ro2, l1);
+          split_quad(*reinterpret_cast<const float(*)[4]>(kg), h0, l0);
+          split_quad(*reinterpret_cast<const float(*)[4]>(kg + 4), h1, l1);
+          if (!exact) {   // the exact path keeps its G table in this region
+            lds_put(smem, sb + SL::KG + ro, h0);
+            lds_put(smem, sb + SL::KG + ro2, h1);
+            lds_put(smem, sb + SL::KG + SL::PL + ro, l0);
+            lds_put(smem, sb + SL::KG + SL::PL + ro2, l1);
+          }
+          kwh[u][0] = h0.x; kwh[u][1] = h0.y; kwh[u][2] = h1.x; kwh[u][3] = h1.y;
+          kwl[u][0] = l0.x; kwl[u][1] = l0.y; kwl[u][2] = l1.x; kwl[u][3] = l1.y;
         }
+        kt_store(r2, kwh, kwl);
+        __builtin_amdgcn_sched_barrier(0);   // two tokens at a time: bounded live range
       }
 
       if (!exact) {
+
         // ---- A and P for the block, computed transposed: the MFMA's row operand
         // is K/gamma', its column operand -(gamma' K) or gamma' Q, so lane
         // (g, l) holds row l and columns 4g .. 4g+3.  The wave reads only
@@ -613,9 +680,6 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
 
       // ---- state factor gamma_n, beta, mode
       if (tg == 0) {
-        float gn[8];   // gamma_n, signed
-#pragma unroll
-        for (int cc = 0; cc < 8; ++cc) gn[cc] = with_sign(fexp2(Gend[cc]), (endP >> cc) & 1u);
         lds_put(smem, sb + SL::PRE + 4 * c0, make_float4(gn[0], gn[1], gn[2], gn[3]));
         lds_put(smem, sb + SL::PRE + 4 * c0 + 16, make_float4(gn[4], gn[5], gn[6], gn[7]));
       }
