@@ -642,7 +642,6 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
       }
 
       if (!exact) {
-
         // ---- A and P for the block, computed transposed: the MFMA's row operand
         // is K/gamma', its column operand -(gamma' K) or gamma' Q, so lane
         // (g, l) holds row l and columns 4g .. 4g+3.  The wave reads only
