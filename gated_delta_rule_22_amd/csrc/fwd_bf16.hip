@@ -178,19 +178,21 @@ __device__ __forceinline__ bf16x4 frag16o(const char *smem, int base, int imm) {
 // block, plus the preparation wave's own scratch.  bf16 planes are hi then lo.
 // [CB][DK] rows are padded by 16 bytes and their channels permuted within each
 // 32-channel block, so a lane's 16x16x32 fragment is one aligned 16-byte read;
-// [DK][CB] rows and the tiles are padded by 8 bytes.
+// the tiles' rows are padded by 8 bytes.  (K / gamma')^T is kept in 16x16x16
+// fragment order: one 16-byte unit per (16-channel tile, lane), the hi and lo
+// words of tokens 4g, 4g+1 then of 4g+2, 4g+3 (kt_unit).
 template <int DK>
 struct Slot {
   static constexpr int RW = DK + 8;             // row of a [CB][DK] plane (elements, 16-byte rows)
   static constexpr int PL = CB * RW * 2;        // bytes of one half of such a plane
   static constexpr int TW = CB + PADB;          // row of a [DK][CB] plane or of a tile
-  static constexpr int KTH = DK * TW * 2;       // bytes of one half of the [DK][CB] plane
+  static constexpr int KTS = 16 * 129 * (DK / 32);   // bytes of the (K / gamma')^T fragments
   static constexpr int TH = CB * TW * 2;        // bytes of one half of a 16 x 16 tile
   static constexpr int GK = 0;                  // -(gamma' K)        [CB][DK]
   static constexpr int GQ = GK + 2 * PL;        // gamma' Q           [CB][DK]
   static constexpr int KG = GQ + 2 * PL;        // K / gamma'         [CB][DK] (preparation only)
-  static constexpr int KT = KG + 2 * PL;        // (K / gamma')^T     [DK][CB]
-  static constexpr int TT = KT + 2 * KTH;       // (I + A)^-1         [CB][CB]
+  static constexpr int KT = KG + 2 * PL;        // (K / gamma')^T     16-byte units (kt_unit)
+  static constexpr int TT = KT + KTS;           // (I + A)^-1         [CB][CB]
   static constexpr int PT = TT + 2 * TH;        // P, zero above the diagonal
   static constexpr int AD = PT + 2 * TH;        // A fp32, transposed [CB][ADS] (preparation only)
   static constexpr int PRE = AD + CB * ADS * 4; // gamma_n [DK], signed
@@ -211,8 +213,26 @@ struct PrepGeom {                 // preparation lanes: 8 channels x TPL tokens 
   static constexpr int CG = DK / 8;       // channel groups
   static constexpr int TG = 64 / CG;      // token groups
   static constexpr int TPL = CB / TG;     // tokens per lane
-  static_assert(TG * TPL == CB && TPL >= 2, "preparation geometry");
+  static_assert(TG * TPL == CB && TPL >= 2 && CG % 4 == 0, "preparation geometry");
+  // Channel group cg holds channels base .. base+3 (cc = 0..3) and base+16 ..
+  // base+19 (cc = 4..7), base = 32 (cg / 4) + 4 (cg % 4): the eight are one
+  // 16-byte run of the permuted [CB][DK] planes.
+  static __device__ __forceinline__ int base(int cg) { return 32 * (cg / 4) + 4 * (cg % 4); }
+  static __device__ __forceinline__ int chan(int cg, int cc) {
+    return base(cg) + (cc & 3) + 16 * (cc >> 2);
+  }
+  static __device__ __forceinline__ int group_of(int c) { return 4 * (c / 32) + (c % 16) / 4; }
+  static __device__ __forceinline__ int index_of(int c) { return 4 * ((c % 32) / 16) + c % 4; }
 };
+
+// Unit of (16-channel tile tt, lane group g, row l16) among the (K / gamma')^T
+// fragments.  Tiles go in pairs of 128 units plus one unit of padding: a
+// state-pass lane group reads sixteen consecutive units, and the sixteen
+// preparation lanes that store one channel slot each (channel 32a + 4m + i,
+// a, m = 0..3) reach units a + 4m + const modulo 16, all in different banks.
+__device__ __forceinline__ int kt_unit(int tt, int g, int l16) {
+  return 129 * (tt >> 1) + 64 * (tt & 1) + 16 * g + l16;
+}
 
 // Hand-over counters in LDS.  Every lane of a wave reads the same word, so the
 // polling loop is uniform; it gives up after kSpinLimit polls, so a wait can
@@ -266,7 +286,8 @@ __device__ __forceinline__ void exact_tiles(char *smem, int sb, int lane, float 
   const uint32_t *xp = reinterpret_cast<const uint32_t *>(smem + sb + SL::XP);
   const float *xf = reinterpret_cast<const float *>(smem + sb + SL::TT);   // [CB][2] factors
   auto par1 = [&](int t, int c) {    // parity of (t, c)
-    return (xp[(t / TPL) * CG + c / 8] >> ((t % TPL) * 8 + (c % 8))) & 1u;
+    using PG = PrepGeom<DK>;
+    return (xp[(t / TPL) * CG + PG::group_of(c)] >> ((t % TPL) * 8 + PG::index_of(c))) & 1u;
   };
   auto bf = [](unsigned short x) { return __builtin_bit_cast(float, (uint32_t)x << 16); };
   float accA[4] = {0.f, 0.f, 0.f, 0.f}, accP[4] = {0.f, 0.f, 0.f, 0.f};
@@ -353,7 +374,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
   if (w >= 4) {
     // ======================= preparation: wave 4 + I fills slot I
     const int I = w - 4, sb = I * SLOT;
-    const int tg = lane / CG, cg = lane % CG, c0 = 8 * cg;
+    const int tg = lane / CG, cg = lane % CG, ca = PG::base(cg);
     float4 in_a[TPL][2];
     uint4 in_k[TPL], in_q[TPL];
     float in_b = 0.f;
@@ -368,10 +389,14 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
 #pragma unroll
       for (int r = 0; r < TPL; ++r) {
         const int t = tg * TPL + r;
-        in_a[r][0] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rg, t * rsg + 4 * c0, 0, 0));
-        in_a[r][1] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rg, t * rsg + 4 * c0 + 16, 0, 0));
-        in_k[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, t * rsk + 2 * c0, 0, 0));
-        in_q[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, t * rsk + 2 * c0, 0, 0));
+        in_a[r][0] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rg, t * rsg + 4 * ca, 0, 0));
+        in_a[r][1] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rg, t * rsg + 4 * ca + 64, 0, 0));
+        const uint2 k0 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rk, t * rsk + 2 * ca, 0, 0));
+        const uint2 k1 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rk, t * rsk + 2 * ca + 32, 0, 0));
+        const uint2 q0 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rq, t * rsk + 2 * ca, 0, 0));
+        const uint2 q1 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rq, t * rsk + 2 * ca + 32, 0, 0));
+        in_k[r] = make_uint4(k0.x, k0.y, k1.x, k1.y);
+        in_q[r] = make_uint4(q0.x, q0.y, q1.x, q1.y);
       }
       const auto rb = rsrc(beta + row0, (nbt - 1) * H * 4 + 4);
       in_b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, lane * H * 4, 0, 0));
@@ -469,17 +494,20 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
       // ---- the slot is free once the state pass is done with the previous round
       wait_for(s_done + I, 4 * lc);
 
-      // (K / gamma')^T of tokens r2, r2 + 1 (hi and lo words of eight channels
-      // each): channel rows, two consecutive tokens per 4-byte store
+      // (K / gamma')^T of tokens t0 = tg * TPL + r2 and t0 + 1 (hi and lo words
+      // of eight channels each): per channel, the hi and lo words of the token
+      // pair go to their fragment unit in one 8-byte store
       auto kt_store = [&](int r2, const uint32_t (&kwh)[2][4], const uint32_t (&kwl)[2][4]) {
+        // channel ca + (cc & 3) + 16 (cc >> 2) sits in tile 2 (cg / 4) + (cc >> 2), row
+        // 4 (cg % 4) + (cc & 3): a lane base plus a constant per cc
+        const int t0 = tg * TPL + r2;
+        const int kb = sb + SL::KT + 16 * kt_unit(2 * (cg >> 2), t0 >> 2, 4 * (cg & 3)) + 8 * ((t0 >> 1) & 1);
 #pragma unroll
         for (int cc = 0; cc < 8; ++cc) {
           const int sh = 16 * (cc & 1), wd = cc >> 1;
           const uint32_t hw = ((kwh[0][wd] >> sh) & 0xFFFFu) | (((kwh[1][wd] >> sh) & 0xFFFFu) << 16);
           const uint32_t lw = ((kwl[0][wd] >> sh) & 0xFFFFu) | (((kwl[1][wd] >> sh) & 0xFFFFu) << 16);
-          const int off = 2 * ((c0 + cc) * SL::TW + tg * TPL + r2);
-          lds_put(smem, sb + SL::KT + off, hw);
-          lds_put(smem, sb + SL::KT + SL::KTH + off, lw);
+          lds_put(smem, kb + 16 * kt_unit(cc >> 2, 0, cc & 3), make_uint2(hw, lw));
         }
       };
 
@@ -488,7 +516,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
       float Gend[8];
       uint32_t exP = 0u, endP = 0u, pbits = 0u;
       auto g_at = [&](int r, int hf) {    // exact path: G of the lane's token r, channels 4 hf ..
-        return lds_at<float4>(smem, sb + SL::XG + 4 * ((tg * TPL + r) * DK + c0), 16 * hf);
+        return lds_at<float4>(smem, sb + SL::XG + 4 * ((tg * TPL + r) * DK + ca), 64 * hf);
       };
       if (exact) {
         // Exact path.  G (cumulative log2|alpha|, each term floored at -126) and
@@ -508,9 +536,9 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
             tot[cc] += fmaxf(flog2(fabsf(a8[cc])), kLog2Floor);
             if (SIGNED) ptot ^= (__builtin_bit_cast(uint32_t, a8[cc]) >> 31) << cc;
           }
-          const int go = SL::XG + 4 * ((tg * TPL + r) * DK + c0);
+          const int go = SL::XG + 4 * ((tg * TPL + r) * DK + ca);
           lds_put(smem, sb + go, make_float4(tot[0], tot[1], tot[2], tot[3]));
-          lds_put(smem, sb + go + 16, make_float4(tot[4], tot[5], tot[6], tot[7]));
+          lds_put(smem, sb + go + 64, make_float4(tot[4], tot[5], tot[6], tot[7]));
           pbits |= ptot << (8 * r);
         }
 #pragma unroll
@@ -543,7 +571,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
           for (int hf = 0; hf < 2; ++hf) {
             float4 gg = g_at(r, hf);
             gg.x += ex[4 * hf]; gg.y += ex[4 * hf + 1]; gg.z += ex[4 * hf + 2]; gg.w += ex[4 * hf + 3];
-            lds_put(smem, sb + SL::XG + 4 * ((tg * TPL + r) * DK + c0) + 16 * hf, gg);
+            lds_put(smem, sb + SL::XG + 4 * ((tg * TPL + r) * DK + ca) + 64 * hf, gg);
           }
         {
           uint32_t pw = 0u;
@@ -610,29 +638,22 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
             gq[cc] = qq * gam8[cc];
             kg[cc] = kk * kf8[cc];
           }
-          const int xa = c0 % 32, xb = xa + 4, kb0 = c0 - xa;
-          const int ro = 2 * (t * SL::RW + kb0 + 8 * ((xa % 16) / 4) + 4 * (xa / 16));
-          const int ro2 = 2 * (t * SL::RW + kb0 + 8 * ((xb % 16) / 4) + 4 * (xb / 16));
+          // the lane's eight channels are one 16-byte run of the permuted row
+          const int ro = 2 * (t * SL::RW + 8 * cg);
           uint2 h0, l0, h1, l1;
           split_quad(*reinterpret_cast<const float(*)[4]>(gk), h0, l0);
           split_quad(*reinterpret_cast<const float(*)[4]>(gk + 4), h1, l1);
-          lds_put(smem, sb + SL::GK + ro, h0);
-          lds_put(smem, sb + SL::GK + ro2, h1);
-          lds_put(smem, sb + SL::GK + SL::PL + ro, l0);
-          lds_put(smem, sb + SL::GK + SL::PL + ro2, l1);
+          lds_put(smem, sb + SL::GK + ro, make_uint4(h0.x, h0.y, h1.x, h1.y));
+          lds_put(smem, sb + SL::GK + SL::PL + ro, make_uint4(l0.x, l0.y, l1.x, l1.y));
           split_quad(*reinterpret_cast<const float(*)[4]>(gq), h0, l0);
           split_quad(*reinterpret_cast<const float(*)[4]>(gq + 4), h1, l1);
-          lds_put(smem, sb + SL::GQ + ro, h0);
-          lds_put(smem, sb + SL::GQ + ro2, h1);
-          lds_put(smem, sb + SL::GQ + SL::PL + ro, l0);
-          lds_put(smem, sb + SL::GQ + SL::PL + ro2, l1);
+          lds_put(smem, sb + SL::GQ + ro, make_uint4(h0.x, h0.y, h1.x, h1.y));
+          lds_put(smem, sb + SL::GQ + SL::PL + ro, make_uint4(l0.x, l0.y, l1.x, l1.y));
           split_quad(*reinterpret_cast<const float(*)[4]>(kg), h0, l0);
           split_quad(*reinterpret_cast<const float(*)[4]>(kg + 4), h1, l1);
           if (!exact) {   // the exact path keeps its G table in this region
-            lds_put(smem, sb + SL::KG + ro, h0);
-            lds_put(smem, sb + SL::KG + ro2, h1);
-            lds_put(smem, sb + SL::KG + SL::PL + ro, l0);
-            lds_put(smem, sb + SL::KG + SL::PL + ro2, l1);
+            lds_put(smem, sb + SL::KG + ro, make_uint4(h0.x, h0.y, h1.x, h1.y));
+            lds_put(smem, sb + SL::KG + SL::PL + ro, make_uint4(l0.x, l0.y, l1.x, l1.y));
           }
           kwh[u][0] = h0.x; kwh[u][1] = h0.y; kwh[u][2] = h1.x; kwh[u][3] = h1.y;
           kwl[u][0] = l0.x; kwl[u][1] = l0.y; kwl[u][2] = l1.x; kwl[u][3] = l1.y;
@@ -679,8 +700,8 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
 
       // ---- state factor gamma_n, beta, mode
       if (tg == 0) {
-        lds_put(smem, sb + SL::PRE + 4 * c0, make_float4(gn[0], gn[1], gn[2], gn[3]));
-        lds_put(smem, sb + SL::PRE + 4 * c0 + 16, make_float4(gn[4], gn[5], gn[6], gn[7]));
+        lds_put(smem, sb + SL::PRE + 4 * ca, make_float4(gn[0], gn[1], gn[2], gn[3]));
+        lds_put(smem, sb + SL::PRE + 4 * ca + 64, make_float4(gn[4], gn[5], gn[6], gn[7]));
       }
       if (lane < CB) lds_put(smem, sb + SL::BT + 4 * lane, in_b);
       if (lane == 0) lds_put(smem, sb + SL::MODE, exact ? 1 : 0);
@@ -795,14 +816,15 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
           __builtin_amdgcn_sched_barrier(0);
         }
         // fragments of T, P and (K/gamma')^T for the rest of the block
-        const int ttb = sb + SL::TT + lpT, ptb = sb + SL::PT + lpT, ktb = sb + SL::KT + lpT;
+        const int ttb = sb + SL::TT + lpT, ptb = sb + SL::PT + lpT;
         const bf16x4 th = frag16o(smem, ttb, 0), tl = frag16o(smem, ttb, SL::TH);
         const bf16x4 ph = frag16o(smem, ptb, 0), pl = frag16o(smem, ptb, SL::TH);
         bf16x4 kh[ST], kl[ST];
 #pragma unroll
         for (int tt = 0; tt < ST; ++tt) {
-          kh[tt] = frag16o(smem, ktb, 32 * tt * SL::TW);
-          kl[tt] = frag16o(smem, ktb, SL::KTH + 32 * tt * SL::TW);
+          const uint4 w = lds_at<uint4>(smem, sb + SL::KT + 16 * kt_unit(0, gq, l16), 16 * kt_unit(tt, 0, 0));
+          kh[tt] = __builtin_bit_cast(bf16x4, make_uint2(w.x, w.z));
+          kl[tt] = __builtin_bit_cast(bf16x4, make_uint2(w.y, w.w));
         }
         const float4 bq = lds_at<float4>(smem, sb + SL::BT, 16 * gq);
         // ---- U = (I + A)^-1 Diag(beta) X
