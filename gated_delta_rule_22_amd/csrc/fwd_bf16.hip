@@ -36,8 +36,8 @@
 // inside the sequence loop:
 //   waves 4-7  preparation: wave 4 + b prepares block b of every 64-token
 //              round (gate products, gamma'-scaled operands and their hi/lo bf16
-//              split, A and P on matrix cores, (I + A)^-1 by substitution)
-//              into LDS slot b;
+//              split, A and P on matrix cores, (I + A)^-1 by substitution, a
+//              row per quad of lanes) into LDS slot b;
 //   waves 0-3  state pass, 16 dv columns each: X, O, U and the state update
 //              on matrix cores, slot after slot.
 // Two LDS counters per slot hand it over: `ready` (the slot holds round r's
@@ -47,14 +47,14 @@
 //
 // Precision: every contraction whose operands are not raw bf16 inputs splits
 // each fp32 operand x into hi = bf16(x) and lo = bf16(x - hi) and accumulates
-// hi*hi + hi*lo + lo*hi in fp32 (three MFMAs), keeping ~16 mantissa bits.
+// hi*hi + hi*lo + lo*hi in fp32, keeping ~16 mantissa bits: three MFMAs over
+// 32 channels, or two over 16 tokens (both halves of a 32-deep product used).
 //
-// MFMA shapes (lane l, g = l / 16):
-//   16x16x32: A row l%16 / B column l%16 hold k = 8g .. 8g+7; C rows 4g..4g+3.
-//     An accumulator pair used as a B operand supplies k rows
-//     {4g..4g+3, 16+4g..16+4g+3}; the matching A operand is read in that order.
-//   16x16x16: A row / B column l%16 hold k = 4g .. 4g+3, the accumulator layout,
-//     so a 16-token accumulator is directly the next product's B operand.
+// MFMA shape, 16x16x32 only (lane l, g = l / 16): A row l%16 / B column l%16
+// hold k = 8g .. 8g+7; C rows 4g .. 4g+3.  An accumulator pair used as a B
+// operand supplies k rows {4g..4g+3, 16+4g..16+4g+3}; the matching A operand
+// is read in that order.  Over 16 tokens, lane g's k slots are tokens 4g ..
+// 4g+3 twice: once against the hi operand, once against the lo one.
 #include "ckda_internal.h"
 
 namespace ckda {
@@ -72,7 +72,6 @@ constexpr int CB = 16;           // tokens per block
 constexpr int NB = C / CB;       // block slots, one preparation wave each
 constexpr int NT = 512;          // 8 waves per workgroup
 constexpr int BV = 64;           // dv columns per workgroup (16 per state-pass wave)
-constexpr int PADB = 4;          // [DK][CB] plane and tile row padding (elements)
 constexpr int ADS = 20;          // row stride of the fp32 A tile (16-byte rows)
 constexpr float kLog2Floor = -126.f;
 constexpr float kGuardScale = 0x1p110f;   // bound on gamma_n / gamma_t and its inverse
@@ -82,32 +81,11 @@ constexpr int kSpinLimit = 1 << 18;        // polls of a hand-over counter befor
 __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
 // acc += a*b with a = ah + al, b = bh + bl (al*bl dropped).
 __device__ __forceinline__ f32x4 mfma32x3(f32x4 c, bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl) {
   c = mfma32(al, bh, c);
   c = mfma32(ah, bl, c);
   return mfma32(ah, bh, c);
-}
-__device__ __forceinline__ f32x4 mfma16x3(f32x4 c, bf16x4 ah, bf16x4 al, bf16x4 bh, bf16x4 bl) {
-  c = mfma16(al, bh, c);
-  c = mfma16(ah, bl, c);
-  return mfma16(ah, bh, c);
-}
-// Padding between a 16x16x16 bf16 product and the vector instructions that
-// read its accumulator.  On gfx950 the wait states the compiler inserts there
-// were measured too few: the first registers of the result were read stale.
-// Sixteen idle cycles, fenced so that no instruction moves across them.
-__device__ __forceinline__ void settle16() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_nop 7\n\ts_nop 7");
-  __builtin_amdgcn_sched_barrier(0);
-}
-__device__ __forceinline__ void split1(float x, __bf16 &h, __bf16 &l) {
-  h = (__bf16)x;
-  l = (__bf16)(x - (float)h);
 }
 // hi/lo split of two fp32 values into packed bf16 pairs (round to nearest
 // even on both parts), with one packed conversion for each part.
@@ -169,32 +147,45 @@ __device__ __forceinline__ T lds_at(const char *smem, int base, int imm) {
 __device__ __forceinline__ bf16x8 frag32p(const char *smem, int base, int imm) {
   return __builtin_bit_cast(bf16x8, lds_at<uint4>(smem, base, imm));
 }
-__device__ __forceinline__ bf16x4 frag16o(const char *smem, int base, int imm) {
-  return __builtin_bit_cast(bf16x4, lds_at<uint2>(smem, base, imm));
+// a fragment unit as the 16x16x32 operand [hi | lo]
+__device__ __forceinline__ bf16x8 as_frag8(const uint4 &w) { return __builtin_bit_cast(bf16x8, w); }
+__device__ __forceinline__ bf16x8 cat8(const bf16x4 &a, const bf16x4 &b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+// v from lane s of each quad of lanes (s constant after unrolling)
+__device__ __forceinline__ float quad_bcast(float v, int s) {
+  const int x = __builtin_bit_cast(int, v);
+  switch (s) {
+    case 0: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(x, 0x00, 0xF, 0xF, false));
+    case 1: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(x, 0x55, 0xF, 0xF, false));
+    case 2: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(x, 0xAA, 0xF, 0xF, false));
+    default: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(x, 0xFF, 0xF, 0xF, false));
+  }
 }
 
 // ---------------------------------------------------------------- LDS layout
 // One slot per block position b (0..3): everything the state pass reads for a
 // block, plus the preparation wave's own scratch.  bf16 planes are hi then lo.
 // [CB][DK] rows are padded by 16 bytes and their channels permuted within each
-// 32-channel block, so a lane's 16x16x32 fragment is one aligned 16-byte read;
-// the tiles' rows are padded by 8 bytes.  (K / gamma')^T is kept in 16x16x16
-// fragment order: one 16-byte unit per (16-channel tile, lane), the hi and lo
-// words of tokens 4g, 4g+1 then of 4g+2, 4g+3 (kt_unit).
+// 32-channel block, so a lane's 16x16x32 fragment is one aligned 16-byte read.
+// (K / gamma')^T, T and P are kept in fragment order: one 16-byte unit per
+// (16-row tile, lane (l16, g)), the four hi bf16 of row l16, columns 4g .. 4g+3,
+// then the four lo ones.  Read whole, a unit is the 16x16x32 operand [hi | lo]:
+// against [b_hi | b_hi] it gives hi b_hi + lo b_hi, against [b_lo | 0] hi b_lo.
 template <int DK>
 struct Slot {
   static constexpr int RW = DK + 8;             // row of a [CB][DK] plane (elements, 16-byte rows)
   static constexpr int PL = CB * RW * 2;        // bytes of one half of such a plane
-  static constexpr int TW = CB + PADB;          // row of a [DK][CB] plane or of a tile
   static constexpr int KTS = 16 * 129 * (DK / 32);   // bytes of the (K / gamma')^T fragments
-  static constexpr int TH = CB * TW * 2;        // bytes of one half of a 16 x 16 tile
+  static constexpr int TU = 64 * 16;            // bytes of a 16 x 16 tile in fragment units
   static constexpr int GK = 0;                  // -(gamma' K)        [CB][DK]
   static constexpr int GQ = GK + 2 * PL;        // gamma' Q           [CB][DK]
   static constexpr int KG = GQ + 2 * PL;        // K / gamma'         [CB][DK] (preparation only)
   static constexpr int KT = KG + 2 * PL;        // (K / gamma')^T     16-byte units (kt_unit)
-  static constexpr int TT = KT + KTS;           // (I + A)^-1         [CB][CB]
-  static constexpr int PT = TT + 2 * TH;        // P, zero above the diagonal
-  static constexpr int AD = PT + 2 * TH;        // A fp32, transposed [CB][ADS] (preparation only)
+  static constexpr int TT = KT + KTS;           // T = (I + A)^-1     fragment units
+  static constexpr int PT = TT + TU;            // P, zero above the diagonal, fragment units
+  static constexpr int AD = PT + TU;            // A fp32 [CB][ADS], zero on and above the
+                                                // diagonal (preparation only)
   static constexpr int PRE = AD + CB * ADS * 4; // gamma_n [DK], signed
   static constexpr int BT = PRE + DK * 4;       // beta [CB]
   static constexpr int MODE = BT + CB * 4;      // 0: factored, 1: exact
@@ -213,7 +204,7 @@ struct PrepGeom {                 // preparation lanes: 8 channels x TPL tokens 
   static constexpr int CG = DK / 8;       // channel groups
   static constexpr int TG = 64 / CG;      // token groups
   static constexpr int TPL = CB / TG;     // tokens per lane
-  static_assert(TG * TPL == CB && TPL >= 2 && CG % 4 == 0, "preparation geometry");
+  static_assert(TG * TPL == CB && (TPL == 2 || TPL == 4) && CG % 4 == 0, "preparation geometry");
   // Channel group cg holds channels base .. base+3 (cc = 0..3) and base+16 ..
   // base+19 (cc = 4..7), base = 32 (cg / 4) + 4 (cg % 4): the eight are one
   // 16-byte run of the permuted [CB][DK] planes.
@@ -309,16 +300,17 @@ __device__ __forceinline__ void exact_tiles(char *smem, int sb, int lane, float 
     }
   }
   const float fki = NORM ? xf[2 * ii] : 1.f, fqi = NORM ? xf[2 * ii + 1] : 1.f;
-  float *ad = reinterpret_cast<float *>(smem + sb + SL::AD);
+  float av[4], pv[4];
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
     const int j = 4 * jq + jj;
-    ad[j * ADS + ii] = j < ii ? bi * fki * accA[jj] : 0.f;
-    __bf16 hh, ll;
-    split1(j <= ii ? fqi * accP[jj] : 0.f, hh, ll);
-    lds_put(smem, sb + SL::PT + 2 * (ii * SL::TW + j), hh);
-    lds_put(smem, sb + SL::PT + SL::TH + 2 * (ii * SL::TW + j), ll);
+    av[jj] = j < ii ? bi * fki * accA[jj] : 0.f;
+    pv[jj] = j <= ii ? fqi * accP[jj] : 0.f;
   }
+  lds_put(smem, sb + SL::AD + 4 * (ii * ADS + 4 * jq), make_float4(av[0], av[1], av[2], av[3]));
+  uint2 hh, ll;
+  split_quad(pv, hh, ll);
+  lds_put(smem, sb + SL::PT + 16 * (16 * jq + ii), make_uint4(hh.x, hh.y, ll.x, ll.y));
 }
 
 // ---------------------------------------------------------------- kernel
@@ -497,17 +489,36 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
       // (K / gamma')^T of tokens t0 = tg * TPL + r2 and t0 + 1 (hi and lo words
       // of eight channels each): per channel, the hi and lo words of the token
       // pair go to their fragment unit in one 8-byte store
+      // (K / gamma')^T of tokens t0 = tg * TPL + r2 and t0 + 1: per channel, the
+      // hi and lo words of the pair (two tokens each).  A unit holds, for tokens
+      // 4g .. 4g+3, [hi 4g,4g+1 | hi 4g+2,4g+3 | lo 4g,4g+1 | lo 4g+2,4g+3], so the
+      // state pass reads both 8-byte fragments in place.  Four tokens per lane
+      // (dk = 128): the later pair's words wait in ph/pl and each unit is one
+      // 16-byte store; two (dk = 64): one 4-byte store per word.
+      uint32_t ph[8], pl[8];
       auto kt_store = [&](int r2, const uint32_t (&kwh)[2][4], const uint32_t (&kwl)[2][4]) {
         // channel ca + (cc & 3) + 16 (cc >> 2) sits in tile 2 (cg / 4) + (cc >> 2), row
         // 4 (cg % 4) + (cc & 3): a lane base plus a constant per cc
         const int t0 = tg * TPL + r2;
-        const int kb = sb + SL::KT + 16 * kt_unit(2 * (cg >> 2), t0 >> 2, 4 * (cg & 3)) + 8 * ((t0 >> 1) & 1);
+        const int kb = sb + SL::KT + 16 * kt_unit(2 * (cg >> 2), t0 >> 2, 4 * (cg & 3));
 #pragma unroll
         for (int cc = 0; cc < 8; ++cc) {
           const int sh = 16 * (cc & 1), wd = cc >> 1;
           const uint32_t hw = ((kwh[0][wd] >> sh) & 0xFFFFu) | (((kwh[1][wd] >> sh) & 0xFFFFu) << 16);
           const uint32_t lw = ((kwl[0][wd] >> sh) & 0xFFFFu) | (((kwl[1][wd] >> sh) & 0xFFFFu) << 16);
-          lds_put(smem, kb + 16 * kt_unit(cc >> 2, 0, cc & 3), make_uint2(hw, lw));
+          const int ko = kb + 16 * kt_unit(cc >> 2, 0, cc & 3);
+          if (TPL == 4) {
+            if (r2 == 2) {
+              ph[cc] = hw;
+              pl[cc] = lw;
+            } else {
+              lds_put(smem, ko, make_uint4(hw, ph[cc], lw, pl[cc]));
+            }
+          } else {
+            const int pw = 4 * ((t0 >> 1) & 1);
+            lds_put(smem, ko + pw, hw);
+            lds_put(smem, ko + 8 + pw, lw);
+          }
         }
       };
 
@@ -681,21 +692,20 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
           pA = mfma32x3(pA, ka_h, ka_l, rk_h, rk_l);
           pP = mfma32x3(pP, ka_h, ka_l, rq_h, rq_l);
         }
-        // pA holds -A_lj / beta_l; A goes to the fp32 store transposed, zero on
-        // and above the diagonal
+        // pA holds -A_lj / beta_l: row l of A, zero on and above the diagonal, to
+        // the fp32 store; row l of P to its fragment unit (l, gg)
         const float bl = __shfl(in_b, l);
-        float *ad = reinterpret_cast<float *>(smem + sb + SL::AD);
-        float pv[4];
+        float av[4], pv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int j = 4 * gg + e;
-          ad[j * ADS + l] = j < l ? -pA[e] * bl : 0.f;
+          av[e] = j < l ? -pA[e] * bl : 0.f;
           pv[e] = j <= l ? pP[e] : 0.f;
         }
+        lds_put(smem, sb + SL::AD + 4 * (l * ADS + 4 * gg), make_float4(av[0], av[1], av[2], av[3]));
         uint2 hh, ll;
         split_quad(pv, hh, ll);
-        lds_put(smem, sb + SL::PT + 2 * (l * SL::TW + 4 * gg), hh);
-        lds_put(smem, sb + SL::PT + SL::TH + 2 * (l * SL::TW + 4 * gg), ll);
+        lds_put(smem, sb + SL::PT + 16 * lane, make_uint4(hh.x, hh.y, ll.x, ll.y));
       }
 
       // ---- state factor gamma_n, beta, mode
@@ -705,39 +715,32 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
       }
       if (lane < CB) lds_put(smem, sb + SL::BT + 4 * lane, in_b);
       if (lane == 0) lds_put(smem, sb + SL::MODE, exact ? 1 : 0);
-      // ---- (I + A)^-1 by right-looking forward substitution, column j per
-      // lane: once x_m is final it is subtracted from every later row; row m of
-      // the transposed store holds the entries below x_m.
-      if (lane < CB) {
-        const int j = lane;
-        const int adb = sb + SL::AD;
-        float x[CB];
+      // ---- T = (I + A)^-1, row i per quad of lanes: lane 4i + q holds T[i][4q ..
+      // 4q+3].  T (I + A) = I gives T[i][j] = delta_ij - sum_{k > j} T[i][k] A[k][j];
+      // for k from 15 down, T[i][k] is then final: it is broadcast within the
+      // quad and, times row k of A (zero from column k on), subtracted from the
+      // quad's columns.  The finished row goes to fragment unit (i, q).
+      {
+        const int i = lane >> 2, q = lane & 3;
+        const int adq = sb + SL::AD + 16 * q;
+        float x[4];
 #pragma unroll
-        for (int i = 0; i < CB; ++i) x[i] = (i == j) ? 1.f : 0.f;
-        float4 rw[2][4];
+        for (int r = 0; r < 4; ++r) x[r] = (4 * q + r == i) ? 1.f : 0.f;
+        float4 ar[2];
+        ar[(CB - 1) & 1] = lds_at<float4>(smem, adq, 4 * (CB - 1) * ADS);
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) rw[0][q4] = lds_at<float4>(smem, adb, 16 * q4);
-#pragma unroll
-        for (int m = 0; m < CB - 1; ++m) {
-          if (m + 1 < CB - 1) {
-#pragma unroll
-            for (int q4 = (m + 2) / 4; q4 < 4; ++q4)
-              rw[(m + 1) & 1][q4] = lds_at<float4>(smem, adb, 4 * ((m + 1) * ADS + 4 * q4));
-          }
-#pragma unroll
-          for (int i = m + 1; i < CB; ++i) {
-            const float4 &rq = rw[m & 1][i / 4];
-            const float a = (i & 3) == 0 ? rq.x : (i & 3) == 1 ? rq.y : (i & 3) == 2 ? rq.z : rq.w;
-            x[i] -= a * x[m];
-          }
+        for (int kk = CB - 1; kk >= 1; --kk) {
+          if (kk > 1) ar[(kk - 1) & 1] = lds_at<float4>(smem, adq, 4 * (kk - 1) * ADS);
+          const float tk = quad_bcast(x[kk & 3], kk >> 2);
+          const float4 &a = ar[kk & 1];
+          x[0] -= tk * a.x;
+          x[1] -= tk * a.y;
+          x[2] -= tk * a.z;
+          x[3] -= tk * a.w;
         }
-#pragma unroll
-        for (int i = 0; i < CB; ++i) {
-          __bf16 hh, ll;
-          split1(x[i], hh, ll);
-          lds_put(smem, sb + SL::TT + 2 * (i * SL::TW + j), hh);
-          lds_put(smem, sb + SL::TT + SL::TH + 2 * (i * SL::TW + j), ll);
-        }
+        uint2 hh, ll;
+        split_quad(x, hh, ll);
+        lds_put(smem, sb + SL::TT + 16 * (16 * q + i), make_uint4(hh.x, hh.y, ll.x, ll.y));
       }
 
       // ---- hand the slot over
@@ -755,7 +758,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         accS[tt][e] = S0 ? S0[(((size_t)n * H + h) * DK + 16 * tt + 4 * gq + e) * DV + col] : 0.f;
-    const int lpD = 2 * (l16 * SL::RW + 8 * gq), lpT = 2 * (l16 * SL::TW + 4 * gq);
+    const int lpD = 2 * (l16 * SL::RW + 8 * gq);
     const int rs_v = H * DV * 2;
     // v of the next block, one block ahead
     unsigned short nv[4] = {0, 0, 0, 0};
@@ -815,17 +818,13 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
           accO = mfma32x3(accO, fq_h[s], fq_l[s], sh[kb], sl[kb]);
           __builtin_amdgcn_sched_barrier(0);
         }
-        // fragments of T, P and (K/gamma')^T for the rest of the block
-        const int ttb = sb + SL::TT + lpT, ptb = sb + SL::PT + lpT;
-        const bf16x4 th = frag16o(smem, ttb, 0), tl = frag16o(smem, ttb, SL::TH);
-        const bf16x4 ph = frag16o(smem, ptb, 0), pl = frag16o(smem, ptb, SL::TH);
-        bf16x4 kh[ST], kl[ST];
+        // fragment units of T, P and (K/gamma')^T for the rest of the block
+        const uint4 tw = lds_at<uint4>(smem, sb + SL::TT + 16 * lane, 0);
+        const uint4 pw = lds_at<uint4>(smem, sb + SL::PT + 16 * lane, 0);
+        uint4 kw[ST];
 #pragma unroll
-        for (int tt = 0; tt < ST; ++tt) {
-          const uint4 w = lds_at<uint4>(smem, sb + SL::KT + 16 * kt_unit(0, gq, l16), 16 * kt_unit(tt, 0, 0));
-          kh[tt] = __builtin_bit_cast(bf16x4, make_uint2(w.x, w.z));
-          kl[tt] = __builtin_bit_cast(bf16x4, make_uint2(w.y, w.w));
-        }
+        for (int tt = 0; tt < ST; ++tt)
+          kw[tt] = lds_at<uint4>(smem, sb + SL::KT + 16 * kt_unit(0, gq, l16), 16 * kt_unit(tt, 0, 0));
         const float4 bq = lds_at<float4>(smem, sb + SL::BT, 16 * gq);
         // ---- U = (I + A)^-1 Diag(beta) X
         f32x4 y;
@@ -833,15 +832,20 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
         y[1] = bq.y * (accX[1] + bf16_to_f32(cv[1]));
         y[2] = bq.z * (accX[2] + bf16_to_f32(cv[2]));
         y[3] = bq.w * (accX[3] + bf16_to_f32(cv[3]));
+        // each three-term product is two 16x16x32 MFMAs of the fragment unit
+        // [hi | lo]: against [b_hi | b_hi], then against [b_lo | 0]
+        const bf16x4 z4 = {};
         bf16x4 yh, yl;
         split4(y, yh, yl);
         f32x4 u = {0.f, 0.f, 0.f, 0.f};
-        u = mfma16x3(u, th, tl, yh, yl);
-        settle16();
+        u = mfma32(as_frag8(tw), cat8(yh, yh), u);
+        u = mfma32(as_frag8(tw), cat8(yl, z4), u);
         bf16x4 uh, ul;
         split4(u, uh, ul);
+        const bf16x8 uu = cat8(uh, uh), ul0 = cat8(ul, z4);
         // ---- O += P U;  S <- S_pre + (K/gamma')^T U  (exact: Diag(gamma_n) S + ...)
-        accO = mfma16x3(accO, ph, pl, uh, ul);
+        accO = mfma32(as_frag8(pw), uu, accO);
+        accO = mfma32(as_frag8(pw), ul0, accO);
         if (exact) {
 #pragma unroll
           for (int tt = 0; tt < ST; ++tt) {
@@ -850,9 +854,11 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
           }
         }
 #pragma unroll
-        for (int tt = 0; tt < ST; ++tt) accS[tt] = mfma16x3(accS[tt], kh[tt], kl[tt], uh, ul);
+        for (int tt = 0; tt < ST; ++tt) {
+          accS[tt] = mfma32(as_frag8(kw[tt]), uu, accS[tt]);
+          accS[tt] = mfma32(as_frag8(kw[tt]), ul0, accS[tt]);
+        }
         count_done(s_done + I, lane == 0);
-        settle16();
         // ---- store o (rows past the sequence end are dropped by the resource)
         if (OBF16) {
           const int rs = H * DV * 2;
