@@ -81,12 +81,6 @@ constexpr int kSpinLimit = 1 << 18;        // polls of a hand-over counter befor
 __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-// acc += a*b with a = ah + al, b = bh + bl (al*bl dropped).
-__device__ __forceinline__ f32x4 mfma32x3(f32x4 c, bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl) {
-  c = mfma32(al, bh, c);
-  c = mfma32(ah, bl, c);
-  return mfma32(ah, bh, c);
-}
 // hi/lo split of two fp32 values into packed bf16 pairs (round to nearest
 // even on both parts), with one packed conversion for each part.
 __device__ __forceinline__ void split2(float a, float b, uint32_t &h, uint32_t &l) {
@@ -350,7 +344,9 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
     len = T;
   }
   const int nch = (len + C - 1) / C;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the wave index is uniform: in a scalar register, buffer resources built
+  // from it need no per-lane loop
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
 
   if (threadIdx.x < 2 * NB) s_ready[threadIdx.x] = 0;   // ready[], then done[]
   __syncthreads();
@@ -672,6 +668,10 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
         kt_store(r2, kwh, kwl);
         __builtin_amdgcn_sched_barrier(0);   // two tokens at a time: bounded live range
       }
+      // The block's inputs are consumed (beta aside): the next round's block is
+      // loaded now, in flight during the tiles and the inverse.
+      const float cur_b = in_b;
+      if ((lc + 1) * C + CB * I < len) load(lc + 1);
 
       if (!exact) {
         // ---- A and P for the block, computed transposed: the MFMA's row operand
@@ -689,12 +689,16 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
           const bf16x8 rk_l = frag32p(smem, rb + SL::GK + SL::PL, 64 * kb);
           const bf16x8 rq_h = frag32p(smem, rb + SL::GQ, 64 * kb);
           const bf16x8 rq_l = frag32p(smem, rb + SL::GQ + SL::PL, 64 * kb);
-          pA = mfma32x3(pA, ka_h, ka_l, rk_h, rk_l);
-          pP = mfma32x3(pP, ka_h, ka_l, rq_h, rq_l);
+          pA = mfma32(ka_l, rk_h, pA);     // A and P alternate (independent chains)
+          pP = mfma32(ka_l, rq_h, pP);
+          pA = mfma32(ka_h, rk_l, pA);
+          pP = mfma32(ka_h, rq_l, pP);
+          pA = mfma32(ka_h, rk_h, pA);
+          pP = mfma32(ka_h, rq_h, pP);
         }
         // pA holds -A_lj / beta_l: row l of A, zero on and above the diagonal, to
         // the fp32 store; row l of P to its fragment unit (l, gg)
-        const float bl = __shfl(in_b, l);
+        const float bl = __shfl(cur_b, l);
         float av[4], pv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -713,7 +717,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
         lds_put(smem, sb + SL::PRE + 4 * ca, make_float4(gn[0], gn[1], gn[2], gn[3]));
         lds_put(smem, sb + SL::PRE + 4 * ca + 64, make_float4(gn[4], gn[5], gn[6], gn[7]));
       }
-      if (lane < CB) lds_put(smem, sb + SL::BT + 4 * lane, in_b);
+      if (lane < CB) lds_put(smem, sb + SL::BT + 4 * lane, cur_b);
       if (lane == 0) lds_put(smem, sb + SL::MODE, exact ? 1 : 0);
       // ---- T = (I + A)^-1, row i per quad of lanes: lane 4i + q holds T[i][4q ..
       // 4q+3].  T (I + A) = I gives T[i][j] = delta_ij - sum_{k > j} T[i][k] A[k][j];
@@ -745,8 +749,6 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
 
       // ---- hand the slot over
       publish(s_ready + I, lc + 1, lane == 0);
-
-      if ((lc + 1) * C + CB * I < len) load(lc + 1);   // next round's block, in flight meanwhile
     }
   } else {
     // ======================= state pass (waves 0-3)
@@ -758,29 +760,38 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         accS[tt][e] = S0 ? S0[(((size_t)n * H + h) * DK + 16 * tt + 4 * gq + e) * DV + col] : 0.f;
+    // the initial state is in registers before the loop, so no wait inside the
+    // loop is charged with these loads (vmcnt(0); expcnt, lgkmcnt untouched)
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     const int lpD = 2 * (l16 * SL::RW + 8 * gq);
     const int rs_v = H * DV * 2;
-    // v of the next block, one block ahead
-    unsigned short nv[4] = {0, 0, 0, 0};
+    // v, two blocks ahead: block b of a round reads ring entry b, so every
+    // index is known at compile time and the wait for a load falls at its use
+    unsigned short nv[NB][4];
     auto load_v = [&](int lc, int I) {
       const int t0 = start + lc * C, nt = min(C, len - lc * C);
       const auto rv = rsrc(v + ((size_t)t0 * H + h) * DV, (nt - 1) * rs_v + DV * 2);
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        nv[e] = __builtin_amdgcn_raw_buffer_load_b16(rv, (CB * I + 4 * gq + e) * rs_v + 2 * col, 0, 0);
+        nv[I][e] = __builtin_amdgcn_raw_buffer_load_b16(rv, (CB * I + 4 * gq + e) * rs_v + 2 * col, 0, 0);
     };
-    if (nch > 0) load_v(0, 0);
+    static_assert(NB >= 3, "the v ring holds the current block and the next two");
+    if (nch > 0) {      // rows past the sequence end read as zero
+      load_v(0, 0);
+      load_v(0, 1);
+    }
 
     for (int lc = 0; lc < nch; ++lc) {
       const int t0 = start + lc * C, nt = min(C, len - lc * C);
 #pragma unroll
       for (int I = 0; I < NB; ++I) {
         if (CB * I >= nt) break;
-        unsigned short cv[4] = {nv[0], nv[1], nv[2], nv[3]};
-        if (I + 1 < NB && CB * (I + 1) < nt)
-          load_v(lc, I + 1);
-        else if (I + 1 == NB && lc + 1 < nch)
-          load_v(lc + 1, 0);
+        if (I + 2 < NB) {
+          if (CB * (I + 2) < nt) load_v(lc, I + 2);
+        } else if (lc + 1 < nch) {
+          load_v(lc + 1, I + 2 - NB);
+        }
+        const unsigned short(&cv)[4] = nv[I];
 
         wait_for(s_ready + I, lc + 1);
         const int sb = I * SLOT;
@@ -814,8 +825,14 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
           if (kb + 1 < KB) ld(kb + 1);
           __builtin_amdgcn_sched_barrier(0);
           const int s = kb & 1;
-          accX = mfma32x3(accX, fk_h[s], fk_l[s], sh[kb], sl[kb]);
-          accO = mfma32x3(accO, fq_h[s], fq_l[s], sh[kb], sl[kb]);
+          // X and O alternate, so each product waits on its chain two
+          // instructions back rather than one
+          accX = mfma32(fk_l[s], sh[kb], accX);
+          accO = mfma32(fq_l[s], sh[kb], accO);
+          accX = mfma32(fk_h[s], sl[kb], accX);
+          accO = mfma32(fq_h[s], sl[kb], accO);
+          accX = mfma32(fk_h[s], sh[kb], accX);
+          accO = mfma32(fq_h[s], sh[kb], accO);
           __builtin_amdgcn_sched_barrier(0);
         }
         // fragment units of T, P and (K/gamma')^T for the rest of the block
@@ -837,15 +854,15 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
         const bf16x4 z4 = {};
         bf16x4 yh, yl;
         split4(y, yh, yl);
-        f32x4 u = {0.f, 0.f, 0.f, 0.f};
+        f32x4 u = {0.f, 0.f, 0.f, 0.f}, u2 = {0.f, 0.f, 0.f, 0.f};
         u = mfma32(as_frag8(tw), cat8(yh, yh), u);
-        u = mfma32(as_frag8(tw), cat8(yl, z4), u);
+        u2 = mfma32(as_frag8(tw), cat8(yl, z4), u2);
+        u += u2;
         bf16x4 uh, ul;
         split4(u, uh, ul);
         const bf16x8 uu = cat8(uh, uh), ul0 = cat8(ul, z4);
         // ---- O += P U;  S <- S_pre + (K/gamma')^T U  (exact: Diag(gamma_n) S + ...)
         accO = mfma32(as_frag8(pw), uu, accO);
-        accO = mfma32(as_frag8(pw), ul0, accO);
         if (exact) {
 #pragma unroll
           for (int tt = 0; tt < ST; ++tt) {
@@ -853,11 +870,12 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
             accS[tt][0] *= gn.x; accS[tt][1] *= gn.y; accS[tt][2] *= gn.z; accS[tt][3] *= gn.w;
           }
         }
+        // all hi terms, then all lo terms: no product waits on the one before
 #pragma unroll
-        for (int tt = 0; tt < ST; ++tt) {
-          accS[tt] = mfma32(as_frag8(kw[tt]), uu, accS[tt]);
-          accS[tt] = mfma32(as_frag8(kw[tt]), ul0, accS[tt]);
-        }
+        for (int tt = 0; tt < ST; ++tt) accS[tt] = mfma32(as_frag8(kw[tt]), uu, accS[tt]);
+        accO = mfma32(as_frag8(pw), ul0, accO);
+#pragma unroll
+        for (int tt = 0; tt < ST; ++tt) accS[tt] = mfma32(as_frag8(kw[tt]), ul0, accS[tt]);
         count_done(s_done + I, lane == 0);
         // ---- store o (rows past the sequence end are dropped by the resource)
         if (OBF16) {
