@@ -795,8 +795,16 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
 
         wait_for(s_ready + I, lc + 1);
         const int sb = I * SLOT;
-        const int exact = __builtin_amdgcn_readfirstlane(lds_at<int>(smem, sb, SL::MODE));
-        // operand fragments of the first two k blocks, in flight during the split
+        // Reads in the order they are needed, all issued before the first wait:
+        // the mode, gamma_n, the first k block's operand fragments, then T, P
+        // and beta (needed after the X and O products).
+        const int mode = lds_at<int>(smem, sb, SL::MODE);
+        __builtin_amdgcn_sched_barrier(0);
+        float4 gnv[ST];
+#pragma unroll
+        for (int tt = 0; tt < ST; ++tt)
+          gnv[tt] = lds_at<float4>(smem, sb + SL::PRE, 4 * (16 * tt + 4 * gq));
+        __builtin_amdgcn_sched_barrier(0);
         const int gkb = sb + SL::GK + lpD, gqb = sb + SL::GQ + lpD;
         bf16x8 fk_h[2], fk_l[2], fq_h[2], fq_l[2];
         auto ld = [&](int kb) {
@@ -807,11 +815,16 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
           fq_l[s] = frag32p(smem, gqb, SL::PL + 64 * kb);
         };
         ld(0);
+        const uint4 tw = lds_at<uint4>(smem, sb + SL::TT + 16 * lane, 0);
+        const uint4 pw = lds_at<uint4>(smem, sb + SL::PT + 16 * lane, 0);
+        const float4 bq = lds_at<float4>(smem, sb + SL::BT, 16 * gq);
+        __builtin_amdgcn_sched_barrier(0);
+        const int exact = __builtin_amdgcn_readfirstlane(mode);
         // ---- S_pre = Diag(gamma_n) S (factored blocks), split for the products
         if (!exact) {
 #pragma unroll
           for (int tt = 0; tt < ST; ++tt) {
-            const float4 gn = lds_at<float4>(smem, sb + SL::PRE, 4 * (16 * tt + 4 * gq));
+            const float4 gn = gnv[tt];
             accS[tt][0] *= gn.x; accS[tt][1] *= gn.y; accS[tt][2] *= gn.z; accS[tt][3] *= gn.w;
           }
         }
@@ -820,9 +833,16 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
         for (int kb = 0; kb < KB; ++kb) split8_acc(accS[2 * kb], accS[2 * kb + 1], sh[kb], sl[kb]);
         // ---- X = V - (gamma' K) S_pre;  O = (gamma' Q) S_pre
         f32x4 accX = {0.f, 0.f, 0.f, 0.f}, accO = {0.f, 0.f, 0.f, 0.f};
+        uint4 kw[ST];     // (K/gamma')^T fragment units, read once the operand reads are out
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-          if (kb + 1 < KB) ld(kb + 1);
+          if (kb + 1 < KB) {
+            ld(kb + 1);
+          } else {
+#pragma unroll
+            for (int tt = 0; tt < ST; ++tt)
+              kw[tt] = lds_at<uint4>(smem, sb + SL::KT + 16 * kt_unit(0, gq, l16), 16 * kt_unit(tt, 0, 0));
+          }
           __builtin_amdgcn_sched_barrier(0);
           const int s = kb & 1;
           // X and O alternate, so each product waits on its chain two
@@ -835,14 +855,6 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
           accO = mfma32(fq_h[s], sh[kb], accO);
           __builtin_amdgcn_sched_barrier(0);
         }
-        // fragment units of T, P and (K/gamma')^T for the rest of the block
-        const uint4 tw = lds_at<uint4>(smem, sb + SL::TT + 16 * lane, 0);
-        const uint4 pw = lds_at<uint4>(smem, sb + SL::PT + 16 * lane, 0);
-        uint4 kw[ST];
-#pragma unroll
-        for (int tt = 0; tt < ST; ++tt)
-          kw[tt] = lds_at<uint4>(smem, sb + SL::KT + 16 * kt_unit(0, gq, l16), 16 * kt_unit(tt, 0, 0));
-        const float4 bq = lds_at<float4>(smem, sb + SL::BT, 16 * gq);
         // ---- U = (I + A)^-1 Diag(beta) X
         f32x4 y;
         y[0] = bq.x * (accX[0] + bf16_to_f32(cv[0]));
