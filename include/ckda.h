@@ -95,9 +95,12 @@ size_t ckda_forward_workspace_bytes(int B, int T, int H, int dk, int dv, int N,
 /*
  * Chunkwise-parallel CKDA forward over a batch of sequences.
  *
- * The token recurrence above, computed in chunks of 64 tokens with the
- * WY/UT form of the delta rule and the signed-gate split the CKDA summary's
- * methodology describes (sign kept apart from the log-space gate magnitude).
+ * The token recurrence above, computed chunkwise with the WY/UT form of the
+ * delta rule: fp32 inputs in chunks of 64 tokens, bf16 inputs with the state
+ * stepped every 16 tokens.  Gate signs follow the CKDA summary's methodology
+ * (the sign kept apart from the log-space magnitude) wherever the gates'
+ * range within a chunk or block needs log space; otherwise the signed gates
+ * enter as products.
  *
  *  q, k        [B, T, H, dk]  in_dtype
  *  v           [B, T, H, dv]  in_dtype
