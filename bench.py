@@ -345,7 +345,8 @@ def main():
             "steps": args.bwd_steps, "arithmetic": "f64",
             "kda_ms_per_step": ms_bk,
             "fwd_bwd_ckda_over_kda_throughput": (
-                (out["kda"]["ms_per_step"] + ms_bk) / (out["ms_per_step"] + ms_b)
+                (out["kda"]["ms_per_step"] + ms_bk)
+                / (out["kda"]["ckda_ms_per_step_alternating"] + ms_b)
                 if "kda" in out else None),
             "f64_tflops": bflops / (ms_b * 1e-3) / 1e12, "f64_peak_tflops": F64_PEAK_TFLOPS,
             "f64_frac": bflops / (ms_b * 1e-3) / 1e12 / F64_PEAK_TFLOPS,
