@@ -319,30 +319,33 @@ def main():
         print(f"[bench] backward: timing {args.bwd_steps} steps", file=sys.stderr, flush=True)
         stream = torch.cuda.current_stream()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(args.bwd_steps):
-            run_b()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms_b = e0.elapsed_time(e1) / args.bwd_steps
         # KDA mode of the backward on |alpha|: with the KDA forward, the pages'
-        # forward-plus-backward throughput comparison.
+        # forward-plus-backward throughput comparison.  CKDA and KDA are timed in
+        # the block order CKDA, KDA, KDA, CKDA, so a steady clock drift cancels.
         ga = g.abs()
         run_bk = lambda: ck.backward(q, k, v, ga, beta, do, dS_T=dST, workspace=ws, kda=True)
         run_bk()
         torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(args.bwd_steps):
-            run_bk()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms_bk = e0.elapsed_time(e1) / args.bwd_steps
+        per_blk = max(1, args.bwd_steps // 2)
+        t_b = t_bk = 0.0
+        for fn, is_ckda in ((run_b, True), (run_bk, False), (run_bk, False), (run_b, True)):
+            e0.record(stream)
+            for _ in range(per_blk):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if is_ckda:
+                t_b += e0.elapsed_time(e1)
+            else:
+                t_bk += e0.elapsed_time(e1)
+        ms_b = t_b / (2 * per_blk)
+        ms_bk = t_bk / (2 * per_blk)
         bbytes, bflops, bper_th = bwd_algorithmic(w)
         out["backward"] = {
             "ms_per_step": ms_b, "tokens_per_s": w.B * w.T / (ms_b * 1e-3),
             "fwd_plus_bwd_tokens_per_s": (w.B * w.T / ((ms_b + out["ms_per_step"]) * 1e-3)
                                           if "ms_per_step" in out else None),
-            "steps": args.bwd_steps, "arithmetic": "f64",
+            "steps": 2 * per_blk, "arithmetic": "f64",
             "kda_ms_per_step": ms_bk,
             "fwd_bwd_ckda_over_kda_throughput": (
                 (out["kda"]["ms_per_step"] + ms_bk)
