@@ -143,6 +143,39 @@ def test_forward_bf16_strong_decay_chunks(dk, dv):
     _check_full(x, f"strong decay {dk}x{dv}")
 
 
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128)])
+def test_forward_bf16_guard_boundary(dk, dv):
+    """Blocks on both sides of the bf16 path's factored-form range (every
+    product of the gates after a token within 2^+-110 in its 16-token block):
+    whole 16-token blocks where some channels decay by 2^-6.25 per token
+    (15 later gates: 2^-93.75, factored), next to blocks where they decay by
+    2^-7.5 per token (2^-112.5, element-wise), with random signs, packed
+    sequences and a ragged tail."""
+    lens = [160, 93, 64]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    x = _rand_forward(57, B=1, T=int(cu[-1]), H=2, dk=dk, dv=dv, dtype="bf16", cu=cu)
+    g = x["g"]
+    rng = np.random.default_rng(8)
+    for blk, t0 in enumerate(range(0, int(cu[-1]) - 16, 16)):
+        mag = 2.0 ** (-6.25 if blk % 2 == 0 else -7.5)
+        chans = rng.choice(dk, size=dk // 8, replace=False)
+        sgn = np.where(rng.random((16, 2, chans.size)) < 0.5, -1.0, 1.0)
+        g[0, t0:t0 + 16][:, :, chans] = (sgn * mag).astype(np.float32)
+    # the inputs hold blocks on both sides of the range (blocks restart at each
+    # sequence start): log2 of the product of the gates after each token
+    inside = outside = 0
+    for n in range(len(lens)):
+        for b0 in range(int(cu[n]), int(cu[n + 1]), 16):
+            lg = np.log2(np.maximum(np.abs(g[0, b0:min(b0 + 16, int(cu[n + 1]))]), 2.0 ** -126))
+            after = lg[::-1].cumsum(axis=0)[::-1] - lg        # per token, head, channel
+            if np.abs(after).max() <= 110:
+                inside += 1
+            else:
+                outside += 1
+    assert inside > 0 and outside > 0, (inside, outside)
+    _check_full(x, f"guard boundary {dk}x{dv}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("bmax,amax", [(2.5, 1.1), (3.0, 1.05)])
 def test_forward_expansive_regime(dtype, bmax, amax):
