@@ -213,8 +213,10 @@ def main():
         for _ in range(max(3, args.warmup // 4)):
             run_kda()
         torch.cuda.synchronize()
+        # at least 16 launches per block: the launches queued right after each
+        # block's synchronisation would otherwise weigh on the average
         n_blk = 6
-        per_blk = max(1, args.steps // n_blk)
+        per_blk = max(16, args.steps // n_blk)
         t_ckda = t_kda = 0.0
         for blk in range(n_blk):
             order = ((run, True), (run_kda, False)) if blk % 2 == 0 else ((run_kda, False), (run, True))
