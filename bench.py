@@ -398,7 +398,8 @@ def main():
     # ------------------------------------------------------------- other configs (time only)
     if not args.skip_forward and not args.skip_others:
         others = {}
-        for name in ("tiny_f32", "rotation_f32", "varlen_64k_bf16", "layer_1p3b_fastdecay_bf16"):
+        for name in ("tiny_f32", "rotation_f32", "varlen_64k_bf16", "layer_1p3b_fastdecay_bf16",
+                     "layer_1p3b_rapiddecay_bf16"):
             wo = wl.WORKLOADS[name]
             xo = wl.forward_inputs(wo)
             dt = torch.bfloat16 if wo.dtype == "bf16" else torch.float32
@@ -420,7 +421,7 @@ def main():
             ms_o = e0.elapsed_time(e1) / n_o
             toks = int(xo["q"].shape[0] * xo["q"].shape[1])
             others[name] = {"ms_per_forward": ms_o, "tokens_per_s": toks / (ms_o * 1e-3)}
-            if name == "layer_1p3b_fastdecay_bf16" and "ms_per_step" in out:
+            if name.startswith("layer_1p3b_") and "ms_per_step" in out:
                 # strongly forgetting channels against the headline layer
                 others[name]["time_over_layer"] = ms_o / out["ms_per_step"]
             del qo, ko, vo, go, bo, so, cu

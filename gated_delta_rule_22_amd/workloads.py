@@ -57,6 +57,13 @@ WORKLOADS = {
     "layer_1p3b_fastdecay_bf16": Workload("layer_1p3b_fastdecay_bf16", B=8, T=4096, H=16,
                                           dk=128, dv=128, dtype="bf16", gate="tanh_fastdecay",
                                           q_scale=False, s0="zero"),
+    # Every eighth key channel forgetting faster still (|alpha| in [0.001,
+    # 0.01]): over the 15 later gates of a 16-token block those channels fall
+    # by 2^-100 to 2^-150, so most blocks leave the range of the factored
+    # block form and take the exact (log-space) block path.
+    "layer_1p3b_rapiddecay_bf16": Workload("layer_1p3b_rapiddecay_bf16", B=8, T=4096, H=16,
+                                           dk=128, dv=128, dtype="bf16", gate="tanh_rapiddecay",
+                                           q_scale=False, s0="zero"),
     # 65536 packed tokens in 12 sequences of log-uniform length.
     "varlen_64k_bf16": Workload("varlen_64k_bf16", B=1, T=65536, H=16, dk=128, dv=128,
                                 dtype="bf16", gate="rotation", q_scale=False, s0="zero",
@@ -97,13 +104,17 @@ def _gates(rng, shape, kind):
     if kind == "rotation":
         neg = rng.random(shape) < 0.5            # gate sign only, |alpha| = 1
         return np.where(neg, -1.0, 1.0)
-    if kind in ("tanh", "tanh_fastdecay"):
+    if kind in ("tanh", "tanh_fastdecay", "tanh_rapiddecay"):
         a = np.tanh(rng.normal(0.0, 1.5, shape))  # std 1.5
         sgn = np.where(a < 0, -1.0, 1.0)          # sign(0) := +
         mag = np.maximum(np.abs(a), 1e-3)
         if kind == "tanh_fastdecay":
             # every eighth channel forgets fast: |alpha| uniform in [0.01, 0.1]
             fast = rng.uniform(0.01, 0.1, shape)
+            mag = np.where(np.arange(shape[-1]) % 8 == 7, fast, mag)
+        if kind == "tanh_rapiddecay":
+            # every eighth channel: |alpha| uniform in [0.001, 0.01]
+            fast = rng.uniform(0.001, 0.01, shape)
             mag = np.where(np.arange(shape[-1]) % 8 == 7, fast, mag)
         return sgn * mag
     raise ValueError(kind)

@@ -227,6 +227,13 @@ def test_forward_layer_fastdecay_full():
     _check_full(wl.forward_inputs("layer_1p3b_fastdecay_bf16"), "layer_1p3b_fastdecay_bf16")
 
 
+def test_forward_layer_rapiddecay_full():
+    """The layer workload with every eighth key channel at |alpha| in [0.001,
+    0.01] (most 16-token blocks leave the factored range and take the exact
+    block path): every element of o and S_T against the oracle."""
+    _check_full(wl.forward_inputs("layer_1p3b_rapiddecay_bf16"), "layer_1p3b_rapiddecay_bf16")
+
+
 def test_forward_varlen_64k_full():
     """12 packed sequences, 65,536 tokens, H=16: every element of o and of the
     per-sequence final states against the oracle."""
