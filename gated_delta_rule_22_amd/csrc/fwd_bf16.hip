@@ -28,9 +28,14 @@
 // A block whose spread is wider takes an exact path that works in log space,
 // as the CKDA summary ("Methodology in Plain English") keeps gate magnitudes:
 // per channel the cumulative sum G of log2|alpha| (each term floored at -126)
-// and the cumulative parity of negative gates; A and P element by element
-// from fp32 ratios 2^(G_i - G_j), the row operands referenced to the block
-// start (X = V - (gamma K) S), S' = Diag(gamma_n) S + (K gamma_n / gamma)^T U.
+// and the cumulative parity of negative gates.  A and P come from two
+// matrix-core passes with half-block references (each ratio split about the
+// last token of its column's half, so inside a half it is the factored form of
+// an eight-token block, and across the halves both factors are products of
+// gates); a half whose own spread exceeds 2^110 sends the block to A and P
+// element by element from fp32 ratios 2^(G_i - G_j).  Either way the state
+// pass's operands are referenced to the block start (X = V - (gamma K) S),
+// S' = Diag(gamma_n) S + (K gamma_n / gamma)^T U.
 //
 // Work split inside the workgroup (512 threads), a pipeline with no barrier
 // inside the sequence loop:
@@ -76,8 +81,13 @@ constexpr int ADS = 20;          // row stride of the fp32 A tile (16-byte rows)
 constexpr float kLog2Floor = -126.f;
 constexpr float kGuardScale = 0x1p110f;   // bound on gamma_n / gamma_t and its inverse
 constexpr float kGateFloor = 0x1p-126f;    // floor of a gate's magnitude
+constexpr float kHalfRange = 110.f;        // exact blocks: bound on |log2| of a half-block factor
 constexpr int kBufferFlags = 0x00020000;   // buffer resource word 3: raw 32-bit data
 constexpr int kSpinLimit = 1 << 18;        // polls of a hand-over counter before giving up
+template <bool B>
+struct Kind {                    // compile-time block kind (true: exact)
+  static constexpr bool value = B;
+};
 __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -191,6 +201,8 @@ struct Slot {
   static constexpr int XP = KG + CB * DK * 4;
   static_assert(CB * DK * 4 + 64 * 4 <= 2 * PL, "exact-path tables fit the K/gamma' region");
   static_assert(SIZE % 16 == 0 && XG % 16 == 0 && GQ % 16 == 0, "16-byte alignment");
+  // exact blocks: a [CB][DK] column plane in the (K / gamma')^T and T regions
+  static_assert(KT + 2 * PL <= PT && KT % 16 == 0, "column plane below the P tile");
 };
 
 template <int DK>
@@ -518,97 +530,92 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
         }
       };
 
-      // exact path: G at the block end, parities (block start to the lane's
-      // first token, and of the whole block), lane-local parities
-      float Gend[8];
-      uint32_t exP = 0u, endP = 0u, pbits = 0u;
-      auto g_at = [&](int r, int hf) {    // exact path: G of the lane's token r, channels 4 hf ..
-        return lds_at<float4>(smem, sb + SL::XG + 4 * ((tg * TPL + r) * DK + ca), 64 * hf);
-      };
-      if (exact) {
-        // Exact path.  G (cumulative log2|alpha|, each term floored at -126) and
-        // the parities of negative gates go to LDS rather than registers: the
-        // lane-local running sums first, then the earlier token groups' prefix is
-        // added in place.
-        float tot[8];
-        uint32_t ptot = 0u;
+      // ---- A and P tiles from the KG, GK and GQ planes in the slot, computed
+      // transposed: the MFMA's row operand is the column plane (K/gamma' in the
+      // factored form), its column operand -(gamma' K) or gamma' Q, so lane (g, l)
+      // holds row l and columns 4g .. 4g+3.  The wave reads only what it wrote,
+      // and LDS serves one wave's accesses in order.
+      auto ap_tiles = [&](f32x4 &pA, f32x4 &pP, int col_plane) {
+        const int l = lane & 15, gg = lane >> 4;
+        const int rb = sb + 2 * (l * SL::RW + 8 * gg);
+        pA = f32x4{0.f, 0.f, 0.f, 0.f};
+        pP = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int cc = 0; cc < 8; ++cc) tot[cc] = 0.f;
+        for (int kb = 0; kb < KB; ++kb) {
+          const bf16x8 ka_h = frag32p(smem, rb + col_plane, 64 * kb);
+          const bf16x8 ka_l = frag32p(smem, rb + col_plane + SL::PL, 64 * kb);
+          const bf16x8 rk_h = frag32p(smem, rb + SL::GK, 64 * kb);
+          const bf16x8 rk_l = frag32p(smem, rb + SL::GK + SL::PL, 64 * kb);
+          const bf16x8 rq_h = frag32p(smem, rb + SL::GQ, 64 * kb);
+          const bf16x8 rq_l = frag32p(smem, rb + SL::GQ + SL::PL, 64 * kb);
+          pA = mfma32(ka_l, rk_h, pA);     // A and P alternate (independent chains)
+          pP = mfma32(ka_l, rq_h, pP);
+          pA = mfma32(ka_h, rk_l, pA);
+          pP = mfma32(ka_h, rq_l, pP);
+          pA = mfma32(ka_h, rk_h, pA);
+          pP = mfma32(ka_h, rq_h, pP);
+        }
+      };
+      // pA holds -A_lj / beta_l: row l of A, zero on and above the diagonal, to
+      // the fp32 store; row l of P to its fragment unit (l, g).  `bcur` holds
+      // beta of token `lane`.
+      auto ap_store = [&](const f32x4 &pA, const f32x4 &pP, float bcur) {
+        const int l = lane & 15, gg = lane >> 4;
+        const float bl = __shfl(bcur, l);
+        float av[4], pv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = 4 * gg + e;
+          av[e] = j < l ? -pA[e] * bl : 0.f;
+          pv[e] = j <= l ? pP[e] : 0.f;
+        }
+        lds_put(smem, sb + SL::AD + 4 * (l * ADS + 4 * gg), make_float4(av[0], av[1], av[2], av[3]));
+        uint2 hh, ll;
+        split_quad(pv, hh, ll);
+        lds_put(smem, sb + SL::PT + 16 * lane, make_uint4(hh.x, hh.y, ll.x, ll.y));
+      };
+      // the lane's eight channels of token t, split hi/lo, as one 16-byte run of
+      // a permuted [CB][DK] row plane
+      auto put_row = [&](int region, int t, const float (&x)[8]) {
+        const int ro = 2 * (t * SL::RW + 8 * cg);
+        uint2 h0, l0, h1, l1;
+        split_quad(*reinterpret_cast<const float(*)[4]>(x), h0, l0);
+        split_quad(*reinterpret_cast<const float(*)[4]>(x + 4), h1, l1);
+        lds_put(smem, sb + region + ro, make_uint4(h0.x, h0.y, h1.x, h1.y));
+        lds_put(smem, sb + region + SL::PL + ro, make_uint4(l0.x, l0.y, l1.x, l1.y));
+      };
+
+      // The keys and queries as values the compiler must reload: a pass that
+      // recomputes its operands from them does not keep another pass's alive.
+      auto opaque_inputs = [&]() {
 #pragma unroll
         for (int r = 0; r < TPL; ++r) {
-          const float a8[8] = {in_a[r][0].x, in_a[r][0].y, in_a[r][0].z, in_a[r][0].w,
-                               in_a[r][1].x, in_a[r][1].y, in_a[r][1].z, in_a[r][1].w};
-#pragma unroll
-          for (int cc = 0; cc < 8; ++cc) {
-            tot[cc] += fmaxf(flog2(fabsf(a8[cc])), kLog2Floor);
-            if (SIGNED) ptot ^= (__builtin_bit_cast(uint32_t, a8[cc]) >> 31) << cc;
-          }
-          const int go = SL::XG + 4 * ((tg * TPL + r) * DK + ca);
-          lds_put(smem, sb + go, make_float4(tot[0], tot[1], tot[2], tot[3]));
-          lds_put(smem, sb + go + 64, make_float4(tot[4], tot[5], tot[6], tot[7]));
-          pbits |= ptot << (8 * r);
+          asm volatile("" : "+v"(in_k[r].x), "+v"(in_k[r].y), "+v"(in_k[r].z), "+v"(in_k[r].w));
+          asm volatile("" : "+v"(in_q[r].x), "+v"(in_q[r].y), "+v"(in_q[r].z), "+v"(in_q[r].w));
         }
-#pragma unroll
-        for (int d = 1; d < TG; d <<= 1) {
-#pragma unroll
-          for (int cc = 0; cc < 8; ++cc) {
-            const float y = __shfl_up(tot[cc], d * CG);
-            if (tg >= d) tot[cc] += y;
-          }
-          if (SIGNED) {
-            const uint32_t y = __shfl_up(ptot, d * CG);
-            if (tg >= d) ptot ^= y;
-          }
-        }
-        float ex[8];
-#pragma unroll
-        for (int cc = 0; cc < 8; ++cc) {
-          const float y = __shfl_up(tot[cc], CG);
-          ex[cc] = tg ? y : 0.f;
-          Gend[cc] = __shfl(tot[cc], (TG - 1) * CG + cg);
-        }
-        if (SIGNED) {
-          const uint32_t y = __shfl_up(ptot, CG);
-          exP = tg ? y : 0u;
-          endP = __shfl(ptot, (TG - 1) * CG + cg);
-        }
-#pragma unroll
-        for (int r = 0; r < TPL; ++r)
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf) {
-            float4 gg = g_at(r, hf);
-            gg.x += ex[4 * hf]; gg.y += ex[4 * hf + 1]; gg.z += ex[4 * hf + 2]; gg.w += ex[4 * hf + 3];
-            lds_put(smem, sb + SL::XG + 4 * ((tg * TPL + r) * DK + ca) + 64 * hf, gg);
-          }
-        {
-          uint32_t pw = 0u;
-#pragma unroll
-          for (int r = 0; r < TPL; ++r) pw |= ((exP ^ (pbits >> (8 * r))) & 0xFFu) << (8 * r);
-          lds_put(smem, sb + SL::XP + 4 * lane, pw);
-        }
-        if (NORM) {    // per-token factors into the T tile (written only later)
-#pragma unroll
-          for (int r = 0; r < TPL; ++r) {
-            float fk, fq;
-            norm_factors(r, fk, fq);
-            if (cg == 0) lds_put(smem, sb + SL::TT + 8 * (tg * TPL + r), make_float2(fk, fq));
-          }
-        }
-        const size_t row0 = (size_t)(start + tb) * H + h;
-        const int rsk = H * DK * 2;
-        exact_tiles<DK, SIGNED, NORM>(smem, sb, lane, __shfl(in_b, lane >> 2),
-                                      rsrc(k + row0 * DK, (nbt - 1) * rsk + DK * 2),
-                                      rsrc(q + row0 * DK, (nbt - 1) * rsk + DK * 2), rsk);
+      };
 
-      }
+      // ---- exact blocks.  G (the cumulative sum of log2|alpha| from the block
+      // start, each term floored at -126) and the cumulative parity of negative
+      // gates, per (token, channel), in registers.
+      float Gend[8];
+      uint32_t parw[TPL], endP = 0u;
+#pragma unroll
+      for (int r = 0; r < TPL; ++r) parw[r] = 0u;
+      auto g_at = [&](int r, int hf) {    // G of the lane's token r, channels 4 hf .. 4 hf + 3
+        return lds_at<float4>(smem, sb + SL::XG + 4 * ((tg * TPL + r) * DK + ca), 64 * hf);
+      };
 
       // ---- operands: rows gamma' K and gamma' Q, columns K / gamma'.  Factored:
       // gamma' = gamma_t / gamma_n = 1 / (product of the gates after t), a running
       // product going backwards from the block end.  Exact: rows gamma_t (from the
-      // block start) and columns gamma_n / gamma_t, from G.
+      // block start) and columns gamma_n / gamma_t, from G.  One copy of the loop
+      // per block kind, so neither carries the other's values.
+      auto operand_planes = [&](auto kind) {
+      constexpr bool EX = decltype(kind)::value;
       float run[8];
 #pragma unroll
-      for (int cc = 0; cc < 8; ++cc) run[cc] = exS[cc];
+      for (int cc = 0; cc < 8; ++cc) run[cc] = EX ? 1.f : exS[cc];
 #pragma unroll
       for (int r2 = TPL - 2; r2 >= 0; r2 -= 2) {
         uint32_t kwh[2][4], kwl[2][4];
@@ -618,7 +625,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
           float fk, fq;
           norm_factors(r, fk, fq);
           float gam8[8], kf8[8];
-          if (!exact) {
+          if constexpr (!EX) {
 #pragma unroll
             for (int cc = 0; cc < 8; ++cc) {
               const float sa = run[cc];                      // gamma_n / gamma_t
@@ -627,8 +634,8 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
               run[cc] = sa * gate(r, cc);
             }
           } else {
-            const uint32_t pr = (exP ^ (pbits >> (8 * r))) & 0xFFu;   // parity from the block start
-            const uint32_t pc = pr ^ (endP & 0xFFu);
+            const uint32_t pr = parw[r];                 // parity from the block start
+            const uint32_t pc = pr ^ endP;
             const float4 g0 = g_at(r, 0), g1 = g_at(r, 1);
             const float G8[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
 #pragma unroll
@@ -658,7 +665,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
           lds_put(smem, sb + SL::GQ + SL::PL + ro, make_uint4(l0.x, l0.y, l1.x, l1.y));
           split_quad(*reinterpret_cast<const float(*)[4]>(kg), h0, l0);
           split_quad(*reinterpret_cast<const float(*)[4]>(kg + 4), h1, l1);
-          if (!exact) {   // the exact path keeps its G table in this region
+          if constexpr (!EX) {   // the exact path keeps its G table in this region
             lds_put(smem, sb + SL::KG + ro, make_uint4(h0.x, h0.y, h1.x, h1.y));
             lds_put(smem, sb + SL::KG + SL::PL + ro, make_uint4(l0.x, l0.y, l1.x, l1.y));
           }
@@ -668,48 +675,179 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
         kt_store(r2, kwh, kwl);
         __builtin_amdgcn_sched_barrier(0);   // two tokens at a time: bounded live range
       }
+      };
+
+      if (exact) {
+        float Gr[TPL][8], tot[8];
+        uint32_t ptot = 0u, pbits = 0u;
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc) tot[cc] = 0.f;
+#pragma unroll
+        for (int r = 0; r < TPL; ++r) {
+          const float a8[8] = {in_a[r][0].x, in_a[r][0].y, in_a[r][0].z, in_a[r][0].w,
+                               in_a[r][1].x, in_a[r][1].y, in_a[r][1].z, in_a[r][1].w};
+#pragma unroll
+          for (int cc = 0; cc < 8; ++cc) {
+            tot[cc] += fmaxf(flog2(fabsf(a8[cc])), kLog2Floor);
+            if (SIGNED) ptot ^= (__builtin_bit_cast(uint32_t, a8[cc]) >> 31) << cc;
+            Gr[r][cc] = tot[cc];
+          }
+          pbits |= ptot << (8 * r);
+        }
+        // the earlier token groups' sums (and parities) are added to the lane's
+#pragma unroll
+        for (int d = 1; d < TG; d <<= 1) {
+#pragma unroll
+          for (int cc = 0; cc < 8; ++cc) {
+            const float y = __shfl_up(tot[cc], d * CG);
+            if (tg >= d) tot[cc] += y;
+          }
+          if (SIGNED) {
+            const uint32_t y = __shfl_up(ptot, d * CG);
+            if (tg >= d) ptot ^= y;
+          }
+        }
+        uint32_t exP = 0u;
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc) {
+          const float y = __shfl_up(tot[cc], CG);
+          const float ex = tg ? y : 0.f;
+#pragma unroll
+          for (int r = 0; r < TPL; ++r) Gr[r][cc] += ex;
+          Gend[cc] = __shfl(tot[cc], (TG - 1) * CG + cg);
+        }
+        if (SIGNED) {
+          const uint32_t y = __shfl_up(ptot, CG);
+          exP = tg ? y : 0u;
+          endP = __shfl(ptot, (TG - 1) * CG + cg) & 0xFFu;
+        }
+#pragma unroll
+        for (int r = 0; r < TPL; ++r) parw[r] = (exP ^ (pbits >> (8 * r))) & 0xFFu;
+        // the G table (read back for the state pass's operands below)
+#pragma unroll
+        for (int r = 0; r < TPL; ++r)
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf)
+            lds_put(smem, sb + SL::XG + 4 * ((tg * TPL + r) * DK + ca) + 64 * hf,
+                    make_float4(Gr[r][4 * hf], Gr[r][4 * hf + 1], Gr[r][4 * hf + 2],
+                                Gr[r][4 * hf + 3]));
+
+        // Half-block references: every ratio gamma_i / gamma_j (j <= i) splits as
+        // (gamma_i / gamma_ref)(gamma_ref / gamma_j) about the last token of j's
+        // half (token 7 or 15).  Inside a half that is the factored form of an
+        // eight-token block; for i in the second half and j in the first, both
+        // factors are products of gates (no inverse), so a decaying gate can only
+        // make them small.  The tiles are two matrix-core passes: rows and columns
+        // referenced to their own half's end, then the second half's rows
+        // referenced to token 7 against the same columns.
+        constexpr int kLane7 = (CB / 2 - 1) / TPL * CG;   // holds token 7 as its last
+        float G7[8];
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc) G7[cc] = __shfl(Gr[TPL - 1][cc], kLane7 + cg);
+        const uint32_t P7 = SIGNED ? (uint32_t)__shfl((int)parw[TPL - 1], kLane7 + cg) : 0u;
+        const bool second = tg * TPL >= CB / 2;     // the lane's tokens are in the second half
+        bool wide = false;
+#pragma unroll
+        for (int r = 0; r < TPL; ++r)
+#pragma unroll
+          for (int cc = 0; cc < 8; ++cc) {
+            wide |= !(fabsf(Gr[r][cc] - (second ? Gend[cc] : G7[cc])) <= kHalfRange);
+            if (second) wide |= !(Gr[r][cc] - G7[cc] <= kHalfRange);
+          }
+        if (!__any(wide)) {
+          const uint32_t pref = second ? endP : P7;
+#pragma unroll
+          for (int r = 0; r < TPL; ++r) {
+            float fk, fq;
+            norm_factors(r, fk, fq);
+            float gk[8], gq[8], kg[8];
+            const float4 g0 = g_at(r, 0), g1 = g_at(r, 1);
+            const float G8[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+            for (int cc = 0; cc < 8; ++cc) {
+              const float x = G8[cc] - (second ? Gend[cc] : G7[cc]);
+              const uint32_t odd = SIGNED ? ((parw[r] ^ pref) >> cc) & 1u : 0u;
+              const float rho = with_sign(fexp2(x), odd), kap = with_sign(fexp2(-x), odd);
+              const float kk = bf16_of(in_k[r], cc) * fk, qq = bf16_of(in_q[r], cc) * fq;
+              gk[cc] = -kk * rho;
+              gq[cc] = qq * rho;
+              kg[cc] = kk * kap;
+            }
+            const int t = tg * TPL + r;
+            put_row(SL::GK, t, gk);
+            put_row(SL::GQ, t, gq);
+            put_row(SL::KT, t, kg);
+            __builtin_amdgcn_sched_barrier(0);   // a token at a time: bounded live range
+          }
+          f32x4 pA1, pP1, pA2, pP2;
+          ap_tiles(pA1, pP1, SL::KT);
+          opaque_inputs();
+          // second pass: the second half's rows about token 7 (the first half's
+          // rows keep the first pass's values; their results are not used)
+#pragma unroll
+          for (int r = 0; r < TPL; ++r) {
+            float fk, fq;
+            norm_factors(r, fk, fq);
+            float gk[8], gq[8];
+            const float4 g0 = g_at(r, 0), g1 = g_at(r, 1);
+            const float G8[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+            for (int cc = 0; cc < 8; ++cc) {
+              const uint32_t odd = SIGNED ? ((parw[r] ^ P7) >> cc) & 1u : 0u;
+              const float rho = with_sign(fexp2(G8[cc] - G7[cc]), odd);
+              const float kk = bf16_of(in_k[r], cc) * fk, qq = bf16_of(in_q[r], cc) * fq;
+              gk[cc] = -kk * rho;
+              gq[cc] = qq * rho;
+            }
+            if (second) {
+              const int t = tg * TPL + r;
+              put_row(SL::GK, t, gk);
+              put_row(SL::GQ, t, gq);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          ap_tiles(pA2, pP2, SL::KT);
+          opaque_inputs();
+          // row l in the second half and columns 4g .. 4g+3 in the first: pass two
+          const bool cross = (lane & 15) >= CB / 2 && 4 * (lane >> 4) < CB / 2;
+          ap_store(cross ? pA2 : pA1, cross ? pP2 : pP1, in_b);
+        } else {
+          // A fall beyond 2^-110 inside a half: A and P element by element from
+          // fp32 ratios 2^(G_i - G_j), with the G table and the parity words.
+          {
+            uint32_t pw = 0u;
+#pragma unroll
+            for (int r = 0; r < TPL; ++r) pw |= parw[r] << (8 * r);
+            lds_put(smem, sb + SL::XP + 4 * lane, pw);
+          }
+          if (NORM) {    // per-token factors into the T tile (written only later)
+#pragma unroll
+            for (int r = 0; r < TPL; ++r) {
+              float fk, fq;
+              norm_factors(r, fk, fq);
+              if (cg == 0) lds_put(smem, sb + SL::TT + 8 * (tg * TPL + r), make_float2(fk, fq));
+            }
+          }
+          const size_t row0 = (size_t)(start + tb) * H + h;
+          const int rsk = H * DK * 2;
+          exact_tiles<DK, SIGNED, NORM>(smem, sb, lane, __shfl(in_b, lane >> 2),
+                                        rsrc(k + row0 * DK, (nbt - 1) * rsk + DK * 2),
+                                        rsrc(q + row0 * DK, (nbt - 1) * rsk + DK * 2), rsk);
+        }
+        operand_planes(Kind<true>{});
+      } else {
+        operand_planes(Kind<false>{});
+      }
+
       // The block's inputs are consumed (beta aside): the next round's block is
       // loaded now, in flight during the tiles and the inverse.
       const float cur_b = in_b;
       if ((lc + 1) * C + CB * I < len) load(lc + 1);
 
       if (!exact) {
-        // ---- A and P for the block, computed transposed: the MFMA's row operand
-        // is K/gamma', its column operand -(gamma' K) or gamma' Q, so lane
-        // (g, l) holds row l and columns 4g .. 4g+3.  The wave reads only
-        // what it wrote, and LDS serves one wave's accesses in order.
-        const int l = lane & 15, gg = lane >> 4;
-        const int rb = sb + 2 * (l * SL::RW + 8 * gg);
-        f32x4 pA = {0.f, 0.f, 0.f, 0.f}, pP = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const bf16x8 ka_h = frag32p(smem, rb + SL::KG, 64 * kb);
-          const bf16x8 ka_l = frag32p(smem, rb + SL::KG + SL::PL, 64 * kb);
-          const bf16x8 rk_h = frag32p(smem, rb + SL::GK, 64 * kb);
-          const bf16x8 rk_l = frag32p(smem, rb + SL::GK + SL::PL, 64 * kb);
-          const bf16x8 rq_h = frag32p(smem, rb + SL::GQ, 64 * kb);
-          const bf16x8 rq_l = frag32p(smem, rb + SL::GQ + SL::PL, 64 * kb);
-          pA = mfma32(ka_l, rk_h, pA);     // A and P alternate (independent chains)
-          pP = mfma32(ka_l, rq_h, pP);
-          pA = mfma32(ka_h, rk_l, pA);
-          pP = mfma32(ka_h, rq_l, pP);
-          pA = mfma32(ka_h, rk_h, pA);
-          pP = mfma32(ka_h, rq_h, pP);
-        }
-        // pA holds -A_lj / beta_l: row l of A, zero on and above the diagonal, to
-        // the fp32 store; row l of P to its fragment unit (l, gg)
-        const float bl = __shfl(cur_b, l);
-        float av[4], pv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = 4 * gg + e;
-          av[e] = j < l ? -pA[e] * bl : 0.f;
-          pv[e] = j <= l ? pP[e] : 0.f;
-        }
-        lds_put(smem, sb + SL::AD + 4 * (l * ADS + 4 * gg), make_float4(av[0], av[1], av[2], av[3]));
-        uint2 hh, ll;
-        split_quad(pv, hh, ll);
-        lds_put(smem, sb + SL::PT + 16 * lane, make_uint4(hh.x, hh.y, ll.x, ll.y));
+        f32x4 pA, pP;
+        ap_tiles(pA, pP, SL::KG);
+        ap_store(pA, pP, cur_b);
       }
 
       // ---- state factor gamma_n, beta, mode
