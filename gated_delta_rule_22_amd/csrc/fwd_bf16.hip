@@ -81,7 +81,6 @@ constexpr int ADS = 20;          // row stride of the fp32 A tile (16-byte rows)
 constexpr float kLog2Floor = -126.f;
 constexpr float kGuardScale = 0x1p110f;   // bound on gamma_n / gamma_t and its inverse
 constexpr float kGateFloor = 0x1p-126f;    // floor of a gate's magnitude
-constexpr float kHalfRange = 110.f;        // exact blocks: bound on |log2| of a half-block factor
 constexpr int kBufferFlags = 0x00020000;   // buffer resource word 3: raw 32-bit data
 constexpr int kSpinLimit = 1 << 18;        // polls of a hand-over counter before giving up
 template <bool B>
@@ -193,7 +192,9 @@ struct Slot {
   static constexpr int PRE = AD + CB * ADS * 4; // gamma_n [DK], signed
   static constexpr int BT = PRE + DK * 4;       // beta [CB]
   static constexpr int MODE = BT + CB * 4;      // 0: factored, 1: exact
-  static constexpr int SIZE = MODE + 16;
+  static constexpr int NF = MODE + 16;          // q/k normalisation factors [CB][2]
+                                                // (preparation only)
+  static constexpr int SIZE = NF + CB * 8;
   // Exact path scratch: G fp32 [CB][DK] and the parity words in the K/gamma'
   // region; the raw (normalised) keys and queries, fp32 [CB][DK], in the GK and
   // GQ regions until the operands overwrite them.
@@ -270,7 +271,7 @@ __device__ __forceinline__ float bf16_of(const uint4 &w, int cc) {
 // 2^(G_i - G_j) (signs from the parity words), with the G table and parity
 // words the caller left in slot `sb`, the keys and queries read from global
 // memory through the block's buffer resources (row stride `rsk` bytes) and,
-// with NORM, the per-token factors the caller left in the slot's T tile.
+// with NORM, the per-token factors in the slot's normalisation table.
 // Lane -> row i = lane / 4, columns 4 (lane % 4) .. +3; `bi` is beta of row i.
 template <int DK, bool SIGNED, bool NORM>
 __device__ __forceinline__ void exact_tiles(char *smem, int sb, int lane, float bi,
@@ -281,7 +282,7 @@ __device__ __forceinline__ void exact_tiles(char *smem, int sb, int lane, float 
   const int ii = lane >> 2, jq = lane & 3;
   const float *xg = reinterpret_cast<const float *>(smem + sb + SL::XG);
   const uint32_t *xp = reinterpret_cast<const uint32_t *>(smem + sb + SL::XP);
-  const float *xf = reinterpret_cast<const float *>(smem + sb + SL::TT);   // [CB][2] factors
+  const float *xf = reinterpret_cast<const float *>(smem + sb + SL::NF);   // [CB][2] factors
   auto par1 = [&](int t, int c) {    // parity of (t, c)
     using PG = PrepGeom<DK>;
     return (xp[(t / TPL) * CG + PG::group_of(c)] >> ((t % TPL) * 8 + PG::index_of(c))) & 1u;
@@ -417,13 +418,13 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
             in_q[r] = in_k[r];
           }
       }
-      // q/k normalisation factors (sum of squares + 1e-6)^(-1/2) of token r: the
-      // CG lanes of a token group hold one token's channels.  Recomputed where
-      // needed rather than kept, to spare registers.
-      auto norm_factors = [&](int r, float &fk, float &fq) {
-        fk = 1.f;
-        fq = 1.f;
-        if (NORM) {
+      // q/k normalisation factors (sum of squares + 1e-6)^(-1/2) of each token:
+      // the CG lanes of a token group hold one token's channels.  They go to the
+      // slot's table (a region only this wave touches) and are read back where
+      // needed, which spares registers.
+      if (NORM) {
+#pragma unroll
+        for (int r = 0; r < TPL; ++r) {
           float sk = 0.f, sq = 0.f;
 #pragma unroll
           for (int cc = 0; cc < 8; ++cc) {
@@ -436,8 +437,18 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
             sk += __shfl_xor(sk, m);
             sq += __shfl_xor(sq, m);
           }
-          fk = __builtin_amdgcn_rsqf(sk + 1e-6f);
-          fq = __builtin_amdgcn_rsqf(sq + 1e-6f);
+          if (cg == 0)
+            lds_put(smem, sb + SL::NF + 8 * (tg * TPL + r),
+                    make_float2(__builtin_amdgcn_rsqf(sk + 1e-6f), __builtin_amdgcn_rsqf(sq + 1e-6f)));
+        }
+      }
+      auto norm_factors = [&](int r, float &fk, float &fq) {
+        fk = 1.f;
+        fq = 1.f;
+        if (NORM) {
+          const float2 f = lds_at<float2>(smem, sb + SL::NF, 8 * (tg * TPL + r));
+          fk = f.x;
+          fq = f.y;
         }
       };
 
@@ -453,19 +464,22 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
       };
       // lane-local: the product of the lane's gates, and the extremes of the
       // products of the gates after each of its tokens (within the lane)
-      float tp[8], smin[8], smax[8];
+      auto lane_products = [&](float (&tp)[8], float (&smin)[8], float (&smax)[8]) {
 #pragma unroll
-      for (int cc = 0; cc < 8; ++cc) { tp[cc] = 1.f; smin[cc] = 1.f; smax[cc] = 1.f; }
+        for (int cc = 0; cc < 8; ++cc) { tp[cc] = 1.f; smin[cc] = 1.f; smax[cc] = 1.f; }
 #pragma unroll
-      for (int r = TPL - 1; r >= 0; --r)
+        for (int r = TPL - 1; r >= 0; --r)
 #pragma unroll
-        for (int cc = 0; cc < 8; ++cc) {
-          if (r < TPL - 1) {
-            smin[cc] = fminf(smin[cc], fabsf(tp[cc]));
-            smax[cc] = fmaxf(smax[cc], fabsf(tp[cc]));
+          for (int cc = 0; cc < 8; ++cc) {
+            if (r < TPL - 1) {
+              smin[cc] = fminf(smin[cc], fabsf(tp[cc]));
+              smax[cc] = fmaxf(smax[cc], fabsf(tp[cc]));
+            }
+            tp[cc] *= gate(r, cc);
           }
-          tp[cc] *= gate(r, cc);
-        }
+      };
+      float tp[8], smin[8], smax[8];
+      lane_products(tp, smin, smax);
       // across token groups: exS = product of the gates of all later groups,
       // gn = gamma_n, the product of all sixteen
       float exS[8], gn[8];
@@ -592,17 +606,19 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
         for (int r = 0; r < TPL; ++r) {
           asm volatile("" : "+v"(in_k[r].x), "+v"(in_k[r].y), "+v"(in_k[r].z), "+v"(in_k[r].w));
           asm volatile("" : "+v"(in_q[r].x), "+v"(in_q[r].y), "+v"(in_q[r].z), "+v"(in_q[r].w));
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf)
+            asm volatile("" : "+v"(in_a[r][hf].x), "+v"(in_a[r][hf].y), "+v"(in_a[r][hf].z),
+                         "+v"(in_a[r][hf].w));
         }
       };
 
       // ---- exact blocks.  G (the cumulative sum of log2|alpha| from the block
       // start, each term floored at -126) and the cumulative parity of negative
       // gates, per (token, channel), in registers.
-      float Gend[8];
-      uint32_t parw[TPL], endP = 0u;
-#pragma unroll
-      for (int r = 0; r < TPL; ++r) parw[r] = 0u;
-      auto g_at = [&](int r, int hf) {    // G of the lane's token r, channels 4 hf .. 4 hf + 3
+      // the lane's token r, channels 4 hf .. 4 hf + 3, of the slot's fp32 [CB][DK]
+      // table (G, then the state pass's row factors)
+      auto g_at = [&](int r, int hf) {
         return lds_at<float4>(smem, sb + SL::XG + 4 * ((tg * TPL + r) * DK + ca), 64 * hf);
       };
 
@@ -615,7 +631,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
       constexpr bool EX = decltype(kind)::value;
       float run[8];
 #pragma unroll
-      for (int cc = 0; cc < 8; ++cc) run[cc] = EX ? 1.f : exS[cc];
+      for (int cc = 0; cc < 8; ++cc) run[cc] = exS[cc];
 #pragma unroll
       for (int r2 = TPL - 2; r2 >= 0; r2 -= 2) {
         uint32_t kwh[2][4], kwl[2][4];
@@ -634,14 +650,13 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
               run[cc] = sa * gate(r, cc);
             }
           } else {
-            const uint32_t pr = parw[r];                 // parity from the block start
-            const uint32_t pc = pr ^ endP;
-            const float4 g0 = g_at(r, 0), g1 = g_at(r, 1);
+            const float4 g0 = g_at(r, 0), g1 = g_at(r, 1);  // gamma_t from the block start
             const float G8[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
 #pragma unroll
             for (int cc = 0; cc < 8; ++cc) {
-              gam8[cc] = with_sign(fexp2(G8[cc]), (pr >> cc) & 1u);
-              kf8[cc] = with_sign(fexp2(Gend[cc] - G8[cc]), (pc >> cc) & 1u);
+              gam8[cc] = G8[cc];
+              kf8[cc] = run[cc];                             // gamma_n / gamma_t
+              run[cc] *= gate(r, cc);
             }
           }
           float gk[8], gq[8], kg[8];
@@ -678,60 +693,6 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
       };
 
       if (exact) {
-        float Gr[TPL][8], tot[8];
-        uint32_t ptot = 0u, pbits = 0u;
-#pragma unroll
-        for (int cc = 0; cc < 8; ++cc) tot[cc] = 0.f;
-#pragma unroll
-        for (int r = 0; r < TPL; ++r) {
-          const float a8[8] = {in_a[r][0].x, in_a[r][0].y, in_a[r][0].z, in_a[r][0].w,
-                               in_a[r][1].x, in_a[r][1].y, in_a[r][1].z, in_a[r][1].w};
-#pragma unroll
-          for (int cc = 0; cc < 8; ++cc) {
-            tot[cc] += fmaxf(flog2(fabsf(a8[cc])), kLog2Floor);
-            if (SIGNED) ptot ^= (__builtin_bit_cast(uint32_t, a8[cc]) >> 31) << cc;
-            Gr[r][cc] = tot[cc];
-          }
-          pbits |= ptot << (8 * r);
-        }
-        // the earlier token groups' sums (and parities) are added to the lane's
-#pragma unroll
-        for (int d = 1; d < TG; d <<= 1) {
-#pragma unroll
-          for (int cc = 0; cc < 8; ++cc) {
-            const float y = __shfl_up(tot[cc], d * CG);
-            if (tg >= d) tot[cc] += y;
-          }
-          if (SIGNED) {
-            const uint32_t y = __shfl_up(ptot, d * CG);
-            if (tg >= d) ptot ^= y;
-          }
-        }
-        uint32_t exP = 0u;
-#pragma unroll
-        for (int cc = 0; cc < 8; ++cc) {
-          const float y = __shfl_up(tot[cc], CG);
-          const float ex = tg ? y : 0.f;
-#pragma unroll
-          for (int r = 0; r < TPL; ++r) Gr[r][cc] += ex;
-          Gend[cc] = __shfl(tot[cc], (TG - 1) * CG + cg);
-        }
-        if (SIGNED) {
-          const uint32_t y = __shfl_up(ptot, CG);
-          exP = tg ? y : 0u;
-          endP = __shfl(ptot, (TG - 1) * CG + cg) & 0xFFu;
-        }
-#pragma unroll
-        for (int r = 0; r < TPL; ++r) parw[r] = (exP ^ (pbits >> (8 * r))) & 0xFFu;
-        // the G table (read back for the state pass's operands below)
-#pragma unroll
-        for (int r = 0; r < TPL; ++r)
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf)
-            lds_put(smem, sb + SL::XG + 4 * ((tg * TPL + r) * DK + ca) + 64 * hf,
-                    make_float4(Gr[r][4 * hf], Gr[r][4 * hf + 1], Gr[r][4 * hf + 2],
-                                Gr[r][4 * hf + 3]));
-
         // Half-block references: every ratio gamma_i / gamma_j (j <= i) splits as
         // (gamma_i / gamma_ref)(gamma_ref / gamma_j) about the last token of j's
         // half (token 7 or 15).  Inside a half that is the factored form of an
@@ -739,35 +700,87 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
         // factors are products of gates (no inverse), so a decaying gate can only
         // make them small.  The tiles are two matrix-core passes: rows and columns
         // referenced to their own half's end, then the second half's rows
-        // referenced to token 7 against the same columns.
-        constexpr int kLane7 = (CB / 2 - 1) / TPL * CG;   // holds token 7 as its last
-        float G7[8];
-#pragma unroll
-        for (int cc = 0; cc < 8; ++cc) G7[cc] = __shfl(Gr[TPL - 1][cc], kLane7 + cg);
-        const uint32_t P7 = SIGNED ? (uint32_t)__shfl((int)parw[TPL - 1], kLane7 + cg) : 0u;
-        const bool second = tg * TPL >= CB / 2;     // the lane's tokens are in the second half
+        // referenced to token 7 against the same columns.  Every factor is a
+        // running product of the signed gates.
+        //   eh: product of the later token groups of the lane's half,
+        //   ph: product of the earlier token groups of the lane's half,
+        //   pp: product of all earlier token groups (from the block start).
+        constexpr int GH = TG / 2;                 // token groups per half
+        const int th = tg % GH;                    // the lane's group within its half
+        const bool second = tg >= GH;              // the lane's tokens are in the second half
+        opaque_inputs();
+        float eh[8], ph[8];
         bool wide = false;
+        {
+          float tl[8], mn[8], mx[8], sh[8];
+          lane_products(tl, mn, mx);
 #pragma unroll
-        for (int r = 0; r < TPL; ++r)
+          for (int cc = 0; cc < 8; ++cc) { sh[cc] = tl[cc]; ph[cc] = tl[cc]; }
+#pragma unroll
+          for (int d = 1; d < GH; d <<= 1)
+#pragma unroll
+            for (int cc = 0; cc < 8; ++cc) {
+              const float y = __shfl_down(sh[cc], d * CG), z = __shfl_up(ph[cc], d * CG);
+              if (th + d < GH) sh[cc] *= y;
+              if (th >= d) ph[cc] *= z;
+            }
 #pragma unroll
           for (int cc = 0; cc < 8; ++cc) {
-            wide |= !(fabsf(Gr[r][cc] - (second ? Gend[cc] : G7[cc])) <= kHalfRange);
-            if (second) wide |= !(Gr[r][cc] - G7[cc] <= kHalfRange);
+            const float y = __shfl_down(sh[cc], CG), z = __shfl_up(ph[cc], CG);
+            eh[cc] = th + 1 < GH ? y : 1.f;
+            ph[cc] = th ? z : 1.f;
+            // the half's factors within 2^+-110
+            const float e = fabsf(eh[cc]);
+            wide |= !(e * mx[cc] <= kGuardScale && e * mn[cc] >= 1.f / kGuardScale);
           }
-        if (!__any(wide)) {
-          const uint32_t pref = second ? endP : P7;
+        }
+        // the state pass's row factors gamma_t (from the block start) to the
+        // slot's table: pp, the product of all earlier token groups, times the
+        // lane's running product
+        auto gamma_table = [&]() {
+          float tl[8], mn[8], mx[8], pr[8];
+          lane_products(tl, mn, mx);
+#pragma unroll
+          for (int cc = 0; cc < 8; ++cc) pr[cc] = tl[cc];
+#pragma unroll
+          for (int d = 1; d < TG; d <<= 1)
+#pragma unroll
+            for (int cc = 0; cc < 8; ++cc) {
+              const float y = __shfl_up(pr[cc], d * CG);
+              if (tg >= d) pr[cc] *= y;
+            }
+          float run[8];
+#pragma unroll
+          for (int cc = 0; cc < 8; ++cc) {
+            const float x = __shfl_up(pr[cc], CG);
+            run[cc] = tg ? x : 1.f;
+          }
 #pragma unroll
           for (int r = 0; r < TPL; ++r) {
+#pragma unroll
+            for (int cc = 0; cc < 8; ++cc) run[cc] *= gate(r, cc);
+            lds_put(smem, sb + SL::XG + 4 * ((tg * TPL + r) * DK + ca),
+                    make_float4(run[0], run[1], run[2], run[3]));
+            lds_put(smem, sb + SL::XG + 4 * ((tg * TPL + r) * DK + ca) + 64,
+                    make_float4(run[4], run[5], run[6], run[7]));
+          }
+        };
+        if (!__any(wide)) {
+          gamma_table();
+          // pass one: columns kappa_t = gamma_ref / gamma_t (the product of the
+          // half's gates after t), rows 1 / kappa_t
+          float run[8];
+#pragma unroll
+          for (int cc = 0; cc < 8; ++cc) run[cc] = eh[cc];
+#pragma unroll
+          for (int r = TPL - 1; r >= 0; --r) {
             float fk, fq;
             norm_factors(r, fk, fq);
             float gk[8], gq[8], kg[8];
-            const float4 g0 = g_at(r, 0), g1 = g_at(r, 1);
-            const float G8[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
 #pragma unroll
             for (int cc = 0; cc < 8; ++cc) {
-              const float x = G8[cc] - (second ? Gend[cc] : G7[cc]);
-              const uint32_t odd = SIGNED ? ((parw[r] ^ pref) >> cc) & 1u : 0u;
-              const float rho = with_sign(fexp2(x), odd), kap = with_sign(fexp2(-x), odd);
+              const float kap = run[cc], rho = __builtin_amdgcn_rcpf(kap);
+              run[cc] = kap * gate(r, cc);
               const float kk = bf16_of(in_k[r], cc) * fk, qq = bf16_of(in_q[r], cc) * fq;
               gk[cc] = -kk * rho;
               gq[cc] = qq * rho;
@@ -782,22 +795,22 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
           f32x4 pA1, pP1, pA2, pP2;
           ap_tiles(pA1, pP1, SL::KT);
           opaque_inputs();
-          // second pass: the second half's rows about token 7 (the first half's
-          // rows keep the first pass's values; their results are not used)
+          // pass two: the second half's rows gamma_t / gamma_7 (the product of the
+          // gates from token 8 to t); the first half's rows keep pass one's values,
+          // whose results are not used
+#pragma unroll
+          for (int cc = 0; cc < 8; ++cc) run[cc] = ph[cc];
 #pragma unroll
           for (int r = 0; r < TPL; ++r) {
             float fk, fq;
             norm_factors(r, fk, fq);
             float gk[8], gq[8];
-            const float4 g0 = g_at(r, 0), g1 = g_at(r, 1);
-            const float G8[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
 #pragma unroll
             for (int cc = 0; cc < 8; ++cc) {
-              const uint32_t odd = SIGNED ? ((parw[r] ^ P7) >> cc) & 1u : 0u;
-              const float rho = with_sign(fexp2(G8[cc] - G7[cc]), odd);
+              run[cc] *= gate(r, cc);
               const float kk = bf16_of(in_k[r], cc) * fk, qq = bf16_of(in_q[r], cc) * fq;
-              gk[cc] = -kk * rho;
-              gq[cc] = qq * rho;
+              gk[cc] = -kk * run[cc];
+              gq[cc] = qq * run[cc];
             }
             if (second) {
               const int t = tg * TPL + r;
@@ -813,26 +826,72 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
           ap_store(cross ? pA2 : pA1, cross ? pP2 : pP1, in_b);
         } else {
           // A fall beyond 2^-110 inside a half: A and P element by element from
-          // fp32 ratios 2^(G_i - G_j), with the G table and the parity words.
+          // fp32 ratios 2^(G_i - G_j), with G (the cumulative sum of log2|alpha|,
+          // each term floored at -126) and the cumulative parities of negative
+          // gates in tables in the slot.
+          float tot[8];
+          uint32_t ptot = 0u, pbits = 0u;
+#pragma unroll
+          for (int cc = 0; cc < 8; ++cc) tot[cc] = 0.f;
+#pragma unroll
+          for (int r = 0; r < TPL; ++r) {
+            const float a8[8] = {in_a[r][0].x, in_a[r][0].y, in_a[r][0].z, in_a[r][0].w,
+                                 in_a[r][1].x, in_a[r][1].y, in_a[r][1].z, in_a[r][1].w};
+#pragma unroll
+            for (int cc = 0; cc < 8; ++cc) {
+              tot[cc] += fmaxf(flog2(fabsf(a8[cc])), kLog2Floor);
+              if (SIGNED) ptot ^= (__builtin_bit_cast(uint32_t, a8[cc]) >> 31) << cc;
+            }
+            lds_put(smem, sb + SL::XG + 4 * ((tg * TPL + r) * DK + ca),
+                    make_float4(tot[0], tot[1], tot[2], tot[3]));
+            lds_put(smem, sb + SL::XG + 4 * ((tg * TPL + r) * DK + ca) + 64,
+                    make_float4(tot[4], tot[5], tot[6], tot[7]));
+            pbits |= ptot << (8 * r);
+          }
+          // the earlier token groups' sums (and parities) are added to the lane's
+#pragma unroll
+          for (int d = 1; d < TG; d <<= 1) {
+#pragma unroll
+            for (int cc = 0; cc < 8; ++cc) {
+              const float y = __shfl_up(tot[cc], d * CG);
+              if (tg >= d) tot[cc] += y;
+            }
+            if (SIGNED) {
+              const uint32_t y = __shfl_up(ptot, d * CG);
+              if (tg >= d) ptot ^= y;
+            }
+          }
+          float ex[8];
+          uint32_t exP = 0u;
+#pragma unroll
+          for (int cc = 0; cc < 8; ++cc) {
+            const float y = __shfl_up(tot[cc], CG);
+            ex[cc] = tg ? y : 0.f;
+          }
+          if (SIGNED) {
+            const uint32_t y = __shfl_up(ptot, CG);
+            exP = tg ? y : 0u;
+          }
+#pragma unroll
+          for (int r = 0; r < TPL; ++r)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+              float4 gg = g_at(r, hf);
+              gg.x += ex[4 * hf]; gg.y += ex[4 * hf + 1]; gg.z += ex[4 * hf + 2]; gg.w += ex[4 * hf + 3];
+              lds_put(smem, sb + SL::XG + 4 * ((tg * TPL + r) * DK + ca) + 64 * hf, gg);
+            }
           {
             uint32_t pw = 0u;
 #pragma unroll
-            for (int r = 0; r < TPL; ++r) pw |= parw[r] << (8 * r);
+            for (int r = 0; r < TPL; ++r) pw |= ((exP ^ (pbits >> (8 * r))) & 0xFFu) << (8 * r);
             lds_put(smem, sb + SL::XP + 4 * lane, pw);
-          }
-          if (NORM) {    // per-token factors into the T tile (written only later)
-#pragma unroll
-            for (int r = 0; r < TPL; ++r) {
-              float fk, fq;
-              norm_factors(r, fk, fq);
-              if (cg == 0) lds_put(smem, sb + SL::TT + 8 * (tg * TPL + r), make_float2(fk, fq));
-            }
           }
           const size_t row0 = (size_t)(start + tb) * H + h;
           const int rsk = H * DK * 2;
           exact_tiles<DK, SIGNED, NORM>(smem, sb, lane, __shfl(in_b, lane >> 2),
                                         rsrc(k + row0 * DK, (nbt - 1) * rsk + DK * 2),
                                         rsrc(q + row0 * DK, (nbt - 1) * rsk + DK * 2), rsk);
+          gamma_table();   // over the G table, which the tiles have finished reading
         }
         operand_planes(Kind<true>{});
       } else {
