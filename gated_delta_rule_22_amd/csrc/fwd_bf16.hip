@@ -525,9 +525,12 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
         const int kb = sb + SL::KT + 16 * kt_unit(2 * (cg >> 2), t0 >> 2, 4 * (cg & 3));
 #pragma unroll
         for (int cc = 0; cc < 8; ++cc) {
-          const int sh = 16 * (cc & 1), wd = cc >> 1;
-          const uint32_t hw = ((kwh[0][wd] >> sh) & 0xFFFFu) | (((kwh[1][wd] >> sh) & 0xFFFFu) << 16);
-          const uint32_t lw = ((kwl[0][wd] >> sh) & 0xFFFFu) | (((kwl[1][wd] >> sh) & 0xFFFFu) << 16);
+          // half-word cc & 1 of token t0's word, then of token t0 + 1's, in one byte
+          // permute (bytes 0-3 select from the second operand, 4-7 from the first)
+          const int wd = cc >> 1;
+          const uint32_t sel = (cc & 1) ? 0x07060302u : 0x05040100u;
+          const uint32_t hw = __builtin_amdgcn_perm(kwh[1][wd], kwh[0][wd], sel);
+          const uint32_t lw = __builtin_amdgcn_perm(kwl[1][wd], kwl[0][wd], sel);
           const int ko = kb + 16 * kt_unit(cc >> 2, 0, cc & 3);
           if (TPL == 4) {
             if (r2 == 2) {
