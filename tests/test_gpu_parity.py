@@ -314,6 +314,33 @@ def test_forward_fused_qk_l2norm(dtype, dk, dv):
     assert eo <= TOL[dtype] and es <= TOL[dtype]
 
 
+@pytest.mark.parametrize("kda", [False, True])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128)])
+def test_forward_half_block_exact_path_with_options(dk, dv, kda):
+    """bf16 path, every fourth key channel at |alpha| in [0.001, 0.01] (most
+    16-token blocks leave the factored range and take the exact path with
+    half-block references), un-normalised q/k with the fused normalisation,
+    KDA mode on and off, ragged packed sequences and S0."""
+    from tests._gpu import upload
+    lens = [150, 33, 96]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    x = _raw_qk(_rand_forward(66, B=1, T=int(cu[-1]), H=2, dk=dk, dv=dv, dtype="bf16", cu=cu), 67)
+    rng = np.random.default_rng(68)
+    fast = rng.uniform(0.001, 0.01, size=x["g"].shape) * np.sign(x["g"])
+    x["g"] = np.where(np.arange(dk) % 4 == 3, fast, x["g"]).astype(np.float32)
+    d = upload(x)
+    say(f"[gpu] ckda_forward_ex half-block exact path, normalize_qk, kda={kda} {dk}x{dv}")
+    o, S = ck.forward(d["q"], d["k"], d["v"], d["g"], d["beta"], S0=d["S0"],
+                      cu_seqlens=d["cu_seqlens"], normalize_qk=True, kda=kda)
+    torch.cuda.synchronize()
+    g = np.abs(x["g"]) if kda else x["g"]
+    o_ref, S_ref = oracle.forward(oracle.l2_normalise(x["q"]), oracle.l2_normalise(x["k"]), x["v"], g,
+                                  x["beta"], S0=x["S0"], cu_seqlens=x["cu_seqlens"])
+    eo, es = rel_err(o.cpu().numpy(), o_ref), rel_err(S.cpu().numpy(), S_ref)
+    say(f"  err(o)={eo:.3e} err(S_T)={es:.3e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
 def _bf16_bound(o_gpu, o_ref, tol):
     """Error beyond one bf16 rounding of the reference, relative to its RMS."""
     o_gpu = np.asarray(o_gpu, np.float64)
