@@ -125,6 +125,8 @@ def main():
     ap.add_argument("--skip-forward", action="store_true")
     ap.add_argument("--skip-backward", action="store_true")
     ap.add_argument("--bwd-steps", type=int, default=10)
+    ap.add_argument("--skip-split", action="store_true",
+                    help="skip timing the two-kernel hand-off variant of the forward")
     ap.add_argument("--skip-others", action="store_true",
                     help="skip timing the fp32 and packed-varlen forward configs")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -237,6 +239,47 @@ def main():
                       "ckda_over_kda_throughput": ms_kda / ms_ckda_alt,
                       "timing": f"{n_blk} alternating blocks of {per_blk} launches each",
                       "gates": "|alpha| of the same workload"}
+        if not args.skip_split:
+            # The two-kernel hand-off the fused kernel replaced (CKDA_OPT_SPLIT: a
+            # preparation kernel writes every prepared block, a state kernel reads
+            # them), the same arithmetic, timed in alternating blocks against the
+            # fused kernel.  Its results are checked bit-identical to the fused ones.
+            from gated_delta_rule_22_amd import _lib
+            ws_bytes = ck.forward_workspace_bytes(w.B, w.T, w.H, w.dk, w.dv, w.B, torch.bfloat16,
+                                                  _lib.OPT_SPLIT)
+            ws_split = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+            o_split = torch.empty_like(o)
+            S_split = torch.empty_like(S_T)
+            run_split = lambda: ck.forward(q, k, v, g, beta, out=o_split, final_state=S_split,
+                                           workspace=ws_split, split=True)
+            run()
+            for _ in range(max(3, args.warmup // 4)):
+                run_split()
+            torch.cuda.synchronize()
+            identical = bool(torch.equal(o, o_split) and torch.equal(S_T, S_split))
+            t_fused = t_split = 0.0
+            for blk in range(n_blk):
+                order = ((run, True), (run_split, False)) if blk % 2 == 0 else ((run_split, False), (run, True))
+                for fn, is_fused in order:
+                    e0.record(stream)
+                    for _ in range(per_blk):
+                        fn()
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    if is_fused:
+                        t_fused += e0.elapsed_time(e1)
+                    else:
+                        t_split += e0.elapsed_time(e1)
+            ms_fused = t_fused / (n_blk * per_blk)
+            ms_split = t_split / (n_blk * per_blk)
+            out["hand_off"] = {"ms_per_step": ms_split, "fused_ms_per_step_alternating": ms_fused,
+                               "over_fused": ms_split / ms_fused,
+                               "bit_identical_to_fused": identical,
+                               "prepared_bytes": ws_bytes,
+                               "timing": f"{n_blk} alternating blocks of {per_blk} launches each",
+                               "what": "preparation kernel writing every prepared 16-token "
+                                       "block, then the state-pass kernel reading them"}
+            del ws_split, o_split, S_split
         del q, k, v, g, ga, beta, o, S_T, ws
         torch.cuda.empty_cache()
 

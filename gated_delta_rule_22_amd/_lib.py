@@ -41,6 +41,8 @@ def library() -> ctypes.CDLL:
         lib.ckda_status_string.restype = ctypes.c_char_p
         lib.ckda_forward_workspace_bytes.argtypes = [ci] * 7
         lib.ckda_forward_workspace_bytes.restype = sz
+        lib.ckda_forward_ex_workspace_bytes.argtypes = [ci] * 8
+        lib.ckda_forward_ex_workspace_bytes.restype = sz
         lib.ckda_forward.argtypes = [vp] * 7 + [ci] * 7 + [vp, vp, vp, sz, vp]
         lib.ckda_forward.restype = ci
         lib.kda_forward.argtypes = [vp] * 7 + [ci] * 7 + [vp, vp, vp, sz, vp]
@@ -87,8 +89,10 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def forward_workspace_bytes(B, T, H, dk, dv, N, dtype) -> int:
+def forward_workspace_bytes(B, T, H, dk, dv, N, dtype, options=0) -> int:
     code = dtype if isinstance(dtype, int) else (CKDA_BF16 if dtype == torch.bfloat16 else CKDA_F32)
+    if options:
+        return int(library().ckda_forward_ex_workspace_bytes(B, T, H, dk, dv, N, code, options))
     return int(library().ckda_forward_workspace_bytes(B, T, H, dk, dv, N, code))
 
 
@@ -103,12 +107,12 @@ def _need(t, name, dtype=None, shape=None):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
-OPT_KDA, OPT_QK_L2NORM, OPT_O_BF16 = 1, 2, 4     # CKDA_OPT_* in include/ckda.h
+OPT_KDA, OPT_QK_L2NORM, OPT_O_BF16, OPT_SPLIT = 1, 2, 4, 8   # CKDA_OPT_* in include/ckda.h
 
 
 def forward(q, k, v, g, beta, S0=None, cu_seqlens=None, *, out=None, final_state=None,
             workspace=None, output_final_state=True, normalize_qk=False,
-            out_dtype=torch.float32, kda=False, no_alloc=False):
+            out_dtype=torch.float32, kda=False, no_alloc=False, split=False):
     """CKDA chunkwise forward.  Returns ``(o, S_T)`` (``S_T`` is None when
     ``output_final_state`` is False).  See ``ckda_forward`` in include/ckda.h
     for shapes; ``final_state`` may be ``S0`` itself to advance it in place.
@@ -119,11 +123,12 @@ def forward(q, k, v, g, beta, S0=None, cu_seqlens=None, *, out=None, final_state
     to ``ckda_forward``.  ``no_alloc=True`` calls ``ckda_forward_noalloc``,
     which uses the library's fixed scratch instead of a workspace (pass
     ``out``, and ``final_state`` or ``output_final_state=False``, so that
-    nothing is allocated here either)."""
+    nothing is allocated here either).  ``split=True`` runs the two-kernel
+    hand-off (``CKDA_OPT_SPLIT``) in place of the fused kernel."""
     if out_dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("out_dtype must be torch.float32 or torch.bfloat16")
     opts = ((OPT_KDA if kda else 0) | (OPT_QK_L2NORM if normalize_qk else 0)
-            | (OPT_O_BF16 if out_dtype == torch.bfloat16 else 0))
+            | (OPT_O_BF16 if out_dtype == torch.bfloat16 else 0) | (OPT_SPLIT if split else 0))
     entry = "ckda_forward_noalloc" if no_alloc else (
         "ckda_forward_ex" if opts else "ckda_forward")
     return _forward(entry, q, k, v, g, beta, S0, cu_seqlens, out, final_state, workspace,
@@ -171,7 +176,7 @@ def _forward(entry, q, k, v, g, beta, S0, cu_seqlens, out, final_state, workspac
         st = library().ckda_forward_noalloc(*head, opts, _ptr(o), _ptr(S_T), _stream(dev))
         _check(st, entry)
         return o, S_T
-    ws_bytes = forward_workspace_bytes(B, T, H, dk, dv, N, code)
+    ws_bytes = forward_workspace_bytes(B, T, H, dk, dv, N, code, opts)
     if workspace is None or workspace.numel() * workspace.element_size() < ws_bytes:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     tail = (_ptr(o), _ptr(S_T), _ptr(workspace), ws_bytes, _stream(dev))

@@ -164,16 +164,38 @@ extern "C" size_t ckda_forward_workspace_bytes(int B, int T, int H, int dk, int 
 
 namespace {
 
+// Workspace of a forward with these options: the layout above, then (with
+// CKDA_OPT_SPLIT) the slot images of the two-kernel hand-off.
+size_t forward_ex_bytes(int B, int T, int H, int dk, int dv, int N, int in_dtype, int options) {
+  const size_t base = fwd_layout(B, T, H, dk, dv, N, in_dtype).total;
+  if (!(options & CKDA_OPT_SPLIT)) return base;
+  return align256(base) + fwd_bf16_split_bytes(T, H, dk, N);
+}
+
+}  // namespace
+
+extern "C" size_t ckda_forward_ex_workspace_bytes(int B, int T, int H, int dk, int dv, int N,
+                                                  int in_dtype, int options) {
+  if (forward_shape_status(B, T, H, dk, dv, N, in_dtype, B == 1 && N != B) != CKDA_OK)
+    return 0;
+  return forward_ex_bytes(B, T, H, dk, dv, N, in_dtype, options);
+}
+
+namespace {
+
 int forward_impl(const void *q, const void *k, const void *v, const float *g, const float *beta,
                  const float *S0, const int32_t *cu_seqlens, int B, int T, int H, int dk, int dv,
                  int N, int in_dtype, int options, void *o, float *S_T, void *workspace,
                  size_t workspace_bytes, void *stream) {
   const bool packed = cu_seqlens != nullptr;
   if (int s = forward_shape_status(B, T, H, dk, dv, N, in_dtype, packed)) return s;
-  if (options & ~(CKDA_OPT_KDA | CKDA_OPT_QK_L2NORM | CKDA_OPT_O_BF16)) return CKDA_ERR_SHAPE;
+  if (options & ~(CKDA_OPT_KDA | CKDA_OPT_QK_L2NORM | CKDA_OPT_O_BF16 | CKDA_OPT_SPLIT))
+    return CKDA_ERR_SHAPE;
   const int signed_gates = (options & CKDA_OPT_KDA) ? 0 : 1;
   const int l2norm = (options & CKDA_OPT_QK_L2NORM) ? 1 : 0;
   const int o_bf16 = (options & CKDA_OPT_O_BF16) ? 1 : 0;
+  const bool split = (options & CKDA_OPT_SPLIT) != 0;
+  if (split && (in_dtype != CKDA_BF16 || packed || l2norm || o_bf16)) return CKDA_ERR_SHAPE;
   const size_t rows = (size_t)B * T * H;
   if (rows > 0 && (!q || !k || !v || !g || !beta || !o)) return CKDA_ERR_NULL;
   const void *ptrs[] = {q, k, v, g, S0, o, S_T, workspace};
@@ -196,12 +218,13 @@ int forward_impl(const void *q, const void *k, const void *v, const float *g, co
   if (S_T != S0 && overlaps(S_T, st_bytes, S0, st_bytes)) return CKDA_ERR_ALIAS;
 
   const FwdLayout L = fwd_layout(B, T, H, dk, dv, N, in_dtype);
-  if (!workspace || workspace_bytes < L.total) return CKDA_ERR_WORKSPACE;
-  if (overlaps(workspace, L.total, o, o_bytes) || overlaps(workspace, L.total, S_T, st_bytes) ||
-      overlaps(workspace, L.total, S0, st_bytes))
+  const size_t need = forward_ex_bytes(B, T, H, dk, dv, N, in_dtype, options);
+  if (!workspace || workspace_bytes < need) return CKDA_ERR_WORKSPACE;
+  if (overlaps(workspace, need, o, o_bytes) || overlaps(workspace, need, S_T, st_bytes) ||
+      overlaps(workspace, need, S0, st_bytes))
     return CKDA_ERR_ALIAS;
   for (const Span &s : ins)
-    if (overlaps(workspace, L.total, s.p, s.n)) return CKDA_ERR_ALIAS;
+    if (overlaps(workspace, need, s.p, s.n)) return CKDA_ERR_ALIAS;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (int s = debug_prologue(cu_seqlens, N, T, workspace, L.total, st)) return s;
@@ -211,8 +234,12 @@ int forward_impl(const void *q, const void *k, const void *v, const float *g, co
     // Uniform rows need no table: the kernel derives each sequence from its row.
     if (packed && launch_seq_table(cu_seqlens, B, T, N, tab, st) != hipSuccess)
       return CKDA_ERR_LAUNCH;
-    e = launch_fwd_bf16(q, k, v, g, beta, S0, o, S_T, T, H, dk, dv, N, tab, packed ? 1 : 0,
-                        signed_gates, l2norm, o_bf16, st);
+    if (split)
+      e = launch_fwd_bf16_split(q, k, v, g, beta, S0, o, S_T, T, H, dk, dv, N, tab, signed_gates,
+                                static_cast<char *>(workspace) + align256(L.total), st);
+    else
+      e = launch_fwd_bf16(q, k, v, g, beta, S0, o, S_T, T, H, dk, dv, N, tab, packed ? 1 : 0,
+                          signed_gates, l2norm, o_bf16, st);
   } else {
     if (launch_seq_table(cu_seqlens, B, T, N, tab, st) != hipSuccess) return CKDA_ERR_LAUNCH;
     void *records = static_cast<char *>(workspace) + L.table_bytes;
@@ -288,7 +315,7 @@ extern "C" int ckda_forward_noalloc(const void *q, const void *k, const void *v,
                                     float *S_T, void *stream) {
   const bool packed = cu_seqlens != nullptr;
   if (int s = forward_shape_status(B, T, H, dk, dv, N, in_dtype, packed)) return s;
-  if (fwd_layout(B, T, H, dk, dv, N, in_dtype).total > kStaticScratchBytes)
+  if (forward_ex_bytes(B, T, H, dk, dv, N, in_dtype, options) > kStaticScratchBytes)
     return CKDA_ERR_SCRATCH;
   void *ws = static_scratch();
   if (!ws) return CKDA_ERR_LAUNCH;

@@ -74,6 +74,16 @@ hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, const fl
                            int dk, int dv, int N, SeqTable tab, int packed, int signed_gates,
                            int l2norm, int o_bf16, hipStream_t stream);
 
+// The same forward as two kernels (uniform rows, no fused options): a
+// preparation kernel writes every prepared 16-token block's slot image to
+// `img` (fwd_bf16_split_bytes bytes), then a state kernel loads them.  Kept to
+// measure the hand-off the fused kernel replaced; results are bit-identical.
+size_t fwd_bf16_split_bytes(int T, int H, int dk, int N);
+hipError_t launch_fwd_bf16_split(const void *q, const void *k, const void *v, const float *g,
+                                 const float *beta, const float *S0, void *o, float *S_T, int T,
+                                 int H, int dk, int dv, int N, SeqTable tab, int signed_gates,
+                                 void *img, hipStream_t stream);
+
 // fp64 chunkwise backward (both input dtypes).  Runs the records and the
 // forward's serial pass (keeping per-chunk states and U), the reverse pass of
 // the state gradient, then the per-chunk gradients.  signed_gates = 0 is KDA

@@ -323,12 +323,18 @@ __device__ __forceinline__ void exact_tiles(char *smem, int sb, int lane, float 
 // ---------------------------------------------------------------- kernel
 // SIGNED: CKDA (false: KDA mode, gate signs ignored).  NORM: q and k are
 // L2-normalised per (token, head) on the fly.  OBF16: o is written as bf16.
-template <int DK, bool SIGNED, bool NORM, bool OBF16>
+// PIPE: 0, the fused kernel; 1 and 2, the two halves of the two-kernel
+// hand-off it replaced (uniform rows only), kept for measurement: 1 runs only
+// the preparation, one workgroup of four preparation waves per (sequence,
+// head, 64-token round), and writes each prepared block's slot image to `img`;
+// 2 runs the state pass with waves 4-7 loading those images into the slots.
+template <int DK, bool SIGNED, bool NORM, bool OBF16, int PIPE>
 __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
     const __hip_bfloat16 *__restrict__ q, const __hip_bfloat16 *__restrict__ k,
     const __hip_bfloat16 *__restrict__ v, const float *__restrict__ g,
     const float *__restrict__ beta, const float *S0, void *__restrict__ o,
-    float *S_T, int T, int H, int DV, int NH, int NV, SeqTable tab, int packed) {
+    float *S_T, int T, int H, int DV, int NH, int NV, SeqTable tab, int packed,
+    char *__restrict__ img) {
   using SL = Slot<DK>;
   using PG = PrepGeom<DK>;
   constexpr int CG = PG::CG, TG = PG::TG, TPL = PG::TPL;
@@ -342,8 +348,17 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
   // ---- which (sequence, head, dv block): XCD-aware.  Workgroup b runs on XCD
   // b % 8; the NV dv blocks of one (sequence, head) share an XCD (and its L2),
   // and low ranks (the longest sequences when packed) start first.
-  const int b = blockIdx.x, xcd = b & 7, slot = b >> 3;
-  const int pidx = (slot / NV) * 8 + xcd, vb = slot % NV;
+  int pidx, vb, lc1 = 0;
+  if constexpr (PIPE == 1) {         // (sequence, head, round) of uniform rows
+    const int nr = (T + C - 1) / C;
+    pidx = (int)(blockIdx.x / (unsigned)nr);
+    lc1 = (int)(blockIdx.x % (unsigned)nr);
+    vb = 0;
+  } else {
+    const int b = blockIdx.x, xcd = b & 7, slot = b >> 3;
+    pidx = (slot / NV) * 8 + xcd;
+    vb = slot % NV;
+  }
   if (pidx >= NH) return;
   const int rank = pidx / H, h = pidx % H;
   int n, start, len;
@@ -371,10 +386,32 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
   auto rsrc = [&](const void *p, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, bytes, kBufferFlags);
   };
+  // Slot image of the two-kernel hand-off: the parts of a slot the state pass
+  // reads, the row planes and then the (K / gamma')^T units through the mode
+  // word, for block b = 4 lc + I of (sequence, head) pidx of uniform rows.
+  constexpr int IMG_A = 4 * SL::PL, IMG = IMG_A + (SL::NF - SL::KT);
+  auto image = [&](int lcx, int Ix) {
+    const size_t nblk = (size_t)((T + CB - 1) / CB);
+    return img + ((size_t)pidx * nblk + (size_t)lcx * NB + (size_t)Ix) * IMG;
+  };
+  auto slot_offset = [](int i) { return i < IMG_A ? SL::GK + i : SL::KT + (i - IMG_A); };
 
-  if (w >= 4) {
+  if (PIPE == 1 || w >= 4) {
     // ======================= preparation: wave 4 + I fills slot I
-    const int I = w - 4, sb = I * SLOT;
+    const int I = PIPE == 1 ? w : w - 4, sb = I * SLOT;
+    if constexpr (PIPE == 2) {
+      // the slot images of the preparation kernel, loaded in place of it
+      for (int lc = 0; lc < nch; ++lc) {
+        if (lc * C + CB * I >= len) break;
+        wait_for(s_done + I, 4 * lc);    // the state pass is done with the slot
+        const char *src = image(lc, I);
+        for (int i = 16 * lane; i < IMG; i += 16 * 64)
+          lds_put(smem, sb + slot_offset(i), *reinterpret_cast<const uint4 *>(src + i));
+        publish(s_ready + I, lc + 1, lane == 0);
+      }
+      return;
+    }
+
     const int tg = lane / CG, cg = lane % CG, ca = PG::base(cg);
     float4 in_a[TPL][2];
     uint4 in_k[TPL], in_q[TPL];
@@ -402,9 +439,10 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
       const auto rb = rsrc(beta + row0, (nbt - 1) * H * 4 + 4);
       in_b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, lane * H * 4, 0, 0));
     };
-    if (CB * I < len) load(0);
+    const int lc_lo = PIPE == 1 ? lc1 : 0, lc_hi = PIPE == 1 ? lc1 + 1 : nch;
+    if (lc_lo * C + CB * I < len) load(lc_lo);
 
-    for (int lc = 0; lc < nch; ++lc) {
+    for (int lc = lc_lo; lc < lc_hi; ++lc) {
       const int tb = lc * C + CB * I;
       if (tb >= len) break;              // past the sequence end (last round only)
       const int nbt = min(CB, len - tb);
@@ -506,7 +544,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
       const bool exact = __any(bad);
 
       // ---- the slot is free once the state pass is done with the previous round
-      wait_for(s_done + I, 4 * lc);
+      if constexpr (PIPE == 0) wait_for(s_done + I, 4 * lc);
 
       // (K / gamma')^T of tokens t0 = tg * TPL + r2 and t0 + 1 (hi and lo words
       // of eight channels each): per channel, the hi and lo words of the token
@@ -904,7 +942,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
       // The block's inputs are consumed (beta aside): the next round's block is
       // loaded now, in flight during the tiles and the inverse.
       const float cur_b = in_b;
-      if ((lc + 1) * C + CB * I < len) load(lc + 1);
+      if (PIPE == 0 && (lc + 1) * C + CB * I < len) load(lc + 1);
 
       if (!exact) {
         f32x4 pA, pP;
@@ -947,10 +985,16 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
         lds_put(smem, sb + SL::TT + 16 * (16 * q + i), make_uint4(hh.x, hh.y, ll.x, ll.y));
       }
 
-      // ---- hand the slot over
-      publish(s_ready + I, lc + 1, lane == 0);
+      // ---- hand the slot over (two-kernel hand-off: write its image)
+      if constexpr (PIPE == 1) {
+        char *dst = image(lc, I);
+        for (int i = 16 * lane; i < IMG; i += 16 * 64)
+          *reinterpret_cast<uint4 *>(dst + i) = lds_at<uint4>(smem, sb + slot_offset(i), 0);
+      } else {
+        publish(s_ready + I, lc + 1, lane == 0);
+      }
     }
-  } else {
+  } else if constexpr (PIPE != 1) {
     // ======================= state pass (waves 0-3)
     const int l16 = lane & 15, gq = lane >> 4;
     const int col = vb * BV + 16 * w + l16;
@@ -1124,18 +1168,37 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
   }
 }
 
-template <int DK, bool SIGNED, bool NORM, bool OBF16>
+template <int DK, bool SIGNED, bool NORM, bool OBF16, int PIPE = 0>
 hipError_t launch_dk(const void *q, const void *k, const void *v, const float *g,
                      const float *beta, const float *S0, void *o, float *S_T, int T, int H,
-                     int DV, int N, SeqTable tab, int packed, hipStream_t stream) {
+                     int DV, int N, SeqTable tab, int packed, hipStream_t stream,
+                     char *img = nullptr) {
   const int NH = N * H, NV = DV / BV;
   const int groups = (NH + 7) / 8;
-  const dim3 grid((unsigned)groups * 8u * (unsigned)NV), block(NT);
-  hipLaunchKernelGGL((fwd_bf16_kernel<DK, SIGNED, NORM, OBF16>), grid, block, 0, stream,
+  dim3 grid((unsigned)groups * 8u * (unsigned)NV), block(NT);
+  if (PIPE == 1) {
+    grid = dim3((unsigned)NH * (unsigned)((T + C - 1) / C));
+    block = dim3(NT / 2);          // the four preparation waves
+  }
+  hipLaunchKernelGGL((fwd_bf16_kernel<DK, SIGNED, NORM, OBF16, PIPE>), grid, block, 0, stream,
                      static_cast<const __hip_bfloat16 *>(q), static_cast<const __hip_bfloat16 *>(k),
                      static_cast<const __hip_bfloat16 *>(v), g, beta, S0, o, S_T, T, H, DV, NH, NV,
-                     tab, packed);
+                     tab, packed, img);
   return hipGetLastError();
+}
+
+// The two-kernel hand-off: the preparation kernel, then the state kernel.
+template <int DK, bool SIGNED>
+hipError_t launch_split(const void *q, const void *k, const void *v, const float *g,
+                        const float *beta, const float *S0, void *o, float *S_T, int T, int H,
+                        int DV, int N, SeqTable tab, char *img, hipStream_t stream) {
+  if (T == 0) return launch_dk<DK, SIGNED, false, false, 0>(q, k, v, g, beta, S0, o, S_T, T, H,
+                                                             DV, N, tab, 0, stream);
+  hipError_t e = launch_dk<DK, SIGNED, false, false, 1>(q, k, v, g, beta, S0, o, S_T, T, H, DV, N,
+                                                        tab, 0, stream, img);
+  if (e != hipSuccess) return e;
+  return launch_dk<DK, SIGNED, false, false, 2>(q, k, v, g, beta, S0, o, S_T, T, H, DV, N, tab,
+                                                0, stream, img);
 }
 
 // One kernel per option combination, so no option costs a branch in the loop.
@@ -1161,6 +1224,31 @@ hipError_t launch_opts(const void *q, const void *k, const void *v, const float 
 }
 
 }  // namespace
+
+size_t fwd_bf16_split_bytes(int T, int H, int dk, int N) {
+  const size_t blocks = (size_t)N * H * (size_t)((T + CB - 1) / CB);
+  auto image = [](auto slot) {
+    using SL = decltype(slot);
+    return (size_t)(4 * SL::PL + (SL::NF - SL::KT));
+  };
+  return blocks * (dk == 64 ? image(Slot<64>{}) : image(Slot<128>{}));
+}
+
+hipError_t launch_fwd_bf16_split(const void *q, const void *k, const void *v, const float *g,
+                                 const float *beta, const float *S0, void *o, float *S_T, int T,
+                                 int H, int dk, int dv, int N, SeqTable tab, int signed_gates,
+                                 void *img, hipStream_t stream) {
+  char *im = static_cast<char *>(img);
+  if (dk == 64)
+    return signed_gates
+               ? launch_split<64, true>(q, k, v, g, beta, S0, o, S_T, T, H, dv, N, tab, im, stream)
+               : launch_split<64, false>(q, k, v, g, beta, S0, o, S_T, T, H, dv, N, tab, im, stream);
+  if (dk == 128)
+    return signed_gates
+               ? launch_split<128, true>(q, k, v, g, beta, S0, o, S_T, T, H, dv, N, tab, im, stream)
+               : launch_split<128, false>(q, k, v, g, beta, S0, o, S_T, T, H, dv, N, tab, im, stream);
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, const float *g,
                            const float *beta, const float *S0, void *o, float *S_T, int T, int H,

@@ -74,7 +74,9 @@ enum {
 enum {
     CKDA_OPT_KDA = 1,        /* KDA mode: gate signs ignored (|g| is used) */
     CKDA_OPT_QK_L2NORM = 2,  /* q and k L2-normalised per (token, head) in the kernel */
-    CKDA_OPT_O_BF16 = 4      /* o written as bfloat16 (round to nearest even) */
+    CKDA_OPT_O_BF16 = 4,     /* o written as bfloat16 (round to nearest even) */
+    CKDA_OPT_SPLIT = 8       /* two-kernel hand-off instead of the fused kernel
+                                (kept for measurement; see ckda_forward_ex) */
 };
 
 /* Version of this ABI (bumped on any incompatible change). */
@@ -170,17 +172,38 @@ int kda_forward(const void *q, const void *k, const void *v, const float *g,
  *                        caller's arrays are not modified
  *    CKDA_OPT_O_BF16     o is [B, T, H, dv] bfloat16: the fp32 result rounded
  *                        to nearest even (halves o's HBM traffic)
+ *    CKDA_OPT_SPLIT      the chunk preparation as its own kernel: it writes
+ *                        every prepared 16-token block (operand planes, T, P,
+ *                        gate factors; about 1.8 KB per token and head) to
+ *                        the workspace, and a second kernel runs the state
+ *                        pass on them.  The same arithmetic as the fused
+ *                        kernel, so the results are bit-identical; kept to
+ *                        measure that hand-off against the fused kernel.
+ *                        bf16 inputs and uniform rows (cu_seqlens NULL) only,
+ *                        without CKDA_OPT_QK_L2NORM or CKDA_OPT_O_BF16
+ *                        (CKDA_ERR_SHAPE otherwise); the workspace must hold
+ *                        ckda_forward_ex_workspace_bytes(...) bytes
  *  o        fp32 or bf16 per CKDA_OPT_O_BF16; 16-byte aligned
  *
- * Every other argument, the workspace size and all error rules are those of
- * ckda_forward; unknown option bits return CKDA_ERR_SHAPE.  ckda_forward is
- * ckda_forward_ex with options 0, kda_forward with CKDA_OPT_KDA.
+ * Every other argument, the workspace size (but for CKDA_OPT_SPLIT) and all
+ * error rules are those of ckda_forward; unknown option bits return
+ * CKDA_ERR_SHAPE.  ckda_forward is ckda_forward_ex with options 0,
+ * kda_forward with CKDA_OPT_KDA.
  */
 int ckda_forward_ex(const void *q, const void *k, const void *v, const float *g,
                     const float *beta, const float *S0, const int32_t *cu_seqlens,
                     int B, int T, int H, int dk, int dv, int N, int in_dtype, int options,
                     void *o, float *S_T, void *workspace, size_t workspace_bytes,
                     void *stream);
+
+/*
+ * Workspace needed by ckda_forward_ex (and, for its fixed scratch, by
+ * ckda_forward_noalloc) with these options, in bytes: that of ckda_forward,
+ * plus with CKDA_OPT_SPLIT the hand-off's prepared blocks.  Returns 0 if the
+ * sizes are invalid.
+ */
+size_t ckda_forward_ex_workspace_bytes(int B, int T, int H, int dk, int dv, int N,
+                                       int in_dtype, int options);
 
 /*
  * ckda_forward_ex for callers that cannot allocate device memory: code under
@@ -191,10 +214,10 @@ int ckda_forward_ex(const void *q, const void *k, const void *v, const float *g,
  * nothing (host or device).  Every other argument, layout, option and error
  * is that of ckda_forward_ex; the results are bit-identical to it.
  *
- *  Returns CKDA_ERR_SCRATCH when ckda_forward_workspace_bytes(...) for the
- *  call exceeds the fixed size (bf16 inputs need only a sequence table of
- *  16 bytes per sequence; fp32 inputs need their per-chunk records, so only
- *  small fp32 calls fit).
+ *  Returns CKDA_ERR_SCRATCH when ckda_forward_ex_workspace_bytes(...) for
+ *  the call exceeds the fixed size (bf16 inputs need only a sequence table of
+ *  16 bytes per sequence; fp32 inputs need their per-chunk records, and
+ *  CKDA_OPT_SPLIT its prepared blocks, so only small such calls fit).
  *
  *  Concurrency: all calls on one GPU share that GPU's scratch, which keeps
  *  the last call's contents (nothing in it needs to start at zero).  Calls

@@ -95,11 +95,35 @@ def test_forward_ex_rejects_unknown_options(lib):
     o = ctypes.c_void_p(1 << 32)
     call = lambda opts: lib.ckda_forward_ex(p, p, p, p, p, None, None, 2, 64, 2, 128, 128, 2, 0,
                                            opts, o, None, ctypes.c_void_p(1 << 20), 1 << 40, None)
-    assert call(8) == 2 and call(16) == 2
+    assert call(16) == 2 and call(32) == 2
     q_bad = lambda opts: lib.ckda_forward_ex(ctypes.c_void_p(18), p, p, p, p, None, None, 2, 64, 2,
                                              128, 128, 2, 0, opts, o, None,
                                              ctypes.c_void_p(1 << 20), 1 << 40, None)
     assert q_bad(7) == 4                                        # still checks alignment
+
+
+def test_split_option_limits_and_workspace(lib):
+    """CKDA_OPT_SPLIT: bf16 inputs and uniform rows only, without the fused
+    normalisation or a bf16 o; its workspace adds the prepared blocks (16-token
+    blocks of every (sequence, head)), and a smaller one is refused.  Every
+    call fails validation before any launch."""
+    SPLIT = 8
+    p = ctypes.c_void_p(16)
+    o = ctypes.c_void_p(1 << 32)
+    cu = ctypes.c_void_p(1 << 36)
+
+    def call(opts, dtype=0, cu_seqlens=None, B=2, N=2, ws_bytes=1 << 40):
+        return lib.ckda_forward_ex(p, p, p, p, p, None, cu_seqlens, B, 64, 2, 128, 128, N, dtype,
+                                   opts, o, None, ctypes.c_void_p(1 << 20), ws_bytes, None)
+    assert call(SPLIT, dtype=1) == 2                            # fp32 inputs
+    assert call(SPLIT, cu_seqlens=cu, B=1, N=3) == 2            # packed sequences
+    assert call(SPLIT | 2) == 2 and call(SPLIT | 4) == 2        # fused options
+    base = lib.ckda_forward_ex_workspace_bytes(2, 64, 2, 128, 128, 2, 0, 0)
+    need = lib.ckda_forward_ex_workspace_bytes(2, 64, 2, 128, 128, 2, 0, SPLIT)
+    assert base == lib.ckda_forward_workspace_bytes(2, 64, 2, 128, 128, 2, 0)
+    assert need >= base + 2 * 2 * (64 // 16) * 16 * 1024        # at least 1 KB per token and head
+    assert call(SPLIT, ws_bytes=need - 1) == 5
+    assert lib.ckda_forward_ex_workspace_bytes(2, 64, 2, 100, 128, 2, 0, SPLIT) == 0
 
 
 def _bwd(lib, B=2, T=64, H=2, dk=128, dv=128, N=None, dtype=0, ws=1 << 40, null=(), misalign=(),

@@ -341,6 +341,40 @@ def test_forward_half_block_exact_path_with_options(dk, dv, kda):
     assert eo <= TOL["bf16"] and es <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("kda", [False, True])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (128, 64)])
+def test_forward_split_hand_off_equals_fused(dk, dv, kda):
+    """CKDA_OPT_SPLIT (a preparation kernel writes every prepared 16-token
+    block to the workspace, a state kernel runs on them) does the fused
+    kernel's arithmetic: bit-identical o and S_T, and both match the oracle.
+    Uniform rows with a ragged last round, S0, and blocks on the exact path."""
+    from tests._gpu import upload
+    x = _rand_forward(70, B=3, T=150, H=2, dk=dk, dv=dv, dtype="bf16")
+    x["g"][1, 40:48, 1, :5] = 2e-3            # exact blocks (half-block references)
+    x["g"][2, 100:103, 0, :2] = 1e-30         # an exact block element by element
+    d = upload(x)
+    say(f"[gpu] ckda_forward_ex split hand-off kda={kda} {dk}x{dv}")
+    o1, S1 = ck.forward(d["q"], d["k"], d["v"], d["g"], d["beta"], S0=d["S0"], kda=kda)
+    o2, S2 = ck.forward(d["q"], d["k"], d["v"], d["g"], d["beta"], S0=d["S0"], kda=kda, split=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    g = np.abs(x["g"]) if kda else x["g"]
+    o_ref, S_ref = oracle.forward(x["q"], x["k"], x["v"], g, x["beta"], S0=x["S0"])
+    eo, es = rel_err(o2.cpu().numpy(), o_ref), rel_err(S2.cpu().numpy(), S_ref)
+    say(f"  err(o)={eo:.3e} err(S_T)={es:.3e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+def test_forward_split_empty_rows_keep_the_state():
+    """T = 0 with CKDA_OPT_SPLIT: S_T equals S0 and nothing else runs."""
+    from tests._gpu import upload
+    x = _rand_forward(71, B=2, T=0, H=2, dk=128, dv=128, dtype="bf16")
+    d = upload(x)
+    o, S = ck.forward(d["q"], d["k"], d["v"], d["g"], d["beta"], S0=d["S0"], split=True)
+    torch.cuda.synchronize()
+    assert o.numel() == 0 and torch.equal(S, d["S0"])
+
+
 def _bf16_bound(o_gpu, o_ref, tol):
     """Error beyond one bf16 rounding of the reference, relative to its RMS."""
     o_gpu = np.asarray(o_gpu, np.float64)
