@@ -400,14 +400,30 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(
     // ======================= preparation: wave 4 + I fills slot I
     const int I = PIPE == 1 ? w : w - 4, sb = I * SLOT;
     if constexpr (PIPE == 2) {
-      // the slot images of the preparation kernel, loaded in place of it
+      // the slot images of the preparation kernel, loaded in place of it: a
+      // round's image is read into registers while the state pass still works
+      // on the slot's previous block, then written once the slot is free
+      constexpr int NU = (IMG + 1023) / 1024;      // 16-byte units per lane
+      uint4 buf[NU];
+      auto fetch = [&](int lc) {
+        const char *src = image(lc, I);
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+          const int i = 1024 * u + 16 * lane;
+          if (i < IMG) buf[u] = *reinterpret_cast<const uint4 *>(src + i);
+        }
+      };
+      if (CB * I < len) fetch(0);
       for (int lc = 0; lc < nch; ++lc) {
         if (lc * C + CB * I >= len) break;
         wait_for(s_done + I, 4 * lc);    // the state pass is done with the slot
-        const char *src = image(lc, I);
-        for (int i = 16 * lane; i < IMG; i += 16 * 64)
-          lds_put(smem, sb + slot_offset(i), *reinterpret_cast<const uint4 *>(src + i));
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+          const int i = 1024 * u + 16 * lane;
+          if (i < IMG) lds_put(smem, sb + slot_offset(i), buf[u]);
+        }
         publish(s_ready + I, lc + 1, lane == 0);
+        if ((lc + 1) * C + CB * I < len) fetch(lc + 1);
       }
       return;
     }
