@@ -365,6 +365,27 @@ def test_forward_split_hand_off_equals_fused(dk, dv, kda):
     assert eo <= TOL["bf16"] and es <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("B,T,dk,dv", [(1, 17, 64, 128), (2, 64, 128, 64), (1, 1, 128, 128)])
+def test_forward_split_edge_shapes_and_no_alloc(B, T, dk, dv):
+    """CKDA_OPT_SPLIT at a partial block, one exact round and a single token,
+    through the workspace entry and through ckda_forward_noalloc (its fixed
+    scratch holds the prepared blocks of such small calls): bit-identical to
+    the fused kernel."""
+    from tests._gpu import upload
+    x = _rand_forward(72, B=B, T=T, H=3, dk=dk, dv=dv, dtype="bf16")
+    d = upload(x)
+    args = (d["q"], d["k"], d["v"], d["g"], d["beta"])
+    say(f"[gpu] ckda_forward_ex split B={B} T={T} {dk}x{dv}, workspace and no-alloc entries")
+    o1, S1 = ck.forward(*args, S0=d["S0"])
+    o2, S2 = ck.forward(*args, S0=d["S0"], split=True)
+    o3 = torch.full_like(o1, float("nan"))
+    S3 = torch.full_like(S1, float("nan"))
+    ck.forward(*args, S0=d["S0"], out=o3, final_state=S3, no_alloc=True, split=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    assert torch.equal(o1, o3) and torch.equal(S1, S3)
+
+
 def test_forward_split_empty_rows_keep_the_state():
     """T = 0 with CKDA_OPT_SPLIT: S_T equals S0 and nothing else runs."""
     from tests._gpu import upload
