@@ -39,6 +39,10 @@
  *    the kernels run.
  *  - Calls that share no output buffer may run concurrently on different
  *    streams.
+ *  - A call enqueues kernel launches only (no memset, copy or allocation;
+ *    CKDA_DEBUG aside), so it may be captured into a HIP graph on `stream`.
+ *    A replay runs the same kernels on the same pointers and sizes and reads
+ *    the buffers' contents at replay time.
  */
 #ifndef CKDA_H
 #define CKDA_H
