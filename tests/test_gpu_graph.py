@@ -67,10 +67,14 @@ def _capture(fn):
     return graph, outs
 
 
+@pytest.mark.parametrize("no_alloc", [False, True])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("packed", [False, True])
-def test_forward_replays_match_eager(dtype, packed):
-    H, dk, dv = 4, 128, 128
+def test_forward_replays_match_eager(dtype, packed, no_alloc):
+    """``no_alloc`` captures ckda_forward_noalloc (outputs allocated before the
+    capture, the library's fixed scratch in place of a workspace) and checks it
+    against eager ckda_forward calls."""
+    H, dk, dv = (2 if no_alloc else 4), 128, 128
     if packed:
         lens = [70, 1, 193, 0, 64]
         B, T = 1, sum(lens)
@@ -78,10 +82,21 @@ def test_forward_replays_match_eager(dtype, packed):
         N = len(lens)
     else:
         B, T, cu, N = 2, 150, None, 2
-    say(f"[gpu] graph capture of ckda_forward {dtype} packed={packed} B={B} T={T} H={H}")
+    if no_alloc:   # host-side check that the case fits the fixed scratch
+        need = ck.forward_workspace_bytes(
+            B, T, H, dk, dv, N, torch.bfloat16 if dtype == "bf16" else torch.float32)
+        assert need <= ck.library().ckda_forward_noalloc_max_bytes()
+    say(f"[gpu] graph capture of ckda_forward{'_noalloc' if no_alloc else ''} {dtype} "
+        f"packed={packed} B={B} T={T} H={H}")
     static = _draw(100, B, T, H, dk, dv, dtype, N)
+    o_pre = torch.empty((B, T, H, dv), dtype=torch.float32, device="cuda")
+    S_pre = torch.empty((N, H, dk, dv), dtype=torch.float32, device="cuda")
 
-    def call():
+    def call(captured=True):
+        if no_alloc and captured:
+            return ck.forward(static["q"], static["k"], static["v"], static["g"], static["beta"],
+                              S0=static["S0"], cu_seqlens=cu, out=o_pre, final_state=S_pre,
+                              no_alloc=True)
         return ck.forward(static["q"], static["k"], static["v"], static["g"], static["beta"],
                           S0=static["S0"], cu_seqlens=cu)
 
@@ -91,7 +106,7 @@ def test_forward_replays_match_eager(dtype, packed):
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        o_e, S_e = call()                  # eager, on the same inputs
+        o_e, S_e = call(captured=False)    # eager ckda_forward, on the same inputs
         torch.cuda.synchronize()
         say(f"  replay {r}: |o|max={o_g.abs().max().item():.3f}")
         _same(o_g, o_e, f"o, replay {r}")
